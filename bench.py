@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Benchmark of the PowerSGD compression step with error feedback on one MI355X.
+
+Workload: ResNet-18 (CIFAR) gradient shapes, 21 compressed matrices + 41 uncompressed
+tensors (11,173,962 parameters), rank 2, W = 16 simulated workers held as 16 slices in
+HBM, fp32.  One step = one psgd_compress_step over all tensors (EF add, P = M Q, worker
+mean, Gram-Schmidt, Q = M^T P, worker mean, decompress, new errors).  Inputs are
+synthetic (planted low-rank part + worker noise), drawn on the device before timing.
+
+Prints one JSON line:
+  value          gradient GB/s = W * numel * 4 bytes / step time (whole job, one GPU)
+  pct_hbm_peak   minimal HBM bytes of a step / step time / 8 TB/s
+  roofline       the longest kernel: algorithmic bytes per launch / its mean duration
+                 (HIP events recorded on the launch stream around every launch)
+  cpu_baseline   the CPU oracle timed on a bounded sample of the same workload
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+METRIC = "PowerSGD step gradient GB/s (ResNet-18 shapes, r=2, W=16) & % HBM peak"
+KERNEL_SRC = os.path.join(ROOT, "distributed_sgd_gradient_ef_amd", "csrc", "kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_resnet18_r2_w16.json")
+
+
+def kernel_bytes(plan, dtype_bytes: int) -> dict:
+    """Algorithmic HBM bytes per launch of each kernel for this plan."""
+    s = plan.sizes
+    W, r = s["n_workers"], s["rank"]
+    mn, vn = s["matrix_numel"], s["vector_numel"]
+    gb = dtype_bytes
+    return {
+        # read G_w, E_w on every worker, write the mean once; tensors without error: G only
+        "k_ef_mean": (W * (gb + 4) + 4) * mn + (W * gb + 4) * vn,
+        # read Mbar once (Q, P are cache-resident)
+        "k_p_rows": 4 * mn + 4 * s["p_elems"],
+        "k_q_partial": 4 * mn,
+        # read G_w, E_w and write E'_w on every worker, write U once; tensors without
+        # error: read the mean, write the update
+        "k_apply": (W * (gb + 8) + 4) * mn + 8 * vn,
+    }
+
+
+def traffic_for(kernel: str):
+    """Measured HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        with open(KERNEL_SRC, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    if not k or t.get("kernel_source_sha256") != sha:
+        return None
+    return k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, seconds: float) -> dict:
+    """Time the CPU oracle on whole steps of the same workload (at least one step)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from distributed_sgd_gradient_ef_amd import workloads as WL
+    from oracle import powersgd_ef as O
+
+    grads = WL.grads(wl, 0)
+    layers = []
+    for i, (_, shp) in enumerate(wl.shapes):
+        q = WL.q0(wl, i) if WL.is_matrix(shp, wl.rank) else None
+        layers.append(O.LayerState(grads[i], np.zeros_like(grads[i]), q))
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        O.compress_layers(layers)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    t_step = el / steps
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    gbytes = wl.workers * wl.numel() * 4 / 1e9
+    return {"value": round(gbytes / t_step, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{steps} whole step(s) of the same workload (all 21 matrices and 41 tensors, "
+                      f"W=16, r=2), numpy float64 oracle, {t_step:.2f} s per step; BLAS threads = cores"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline sample length")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the W data-parallel workers are simulated as slices of "
+              "one GPU's HBM, and no multi-GPU path is built. Use --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from distributed_sgd_gradient_ef_amd import psgd
+    from distributed_sgd_gradient_ef_amd import workloads as WL
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        return 1
+    psgd.load_library()
+    dev = torch.device("cuda:0")
+    wl = WL.workload("resnet18")
+    shapes = [s for _, s in wl.shapes]
+    plan = psgd.psgd_plan_create(shapes, wl.rank, wl.workers)
+    s = plan.sizes
+    W, ld = wl.workers, s["worker_stride"]
+    grads = torch.zeros((W, ld), dtype=torch.float32, device=dev)
+    errors = torch.zeros((W, ld), dtype=torch.float32, device=dev)
+    q = torch.zeros(s["q_elems"], dtype=torch.float32, device=dev)
+    p = torch.zeros(s["p_elems"], dtype=torch.float32, device=dev)
+    update = torch.zeros(ld, dtype=torch.float32, device=dev)
+    workspace = torch.empty(s["workspace_bytes"], dtype=torch.uint8, device=dev)
+    WL.device_grads(wl, 0, [(L.offset, L.rows, L.cols) for L in plan.layers], grads)
+    qh = psgd.pack_factors(plan, {i: WL.q0(wl, i) for i, L in enumerate(plan.layers) if L.compressed}, "q")
+    q.copy_(torch.from_numpy(qh).to(dev))
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        psgd.psgd_compress_step(plan, grads, errors, q, p, update, workspace, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+
+    # timed region 1: the step as a caller runs it
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - wall0
+    ms = t0.elapsed_time(t1) / args.steps
+
+    # timed region 2: the same steps with every kernel bracketed by HIP events
+    psgd.psgd_plan_set_timing(plan, True)
+    psgd.psgd_plan_kernel_stats(plan, reset=True)
+    t2, t3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t2.record(stream)
+    for _ in range(args.steps):
+        step()
+    t3.record(stream)
+    torch.cuda.synchronize(dev)
+    ms_timed = t2.elapsed_time(t3) / args.steps
+    stats = psgd.psgd_plan_kernel_stats(plan, reset=True)
+    psgd.psgd_plan_set_timing(plan, False)
+
+    kb = kernel_bytes(plan, 4)
+    kernels = {}
+    for name, (n, tot) in stats.items():
+        us = 1e3 * tot / max(n, 1)
+        entry = {"mean_us": round(us, 2), "launches": n}
+        if name in kb:
+            entry["alg_bytes"] = kb[name]
+            entry["alg_GBps"] = round(kb[name] / (us * 1e-6) / 1e9, 1)
+        kernels[name] = entry
+    dom = max(kernels, key=lambda k: kernels[k]["mean_us"])
+    dom_us = kernels[dom]["mean_us"]
+    achieved = kb[dom] / (dom_us * 1e-6) / 1e9
+    traffic = traffic_for(dom)
+
+    grad_bytes = W * s["numel"] * 4
+    value = grad_bytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (planted low-rank + 0.05*N(0,1) worker noise, drawn on device)",
+        "config": {"workload": "resnet18_cifar_shapes", "rank": wl.rank, "workers": W,
+                   "matrices": s["n_matrices"], "uncompressed_tensors": s["n_vectors"],
+                   "params": s["numel"], "grad_bytes_per_step": grad_bytes},
+        "pct_hbm_peak": round(100.0 * s["model_bytes"] / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 2),
+        "model_bytes_per_step": s["model_bytes"],
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "alg_bytes_per_launch": kb[dom], "mean_us": dom_us},
+        "kernels": kernels,
+        "ms_per_step_with_kernel_events": round(ms_timed, 4),
+        "wall_s_timed_region": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

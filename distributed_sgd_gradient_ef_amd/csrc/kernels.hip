@@ -1,0 +1,622 @@
+// gfx950 kernels of libpsgd and the two step entry points.
+//
+// One step (the PowerSGD review page, section "Proposed method": EF add, P = M Q from
+// the warm-start Q, all-reduce, orthonormalise, Q = M^T P, all-reduce, decompress
+// P Q^T, keep the error; then momentum SGD) runs as six batched launches over every
+// tensor of the plan:
+//
+//   k_ef_mean     streams G_w and E_w of all W workers once and writes the worker
+//                 mean Mbar = mean_w (G_w + E_w) (for uncompressed tensors: mean_w G_w).
+//                 Because the compressor is linear and the W workers share one Q,
+//                 mean_w M_w Q = Mbar Q and mean_w M_w^T P = Mbar^T P: the in-HBM
+//                 all-reduce of P and Q becomes one pass over the worker slices.
+//   k_p_rows      P-bar = Mbar Q_in, one wave per row, lanes across the columns.
+//   k_mgs         modified Gram-Schmidt of P-bar, one workgroup per matrix.
+//   k_q_partial   Q partials = Mbar^T P over row blocks and column strips.
+//   k_q_reduce    Q = sum of the partials (fixed order, deterministic).
+//   k_apply       streams G_w and E_w again: E'_w = (G_w + E_w) - P Q^T, writes the
+//                 decompressed update once, and in the momentum entry point updates
+//                 momentum and parameters in the same pass.
+//
+// All streaming work is HBM-bound (about one flop per byte), so no MFMA is used.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <string>
+
+#include "plan.hpp"
+
+namespace psgd {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+
+struct bf16 {
+  unsigned short bits;
+};
+
+// ------------------------------------------------------------------ loads and stores
+__device__ __forceinline__ f4 load4(const float* p) { return *reinterpret_cast<const f4*>(p); }
+
+__device__ __forceinline__ f4 load4(const bf16* p) {
+  const u16x4 v = *reinterpret_cast<const u16x4*>(p);
+  f4 r;
+  r.x = __uint_as_float(uint32_t(v.x) << 16);
+  r.y = __uint_as_float(uint32_t(v.y) << 16);
+  r.z = __uint_as_float(uint32_t(v.z) << 16);
+  r.w = __uint_as_float(uint32_t(v.w) << 16);
+  return r;
+}
+
+// Store the first `valid` (>= 1) lanes of v; all four when valid >= 4.
+__device__ __forceinline__ void store4(float* p, const f4 v, int64_t valid) {
+  if (valid >= 4) {
+    *reinterpret_cast<f4*>(p) = v;
+  } else {
+    p[0] = v.x;
+    if (valid > 1) p[1] = v.y;
+    if (valid > 2) p[2] = v.z;
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Sum over the workgroup; every thread gets the same value (same order everywhere).
+__device__ double block_sum(double v, double* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  double s = 0.0;
+  const int nw = blockDim.x >> 6;
+  for (int i = 0; i < nw; ++i) s += red[i];
+  return s;
+}
+
+// ------------------------------------------------------------------ pass 1: EF add + mean
+template <typename GT>
+__global__ __launch_bounds__(kStreamThreads) void k_ef_mean(const StreamTile* __restrict__ tiles,
+                                                            const GT* __restrict__ G,
+                                                            const float* __restrict__ E,
+                                                            float* __restrict__ Mbar, int W,
+                                                            int64_t ld, float inv_w) {
+  const StreamTile t = tiles[blockIdx.x];
+  const bool mat = t.mat >= 0;
+  for (int64_t c = t.begin + int64_t(threadIdx.x) * 4; c < t.end; c += kStreamThreads * 4) {
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    int w = 0;
+    if (mat) {
+      for (; w + 4 <= W; w += 4) {
+        const f4 g0 = load4(G + (w + 0) * ld + c), e0 = load4(E + (w + 0) * ld + c);
+        const f4 g1 = load4(G + (w + 1) * ld + c), e1 = load4(E + (w + 1) * ld + c);
+        const f4 g2 = load4(G + (w + 2) * ld + c), e2 = load4(E + (w + 2) * ld + c);
+        const f4 g3 = load4(G + (w + 3) * ld + c), e3 = load4(E + (w + 3) * ld + c);
+        acc += g0 + e0;
+        acc += g1 + e1;
+        acc += g2 + e2;
+        acc += g3 + e3;
+      }
+      for (; w < W; ++w) acc += load4(G + w * ld + c) + load4(E + w * ld + c);
+    } else {
+      for (; w + 4 <= W; w += 4) {
+        const f4 g0 = load4(G + (w + 0) * ld + c), g1 = load4(G + (w + 1) * ld + c);
+        const f4 g2 = load4(G + (w + 2) * ld + c), g3 = load4(G + (w + 3) * ld + c);
+        acc += g0;
+        acc += g1;
+        acc += g2;
+        acc += g3;
+      }
+      for (; w < W; ++w) acc += load4(G + w * ld + c);
+    }
+    store4(Mbar + c, acc * inv_w, t.end - c);
+  }
+}
+
+// ------------------------------------------------------------------ P-bar = Mbar Q
+template <int R>
+__global__ __launch_bounds__(kRowThreads) void k_p_rows(const RowTile* __restrict__ tiles,
+                                                        const MatInfo* __restrict__ mats,
+                                                        const float* __restrict__ Mbar,
+                                                        const float* __restrict__ Q,
+                                                        float* __restrict__ Pbar) {
+  const RowTile t = tiles[blockIdx.x];
+  const MatInfo mi = mats[t.mat];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float* Qm = Q + mi.q_off;
+  const int cols = mi.cols;
+  for (int row = t.row_begin + wave; row < t.row_end; row += kRowThreads / 64) {
+    const float* mrow = Mbar + mi.offset + int64_t(row) * cols;
+    float acc[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k) acc[k] = 0.f;
+    if (mi.vec4) {
+      for (int j = lane * 4; j < cols; j += 256) {
+        const f4 v = load4(mrow + j);
+        const float* qj = Qm + int64_t(j) * R;
+#pragma unroll
+        for (int k = 0; k < R; ++k)
+          acc[k] += v.x * qj[k] + v.y * qj[R + k] + v.z * qj[2 * R + k] + v.w * qj[3 * R + k];
+      }
+    } else {
+      for (int j = lane; j < cols; j += 64) {
+        const float v = mrow[j];
+#pragma unroll
+        for (int k = 0; k < R; ++k) acc[k] += v * Qm[int64_t(j) * R + k];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k) acc[k] = wave_sum(acc[k]);
+    if (lane == 0) {
+#pragma unroll
+      for (int k = 0; k < R; ++k) Pbar[mi.p_off + int64_t(row) * R + k] = acc[k];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ Gram-Schmidt
+// Modified Gram-Schmidt over the R columns of P-bar (rows x R, row-major), in column
+// order.  Dot products and norms accumulate in double.  A column whose residual norm
+// is at most 1e-4 of its norm before orthogonalisation (or zero) becomes zero.
+// Each thread only touches its own rows, so only the reductions synchronise.
+template <int R>
+__global__ __launch_bounds__(kMgsThreads) void k_mgs(const MatInfo* __restrict__ mats,
+                                                     const float* __restrict__ Pbar,
+                                                     float* __restrict__ P) {
+  __shared__ double red[kMgsThreads / 64];
+  const MatInfo mi = mats[blockIdx.x];
+  const float* src = Pbar + mi.p_off;
+  float* dst = P + mi.p_off;
+  const int n = mi.rows;
+  for (int k = 0; k < R; ++k) {
+    double s = 0.0;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      const float v = src[int64_t(i) * R + k];
+      dst[int64_t(i) * R + k] = v;
+      s += double(v) * double(v);
+    }
+    const double before = sqrt(block_sum(s, red));
+    for (int l = 0; l < k; ++l) {
+      double c = 0.0;
+      for (int i = threadIdx.x; i < n; i += blockDim.x)
+        c += double(dst[int64_t(i) * R + l]) * double(dst[int64_t(i) * R + k]);
+      c = block_sum(c, red);
+      for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        const int64_t o = int64_t(i) * R;
+        dst[o + k] = float(double(dst[o + k]) - c * double(dst[o + l]));
+      }
+    }
+    double s2 = 0.0;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      const double v = dst[int64_t(i) * R + k];
+      s2 += v * v;
+    }
+    const double after = sqrt(block_sum(s2, red));
+    const double scale = (after > 0.0 && after > 1e-4 * before) ? 1.0 / after : 0.0;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      const int64_t o = int64_t(i) * R + k;
+      dst[o] = float(double(dst[o]) * scale);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ Q = Mbar^T P
+template <int R>
+__global__ __launch_bounds__(kQThreads) void k_q_partial(const QTile* __restrict__ tiles,
+                                                         const MatInfo* __restrict__ mats,
+                                                         const float* __restrict__ Mbar,
+                                                         const float* __restrict__ P,
+                                                         float* __restrict__ Qpart) {
+  const QTile t = tiles[blockIdx.x];
+  const MatInfo mi = mats[t.mat];
+  const int cols = mi.cols;
+  const int r0 = t.blk * mi.rows_per_blk;
+  const int r1 = min(mi.rows, r0 + mi.rows_per_blk);
+  const float* Pm = P + mi.p_off;
+  const float* base = Mbar + mi.offset;
+  float* out = Qpart + mi.qpart_off + int64_t(t.blk) * cols * R;
+  if (mi.vec4) {
+    const int j = t.col_begin + int(threadIdx.x) * 4;
+    if (j >= t.col_end) return;
+    float acc[4][R];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int k = 0; k < R; ++k) acc[q][k] = 0.f;
+    for (int i = r0; i < r1; ++i) {
+      const f4 v = load4(base + int64_t(i) * cols + j);
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const float pk = Pm[int64_t(i) * R + k];
+        acc[0][k] += v.x * pk;
+        acc[1][k] += v.y * pk;
+        acc[2][k] += v.z * pk;
+        acc[3][k] += v.w * pk;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int k = 0; k < R; ++k) out[int64_t(j + q) * R + k] = acc[q][k];
+  } else {
+    const int j = t.col_begin + int(threadIdx.x);
+    if (j >= t.col_end) return;
+    float acc[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k) acc[k] = 0.f;
+    for (int i = r0; i < r1; ++i) {
+      const float v = base[int64_t(i) * cols + j];
+#pragma unroll
+      for (int k = 0; k < R; ++k) acc[k] += v * Pm[int64_t(i) * R + k];
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k) out[int64_t(j) * R + k] = acc[k];
+  }
+}
+
+__global__ __launch_bounds__(kQRedThreads) void k_q_reduce(const MatInfo* __restrict__ mats,
+                                                           const float* __restrict__ Qpart,
+                                                           float* __restrict__ Q, int R) {
+  const MatInfo mi = mats[blockIdx.y];
+  const int64_t n = int64_t(mi.cols) * R;
+  const float* part = Qpart + mi.qpart_off;
+  for (int64_t idx = int64_t(blockIdx.x) * kQRedThreads + threadIdx.x; idx < n;
+       idx += int64_t(gridDim.x) * kQRedThreads) {
+    float s = 0.f;
+    for (int b = 0; b < mi.nblk; ++b) s += part[int64_t(b) * n + idx];
+    Q[mi.q_off + idx] = s;
+  }
+}
+
+// ------------------------------------------------------------------ pass 2: error + update
+enum ApplyMode { kCompress = 0, kMomentum = 1, kNesterov = 2 };
+
+template <int MODE>
+__device__ __forceinline__ void momentum4(float* mom, float* x, const f4 u, int64_t c, int64_t valid,
+                                          float lr, float mu) {
+  if (MODE == kCompress) return;
+  const f4 m0 = load4(mom + c), x0 = load4(x + c);
+  const f4 m1 = mu * m0 + u;
+  const f4 x1 = (MODE == kNesterov) ? x0 - lr * (u + mu * m1) : x0 - lr * m1;
+  store4(mom + c, m1, valid);
+  store4(x + c, x1, valid);
+}
+
+template <typename GT, int R, int MODE>
+__global__ __launch_bounds__(kStreamThreads) void k_apply(
+    const StreamTile* __restrict__ tiles, const MatInfo* __restrict__ mats, const GT* __restrict__ G,
+    float* __restrict__ E, const float* __restrict__ Mbar, const float* __restrict__ P,
+    const float* __restrict__ Q, float* __restrict__ update, float* __restrict__ mom,
+    float* __restrict__ x, int W, int64_t ld, float lr, float mu) {
+  const StreamTile t = tiles[blockIdx.x];
+  if (t.mat < 0) {  // uncompressed tensor: the update is the worker mean
+    for (int64_t c = t.begin + int64_t(threadIdx.x) * 4; c < t.end; c += kStreamThreads * 4) {
+      const f4 u = load4(Mbar + c);
+      const int64_t valid = t.end - c;
+      if (update != nullptr) store4(update + c, u, valid);
+      momentum4<MODE>(mom, x, u, c, valid, lr, mu);
+    }
+    return;
+  }
+  const MatInfo mi = mats[t.mat];
+  const float* Pm = P + mi.p_off;
+  const float* Qm = Q + mi.q_off;
+  const int cols = mi.cols;
+  for (int64_t c = t.begin + int64_t(threadIdx.x) * 4; c < t.end; c += kStreamThreads * 4) {
+    const int64_t valid = t.end - c;
+    const int e0 = int(c - mi.offset);
+    int i = e0 / cols;
+    int j = e0 - i * cols;
+    float u[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float s = 0.f;
+      if (q < valid) {
+#pragma unroll
+        for (int k = 0; k < R; ++k) s += Pm[int64_t(i) * R + k] * Qm[int64_t(j) * R + k];
+      }
+      u[q] = s;
+      if (++j == cols) {
+        j = 0;
+        ++i;
+      }
+    }
+    const f4 uv = {u[0], u[1], u[2], u[3]};
+    int w = 0;
+    for (; w + 4 <= W; w += 4) {
+      const f4 g0 = load4(G + (w + 0) * ld + c), e0v = load4(E + (w + 0) * ld + c);
+      const f4 g1 = load4(G + (w + 1) * ld + c), e1v = load4(E + (w + 1) * ld + c);
+      const f4 g2 = load4(G + (w + 2) * ld + c), e2v = load4(E + (w + 2) * ld + c);
+      const f4 g3 = load4(G + (w + 3) * ld + c), e3v = load4(E + (w + 3) * ld + c);
+      store4(E + (w + 0) * ld + c, (g0 + e0v) - uv, valid);
+      store4(E + (w + 1) * ld + c, (g1 + e1v) - uv, valid);
+      store4(E + (w + 2) * ld + c, (g2 + e2v) - uv, valid);
+      store4(E + (w + 3) * ld + c, (g3 + e3v) - uv, valid);
+    }
+    for (; w < W; ++w) {
+      const f4 g = load4(G + w * ld + c), e = load4(E + w * ld + c);
+      store4(E + w * ld + c, (g + e) - uv, valid);
+    }
+    if (update != nullptr) store4(update + c, uv, valid);
+    momentum4<MODE>(mom, x, uv, c, valid, lr, mu);
+  }
+}
+
+// ------------------------------------------------------------------ host helpers
+psgd_status hip_fail(const char* what, hipError_t e) {
+  set_error(std::string(what) + ": " + hipGetErrorString(e));
+  return PSGD_ERR_HIP;
+}
+
+uint64_t align256(uint64_t x) { return (x + 255) / 256 * 256; }
+
+psgd_status ensure_tables(psgd_plan* plan, DeviceTables** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+  auto it = plan->dev.find(dev);
+  if (it != plan->dev.end()) {
+    *out = &it->second;
+    return PSGD_OK;
+  }
+  const uint64_t b_mats = align256(plan->mats.size() * sizeof(MatInfo) + 1);
+  const uint64_t b_st = align256(plan->stiles.size() * sizeof(StreamTile) + 1);
+  const uint64_t b_rt = align256(plan->rtiles.size() * sizeof(RowTile) + 1);
+  const uint64_t b_qt = align256(plan->qtiles.size() * sizeof(QTile) + 1);
+  void* base = nullptr;
+  e = hipMalloc(&base, b_mats + b_st + b_rt + b_qt);
+  if (e != hipSuccess) {
+    set_error(std::string("hipMalloc of the plan's device tables: ") + hipGetErrorString(e));
+    return PSGD_ERR_NO_MEMORY;
+  }
+  DeviceTables t;
+  t.base = base;
+  char* b = static_cast<char*>(base);
+  t.mats = reinterpret_cast<MatInfo*>(b);
+  t.stiles = reinterpret_cast<StreamTile*>(b + b_mats);
+  t.rtiles = reinterpret_cast<RowTile*>(b + b_mats + b_st);
+  t.qtiles = reinterpret_cast<QTile*>(b + b_mats + b_st + b_rt);
+  struct {
+    void* dst;
+    const void* src;
+    size_t bytes;
+  } copies[] = {
+      {t.mats, plan->mats.data(), plan->mats.size() * sizeof(MatInfo)},
+      {t.stiles, plan->stiles.data(), plan->stiles.size() * sizeof(StreamTile)},
+      {t.rtiles, plan->rtiles.data(), plan->rtiles.size() * sizeof(RowTile)},
+      {t.qtiles, plan->qtiles.data(), plan->qtiles.size() * sizeof(QTile)},
+  };
+  for (const auto& c : copies) {
+    if (c.bytes == 0) continue;
+    e = hipMemcpy(c.dst, c.src, c.bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      (void)hipFree(base);
+      return hip_fail("hipMemcpy of the plan's device tables", e);
+    }
+  }
+  auto ins = plan->dev.emplace(dev, t);
+  *out = &ins.first->second;
+  return PSGD_OK;
+}
+
+struct Range {
+  const char* name;
+  uintptr_t lo, hi;
+};
+
+psgd_status check_ptr(const char* fn, const char* name, const void* p, bool nullable) {
+  if (p == nullptr) {
+    if (nullable) return PSGD_OK;
+    set_error(std::string(fn) + ": " + name + " is NULL");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (reinterpret_cast<uintptr_t>(p) % 16 != 0) {
+    set_error(std::string(fn) + ": " + name + " is not 16-byte aligned");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  return PSGD_OK;
+}
+
+psgd_status take_event(psgd_plan* plan, hipEvent_t* ev) {
+  if (!plan->event_pool.empty()) {
+    *ev = plan->event_pool.back();
+    plan->event_pool.pop_back();
+    return PSGD_OK;
+  }
+  hipError_t e = hipEventCreate(ev);
+  return e == hipSuccess ? PSGD_OK : hip_fail("hipEventCreate", e);
+}
+
+// Launch through `launch()`; with timing enabled, bracket it with two events on `st`.
+template <typename F>
+psgd_status launch_timed(psgd_plan* plan, hipStream_t st, int kid, F&& launch) {
+  hipEvent_t a = nullptr, b = nullptr;
+  if (plan->timing) {
+    psgd_status s = take_event(plan, &a);
+    if (s == PSGD_OK) s = take_event(plan, &b);
+    if (s != PSGD_OK) {
+      if (a) plan->event_pool.push_back(a);
+      return s;
+    }
+    hipError_t e = hipEventRecord(a, st);
+    if (e != hipSuccess) {
+      plan->event_pool.push_back(a);
+      plan->event_pool.push_back(b);
+      return hip_fail("hipEventRecord", e);
+    }
+  }
+  launch();
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && plan->timing) e = hipEventRecord(b, st);
+  if (e != hipSuccess) {
+    if (plan->timing) {
+      plan->event_pool.push_back(a);
+      plan->event_pool.push_back(b);
+    }
+    return hip_fail((std::string("launch ") + kKernelNames[kid]).c_str(), e);
+  }
+  if (plan->timing) plan->pending.push_back(PendingTiming{kid, a, b});
+  return PSGD_OK;
+}
+
+template <int R>
+psgd_status launch_all(psgd_plan* plan, const DeviceTables& dt, const void* grads, float* errors,
+                       float* q, float* p, float* update, float* mom, float* x, float lr, float mu,
+                       char* ws, hipStream_t stream, int mode) {
+  const int W = plan->n_workers;
+  const int64_t ld = plan->worker_stride;
+  float* Mbar = reinterpret_cast<float*>(ws + plan->ws_mbar);
+  float* Pbar = reinterpret_cast<float*>(ws + plan->ws_pbar);
+  float* Qpart = reinterpret_cast<float*>(ws + plan->ws_qpart);
+  const unsigned n_st = unsigned(plan->stiles.size());
+  const unsigned n_mats = unsigned(plan->mats.size());
+  const bool bf = plan->dtype == PSGD_BF16;
+  const float inv_w = 1.0f / float(W);
+  psgd_status s;
+
+  s = launch_timed(plan, stream, kKEfMean, [&] {
+    if (bf)
+      hipLaunchKernelGGL(k_ef_mean<bf16>, dim3(n_st), dim3(kStreamThreads), 0, stream, dt.stiles,
+                         static_cast<const bf16*>(grads), errors, Mbar, W, ld, inv_w);
+    else
+      hipLaunchKernelGGL(k_ef_mean<float>, dim3(n_st), dim3(kStreamThreads), 0, stream, dt.stiles,
+                         static_cast<const float*>(grads), errors, Mbar, W, ld, inv_w);
+  });
+  if (s != PSGD_OK) return s;
+
+  if (n_mats > 0) {
+    s = launch_timed(plan, stream, kKPRows, [&] {
+      hipLaunchKernelGGL(k_p_rows<R>, dim3(unsigned(plan->rtiles.size())), dim3(kRowThreads), 0, stream,
+                         dt.rtiles, dt.mats, Mbar, q, Pbar);
+    });
+    if (s != PSGD_OK) return s;
+    s = launch_timed(plan, stream, kKMgs, [&] {
+      hipLaunchKernelGGL(k_mgs<R>, dim3(n_mats), dim3(kMgsThreads), 0, stream, dt.mats, Pbar, p);
+    });
+    if (s != PSGD_OK) return s;
+    s = launch_timed(plan, stream, kKQPartial, [&] {
+      hipLaunchKernelGGL(k_q_partial<R>, dim3(unsigned(plan->qtiles.size())), dim3(kQThreads), 0, stream,
+                         dt.qtiles, dt.mats, Mbar, p, Qpart);
+    });
+    if (s != PSGD_OK) return s;
+    const unsigned gx = unsigned((plan->max_q_elems_per_matrix + kQRedThreads - 1) / kQRedThreads);
+    s = launch_timed(plan, stream, kKQReduce, [&] {
+      hipLaunchKernelGGL(k_q_reduce, dim3(gx, n_mats), dim3(kQRedThreads), 0, stream, dt.mats, Qpart, q, R);
+    });
+    if (s != PSGD_OK) return s;
+  }
+
+#define PSGD_APPLY(GT, MODE)                                                                     \
+  hipLaunchKernelGGL((k_apply<GT, R, MODE>), dim3(n_st), dim3(kStreamThreads), 0, stream, dt.stiles, \
+                     dt.mats, static_cast<const GT*>(grads), errors, Mbar, p, q, update, mom, x, W, \
+                     ld, lr, mu)
+  s = launch_timed(plan, stream, kKApply, [&] {
+    if (bf) {
+      if (mode == kCompress) PSGD_APPLY(bf16, kCompress);
+      else if (mode == kMomentum) PSGD_APPLY(bf16, kMomentum);
+      else PSGD_APPLY(bf16, kNesterov);
+    } else {
+      if (mode == kCompress) PSGD_APPLY(float, kCompress);
+      else if (mode == kMomentum) PSGD_APPLY(float, kMomentum);
+      else PSGD_APPLY(float, kNesterov);
+    }
+  });
+#undef PSGD_APPLY
+  return s;
+}
+
+psgd_status run_step(const char* fn, psgd_plan* plan, const void* grads, float* errors, float* q,
+                     float* p, float* update, float* mom, float* x, float lr, float mu, void* workspace,
+                     void* stream, int mode) {
+  if (plan == nullptr) {
+    set_error(std::string(fn) + ": plan is NULL");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  const bool has_mats = !plan->mats.empty();
+  psgd_status s;
+  if ((s = check_ptr(fn, "grads", grads, false)) != PSGD_OK) return s;
+  if ((s = check_ptr(fn, "errors", errors, !has_mats)) != PSGD_OK) return s;
+  if ((s = check_ptr(fn, "q", q, !has_mats)) != PSGD_OK) return s;
+  if ((s = check_ptr(fn, "p", p, !has_mats)) != PSGD_OK) return s;
+  if ((s = check_ptr(fn, "update", update, true)) != PSGD_OK) return s;
+  if ((s = check_ptr(fn, "workspace", workspace, false)) != PSGD_OK) return s;
+  if (mode != kCompress) {
+    if ((s = check_ptr(fn, "momentum", mom, false)) != PSGD_OK) return s;
+    if ((s = check_ptr(fn, "params", x, false)) != PSGD_OK) return s;
+    if (!std::isfinite(lr) || !std::isfinite(mu)) {
+      set_error(std::string(fn) + ": lr and mu must be finite");
+      return PSGD_ERR_INVALID_ARG;
+    }
+  }
+  // No two buffers may overlap (errors, q, momentum, params are in/out in place).
+  const uint64_t W = uint64_t(plan->n_workers), ld = uint64_t(plan->worker_stride);
+  const uint64_t gb = plan->dtype == PSGD_BF16 ? 2 : 4;
+  Range rs[8];
+  int nr = 0;
+  auto add = [&](const char* name, const void* ptr, uint64_t bytes) {
+    if (ptr != nullptr && bytes > 0)
+      rs[nr++] = Range{name, reinterpret_cast<uintptr_t>(ptr), reinterpret_cast<uintptr_t>(ptr) + bytes};
+  };
+  add("grads", grads, W * ld * gb);
+  add("errors", has_mats ? errors : nullptr, W * ld * 4);
+  add("q", has_mats ? q : nullptr, uint64_t(plan->q_elems) * 4);
+  add("p", has_mats ? p : nullptr, uint64_t(plan->p_elems) * 4);
+  add("update", update, ld * 4);
+  add("workspace", workspace, plan->workspace_bytes);
+  if (mode != kCompress) {
+    add("momentum", mom, ld * 4);
+    add("params", x, ld * 4);
+  }
+  for (int a = 0; a < nr; ++a)
+    for (int b = a + 1; b < nr; ++b)
+      if (rs[a].lo < rs[b].hi && rs[b].lo < rs[a].hi) {
+        set_error(std::string(fn) + ": buffers " + rs[a].name + " and " + rs[b].name + " overlap");
+        return PSGD_ERR_INVALID_ARG;
+      }
+
+  DeviceTables* dt = nullptr;
+  if ((s = ensure_tables(plan, &dt)) != PSGD_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  switch (plan->rank) {
+    case 1: return launch_all<1>(plan, *dt, grads, errors, q, p, update, mom, x, lr, mu, ws, st, mode);
+    case 2: return launch_all<2>(plan, *dt, grads, errors, q, p, update, mom, x, lr, mu, ws, st, mode);
+    case 3: return launch_all<3>(plan, *dt, grads, errors, q, p, update, mom, x, lr, mu, ws, st, mode);
+    case 4: return launch_all<4>(plan, *dt, grads, errors, q, p, update, mom, x, lr, mu, ws, st, mode);
+  }
+  set_error(std::string(fn) + ": rank outside 1..4");
+  return PSGD_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+}  // namespace psgd
+
+using namespace psgd;
+
+extern "C" psgd_status psgd_compress_step(psgd_plan* plan, const void* grads, float* errors, float* q,
+                                          float* p, float* update, void* workspace, void* stream) {
+  return run_step("psgd_compress_step", plan, grads, errors, q, p, update, nullptr, nullptr, 0.f, 0.f,
+                  workspace, stream, kCompress);
+}
+
+extern "C" psgd_status psgd_ef_momentum_apply(psgd_plan* plan, const void* grads, float* errors,
+                                              float* q, float* p, float* momentum, float* params,
+                                              float lr, float mu, float* update, void* workspace,
+                                              void* stream) {
+  const int mode = (plan != nullptr && (plan->flags & PSGD_FLAG_NESTEROV)) ? kNesterov : kMomentum;
+  return run_step("psgd_ef_momentum_apply", plan, grads, errors, q, p, update, momentum, params, lr, mu,
+                  workspace, stream, mode);
+}

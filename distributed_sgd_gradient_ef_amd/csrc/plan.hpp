@@ -1,0 +1,111 @@
+// Internal host/device structures of libpsgd (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "psgd.h"
+
+namespace psgd {
+
+constexpr int64_t kAlignElems = 64;  // every tensor starts on a 256-byte boundary
+
+// Streaming passes (EF add + worker mean, and the final error/update pass): one
+// workgroup of kStreamThreads handles one tile of up to kStreamTileElems consecutive
+// elements of one tensor, as float4 chunks.
+constexpr int kStreamThreads = 256;
+constexpr int kStreamTileElems = kStreamThreads * 4 * 4;
+
+// P = Mbar Q: one workgroup of kRowThreads handles kRowsPerTile rows; one wave per row.
+constexpr int kRowThreads = 256;
+constexpr int kRowsPerTile = 16;
+
+// Q partials = Mbar^T P over a block of rows and a strip of columns.
+constexpr int kQThreads = 256;
+constexpr int kQTargetRowsPerBlock = 64;
+constexpr int kQMaxRowBlocks = 32;
+
+// Gram-Schmidt: one workgroup per matrix.
+constexpr int kMgsThreads = 1024;
+
+// Reduction of the Q partials: one thread per element of Q.
+constexpr int kQRedThreads = 256;
+
+struct MatInfo {
+  int64_t offset;     // element offset of the matrix in a worker slice / Mbar / update
+  int64_t p_off;      // element offset of P in p and in the P-bar workspace
+  int64_t q_off;      // element offset of Q in q
+  int64_t qpart_off;  // float offset of this matrix's Q partials in the workspace
+  int32_t rows, cols;
+  int32_t rows_per_blk;  // rows summed into one Q partial
+  int32_t nblk;          // number of Q partials (row blocks)
+  int32_t vec4;          // 1 if cols % 4 == 0 (rows are 16-byte aligned)
+  int32_t pad_;
+};
+
+struct StreamTile {
+  int64_t begin;  // first element (multiple of 4) inside a worker slice
+  int64_t end;    // one past the last valid element of the tensor inside this tile
+  int32_t mat;    // compressed matrix index, or -1 for an uncompressed tensor
+  int32_t pad_;
+};
+
+struct RowTile {
+  int32_t mat, row_begin, row_end, pad_;
+};
+
+struct QTile {
+  int32_t mat, blk, col_begin, col_end;
+};
+
+struct DeviceTables {
+  void* base = nullptr;
+  MatInfo* mats = nullptr;
+  StreamTile* stiles = nullptr;
+  RowTile* rtiles = nullptr;
+  QTile* qtiles = nullptr;
+};
+
+void set_error(const std::string& msg);
+
+enum KernelId { kKEfMean = 0, kKPRows, kKMgs, kKQPartial, kKQReduce, kKApply, kNumKernels };
+extern const char* const kKernelNames[kNumKernels];
+
+struct PendingTiming {
+  int kernel;
+  hipEvent_t start, stop;
+};
+
+struct KernelStat {
+  int64_t launches = 0;
+  double total_ms = 0.0;
+};
+
+}  // namespace psgd
+
+struct psgd_plan {
+  int32_t rank = 0;
+  int32_t n_workers = 0;
+  psgd_dtype dtype = PSGD_F32;
+  uint32_t flags = 0;
+  std::vector<psgd_layer_info> layers;
+  std::vector<psgd::MatInfo> mats;
+  std::vector<psgd::StreamTile> stiles;
+  std::vector<psgd::RowTile> rtiles;
+  std::vector<psgd::QTile> qtiles;
+  int64_t worker_stride = 0, numel = 0, matrix_numel = 0, vector_numel = 0;
+  int64_t p_elems = 0, q_elems = 0, qpart_elems = 0;
+  int64_t max_q_elems_per_matrix = 0;
+  uint64_t ws_mbar = 0, ws_pbar = 0, ws_qpart = 0, workspace_bytes = 0;
+  uint64_t message_bytes = 0, model_bytes = 0, model_bytes_momentum = 0;
+  std::map<int, psgd::DeviceTables> dev;  // per HIP device id
+  // kernel timing (psgd_plan_set_timing)
+  bool timing = false;
+  std::vector<psgd::PendingTiming> pending;
+  std::vector<hipEvent_t> event_pool;
+  psgd::KernelStat stats[psgd::kNumKernels];
+};

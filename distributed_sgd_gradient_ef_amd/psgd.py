@@ -1,0 +1,266 @@
+"""Thin ctypes binding of libpsgd (C ABI declared in include/psgd.h).
+
+Functions carry the C names.  The step functions take torch tensors on a ROCm device
+and pass their device pointers and the current HIP stream; every step of the
+computation runs in the library's HIP kernels.  Nothing here computes: if the library
+is missing the import of a step function fails loudly.
+
+Besides the C calls there are two layout helpers, ``pack`` and ``unpack``, which move
+per-tensor arrays into and out of the plan's packed [workers][worker_stride] layout.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpsgd.so")
+
+PSGD_OK = 0
+PSGD_ERR_INVALID_ARG = 1
+PSGD_ERR_UNSUPPORTED = 2
+PSGD_ERR_NO_MEMORY = 3
+PSGD_ERR_HIP = 4
+PSGD_F32 = 0
+PSGD_BF16 = 1
+PSGD_FLAG_NESTEROV = 0x1
+
+EXPORTED = [
+    "psgd_plan_create", "psgd_plan_sizes", "psgd_plan_layer_info", "psgd_plan_destroy",
+    "psgd_compress_step", "psgd_ef_momentum_apply", "psgd_plan_set_timing",
+    "psgd_plan_kernel_stats", "psgd_status_string", "psgd_last_error",
+]
+
+
+class PsgdError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+class _Layer(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+class _LayerInfo(ctypes.Structure):
+    _fields_ = [("compressed", ctypes.c_int32), ("matrix_index", ctypes.c_int32),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("offset", ctypes.c_int64),
+                ("p_offset", ctypes.c_int64), ("q_offset", ctypes.c_int64)]
+
+
+class _KernelStat(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
+
+
+class _Sizes(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("n_matrices", ctypes.c_int32),
+                ("n_vectors", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("n_workers", ctypes.c_int32), ("grad_dtype", ctypes.c_int32),
+                ("worker_stride", ctypes.c_int64), ("numel", ctypes.c_int64),
+                ("matrix_numel", ctypes.c_int64), ("vector_numel", ctypes.c_int64),
+                ("p_elems", ctypes.c_int64), ("q_elems", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_uint64), ("message_bytes", ctypes.c_uint64),
+                ("model_bytes", ctypes.c_uint64), ("model_bytes_momentum", ctypes.c_uint64)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libpsgd.so (once).  Import torch first so the HIP runtime it carries is the
+    one the library binds to (both use the soname libamdhip64.so.7)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m distributed_sgd_gradient_ef_amd.build`")
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    lib.psgd_plan_create.argtypes = [ctypes.POINTER(_Layer), i32, i32, i32, i32, ctypes.c_uint32,
+                                     ctypes.POINTER(vp)]
+    lib.psgd_plan_sizes.argtypes = [vp, ctypes.POINTER(_Sizes)]
+    lib.psgd_plan_layer_info.argtypes = [vp, i32, ctypes.POINTER(_LayerInfo)]
+    lib.psgd_plan_destroy.argtypes = [vp]
+    lib.psgd_compress_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.psgd_ef_momentum_apply.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, f32, vp, vp, vp]
+    lib.psgd_plan_set_timing.argtypes = [vp, i32]
+    lib.psgd_plan_kernel_stats.argtypes = [vp, ctypes.POINTER(_KernelStat), i32, ctypes.POINTER(i32), i32]
+    for name in EXPORTED[:8]:
+        getattr(lib, name).restype = ctypes.c_int
+    lib.psgd_status_string.argtypes = [ctypes.c_int]
+    lib.psgd_status_string.restype = ctypes.c_char_p
+    lib.psgd_last_error.argtypes = []
+    lib.psgd_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != PSGD_OK:
+        lib = load_library()
+        raise PsgdError(status, lib.psgd_last_error().decode() or lib.psgd_status_string(status).decode())
+
+
+@dataclass
+class LayerInfo:
+    compressed: bool
+    matrix_index: int
+    rows: int
+    cols: int
+    offset: int
+    p_offset: int
+    q_offset: int
+
+
+class Plan:
+    """Owns a psgd_plan*; freed by psgd_plan_destroy (or when garbage collected)."""
+
+    def __init__(self, handle: int, shapes: Sequence[Tuple[int, int]]):
+        self.handle = handle
+        self.shapes = [tuple(int(v) for v in s) for s in shapes]
+        self.sizes = psgd_plan_sizes(self)
+        self.layers: List[LayerInfo] = [psgd_plan_layer_info(self, i) for i in range(len(shapes))]
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            try:
+                psgd_plan_destroy(self)
+            except Exception:
+                pass
+
+
+# ------------------------------------------------------------------------ C calls
+def psgd_plan_create(shapes: Sequence[Tuple[int, int]], rank: int, n_workers: int,
+                     grad_dtype: int = PSGD_F32, flags: int = 0) -> Plan:
+    lib = load_library()
+    arr = (_Layer * max(1, len(shapes)))(*[_Layer(int(r), int(c)) for r, c in shapes])
+    h = ctypes.c_void_p()
+    _check(lib.psgd_plan_create(arr, len(shapes), int(rank), int(n_workers), int(grad_dtype),
+                                int(flags), ctypes.byref(h)))
+    return Plan(h.value, shapes)
+
+
+def psgd_plan_sizes(plan: Plan) -> dict:
+    s = _Sizes()
+    _check(load_library().psgd_plan_sizes(plan.handle, ctypes.byref(s)))
+    return {name: getattr(s, name) for name, _ in _Sizes._fields_}
+
+
+def psgd_plan_layer_info(plan: Plan, layer: int) -> LayerInfo:
+    li = _LayerInfo()
+    _check(load_library().psgd_plan_layer_info(plan.handle, int(layer), ctypes.byref(li)))
+    return LayerInfo(bool(li.compressed), li.matrix_index, li.rows, li.cols, li.offset, li.p_offset,
+                     li.q_offset)
+
+
+def psgd_plan_destroy(plan: Plan) -> None:
+    h, plan.handle = plan.handle, None
+    if h:
+        _check(load_library().psgd_plan_destroy(h))
+
+
+def psgd_plan_set_timing(plan: Plan, enable: bool) -> None:
+    _check(load_library().psgd_plan_set_timing(plan.handle, 1 if enable else 0))
+
+
+def psgd_plan_kernel_stats(plan: Plan, reset: bool = False) -> dict:
+    """{kernel name: (launches, total_ms)}; waits for every timed launch so far."""
+    arr = (_KernelStat * 16)()
+    n = ctypes.c_int32()
+    _check(load_library().psgd_plan_kernel_stats(plan.handle, arr, 16, ctypes.byref(n), 1 if reset else 0))
+    return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(n.value)}
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def _stream(stream, ref):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(ref.device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream or 0)
+
+
+def psgd_compress_step(plan: Plan, grads, errors, q, p, update, workspace, stream=None) -> None:
+    """Enqueue one compression step (tensors on a ROCm device; see include/psgd.h)."""
+    import torch
+
+    with torch.cuda.device(grads.device):
+        _check(load_library().psgd_compress_step(
+            plan.handle, _ptr(grads), _ptr(errors), _ptr(q), _ptr(p), _ptr(update), _ptr(workspace),
+            _stream(stream, grads)))
+
+
+def psgd_ef_momentum_apply(plan: Plan, grads, errors, q, p, momentum, params, lr: float, mu: float,
+                           update, workspace, stream=None) -> None:
+    """Enqueue one compression step fused with the momentum-SGD update."""
+    import torch
+
+    with torch.cuda.device(grads.device):
+        _check(load_library().psgd_ef_momentum_apply(
+            plan.handle, _ptr(grads), _ptr(errors), _ptr(q), _ptr(p), _ptr(momentum), _ptr(params),
+            float(lr), float(mu), _ptr(update), _ptr(workspace), _stream(stream, grads)))
+
+
+# ------------------------------------------------------------------------ layout helpers
+def pack(plan: Plan, per_layer: Sequence[np.ndarray], dtype=np.float32, workers: Optional[int] = None,
+         layers: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Place per-tensor arrays into the packed layout.
+
+    per_layer[i] has shape (W, rows, cols) (or (rows, cols) when ``workers`` is 0, for
+    update/momentum/params).  Returns (W, worker_stride) or (worker_stride,); padding is 0.
+    """
+    ld = plan.sizes["worker_stride"]
+    W = plan.sizes["n_workers"] if workers is None else workers
+    out = np.zeros((W, ld) if W else (ld,), dtype=dtype)
+    idx = range(len(plan.layers)) if layers is None else layers
+    for a, li in zip(per_layer, idx):
+        L = plan.layers[li]
+        n = L.rows * L.cols
+        if W:
+            out[:, L.offset:L.offset + n] = np.asarray(a).reshape(W, n)
+        else:
+            out[L.offset:L.offset + n] = np.asarray(a).reshape(n)
+    return out
+
+
+def unpack(plan: Plan, flat: np.ndarray, layer: int) -> np.ndarray:
+    """Inverse of ``pack`` for one tensor: (W, rows, cols) or (rows, cols)."""
+    L = plan.layers[layer]
+    n = L.rows * L.cols
+    if flat.ndim == 2:
+        return flat[:, L.offset:L.offset + n].reshape(flat.shape[0], L.rows, L.cols)
+    return flat[L.offset:L.offset + n].reshape(L.rows, L.cols)
+
+
+def factor_slice(plan: Plan, flat: np.ndarray, layer: int, which: str) -> np.ndarray:
+    """P (rows x rank) or Q (cols x rank) of one compressed matrix from the flat p or q."""
+    L = plan.layers[layer]
+    r = plan.sizes["rank"]
+    if which == "p":
+        return flat[L.p_offset:L.p_offset + L.rows * r].reshape(L.rows, r)
+    return flat[L.q_offset:L.q_offset + L.cols * r].reshape(L.cols, r)
+
+
+def pack_factors(plan: Plan, per_matrix: dict, which: str) -> np.ndarray:
+    """Concatenate per-layer P or Q arrays ({layer: array}) into the flat p or q buffer."""
+    r = plan.sizes["rank"]
+    n = plan.sizes["p_elems" if which == "p" else "q_elems"]
+    out = np.zeros(n, dtype=np.float32)
+    for li, a in per_matrix.items():
+        L = plan.layers[li]
+        off = L.p_offset if which == "p" else L.q_offset
+        k = (L.rows if which == "p" else L.cols) * r
+        out[off:off + k] = np.asarray(a, dtype=np.float32).reshape(k)
+    return out

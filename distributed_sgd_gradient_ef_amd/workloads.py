@@ -17,6 +17,7 @@ with a planted low-rank part plus worker noise, as described per workload below.
 
 from __future__ import annotations
 
+import functools
 import math
 from dataclasses import dataclass, field
 from typing import List, Optional, Sequence, Tuple
@@ -193,11 +194,13 @@ def _spectrum(signal: str, n: int, m: int) -> np.ndarray:
     raise ValueError(signal)
 
 
+@functools.lru_cache(maxsize=4096)
 def planted(wl: Workload, layer: int, step: int = 0) -> Optional[Planted]:
     """Planted low-rank part of matrix ``layer`` at ``step`` (None for tensors without one).
 
     With ``drift_rad`` > 0 the subspaces turn by exactly that angle per step (see
-    ``_drift``); step 0 is the undrifted draw.
+    ``_drift``); step 0 is the undrifted draw.  Results are cached, so walking the steps
+    in order costs one rotation per step.
     """
     name, (n, m) = wl.shapes[layer]
     if not is_matrix((n, m), wl.rank):
@@ -206,12 +209,13 @@ def planted(wl: Workload, layer: int, step: int = 0) -> Optional[Planted]:
         return None  # sparse rows instead of a planted part
     s = _spectrum(wl.signal, n, m)
     k = len(s)
-    u = haar_orthonormal(stream(wl.seed, _P_FACTOR_U, 0, 0, layer), n, k)
-    v = haar_orthonormal(stream(wl.seed, _P_FACTOR_V, 0, 0, layer), m, k)
-    for t in range(1, step + 1):
-        if wl.drift_rad:
-            u = _drift(u, wl.drift_rad, stream(wl.seed, _P_DRIFT, t, 0, 2 * layer))
-            v = _drift(v, wl.drift_rad, stream(wl.seed, _P_DRIFT, t, 0, 2 * layer + 1))
+    if step == 0 or not wl.drift_rad:
+        u = haar_orthonormal(stream(wl.seed, _P_FACTOR_U, 0, 0, layer), n, k)
+        v = haar_orthonormal(stream(wl.seed, _P_FACTOR_V, 0, 0, layer), m, k)
+        return Planted(u, v, s)
+    prev = planted(wl, layer, step - 1)
+    u = _drift(prev.u, wl.drift_rad, stream(wl.seed, _P_DRIFT, step, 0, 2 * layer))
+    v = _drift(prev.v, wl.drift_rad, stream(wl.seed, _P_DRIFT, step, 0, 2 * layer + 1))
     return Planted(u, v, s)
 
 
@@ -310,3 +314,55 @@ def to_bf16_values(a: np.ndarray) -> np.ndarray:
 def bf16_bits(a_bf16_values: np.ndarray) -> np.ndarray:
     """Upper 16 bits of float32 values that are already bfloat16-representable."""
     return (np.ascontiguousarray(a_bf16_values, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+# --------------------------------------------------------------------------- on device
+def device_grads(wl: Workload, step: int, layers, out, low_rank_cache: Optional[dict] = None) -> None:
+    """Fill ``out`` (a torch float32 tensor [W, worker_stride] on a ROCm device) with the
+    gradients of ``step``, drawn on the device for workloads too large to draw on the
+    host.  ``layers`` lists (offset, rows, cols) per tensor in the packed layout.
+
+    Same recipe as ``grad_layer`` (planted part from the host, noise drawn with torch's
+    seeded device generator), but not the same bits: tests feed the CPU oracle with the
+    values read back from ``out``.
+    """
+    import torch
+
+    dev = out.device
+    W = out.shape[0]
+    sig = wl.signal
+    for li, (off, n, m) in enumerate(layers):
+        numel = n * m
+        lr = None
+        if is_matrix((n, m), wl.rank):
+            p = planted(wl, li, step)
+            if p is not None:
+                key = (li, step)
+                if low_rank_cache is not None and key in low_rank_cache:
+                    lr = low_rank_cache[key]
+                else:
+                    lr = torch.from_numpy(p.dense().reshape(-1)).to(dev)
+                    if low_rank_cache is not None and not wl.drift_rad:
+                        low_rank_cache[key] = lr
+        for w in range(W):
+            g = torch.Generator(device=dev)
+            g.manual_seed(int(np.random.SeedSequence([wl.seed, _P_NOISE, step, w, li]).generate_state(1)[0]))
+            dst = out[w, off:off + numel]
+            if sig == "lstm" and lr is None and is_matrix((n, m), wl.rank):
+                dst.zero_()
+                k = int(round(0.05 * n))
+                rows = torch.randperm(n, generator=g, device=dev)[:k]
+                vals = torch.randn((k, m), generator=g, device=dev)
+                dst.view(n, m)[rows] = vals
+                continue
+            if sig == "stress" and is_matrix((n, m), wl.rank):
+                z = torch.randn(numel, generator=g, device=dev)
+                chi = torch.randn((3, numel), generator=g, device=dev).square_().sum(dim=0)
+                dst.copy_(z / torch.sqrt(chi / 3.0))
+                del z, chi
+            else:
+                scale = {"single": 0.01, "resnet": 0.05, "lstm": 0.01, "stress": 1.0}[sig]
+                torch.randn(numel, generator=g, device=dev, out=dst)
+                dst.mul_(scale)
+            if lr is not None:
+                dst.add_(lr)

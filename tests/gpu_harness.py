@@ -1,0 +1,181 @@
+"""Helpers shared by the GPU tests and the smoke check: device buffers for a plan, the
+C-ABI step calls, read-back of every output, and the parity metric.
+
+The metric: rel(a, o) = ||a - o||_F / ||o||_F in float64, per matrix for P, Q and U and
+per matrix per worker for E'.  When ||o||_F is below 1e-6 ||Mbar||_F (an output that is
+zero up to rounding, e.g. the error of an exactly low-rank matrix) the denominator is
+||Mbar||_F instead.
+"""
+
+from __future__ import annotations
+
+import sys
+from dataclasses import dataclass
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+from distributed_sgd_gradient_ef_amd import psgd
+from distributed_sgd_gradient_ef_amd import workloads as WL
+
+
+def log(*args):
+    print(*args, flush=True)
+    sys.stdout.flush()
+
+
+def rel(a, o, scale: float) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    den = np.linalg.norm(o)
+    if den < 1e-6 * scale:
+        den = scale
+    if den == 0.0:
+        return float(np.linalg.norm(a - o))
+    return float(np.linalg.norm(a - o) / den)
+
+
+class DeviceRun:
+    """Device buffers of one plan, in the packed layout, and the step calls."""
+
+    def __init__(self, shapes, rank, workers, device="cuda:0", bf16=False, flags=0, momentum=False):
+        import torch
+
+        self.torch = torch
+        self.dev = torch.device(device)
+        self.bf16 = bf16
+        self.plan = psgd.psgd_plan_create(shapes, rank, workers,
+                                          psgd.PSGD_BF16 if bf16 else psgd.PSGD_F32, flags)
+        s = self.plan.sizes
+        self.W, self.ld, self.r = workers, s["worker_stride"], rank
+        gdt = torch.bfloat16 if bf16 else torch.float32
+        self.grads = torch.zeros((self.W, self.ld), dtype=gdt, device=self.dev)
+        self.errors = torch.zeros((self.W, self.ld), dtype=torch.float32, device=self.dev)
+        self.q = torch.zeros(max(1, s["q_elems"]), dtype=torch.float32, device=self.dev)
+        self.p = torch.zeros(max(1, s["p_elems"]), dtype=torch.float32, device=self.dev)
+        self.update = torch.zeros(self.ld, dtype=torch.float32, device=self.dev)
+        self.workspace = torch.empty(s["workspace_bytes"], dtype=torch.uint8, device=self.dev)
+        self.momentum = self.params = None
+        if momentum:
+            self.momentum = torch.zeros(self.ld, dtype=torch.float32, device=self.dev)
+            self.params = torch.zeros(self.ld, dtype=torch.float32, device=self.dev)
+
+    # -- inputs
+    def set_grads_host(self, per_layer: Sequence[np.ndarray]) -> None:
+        flat = psgd.pack(self.plan, per_layer)
+        t = self.torch.from_numpy(flat)
+        if self.bf16:
+            t = t.to(self.torch.bfloat16)
+        self.grads.copy_(t.to(self.dev))
+
+    def set_q_host(self, per_matrix: Dict[int, np.ndarray]) -> None:
+        q = psgd.pack_factors(self.plan, per_matrix, "q")
+        self.q[: q.size].copy_(self.torch.from_numpy(q).to(self.dev))
+
+    def set_errors_host(self, per_layer: Sequence[np.ndarray]) -> None:
+        self.errors.copy_(self.torch.from_numpy(psgd.pack(self.plan, per_layer)).to(self.dev))
+
+    def set_params_host(self, per_layer: Sequence[np.ndarray]) -> None:
+        self.params.copy_(self.torch.from_numpy(psgd.pack(self.plan, per_layer, workers=0)).to(self.dev))
+
+    # -- steps (through the C ABI)
+    def compress(self, update=True, stream=None) -> None:
+        psgd.psgd_compress_step(self.plan, self.grads, self.errors, self.q, self.p,
+                                self.update if update else None, self.workspace, stream)
+
+    def momentum_step(self, lr, mu, update=True, stream=None) -> None:
+        psgd.psgd_ef_momentum_apply(self.plan, self.grads, self.errors, self.q, self.p, self.momentum,
+                                    self.params, lr, mu, self.update if update else None,
+                                    self.workspace, stream)
+
+    # -- outputs
+    def host(self, t) -> np.ndarray:
+        self.torch.cuda.synchronize(self.dev)
+        return t.float().cpu().numpy() if t.dtype != self.torch.float32 else t.cpu().numpy()
+
+    def layer(self, flat: np.ndarray, li: int) -> np.ndarray:
+        return psgd.unpack(self.plan, flat, li)
+
+    def factor(self, flat: np.ndarray, li: int, which: str) -> np.ndarray:
+        return psgd.factor_slice(self.plan, flat, li, which)
+
+    def grads_layer(self, li: int) -> np.ndarray:
+        L = self.plan.layers[li]
+        n = L.rows * L.cols
+        return self.grads[:, L.offset:L.offset + n].float().cpu().numpy().reshape(self.W, L.rows, L.cols)
+
+    def errors_layer(self, li: int) -> np.ndarray:
+        L = self.plan.layers[li]
+        n = L.rows * L.cols
+        return self.errors[:, L.offset:L.offset + n].cpu().numpy().reshape(self.W, L.rows, L.cols)
+
+    def vec_layer(self, t, li: int) -> np.ndarray:
+        L = self.plan.layers[li]
+        n = L.rows * L.cols
+        return t[L.offset:L.offset + n].cpu().numpy().reshape(L.rows, L.cols)
+
+    def q_layer(self, li: int) -> np.ndarray:
+        L = self.plan.layers[li]
+        return self.q[L.q_offset:L.q_offset + L.cols * self.r].cpu().numpy().reshape(L.cols, self.r)
+
+    def p_layer(self, li: int) -> np.ndarray:
+        L = self.plan.layers[li]
+        return self.p[L.p_offset:L.p_offset + L.rows * self.r].cpu().numpy().reshape(L.rows, self.r)
+
+
+@dataclass
+class LayerSnapshot:
+    """GPU state of one tensor before a step, read back for the oracle."""
+
+    g: np.ndarray
+    e: np.ndarray
+    q: Optional[np.ndarray]
+
+
+def snapshot(run: DeviceRun, layers: Sequence[int]) -> Dict[int, LayerSnapshot]:
+    run.torch.cuda.synchronize(run.dev)
+    out = {}
+    for li in layers:
+        L = run.plan.layers[li]
+        g = run.grads_layer(li)
+        e = run.errors_layer(li) if L.compressed else np.zeros_like(g)
+        out[li] = LayerSnapshot(g, e, run.q_layer(li) if L.compressed else None)
+    return out
+
+
+def compare_step(run: DeviceRun, snap: Dict[int, LayerSnapshot], oracle_mod, tol: float,
+                 check_p: bool = True, what: str = "") -> Dict[str, float]:
+    """Run the oracle on the snapshot and compare with the GPU outputs of the step that
+    followed it.  Returns the worst relative error per output kind; asserts <= tol."""
+    run.torch.cuda.synchronize(run.dev)
+    upd = run.update.cpu().numpy()
+    worst = {"p": 0.0, "q": 0.0, "u": 0.0, "e": 0.0, "v": 0.0}
+    for li, s in snap.items():
+        L = run.plan.layers[li]
+        if not L.compressed:
+            ref = oracle_mod.average_tensor(s.g)
+            err = rel(psgd.unpack(run.plan, upd, li), ref, np.linalg.norm(ref) + 1e-30)
+            worst["v"] = max(worst["v"], err)
+            assert err <= tol, f"{what} layer {li} mean: rel {err:.3e}"
+            continue
+        ref = oracle_mod.compress_matrix(s.g, s.e, s.q)
+        mbar = np.linalg.norm((s.g.astype(np.float64) + s.e).mean(axis=0))
+        errs = {
+            "p": rel(run.p_layer(li), ref.p_hat, 1.0) if check_p else 0.0,
+            "q": rel(run.q_layer(li), ref.q_bar, mbar),
+            "u": rel(psgd.unpack(run.plan, upd, li), ref.update, mbar),
+        }
+        e_gpu = run.errors_layer(li)
+        errs["e"] = max(rel(e_gpu[w], ref.errors[w], mbar) for w in range(run.W))
+        for k, v in errs.items():
+            worst[k] = max(worst[k], v)
+            assert v <= tol, f"{what} layer {li} ({L.rows}x{L.cols}) {k}: rel {v:.3e} > {tol}"
+    return worst
+
+
+def host_inputs(wl: WL.Workload, step: int) -> List[np.ndarray]:
+    return WL.grads(wl, step)
+
+
+def device_layers(run: DeviceRun):
+    return [(L.offset, L.rows, L.cols) for L in run.plan.layers]

@@ -1,0 +1,170 @@
+"""The C ABI without a GPU: the library loads, exports every function include/psgd.h
+declares, validates its arguments before touching the device, and its plan reproduces
+the layout and byte accounting the workloads need."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from distributed_sgd_gradient_ef_amd import psgd
+from distributed_sgd_gradient_ef_amd import workloads as WL
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "psgd.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(psgd.LIB_PATH), reason="libpsgd.so not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(psgd_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = psgd.load_library()
+    names = _declared()
+    assert set(names) == set(psgd.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = psgd.load_library()
+    for code in range(5):
+        assert lib.psgd_status_string(code)
+    assert lib.psgd_status_string(99) == b"unknown status"
+
+
+def _create(shapes, rank=2, workers=4, dtype=psgd.PSGD_F32, flags=0):
+    lib = psgd.load_library()
+    arr = (psgd._Layer * max(1, len(shapes)))(*[psgd._Layer(r, c) for r, c in shapes])
+    h = ctypes.c_void_p()
+    st = lib.psgd_plan_create(arr if shapes else None, len(shapes), rank, workers, dtype, flags, ctypes.byref(h))
+    if st == 0:
+        lib.psgd_plan_destroy(h)
+    return st
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(rank=0), psgd.PSGD_ERR_UNSUPPORTED),
+    (dict(rank=5), psgd.PSGD_ERR_UNSUPPORTED),
+    (dict(workers=0), psgd.PSGD_ERR_INVALID_ARG),
+    (dict(workers=70000), psgd.PSGD_ERR_INVALID_ARG),
+    (dict(dtype=7), psgd.PSGD_ERR_UNSUPPORTED),
+    (dict(flags=0x80), psgd.PSGD_ERR_UNSUPPORTED),
+    (dict(), psgd.PSGD_OK),
+])
+def test_plan_create_validation(kw, expect):
+    assert _create([(64, 27), (1, 10)], **kw) == expect
+
+
+@pytest.mark.parametrize("shapes", [[(0, 5)], [(5, -1)], [(1 << 16, 1 << 15)], []])
+def test_plan_create_bad_shapes(shapes):
+    assert _create(shapes) == psgd.PSGD_ERR_INVALID_ARG
+    assert psgd.load_library().psgd_last_error()
+
+
+def test_plan_null_out():
+    lib = psgd.load_library()
+    arr = (psgd._Layer * 1)(psgd._Layer(4, 4))
+    assert lib.psgd_plan_create(arr, 1, 1, 1, 0, 0, None) == psgd.PSGD_ERR_INVALID_ARG
+    assert lib.psgd_plan_sizes(None, None) == psgd.PSGD_ERR_INVALID_ARG
+    assert lib.psgd_plan_destroy(None) == psgd.PSGD_OK
+
+
+def test_layout_offsets_aligned_and_disjoint():
+    shapes = [s for _, s in WL.resnet18_cifar_shapes()]
+    plan = psgd.psgd_plan_create(shapes, 2, 16)
+    prev_end = 0
+    p_next = q_next = 0
+    for li, (r, c) in zip(plan.layers, shapes):
+        assert li.offset % 64 == 0 and li.offset >= prev_end
+        assert (li.rows, li.cols) == (r, c)
+        prev_end = li.offset + r * c
+        assert li.compressed == WL.is_matrix((r, c), 2)
+        if li.compressed:
+            assert li.p_offset == p_next and li.q_offset == q_next
+            p_next += r * 2
+            q_next += c * 2
+        else:
+            assert li.p_offset == -1 and li.matrix_index == -1
+    s = plan.sizes
+    assert s["worker_stride"] >= prev_end and s["worker_stride"] % 64 == 0
+    assert s["p_elems"] == p_next == 2 * 4810 and s["q_elems"] == q_next == 2 * 31515
+    with pytest.raises(psgd.PsgdError):
+        psgd.psgd_plan_layer_info(plan, len(shapes))
+
+
+@pytest.mark.parametrize("rank,mib", [(1, 4), (2, 8), (4, 14)])
+def test_plan_message_bytes_match_results_table(rank, mib):
+    """The plan's per-worker message bytes x 24 steps/epoch give the page's MB column."""
+    shapes = [s for _, s in WL.resnet18_cifar_shapes()]
+    s = psgd.psgd_plan_create(shapes, rank, 16).sizes
+    assert s["numel"] == 11_173_962
+    assert round(24 * s["message_bytes"] / 2 ** 20) == mib
+
+
+@pytest.mark.parametrize("dtype,gb", [(psgd.PSGD_F32, 4), (psgd.PSGD_BF16, 2)])
+def test_plan_model_bytes(dtype, gb):
+    shapes = [s for _, s in WL.resnet18_cifar_shapes()]
+    W = 16
+    s = psgd.psgd_plan_create(shapes, 2, W, grad_dtype=dtype).sizes
+    mn, vn = 11_164_352, 9_610
+    assert s["matrix_numel"] == mn and s["vector_numel"] == vn
+    assert s["model_bytes"] == (W * (gb + 8) + 4) * mn + (W * gb + 4) * vn
+    assert s["model_bytes_momentum"] == (W * (gb + 8) + 16) * mn + (W * gb + 16) * vn
+    if dtype == psgd.PSGD_F32:
+        assert abs(s["model_bytes"] / 1e9 - 2.189) < 0.001
+
+
+def test_rank_at_least_min_side_is_uncompressed():
+    plan = psgd.psgd_plan_create([(3, 100), (5, 4), (8, 8)], 4, 2)
+    assert [l.compressed for l in plan.layers] == [False, False, True]
+
+
+def _step(plan_handle, **ptrs):
+    lib = psgd.load_library()
+    a = dict(grads=0x10000, errors=0x20000000, q=0x30000000, p=0x40000000, update=0x50000000,
+             workspace=0x60000000)
+    a.update(ptrs)
+    return lib.psgd_compress_step(plan_handle, a["grads"], a["errors"], a["q"], a["p"], a["update"],
+                                  a["workspace"], None)
+
+
+@pytest.mark.parametrize("bad", [dict(grads=None), dict(errors=None), dict(q=None), dict(p=None),
+                                 dict(workspace=None), dict(grads=0x10004), dict(q=0x30000008),
+                                 dict(update=0x10010)])
+def test_step_rejects_bad_pointers_before_any_device_call(bad):
+    """Null, misaligned or overlapping buffers fail synchronously; nothing is enqueued
+    (the fake addresses are never dereferenced)."""
+    plan = psgd.psgd_plan_create([(64, 64), (1, 10)], 2, 2)
+    assert _step(plan.handle, **bad) == psgd.PSGD_ERR_INVALID_ARG
+    assert psgd.load_library().psgd_last_error()
+    assert _step(None) == psgd.PSGD_ERR_INVALID_ARG
+
+
+def test_momentum_rejects_non_finite_lr():
+    lib = psgd.load_library()
+    plan = psgd.psgd_plan_create([(64, 64)], 2, 2)
+    st = lib.psgd_ef_momentum_apply(plan.handle, 0x10000, 0x20000000, 0x30000000, 0x40000000,
+                                    0x70000000, 0x80000000, float("nan"), 0.9, None, 0x60000000, None)
+    assert st == psgd.PSGD_ERR_INVALID_ARG
+
+
+def test_pack_unpack_roundtrip():
+    shapes = [(6, 5), (1, 3), (4, 7)]
+    plan = psgd.psgd_plan_create(shapes, 2, 3)
+    rng = np.random.default_rng(0)
+    arrs = [rng.standard_normal((3,) + s).astype(np.float32) for s in shapes]
+    flat = psgd.pack(plan, arrs)
+    assert flat.shape == (3, plan.sizes["worker_stride"])
+    for i, a in enumerate(arrs):
+        assert np.array_equal(psgd.unpack(plan, flat, i), a)
+    qs = {0: rng.standard_normal((5, 2)), 2: rng.standard_normal((7, 2))}
+    qflat = psgd.pack_factors(plan, qs, "q")
+    for li, a in qs.items():
+        assert np.allclose(psgd.factor_slice(plan, qflat, li, "q"), a)
