@@ -33,21 +33,22 @@ KERNEL_SRC = os.path.join(ROOT, "distributed_sgd_gradient_ef_amd", "csrc", "kern
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_resnet18_r2_w16.json")
 
 
-def kernel_bytes(plan, dtype_bytes: int) -> dict:
+def kernel_bytes(plan, dtype_bytes: int, carry: bool) -> dict:
     """Algorithmic HBM bytes per launch of each kernel for this plan."""
     s = plan.sizes
-    W, r = s["n_workers"], s["rank"]
+    W = s["n_workers"]
     mn, vn = s["matrix_numel"], s["vector_numel"]
     gb = dtype_bytes
     return {
-        # read G_w, E_w on every worker, write the mean once; tensors without error: G only
-        "k_ef_mean": (W * (gb + 4) + 4) * mn + (W * gb + 4) * vn,
+        # read G_w (and E_w, or the carried error mean once) on every worker, write the
+        # mean once; tensors without error: G only
+        "k_ef_mean": ((W * gb + 8) if carry else (W * (gb + 4) + 4)) * mn + (W * gb + 4) * vn,
         # read Mbar once (Q, P are cache-resident)
         "k_p_rows": 4 * mn + 4 * s["p_elems"],
         "k_q_partial": 4 * mn,
-        # read G_w, E_w and write E'_w on every worker, write U once; tensors without
-        # error: read the mean, write the update
-        "k_apply": (W * (gb + 8) + 4) * mn + 8 * vn,
+        # read G_w, E_w and write E'_w on every worker, write U once (and the new error
+        # mean in carry mode); tensors without error: read the mean, write the update
+        "k_apply": (W * (gb + 8) + (8 if carry else 4)) * mn + 8 * vn,
     }
 
 
@@ -102,6 +103,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline sample length")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=["both", "carry", "plain"], default="both",
+                    help="plan variants to time (profiling runs use one)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -121,71 +124,75 @@ def main() -> int:
     dev = torch.device("cuda:0")
     wl = WL.workload("resnet18")
     shapes = [s for _, s in wl.shapes]
-    plan = psgd.psgd_plan_create(shapes, wl.rank, wl.workers)
-    s = plan.sizes
-    W, ld = wl.workers, s["worker_stride"]
-    grads = torch.zeros((W, ld), dtype=torch.float32, device=dev)
-    errors = torch.zeros((W, ld), dtype=torch.float32, device=dev)
-    q = torch.zeros(s["q_elems"], dtype=torch.float32, device=dev)
-    p = torch.zeros(s["p_elems"], dtype=torch.float32, device=dev)
-    update = torch.zeros(ld, dtype=torch.float32, device=dev)
-    workspace = torch.empty(s["workspace_bytes"], dtype=torch.uint8, device=dev)
-    WL.device_grads(wl, 0, [(L.offset, L.rows, L.cols) for L in plan.layers], grads)
-    qh = psgd.pack_factors(plan, {i: WL.q0(wl, i) for i, L in enumerate(plan.layers) if L.compressed}, "q")
-    q.copy_(torch.from_numpy(qh).to(dev))
-    stream = torch.cuda.current_stream(dev)
+    W = wl.workers
 
-    def step():
-        psgd.psgd_compress_step(plan, grads, errors, q, p, update, workspace, stream)
+    def measure(flags: int) -> dict:
+        plan = psgd.psgd_plan_create(shapes, wl.rank, W, psgd.PSGD_F32, flags)
+        s = plan.sizes
+        ld = s["worker_stride"]
+        grads = torch.zeros((W, ld), dtype=torch.float32, device=dev)
+        errors = torch.zeros((W, ld), dtype=torch.float32, device=dev)
+        q = torch.zeros(s["q_elems"], dtype=torch.float32, device=dev)
+        p = torch.zeros(s["p_elems"], dtype=torch.float32, device=dev)
+        update = torch.zeros(ld, dtype=torch.float32, device=dev)
+        workspace = torch.empty(s["workspace_bytes"], dtype=torch.uint8, device=dev)
+        WL.device_grads(wl, 0, [(L.offset, L.rows, L.cols) for L in plan.layers], grads)
+        qh = psgd.pack_factors(plan, {i: WL.q0(wl, i) for i, L in enumerate(plan.layers) if L.compressed}, "q")
+        q.copy_(torch.from_numpy(qh).to(dev))
+        stream = torch.cuda.current_stream(dev)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize(dev)
+        def step():
+            psgd.psgd_compress_step(plan, grads, errors, q, p, update, workspace, stream)
 
-    # timed region 1: the step as a caller runs it
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize(dev)
-    wall0 = time.perf_counter()
-    t0.record(stream)
-    for _ in range(args.steps):
-        step()
-    t1.record(stream)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - wall0
-    ms = t0.elapsed_time(t1) / args.steps
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize(dev)
+        # timed region 1: the step as a caller runs it
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(args.steps):
+            step()
+        t1.record(stream)
+        torch.cuda.synchronize(dev)
+        ms = t0.elapsed_time(t1) / args.steps
+        # timed region 2: the same steps with every kernel bracketed by HIP events
+        psgd.psgd_plan_set_timing(plan, True)
+        psgd.psgd_plan_kernel_stats(plan, reset=True)
+        t2, t3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t2.record(stream)
+        for _ in range(args.steps):
+            step()
+        t3.record(stream)
+        torch.cuda.synchronize(dev)
+        ms_timed = t2.elapsed_time(t3) / args.steps
+        stats = psgd.psgd_plan_kernel_stats(plan, reset=True)
+        psgd.psgd_plan_set_timing(plan, False)
+        kb = kernel_bytes(plan, 4, bool(flags & psgd.PSGD_FLAG_CARRY_ERROR_MEAN))
+        kernels = {}
+        for name, (n, tot) in stats.items():
+            us = 1e3 * tot / max(n, 1)
+            entry = {"mean_us": round(us, 2), "launches": n}
+            if name in kb:
+                entry["alg_bytes"] = kb[name]
+                entry["alg_GBps"] = round(kb[name] / (us * 1e-6) / 1e9, 1)
+            kernels[name] = entry
+        grad_bytes = W * s["numel"] * 4
+        del grads, errors, workspace
+        return {"ms": ms, "ms_timed": ms_timed, "kernels": kernels, "kb": kb, "sizes": s,
+                "value": grad_bytes / (ms * 1e-3) / 1e9, "grad_bytes": grad_bytes,
+                "pct": 100.0 * s["model_bytes"] / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9)}
 
-    # timed region 2: the same steps with every kernel bracketed by HIP events
-    psgd.psgd_plan_set_timing(plan, True)
-    psgd.psgd_plan_kernel_stats(plan, reset=True)
-    t2, t3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t2.record(stream)
-    for _ in range(args.steps):
-        step()
-    t3.record(stream)
-    torch.cuda.synchronize(dev)
-    ms_timed = t2.elapsed_time(t3) / args.steps
-    stats = psgd.psgd_plan_kernel_stats(plan, reset=True)
-    psgd.psgd_plan_set_timing(plan, False)
-
-    kb = kernel_bytes(plan, 4)
-    kernels = {}
-    for name, (n, tot) in stats.items():
-        us = 1e3 * tot / max(n, 1)
-        entry = {"mean_us": round(us, 2), "launches": n}
-        if name in kb:
-            entry["alg_bytes"] = kb[name]
-            entry["alg_GBps"] = round(kb[name] / (us * 1e-6) / 1e9, 1)
-        kernels[name] = entry
+    plain = measure(0) if args.mode in ("both", "plain") else None
+    main_run = measure(psgd.PSGD_FLAG_CARRY_ERROR_MEAN) if args.mode != "plain" else plain
+    kernels, kb, s = main_run["kernels"], main_run["kb"], main_run["sizes"]
     dom = max(kernels, key=lambda k: kernels[k]["mean_us"])
     dom_us = kernels[dom]["mean_us"]
     achieved = kb[dom] / (dom_us * 1e-6) / 1e9
     traffic = traffic_for(dom)
-
-    grad_bytes = W * s["numel"] * 4
-    value = grad_bytes / (ms * 1e-3) / 1e9
+    ms = main_run["ms"]
     out = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": round(main_run["value"], 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -198,16 +205,21 @@ def main() -> int:
         "data": "synthetic (planted low-rank + 0.05*N(0,1) worker noise, drawn on device)",
         "config": {"workload": "resnet18_cifar_shapes", "rank": wl.rank, "workers": W,
                    "matrices": s["n_matrices"], "uncompressed_tensors": s["n_vectors"],
-                   "params": s["numel"], "grad_bytes_per_step": grad_bytes},
-        "pct_hbm_peak": round(100.0 * s["model_bytes"] / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 2),
+                   "params": s["numel"], "grad_bytes_per_step": main_run["grad_bytes"],
+                   "plan_flags": "PSGD_FLAG_CARRY_ERROR_MEAN"},
+        "pct_hbm_peak": round(main_run["pct"], 2),
         "model_bytes_per_step": s["model_bytes"],
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "alg_bytes_per_launch": kb[dom], "mean_us": dom_us},
         "kernels": kernels,
-        "ms_per_step_with_kernel_events": round(ms_timed, 4),
-        "wall_s_timed_region": round(wall, 3),
+        "ms_per_step_with_kernel_events": round(main_run["ms_timed"], 4),
     }
+    if args.mode == "plain":
+        out["config"]["plan_flags"] = "0"
+    elif plain is not None:
+        out["without_carry"] = {"value": round(plain["value"], 2), "ms_per_step": round(plain["ms"], 4),
+                                "pct_hbm_peak": round(plain["pct"], 2), "kernels": plain["kernels"]}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -39,10 +39,16 @@ struct bf16 {
 };
 
 // ------------------------------------------------------------------ loads and stores
+// Gradients and errors are touched once per pass and never reused from cache, so the
+// streaming passes load and store them non-temporally; buffers that a later kernel of
+// the same step reads again (Mbar, the carried error mean) use ordinary accesses.
 __device__ __forceinline__ f4 load4(const float* p) { return *reinterpret_cast<const f4*>(p); }
 
-__device__ __forceinline__ f4 load4(const bf16* p) {
-  const u16x4 v = *reinterpret_cast<const u16x4*>(p);
+__device__ __forceinline__ f4 load4_nt(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f4*>(p));
+}
+
+__device__ __forceinline__ f4 widen(const u16x4 v) {
   f4 r;
   r.x = __uint_as_float(uint32_t(v.x) << 16);
   r.y = __uint_as_float(uint32_t(v.y) << 16);
@@ -51,10 +57,24 @@ __device__ __forceinline__ f4 load4(const bf16* p) {
   return r;
 }
 
+__device__ __forceinline__ f4 load4_nt(const bf16* p) {
+  return widen(__builtin_nontemporal_load(reinterpret_cast<const u16x4*>(p)));
+}
+
 // Store the first `valid` (>= 1) lanes of v; all four when valid >= 4.
 __device__ __forceinline__ void store4(float* p, const f4 v, int64_t valid) {
   if (valid >= 4) {
     *reinterpret_cast<f4*>(p) = v;
+  } else {
+    p[0] = v.x;
+    if (valid > 1) p[1] = v.y;
+    if (valid > 2) p[2] = v.z;
+  }
+}
+
+__device__ __forceinline__ void store4_nt(float* p, const f4 v, int64_t valid) {
+  if (valid >= 4) {
+    __builtin_nontemporal_store(v, reinterpret_cast<f4*>(p));
   } else {
     p[0] = v.x;
     if (valid > 1) p[1] = v.y;
@@ -88,42 +108,66 @@ __device__ double block_sum(double v, double* red) {
 }
 
 // ------------------------------------------------------------------ pass 1: EF add + mean
-template <typename GT>
+// One float4 chunk per thread, every worker's slice of it loaded before any is used.
+// WT > 0: the worker count is the compile-time WT (loop fully unrolled); WT == 0: any
+// worker count.  With `ebar` set (carried error mean from the previous step) only the
+// gradients are read: Mbar = mean_w G_w + ebar, equal to mean_w (G_w + E_w) because the
+// carried ebar is the mean of exactly the E_w stored by that step.
+template <typename GT, int WT>
 __global__ __launch_bounds__(kStreamThreads) void k_ef_mean(const StreamTile* __restrict__ tiles,
                                                             const GT* __restrict__ G,
                                                             const float* __restrict__ E,
+                                                            const float* __restrict__ ebar,
                                                             float* __restrict__ Mbar, int W,
                                                             int64_t ld, float inv_w) {
   const StreamTile t = tiles[blockIdx.x];
-  const bool mat = t.mat >= 0;
-  for (int64_t c = t.begin + int64_t(threadIdx.x) * 4; c < t.end; c += kStreamThreads * 4) {
-    f4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int64_t c = t.begin + int64_t(threadIdx.x) * 4;
+  if (c >= t.end) return;
+  const bool with_errors = t.mat >= 0 && ebar == nullptr;
+  f4 acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (WT > 0) {
+    f4 g[WT];
+#pragma unroll
+    for (int w = 0; w < WT; ++w) g[w] = load4_nt(G + w * ld + c);
+    if (with_errors) {
+      f4 e[WT];
+#pragma unroll
+      for (int w = 0; w < WT; ++w) e[w] = load4_nt(E + w * ld + c);
+#pragma unroll
+      for (int w = 0; w < WT; ++w) acc += g[w] + e[w];
+    } else {
+#pragma unroll
+      for (int w = 0; w < WT; ++w) acc += g[w];
+    }
+  } else {
     int w = 0;
-    if (mat) {
+    if (with_errors) {
       for (; w + 4 <= W; w += 4) {
-        const f4 g0 = load4(G + (w + 0) * ld + c), e0 = load4(E + (w + 0) * ld + c);
-        const f4 g1 = load4(G + (w + 1) * ld + c), e1 = load4(E + (w + 1) * ld + c);
-        const f4 g2 = load4(G + (w + 2) * ld + c), e2 = load4(E + (w + 2) * ld + c);
-        const f4 g3 = load4(G + (w + 3) * ld + c), e3 = load4(E + (w + 3) * ld + c);
+        const f4 g0 = load4_nt(G + (w + 0) * ld + c), e0 = load4_nt(E + (w + 0) * ld + c);
+        const f4 g1 = load4_nt(G + (w + 1) * ld + c), e1 = load4_nt(E + (w + 1) * ld + c);
+        const f4 g2 = load4_nt(G + (w + 2) * ld + c), e2 = load4_nt(E + (w + 2) * ld + c);
+        const f4 g3 = load4_nt(G + (w + 3) * ld + c), e3 = load4_nt(E + (w + 3) * ld + c);
         acc += g0 + e0;
         acc += g1 + e1;
         acc += g2 + e2;
         acc += g3 + e3;
       }
-      for (; w < W; ++w) acc += load4(G + w * ld + c) + load4(E + w * ld + c);
+      for (; w < W; ++w) acc += load4_nt(G + w * ld + c) + load4_nt(E + w * ld + c);
     } else {
       for (; w + 4 <= W; w += 4) {
-        const f4 g0 = load4(G + (w + 0) * ld + c), g1 = load4(G + (w + 1) * ld + c);
-        const f4 g2 = load4(G + (w + 2) * ld + c), g3 = load4(G + (w + 3) * ld + c);
+        const f4 g0 = load4_nt(G + (w + 0) * ld + c), g1 = load4_nt(G + (w + 1) * ld + c);
+        const f4 g2 = load4_nt(G + (w + 2) * ld + c), g3 = load4_nt(G + (w + 3) * ld + c);
         acc += g0;
         acc += g1;
         acc += g2;
         acc += g3;
       }
-      for (; w < W; ++w) acc += load4(G + w * ld + c);
+      for (; w < W; ++w) acc += load4_nt(G + w * ld + c);
     }
-    store4(Mbar + c, acc * inv_w, t.end - c);
   }
+  acc *= inv_w;
+  if (t.mat >= 0 && ebar != nullptr) acc += load4(ebar + c);
+  store4(Mbar + c, acc, t.end - c);
 }
 
 // ------------------------------------------------------------------ P-bar = Mbar Q
@@ -144,6 +188,7 @@ __global__ __launch_bounds__(kRowThreads) void k_p_rows(const RowTile* __restric
 #pragma unroll
     for (int k = 0; k < R; ++k) acc[k] = 0.f;
     if (mi.vec4) {
+#pragma unroll 4
       for (int j = lane * 4; j < cols; j += 256) {
         const f4 v = load4(mrow + j);
         const float* qj = Qm + int64_t(j) * R;
@@ -152,6 +197,7 @@ __global__ __launch_bounds__(kRowThreads) void k_p_rows(const RowTile* __restric
           acc[k] += v.x * qj[k] + v.y * qj[R + k] + v.z * qj[2 * R + k] + v.w * qj[3 * R + k];
       }
     } else {
+#pragma unroll 4
       for (int j = lane; j < cols; j += 64) {
         const float v = mrow[j];
 #pragma unroll
@@ -236,6 +282,7 @@ __global__ __launch_bounds__(kQThreads) void k_q_partial(const QTile* __restrict
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int k = 0; k < R; ++k) acc[q][k] = 0.f;
+#pragma unroll 8
     for (int i = r0; i < r1; ++i) {
       const f4 v = load4(base + int64_t(i) * cols + j);
 #pragma unroll
@@ -257,6 +304,7 @@ __global__ __launch_bounds__(kQThreads) void k_q_partial(const QTile* __restrict
     float acc[R];
 #pragma unroll
     for (int k = 0; k < R; ++k) acc[k] = 0.f;
+#pragma unroll 8
     for (int i = r0; i < r1; ++i) {
       const float v = base[int64_t(i) * cols + j];
 #pragma unroll
@@ -284,39 +332,29 @@ __global__ __launch_bounds__(kQRedThreads) void k_q_reduce(const MatInfo* __rest
 // ------------------------------------------------------------------ pass 2: error + update
 enum ApplyMode { kCompress = 0, kMomentum = 1, kNesterov = 2 };
 
-template <int MODE>
-__device__ __forceinline__ void momentum4(float* mom, float* x, const f4 u, int64_t c, int64_t valid,
-                                          float lr, float mu) {
-  if (MODE == kCompress) return;
-  const f4 m0 = load4(mom + c), x0 = load4(x + c);
-  const f4 m1 = mu * m0 + u;
-  const f4 x1 = (MODE == kNesterov) ? x0 - lr * (u + mu * m1) : x0 - lr * m1;
-  store4(mom + c, m1, valid);
-  store4(x + c, x1, valid);
-}
-
-template <typename GT, int R, int MODE>
+// One float4 chunk per thread.  For a compressed matrix: u = P Q^T at the chunk's four
+// elements (rank R <= 4), E'_w = (G_w + E_w) - u for every worker, and (carry mode) the
+// mean of the stored E'_w into `ebar`.  Every tensor: the update u is written once and,
+// in the momentum modes, mom <- mu*mom + u; x <- x - lr*mom (or x - lr*(u + mu*mom)).
+template <typename GT, int WT>
 __global__ __launch_bounds__(kStreamThreads) void k_apply(
     const StreamTile* __restrict__ tiles, const MatInfo* __restrict__ mats, const GT* __restrict__ G,
     float* __restrict__ E, const float* __restrict__ Mbar, const float* __restrict__ P,
     const float* __restrict__ Q, float* __restrict__ update, float* __restrict__ mom,
-    float* __restrict__ x, int W, int64_t ld, float lr, float mu) {
+    float* __restrict__ x, float* __restrict__ ebar, int W, int64_t ld, int R, int mode, float lr,
+    float mu, float inv_w) {
   const StreamTile t = tiles[blockIdx.x];
+  const int64_t c = t.begin + int64_t(threadIdx.x) * 4;
+  if (c >= t.end) return;
+  const int64_t valid = t.end - c;
+  f4 uv;
   if (t.mat < 0) {  // uncompressed tensor: the update is the worker mean
-    for (int64_t c = t.begin + int64_t(threadIdx.x) * 4; c < t.end; c += kStreamThreads * 4) {
-      const f4 u = load4(Mbar + c);
-      const int64_t valid = t.end - c;
-      if (update != nullptr) store4(update + c, u, valid);
-      momentum4<MODE>(mom, x, u, c, valid, lr, mu);
-    }
-    return;
-  }
-  const MatInfo mi = mats[t.mat];
-  const float* Pm = P + mi.p_off;
-  const float* Qm = Q + mi.q_off;
-  const int cols = mi.cols;
-  for (int64_t c = t.begin + int64_t(threadIdx.x) * 4; c < t.end; c += kStreamThreads * 4) {
-    const int64_t valid = t.end - c;
+    uv = load4(Mbar + c);
+  } else {
+    const MatInfo mi = mats[t.mat];
+    const float* Pm = P + mi.p_off;
+    const float* Qm = Q + mi.q_off;
+    const int cols = mi.cols;
     const int e0 = int(c - mi.offset);
     int i = e0 / cols;
     int j = e0 - i * cols;
@@ -326,7 +364,8 @@ __global__ __launch_bounds__(kStreamThreads) void k_apply(
       float s = 0.f;
       if (q < valid) {
 #pragma unroll
-        for (int k = 0; k < R; ++k) s += Pm[int64_t(i) * R + k] * Qm[int64_t(j) * R + k];
+        for (int k = 0; k < 4; ++k)
+          if (k < R) s += Pm[int64_t(i) * R + k] * Qm[int64_t(j) * R + k];
       }
       u[q] = s;
       if (++j == cols) {
@@ -334,24 +373,53 @@ __global__ __launch_bounds__(kStreamThreads) void k_apply(
         ++i;
       }
     }
-    const f4 uv = {u[0], u[1], u[2], u[3]};
-    int w = 0;
-    for (; w + 4 <= W; w += 4) {
-      const f4 g0 = load4(G + (w + 0) * ld + c), e0v = load4(E + (w + 0) * ld + c);
-      const f4 g1 = load4(G + (w + 1) * ld + c), e1v = load4(E + (w + 1) * ld + c);
-      const f4 g2 = load4(G + (w + 2) * ld + c), e2v = load4(E + (w + 2) * ld + c);
-      const f4 g3 = load4(G + (w + 3) * ld + c), e3v = load4(E + (w + 3) * ld + c);
-      store4(E + (w + 0) * ld + c, (g0 + e0v) - uv, valid);
-      store4(E + (w + 1) * ld + c, (g1 + e1v) - uv, valid);
-      store4(E + (w + 2) * ld + c, (g2 + e2v) - uv, valid);
-      store4(E + (w + 3) * ld + c, (g3 + e3v) - uv, valid);
+    uv = f4{u[0], u[1], u[2], u[3]};
+    f4 es = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (WT > 0) {
+      f4 g[WT], e[WT];
+#pragma unroll
+      for (int w = 0; w < WT; ++w) {
+        g[w] = load4_nt(G + w * ld + c);
+        e[w] = load4_nt(E + w * ld + c);
+      }
+#pragma unroll
+      for (int w = 0; w < WT; ++w) {
+        const f4 ew = (g[w] + e[w]) - uv;
+        store4_nt(E + w * ld + c, ew, valid);
+        es += ew;
+      }
+    } else {
+      int w = 0;
+      for (; w + 4 <= W; w += 4) {
+        const f4 g0 = load4_nt(G + (w + 0) * ld + c), e0v = load4_nt(E + (w + 0) * ld + c);
+        const f4 g1 = load4_nt(G + (w + 1) * ld + c), e1v = load4_nt(E + (w + 1) * ld + c);
+        const f4 g2 = load4_nt(G + (w + 2) * ld + c), e2v = load4_nt(E + (w + 2) * ld + c);
+        const f4 g3 = load4_nt(G + (w + 3) * ld + c), e3v = load4_nt(E + (w + 3) * ld + c);
+        const f4 n0 = (g0 + e0v) - uv, n1 = (g1 + e1v) - uv, n2 = (g2 + e2v) - uv, n3 = (g3 + e3v) - uv;
+        store4_nt(E + (w + 0) * ld + c, n0, valid);
+        store4_nt(E + (w + 1) * ld + c, n1, valid);
+        store4_nt(E + (w + 2) * ld + c, n2, valid);
+        store4_nt(E + (w + 3) * ld + c, n3, valid);
+        es += n0;
+        es += n1;
+        es += n2;
+        es += n3;
+      }
+      for (; w < W; ++w) {
+        const f4 n = (load4_nt(G + w * ld + c) + load4_nt(E + w * ld + c)) - uv;
+        store4_nt(E + w * ld + c, n, valid);
+        es += n;
+      }
     }
-    for (; w < W; ++w) {
-      const f4 g = load4(G + w * ld + c), e = load4(E + w * ld + c);
-      store4(E + w * ld + c, (g + e) - uv, valid);
-    }
-    if (update != nullptr) store4(update + c, uv, valid);
-    momentum4<MODE>(mom, x, uv, c, valid, lr, mu);
+    if (ebar != nullptr) store4(ebar + c, es * inv_w, valid);
+  }
+  if (update != nullptr) store4_nt(update + c, uv, valid);
+  if (mode != kCompress) {
+    const f4 m0 = load4_nt(mom + c), x0 = load4_nt(x + c);
+    const f4 m1 = mu * m0 + uv;
+    const f4 x1 = (mode == kNesterov) ? x0 - lr * (uv + mu * m1) : x0 - lr * m1;
+    store4_nt(mom + c, m1, valid);
+    store4_nt(x + c, x1, valid);
   }
 }
 
@@ -472,29 +540,69 @@ psgd_status launch_timed(psgd_plan* plan, hipStream_t st, int kid, F&& launch) {
   return PSGD_OK;
 }
 
+// Worker-count specialisations of the streaming passes: W in {1,2,4,8,16} unrolls fully,
+// anything else takes the generic loop.
+template <typename GT, int WT>
+void launch_stream_pair(bool first, unsigned grid, hipStream_t st, const DeviceTables& dt,
+                        const void* grads, float* errors, const float* ebar_in, float* ebar_out,
+                        float* Mbar, const float* p, const float* q, float* update, float* mom, float* x,
+                        int W, int64_t ld, int R, int mode, float lr, float mu, float inv_w) {
+  if (first)
+    hipLaunchKernelGGL((k_ef_mean<GT, WT>), dim3(grid), dim3(kStreamThreads), 0, st, dt.stiles,
+                       static_cast<const GT*>(grads), errors, ebar_in, Mbar, W, ld, inv_w);
+  else
+    hipLaunchKernelGGL((k_apply<GT, WT>), dim3(grid), dim3(kStreamThreads), 0, st, dt.stiles, dt.mats,
+                       static_cast<const GT*>(grads), errors, Mbar, p, q, update, mom, x, ebar_out, W, ld,
+                       R, mode, lr, mu, inv_w);
+}
+
+template <typename GT>
+void launch_stream(bool first, unsigned grid, hipStream_t st, const DeviceTables& dt, const void* grads,
+                   float* errors, const float* ebar_in, float* ebar_out, float* Mbar, const float* p,
+                   const float* q, float* update, float* mom, float* x, int W, int64_t ld, int R, int mode,
+                   float lr, float mu, float inv_w) {
+#define PSGD_STREAM(WT)                                                                              \
+  launch_stream_pair<GT, WT>(first, grid, st, dt, grads, errors, ebar_in, ebar_out, Mbar, p, q, update, \
+                             mom, x, W, ld, R, mode, lr, mu, inv_w)
+  switch (W) {
+    case 1: PSGD_STREAM(1); break;
+    case 2: PSGD_STREAM(2); break;
+    case 4: PSGD_STREAM(4); break;
+    case 8: PSGD_STREAM(8); break;
+    case 16: PSGD_STREAM(16); break;
+    default: PSGD_STREAM(0); break;
+  }
+#undef PSGD_STREAM
+}
+
 template <int R>
 psgd_status launch_all(psgd_plan* plan, const DeviceTables& dt, const void* grads, float* errors,
                        float* q, float* p, float* update, float* mom, float* x, float lr, float mu,
-                       char* ws, hipStream_t stream, int mode) {
+                       char* ws, bool use_carry, hipStream_t stream, int mode) {
   const int W = plan->n_workers;
   const int64_t ld = plan->worker_stride;
   float* Mbar = reinterpret_cast<float*>(ws + plan->ws_mbar);
   float* Pbar = reinterpret_cast<float*>(ws + plan->ws_pbar);
   float* Qpart = reinterpret_cast<float*>(ws + plan->ws_qpart);
+  float* ebar = (plan->flags & PSGD_FLAG_CARRY_ERROR_MEAN) ? reinterpret_cast<float*>(ws + plan->ws_ebar)
+                                                           : nullptr;
+  const float* ebar_in = use_carry ? ebar : nullptr;
   const unsigned n_st = unsigned(plan->stiles.size());
   const unsigned n_mats = unsigned(plan->mats.size());
   const bool bf = plan->dtype == PSGD_BF16;
   const float inv_w = 1.0f / float(W);
   psgd_status s;
 
-  s = launch_timed(plan, stream, kKEfMean, [&] {
+  auto stream_pass = [&](bool first) {
     if (bf)
-      hipLaunchKernelGGL(k_ef_mean<bf16>, dim3(n_st), dim3(kStreamThreads), 0, stream, dt.stiles,
-                         static_cast<const bf16*>(grads), errors, Mbar, W, ld, inv_w);
+      launch_stream<bf16>(first, n_st, stream, dt, grads, errors, ebar_in, ebar, Mbar, p, q, update, mom, x,
+                          W, ld, R, mode, lr, mu, inv_w);
     else
-      hipLaunchKernelGGL(k_ef_mean<float>, dim3(n_st), dim3(kStreamThreads), 0, stream, dt.stiles,
-                         static_cast<const float*>(grads), errors, Mbar, W, ld, inv_w);
-  });
+      launch_stream<float>(first, n_st, stream, dt, grads, errors, ebar_in, ebar, Mbar, p, q, update, mom,
+                           x, W, ld, R, mode, lr, mu, inv_w);
+  };
+
+  s = launch_timed(plan, stream, kKEfMean, [&] { stream_pass(true); });
   if (s != PSGD_OK) return s;
 
   if (n_mats > 0) {
@@ -518,24 +626,7 @@ psgd_status launch_all(psgd_plan* plan, const DeviceTables& dt, const void* grad
     });
     if (s != PSGD_OK) return s;
   }
-
-#define PSGD_APPLY(GT, MODE)                                                                     \
-  hipLaunchKernelGGL((k_apply<GT, R, MODE>), dim3(n_st), dim3(kStreamThreads), 0, stream, dt.stiles, \
-                     dt.mats, static_cast<const GT*>(grads), errors, Mbar, p, q, update, mom, x, W, \
-                     ld, lr, mu)
-  s = launch_timed(plan, stream, kKApply, [&] {
-    if (bf) {
-      if (mode == kCompress) PSGD_APPLY(bf16, kCompress);
-      else if (mode == kMomentum) PSGD_APPLY(bf16, kMomentum);
-      else PSGD_APPLY(bf16, kNesterov);
-    } else {
-      if (mode == kCompress) PSGD_APPLY(float, kCompress);
-      else if (mode == kMomentum) PSGD_APPLY(float, kMomentum);
-      else PSGD_APPLY(float, kNesterov);
-    }
-  });
-#undef PSGD_APPLY
-  return s;
+  return launch_timed(plan, stream, kKApply, [&] { stream_pass(false); });
 }
 
 psgd_status run_step(const char* fn, psgd_plan* plan, const void* grads, float* errors, float* q,
@@ -589,16 +680,33 @@ psgd_status run_step(const char* fn, psgd_plan* plan, const void* grads, float* 
 
   DeviceTables* dt = nullptr;
   if ((s = ensure_tables(plan, &dt)) != PSGD_OK) return s;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
+  // The carried error mean is used only if the previous step of this plan ran on the
+  // same device with the same error and workspace buffers.
+  const bool carry = (plan->flags & PSGD_FLAG_CARRY_ERROR_MEAN) != 0;
+  const bool use_carry = carry && plan->carry_valid && plan->carry_errors == errors &&
+                         plan->carry_workspace == workspace && plan->carry_device == dev;
+  plan->carry_valid = false;
   switch (plan->rank) {
-    case 1: return launch_all<1>(plan, *dt, grads, errors, q, p, update, mom, x, lr, mu, ws, st, mode);
-    case 2: return launch_all<2>(plan, *dt, grads, errors, q, p, update, mom, x, lr, mu, ws, st, mode);
-    case 3: return launch_all<3>(plan, *dt, grads, errors, q, p, update, mom, x, lr, mu, ws, st, mode);
-    case 4: return launch_all<4>(plan, *dt, grads, errors, q, p, update, mom, x, lr, mu, ws, st, mode);
+    case 1: s = launch_all<1>(plan, *dt, grads, errors, q, p, update, mom, x, lr, mu, ws, use_carry, st, mode); break;
+    case 2: s = launch_all<2>(plan, *dt, grads, errors, q, p, update, mom, x, lr, mu, ws, use_carry, st, mode); break;
+    case 3: s = launch_all<3>(plan, *dt, grads, errors, q, p, update, mom, x, lr, mu, ws, use_carry, st, mode); break;
+    case 4: s = launch_all<4>(plan, *dt, grads, errors, q, p, update, mom, x, lr, mu, ws, use_carry, st, mode); break;
+    default:
+      set_error(std::string(fn) + ": rank outside 1..4");
+      return PSGD_ERR_UNSUPPORTED;
   }
-  set_error(std::string(fn) + ": rank outside 1..4");
-  return PSGD_ERR_UNSUPPORTED;
+  if (s == PSGD_OK && carry && has_mats) {
+    plan->carry_valid = true;
+    plan->carry_errors = errors;
+    plan->carry_workspace = workspace;
+    plan->carry_device = dev;
+  }
+  plan->last_step_carried = use_carry;
+  return s;
 }
 
 }  // namespace
@@ -610,6 +718,15 @@ extern "C" psgd_status psgd_compress_step(psgd_plan* plan, const void* grads, fl
                                           float* p, float* update, void* workspace, void* stream) {
   return run_step("psgd_compress_step", plan, grads, errors, q, p, update, nullptr, nullptr, 0.f, 0.f,
                   workspace, stream, kCompress);
+}
+
+extern "C" psgd_status psgd_plan_reset_carry(psgd_plan* plan) {
+  if (plan == nullptr) {
+    set_error("psgd_plan_reset_carry: plan is NULL");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  plan->carry_valid = false;
+  return PSGD_OK;
 }
 
 extern "C" psgd_status psgd_ef_momentum_apply(psgd_plan* plan, const void* grads, float* errors,

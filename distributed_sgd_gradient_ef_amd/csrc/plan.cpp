@@ -64,7 +64,7 @@ extern "C" psgd_status psgd_plan_create(const psgd_layer* layers, int32_t n_laye
     return fail(PSGD_ERR_INVALID_ARG, "psgd_plan_create: n_workers must be in 1..65536");
   if (grad_dtype != PSGD_F32 && grad_dtype != PSGD_BF16)
     return fail(PSGD_ERR_UNSUPPORTED, "psgd_plan_create: unknown gradient dtype");
-  if (flags & ~uint32_t(PSGD_FLAG_NESTEROV))
+  if (flags & ~uint32_t(PSGD_FLAG_NESTEROV | PSGD_FLAG_CARRY_ERROR_MEAN))
     return fail(PSGD_ERR_UNSUPPORTED, "psgd_plan_create: unknown flag bits");
 
   psgd_plan* plan = new (std::nothrow) psgd_plan();
@@ -160,6 +160,8 @@ extern "C" psgd_status psgd_plan_create(const psgd_layer* layers, int32_t n_laye
     ws += uint64_t(round_up(std::max<int64_t>(plan->p_elems, 1) * 4, 256));
     plan->ws_qpart = ws;
     ws += uint64_t(round_up(std::max<int64_t>(plan->qpart_elems, 1) * 4, 256));
+    plan->ws_ebar = ws;
+    if (flags & PSGD_FLAG_CARRY_ERROR_MEAN) ws += uint64_t(round_up(plan->worker_stride * 4, 256));
     plan->workspace_bytes = ws;
 
     const uint64_t W = uint64_t(n_workers);

@@ -16,9 +16,9 @@ constexpr int64_t kAlignElems = 64;  // every tensor starts on a 256-byte bounda
 
 // Streaming passes (EF add + worker mean, and the final error/update pass): one
 // workgroup of kStreamThreads handles one tile of up to kStreamTileElems consecutive
-// elements of one tensor, as float4 chunks.
+// elements of one tensor, one float4 chunk per thread.
 constexpr int kStreamThreads = 256;
-constexpr int kStreamTileElems = kStreamThreads * 4 * 4;
+constexpr int kStreamTileElems = kStreamThreads * 4;
 
 // P = Mbar Q: one workgroup of kRowThreads handles kRowsPerTile rows; one wave per row.
 constexpr int kRowThreads = 256;
@@ -26,7 +26,7 @@ constexpr int kRowsPerTile = 16;
 
 // Q partials = Mbar^T P over a block of rows and a strip of columns.
 constexpr int kQThreads = 256;
-constexpr int kQTargetRowsPerBlock = 64;
+constexpr int kQTargetRowsPerBlock = 32;
 constexpr int kQMaxRowBlocks = 32;
 
 // Gram-Schmidt: one workgroup per matrix.
@@ -100,9 +100,15 @@ struct psgd_plan {
   int64_t worker_stride = 0, numel = 0, matrix_numel = 0, vector_numel = 0;
   int64_t p_elems = 0, q_elems = 0, qpart_elems = 0;
   int64_t max_q_elems_per_matrix = 0;
-  uint64_t ws_mbar = 0, ws_pbar = 0, ws_qpart = 0, workspace_bytes = 0;
+  uint64_t ws_mbar = 0, ws_pbar = 0, ws_qpart = 0, ws_ebar = 0, workspace_bytes = 0;
   uint64_t message_bytes = 0, model_bytes = 0, model_bytes_momentum = 0;
   std::map<int, psgd::DeviceTables> dev;  // per HIP device id
+  // carried worker mean of the errors (PSGD_FLAG_CARRY_ERROR_MEAN)
+  bool carry_valid = false;
+  bool last_step_carried = false;
+  const void* carry_errors = nullptr;
+  const void* carry_workspace = nullptr;
+  int carry_device = -1;
   // kernel timing (psgd_plan_set_timing)
   bool timing = false;
   std::vector<psgd::PendingTiming> pending;

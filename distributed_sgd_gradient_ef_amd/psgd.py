@@ -29,11 +29,12 @@ PSGD_ERR_HIP = 4
 PSGD_F32 = 0
 PSGD_BF16 = 1
 PSGD_FLAG_NESTEROV = 0x1
+PSGD_FLAG_CARRY_ERROR_MEAN = 0x2
 
 EXPORTED = [
     "psgd_plan_create", "psgd_plan_sizes", "psgd_plan_layer_info", "psgd_plan_destroy",
     "psgd_compress_step", "psgd_ef_momentum_apply", "psgd_plan_set_timing",
-    "psgd_plan_kernel_stats", "psgd_status_string", "psgd_last_error",
+    "psgd_plan_kernel_stats", "psgd_plan_reset_carry", "psgd_status_string", "psgd_last_error",
 ]
 
 
@@ -94,7 +95,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.psgd_ef_momentum_apply.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, f32, vp, vp, vp]
     lib.psgd_plan_set_timing.argtypes = [vp, i32]
     lib.psgd_plan_kernel_stats.argtypes = [vp, ctypes.POINTER(_KernelStat), i32, ctypes.POINTER(i32), i32]
-    for name in EXPORTED[:8]:
+    lib.psgd_plan_reset_carry.argtypes = [vp]
+    for name in EXPORTED[:9]:
         getattr(lib, name).restype = ctypes.c_int
     lib.psgd_status_string.argtypes = [ctypes.c_int]
     lib.psgd_status_string.restype = ctypes.c_char_p
@@ -178,6 +180,10 @@ def psgd_plan_kernel_stats(plan: Plan, reset: bool = False) -> dict:
     n = ctypes.c_int32()
     _check(load_library().psgd_plan_kernel_stats(plan.handle, arr, 16, ctypes.byref(n), 1 if reset else 0))
     return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(n.value)}
+
+
+def psgd_plan_reset_carry(plan: Plan) -> None:
+    _check(load_library().psgd_plan_reset_carry(plan.handle))
 
 
 def _ptr(t) -> Optional[int]:

@@ -84,6 +84,17 @@ typedef enum psgd_dtype {
 
 /* Plan flags. */
 #define PSGD_FLAG_NESTEROV 0x1u /* psgd_ef_momentum_apply uses x <- x - lr*(U + mu*mom) */
+/* Carry the workers' mean error from one step to the next.  The first pass of a step
+ * needs mean_w (G_w + E_w) = mean_w G_w + mean_w E_w; the final pass of the previous
+ * step already held every E_w it stored, so it also writes their mean into the
+ * workspace, and the next step's first pass then reads only the gradients (4W + 8
+ * instead of 8W + 4 bytes per element).  The results are the same up to float
+ * rounding order.  Contract: between consecutive steps of the plan the caller passes
+ * the same `errors` and `workspace` pointers and modifies neither.  A step falls back to
+ * reading all errors when it is the plan's first, follows psgd_plan_reset_carry, or
+ * sees other errors/workspace pointers or another device than the previous step; a
+ * failed step also forces the fallback.  The workspace grows by worker_stride floats. */
+#define PSGD_FLAG_CARRY_ERROR_MEAN 0x2u
 
 /* One tensor of the layer list.  rows == 1 or cols == 1 marks a 1-D tensor. */
 typedef struct psgd_layer {
@@ -184,6 +195,10 @@ psgd_status psgd_plan_set_timing(psgd_plan* plan, int32_t enable);
  * event could not be read. */
 psgd_status psgd_plan_kernel_stats(psgd_plan* plan, psgd_kernel_stat* out, int32_t capacity,
                                    int32_t* count, int32_t reset);
+
+/* Make the next step of a PSGD_FLAG_CARRY_ERROR_MEAN plan read all errors again (call
+ * after writing `errors` or the workspace yourself, e.g. when restoring a checkpoint). */
+psgd_status psgd_plan_reset_carry(psgd_plan* plan);
 
 /* Static text for a status code. */
 const char* psgd_status_string(psgd_status status);

@@ -39,6 +39,7 @@ class DeviceRun:
     """Device buffers of one plan, in the packed layout, and the step calls."""
 
     def __init__(self, shapes, rank, workers, device="cuda:0", bf16=False, flags=0, momentum=False):
+        self.flags = flags
         import torch
 
         self.torch = torch
@@ -148,13 +149,12 @@ def compare_step(run: DeviceRun, snap: Dict[int, LayerSnapshot], oracle_mod, tol
     """Run the oracle on the snapshot and compare with the GPU outputs of the step that
     followed it.  Returns the worst relative error per output kind; asserts <= tol."""
     run.torch.cuda.synchronize(run.dev)
-    upd = run.update.cpu().numpy()
     worst = {"p": 0.0, "q": 0.0, "u": 0.0, "e": 0.0, "v": 0.0}
     for li, s in snap.items():
         L = run.plan.layers[li]
         if not L.compressed:
             ref = oracle_mod.average_tensor(s.g)
-            err = rel(psgd.unpack(run.plan, upd, li), ref, np.linalg.norm(ref) + 1e-30)
+            err = rel(run.vec_layer(run.update, li), ref, np.linalg.norm(ref) + 1e-30)
             worst["v"] = max(worst["v"], err)
             assert err <= tol, f"{what} layer {li} mean: rel {err:.3e}"
             continue
@@ -163,7 +163,7 @@ def compare_step(run: DeviceRun, snap: Dict[int, LayerSnapshot], oracle_mod, tol
         errs = {
             "p": rel(run.p_layer(li), ref.p_hat, 1.0) if check_p else 0.0,
             "q": rel(run.q_layer(li), ref.q_bar, mbar),
-            "u": rel(psgd.unpack(run.plan, upd, li), ref.update, mbar),
+            "u": rel(run.vec_layer(run.update, li), ref.update, mbar),
         }
         e_gpu = run.errors_layer(li)
         errs["e"] = max(rel(e_gpu[w], ref.errors[w], mbar) for w in range(run.W))

@@ -121,6 +121,23 @@ def test_plan_model_bytes(dtype, gb):
         assert abs(s["model_bytes"] / 1e9 - 2.189) < 0.001
 
 
+def test_carry_flag_grows_workspace_by_one_slice():
+    shapes = [s for _, s in WL.resnet18_cifar_shapes()]
+    a = psgd.psgd_plan_create(shapes, 2, 16).sizes
+    b = psgd.psgd_plan_create(shapes, 2, 16, flags=psgd.PSGD_FLAG_CARRY_ERROR_MEAN).sizes
+    assert b["workspace_bytes"] - a["workspace_bytes"] == -(-a["worker_stride"] * 4 // 256) * 256
+    plan = psgd.psgd_plan_create(shapes, 2, 16, flags=psgd.PSGD_FLAG_CARRY_ERROR_MEAN | psgd.PSGD_FLAG_NESTEROV)
+    psgd.psgd_plan_reset_carry(plan)
+    assert psgd.load_library().psgd_plan_reset_carry(None) == psgd.PSGD_ERR_INVALID_ARG
+
+
+def test_timing_calls_without_gpu():
+    plan = psgd.psgd_plan_create([(8, 8)], 2, 2)
+    psgd.psgd_plan_set_timing(plan, True)
+    assert psgd.psgd_plan_kernel_stats(plan, reset=True) == {}
+    psgd.psgd_plan_set_timing(plan, False)
+
+
 def test_rank_at_least_min_side_is_uncompressed():
     plan = psgd.psgd_plan_create([(3, 100), (5, 4), (8, 8)], 4, 2)
     assert [l.compressed for l in plan.layers] == [False, False, True]

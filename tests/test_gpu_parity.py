@@ -192,6 +192,60 @@ def test_deterministic(torch_gpu):
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
+# ----------------------------------------------------------------------- carried error mean
+CARRY_SHAPES = [(64, 27), (1, 64), (128, 576), (512, 4608), (37, 29), (1, 10), (10, 512)]
+
+
+@pytest.mark.parametrize("W,r", [(16, 2), (5, 3)])
+def test_carry_error_mean_each_step(torch_gpu, W, r):
+    """With the carried error mean the first pass reads only the gradients; every step
+    still matches the oracle run on the errors actually stored on the GPU."""
+    from distributed_sgd_gradient_ef_amd import psgd
+
+    log(f"[case] carry W={W} r={r}")
+    rng = np.random.default_rng(31 + W)
+    run = DeviceRun(CARRY_SHAPES, r, W, flags=psgd.PSGD_FLAG_CARRY_ERROR_MEAN)
+    run.set_q_host({i: rng.standard_normal((s[1], r)).astype(np.float32)
+                    for i, s in enumerate(CARRY_SHAPES) if WL.is_matrix(s, r)})
+    for t in range(4):
+        run.set_grads_host([rng.standard_normal((W,) + s).astype(np.float32) for s in CARRY_SHAPES])
+        snap = snapshot(run, range(len(CARRY_SHAPES)))
+        run.compress()
+        compare_step(run, snap, O, TOL, what=f"carry step {t}")
+
+
+def test_carry_is_used_and_reset_restores_exactness(torch_gpu):
+    """Writing the errors behind the plan's back makes the carried mean stale (which
+    shows the carry path is live); psgd_plan_reset_carry makes the next step exact."""
+    from distributed_sgd_gradient_ef_amd import psgd
+
+    log("[case] carry reset")
+    shapes = [(256, 1152), (1, 64)]
+    W, r = 4, 2
+    rng = np.random.default_rng(8)
+    run = DeviceRun(shapes, r, W, flags=psgd.PSGD_FLAG_CARRY_ERROR_MEAN)
+    run.set_q_host({0: rng.standard_normal((1152, r)).astype(np.float32)})
+    g = [rng.standard_normal((W,) + s).astype(np.float32) for s in shapes]
+    run.set_grads_host(g)
+    run.compress()
+    run.set_errors_host([np.zeros((W,) + s, np.float32) for s in shapes])  # behind the plan's back
+    snap = snapshot(run, [0])
+    run.compress()
+    with pytest.raises(AssertionError):
+        compare_step(run, snap, O, TOL, what="stale carry")
+    run.set_errors_host([np.zeros((W,) + s, np.float32) for s in shapes])
+    psgd.psgd_plan_reset_carry(run.plan)
+    snap = snapshot(run, [0, 1])
+    run.compress()
+    compare_step(run, snap, O, TOL, what="after reset")
+    # a different workspace buffer also falls back to a full read
+    run.set_errors_host([np.zeros((W,) + s, np.float32) for s in shapes])
+    run.workspace = run.torch.empty_like(run.workspace)
+    snap = snapshot(run, [0, 1])
+    run.compress()
+    compare_step(run, snap, O, TOL, what="new workspace")
+
+
 # ----------------------------------------------------------------------- workloads
 def test_resnet18_three_steps(torch_gpu):
     """ResNet-18 shapes, r=2, W=16, three steps with fresh worker noise, every tensor."""
@@ -254,7 +308,7 @@ def test_stress_full_size_sampled(torch_gpu, r, bf16):
             g = originals[li].reshape(run.W, L.rows, L.cols)
             ref = O.compress_matrix(g, np.zeros_like(g), q0[li])
             mb = np.linalg.norm(g.astype(np.float64).mean(axis=0))
-            bad = max(bad, rel(run.layer(run.host(run.update), li), ref.update, mb))
+            bad = max(bad, rel(run.vec_layer(run.update, li), ref.update, mb))
         log(f"bf16 vs oracle on the fp32 originals: U rel {bad:.2e}")
         assert bad <= 2e-2
     # whole-set properties: E' + U = G + E (E was zero) for every matrix, P orthonormal
