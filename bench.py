@@ -182,6 +182,21 @@ def main() -> int:
                 "value": grad_bytes / (ms * 1e-3) / 1e9, "grad_bytes": grad_bytes,
                 "pct": 100.0 * s["model_bytes"] / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9)}
 
+    # context: the plain-copy bandwidth the device reaches (1 GiB read + 1 GiB written)
+    cbytes = 1 << 30
+    src = torch.empty(cbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    psgd.psgd_stream_copy(src, dst, cbytes)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    c0.record()
+    for _ in range(5):
+        psgd.psgd_stream_copy(src, dst, cbytes)
+    c1.record()
+    torch.cuda.synchronize(dev)
+    copy_gbs = 2 * cbytes * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+
     plain = measure(0) if args.mode in ("both", "plain") else None
     main_run = measure(psgd.PSGD_FLAG_CARRY_ERROR_MEAN) if args.mode != "plain" else plain
     kernels, kb, s = main_run["kernels"], main_run["kb"], main_run["sizes"]
@@ -214,6 +229,7 @@ def main() -> int:
                      "alg_bytes_per_launch": kb[dom], "mean_us": dom_us},
         "kernels": kernels,
         "ms_per_step_with_kernel_events": round(main_run["ms_timed"], 4),
+        "stream_copy_GBps": round(copy_gbs, 1),
     }
     if args.mode == "plain":
         out["config"]["plan_flags"] = "0"

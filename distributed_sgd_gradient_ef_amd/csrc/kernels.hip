@@ -423,6 +423,13 @@ __global__ __launch_bounds__(kStreamThreads) void k_apply(
   }
 }
 
+// ------------------------------------------------------------------ calibration copy
+__global__ __launch_bounds__(256) void k_stream_copy(const float* __restrict__ src, float* __restrict__ dst,
+                                                     int64_t n4) {
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n4; i += int64_t(gridDim.x) * 256)
+    __builtin_nontemporal_store(load4_nt(src + 4 * i), reinterpret_cast<f4*>(dst + 4 * i));
+}
+
 // ------------------------------------------------------------------ host helpers
 psgd_status hip_fail(const char* what, hipError_t e) {
   set_error(std::string(what) + ": " + hipGetErrorString(e));
@@ -718,6 +725,28 @@ extern "C" psgd_status psgd_compress_step(psgd_plan* plan, const void* grads, fl
                                           float* p, float* update, void* workspace, void* stream) {
   return run_step("psgd_compress_step", plan, grads, errors, q, p, update, nullptr, nullptr, 0.f, 0.f,
                   workspace, stream, kCompress);
+}
+
+extern "C" psgd_status psgd_stream_copy(const void* src, void* dst, uint64_t bytes, void* stream) {
+  psgd_status s;
+  if ((s = check_ptr("psgd_stream_copy", "src", src, false)) != PSGD_OK) return s;
+  if ((s = check_ptr("psgd_stream_copy", "dst", dst, false)) != PSGD_OK) return s;
+  if (bytes % 16 != 0) {
+    set_error("psgd_stream_copy: bytes must be a multiple of 16");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  if (a < b + bytes && b < a + bytes) {
+    set_error("psgd_stream_copy: src and dst overlap");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (bytes == 0) return PSGD_OK;
+  // 1024 workgroups of 256 threads (4 per CU) grid-striding: the fastest shape found
+  // for a plain copy on the 256-CU device.
+  hipLaunchKernelGGL(k_stream_copy, dim3(1024), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const float*>(src), static_cast<float*>(dst), int64_t(bytes / 16));
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PSGD_OK : hip_fail("launch k_stream_copy", e);
 }
 
 extern "C" psgd_status psgd_plan_reset_carry(psgd_plan* plan) {

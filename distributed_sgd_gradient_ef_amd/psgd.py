@@ -34,7 +34,8 @@ PSGD_FLAG_CARRY_ERROR_MEAN = 0x2
 EXPORTED = [
     "psgd_plan_create", "psgd_plan_sizes", "psgd_plan_layer_info", "psgd_plan_destroy",
     "psgd_compress_step", "psgd_ef_momentum_apply", "psgd_plan_set_timing",
-    "psgd_plan_kernel_stats", "psgd_plan_reset_carry", "psgd_status_string", "psgd_last_error",
+    "psgd_plan_kernel_stats", "psgd_plan_reset_carry", "psgd_stream_copy", "psgd_status_string",
+    "psgd_last_error",
 ]
 
 
@@ -96,7 +97,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.psgd_plan_set_timing.argtypes = [vp, i32]
     lib.psgd_plan_kernel_stats.argtypes = [vp, ctypes.POINTER(_KernelStat), i32, ctypes.POINTER(i32), i32]
     lib.psgd_plan_reset_carry.argtypes = [vp]
-    for name in EXPORTED[:9]:
+    lib.psgd_stream_copy.argtypes = [vp, vp, ctypes.c_uint64, vp]
+    for name in EXPORTED[:10]:
         getattr(lib, name).restype = ctypes.c_int
     lib.psgd_status_string.argtypes = [ctypes.c_int]
     lib.psgd_status_string.restype = ctypes.c_char_p
@@ -184,6 +186,14 @@ def psgd_plan_kernel_stats(plan: Plan, reset: bool = False) -> dict:
 
 def psgd_plan_reset_carry(plan: Plan) -> None:
     _check(load_library().psgd_plan_reset_carry(plan.handle))
+
+
+def psgd_stream_copy(src, dst, nbytes: int, stream=None) -> None:
+    """Calibration copy of `nbytes` from tensor `src` to tensor `dst` (same device)."""
+    import torch
+
+    with torch.cuda.device(src.device):
+        _check(load_library().psgd_stream_copy(_ptr(src), _ptr(dst), int(nbytes), _stream(stream, src)))
 
 
 def _ptr(t) -> Optional[int]:

@@ -200,6 +200,12 @@ psgd_status psgd_plan_kernel_stats(psgd_plan* plan, psgd_kernel_stat* out, int32
  * after writing `errors` or the workspace yourself, e.g. when restoring a checkpoint). */
 psgd_status psgd_plan_reset_carry(psgd_plan* plan);
 
+/* Calibration probe: copy `bytes` (a multiple of 16) from `src` to `dst` on `stream`
+ * with the same non-temporal float4 accesses the streaming passes use.  It measures the
+ * copy bandwidth the device reaches, and gives hardware counters a transfer of known
+ * size to be scaled against.  Device pointers, 16-byte aligned, not overlapping. */
+psgd_status psgd_stream_copy(const void* src, void* dst, uint64_t bytes, void* stream);
+
 /* Static text for a status code. */
 const char* psgd_status_string(psgd_status status);
 

@@ -164,6 +164,14 @@ def test_step_rejects_bad_pointers_before_any_device_call(bad):
     assert _step(None) == psgd.PSGD_ERR_INVALID_ARG
 
 
+def test_stream_copy_validation():
+    lib = psgd.load_library()
+    assert lib.psgd_stream_copy(None, 0x1000, 16, None) == psgd.PSGD_ERR_INVALID_ARG
+    assert lib.psgd_stream_copy(0x1000, 0x2000, 15, None) == psgd.PSGD_ERR_INVALID_ARG
+    assert lib.psgd_stream_copy(0x1000, 0x1010, 64, None) == psgd.PSGD_ERR_INVALID_ARG
+    assert lib.psgd_stream_copy(0x1000, 0x2000, 0, None) == psgd.PSGD_OK
+
+
 def test_momentum_rejects_non_finite_lr():
     lib = psgd.load_library()
     plan = psgd.psgd_plan_create([(64, 64)], 2, 2)

@@ -174,6 +174,17 @@ def test_update_null_and_side_stream(torch_gpu):
     assert torch_gpu.isfinite(run.errors).all().item()
 
 
+def test_stream_copy(torch_gpu):
+    from distributed_sgd_gradient_ef_amd import psgd
+
+    log("[case] stream copy")
+    src = torch_gpu.randn(1 << 20, device="cuda:0")
+    dst = torch_gpu.zeros_like(src)
+    psgd.psgd_stream_copy(src, dst, 4 * src.numel())
+    torch_gpu.cuda.synchronize()
+    assert torch_gpu.equal(src, dst)
+
+
 def test_deterministic(torch_gpu):
     """Same inputs twice give bitwise identical outputs (fixed-order reductions)."""
     log("[case] determinism")
