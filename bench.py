@@ -7,6 +7,12 @@ HBM, fp32.  One step = one psgd_compress_step over all tensors (EF add, P = M Q,
 mean, Gram-Schmidt, Q = M^T P, worker mean, decompress, new errors).  Inputs are
 synthetic (planted low-rank part + worker noise), drawn on the device before timing.
 
+Three plan variants are timed: "deferred" (PSGD_FLAG_DEFERRED_ERROR: one pass over the
+workers' G and E per step; the error buffer holds M_w and the previous step's P Q^T is
+subtracted in the next step's pass), "carry" (PSGD_FLAG_CARRY_ERROR_MEAN: the plain error
+E'_w is written every step, and the next step's first pass reads only G plus the
+carried error mean) and "plain" (no cross-step state).  `value` is the --primary one.
+
 Prints one JSON line:
   value          gradient GB/s = W * numel * 4 bytes / step time (whole job, one GPU)
   pct_hbm_peak   minimal HBM bytes of a step / step time / 8 TB/s
@@ -40,6 +46,10 @@ def kernel_bytes(plan, dtype_bytes: int, carry: bool) -> dict:
     mn, vn = s["matrix_numel"], s["vector_numel"]
     gb = dtype_bytes
     return {
+        # deferred mode: read G_w, E_w, write M_w on every worker and Mbar once
+        "k_ef_defer": (W * (gb + 8) + 4) * mn + (W * gb + 4) * vn,
+        # deferred mode: write U once; 1-D tensors read the mean and write the update
+        "k_update": 4 * mn + 8 * vn,
         # read G_w (and E_w, or the carried error mean once) on every worker, write the
         # mean once; tensors without error: G only
         "k_ef_mean": ((W * gb + 8) if carry else (W * (gb + 4) + 4)) * mn + (W * gb + 4) * vn,
@@ -103,8 +113,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline sample length")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["both", "carry", "plain"], default="both",
+    ap.add_argument("--mode", choices=["all", "carry", "plain", "deferred"], default="all",
                     help="plan variants to time (profiling runs use one)")
+    ap.add_argument("--primary", choices=["carry", "deferred", "plain"], default="deferred",
+                    help="variant reported as `value` when several are timed")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -197,8 +209,11 @@ def main() -> int:
     copy_gbs = 2 * cbytes * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
 
-    plain = measure(0) if args.mode in ("both", "plain") else None
-    main_run = measure(psgd.PSGD_FLAG_CARRY_ERROR_MEAN) if args.mode != "plain" else plain
+    flag_of = {"plain": 0, "carry": psgd.PSGD_FLAG_CARRY_ERROR_MEAN, "deferred": psgd.PSGD_FLAG_DEFERRED_ERROR}
+    names = ["plain", "carry", "deferred"] if args.mode == "all" else [args.mode]
+    results = {n: measure(flag_of[n]) for n in names}
+    primary = args.primary if args.primary in results else names[0]
+    main_run = results[primary]
     kernels, kb, s = main_run["kernels"], main_run["kb"], main_run["sizes"]
     dom = max(kernels, key=lambda k: kernels[k]["mean_us"])
     dom_us = kernels[dom]["mean_us"]
@@ -221,7 +236,8 @@ def main() -> int:
         "config": {"workload": "resnet18_cifar_shapes", "rank": wl.rank, "workers": W,
                    "matrices": s["n_matrices"], "uncompressed_tensors": s["n_vectors"],
                    "params": s["numel"], "grad_bytes_per_step": main_run["grad_bytes"],
-                   "plan_flags": "PSGD_FLAG_CARRY_ERROR_MEAN"},
+                   "plan_flags": {"plain": "0", "carry": "PSGD_FLAG_CARRY_ERROR_MEAN",
+                                  "deferred": "PSGD_FLAG_DEFERRED_ERROR"}[primary]},
         "pct_hbm_peak": round(main_run["pct"], 2),
         "model_bytes_per_step": s["model_bytes"],
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -231,11 +247,10 @@ def main() -> int:
         "ms_per_step_with_kernel_events": round(main_run["ms_timed"], 4),
         "stream_copy_GBps": round(copy_gbs, 1),
     }
-    if args.mode == "plain":
-        out["config"]["plan_flags"] = "0"
-    elif plain is not None:
-        out["without_carry"] = {"value": round(plain["value"], 2), "ms_per_step": round(plain["ms"], 4),
-                                "pct_hbm_peak": round(plain["pct"], 2), "kernels": plain["kernels"]}
+    out["variants"] = {n: {"value": round(r["value"], 2), "ms_per_step": round(r["ms"], 4),
+                           "pct_hbm_peak": round(r["pct"], 2),
+                           "kernels_mean_us": {k: v["mean_us"] for k, v in r["kernels"].items()}}
+                       for n, r in results.items() if n != primary}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -107,6 +107,55 @@ __device__ double block_sum(double v, double* red) {
   return s;
 }
 
+// Two sums over the workgroup in one round of barriers.
+__device__ void block_sum2(double& a, double& b, double* red) {
+  a = wave_sum(a);
+  b = wave_sum(b);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) {
+    red[2 * wave] = a;
+    red[2 * wave + 1] = b;
+  }
+  __syncthreads();
+  double sa = 0.0, sb = 0.0;
+  const int nw = blockDim.x >> 6;
+  for (int i = 0; i < nw; ++i) {
+    sa += red[2 * i];
+    sb += red[2 * i + 1];
+  }
+  a = sa;
+  b = sb;
+}
+
+// u = P Q^T at the four elements of the float4 chunk starting at element c of matrix mi
+// (row-major, rank R <= 4); lanes past `valid` are zero.
+__device__ __forceinline__ f4 lowrank_chunk(const MatInfo& mi, const float* __restrict__ P,
+                                            const float* __restrict__ Q, int64_t c, int64_t valid, int R) {
+  const float* Pm = P + mi.p_off;
+  const float* Qm = Q + mi.q_off;
+  const int cols = mi.cols;
+  const int e0 = int(c - mi.offset);
+  int i = e0 / cols;
+  int j = e0 - i * cols;
+  float u[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float s = 0.f;
+    if (q < valid) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (k < R) s += Pm[int64_t(i) * R + k] * Qm[int64_t(j) * R + k];
+    }
+    u[q] = s;
+    if (++j == cols) {
+      j = 0;
+      ++i;
+    }
+  }
+  return f4{u[0], u[1], u[2], u[3]};
+}
+
 // ------------------------------------------------------------------ pass 1: EF add + mean
 // One float4 chunk per thread, every worker's slice of it loaded before any is used.
 // WT > 0: the worker count is the compile-time WT (loop fully unrolled); WT == 0: any
@@ -217,44 +266,56 @@ __global__ __launch_bounds__(kRowThreads) void k_p_rows(const RowTile* __restric
 // Modified Gram-Schmidt over the R columns of P-bar (rows x R, row-major), in column
 // order.  Dot products and norms accumulate in double.  A column whose residual norm
 // is at most 1e-4 of its norm before orthogonalisation (or zero) becomes zero.
-// Each thread only touches its own rows, so only the reductions synchronise.
+// Each thread only touches its own rows, so only the reductions synchronise; the norm
+// of a fresh column and its projection on column 0 share one reduction (both use the
+// unmodified column).  `P2`, if set, receives a copy of the result.
 template <int R>
 __global__ __launch_bounds__(kMgsThreads) void k_mgs(const MatInfo* __restrict__ mats,
                                                      const float* __restrict__ Pbar,
-                                                     float* __restrict__ P) {
-  __shared__ double red[kMgsThreads / 64];
+                                                     float* __restrict__ P, float* __restrict__ P2) {
+  __shared__ double red[2 * (kMgsThreads / 64)];
   const MatInfo mi = mats[blockIdx.x];
   const float* src = Pbar + mi.p_off;
   float* dst = P + mi.p_off;
   const int n = mi.rows;
   for (int k = 0; k < R; ++k) {
-    double s = 0.0;
+    double s = 0.0, c = 0.0;
     for (int i = threadIdx.x; i < n; i += blockDim.x) {
-      const float v = src[int64_t(i) * R + k];
-      dst[int64_t(i) * R + k] = v;
+      const int64_t o = int64_t(i) * R;
+      const float v = src[o + k];
+      dst[o + k] = v;
       s += double(v) * double(v);
+      if (k > 0) c += double(dst[o]) * double(v);
     }
-    const double before = sqrt(block_sum(s, red));
-    for (int l = 0; l < k; ++l) {
-      double c = 0.0;
-      for (int i = threadIdx.x; i < n; i += blockDim.x)
-        c += double(dst[int64_t(i) * R + l]) * double(dst[int64_t(i) * R + k]);
-      c = block_sum(c, red);
-      for (int i = threadIdx.x; i < n; i += blockDim.x) {
-        const int64_t o = int64_t(i) * R;
-        dst[o + k] = float(double(dst[o + k]) - c * double(dst[o + l]));
+    block_sum2(s, c, red);
+    const double before = sqrt(s);
+    double after = before;
+    if (k > 0) {
+      for (int l = 0; l < k; ++l) {
+        if (l > 0) {
+          c = 0.0;
+          for (int i = threadIdx.x; i < n; i += blockDim.x)
+            c += double(dst[int64_t(i) * R + l]) * double(dst[int64_t(i) * R + k]);
+          c = block_sum(c, red);
+        }
+        for (int i = threadIdx.x; i < n; i += blockDim.x) {
+          const int64_t o = int64_t(i) * R;
+          dst[o + k] = float(double(dst[o + k]) - c * double(dst[o + l]));
+        }
       }
+      double s2 = 0.0;
+      for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        const double v = dst[int64_t(i) * R + k];
+        s2 += v * v;
+      }
+      after = sqrt(block_sum(s2, red));
     }
-    double s2 = 0.0;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-      const double v = dst[int64_t(i) * R + k];
-      s2 += v * v;
-    }
-    const double after = sqrt(block_sum(s2, red));
     const double scale = (after > 0.0 && after > 1e-4 * before) ? 1.0 / after : 0.0;
     for (int i = threadIdx.x; i < n; i += blockDim.x) {
       const int64_t o = int64_t(i) * R + k;
-      dst[o] = float(double(dst[o]) * scale);
+      const float v = float(double(dst[o]) * scale);
+      dst[o] = v;
+      if (P2 != nullptr) P2[mi.p_off + o] = v;
     }
   }
 }
@@ -317,7 +378,8 @@ __global__ __launch_bounds__(kQThreads) void k_q_partial(const QTile* __restrict
 
 __global__ __launch_bounds__(kQRedThreads) void k_q_reduce(const MatInfo* __restrict__ mats,
                                                            const float* __restrict__ Qpart,
-                                                           float* __restrict__ Q, int R) {
+                                                           float* __restrict__ Q, float* __restrict__ Q2,
+                                                           int R) {
   const MatInfo mi = mats[blockIdx.y];
   const int64_t n = int64_t(mi.cols) * R;
   const float* part = Qpart + mi.qpart_off;
@@ -326,6 +388,7 @@ __global__ __launch_bounds__(kQRedThreads) void k_q_reduce(const MatInfo* __rest
     float s = 0.f;
     for (int b = 0; b < mi.nblk; ++b) s += part[int64_t(b) * n + idx];
     Q[mi.q_off + idx] = s;
+    if (Q2 != nullptr) Q2[mi.q_off + idx] = s;
   }
 }
 
@@ -351,29 +414,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_apply(
   if (t.mat < 0) {  // uncompressed tensor: the update is the worker mean
     uv = load4(Mbar + c);
   } else {
-    const MatInfo mi = mats[t.mat];
-    const float* Pm = P + mi.p_off;
-    const float* Qm = Q + mi.q_off;
-    const int cols = mi.cols;
-    const int e0 = int(c - mi.offset);
-    int i = e0 / cols;
-    int j = e0 - i * cols;
-    float u[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float s = 0.f;
-      if (q < valid) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          if (k < R) s += Pm[int64_t(i) * R + k] * Qm[int64_t(j) * R + k];
-      }
-      u[q] = s;
-      if (++j == cols) {
-        j = 0;
-        ++i;
-      }
-    }
-    uv = f4{u[0], u[1], u[2], u[3]};
+    uv = lowrank_chunk(mats[t.mat], P, Q, c, valid, R);
     f4 es = {0.f, 0.f, 0.f, 0.f};
     if constexpr (WT > 0) {
       f4 g[WT], e[WT];
@@ -423,6 +464,161 @@ __global__ __launch_bounds__(kStreamThreads) void k_apply(
   }
 }
 
+// ------------------------------------------------------------------ deferred-error mode
+// The error buffer holds M_w = G_w + E_w of the previous step instead of E'_w; the true
+// error is that minus the previous step's P Q^T (kept in the workspace).  The single
+// pass over the workers then folds the previous subtraction into this step's EF add:
+// M_w(t) = G_w(t) + [M_w(t-1) - U(t-1)], stores M_w(t) back and writes Mbar.
+template <typename GT, int WT>
+__global__ __launch_bounds__(kStreamThreads) void k_ef_defer(
+    const StreamTile* __restrict__ tiles, const MatInfo* __restrict__ mats, const GT* __restrict__ G,
+    float* __restrict__ E, const float* __restrict__ Pprev, const float* __restrict__ Qprev,
+    float* __restrict__ Mbar, int W, int64_t ld, int R, float inv_w, int offset_valid) {
+  const StreamTile t = tiles[blockIdx.x];
+  const int64_t c = t.begin + int64_t(threadIdx.x) * 4;
+  if (c >= t.end) return;
+  const int64_t valid = t.end - c;
+  const int Wn = WT > 0 ? WT : W;
+  f4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (t.mat < 0) {
+    for (int w = 0; w < Wn; ++w) acc += load4_nt(G + w * ld + c);
+    store4(Mbar + c, acc * inv_w, valid);
+    return;
+  }
+  const f4 up = offset_valid ? lowrank_chunk(mats[t.mat], Pprev, Qprev, c, valid, R) : f4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (WT > 0) {
+    f4 g[WT], e[WT];
+#pragma unroll
+    for (int w = 0; w < WT; ++w) {
+      g[w] = load4_nt(G + w * ld + c);
+      e[w] = load4_nt(E + w * ld + c);
+    }
+#pragma unroll
+    for (int w = 0; w < WT; ++w) {
+      const f4 m = (g[w] + e[w]) - up;
+      store4_nt(E + w * ld + c, m, valid);
+      acc += m;
+    }
+  } else {
+    int w = 0;
+    for (; w + 4 <= W; w += 4) {
+      const f4 g0 = load4_nt(G + (w + 0) * ld + c), e0v = load4_nt(E + (w + 0) * ld + c);
+      const f4 g1 = load4_nt(G + (w + 1) * ld + c), e1v = load4_nt(E + (w + 1) * ld + c);
+      const f4 g2 = load4_nt(G + (w + 2) * ld + c), e2v = load4_nt(E + (w + 2) * ld + c);
+      const f4 g3 = load4_nt(G + (w + 3) * ld + c), e3v = load4_nt(E + (w + 3) * ld + c);
+      const f4 m0 = (g0 + e0v) - up, m1 = (g1 + e1v) - up, m2 = (g2 + e2v) - up, m3 = (g3 + e3v) - up;
+      store4_nt(E + (w + 0) * ld + c, m0, valid);
+      store4_nt(E + (w + 1) * ld + c, m1, valid);
+      store4_nt(E + (w + 2) * ld + c, m2, valid);
+      store4_nt(E + (w + 3) * ld + c, m3, valid);
+      acc += m0;
+      acc += m1;
+      acc += m2;
+      acc += m3;
+    }
+    for (; w < W; ++w) {
+      const f4 m = (load4_nt(G + w * ld + c) + load4_nt(E + w * ld + c)) - up;
+      store4_nt(E + w * ld + c, m, valid);
+      acc += m;
+    }
+  }
+  store4(Mbar + c, acc * inv_w, valid);
+}
+
+// Deferred mode's last pass: the decompressed update (P Q^T, or the mean for 1-D
+// tensors) and the momentum-SGD update; no worker data is touched.  Matrix tiles are
+// rows x a column strip: a thread keeps Q of its four columns in registers and walks
+// the rows, reading each row of P once per wave.  The sum order over the rank matches
+// lowrank_chunk, so U here equals the U the next step subtracts.
+__device__ __forceinline__ void momentum_store(float* mom, float* x, int64_t c, const f4 uv, int64_t valid,
+                                               int mode, float lr, float mu) {
+  const f4 m0 = load4_nt(mom + c), x0 = load4_nt(x + c);
+  const f4 m1 = mu * m0 + uv;
+  const f4 x1 = (mode == kNesterov) ? x0 - lr * (uv + mu * m1) : x0 - lr * m1;
+  store4_nt(mom + c, m1, valid);
+  store4_nt(x + c, x1, valid);
+}
+
+__global__ __launch_bounds__(kQThreads) void k_update(
+    const UpdTile* __restrict__ tiles, const MatInfo* __restrict__ mats, const float* __restrict__ Mbar,
+    const float* __restrict__ P, const float* __restrict__ Q, float* __restrict__ update,
+    float* __restrict__ mom, float* __restrict__ x, int R, int mode, float lr, float mu) {
+  const UpdTile t = tiles[blockIdx.x];
+  if (t.mat < 0) {
+    const int64_t c = t.begin + int64_t(threadIdx.x) * 4;
+    if (c >= t.end) return;
+    const int64_t valid = t.end - c;
+    const f4 uv = load4(Mbar + c);
+    if (update != nullptr) store4_nt(update + c, uv, valid);
+    if (mode != kCompress) momentum_store(mom, x, c, uv, valid, mode, lr, mu);
+    return;
+  }
+  const MatInfo mi = mats[t.mat];
+  const int cols = mi.cols;
+  const float* Pm = P + mi.p_off;
+  const float* Qm = Q + mi.q_off;
+  if (mi.vec4) {
+    const int j = t.col_begin + int(threadIdx.x) * 4;
+    if (j >= cols) return;
+    float qv[4][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) qv[q][k] = (k < R) ? Qm[int64_t(j + q) * R + k] : 0.f;
+    for (int i = t.row_begin; i < t.row_end; ++i) {
+      float pr[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) pr[k] = (k < R) ? Pm[int64_t(i) * R + k] : 0.f;
+      float u[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float s = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (k < R) s += pr[k] * qv[q][k];
+        u[q] = s;
+      }
+      const f4 uv = {u[0], u[1], u[2], u[3]};
+      const int64_t c = mi.offset + int64_t(i) * cols + j;
+      if (update != nullptr) store4_nt(update + c, uv, 4);
+      if (mode != kCompress) momentum_store(mom, x, c, uv, 4, mode, lr, mu);
+    }
+  } else {
+    const int j = t.col_begin + int(threadIdx.x);
+    if (j >= cols) return;
+    float qv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) qv[k] = (k < R) ? Qm[int64_t(j) * R + k] : 0.f;
+    for (int i = t.row_begin; i < t.row_end; ++i) {
+      float s = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (k < R) s += Pm[int64_t(i) * R + k] * qv[k];
+      const int64_t c = mi.offset + int64_t(i) * cols + j;
+      if (update != nullptr) update[c] = s;
+      if (mode != kCompress) {
+        const float m1 = mu * mom[c] + s;
+        x[c] = (mode == kNesterov) ? x[c] - lr * (s + mu * m1) : x[c] - lr * m1;
+        mom[c] = m1;
+      }
+    }
+  }
+}
+
+// out_w = errors_w - P_prev Q_prev^T for every compressed matrix (the plain error memory
+// of a deferred-mode error buffer); 1-D tensors are skipped.
+__global__ __launch_bounds__(kStreamThreads) void k_materialize(
+    const StreamTile* __restrict__ tiles, const MatInfo* __restrict__ mats, const float* E,
+    float* out, const float* __restrict__ Pprev, const float* __restrict__ Qprev, int W, int64_t ld,
+    int R, int offset_valid) {
+  const StreamTile t = tiles[blockIdx.x];
+  const int64_t c = t.begin + int64_t(threadIdx.x) * 4;
+  if (c >= t.end || t.mat < 0) return;
+  const int64_t valid = t.end - c;
+  const f4 up = offset_valid ? lowrank_chunk(mats[t.mat], Pprev, Qprev, c, valid, R) : f4{0.f, 0.f, 0.f, 0.f};
+  for (int w = 0; w < W; ++w) store4_nt(out + w * ld + c, load4_nt(E + w * ld + c) - up, valid);
+}
+
 // ------------------------------------------------------------------ calibration copy
 __global__ __launch_bounds__(256) void k_stream_copy(const float* __restrict__ src, float* __restrict__ dst,
                                                      int64_t n4) {
@@ -451,8 +647,9 @@ psgd_status ensure_tables(psgd_plan* plan, DeviceTables** out) {
   const uint64_t b_st = align256(plan->stiles.size() * sizeof(StreamTile) + 1);
   const uint64_t b_rt = align256(plan->rtiles.size() * sizeof(RowTile) + 1);
   const uint64_t b_qt = align256(plan->qtiles.size() * sizeof(QTile) + 1);
+  const uint64_t b_ut = align256(plan->utiles.size() * sizeof(UpdTile) + 1);
   void* base = nullptr;
-  e = hipMalloc(&base, b_mats + b_st + b_rt + b_qt);
+  e = hipMalloc(&base, b_mats + b_st + b_rt + b_qt + b_ut);
   if (e != hipSuccess) {
     set_error(std::string("hipMalloc of the plan's device tables: ") + hipGetErrorString(e));
     return PSGD_ERR_NO_MEMORY;
@@ -464,6 +661,7 @@ psgd_status ensure_tables(psgd_plan* plan, DeviceTables** out) {
   t.stiles = reinterpret_cast<StreamTile*>(b + b_mats);
   t.rtiles = reinterpret_cast<RowTile*>(b + b_mats + b_st);
   t.qtiles = reinterpret_cast<QTile*>(b + b_mats + b_st + b_rt);
+  t.utiles = reinterpret_cast<UpdTile*>(b + b_mats + b_st + b_rt + b_qt);
   struct {
     void* dst;
     const void* src;
@@ -473,6 +671,7 @@ psgd_status ensure_tables(psgd_plan* plan, DeviceTables** out) {
       {t.stiles, plan->stiles.data(), plan->stiles.size() * sizeof(StreamTile)},
       {t.rtiles, plan->rtiles.data(), plan->rtiles.size() * sizeof(RowTile)},
       {t.qtiles, plan->qtiles.data(), plan->qtiles.size() * sizeof(QTile)},
+      {t.utiles, plan->utiles.data(), plan->utiles.size() * sizeof(UpdTile)},
   };
   for (const auto& c : copies) {
     if (c.bytes == 0) continue;
@@ -547,93 +746,116 @@ psgd_status launch_timed(psgd_plan* plan, hipStream_t st, int kid, F&& launch) {
   return PSGD_OK;
 }
 
-// Worker-count specialisations of the streaming passes: W in {1,2,4,8,16} unrolls fully,
-// anything else takes the generic loop.
+// Everything one step's launches need.
+struct StepArgs {
+  const void* grads;
+  float* errors;
+  float* q;
+  float* p;
+  float* update;
+  float* mom;
+  float* x;
+  float lr, mu, inv_w;
+  float* Mbar;
+  float* Pbar;
+  float* Qpart;
+  const float* ebar_in;  // carried error mean to read (carry mode, valid carry)
+  float* ebar_out;       // error mean to write (carry mode)
+  float* Pprev;          // previous P, Q (deferred mode)
+  float* Qprev;
+  int offset_valid;      // deferred mode: errors hold M of the previous step
+  int W, R, mode;
+  int64_t ld;
+  unsigned n_st;
+  hipStream_t st;
+};
+
+enum PassKind { kPassMean = 0, kPassApply = 1, kPassDefer = 2 };
+
 template <typename GT, int WT>
-void launch_stream_pair(bool first, unsigned grid, hipStream_t st, const DeviceTables& dt,
-                        const void* grads, float* errors, const float* ebar_in, float* ebar_out,
-                        float* Mbar, const float* p, const float* q, float* update, float* mom, float* x,
-                        int W, int64_t ld, int R, int mode, float lr, float mu, float inv_w) {
-  if (first)
-    hipLaunchKernelGGL((k_ef_mean<GT, WT>), dim3(grid), dim3(kStreamThreads), 0, st, dt.stiles,
-                       static_cast<const GT*>(grads), errors, ebar_in, Mbar, W, ld, inv_w);
+void launch_pass(int which, const DeviceTables& dt, const StepArgs& a) {
+  const GT* g = static_cast<const GT*>(a.grads);
+  if (which == kPassMean)
+    hipLaunchKernelGGL((k_ef_mean<GT, WT>), dim3(a.n_st), dim3(kStreamThreads), 0, a.st, dt.stiles, g, a.errors,
+                       a.ebar_in, a.Mbar, a.W, a.ld, a.inv_w);
+  else if (which == kPassApply)
+    hipLaunchKernelGGL((k_apply<GT, WT>), dim3(a.n_st), dim3(kStreamThreads), 0, a.st, dt.stiles, dt.mats, g,
+                       a.errors, a.Mbar, a.p, a.q, a.update, a.mom, a.x, a.ebar_out, a.W, a.ld, a.R, a.mode,
+                       a.lr, a.mu, a.inv_w);
   else
-    hipLaunchKernelGGL((k_apply<GT, WT>), dim3(grid), dim3(kStreamThreads), 0, st, dt.stiles, dt.mats,
-                       static_cast<const GT*>(grads), errors, Mbar, p, q, update, mom, x, ebar_out, W, ld,
-                       R, mode, lr, mu, inv_w);
+    hipLaunchKernelGGL((k_ef_defer<GT, WT>), dim3(a.n_st), dim3(kStreamThreads), 0, a.st, dt.stiles, dt.mats,
+                       g, a.errors, a.Pprev, a.Qprev, a.Mbar, a.W, a.ld, a.R, a.inv_w, a.offset_valid);
 }
 
+// Worker-count specialisations of the streaming passes: W in {1,2,4,8,16} unrolls fully,
+// anything else takes the generic loop.
 template <typename GT>
-void launch_stream(bool first, unsigned grid, hipStream_t st, const DeviceTables& dt, const void* grads,
-                   float* errors, const float* ebar_in, float* ebar_out, float* Mbar, const float* p,
-                   const float* q, float* update, float* mom, float* x, int W, int64_t ld, int R, int mode,
-                   float lr, float mu, float inv_w) {
-#define PSGD_STREAM(WT)                                                                              \
-  launch_stream_pair<GT, WT>(first, grid, st, dt, grads, errors, ebar_in, ebar_out, Mbar, p, q, update, \
-                             mom, x, W, ld, R, mode, lr, mu, inv_w)
-  switch (W) {
-    case 1: PSGD_STREAM(1); break;
-    case 2: PSGD_STREAM(2); break;
-    case 4: PSGD_STREAM(4); break;
-    case 8: PSGD_STREAM(8); break;
-    case 16: PSGD_STREAM(16); break;
-    default: PSGD_STREAM(0); break;
+void launch_pass_w(int which, const DeviceTables& dt, const StepArgs& a) {
+  switch (a.W) {
+    case 1: launch_pass<GT, 1>(which, dt, a); break;
+    case 2: launch_pass<GT, 2>(which, dt, a); break;
+    case 4: launch_pass<GT, 4>(which, dt, a); break;
+    case 8: launch_pass<GT, 8>(which, dt, a); break;
+    case 16: launch_pass<GT, 16>(which, dt, a); break;
+    default: launch_pass<GT, 0>(which, dt, a); break;
   }
-#undef PSGD_STREAM
 }
 
 template <int R>
-psgd_status launch_all(psgd_plan* plan, const DeviceTables& dt, const void* grads, float* errors,
-                       float* q, float* p, float* update, float* mom, float* x, float lr, float mu,
-                       char* ws, bool use_carry, hipStream_t stream, int mode) {
-  const int W = plan->n_workers;
-  const int64_t ld = plan->worker_stride;
-  float* Mbar = reinterpret_cast<float*>(ws + plan->ws_mbar);
-  float* Pbar = reinterpret_cast<float*>(ws + plan->ws_pbar);
-  float* Qpart = reinterpret_cast<float*>(ws + plan->ws_qpart);
-  float* ebar = (plan->flags & PSGD_FLAG_CARRY_ERROR_MEAN) ? reinterpret_cast<float*>(ws + plan->ws_ebar)
-                                                           : nullptr;
-  const float* ebar_in = use_carry ? ebar : nullptr;
-  const unsigned n_st = unsigned(plan->stiles.size());
-  const unsigned n_mats = unsigned(plan->mats.size());
+psgd_status launch_all(psgd_plan* plan, const DeviceTables& dt, const StepArgs& a) {
+  const bool deferred = (plan->flags & PSGD_FLAG_DEFERRED_ERROR) != 0;
   const bool bf = plan->dtype == PSGD_BF16;
-  const float inv_w = 1.0f / float(W);
+  const unsigned n_mats = unsigned(plan->mats.size());
+  hipStream_t stream = a.st;
   psgd_status s;
-
-  auto stream_pass = [&](bool first) {
+  auto pass = [&](int which) {
     if (bf)
-      launch_stream<bf16>(first, n_st, stream, dt, grads, errors, ebar_in, ebar, Mbar, p, q, update, mom, x,
-                          W, ld, R, mode, lr, mu, inv_w);
+      launch_pass_w<bf16>(which, dt, a);
     else
-      launch_stream<float>(first, n_st, stream, dt, grads, errors, ebar_in, ebar, Mbar, p, q, update, mom,
-                           x, W, ld, R, mode, lr, mu, inv_w);
+      launch_pass_w<float>(which, dt, a);
   };
 
-  s = launch_timed(plan, stream, kKEfMean, [&] { stream_pass(true); });
+  if (deferred)
+    s = launch_timed(plan, stream, kKEfDefer, [&] { pass(kPassDefer); });
+  else
+    s = launch_timed(plan, stream, kKEfMean, [&] { pass(kPassMean); });
   if (s != PSGD_OK) return s;
 
   if (n_mats > 0) {
     s = launch_timed(plan, stream, kKPRows, [&] {
       hipLaunchKernelGGL(k_p_rows<R>, dim3(unsigned(plan->rtiles.size())), dim3(kRowThreads), 0, stream,
-                         dt.rtiles, dt.mats, Mbar, q, Pbar);
+                         dt.rtiles, dt.mats, a.Mbar, a.q, a.Pbar);
     });
     if (s != PSGD_OK) return s;
     s = launch_timed(plan, stream, kKMgs, [&] {
-      hipLaunchKernelGGL(k_mgs<R>, dim3(n_mats), dim3(kMgsThreads), 0, stream, dt.mats, Pbar, p);
+      hipLaunchKernelGGL(k_mgs<R>, dim3(n_mats), dim3(plan->mgs_threads), 0, stream, dt.mats, a.Pbar, a.p,
+                         deferred ? a.Pprev : nullptr);
     });
     if (s != PSGD_OK) return s;
     s = launch_timed(plan, stream, kKQPartial, [&] {
       hipLaunchKernelGGL(k_q_partial<R>, dim3(unsigned(plan->qtiles.size())), dim3(kQThreads), 0, stream,
-                         dt.qtiles, dt.mats, Mbar, p, Qpart);
+                         dt.qtiles, dt.mats, a.Mbar, a.p, a.Qpart);
     });
     if (s != PSGD_OK) return s;
     const unsigned gx = unsigned((plan->max_q_elems_per_matrix + kQRedThreads - 1) / kQRedThreads);
     s = launch_timed(plan, stream, kKQReduce, [&] {
-      hipLaunchKernelGGL(k_q_reduce, dim3(gx, n_mats), dim3(kQRedThreads), 0, stream, dt.mats, Qpart, q, R);
+      hipLaunchKernelGGL(k_q_reduce, dim3(gx, n_mats), dim3(kQRedThreads), 0, stream, dt.mats, a.Qpart, a.q,
+                         deferred ? a.Qprev : nullptr, R);
     });
     if (s != PSGD_OK) return s;
   }
-  return launch_timed(plan, stream, kKApply, [&] { stream_pass(false); });
+  if (deferred)
+    return launch_timed(plan, stream, kKUpdate, [&] {
+      hipLaunchKernelGGL(k_update, dim3(unsigned(plan->utiles.size())), dim3(kQThreads), 0, stream, dt.utiles,
+                         dt.mats, a.Mbar, a.p, a.q, a.update, a.mom, a.x, R, a.mode, a.lr, a.mu);
+    });
+  return launch_timed(plan, stream, kKApply, [&] { pass(kPassApply); });
+}
+
+// Same device, same error and workspace buffers as the step that left the state.
+bool state_matches(const psgd_plan* plan, const void* errors, const void* workspace, int dev) {
+  return plan->state_valid && plan->state_errors == errors && plan->state_workspace == workspace &&
+         plan->state_device == dev;
 }
 
 psgd_status run_step(const char* fn, psgd_plan* plan, const void* grads, float* errors, float* q,
@@ -678,10 +900,10 @@ psgd_status run_step(const char* fn, psgd_plan* plan, const void* grads, float* 
     add("momentum", mom, ld * 4);
     add("params", x, ld * 4);
   }
-  for (int a = 0; a < nr; ++a)
-    for (int b = a + 1; b < nr; ++b)
-      if (rs[a].lo < rs[b].hi && rs[b].lo < rs[a].hi) {
-        set_error(std::string(fn) + ": buffers " + rs[a].name + " and " + rs[b].name + " overlap");
+  for (int i = 0; i < nr; ++i)
+    for (int j = i + 1; j < nr; ++j)
+      if (rs[i].lo < rs[j].hi && rs[j].lo < rs[i].hi) {
+        set_error(std::string(fn) + ": buffers " + rs[i].name + " and " + rs[j].name + " overlap");
         return PSGD_ERR_INVALID_ARG;
       }
 
@@ -689,30 +911,55 @@ psgd_status run_step(const char* fn, psgd_plan* plan, const void* grads, float* 
   if ((s = ensure_tables(plan, &dt)) != PSGD_OK) return s;
   int dev = 0;
   (void)hipGetDevice(&dev);
-  hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  // The carried error mean is used only if the previous step of this plan ran on the
-  // same device with the same error and workspace buffers.
   const bool carry = (plan->flags & PSGD_FLAG_CARRY_ERROR_MEAN) != 0;
-  const bool use_carry = carry && plan->carry_valid && plan->carry_errors == errors &&
-                         plan->carry_workspace == workspace && plan->carry_device == dev;
-  plan->carry_valid = false;
+  const bool deferred = (plan->flags & PSGD_FLAG_DEFERRED_ERROR) != 0;
+  // Cross-step state (carried error mean, or the deferred offset) is used only if the
+  // previous step of this plan left it on this device in these error/workspace buffers.
+  const bool use_state = (carry || deferred) && state_matches(plan, errors, workspace, dev);
+  plan->state_valid = false;
+
+  StepArgs a{};
+  a.grads = grads;
+  a.errors = errors;
+  a.q = q;
+  a.p = p;
+  a.update = update;
+  a.mom = mom;
+  a.x = x;
+  a.lr = lr;
+  a.mu = mu;
+  a.inv_w = 1.0f / float(plan->n_workers);
+  a.Mbar = reinterpret_cast<float*>(ws + plan->ws_mbar);
+  a.Pbar = reinterpret_cast<float*>(ws + plan->ws_pbar);
+  a.Qpart = reinterpret_cast<float*>(ws + plan->ws_qpart);
+  a.ebar_out = carry ? reinterpret_cast<float*>(ws + plan->ws_ebar) : nullptr;
+  a.ebar_in = (carry && use_state) ? a.ebar_out : nullptr;
+  a.Pprev = deferred ? reinterpret_cast<float*>(ws + plan->ws_pprev) : nullptr;
+  a.Qprev = deferred ? reinterpret_cast<float*>(ws + plan->ws_qprev) : nullptr;
+  a.offset_valid = (deferred && use_state) ? 1 : 0;
+  a.W = plan->n_workers;
+  a.R = plan->rank;
+  a.mode = mode;
+  a.ld = plan->worker_stride;
+  a.n_st = unsigned(plan->stiles.size());
+  a.st = static_cast<hipStream_t>(stream);
   switch (plan->rank) {
-    case 1: s = launch_all<1>(plan, *dt, grads, errors, q, p, update, mom, x, lr, mu, ws, use_carry, st, mode); break;
-    case 2: s = launch_all<2>(plan, *dt, grads, errors, q, p, update, mom, x, lr, mu, ws, use_carry, st, mode); break;
-    case 3: s = launch_all<3>(plan, *dt, grads, errors, q, p, update, mom, x, lr, mu, ws, use_carry, st, mode); break;
-    case 4: s = launch_all<4>(plan, *dt, grads, errors, q, p, update, mom, x, lr, mu, ws, use_carry, st, mode); break;
+    case 1: s = launch_all<1>(plan, *dt, a); break;
+    case 2: s = launch_all<2>(plan, *dt, a); break;
+    case 3: s = launch_all<3>(plan, *dt, a); break;
+    case 4: s = launch_all<4>(plan, *dt, a); break;
     default:
       set_error(std::string(fn) + ": rank outside 1..4");
       return PSGD_ERR_UNSUPPORTED;
   }
-  if (s == PSGD_OK && carry && has_mats) {
-    plan->carry_valid = true;
-    plan->carry_errors = errors;
-    plan->carry_workspace = workspace;
-    plan->carry_device = dev;
+  if (s == PSGD_OK && (carry || deferred) && has_mats) {
+    plan->state_valid = true;
+    plan->state_errors = errors;
+    plan->state_workspace = workspace;
+    plan->state_device = dev;
   }
-  plan->last_step_carried = use_carry;
+  plan->last_step_used_state = use_state;
   return s;
 }
 
@@ -754,7 +1001,44 @@ extern "C" psgd_status psgd_plan_reset_carry(psgd_plan* plan) {
     set_error("psgd_plan_reset_carry: plan is NULL");
     return PSGD_ERR_INVALID_ARG;
   }
-  plan->carry_valid = false;
+  plan->state_valid = false;
+  return PSGD_OK;
+}
+
+extern "C" psgd_status psgd_errors_materialize(psgd_plan* plan, const float* errors, float* out,
+                                               void* workspace, void* stream) {
+  const char* fn = "psgd_errors_materialize";
+  if (plan == nullptr) {
+    set_error(std::string(fn) + ": plan is NULL");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  psgd_status s;
+  if ((s = check_ptr(fn, "errors", errors, false)) != PSGD_OK) return s;
+  if ((s = check_ptr(fn, "out", out, false)) != PSGD_OK) return s;
+  if ((s = check_ptr(fn, "workspace", workspace, false)) != PSGD_OK) return s;
+  const uint64_t bytes = uint64_t(plan->n_workers) * uint64_t(plan->worker_stride) * 4;
+  const uintptr_t e0 = reinterpret_cast<uintptr_t>(errors), o0 = reinterpret_cast<uintptr_t>(out);
+  if (out != errors && e0 < o0 + bytes && o0 < e0 + bytes) {
+    set_error(std::string(fn) + ": out partly overlaps errors (pass the same pointer for in place)");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (plan->mats.empty()) return PSGD_OK;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  const bool deferred = (plan->flags & PSGD_FLAG_DEFERRED_ERROR) != 0;
+  const bool offset = deferred && state_matches(plan, errors, workspace, dev);
+  if (!offset && out == errors) return PSGD_OK;  // already plain, nothing to write
+  DeviceTables* dt = nullptr;
+  if ((s = ensure_tables(plan, &dt)) != PSGD_OK) return s;
+  char* ws = static_cast<char*>(workspace);
+  const float* Pprev = deferred ? reinterpret_cast<const float*>(ws + plan->ws_pprev) : nullptr;
+  const float* Qprev = deferred ? reinterpret_cast<const float*>(ws + plan->ws_qprev) : nullptr;
+  hipLaunchKernelGGL(k_materialize, dim3(unsigned(plan->stiles.size())), dim3(kStreamThreads), 0,
+                     static_cast<hipStream_t>(stream), dt->stiles, dt->mats, errors, out, Pprev, Qprev,
+                     plan->n_workers, plan->worker_stride, plan->rank, offset ? 1 : 0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail("launch k_materialize", e);
+  if (offset && out == errors) plan->state_valid = false;  // the buffer now holds plain errors
   return PSGD_OK;
 }
 

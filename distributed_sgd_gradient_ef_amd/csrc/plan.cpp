@@ -16,8 +16,8 @@ namespace psgd {
 
 static thread_local std::string g_last_error;
 
-const char* const kKernelNames[kNumKernels] = {"k_ef_mean", "k_p_rows", "k_mgs",
-                                               "k_q_partial", "k_q_reduce", "k_apply"};
+const char* const kKernelNames[kNumKernels] = {"k_ef_mean", "k_p_rows",   "k_mgs",      "k_q_partial",
+                                               "k_q_reduce", "k_apply",    "k_ef_defer", "k_update"};
 
 void set_error(const std::string& msg) { g_last_error = msg; }
 
@@ -64,8 +64,10 @@ extern "C" psgd_status psgd_plan_create(const psgd_layer* layers, int32_t n_laye
     return fail(PSGD_ERR_INVALID_ARG, "psgd_plan_create: n_workers must be in 1..65536");
   if (grad_dtype != PSGD_F32 && grad_dtype != PSGD_BF16)
     return fail(PSGD_ERR_UNSUPPORTED, "psgd_plan_create: unknown gradient dtype");
-  if (flags & ~uint32_t(PSGD_FLAG_NESTEROV | PSGD_FLAG_CARRY_ERROR_MEAN))
+  if (flags & ~uint32_t(PSGD_FLAG_NESTEROV | PSGD_FLAG_CARRY_ERROR_MEAN | PSGD_FLAG_DEFERRED_ERROR))
     return fail(PSGD_ERR_UNSUPPORTED, "psgd_plan_create: unknown flag bits");
+  if ((flags & PSGD_FLAG_CARRY_ERROR_MEAN) && (flags & PSGD_FLAG_DEFERRED_ERROR))
+    return fail(PSGD_ERR_UNSUPPORTED, "psgd_plan_create: PSGD_FLAG_CARRY_ERROR_MEAN and PSGD_FLAG_DEFERRED_ERROR exclude each other");
 
   psgd_plan* plan = new (std::nothrow) psgd_plan();
   if (plan == nullptr) return fail(PSGD_ERR_NO_MEMORY, "psgd_plan_create: out of host memory");
@@ -142,6 +144,30 @@ extern "C" psgd_status psgd_plan_create(const psgd_layer* layers, int32_t n_laye
         plan->stiles.push_back(t);
       }
     }
+    for (const psgd_layer_info& li : plan->layers) {
+      if (li.compressed) {
+        const MatInfo& m = plan->mats[size_t(li.matrix_index)];
+        const int32_t strip = kQThreads * (m.vec4 ? 4 : 1);
+        for (int32_t r0 = 0; r0 < m.rows; r0 += kUpdRowsPerTile)
+          for (int32_t c0 = 0; c0 < m.cols; c0 += strip) {
+            UpdTile u{};
+            u.mat = li.matrix_index;
+            u.row_begin = r0;
+            u.row_end = std::min(m.rows, r0 + kUpdRowsPerTile);
+            u.col_begin = c0;
+            plan->utiles.push_back(u);
+          }
+      } else {
+        const int64_t end = li.offset + li.rows * li.cols;
+        for (int64_t b = li.offset; b < end; b += kStreamTileElems) {
+          UpdTile u{};
+          u.begin = b;
+          u.end = std::min<int64_t>(end, b + kStreamTileElems);
+          u.mat = -1;
+          plan->utiles.push_back(u);
+        }
+      }
+    }
     for (size_t mi = 0; mi < plan->mats.size(); ++mi) {
       const MatInfo& m = plan->mats[mi];
       for (int32_t rb = 0; rb < m.rows; rb += kRowsPerTile)
@@ -162,7 +188,14 @@ extern "C" psgd_status psgd_plan_create(const psgd_layer* layers, int32_t n_laye
     ws += uint64_t(round_up(std::max<int64_t>(plan->qpart_elems, 1) * 4, 256));
     plan->ws_ebar = ws;
     if (flags & PSGD_FLAG_CARRY_ERROR_MEAN) ws += uint64_t(round_up(plan->worker_stride * 4, 256));
+    plan->ws_pprev = ws;
+    if (flags & PSGD_FLAG_DEFERRED_ERROR) ws += uint64_t(round_up(std::max<int64_t>(plan->p_elems, 1) * 4, 256));
+    plan->ws_qprev = ws;
+    if (flags & PSGD_FLAG_DEFERRED_ERROR) ws += uint64_t(round_up(std::max<int64_t>(plan->q_elems, 1) * 4, 256));
     plan->workspace_bytes = ws;
+    int32_t max_rows = 1;
+    for (const MatInfo& m : plan->mats) max_rows = std::max(max_rows, m.rows);
+    plan->mgs_threads = int32_t(std::min<int64_t>(kMgsThreads, round_up(max_rows, 64)));
 
     const uint64_t W = uint64_t(n_workers);
     const uint64_t gb = grad_dtype == PSGD_BF16 ? 2 : 4;

@@ -22,7 +22,7 @@ constexpr int kStreamTileElems = kStreamThreads * 4;
 
 // P = Mbar Q: one workgroup of kRowThreads handles kRowsPerTile rows; one wave per row.
 constexpr int kRowThreads = 256;
-constexpr int kRowsPerTile = 16;
+constexpr int kRowsPerTile = 4;
 
 // Q partials = Mbar^T P over a block of rows and a strip of columns.
 constexpr int kQThreads = 256;
@@ -62,17 +62,27 @@ struct QTile {
   int32_t mat, blk, col_begin, col_end;
 };
 
+// Update pass tiles: for a compressed matrix, rows [row_begin, row_end) x a strip of
+// kQThreads*4 (cols % 4 == 0) or kQThreads columns from col_begin; for an uncompressed
+// tensor (mat < 0), the flat element range [begin, end) as in a StreamTile.
+struct UpdTile {
+  int64_t begin, end;
+  int32_t mat, row_begin, row_end, col_begin;
+};
+constexpr int kUpdRowsPerTile = 8;
+
 struct DeviceTables {
   void* base = nullptr;
   MatInfo* mats = nullptr;
   StreamTile* stiles = nullptr;
   RowTile* rtiles = nullptr;
   QTile* qtiles = nullptr;
+  UpdTile* utiles = nullptr;
 };
 
 void set_error(const std::string& msg);
 
-enum KernelId { kKEfMean = 0, kKPRows, kKMgs, kKQPartial, kKQReduce, kKApply, kNumKernels };
+enum KernelId { kKEfMean = 0, kKPRows, kKMgs, kKQPartial, kKQReduce, kKApply, kKEfDefer, kKUpdate, kNumKernels };
 extern const char* const kKernelNames[kNumKernels];
 
 struct PendingTiming {
@@ -97,18 +107,21 @@ struct psgd_plan {
   std::vector<psgd::StreamTile> stiles;
   std::vector<psgd::RowTile> rtiles;
   std::vector<psgd::QTile> qtiles;
+  std::vector<psgd::UpdTile> utiles;
   int64_t worker_stride = 0, numel = 0, matrix_numel = 0, vector_numel = 0;
   int64_t p_elems = 0, q_elems = 0, qpart_elems = 0;
   int64_t max_q_elems_per_matrix = 0;
-  uint64_t ws_mbar = 0, ws_pbar = 0, ws_qpart = 0, ws_ebar = 0, workspace_bytes = 0;
+  uint64_t ws_mbar = 0, ws_pbar = 0, ws_qpart = 0, ws_ebar = 0, ws_pprev = 0, ws_qprev = 0, workspace_bytes = 0;
+  int32_t mgs_threads = 64;  // Gram-Schmidt block size: enough for the tallest matrix, <= kMgsThreads
   uint64_t message_bytes = 0, model_bytes = 0, model_bytes_momentum = 0;
   std::map<int, psgd::DeviceTables> dev;  // per HIP device id
-  // carried worker mean of the errors (PSGD_FLAG_CARRY_ERROR_MEAN)
-  bool carry_valid = false;
-  bool last_step_carried = false;
-  const void* carry_errors = nullptr;
-  const void* carry_workspace = nullptr;
-  int carry_device = -1;
+  // cross-step state: the carried error mean (PSGD_FLAG_CARRY_ERROR_MEAN) or the deferred
+  // offset (PSGD_FLAG_DEFERRED_ERROR), valid for these error/workspace buffers on this device
+  bool state_valid = false;
+  bool last_step_used_state = false;
+  const void* state_errors = nullptr;
+  const void* state_workspace = nullptr;
+  int state_device = -1;
   // kernel timing (psgd_plan_set_timing)
   bool timing = false;
   std::vector<psgd::PendingTiming> pending;

@@ -30,12 +30,13 @@ PSGD_F32 = 0
 PSGD_BF16 = 1
 PSGD_FLAG_NESTEROV = 0x1
 PSGD_FLAG_CARRY_ERROR_MEAN = 0x2
+PSGD_FLAG_DEFERRED_ERROR = 0x4
 
 EXPORTED = [
     "psgd_plan_create", "psgd_plan_sizes", "psgd_plan_layer_info", "psgd_plan_destroy",
     "psgd_compress_step", "psgd_ef_momentum_apply", "psgd_plan_set_timing",
-    "psgd_plan_kernel_stats", "psgd_plan_reset_carry", "psgd_stream_copy", "psgd_status_string",
-    "psgd_last_error",
+    "psgd_plan_kernel_stats", "psgd_plan_reset_carry", "psgd_errors_materialize", "psgd_stream_copy",
+    "psgd_status_string", "psgd_last_error",
 ]
 
 
@@ -98,7 +99,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.psgd_plan_kernel_stats.argtypes = [vp, ctypes.POINTER(_KernelStat), i32, ctypes.POINTER(i32), i32]
     lib.psgd_plan_reset_carry.argtypes = [vp]
     lib.psgd_stream_copy.argtypes = [vp, vp, ctypes.c_uint64, vp]
-    for name in EXPORTED[:10]:
+    lib.psgd_errors_materialize.argtypes = [vp, vp, vp, vp, vp]
+    for name in EXPORTED[:11]:
         getattr(lib, name).restype = ctypes.c_int
     lib.psgd_status_string.argtypes = [ctypes.c_int]
     lib.psgd_status_string.restype = ctypes.c_char_p
@@ -186,6 +188,15 @@ def psgd_plan_kernel_stats(plan: Plan, reset: bool = False) -> dict:
 
 def psgd_plan_reset_carry(plan: Plan) -> None:
     _check(load_library().psgd_plan_reset_carry(plan.handle))
+
+
+def psgd_errors_materialize(plan: Plan, errors, out, workspace, stream=None) -> None:
+    """Plain error memory of a deferred-mode error buffer into `out` (may be `errors`)."""
+    import torch
+
+    with torch.cuda.device(errors.device):
+        _check(load_library().psgd_errors_materialize(plan.handle, _ptr(errors), _ptr(out), _ptr(workspace),
+                                                      _stream(stream, errors)))
 
 
 def psgd_stream_copy(src, dst, nbytes: int, stream=None) -> None:

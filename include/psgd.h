@@ -95,6 +95,18 @@ typedef enum psgd_dtype {
  * sees other errors/workspace pointers or another device than the previous step; a
  * failed step also forces the fallback.  The workspace grows by worker_stride floats. */
 #define PSGD_FLAG_CARRY_ERROR_MEAN 0x2u
+/* Deferred error subtraction.  The step reads every worker's G and E once: the error
+ * buffer keeps M_w = G_w + E_w of the step that wrote it (the error before subtracting
+ * that step's decompressed update U), and the next step subtracts U while it adds the
+ * new gradient.  A step then moves 12W + 4 bytes per element in its worker pass instead
+ * of two passes over G.  The update, P and Q outputs are unchanged; only the error
+ * buffer's representation differs: after a step, errors_w - P Q^T (P and Q of that step,
+ * kept in the workspace) is the plain error memory E'_w, and psgd_errors_materialize
+ * writes it out.  Contract and fallback as for PSGD_FLAG_CARRY_ERROR_MEAN: the same
+ * errors and workspace pointers, unmodified, between steps (psgd_plan_reset_carry
+ * declares that `errors` now holds plain errors).  Excludes
+ * PSGD_FLAG_CARRY_ERROR_MEAN.  The workspace grows by p_elems + q_elems floats. */
+#define PSGD_FLAG_DEFERRED_ERROR 0x4u
 
 /* One tensor of the layer list.  rows == 1 or cols == 1 marks a 1-D tensor. */
 typedef struct psgd_layer {
@@ -179,7 +191,8 @@ psgd_status psgd_ef_momentum_apply(psgd_plan* plan, const void* grads, float* er
  * kernel a step launches is bracketed by two HIP events recorded on the launch stream;
  * psgd_plan_kernel_stats waits for the recorded events and accumulates their elapsed
  * times per kernel.  Timing adds two event records per launch.  Kernel names:
- * "k_ef_mean", "k_p_rows", "k_mgs", "k_q_partial", "k_q_reduce", "k_apply". */
+ * "k_ef_mean", "k_p_rows", "k_mgs", "k_q_partial", "k_q_reduce", "k_apply", and in the
+ * deferred mode "k_ef_defer" and "k_update" in place of "k_ef_mean" and "k_apply". */
 typedef struct psgd_kernel_stat {
   char name[32];    /* kernel name */
   int64_t launches; /* launches timed since the last reset */
@@ -196,9 +209,20 @@ psgd_status psgd_plan_set_timing(psgd_plan* plan, int32_t enable);
 psgd_status psgd_plan_kernel_stats(psgd_plan* plan, psgd_kernel_stat* out, int32_t capacity,
                                    int32_t* count, int32_t reset);
 
-/* Make the next step of a PSGD_FLAG_CARRY_ERROR_MEAN plan read all errors again (call
- * after writing `errors` or the workspace yourself, e.g. when restoring a checkpoint). */
+/* Forget the plan's cross-step state: the next step of a PSGD_FLAG_CARRY_ERROR_MEAN
+ * plan reads all errors again, and the next step of a PSGD_FLAG_DEFERRED_ERROR plan
+ * treats `errors` as plain errors.  Call it after writing `errors` or the workspace
+ * yourself, e.g. when restoring a checkpoint. */
 psgd_status psgd_plan_reset_carry(psgd_plan* plan);
+
+/* Write the plain error memory of every compressed matrix to `out` ([n_workers]
+ * [worker_stride] float32): for a PSGD_FLAG_DEFERRED_ERROR plan whose last step left
+ * `errors` and `workspace` in the deferred form, out_w = errors_w - P Q^T of that step;
+ * otherwise out_w = errors_w.  `out` may be `errors` (in place; the plan then treats the
+ * buffer as plain) or a separate buffer (the plan's state is kept).  Elements of 1-D
+ * tensors and padding are not written.  Asynchronous on `stream`. */
+psgd_status psgd_errors_materialize(psgd_plan* plan, const float* errors, float* out, void* workspace,
+                                    void* stream);
 
 /* Calibration probe: copy `bytes` (a multiple of 16) from `src` to `dst` on `stream`
  * with the same non-temporal float4 accesses the streaming passes use.  It measures the

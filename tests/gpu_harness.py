@@ -105,10 +105,18 @@ class DeviceRun:
         n = L.rows * L.cols
         return self.grads[:, L.offset:L.offset + n].float().cpu().numpy().reshape(self.W, L.rows, L.cols)
 
-    def errors_layer(self, li: int) -> np.ndarray:
+    def errors_layer(self, li: int, source=None) -> np.ndarray:
         L = self.plan.layers[li]
         n = L.rows * L.cols
-        return self.errors[:, L.offset:L.offset + n].cpu().numpy().reshape(self.W, L.rows, L.cols)
+        t = self.errors if source is None else source
+        return t[:, L.offset:L.offset + n].cpu().numpy().reshape(self.W, L.rows, L.cols)
+
+    def plain_errors(self):
+        """The plain error memory (materialised for a deferred-mode plan) in a new buffer."""
+        out = self.torch.zeros_like(self.errors)
+        psgd.psgd_errors_materialize(self.plan, self.errors, out, self.workspace)
+        self.torch.cuda.synchronize(self.dev)
+        return out
 
     def vec_layer(self, t, li: int) -> np.ndarray:
         L = self.plan.layers[li]
@@ -133,19 +141,19 @@ class LayerSnapshot:
     q: Optional[np.ndarray]
 
 
-def snapshot(run: DeviceRun, layers: Sequence[int]) -> Dict[int, LayerSnapshot]:
+def snapshot(run: DeviceRun, layers: Sequence[int], errors_source=None) -> Dict[int, LayerSnapshot]:
     run.torch.cuda.synchronize(run.dev)
     out = {}
     for li in layers:
         L = run.plan.layers[li]
         g = run.grads_layer(li)
-        e = run.errors_layer(li) if L.compressed else np.zeros_like(g)
+        e = run.errors_layer(li, errors_source) if L.compressed else np.zeros_like(g)
         out[li] = LayerSnapshot(g, e, run.q_layer(li) if L.compressed else None)
     return out
 
 
 def compare_step(run: DeviceRun, snap: Dict[int, LayerSnapshot], oracle_mod, tol: float,
-                 check_p: bool = True, what: str = "") -> Dict[str, float]:
+                 check_p: bool = True, what: str = "", errors_source=None) -> Dict[str, float]:
     """Run the oracle on the snapshot and compare with the GPU outputs of the step that
     followed it.  Returns the worst relative error per output kind; asserts <= tol."""
     run.torch.cuda.synchronize(run.dev)
@@ -165,7 +173,7 @@ def compare_step(run: DeviceRun, snap: Dict[int, LayerSnapshot], oracle_mod, tol
             "q": rel(run.q_layer(li), ref.q_bar, mbar),
             "u": rel(run.vec_layer(run.update, li), ref.update, mbar),
         }
-        e_gpu = run.errors_layer(li)
+        e_gpu = run.errors_layer(li, errors_source)
         errs["e"] = max(rel(e_gpu[w], ref.errors[w], mbar) for w in range(run.W))
         for k, v in errs.items():
             worst[k] = max(worst[k], v)

@@ -131,6 +131,21 @@ def test_carry_flag_grows_workspace_by_one_slice():
     assert psgd.load_library().psgd_plan_reset_carry(None) == psgd.PSGD_ERR_INVALID_ARG
 
 
+def test_deferred_flag_rules():
+    shapes = [(64, 64), (1, 5)]
+    assert _create(shapes, flags=psgd.PSGD_FLAG_DEFERRED_ERROR) == psgd.PSGD_OK
+    assert _create(shapes, flags=psgd.PSGD_FLAG_DEFERRED_ERROR | psgd.PSGD_FLAG_CARRY_ERROR_MEAN) == \
+        psgd.PSGD_ERR_UNSUPPORTED
+    a = psgd.psgd_plan_create(shapes, 2, 4).sizes
+    b = psgd.psgd_plan_create(shapes, 2, 4, flags=psgd.PSGD_FLAG_DEFERRED_ERROR).sizes
+    assert b["workspace_bytes"] - a["workspace_bytes"] == 2 * 512  # P (64x2) and Q (64x2), 256-B rounded
+    lib = psgd.load_library()
+    plan = psgd.psgd_plan_create(shapes, 2, 4, flags=psgd.PSGD_FLAG_DEFERRED_ERROR)
+    assert lib.psgd_errors_materialize(None, 0x1000, 0x1000, 0x2000, None) == psgd.PSGD_ERR_INVALID_ARG
+    assert lib.psgd_errors_materialize(plan.handle, None, 0x1000, 0x2000, None) == psgd.PSGD_ERR_INVALID_ARG
+    assert lib.psgd_errors_materialize(plan.handle, 0x1000, 0x1010, 0x200000, None) == psgd.PSGD_ERR_INVALID_ARG
+
+
 def test_timing_calls_without_gpu():
     plan = psgd.psgd_plan_create([(8, 8)], 2, 2)
     psgd.psgd_plan_set_timing(plan, True)

@@ -257,6 +257,87 @@ def test_carry_is_used_and_reset_restores_exactness(torch_gpu):
     compare_step(run, snap, O, TOL, what="new workspace")
 
 
+# ----------------------------------------------------------------------- deferred error
+@pytest.mark.parametrize("W,r", [(16, 2), (5, 3), (4, 4)])
+def test_deferred_error_each_step(torch_gpu, W, r):
+    """Deferred mode: the error buffer keeps M_w and the subtraction of U moves into the
+    next step.  The materialised errors, P, Q and U match the oracle at every step."""
+    from distributed_sgd_gradient_ef_amd import psgd
+
+    log(f"[case] deferred W={W} r={r}")
+    rng = np.random.default_rng(41 + W)
+    run = DeviceRun(CARRY_SHAPES, r, W, flags=psgd.PSGD_FLAG_DEFERRED_ERROR)
+    run.set_q_host({i: rng.standard_normal((s[1], r)).astype(np.float32)
+                    for i, s in enumerate(CARRY_SHAPES) if WL.is_matrix(s, r)})
+    run.set_errors_host([0.2 * rng.standard_normal((W,) + s).astype(np.float32) for s in CARRY_SHAPES])
+    for t in range(4):
+        run.set_grads_host([rng.standard_normal((W,) + s).astype(np.float32) for s in CARRY_SHAPES])
+        before = run.plain_errors()
+        snap = snapshot(run, range(len(CARRY_SHAPES)), errors_source=before)
+        run.compress()
+        after = run.plain_errors()
+        worst = compare_step(run, snap, O, TOL, what=f"deferred step {t}", errors_source=after)
+        log(f"step {t} worst rel: " + " ".join(f"{k}={v:.2e}" for k, v in worst.items()))
+
+
+def test_deferred_materialize_in_place_and_reset(torch_gpu):
+    """In-place materialisation turns the buffer plain (the next step subtracts nothing
+    more); psgd_plan_reset_carry declares externally written errors plain."""
+    from distributed_sgd_gradient_ef_amd import psgd
+
+    log("[case] deferred materialize in place")
+    shapes = [(300, 700), (1, 33), (64, 27)]
+    W, r = 3, 2
+    rng = np.random.default_rng(17)
+    run = DeviceRun(shapes, r, W, flags=psgd.PSGD_FLAG_DEFERRED_ERROR)
+    run.set_q_host({0: rng.standard_normal((700, r)).astype(np.float32),
+                    2: rng.standard_normal((27, r)).astype(np.float32)})
+    run.set_grads_host([rng.standard_normal((W,) + s).astype(np.float32) for s in shapes])
+    run.compress()
+    psgd.psgd_errors_materialize(run.plan, run.errors, run.errors, run.workspace)
+    snap = snapshot(run, [0, 1, 2])  # plain now
+    run.compress()
+    compare_step(run, snap, O, TOL, what="after in-place materialise", errors_source=run.plain_errors())
+    run.set_errors_host([0.5 * rng.standard_normal((W,) + s).astype(np.float32) for s in shapes])
+    psgd.psgd_plan_reset_carry(run.plan)
+    snap = snapshot(run, [0, 1, 2])
+    run.compress()
+    compare_step(run, snap, O, TOL, what="after reset", errors_source=run.plain_errors())
+
+
+def test_deferred_momentum_matches_eager(torch_gpu):
+    """Momentum SGD in deferred mode gives the eager mode's update, momentum and
+    parameters (to float rounding) over 20 steps, with update=NULL in deferred mode."""
+    from distributed_sgd_gradient_ef_amd import psgd
+
+    log("[case] deferred momentum vs eager")
+    shapes = [(128, 576), (1, 128), (512, 256)]
+    W, r = 16, 4
+    rng = np.random.default_rng(23)
+    q0 = {0: rng.standard_normal((576, r)).astype(np.float32), 2: rng.standard_normal((256, r)).astype(np.float32)}
+    x0 = [0.01 * rng.standard_normal(s).astype(np.float32) for s in shapes]
+    runs = []
+    for flags in (0, psgd.PSGD_FLAG_DEFERRED_ERROR):
+        run = DeviceRun(shapes, r, W, flags=flags, momentum=True)
+        run.set_q_host(q0)
+        run.set_params_host(x0)
+        runs.append(run)
+    for t in range(20):
+        g = [rng.standard_normal((W,) + s).astype(np.float32) for s in shapes]
+        for k, run in enumerate(runs):
+            run.set_grads_host(g)
+            run.momentum_step(0.1, 0.9, update=(k == 0))
+    eager, defer = runs
+    torch_gpu.cuda.synchronize()
+    for name in ("params", "momentum"):
+        a, b = getattr(eager, name), getattr(defer, name)
+        err = ((a - b).norm() / a.norm()).item()
+        assert err < TOL, (name, err)
+    e_plain = defer.plain_errors()
+    err = ((eager.errors - e_plain).norm() / eager.errors.norm()).item()
+    assert err < TOL, err
+
+
 # ----------------------------------------------------------------------- workloads
 def test_resnet18_three_steps(torch_gpu):
     """ResNet-18 shapes, r=2, W=16, three steps with fresh worker noise, every tensor."""
