@@ -39,26 +39,30 @@ KERNEL_SRC = os.path.join(ROOT, "distributed_sgd_gradient_ef_amd", "csrc", "kern
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_resnet18_r2_w16.json")
 
 
-def kernel_bytes(plan, dtype_bytes: int, carry: bool) -> dict:
-    """Algorithmic HBM bytes per launch of each kernel for this plan."""
+def kernel_bytes(plan, dtype_bytes: int, variant: str) -> dict:
+    """Algorithmic HBM bytes per launch of each kernel for this plan and variant."""
     s = plan.sizes
     W = s["n_workers"]
     mn, vn = s["matrix_numel"], s["vector_numel"]
     gb = dtype_bytes
+    first = {
+        # read G_w and E_w on every worker, write Mbar once
+        "plain": W * (gb + 4) + 4,
+        # read G_w on every worker and the carried error mean once, write Mbar once
+        "carry": W * gb + 8,
+        # read G_w and E_w, write M_w on every worker, write Mbar once
+        "deferred": W * (gb + 8) + 4,
+    }[variant]
     return {
-        # deferred mode: read G_w, E_w, write M_w on every worker and Mbar once
-        "k_ef_defer": (W * (gb + 8) + 4) * mn + (W * gb + 4) * vn,
-        # deferred mode: write U once; 1-D tensors read the mean and write the update
-        "k_update": 4 * mn + 8 * vn,
-        # read G_w (and E_w, or the carried error mean once) on every worker, write the
-        # mean once; tensors without error: G only
-        "k_ef_mean": ((W * gb + 8) if carry else (W * (gb + 4) + 4)) * mn + (W * gb + 4) * vn,
-        # read Mbar once (Q, P are cache-resident)
-        "k_p_rows": 4 * mn + 4 * s["p_elems"],
+        # 1-D tensors: read G_w on every worker, write the mean once
+        "k_first": first * mn + (W * gb + 4) * vn,
+        # read Mbar once (P and Q are cache-resident)
         "k_q_partial": 4 * mn,
         # read G_w, E_w and write E'_w on every worker, write U once (and the new error
-        # mean in carry mode); tensors without error: read the mean, write the update
-        "k_apply": (W * (gb + 8) + (8 if carry else 4)) * mn + 8 * vn,
+        # mean in carry mode); 1-D tensors: read the mean, write the update
+        "k_apply": (W * (gb + 8) + (8 if variant == "carry" else 4)) * mn + 8 * vn,
+        # write U once; 1-D tensors: read the mean, write the update
+        "k_update": 4 * mn + 8 * vn,
     }
 
 
@@ -137,8 +141,10 @@ def main() -> int:
     wl = WL.workload("resnet18")
     shapes = [s for _, s in wl.shapes]
     W = wl.workers
+    flag_of = {"plain": 0, "carry": psgd.PSGD_FLAG_CARRY_ERROR_MEAN, "deferred": psgd.PSGD_FLAG_DEFERRED_ERROR}
 
-    def measure(flags: int) -> dict:
+    def measure(variant: str) -> dict:
+        flags = flag_of[variant]
         plan = psgd.psgd_plan_create(shapes, wl.rank, W, psgd.PSGD_F32, flags)
         s = plan.sizes
         ld = s["worker_stride"]
@@ -179,7 +185,7 @@ def main() -> int:
         ms_timed = t2.elapsed_time(t3) / args.steps
         stats = psgd.psgd_plan_kernel_stats(plan, reset=True)
         psgd.psgd_plan_set_timing(plan, False)
-        kb = kernel_bytes(plan, 4, bool(flags & psgd.PSGD_FLAG_CARRY_ERROR_MEAN))
+        kb = kernel_bytes(plan, 4, variant)
         kernels = {}
         for name, (n, tot) in stats.items():
             us = 1e3 * tot / max(n, 1)
@@ -209,9 +215,8 @@ def main() -> int:
     copy_gbs = 2 * cbytes * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
 
-    flag_of = {"plain": 0, "carry": psgd.PSGD_FLAG_CARRY_ERROR_MEAN, "deferred": psgd.PSGD_FLAG_DEFERRED_ERROR}
     names = ["plain", "carry", "deferred"] if args.mode == "all" else [args.mode]
-    results = {n: measure(flag_of[n]) for n in names}
+    results = {n: measure(n) for n in names}
     primary = args.primary if args.primary in results else names[0]
     main_run = results[primary]
     kernels, kb, s = main_run["kernels"], main_run["kb"], main_run["sizes"]

@@ -1,30 +1,39 @@
-// gfx950 kernels of libpsgd and the two step entry points.
+// gfx950 kernels of libpsgd and the step entry points.
 //
 // One step (the PowerSGD review page, section "Proposed method": EF add, P = M Q from
 // the warm-start Q, all-reduce, orthonormalise, Q = M^T P, all-reduce, decompress
-// P Q^T, keep the error; then momentum SGD) runs as six batched launches over every
+// P Q^T, keep the error; then momentum SGD) runs as five batched launches over every
 // tensor of the plan:
 //
-//   k_ef_mean     streams G_w and E_w of all W workers once and writes the worker
-//                 mean Mbar = mean_w (G_w + E_w) (for uncompressed tensors: mean_w G_w).
-//                 Because the compressor is linear and the W workers share one Q,
-//                 mean_w M_w Q = Mbar Q and mean_w M_w^T P = Mbar^T P: the in-HBM
-//                 all-reduce of P and Q becomes one pass over the worker slices.
-//   k_p_rows      P-bar = Mbar Q_in, one wave per row, lanes across the columns.
-//   k_mgs         modified Gram-Schmidt of P-bar, one workgroup per matrix.
-//   k_q_partial   Q partials = Mbar^T P over row blocks and column strips.
-//   k_q_reduce    Q = sum of the partials (fixed order, deterministic).
-//   k_apply       streams G_w and E_w again: E'_w = (G_w + E_w) - P Q^T, writes the
-//                 decompressed update once, and in the momentum entry point updates
-//                 momentum and parameters in the same pass.
+//   k_first      streams the W workers' slices of G (and E) once.  For a compressed
+//                matrix it forms M_w = G_w + E_w, the worker mean Mbar, and the partial
+//                row sums of P-bar = Mbar Q over its column strip.  Because the
+//                compressor is linear and all workers share Q,
+//                mean_w M_w Q = Mbar Q and mean_w M_w^T P = Mbar^T P: the all-reduce of
+//                P and Q becomes this one pass over the worker slices.  1-D tensors get
+//                the worker mean of G.
+//   k_mgs        sums the P-bar partials and runs modified Gram-Schmidt, one workgroup
+//                per matrix.
+//   k_q_partial  Q partials = Mbar^T P over row blocks and column strips.
+//   k_q_reduce   Q = sum of the partials (fixed order, deterministic).
+//   k_apply      streams G and E again: E'_w = (G_w + E_w) - P Q^T, writes the
+//                decompressed update once and, in the momentum entry point, updates
+//                momentum and parameters in the same pass.
 //
-// All streaming work is HBM-bound (about one flop per byte), so no MFMA is used.
+// Deferred-error plans replace k_apply with k_update (U and momentum only) and fold
+// the subtraction of the previous step's P Q^T into the next step's k_first.
+//
+// The worker passes are HBM-bound (about one flop per byte), so no MFMA is used.  They
+// work on tiles of a few rows by a strip of 1024 columns (256 threads x float4): each
+// thread keeps Q of its four columns in registers, reads P one row at a time (the same
+// address across the wave), and has every worker's float4 of a row in flight at once.
 
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
 #include <string>
+#include <type_traits>
 
 #include "plan.hpp"
 
@@ -38,15 +47,18 @@ struct bf16 {
   unsigned short bits;
 };
 
+enum ApplyMode { kCompress = 0, kMomentum = 1, kNesterov = 2 };
+enum FirstPass { kFpMean = 0, kFpCarry = 1, kFpDefer = 2 };
+
 // ------------------------------------------------------------------ loads and stores
 // Gradients and errors are touched once per pass and never reused from cache, so the
-// streaming passes load and store them non-temporally; buffers that a later kernel of
-// the same step reads again (Mbar, the carried error mean) use ordinary accesses.
-__device__ __forceinline__ f4 load4(const float* p) { return *reinterpret_cast<const f4*>(p); }
+// worker passes load and store them non-temporally; buffers that a later kernel of the
+// same step reads again (Mbar, the carried error mean) use ordinary accesses.
+template <int V>
+using vec_t = std::conditional_t<V == 4, f4, float>;
 
-__device__ __forceinline__ f4 load4_nt(const float* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const f4*>(p));
-}
+__device__ __forceinline__ float lane(const f4& x, int q) { return x[q]; }
+__device__ __forceinline__ float lane(const float& x, int) { return x; }
 
 __device__ __forceinline__ f4 widen(const u16x4 v) {
   f4 r;
@@ -57,8 +69,44 @@ __device__ __forceinline__ f4 widen(const u16x4 v) {
   return r;
 }
 
-__device__ __forceinline__ f4 load4_nt(const bf16* p) {
-  return widen(__builtin_nontemporal_load(reinterpret_cast<const u16x4*>(p)));
+template <int V>
+__device__ __forceinline__ vec_t<V> ldv(const float* p) {
+  if constexpr (V == 4)
+    return *reinterpret_cast<const f4*>(p);
+  else
+    return *p;
+}
+
+template <int V>
+__device__ __forceinline__ vec_t<V> ld_nt(const float* p) {
+  if constexpr (V == 4)
+    return __builtin_nontemporal_load(reinterpret_cast<const f4*>(p));
+  else
+    return __builtin_nontemporal_load(p);
+}
+
+template <int V>
+__device__ __forceinline__ vec_t<V> ld_nt(const bf16* p) {
+  if constexpr (V == 4)
+    return widen(__builtin_nontemporal_load(reinterpret_cast<const u16x4*>(p)));
+  else
+    return __uint_as_float(uint32_t(__builtin_nontemporal_load(reinterpret_cast<const unsigned short*>(p))) << 16);
+}
+
+template <int V>
+__device__ __forceinline__ void st(float* p, const vec_t<V> v) {
+  if constexpr (V == 4)
+    *reinterpret_cast<f4*>(p) = v;
+  else
+    *p = v;
+}
+
+template <int V>
+__device__ __forceinline__ void st_nt(float* p, const vec_t<V> v) {
+  if constexpr (V == 4)
+    __builtin_nontemporal_store(v, reinterpret_cast<f4*>(p));
+  else
+    __builtin_nontemporal_store(v, p);
 }
 
 // Store the first `valid` (>= 1) lanes of v; all four when valid >= 4.
@@ -82,6 +130,7 @@ __device__ __forceinline__ void store4_nt(float* p, const f4 v, int64_t valid) {
   }
 }
 
+// ------------------------------------------------------------------ reductions
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -97,9 +146,9 @@ __device__ __forceinline__ double wave_sum(double v) {
 // Sum over the workgroup; every thread gets the same value (same order everywhere).
 __device__ double block_sum(double v, double* red) {
   v = wave_sum(v);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane_id = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __syncthreads();
-  if (lane == 0) red[wave] = v;
+  if (lane_id == 0) red[wave] = v;
   __syncthreads();
   double s = 0.0;
   const int nw = blockDim.x >> 6;
@@ -111,9 +160,9 @@ __device__ double block_sum(double v, double* red) {
 __device__ void block_sum2(double& a, double& b, double* red) {
   a = wave_sum(a);
   b = wave_sum(b);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane_id = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __syncthreads();
-  if (lane == 0) {
+  if (lane_id == 0) {
     red[2 * wave] = a;
     red[2 * wave + 1] = b;
   }
@@ -128,8 +177,74 @@ __device__ void block_sum2(double& a, double& b, double* red) {
   b = sb;
 }
 
-// u = P Q^T at the four elements of the float4 chunk starting at element c of matrix mi
-// (row-major, rank R <= 4); lanes past `valid` are zero.
+// ------------------------------------------------------------------ P Q^T
+// The decompressed value at one element is sum_k P[i,k] Q[j,k] accumulated in k order
+// from zero (one fma per term); every kernel that needs it uses exactly this order, so
+// the U written by one kernel equals the U another subtracts.
+__device__ __forceinline__ float pq_dot(const float* pr, const float* qr, int R) {
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (k < R) s += pr[k] * qr[k];
+  return s;
+}
+
+// Q rows of four consecutive columns: 4*RR floats from a 16-byte aligned address, read
+// as RR float4 loads.
+template <int RR>
+__device__ __forceinline__ void load_q4(float (&qv)[4][4], const float* base) {
+  float flat[4 * RR];
+#pragma unroll
+  for (int v = 0; v < RR; ++v) {
+    const f4 x = reinterpret_cast<const f4*>(base)[v];
+    flat[4 * v + 0] = x.x;
+    flat[4 * v + 1] = x.y;
+    flat[4 * v + 2] = x.z;
+    flat[4 * v + 3] = x.w;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) qv[q][k] = (k < RR) ? flat[q * RR + k] : 0.f;
+}
+
+// Q rows of the thread's V columns starting at j (zeros past the rank or when
+// inactive).  With V = 4, j is a multiple of 4 and every Q block starts on a 16-byte
+// boundary, so the 4R floats are R aligned float4 loads.
+template <int V>
+__device__ __forceinline__ void load_q_cols(float (&qv)[V][4], const float* Qm, int j, int R, bool active) {
+  if constexpr (V == 4) {
+    if (active) {
+      const float* base = Qm + int64_t(j) * R;
+      switch (R) {
+        case 1: load_q4<1>(qv, base); return;
+        case 2: load_q4<2>(qv, base); return;
+        case 3: load_q4<3>(qv, base); return;
+        default: load_q4<4>(qv, base); return;
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < V; ++q)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) qv[q][k] = (active && k < R) ? Qm[int64_t(j + q) * R + k] : 0.f;
+}
+
+__device__ __forceinline__ void load_p_row(float (&pr)[4], const float* Pm, int i, int R) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) pr[k] = (k < R) ? Pm[int64_t(i) * R + k] : 0.f;
+}
+
+template <int V>
+__device__ __forceinline__ vec_t<V> pq_row(const float (&pr)[4], const float (&qv)[V][4], int R) {
+  if constexpr (V == 4)
+    return f4{pq_dot(pr, qv[0], R), pq_dot(pr, qv[1], R), pq_dot(pr, qv[2], R), pq_dot(pr, qv[3], R)};
+  else
+    return pq_dot(pr, qv[0], R);
+}
+
+// u = P Q^T at the four elements of the flat float4 chunk starting at element c of
+// matrix mi (rows may wrap inside the chunk); lanes past `valid` are zero.
 __device__ __forceinline__ f4 lowrank_chunk(const MatInfo& mi, const float* __restrict__ P,
                                             const float* __restrict__ Q, int64_t c, int64_t valid, int R) {
   const float* Pm = P + mi.p_off;
@@ -141,13 +256,15 @@ __device__ __forceinline__ f4 lowrank_chunk(const MatInfo& mi, const float* __re
   float u[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    float s = 0.f;
+    float pr[4], qr[4];
     if (q < valid) {
+      load_p_row(pr, Pm, i, R);
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (k < R) s += Pm[int64_t(i) * R + k] * Qm[int64_t(j) * R + k];
+      for (int k = 0; k < 4; ++k) qr[k] = (k < R) ? Qm[int64_t(j) * R + k] : 0.f;
+      u[q] = pq_dot(pr, qr, R);
+    } else {
+      u[q] = 0.f;
     }
-    u[q] = s;
     if (++j == cols) {
       j = 0;
       ++i;
@@ -156,133 +273,256 @@ __device__ __forceinline__ f4 lowrank_chunk(const MatInfo& mi, const float* __re
   return f4{u[0], u[1], u[2], u[3]};
 }
 
-// ------------------------------------------------------------------ pass 1: EF add + mean
-// One float4 chunk per thread, every worker's slice of it loaded before any is used.
-// WT > 0: the worker count is the compile-time WT (loop fully unrolled); WT == 0: any
-// worker count.  With `ebar` set (carried error mean from the previous step) only the
-// gradients are read: Mbar = mean_w G_w + ebar, equal to mean_w (G_w + E_w) because the
-// carried ebar is the mean of exactly the E_w stored by that step.
-template <typename GT, int WT>
-__global__ __launch_bounds__(kStreamThreads) void k_ef_mean(const StreamTile* __restrict__ tiles,
-                                                            const GT* __restrict__ G,
-                                                            const float* __restrict__ E,
-                                                            const float* __restrict__ ebar,
-                                                            float* __restrict__ Mbar, int W,
-                                                            int64_t ld, float inv_w) {
-  const StreamTile t = tiles[blockIdx.x];
-  const int64_t c = t.begin + int64_t(threadIdx.x) * 4;
-  if (c >= t.end) return;
-  const bool with_errors = t.mat >= 0 && ebar == nullptr;
-  f4 acc = {0.f, 0.f, 0.f, 0.f};
+// ------------------------------------------------------------------ worker loops
+// Every worker's slice of one chunk (V consecutive elements at c) is loaded before any
+// is used.  WT > 0: the worker count is the compile-time WT (fully unrolled); WT == 0:
+// any worker count, four at a time.
+
+// sum_w (G_w + E_w)
+template <int V, typename GT, int WT>
+__device__ __forceinline__ vec_t<V> sum_ge(const GT* G, const float* E, int W, int64_t ld, int64_t c) {
+  vec_t<V> acc{};
   if constexpr (WT > 0) {
-    f4 g[WT];
+    vec_t<V> g[WT], e[WT];
 #pragma unroll
-    for (int w = 0; w < WT; ++w) g[w] = load4_nt(G + w * ld + c);
-    if (with_errors) {
-      f4 e[WT];
+    for (int w = 0; w < WT; ++w) {
+      g[w] = ld_nt<V>(G + w * ld + c);
+      e[w] = ld_nt<V>(E + w * ld + c);
+    }
 #pragma unroll
-      for (int w = 0; w < WT; ++w) e[w] = load4_nt(E + w * ld + c);
+    for (int w = 0; w < WT; ++w) acc += g[w] + e[w];
+  } else {
+    int w = 0;
+    for (; w + 4 <= W; w += 4) {
+      vec_t<V> g[4], e[4];
 #pragma unroll
-      for (int w = 0; w < WT; ++w) acc += g[w] + e[w];
-    } else {
+      for (int k = 0; k < 4; ++k) {
+        g[k] = ld_nt<V>(G + (w + k) * ld + c);
+        e[k] = ld_nt<V>(E + (w + k) * ld + c);
+      }
 #pragma unroll
-      for (int w = 0; w < WT; ++w) acc += g[w];
+      for (int k = 0; k < 4; ++k) acc += g[k] + e[k];
+    }
+    for (; w < W; ++w) acc += ld_nt<V>(G + w * ld + c) + ld_nt<V>(E + w * ld + c);
+  }
+  return acc;
+}
+
+// sum_w G_w
+template <int V, typename GT, int WT>
+__device__ __forceinline__ vec_t<V> sum_g(const GT* G, int W, int64_t ld, int64_t c) {
+  vec_t<V> acc{};
+  if constexpr (WT > 0) {
+    vec_t<V> g[WT];
+#pragma unroll
+    for (int w = 0; w < WT; ++w) g[w] = ld_nt<V>(G + w * ld + c);
+#pragma unroll
+    for (int w = 0; w < WT; ++w) acc += g[w];
+  } else {
+    int w = 0;
+    for (; w + 4 <= W; w += 4) {
+      vec_t<V> g[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) g[k] = ld_nt<V>(G + (w + k) * ld + c);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc += g[k];
+    }
+    for (; w < W; ++w) acc += ld_nt<V>(G + w * ld + c);
+  }
+  return acc;
+}
+
+// E_w <- (G_w + E_w) - u for every worker; returns sum_w of the stored values.
+template <int V, typename GT, int WT>
+__device__ __forceinline__ vec_t<V> update_workers(const GT* G, float* E, int W, int64_t ld, int64_t c,
+                                                   const vec_t<V> u) {
+  vec_t<V> acc{};
+  if constexpr (WT > 0) {
+    vec_t<V> g[WT], e[WT];
+#pragma unroll
+    for (int w = 0; w < WT; ++w) {
+      g[w] = ld_nt<V>(G + w * ld + c);
+      e[w] = ld_nt<V>(E + w * ld + c);
+    }
+#pragma unroll
+    for (int w = 0; w < WT; ++w) {
+      const vec_t<V> n = (g[w] + e[w]) - u;
+      st_nt<V>(E + w * ld + c, n);
+      acc += n;
     }
   } else {
     int w = 0;
-    if (with_errors) {
-      for (; w + 4 <= W; w += 4) {
-        const f4 g0 = load4_nt(G + (w + 0) * ld + c), e0 = load4_nt(E + (w + 0) * ld + c);
-        const f4 g1 = load4_nt(G + (w + 1) * ld + c), e1 = load4_nt(E + (w + 1) * ld + c);
-        const f4 g2 = load4_nt(G + (w + 2) * ld + c), e2 = load4_nt(E + (w + 2) * ld + c);
-        const f4 g3 = load4_nt(G + (w + 3) * ld + c), e3 = load4_nt(E + (w + 3) * ld + c);
-        acc += g0 + e0;
-        acc += g1 + e1;
-        acc += g2 + e2;
-        acc += g3 + e3;
+    for (; w + 4 <= W; w += 4) {
+      vec_t<V> g[4], e[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        g[k] = ld_nt<V>(G + (w + k) * ld + c);
+        e[k] = ld_nt<V>(E + (w + k) * ld + c);
       }
-      for (; w < W; ++w) acc += load4_nt(G + w * ld + c) + load4_nt(E + w * ld + c);
-    } else {
-      for (; w + 4 <= W; w += 4) {
-        const f4 g0 = load4_nt(G + (w + 0) * ld + c), g1 = load4_nt(G + (w + 1) * ld + c);
-        const f4 g2 = load4_nt(G + (w + 2) * ld + c), g3 = load4_nt(G + (w + 3) * ld + c);
-        acc += g0;
-        acc += g1;
-        acc += g2;
-        acc += g3;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const vec_t<V> n = (g[k] + e[k]) - u;
+        st_nt<V>(E + (w + k) * ld + c, n);
+        acc += n;
       }
-      for (; w < W; ++w) acc += load4_nt(G + w * ld + c);
+    }
+    for (; w < W; ++w) {
+      const vec_t<V> n = (ld_nt<V>(G + w * ld + c) + ld_nt<V>(E + w * ld + c)) - u;
+      st_nt<V>(E + w * ld + c, n);
+      acc += n;
     }
   }
-  acc *= inv_w;
-  if (t.mat >= 0 && ebar != nullptr) acc += load4(ebar + c);
-  store4(Mbar + c, acc, t.end - c);
+  return acc;
 }
 
-// ------------------------------------------------------------------ P-bar = Mbar Q
-template <int R>
-__global__ __launch_bounds__(kRowThreads) void k_p_rows(const RowTile* __restrict__ tiles,
-                                                        const MatInfo* __restrict__ mats,
-                                                        const float* __restrict__ Mbar,
-                                                        const float* __restrict__ Q,
-                                                        float* __restrict__ Pbar) {
-  const RowTile t = tiles[blockIdx.x];
-  const MatInfo mi = mats[t.mat];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const float* Qm = Q + mi.q_off;
+template <int V>
+__device__ __forceinline__ void momentum_v(float* mom, float* x, int64_t c, const vec_t<V> u, int mode, float lr,
+                                           float mu) {
+  const vec_t<V> m0 = ld_nt<V>(mom + c), x0 = ld_nt<V>(x + c);
+  const vec_t<V> m1 = mu * m0 + u;
+  const vec_t<V> x1 = (mode == kNesterov) ? x0 - lr * (u + mu * m1) : x0 - lr * m1;
+  st_nt<V>(mom + c, m1);
+  st_nt<V>(x + c, x1);
+}
+
+__device__ __forceinline__ void momentum_masked(float* mom, float* x, int64_t c, const f4 u, int64_t valid,
+                                                int mode, float lr, float mu) {
+  const f4 m0 = *reinterpret_cast<const f4*>(mom + c), x0 = *reinterpret_cast<const f4*>(x + c);
+  const f4 m1 = mu * m0 + u;
+  const f4 x1 = (mode == kNesterov) ? x0 - lr * (u + mu * m1) : x0 - lr * m1;
+  store4_nt(mom + c, m1, valid);
+  store4_nt(x + c, x1, valid);
+}
+
+// ------------------------------------------------------------------ pass 1
+// Matrix tile: rows [row_begin, row_end) (at most kSRowsPerTile) x the thread's V
+// columns.  FP selects the first-pass form:
+//   kFpMean  Mbar = mean_w (G_w + E_w)
+//   kFpCarry Mbar = mean_w G_w + ebar  (ebar = mean of the errors the previous step
+//            stored, carried in the workspace)
+//   kFpDefer M_w = (G_w + E_w) - P_prev Q_prev^T is stored back into E; Mbar = mean_w M_w
+// Then every thread holds its columns' share of P-bar = Mbar Q for each row, and one
+// block reduction writes the tile's partial row sums (one per column strip).
+template <int V, typename GT, int WT, int FP>
+__device__ __forceinline__ void first_matrix_tile(const UpdTile& t, const MatInfo& mi, const GT* G, float* E,
+                                                  const float* ebar, const float* Pprev, const float* Qprev,
+                                                  const float* Qin, float* Mbar, float* Ppart, int W, int64_t ld,
+                                                  int R, float inv_w, int offset_valid, float* red) {
   const int cols = mi.cols;
-  for (int row = t.row_begin + wave; row < t.row_end; row += kRowThreads / 64) {
-    const float* mrow = Mbar + mi.offset + int64_t(row) * cols;
-    float acc[R];
+  const int j = t.col_begin + int(threadIdx.x) * V;
+  const bool active = j < cols;
+  const int nrows = t.row_end - t.row_begin;
+  float qv[V][4];
+  load_q_cols<V>(qv, Qin + mi.q_off, j, R, active);
+  float qp[V][4];
+  if constexpr (FP == kFpDefer) load_q_cols<V>(qp, Qprev + mi.q_off, j, R, active && offset_valid);
+  float part[kSRowsPerTile][4];
 #pragma unroll
-    for (int k = 0; k < R; ++k) acc[k] = 0.f;
-    if (mi.vec4) {
-#pragma unroll 4
-      for (int j = lane * 4; j < cols; j += 256) {
-        const f4 v = load4(mrow + j);
-        const float* qj = Qm + int64_t(j) * R;
+  for (int r = 0; r < kSRowsPerTile; ++r)
 #pragma unroll
-        for (int k = 0; k < R; ++k)
-          acc[k] += v.x * qj[k] + v.y * qj[R + k] + v.z * qj[2 * R + k] + v.w * qj[3 * R + k];
+    for (int k = 0; k < 4; ++k) part[r][k] = 0.f;
+#pragma unroll
+  for (int r = 0; r < kSRowsPerTile; ++r) {
+    if (r < nrows && active) {
+      const int i = t.row_begin + r;
+      const int64_t c = mi.offset + int64_t(i) * cols + j;
+      vec_t<V> mb;
+      if constexpr (FP == kFpDefer) {
+        float pp[4];
+        if (offset_valid) {
+          load_p_row(pp, Pprev + mi.p_off, i, R);
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) pp[k] = 0.f;
+        }
+        mb = update_workers<V, GT, WT>(G, E, W, ld, c, pq_row<V>(pp, qp, R)) * inv_w;
+      } else if constexpr (FP == kFpCarry) {
+        mb = sum_g<V, GT, WT>(G, W, ld, c) * inv_w + ldv<V>(ebar + c);
+      } else {
+        mb = sum_ge<V, GT, WT>(G, E, W, ld, c) * inv_w;
       }
-    } else {
-#pragma unroll 4
-      for (int j = lane; j < cols; j += 64) {
-        const float v = mrow[j];
+      st<V>(Mbar + c, mb);
 #pragma unroll
-        for (int k = 0; k < R; ++k) acc[k] += v * Qm[int64_t(j) * R + k];
+      for (int k = 0; k < 4; ++k) {
+        float s = 0.f;
+#pragma unroll
+        for (int q = 0; q < V; ++q) s += lane(mb, q) * qv[q][k];
+        part[r][k] = s;
       }
-    }
-#pragma unroll
-    for (int k = 0; k < R; ++k) acc[k] = wave_sum(acc[k]);
-    if (lane == 0) {
-#pragma unroll
-      for (int k = 0; k < R; ++k) Pbar[mi.p_off + int64_t(row) * R + k] = acc[k];
     }
   }
+  // Block reduction of the partial row sums, in a fixed order.
+  const int lane_id = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int r = 0; r < kSRowsPerTile; ++r)
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (r < nrows && k < R) {
+        const float v = wave_sum(part[r][k]);
+        if (lane_id == 0) red[(r * 4 + k) * (kStreamThreads / 64) + wave] = v;
+      }
+  __syncthreads();
+  const int tid = threadIdx.x;
+  if (tid < nrows * 4 && (tid & 3) < R) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < kStreamThreads / 64; ++w) s += red[tid * (kStreamThreads / 64) + w];
+    const int r = tid >> 2, k = tid & 3;
+    const int strip = t.col_begin / (kStreamThreads * V);
+    Ppart[mi.ppart_off + (int64_t(strip) * mi.rows + t.row_begin + r) * R + k] = s;
+  }
+}
+
+template <typename GT, int WT, int FP>
+__global__ __launch_bounds__(kStreamThreads) void k_first(const UpdTile* __restrict__ tiles,
+                                                          const MatInfo* __restrict__ mats,
+                                                          const GT* __restrict__ G, float* __restrict__ E,
+                                                          const float* __restrict__ ebar,
+                                                          const float* __restrict__ Pprev,
+                                                          const float* __restrict__ Qprev,
+                                                          const float* __restrict__ Qin, float* __restrict__ Mbar,
+                                                          float* __restrict__ Ppart, int W, int64_t ld, int R,
+                                                          float inv_w, int offset_valid) {
+  __shared__ float red[kSRowsPerTile * 4 * (kStreamThreads / 64)];
+  const UpdTile t = tiles[blockIdx.x];
+  if (t.mat < 0) {  // uncompressed tensor: the worker mean of G
+    const int64_t c = t.begin + int64_t(threadIdx.x) * 4;
+    if (c < t.end) store4(Mbar + c, sum_g<4, GT, WT>(G, W, ld, c) * inv_w, t.end - c);
+    return;
+  }
+  const MatInfo mi = mats[t.mat];
+  if (mi.vec4)
+    first_matrix_tile<4, GT, WT, FP>(t, mi, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, W, ld, R, inv_w,
+                                     offset_valid, red);
+  else
+    first_matrix_tile<1, GT, WT, FP>(t, mi, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, W, ld, R, inv_w,
+                                     offset_valid, red);
 }
 
 // ------------------------------------------------------------------ Gram-Schmidt
-// Modified Gram-Schmidt over the R columns of P-bar (rows x R, row-major), in column
-// order.  Dot products and norms accumulate in double.  A column whose residual norm
-// is at most 1e-4 of its norm before orthogonalisation (or zero) becomes zero.
-// Each thread only touches its own rows, so only the reductions synchronise; the norm
-// of a fresh column and its projection on column 0 share one reduction (both use the
-// unmodified column).  `P2`, if set, receives a copy of the result.
+// P-bar = sum over column strips of the partial row sums (fixed strip order), then
+// modified Gram-Schmidt over its R columns in column order.  Dot products and norms
+// accumulate in double.  A column whose residual norm is at most 1e-4 of its norm
+// before orthogonalisation (or zero) becomes zero.  Each thread only touches its own
+// rows, so only the reductions synchronise; the norm of a fresh column and its
+// projection on column 0 share one reduction (both use the unmodified column).  `P2`,
+// if set, receives a copy of the result.
 template <int R>
 __global__ __launch_bounds__(kMgsThreads) void k_mgs(const MatInfo* __restrict__ mats,
-                                                     const float* __restrict__ Pbar,
+                                                     const float* __restrict__ Ppart,
                                                      float* __restrict__ P, float* __restrict__ P2) {
   __shared__ double red[2 * (kMgsThreads / 64)];
   const MatInfo mi = mats[blockIdx.x];
-  const float* src = Pbar + mi.p_off;
+  const float* src = Ppart + mi.ppart_off;
   float* dst = P + mi.p_off;
   const int n = mi.rows;
+  const int64_t strip_stride = int64_t(n) * R;
   for (int k = 0; k < R; ++k) {
     double s = 0.0, c = 0.0;
     for (int i = threadIdx.x; i < n; i += blockDim.x) {
       const int64_t o = int64_t(i) * R;
-      const float v = src[o + k];
+      float v = 0.f;
+      for (int sidx = 0; sidx < mi.nstrips; ++sidx) v += src[sidx * strip_stride + o + k];
       dst[o + k] = v;
       s += double(v) * double(v);
       if (k > 0) c += double(dst[o]) * double(v);
@@ -345,7 +585,7 @@ __global__ __launch_bounds__(kQThreads) void k_q_partial(const QTile* __restrict
       for (int k = 0; k < R; ++k) acc[q][k] = 0.f;
 #pragma unroll 8
     for (int i = r0; i < r1; ++i) {
-      const f4 v = load4(base + int64_t(i) * cols + j);
+      const f4 v = *reinterpret_cast<const f4*>(base + int64_t(i) * cols + j);
 #pragma unroll
       for (int k = 0; k < R; ++k) {
         const float pk = Pm[int64_t(i) * R + k];
@@ -392,151 +632,80 @@ __global__ __launch_bounds__(kQRedThreads) void k_q_reduce(const MatInfo* __rest
   }
 }
 
-// ------------------------------------------------------------------ pass 2: error + update
-enum ApplyMode { kCompress = 0, kMomentum = 1, kNesterov = 2 };
+// ------------------------------------------------------------------ pass 2 (eager modes)
+// Matrix tile: u = P Q^T for the thread's columns of each row; E'_w = (G_w + E_w) - u
+// on every worker, the mean of the stored E'_w into `ebar` (carry mode), U once, and
+// the momentum-SGD update in the momentum modes.  1-D tensors: the update is the mean.
+template <int V, typename GT, int WT>
+__device__ __forceinline__ void apply_matrix_tile(const UpdTile& t, const MatInfo& mi, const GT* G, float* E,
+                                                  const float* P, const float* Q, float* update, float* mom,
+                                                  float* x, float* ebar, int W, int64_t ld, int R, int mode,
+                                                  float lr, float mu, float inv_w) {
+  const int cols = mi.cols;
+  const int j = t.col_begin + int(threadIdx.x) * V;
+  if (j >= cols) return;
+  float qv[V][4];
+  load_q_cols<V>(qv, Q + mi.q_off, j, R, true);
+  for (int i = t.row_begin; i < t.row_end; ++i) {
+    float pr[4];
+    load_p_row(pr, P + mi.p_off, i, R);
+    const vec_t<V> u = pq_row<V>(pr, qv, R);
+    const int64_t c = mi.offset + int64_t(i) * cols + j;
+    const vec_t<V> es = update_workers<V, GT, WT>(G, E, W, ld, c, u);
+    if (ebar != nullptr) st<V>(ebar + c, es * inv_w);
+    if (update != nullptr) st_nt<V>(update + c, u);
+    if (mode != kCompress) momentum_v<V>(mom, x, c, u, mode, lr, mu);
+  }
+}
 
-// One float4 chunk per thread.  For a compressed matrix: u = P Q^T at the chunk's four
-// elements (rank R <= 4), E'_w = (G_w + E_w) - u for every worker, and (carry mode) the
-// mean of the stored E'_w into `ebar`.  Every tensor: the update u is written once and,
-// in the momentum modes, mom <- mu*mom + u; x <- x - lr*mom (or x - lr*(u + mu*mom)).
 template <typename GT, int WT>
 __global__ __launch_bounds__(kStreamThreads) void k_apply(
-    const StreamTile* __restrict__ tiles, const MatInfo* __restrict__ mats, const GT* __restrict__ G,
+    const UpdTile* __restrict__ tiles, const MatInfo* __restrict__ mats, const GT* __restrict__ G,
     float* __restrict__ E, const float* __restrict__ Mbar, const float* __restrict__ P,
     const float* __restrict__ Q, float* __restrict__ update, float* __restrict__ mom,
     float* __restrict__ x, float* __restrict__ ebar, int W, int64_t ld, int R, int mode, float lr,
     float mu, float inv_w) {
-  const StreamTile t = tiles[blockIdx.x];
-  const int64_t c = t.begin + int64_t(threadIdx.x) * 4;
-  if (c >= t.end) return;
-  const int64_t valid = t.end - c;
-  f4 uv;
-  if (t.mat < 0) {  // uncompressed tensor: the update is the worker mean
-    uv = load4(Mbar + c);
-  } else {
-    uv = lowrank_chunk(mats[t.mat], P, Q, c, valid, R);
-    f4 es = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (WT > 0) {
-      f4 g[WT], e[WT];
-#pragma unroll
-      for (int w = 0; w < WT; ++w) {
-        g[w] = load4_nt(G + w * ld + c);
-        e[w] = load4_nt(E + w * ld + c);
-      }
-#pragma unroll
-      for (int w = 0; w < WT; ++w) {
-        const f4 ew = (g[w] + e[w]) - uv;
-        store4_nt(E + w * ld + c, ew, valid);
-        es += ew;
-      }
-    } else {
-      int w = 0;
-      for (; w + 4 <= W; w += 4) {
-        const f4 g0 = load4_nt(G + (w + 0) * ld + c), e0v = load4_nt(E + (w + 0) * ld + c);
-        const f4 g1 = load4_nt(G + (w + 1) * ld + c), e1v = load4_nt(E + (w + 1) * ld + c);
-        const f4 g2 = load4_nt(G + (w + 2) * ld + c), e2v = load4_nt(E + (w + 2) * ld + c);
-        const f4 g3 = load4_nt(G + (w + 3) * ld + c), e3v = load4_nt(E + (w + 3) * ld + c);
-        const f4 n0 = (g0 + e0v) - uv, n1 = (g1 + e1v) - uv, n2 = (g2 + e2v) - uv, n3 = (g3 + e3v) - uv;
-        store4_nt(E + (w + 0) * ld + c, n0, valid);
-        store4_nt(E + (w + 1) * ld + c, n1, valid);
-        store4_nt(E + (w + 2) * ld + c, n2, valid);
-        store4_nt(E + (w + 3) * ld + c, n3, valid);
-        es += n0;
-        es += n1;
-        es += n2;
-        es += n3;
-      }
-      for (; w < W; ++w) {
-        const f4 n = (load4_nt(G + w * ld + c) + load4_nt(E + w * ld + c)) - uv;
-        store4_nt(E + w * ld + c, n, valid);
-        es += n;
-      }
-    }
-    if (ebar != nullptr) store4(ebar + c, es * inv_w, valid);
+  const UpdTile t = tiles[blockIdx.x];
+  if (t.mat < 0) {
+    const int64_t c = t.begin + int64_t(threadIdx.x) * 4;
+    if (c >= t.end) return;
+    const int64_t valid = t.end - c;
+    const f4 uv = *reinterpret_cast<const f4*>(Mbar + c);
+    if (update != nullptr) store4_nt(update + c, uv, valid);
+    if (mode != kCompress) momentum_masked(mom, x, c, uv, valid, mode, lr, mu);
+    return;
   }
-  if (update != nullptr) store4_nt(update + c, uv, valid);
-  if (mode != kCompress) {
-    const f4 m0 = load4_nt(mom + c), x0 = load4_nt(x + c);
-    const f4 m1 = mu * m0 + uv;
-    const f4 x1 = (mode == kNesterov) ? x0 - lr * (uv + mu * m1) : x0 - lr * m1;
-    store4_nt(mom + c, m1, valid);
-    store4_nt(x + c, x1, valid);
-  }
+  const MatInfo mi = mats[t.mat];
+  if (mi.vec4)
+    apply_matrix_tile<4, GT, WT>(t, mi, G, E, P, Q, update, mom, x, ebar, W, ld, R, mode, lr, mu, inv_w);
+  else
+    apply_matrix_tile<1, GT, WT>(t, mi, G, E, P, Q, update, mom, x, ebar, W, ld, R, mode, lr, mu, inv_w);
 }
 
 // ------------------------------------------------------------------ deferred-error mode
 // The error buffer holds M_w = G_w + E_w of the previous step instead of E'_w; the true
-// error is that minus the previous step's P Q^T (kept in the workspace).  The single
-// pass over the workers then folds the previous subtraction into this step's EF add:
+// error is that minus the previous step's P Q^T (kept in the workspace).  k_first
+// (kFpDefer) folds that subtraction into this step's EF add:
 // M_w(t) = G_w(t) + [M_w(t-1) - U(t-1)], stores M_w(t) back and writes Mbar.
-template <typename GT, int WT>
-__global__ __launch_bounds__(kStreamThreads) void k_ef_defer(
-    const StreamTile* __restrict__ tiles, const MatInfo* __restrict__ mats, const GT* __restrict__ G,
-    float* __restrict__ E, const float* __restrict__ Pprev, const float* __restrict__ Qprev,
-    float* __restrict__ Mbar, int W, int64_t ld, int R, float inv_w, int offset_valid) {
-  const StreamTile t = tiles[blockIdx.x];
-  const int64_t c = t.begin + int64_t(threadIdx.x) * 4;
-  if (c >= t.end) return;
-  const int64_t valid = t.end - c;
-  const int Wn = WT > 0 ? WT : W;
-  f4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (t.mat < 0) {
-    for (int w = 0; w < Wn; ++w) acc += load4_nt(G + w * ld + c);
-    store4(Mbar + c, acc * inv_w, valid);
-    return;
+// k_update is the last pass: the decompressed update (P Q^T, or the mean for 1-D
+// tensors) and the momentum-SGD update; no worker data is touched.
+template <int V>
+__device__ __forceinline__ void update_matrix_tile(const UpdTile& t, const MatInfo& mi, const float* P,
+                                                   const float* Q, float* update, float* mom, float* x, int R,
+                                                   int mode, float lr, float mu) {
+  const int cols = mi.cols;
+  const int j = t.col_begin + int(threadIdx.x) * V;
+  if (j >= cols) return;
+  float qv[V][4];
+  load_q_cols<V>(qv, Q + mi.q_off, j, R, true);
+  for (int i = t.row_begin; i < t.row_end; ++i) {
+    float pr[4];
+    load_p_row(pr, P + mi.p_off, i, R);
+    const vec_t<V> u = pq_row<V>(pr, qv, R);
+    const int64_t c = mi.offset + int64_t(i) * cols + j;
+    if (update != nullptr) st_nt<V>(update + c, u);
+    if (mode != kCompress) momentum_v<V>(mom, x, c, u, mode, lr, mu);
   }
-  const f4 up = offset_valid ? lowrank_chunk(mats[t.mat], Pprev, Qprev, c, valid, R) : f4{0.f, 0.f, 0.f, 0.f};
-  if constexpr (WT > 0) {
-    f4 g[WT], e[WT];
-#pragma unroll
-    for (int w = 0; w < WT; ++w) {
-      g[w] = load4_nt(G + w * ld + c);
-      e[w] = load4_nt(E + w * ld + c);
-    }
-#pragma unroll
-    for (int w = 0; w < WT; ++w) {
-      const f4 m = (g[w] + e[w]) - up;
-      store4_nt(E + w * ld + c, m, valid);
-      acc += m;
-    }
-  } else {
-    int w = 0;
-    for (; w + 4 <= W; w += 4) {
-      const f4 g0 = load4_nt(G + (w + 0) * ld + c), e0v = load4_nt(E + (w + 0) * ld + c);
-      const f4 g1 = load4_nt(G + (w + 1) * ld + c), e1v = load4_nt(E + (w + 1) * ld + c);
-      const f4 g2 = load4_nt(G + (w + 2) * ld + c), e2v = load4_nt(E + (w + 2) * ld + c);
-      const f4 g3 = load4_nt(G + (w + 3) * ld + c), e3v = load4_nt(E + (w + 3) * ld + c);
-      const f4 m0 = (g0 + e0v) - up, m1 = (g1 + e1v) - up, m2 = (g2 + e2v) - up, m3 = (g3 + e3v) - up;
-      store4_nt(E + (w + 0) * ld + c, m0, valid);
-      store4_nt(E + (w + 1) * ld + c, m1, valid);
-      store4_nt(E + (w + 2) * ld + c, m2, valid);
-      store4_nt(E + (w + 3) * ld + c, m3, valid);
-      acc += m0;
-      acc += m1;
-      acc += m2;
-      acc += m3;
-    }
-    for (; w < W; ++w) {
-      const f4 m = (load4_nt(G + w * ld + c) + load4_nt(E + w * ld + c)) - up;
-      store4_nt(E + w * ld + c, m, valid);
-      acc += m;
-    }
-  }
-  store4(Mbar + c, acc * inv_w, valid);
-}
-
-// Deferred mode's last pass: the decompressed update (P Q^T, or the mean for 1-D
-// tensors) and the momentum-SGD update; no worker data is touched.  Matrix tiles are
-// rows x a column strip: a thread keeps Q of its four columns in registers and walks
-// the rows, reading each row of P once per wave.  The sum order over the rank matches
-// lowrank_chunk, so U here equals the U the next step subtracts.
-__device__ __forceinline__ void momentum_store(float* mom, float* x, int64_t c, const f4 uv, int64_t valid,
-                                               int mode, float lr, float mu) {
-  const f4 m0 = load4_nt(mom + c), x0 = load4_nt(x + c);
-  const f4 m1 = mu * m0 + uv;
-  const f4 x1 = (mode == kNesterov) ? x0 - lr * (uv + mu * m1) : x0 - lr * m1;
-  store4_nt(mom + c, m1, valid);
-  store4_nt(x + c, x1, valid);
 }
 
 __global__ __launch_bounds__(kQThreads) void k_update(
@@ -548,65 +717,20 @@ __global__ __launch_bounds__(kQThreads) void k_update(
     const int64_t c = t.begin + int64_t(threadIdx.x) * 4;
     if (c >= t.end) return;
     const int64_t valid = t.end - c;
-    const f4 uv = load4(Mbar + c);
+    const f4 uv = *reinterpret_cast<const f4*>(Mbar + c);
     if (update != nullptr) store4_nt(update + c, uv, valid);
-    if (mode != kCompress) momentum_store(mom, x, c, uv, valid, mode, lr, mu);
+    if (mode != kCompress) momentum_masked(mom, x, c, uv, valid, mode, lr, mu);
     return;
   }
   const MatInfo mi = mats[t.mat];
-  const int cols = mi.cols;
-  const float* Pm = P + mi.p_off;
-  const float* Qm = Q + mi.q_off;
-  if (mi.vec4) {
-    const int j = t.col_begin + int(threadIdx.x) * 4;
-    if (j >= cols) return;
-    float qv[4][4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) qv[q][k] = (k < R) ? Qm[int64_t(j + q) * R + k] : 0.f;
-    for (int i = t.row_begin; i < t.row_end; ++i) {
-      float pr[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) pr[k] = (k < R) ? Pm[int64_t(i) * R + k] : 0.f;
-      float u[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float s = 0.f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          if (k < R) s += pr[k] * qv[q][k];
-        u[q] = s;
-      }
-      const f4 uv = {u[0], u[1], u[2], u[3]};
-      const int64_t c = mi.offset + int64_t(i) * cols + j;
-      if (update != nullptr) store4_nt(update + c, uv, 4);
-      if (mode != kCompress) momentum_store(mom, x, c, uv, 4, mode, lr, mu);
-    }
-  } else {
-    const int j = t.col_begin + int(threadIdx.x);
-    if (j >= cols) return;
-    float qv[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) qv[k] = (k < R) ? Qm[int64_t(j) * R + k] : 0.f;
-    for (int i = t.row_begin; i < t.row_end; ++i) {
-      float s = 0.f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (k < R) s += Pm[int64_t(i) * R + k] * qv[k];
-      const int64_t c = mi.offset + int64_t(i) * cols + j;
-      if (update != nullptr) update[c] = s;
-      if (mode != kCompress) {
-        const float m1 = mu * mom[c] + s;
-        x[c] = (mode == kNesterov) ? x[c] - lr * (s + mu * m1) : x[c] - lr * m1;
-        mom[c] = m1;
-      }
-    }
-  }
+  if (mi.vec4)
+    update_matrix_tile<4>(t, mi, P, Q, update, mom, x, R, mode, lr, mu);
+  else
+    update_matrix_tile<1>(t, mi, P, Q, update, mom, x, R, mode, lr, mu);
 }
 
 // out_w = errors_w - P_prev Q_prev^T for every compressed matrix (the plain error memory
-// of a deferred-mode error buffer); 1-D tensors are skipped.
+// of a deferred-mode error buffer); 1-D tensors are skipped.  E and out may alias.
 __global__ __launch_bounds__(kStreamThreads) void k_materialize(
     const StreamTile* __restrict__ tiles, const MatInfo* __restrict__ mats, const float* E,
     float* out, const float* __restrict__ Pprev, const float* __restrict__ Qprev, int W, int64_t ld,
@@ -616,14 +740,15 @@ __global__ __launch_bounds__(kStreamThreads) void k_materialize(
   if (c >= t.end || t.mat < 0) return;
   const int64_t valid = t.end - c;
   const f4 up = offset_valid ? lowrank_chunk(mats[t.mat], Pprev, Qprev, c, valid, R) : f4{0.f, 0.f, 0.f, 0.f};
-  for (int w = 0; w < W; ++w) store4_nt(out + w * ld + c, load4_nt(E + w * ld + c) - up, valid);
+  for (int w = 0; w < W; ++w)
+    store4_nt(out + w * ld + c, __builtin_nontemporal_load(reinterpret_cast<const f4*>(E + w * ld + c)) - up, valid);
 }
 
 // ------------------------------------------------------------------ calibration copy
 __global__ __launch_bounds__(256) void k_stream_copy(const float* __restrict__ src, float* __restrict__ dst,
                                                      int64_t n4) {
   for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n4; i += int64_t(gridDim.x) * 256)
-    __builtin_nontemporal_store(load4_nt(src + 4 * i), reinterpret_cast<f4*>(dst + 4 * i));
+    __builtin_nontemporal_store(ld_nt<4>(src + 4 * i), reinterpret_cast<f4*>(dst + 4 * i));
 }
 
 // ------------------------------------------------------------------ host helpers
@@ -645,7 +770,7 @@ psgd_status ensure_tables(psgd_plan* plan, DeviceTables** out) {
   }
   const uint64_t b_mats = align256(plan->mats.size() * sizeof(MatInfo) + 1);
   const uint64_t b_st = align256(plan->stiles.size() * sizeof(StreamTile) + 1);
-  const uint64_t b_rt = align256(plan->rtiles.size() * sizeof(RowTile) + 1);
+  const uint64_t b_rt = align256(plan->s2tiles.size() * sizeof(UpdTile) + 1);
   const uint64_t b_qt = align256(plan->qtiles.size() * sizeof(QTile) + 1);
   const uint64_t b_ut = align256(plan->utiles.size() * sizeof(UpdTile) + 1);
   void* base = nullptr;
@@ -659,7 +784,7 @@ psgd_status ensure_tables(psgd_plan* plan, DeviceTables** out) {
   char* b = static_cast<char*>(base);
   t.mats = reinterpret_cast<MatInfo*>(b);
   t.stiles = reinterpret_cast<StreamTile*>(b + b_mats);
-  t.rtiles = reinterpret_cast<RowTile*>(b + b_mats + b_st);
+  t.s2tiles = reinterpret_cast<UpdTile*>(b + b_mats + b_st);
   t.qtiles = reinterpret_cast<QTile*>(b + b_mats + b_st + b_rt);
   t.utiles = reinterpret_cast<UpdTile*>(b + b_mats + b_st + b_rt + b_qt);
   struct {
@@ -669,7 +794,7 @@ psgd_status ensure_tables(psgd_plan* plan, DeviceTables** out) {
   } copies[] = {
       {t.mats, plan->mats.data(), plan->mats.size() * sizeof(MatInfo)},
       {t.stiles, plan->stiles.data(), plan->stiles.size() * sizeof(StreamTile)},
-      {t.rtiles, plan->rtiles.data(), plan->rtiles.size() * sizeof(RowTile)},
+      {t.s2tiles, plan->s2tiles.data(), plan->s2tiles.size() * sizeof(UpdTile)},
       {t.qtiles, plan->qtiles.data(), plan->qtiles.size() * sizeof(QTile)},
       {t.utiles, plan->utiles.data(), plan->utiles.size() * sizeof(UpdTile)},
   };
@@ -757,7 +882,7 @@ struct StepArgs {
   float* x;
   float lr, mu, inv_w;
   float* Mbar;
-  float* Pbar;
+  float* Ppart;
   float* Qpart;
   const float* ebar_in;  // carried error mean to read (carry mode, valid carry)
   float* ebar_out;       // error mean to write (carry mode)
@@ -766,69 +891,68 @@ struct StepArgs {
   int offset_valid;      // deferred mode: errors hold M of the previous step
   int W, R, mode;
   int64_t ld;
-  unsigned n_st;
+  unsigned n_s2;  // worker-pass tiles
   hipStream_t st;
 };
 
-enum PassKind { kPassMean = 0, kPassApply = 1, kPassDefer = 2 };
+enum PassKind { kPassFirst = 0, kPassApply = 1 };
 
 template <typename GT, int WT>
-void launch_pass(int which, const DeviceTables& dt, const StepArgs& a) {
+void launch_pass(int which, int fp, const DeviceTables& dt, const StepArgs& a) {
   const GT* g = static_cast<const GT*>(a.grads);
-  if (which == kPassMean)
-    hipLaunchKernelGGL((k_ef_mean<GT, WT>), dim3(a.n_st), dim3(kStreamThreads), 0, a.st, dt.stiles, g, a.errors,
-                       a.ebar_in, a.Mbar, a.W, a.ld, a.inv_w);
-  else if (which == kPassApply)
-    hipLaunchKernelGGL((k_apply<GT, WT>), dim3(a.n_st), dim3(kStreamThreads), 0, a.st, dt.stiles, dt.mats, g,
-                       a.errors, a.Mbar, a.p, a.q, a.update, a.mom, a.x, a.ebar_out, a.W, a.ld, a.R, a.mode,
-                       a.lr, a.mu, a.inv_w);
+  const dim3 grid(a.n_s2), block(kStreamThreads);
+  if (which == kPassApply) {
+    hipLaunchKernelGGL((k_apply<GT, WT>), grid, block, 0, a.st, dt.s2tiles, dt.mats, g, a.errors, a.Mbar, a.p,
+                       a.q, a.update, a.mom, a.x, a.ebar_out, a.W, a.ld, a.R, a.mode, a.lr, a.mu, a.inv_w);
+    return;
+  }
+#define PSGD_FIRST(FP)                                                                                     \
+  hipLaunchKernelGGL((k_first<GT, WT, FP>), grid, block, 0, a.st, dt.s2tiles, dt.mats, g, a.errors, a.ebar_in, \
+                     a.Pprev, a.Qprev, a.q, a.Mbar, a.Ppart, a.W, a.ld, a.R, a.inv_w, a.offset_valid)
+  if (fp == kFpDefer)
+    PSGD_FIRST(kFpDefer);
+  else if (fp == kFpCarry)
+    PSGD_FIRST(kFpCarry);
   else
-    hipLaunchKernelGGL((k_ef_defer<GT, WT>), dim3(a.n_st), dim3(kStreamThreads), 0, a.st, dt.stiles, dt.mats,
-                       g, a.errors, a.Pprev, a.Qprev, a.Mbar, a.W, a.ld, a.R, a.inv_w, a.offset_valid);
+    PSGD_FIRST(kFpMean);
+#undef PSGD_FIRST
 }
 
 // Worker-count specialisations of the streaming passes: W in {1,2,4,8,16} unrolls fully,
 // anything else takes the generic loop.
 template <typename GT>
-void launch_pass_w(int which, const DeviceTables& dt, const StepArgs& a) {
+void launch_pass_w(int which, int fp, const DeviceTables& dt, const StepArgs& a) {
   switch (a.W) {
-    case 1: launch_pass<GT, 1>(which, dt, a); break;
-    case 2: launch_pass<GT, 2>(which, dt, a); break;
-    case 4: launch_pass<GT, 4>(which, dt, a); break;
-    case 8: launch_pass<GT, 8>(which, dt, a); break;
-    case 16: launch_pass<GT, 16>(which, dt, a); break;
-    default: launch_pass<GT, 0>(which, dt, a); break;
+    case 1: launch_pass<GT, 1>(which, fp, dt, a); break;
+    case 2: launch_pass<GT, 2>(which, fp, dt, a); break;
+    case 4: launch_pass<GT, 4>(which, fp, dt, a); break;
+    case 8: launch_pass<GT, 8>(which, fp, dt, a); break;
+    case 16: launch_pass<GT, 16>(which, fp, dt, a); break;
+    default: launch_pass<GT, 0>(which, fp, dt, a); break;
   }
 }
 
 template <int R>
 psgd_status launch_all(psgd_plan* plan, const DeviceTables& dt, const StepArgs& a) {
   const bool deferred = (plan->flags & PSGD_FLAG_DEFERRED_ERROR) != 0;
+  const int fp = deferred ? kFpDefer : (a.ebar_in != nullptr ? kFpCarry : kFpMean);
   const bool bf = plan->dtype == PSGD_BF16;
   const unsigned n_mats = unsigned(plan->mats.size());
   hipStream_t stream = a.st;
   psgd_status s;
   auto pass = [&](int which) {
     if (bf)
-      launch_pass_w<bf16>(which, dt, a);
+      launch_pass_w<bf16>(which, fp, dt, a);
     else
-      launch_pass_w<float>(which, dt, a);
+      launch_pass_w<float>(which, fp, dt, a);
   };
 
-  if (deferred)
-    s = launch_timed(plan, stream, kKEfDefer, [&] { pass(kPassDefer); });
-  else
-    s = launch_timed(plan, stream, kKEfMean, [&] { pass(kPassMean); });
+  s = launch_timed(plan, stream, kKFirst, [&] { pass(kPassFirst); });
   if (s != PSGD_OK) return s;
 
   if (n_mats > 0) {
-    s = launch_timed(plan, stream, kKPRows, [&] {
-      hipLaunchKernelGGL(k_p_rows<R>, dim3(unsigned(plan->rtiles.size())), dim3(kRowThreads), 0, stream,
-                         dt.rtiles, dt.mats, a.Mbar, a.q, a.Pbar);
-    });
-    if (s != PSGD_OK) return s;
     s = launch_timed(plan, stream, kKMgs, [&] {
-      hipLaunchKernelGGL(k_mgs<R>, dim3(n_mats), dim3(plan->mgs_threads), 0, stream, dt.mats, a.Pbar, a.p,
+      hipLaunchKernelGGL(k_mgs<R>, dim3(n_mats), dim3(plan->mgs_threads), 0, stream, dt.mats, a.Ppart, a.p,
                          deferred ? a.Pprev : nullptr);
     });
     if (s != PSGD_OK) return s;
@@ -931,7 +1055,7 @@ psgd_status run_step(const char* fn, psgd_plan* plan, const void* grads, float* 
   a.mu = mu;
   a.inv_w = 1.0f / float(plan->n_workers);
   a.Mbar = reinterpret_cast<float*>(ws + plan->ws_mbar);
-  a.Pbar = reinterpret_cast<float*>(ws + plan->ws_pbar);
+  a.Ppart = reinterpret_cast<float*>(ws + plan->ws_ppart);
   a.Qpart = reinterpret_cast<float*>(ws + plan->ws_qpart);
   a.ebar_out = carry ? reinterpret_cast<float*>(ws + plan->ws_ebar) : nullptr;
   a.ebar_in = (carry && use_state) ? a.ebar_out : nullptr;
@@ -942,7 +1066,7 @@ psgd_status run_step(const char* fn, psgd_plan* plan, const void* grads, float* 
   a.R = plan->rank;
   a.mode = mode;
   a.ld = plan->worker_stride;
-  a.n_st = unsigned(plan->stiles.size());
+  a.n_s2 = unsigned(plan->s2tiles.size());
   a.st = static_cast<hipStream_t>(stream);
   switch (plan->rank) {
     case 1: s = launch_all<1>(plan, *dt, a); break;

@@ -16,8 +16,8 @@ namespace psgd {
 
 static thread_local std::string g_last_error;
 
-const char* const kKernelNames[kNumKernels] = {"k_ef_mean", "k_p_rows",   "k_mgs",      "k_q_partial",
-                                               "k_q_reduce", "k_apply",    "k_ef_defer", "k_update"};
+const char* const kKernelNames[kNumKernels] = {"k_first",    "k_mgs",   "k_q_partial",
+                                               "k_q_reduce", "k_apply", "k_update"};
 
 void set_error(const std::string& msg) { g_last_error = msg; }
 
@@ -111,9 +111,14 @@ extern "C" psgd_status psgd_plan_create(const psgd_layer* layers, int32_t n_laye
         mi.vec4 = (cols % 4 == 0) ? 1 : 0;
         mi.qpart_off = qpart;
         qpart += int64_t(mi.nblk) * cols * r;
+        const int64_t strip_cols = int64_t(kStreamThreads) * (mi.vec4 ? 4 : 1);
+        mi.nstrips = int32_t((cols + strip_cols - 1) / strip_cols);
+        mi.ppart_off = plan->ppart_elems;
+        plan->ppart_elems += int64_t(mi.nstrips) * rows * r;
         plan->mats.push_back(mi);
-        p_off += rows * r;
-        q_off += cols * r;
+        // each matrix's P and Q block starts on a 16-byte boundary
+        p_off += round_up(rows * r, 4);
+        q_off += round_up(cols * r, 4);
         plan->matrix_numel += numel;
         plan->max_q_elems_per_matrix = std::max(plan->max_q_elems_per_matrix, cols * r);
         plan->message_bytes += uint64_t(4) * uint64_t((rows + cols) * r);
@@ -144,46 +149,50 @@ extern "C" psgd_status psgd_plan_create(const psgd_layer* layers, int32_t n_laye
         plan->stiles.push_back(t);
       }
     }
-    for (const psgd_layer_info& li : plan->layers) {
-      if (li.compressed) {
-        const MatInfo& m = plan->mats[size_t(li.matrix_index)];
-        const int32_t strip = kQThreads * (m.vec4 ? 4 : 1);
-        for (int32_t r0 = 0; r0 < m.rows; r0 += kUpdRowsPerTile)
-          for (int32_t c0 = 0; c0 < m.cols; c0 += strip) {
+    // Row x column-strip tiles: kSRowsPerTile rows for the worker passes, kUpdRowsPerTile
+    // for the update-only pass; 1-D tensors as flat kStreamTileElems ranges.
+    auto build_tiles = [&](std::vector<UpdTile>& out, int32_t rows_per_tile) {
+      for (const psgd_layer_info& li : plan->layers) {
+        if (li.compressed) {
+          const MatInfo& m = plan->mats[size_t(li.matrix_index)];
+          const int32_t strip = kStreamThreads * (m.vec4 ? 4 : 1);
+          for (int32_t r0 = 0; r0 < m.rows; r0 += rows_per_tile)
+            for (int32_t c0 = 0; c0 < m.cols; c0 += strip) {
+              UpdTile u{};
+              u.mat = li.matrix_index;
+              u.row_begin = r0;
+              u.row_end = std::min(m.rows, r0 + rows_per_tile);
+              u.col_begin = c0;
+              out.push_back(u);
+            }
+        } else {
+          const int64_t end = li.offset + li.rows * li.cols;
+          for (int64_t b = li.offset; b < end; b += kStreamTileElems) {
             UpdTile u{};
-            u.mat = li.matrix_index;
-            u.row_begin = r0;
-            u.row_end = std::min(m.rows, r0 + kUpdRowsPerTile);
-            u.col_begin = c0;
-            plan->utiles.push_back(u);
+            u.begin = b;
+            u.end = std::min<int64_t>(end, b + kStreamTileElems);
+            u.mat = -1;
+            out.push_back(u);
           }
-      } else {
-        const int64_t end = li.offset + li.rows * li.cols;
-        for (int64_t b = li.offset; b < end; b += kStreamTileElems) {
-          UpdTile u{};
-          u.begin = b;
-          u.end = std::min<int64_t>(end, b + kStreamTileElems);
-          u.mat = -1;
-          plan->utiles.push_back(u);
         }
       }
-    }
+    };
+    build_tiles(plan->s2tiles, kSRowsPerTile);
+    build_tiles(plan->utiles, kUpdRowsPerTile);
     for (size_t mi = 0; mi < plan->mats.size(); ++mi) {
       const MatInfo& m = plan->mats[mi];
-      for (int32_t rb = 0; rb < m.rows; rb += kRowsPerTile)
-        plan->rtiles.push_back(RowTile{int32_t(mi), rb, std::min(m.rows, rb + kRowsPerTile), 0});
       const int32_t strip = kQThreads * (m.vec4 ? 4 : 1);
       for (int32_t b = 0; b < m.nblk; ++b)
         for (int32_t c = 0; c < m.cols; c += strip)
           plan->qtiles.push_back(QTile{int32_t(mi), b, c, std::min(m.cols, c + strip)});
     }
 
-    // Workspace: Mbar (same layout as update), P-bar, Q partials; 256-byte aligned.
+    // Workspace: Mbar (same layout as update), P-bar partials, Q partials; 256-byte aligned.
     uint64_t ws = 0;
     plan->ws_mbar = ws;
     ws += uint64_t(round_up(plan->worker_stride * 4, 256));
-    plan->ws_pbar = ws;
-    ws += uint64_t(round_up(std::max<int64_t>(plan->p_elems, 1) * 4, 256));
+    plan->ws_ppart = ws;
+    ws += uint64_t(round_up(std::max<int64_t>(plan->ppart_elems, 1) * 4, 256));
     plan->ws_qpart = ws;
     ws += uint64_t(round_up(std::max<int64_t>(plan->qpart_elems, 1) * 4, 256));
     plan->ws_ebar = ws;

@@ -20,9 +20,10 @@ constexpr int64_t kAlignElems = 64;  // every tensor starts on a 256-byte bounda
 constexpr int kStreamThreads = 256;
 constexpr int kStreamTileElems = kStreamThreads * 4;
 
-// P = Mbar Q: one workgroup of kRowThreads handles kRowsPerTile rows; one wave per row.
-constexpr int kRowThreads = 256;
-constexpr int kRowsPerTile = 4;
+// Worker passes over a compressed matrix: one workgroup of kStreamThreads handles
+// kSRowsPerTile rows x a strip of kStreamThreads*4 columns (kStreamThreads columns when
+// cols % 4 != 0).
+constexpr int kSRowsPerTile = 1;
 
 // Q partials = Mbar^T P over a block of rows and a strip of columns.
 constexpr int kQThreads = 256;
@@ -37,14 +38,15 @@ constexpr int kQRedThreads = 256;
 
 struct MatInfo {
   int64_t offset;     // element offset of the matrix in a worker slice / Mbar / update
-  int64_t p_off;      // element offset of P in p and in the P-bar workspace
+  int64_t p_off;      // element offset of P in p
   int64_t q_off;      // element offset of Q in q
   int64_t qpart_off;  // float offset of this matrix's Q partials in the workspace
+  int64_t ppart_off;  // float offset of this matrix's P-bar partials (nstrips x rows x R)
   int32_t rows, cols;
   int32_t rows_per_blk;  // rows summed into one Q partial
   int32_t nblk;          // number of Q partials (row blocks)
   int32_t vec4;          // 1 if cols % 4 == 0 (rows are 16-byte aligned)
-  int32_t pad_;
+  int32_t nstrips;       // column strips of the worker passes (P-bar partials per row)
 };
 
 struct StreamTile {
@@ -52,10 +54,6 @@ struct StreamTile {
   int64_t end;    // one past the last valid element of the tensor inside this tile
   int32_t mat;    // compressed matrix index, or -1 for an uncompressed tensor
   int32_t pad_;
-};
-
-struct RowTile {
-  int32_t mat, row_begin, row_end, pad_;
 };
 
 struct QTile {
@@ -75,14 +73,14 @@ struct DeviceTables {
   void* base = nullptr;
   MatInfo* mats = nullptr;
   StreamTile* stiles = nullptr;
-  RowTile* rtiles = nullptr;
+  UpdTile* s2tiles = nullptr;
   QTile* qtiles = nullptr;
   UpdTile* utiles = nullptr;
 };
 
 void set_error(const std::string& msg);
 
-enum KernelId { kKEfMean = 0, kKPRows, kKMgs, kKQPartial, kKQReduce, kKApply, kKEfDefer, kKUpdate, kNumKernels };
+enum KernelId { kKFirst = 0, kKMgs, kKQPartial, kKQReduce, kKApply, kKUpdate, kNumKernels };
 extern const char* const kKernelNames[kNumKernels];
 
 struct PendingTiming {
@@ -105,13 +103,13 @@ struct psgd_plan {
   std::vector<psgd_layer_info> layers;
   std::vector<psgd::MatInfo> mats;
   std::vector<psgd::StreamTile> stiles;
-  std::vector<psgd::RowTile> rtiles;
+  std::vector<psgd::UpdTile> s2tiles;
   std::vector<psgd::QTile> qtiles;
   std::vector<psgd::UpdTile> utiles;
   int64_t worker_stride = 0, numel = 0, matrix_numel = 0, vector_numel = 0;
-  int64_t p_elems = 0, q_elems = 0, qpart_elems = 0;
+  int64_t p_elems = 0, q_elems = 0, qpart_elems = 0, ppart_elems = 0;
   int64_t max_q_elems_per_matrix = 0;
-  uint64_t ws_mbar = 0, ws_pbar = 0, ws_qpart = 0, ws_ebar = 0, ws_pprev = 0, ws_qprev = 0, workspace_bytes = 0;
+  uint64_t ws_mbar = 0, ws_ppart = 0, ws_qpart = 0, ws_ebar = 0, ws_pprev = 0, ws_qprev = 0, workspace_bytes = 0;
   int32_t mgs_threads = 64;  // Gram-Schmidt block size: enough for the tallest matrix, <= kMgsThreads
   uint64_t message_bytes = 0, model_bytes = 0, model_bytes_momentum = 0;
   std::map<int, psgd::DeviceTables> dev;  // per HIP device id

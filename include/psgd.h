@@ -35,8 +35,9 @@
  *   - grads and errors are [n_workers][worker_stride] (worker w's slice starts at
  *     w * worker_stride elements); update, momentum and params are [worker_stride];
  *   - p is the concatenation, in layer order, of every compressed matrix's P
- *     (rows x rank, row-major); q likewise of every Q (cols x rank, row-major);
- *     psgd_plan_layer_info returns each matrix's p_offset / q_offset;
+ *     (rows x rank, row-major); q likewise of every Q (cols x rank, row-major); each
+ *     block starts at a multiple of 4 floats (16 bytes), and psgd_plan_layer_info
+ *     returns each matrix's p_offset / q_offset;
  *   - padding elements between tensors are never read for results and never written.
  *
  * Ownership.  The caller owns every buffer passed to a step, including the workspace
@@ -130,8 +131,8 @@ typedef struct psgd_sizes {
   int64_t numel;         /* sum of rows*cols over all tensors */
   int64_t matrix_numel;  /* sum of rows*cols over compressed matrices */
   int64_t vector_numel;  /* sum of rows*cols over uncompressed tensors */
-  int64_t p_elems;       /* sum of rows*rank over compressed matrices */
-  int64_t q_elems;       /* sum of cols*rank over compressed matrices */
+  int64_t p_elems;       /* length of p: rows*rank per compressed matrix, each rounded up to 4 */
+  int64_t q_elems;       /* length of q: cols*rank per compressed matrix, each rounded up to 4 */
   uint64_t workspace_bytes; /* device scratch a step needs (caller-allocated, 256-byte aligned) */
   /* fp32 bytes one worker would send per step in a real data-parallel job:
      P and Q of every compressed matrix plus every uncompressed tensor */
