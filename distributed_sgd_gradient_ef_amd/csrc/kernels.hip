@@ -243,36 +243,6 @@ __device__ __forceinline__ vec_t<V> pq_row(const float (&pr)[4], const float (&q
     return pq_dot(pr, qv[0], R);
 }
 
-// u = P Q^T at the four elements of the flat float4 chunk starting at element c of
-// matrix mi (rows may wrap inside the chunk); lanes past `valid` are zero.
-__device__ __forceinline__ f4 lowrank_chunk(const MatInfo& mi, const float* __restrict__ P,
-                                            const float* __restrict__ Q, int64_t c, int64_t valid, int R) {
-  const float* Pm = P + mi.p_off;
-  const float* Qm = Q + mi.q_off;
-  const int cols = mi.cols;
-  const int e0 = int(c - mi.offset);
-  int i = e0 / cols;
-  int j = e0 - i * cols;
-  float u[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    float pr[4], qr[4];
-    if (q < valid) {
-      load_p_row(pr, Pm, i, R);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) qr[k] = (k < R) ? Qm[int64_t(j) * R + k] : 0.f;
-      u[q] = pq_dot(pr, qr, R);
-    } else {
-      u[q] = 0.f;
-    }
-    if (++j == cols) {
-      j = 0;
-      ++i;
-    }
-  }
-  return f4{u[0], u[1], u[2], u[3]};
-}
-
 // ------------------------------------------------------------------ worker loops
 // Every worker's slice of one chunk (V consecutive elements at c) is loaded before any
 // is used.  WT > 0: the worker count is the compile-time WT (fully unrolled); WT == 0:
@@ -395,46 +365,36 @@ __device__ __forceinline__ void momentum_masked(float* mom, float* x, int64_t c,
 }
 
 // ------------------------------------------------------------------ pass 1
-// Matrix tile: rows [row_begin, row_end) (at most kSRowsPerTile) x the thread's V
-// columns.  FP selects the first-pass form:
+// One wave per tile: a run of rows [row_begin, row_end) x the lanes' V columns each.
+// FP selects the first-pass form:
 //   kFpMean  Mbar = mean_w (G_w + E_w)
 //   kFpCarry Mbar = mean_w G_w + ebar  (ebar = mean of the errors the previous step
 //            stored, carried in the workspace)
 //   kFpDefer M_w = (G_w + E_w) - P_prev Q_prev^T is stored back into E; Mbar = mean_w M_w
-// Then every thread holds its columns' share of P-bar = Mbar Q for each row, and one
-// block reduction writes the tile's partial row sums (one per column strip).
+// For every row, each lane's share of P-bar = Mbar Q over its columns is summed across
+// the wave (fixed butterfly order) and lane 0 writes the strip's partial row sum.
 template <int V, typename GT, int WT, int FP>
 __device__ __forceinline__ void first_matrix_tile(const UpdTile& t, const MatInfo& mi, const GT* G, float* E,
                                                   const float* ebar, const float* Pprev, const float* Qprev,
                                                   const float* Qin, float* Mbar, float* Ppart, int W, int64_t ld,
-                                                  int R, float inv_w, int offset_valid, float* red) {
+                                                  int R, float inv_w, int offset_valid) {
   const int cols = mi.cols;
   const int j = t.col_begin + int(threadIdx.x) * V;
   const bool active = j < cols;
-  const int nrows = t.row_end - t.row_begin;
   float qv[V][4];
   load_q_cols<V>(qv, Qin + mi.q_off, j, R, active);
   float qp[V][4];
   if constexpr (FP == kFpDefer) load_q_cols<V>(qp, Qprev + mi.q_off, j, R, active && offset_valid);
-  float part[kSRowsPerTile][4];
-#pragma unroll
-  for (int r = 0; r < kSRowsPerTile; ++r)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) part[r][k] = 0.f;
-#pragma unroll
-  for (int r = 0; r < kSRowsPerTile; ++r) {
-    if (r < nrows && active) {
-      const int i = t.row_begin + r;
+  const int strip = t.col_begin / (kStreamThreads * V);
+  float* prow = Ppart + mi.ppart_off + int64_t(strip) * mi.rows * R;
+  for (int i = t.row_begin; i < t.row_end; ++i) {
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    if (active) {
       const int64_t c = mi.offset + int64_t(i) * cols + j;
       vec_t<V> mb;
       if constexpr (FP == kFpDefer) {
-        float pp[4];
-        if (offset_valid) {
-          load_p_row(pp, Pprev + mi.p_off, i, R);
-        } else {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) pp[k] = 0.f;
-        }
+        float pp[4] = {0.f, 0.f, 0.f, 0.f};
+        if (offset_valid) load_p_row(pp, Pprev + mi.p_off, i, R);
         mb = update_workers<V, GT, WT>(G, E, W, ld, c, pq_row<V>(pp, qp, R)) * inv_w;
       } else if constexpr (FP == kFpCarry) {
         mb = sum_g<V, GT, WT>(G, W, ld, c) * inv_w + ldv<V>(ebar + c);
@@ -447,29 +407,15 @@ __device__ __forceinline__ void first_matrix_tile(const UpdTile& t, const MatInf
         float s = 0.f;
 #pragma unroll
         for (int q = 0; q < V; ++q) s += lane(mb, q) * qv[q][k];
-        part[r][k] = s;
+        part[k] = s;
       }
     }
-  }
-  // Block reduction of the partial row sums, in a fixed order.
-  const int lane_id = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int r = 0; r < kSRowsPerTile; ++r)
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      if (r < nrows && k < R) {
-        const float v = wave_sum(part[r][k]);
-        if (lane_id == 0) red[(r * 4 + k) * (kStreamThreads / 64) + wave] = v;
+      if (k < R) {
+        const float v = wave_sum(part[k]);
+        if (threadIdx.x == 0) prow[int64_t(i) * R + k] = v;
       }
-  __syncthreads();
-  const int tid = threadIdx.x;
-  if (tid < nrows * 4 && (tid & 3) < R) {
-    float s = 0.f;
-#pragma unroll
-    for (int w = 0; w < kStreamThreads / 64; ++w) s += red[tid * (kStreamThreads / 64) + w];
-    const int r = tid >> 2, k = tid & 3;
-    const int strip = t.col_begin / (kStreamThreads * V);
-    Ppart[mi.ppart_off + (int64_t(strip) * mi.rows + t.row_begin + r) * R + k] = s;
   }
 }
 
@@ -483,7 +429,6 @@ __global__ __launch_bounds__(kStreamThreads) void k_first(const UpdTile* __restr
                                                           const float* __restrict__ Qin, float* __restrict__ Mbar,
                                                           float* __restrict__ Ppart, int W, int64_t ld, int R,
                                                           float inv_w, int offset_valid) {
-  __shared__ float red[kSRowsPerTile * 4 * (kStreamThreads / 64)];
   const UpdTile t = tiles[blockIdx.x];
   if (t.mat < 0) {  // uncompressed tensor: the worker mean of G
     const int64_t c = t.begin + int64_t(threadIdx.x) * 4;
@@ -493,20 +438,35 @@ __global__ __launch_bounds__(kStreamThreads) void k_first(const UpdTile* __restr
   const MatInfo mi = mats[t.mat];
   if (mi.vec4)
     first_matrix_tile<4, GT, WT, FP>(t, mi, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, W, ld, R, inv_w,
-                                     offset_valid, red);
+                                     offset_valid);
   else
     first_matrix_tile<1, GT, WT, FP>(t, mi, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, W, ld, R, inv_w,
-                                     offset_valid, red);
+                                     offset_valid);
 }
 
 // ------------------------------------------------------------------ Gram-Schmidt
 // P-bar = sum over column strips of the partial row sums (fixed strip order), then
 // modified Gram-Schmidt over its R columns in column order.  Dot products and norms
-// accumulate in double.  A column whose residual norm is at most 1e-4 of its norm
-// before orthogonalisation (or zero) becomes zero.  Each thread only touches its own
-// rows, so only the reductions synchronise; the norm of a fresh column and its
-// projection on column 0 share one reduction (both use the unmodified column).  `P2`,
-// if set, receives a copy of the result.
+// accumulate in double; the working column is rounded to float after each
+// projection.  A column whose residual norm is at most 1e-4 of its norm before
+// orthogonalisation (or zero) becomes zero.  The norm of a fresh column and its
+// projection on column 0 share one reduction (both use the unmodified column).
+// Matrices with at most kMgsRowsPerThread rows per thread keep their rows in registers;
+// taller ones work through the output buffer, each thread on its own rows.  `P2`, if
+// set, receives a copy of the result.
+constexpr int kMgsRowsPerThread = 4;
+
+template <int R>
+__device__ __forceinline__ void pbar_row(float (&acc)[R], const float* src, int64_t strip_stride, int nst,
+                                         int i) {
+#pragma unroll
+  for (int k = 0; k < R; ++k) acc[k] = 0.f;
+#pragma unroll 6
+  for (int sidx = 0; sidx < nst; ++sidx)
+#pragma unroll
+    for (int k = 0; k < R; ++k) acc[k] += src[sidx * strip_stride + int64_t(i) * R + k];
+}
+
 template <int R>
 __global__ __launch_bounds__(kMgsThreads) void k_mgs(const MatInfo* __restrict__ mats,
                                                      const float* __restrict__ Ppart,
@@ -516,16 +476,82 @@ __global__ __launch_bounds__(kMgsThreads) void k_mgs(const MatInfo* __restrict__
   const float* src = Ppart + mi.ppart_off;
   float* dst = P + mi.p_off;
   const int n = mi.rows;
+  const int nst = mi.nstrips;
   const int64_t strip_stride = int64_t(n) * R;
+  const int bs = blockDim.x;
+
+  if (n <= bs * kMgsRowsPerThread) {
+    float v[kMgsRowsPerThread][R];
+#pragma unroll
+    for (int r = 0; r < kMgsRowsPerThread; ++r) {
+      const int i = threadIdx.x + r * bs;
+      if (i < n) {
+        pbar_row<R>(v[r], src, strip_stride, nst, i);
+      } else {
+#pragma unroll
+        for (int k = 0; k < R; ++k) v[r][k] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      double s = 0.0, c = 0.0;
+#pragma unroll
+      for (int r = 0; r < kMgsRowsPerThread; ++r) {
+        s += double(v[r][k]) * double(v[r][k]);
+        if (k > 0) c += double(v[r][0]) * double(v[r][k]);
+      }
+      block_sum2(s, c, red);
+      const double before = sqrt(s);
+      double after = before;
+      if (k > 0) {
+#pragma unroll
+        for (int l = 0; l < k; ++l) {
+          if (l > 0) {
+            c = 0.0;
+#pragma unroll
+            for (int r = 0; r < kMgsRowsPerThread; ++r) c += double(v[r][l]) * double(v[r][k]);
+            c = block_sum(c, red);
+          }
+#pragma unroll
+          for (int r = 0; r < kMgsRowsPerThread; ++r) v[r][k] = float(double(v[r][k]) - c * double(v[r][l]));
+        }
+        double s2 = 0.0;
+#pragma unroll
+        for (int r = 0; r < kMgsRowsPerThread; ++r) s2 += double(v[r][k]) * double(v[r][k]);
+        after = sqrt(block_sum(s2, red));
+      }
+      const double scale = (after > 0.0 && after > 1e-4 * before) ? 1.0 / after : 0.0;
+#pragma unroll
+      for (int r = 0; r < kMgsRowsPerThread; ++r) v[r][k] = float(double(v[r][k]) * scale);
+    }
+#pragma unroll
+    for (int r = 0; r < kMgsRowsPerThread; ++r) {
+      const int i = threadIdx.x + r * bs;
+      if (i < n) {
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+          dst[int64_t(i) * R + k] = v[r][k];
+          if (P2 != nullptr) P2[mi.p_off + int64_t(i) * R + k] = v[r][k];
+        }
+      }
+    }
+    return;
+  }
+
+  // Tall matrices: the same steps through the output buffer.
+  for (int i = threadIdx.x; i < n; i += bs) {
+    float acc[R];
+    pbar_row<R>(acc, src, strip_stride, nst, i);
+#pragma unroll
+    for (int k = 0; k < R; ++k) dst[int64_t(i) * R + k] = acc[k];
+  }
   for (int k = 0; k < R; ++k) {
     double s = 0.0, c = 0.0;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    for (int i = threadIdx.x; i < n; i += bs) {
       const int64_t o = int64_t(i) * R;
-      float v = 0.f;
-      for (int sidx = 0; sidx < mi.nstrips; ++sidx) v += src[sidx * strip_stride + o + k];
-      dst[o + k] = v;
-      s += double(v) * double(v);
-      if (k > 0) c += double(dst[o]) * double(v);
+      const double v = dst[o + k];
+      s += v * v;
+      if (k > 0) c += double(dst[o]) * v;
     }
     block_sum2(s, c, red);
     const double before = sqrt(s);
@@ -534,24 +560,24 @@ __global__ __launch_bounds__(kMgsThreads) void k_mgs(const MatInfo* __restrict__
       for (int l = 0; l < k; ++l) {
         if (l > 0) {
           c = 0.0;
-          for (int i = threadIdx.x; i < n; i += blockDim.x)
+          for (int i = threadIdx.x; i < n; i += bs)
             c += double(dst[int64_t(i) * R + l]) * double(dst[int64_t(i) * R + k]);
           c = block_sum(c, red);
         }
-        for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        for (int i = threadIdx.x; i < n; i += bs) {
           const int64_t o = int64_t(i) * R;
           dst[o + k] = float(double(dst[o + k]) - c * double(dst[o + l]));
         }
       }
       double s2 = 0.0;
-      for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      for (int i = threadIdx.x; i < n; i += bs) {
         const double v = dst[int64_t(i) * R + k];
         s2 += v * v;
       }
       after = sqrt(block_sum(s2, red));
     }
     const double scale = (after > 0.0 && after > 1e-4 * before) ? 1.0 / after : 0.0;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    for (int i = threadIdx.x; i < n; i += bs) {
       const int64_t o = int64_t(i) * R + k;
       const float v = float(double(dst[o]) * scale);
       dst[o] = v;
@@ -708,7 +734,7 @@ __device__ __forceinline__ void update_matrix_tile(const UpdTile& t, const MatIn
   }
 }
 
-__global__ __launch_bounds__(kQThreads) void k_update(
+__global__ __launch_bounds__(kUpdThreads) void k_update(
     const UpdTile* __restrict__ tiles, const MatInfo* __restrict__ mats, const float* __restrict__ Mbar,
     const float* __restrict__ P, const float* __restrict__ Q, float* __restrict__ update,
     float* __restrict__ mom, float* __restrict__ x, int R, int mode, float lr, float mu) {
@@ -730,18 +756,38 @@ __global__ __launch_bounds__(kQThreads) void k_update(
 }
 
 // out_w = errors_w - P_prev Q_prev^T for every compressed matrix (the plain error memory
-// of a deferred-mode error buffer); 1-D tensors are skipped.  E and out may alias.
+// of a deferred-mode error buffer), on the worker-pass tiles; 1-D tensors are skipped.
+// The subtracted value is computed exactly as the first pass subtracts it.  E and out
+// may alias.
+template <int V>
+__device__ __forceinline__ void materialize_tile(const UpdTile& t, const MatInfo& mi, const float* E, float* out,
+                                                 const float* Pprev, const float* Qprev, int W, int64_t ld, int R,
+                                                 int offset_valid) {
+  const int cols = mi.cols;
+  const int j = t.col_begin + int(threadIdx.x) * V;
+  if (j >= cols) return;
+  float qp[V][4];
+  load_q_cols<V>(qp, Qprev + mi.q_off, j, R, offset_valid != 0);
+  for (int i = t.row_begin; i < t.row_end; ++i) {
+    float pp[4] = {0.f, 0.f, 0.f, 0.f};
+    if (offset_valid) load_p_row(pp, Pprev + mi.p_off, i, R);
+    const vec_t<V> up = pq_row<V>(pp, qp, R);
+    const int64_t c = mi.offset + int64_t(i) * cols + j;
+    for (int w = 0; w < W; ++w) st_nt<V>(out + w * ld + c, ld_nt<V>(E + w * ld + c) - up);
+  }
+}
+
 __global__ __launch_bounds__(kStreamThreads) void k_materialize(
-    const StreamTile* __restrict__ tiles, const MatInfo* __restrict__ mats, const float* E,
-    float* out, const float* __restrict__ Pprev, const float* __restrict__ Qprev, int W, int64_t ld,
-    int R, int offset_valid) {
-  const StreamTile t = tiles[blockIdx.x];
-  const int64_t c = t.begin + int64_t(threadIdx.x) * 4;
-  if (c >= t.end || t.mat < 0) return;
-  const int64_t valid = t.end - c;
-  const f4 up = offset_valid ? lowrank_chunk(mats[t.mat], Pprev, Qprev, c, valid, R) : f4{0.f, 0.f, 0.f, 0.f};
-  for (int w = 0; w < W; ++w)
-    store4_nt(out + w * ld + c, __builtin_nontemporal_load(reinterpret_cast<const f4*>(E + w * ld + c)) - up, valid);
+    const UpdTile* __restrict__ tiles, const MatInfo* __restrict__ mats, const float* E, float* out,
+    const float* __restrict__ Pprev, const float* __restrict__ Qprev, int W, int64_t ld, int R,
+    int offset_valid) {
+  const UpdTile t = tiles[blockIdx.x];
+  if (t.mat < 0) return;
+  const MatInfo mi = mats[t.mat];
+  if (mi.vec4)
+    materialize_tile<4>(t, mi, E, out, Pprev, Qprev, W, ld, R, offset_valid);
+  else
+    materialize_tile<1>(t, mi, E, out, Pprev, Qprev, W, ld, R, offset_valid);
 }
 
 // ------------------------------------------------------------------ calibration copy
@@ -769,12 +815,11 @@ psgd_status ensure_tables(psgd_plan* plan, DeviceTables** out) {
     return PSGD_OK;
   }
   const uint64_t b_mats = align256(plan->mats.size() * sizeof(MatInfo) + 1);
-  const uint64_t b_st = align256(plan->stiles.size() * sizeof(StreamTile) + 1);
   const uint64_t b_rt = align256(plan->s2tiles.size() * sizeof(UpdTile) + 1);
   const uint64_t b_qt = align256(plan->qtiles.size() * sizeof(QTile) + 1);
   const uint64_t b_ut = align256(plan->utiles.size() * sizeof(UpdTile) + 1);
   void* base = nullptr;
-  e = hipMalloc(&base, b_mats + b_st + b_rt + b_qt + b_ut);
+  e = hipMalloc(&base, b_mats + b_rt + b_qt + b_ut);
   if (e != hipSuccess) {
     set_error(std::string("hipMalloc of the plan's device tables: ") + hipGetErrorString(e));
     return PSGD_ERR_NO_MEMORY;
@@ -783,17 +828,15 @@ psgd_status ensure_tables(psgd_plan* plan, DeviceTables** out) {
   t.base = base;
   char* b = static_cast<char*>(base);
   t.mats = reinterpret_cast<MatInfo*>(b);
-  t.stiles = reinterpret_cast<StreamTile*>(b + b_mats);
-  t.s2tiles = reinterpret_cast<UpdTile*>(b + b_mats + b_st);
-  t.qtiles = reinterpret_cast<QTile*>(b + b_mats + b_st + b_rt);
-  t.utiles = reinterpret_cast<UpdTile*>(b + b_mats + b_st + b_rt + b_qt);
+  t.s2tiles = reinterpret_cast<UpdTile*>(b + b_mats);
+  t.qtiles = reinterpret_cast<QTile*>(b + b_mats + b_rt);
+  t.utiles = reinterpret_cast<UpdTile*>(b + b_mats + b_rt + b_qt);
   struct {
     void* dst;
     const void* src;
     size_t bytes;
   } copies[] = {
       {t.mats, plan->mats.data(), plan->mats.size() * sizeof(MatInfo)},
-      {t.stiles, plan->stiles.data(), plan->stiles.size() * sizeof(StreamTile)},
       {t.s2tiles, plan->s2tiles.data(), plan->s2tiles.size() * sizeof(UpdTile)},
       {t.qtiles, plan->qtiles.data(), plan->qtiles.size() * sizeof(QTile)},
       {t.utiles, plan->utiles.data(), plan->utiles.size() * sizeof(UpdTile)},
@@ -970,7 +1013,7 @@ psgd_status launch_all(psgd_plan* plan, const DeviceTables& dt, const StepArgs& 
   }
   if (deferred)
     return launch_timed(plan, stream, kKUpdate, [&] {
-      hipLaunchKernelGGL(k_update, dim3(unsigned(plan->utiles.size())), dim3(kQThreads), 0, stream, dt.utiles,
+      hipLaunchKernelGGL(k_update, dim3(unsigned(plan->utiles.size())), dim3(kUpdThreads), 0, stream, dt.utiles,
                          dt.mats, a.Mbar, a.p, a.q, a.update, a.mom, a.x, R, a.mode, a.lr, a.mu);
     });
   return launch_timed(plan, stream, kKApply, [&] { pass(kPassApply); });
@@ -1157,8 +1200,8 @@ extern "C" psgd_status psgd_errors_materialize(psgd_plan* plan, const float* err
   char* ws = static_cast<char*>(workspace);
   const float* Pprev = deferred ? reinterpret_cast<const float*>(ws + plan->ws_pprev) : nullptr;
   const float* Qprev = deferred ? reinterpret_cast<const float*>(ws + plan->ws_qprev) : nullptr;
-  hipLaunchKernelGGL(k_materialize, dim3(unsigned(plan->stiles.size())), dim3(kStreamThreads), 0,
-                     static_cast<hipStream_t>(stream), dt->stiles, dt->mats, errors, out, Pprev, Qprev,
+  hipLaunchKernelGGL(k_materialize, dim3(unsigned(plan->s2tiles.size())), dim3(kStreamThreads), 0,
+                     static_cast<hipStream_t>(stream), dt->s2tiles, dt->mats, errors, out, Pprev, Qprev,
                      plan->n_workers, plan->worker_stride, plan->rank, offset ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail("launch k_materialize", e);

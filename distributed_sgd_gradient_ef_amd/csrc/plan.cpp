@@ -138,24 +138,13 @@ extern "C" psgd_status psgd_plan_create(const psgd_layer* layers, int32_t n_laye
     plan->q_elems = q_off;
     plan->qpart_elems = qpart;
 
-    // Work-lists.  Streaming tiles cover each tensor in kStreamTileElems pieces.
-    for (const psgd_layer_info& li : plan->layers) {
-      const int64_t end = li.offset + li.rows * li.cols;
-      for (int64_t b = li.offset; b < end; b += kStreamTileElems) {
-        StreamTile t{};
-        t.begin = b;
-        t.end = std::min<int64_t>(end, b + kStreamTileElems);
-        t.mat = li.matrix_index;
-        plan->stiles.push_back(t);
-      }
-    }
-    // Row x column-strip tiles: kSRowsPerTile rows for the worker passes, kUpdRowsPerTile
-    // for the update-only pass; 1-D tensors as flat kStreamTileElems ranges.
-    auto build_tiles = [&](std::vector<UpdTile>& out, int32_t rows_per_tile) {
+    // Work-lists: row x column-strip tiles over the compressed matrices, flat ranges
+    // over the 1-D tensors.
+    auto build_tiles = [&](std::vector<UpdTile>& out, int32_t rows_per_tile, int32_t threads) {
       for (const psgd_layer_info& li : plan->layers) {
         if (li.compressed) {
           const MatInfo& m = plan->mats[size_t(li.matrix_index)];
-          const int32_t strip = kStreamThreads * (m.vec4 ? 4 : 1);
+          const int32_t strip = threads * (m.vec4 ? 4 : 1);
           for (int32_t r0 = 0; r0 < m.rows; r0 += rows_per_tile)
             for (int32_t c0 = 0; c0 < m.cols; c0 += strip) {
               UpdTile u{};
@@ -167,18 +156,21 @@ extern "C" psgd_status psgd_plan_create(const psgd_layer* layers, int32_t n_laye
             }
         } else {
           const int64_t end = li.offset + li.rows * li.cols;
-          for (int64_t b = li.offset; b < end; b += kStreamTileElems) {
+          for (int64_t b = li.offset; b < end; b += int64_t(threads) * 4) {
             UpdTile u{};
             u.begin = b;
-            u.end = std::min<int64_t>(end, b + kStreamTileElems);
+            u.end = std::min<int64_t>(end, b + int64_t(threads) * 4);
             u.mat = -1;
             out.push_back(u);
           }
         }
       }
     };
-    build_tiles(plan->s2tiles, kSRowsPerTile);
-    build_tiles(plan->utiles, kUpdRowsPerTile);
+    int64_t row_strips = 0;
+    for (const MatInfo& m : plan->mats) row_strips += int64_t(m.rows) * m.nstrips;
+    plan->worker_rows_per_tile = int32_t(std::max<int64_t>(1, (row_strips + kMaxWorkerTiles - 1) / kMaxWorkerTiles));
+    build_tiles(plan->s2tiles, plan->worker_rows_per_tile, kStreamThreads);
+    build_tiles(plan->utiles, kUpdRowsPerTile, kUpdThreads);
     for (size_t mi = 0; mi < plan->mats.size(); ++mi) {
       const MatInfo& m = plan->mats[mi];
       const int32_t strip = kQThreads * (m.vec4 ? 4 : 1);

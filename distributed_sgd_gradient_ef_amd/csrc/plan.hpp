@@ -14,16 +14,19 @@ namespace psgd {
 
 constexpr int64_t kAlignElems = 64;  // every tensor starts on a 256-byte boundary
 
-// Streaming passes (EF add + worker mean, and the final error/update pass): one
-// workgroup of kStreamThreads handles one tile of up to kStreamTileElems consecutive
-// elements of one tensor, one float4 chunk per thread.
-constexpr int kStreamThreads = 256;
+// Worker passes (the first pass and the eager error/update pass): one workgroup is one
+// wave of kStreamThreads lanes.  Over a compressed matrix it handles a run of rows x a
+// strip of kStreamThreads*4 columns (kStreamThreads columns when cols % 4 != 0); over a
+// 1-D tensor, kStreamTileElems consecutive elements, one float4 chunk per lane.  A
+// plan uses as many rows per tile as keep its tile count under kMaxWorkerTiles.
+constexpr int kStreamThreads = 64;
 constexpr int kStreamTileElems = kStreamThreads * 4;
+constexpr int64_t kMaxWorkerTiles = 65536;
 
-// Worker passes over a compressed matrix: one workgroup of kStreamThreads handles
-// kSRowsPerTile rows x a strip of kStreamThreads*4 columns (kStreamThreads columns when
-// cols % 4 != 0).
-constexpr int kSRowsPerTile = 1;
+// Update-only pass (deferred mode): workgroups of kUpdThreads over kUpdRowsPerTile rows
+// x a strip of kUpdThreads*4 columns, or kUpdThreads*4 elements of a 1-D tensor.
+constexpr int kUpdThreads = 256;
+constexpr int kUpdRowsPerTile = 8;
 
 // Q partials = Mbar^T P over a block of rows and a strip of columns.
 constexpr int kQThreads = 256;
@@ -49,30 +52,21 @@ struct MatInfo {
   int32_t nstrips;       // column strips of the worker passes (P-bar partials per row)
 };
 
-struct StreamTile {
-  int64_t begin;  // first element (multiple of 4) inside a worker slice
-  int64_t end;    // one past the last valid element of the tensor inside this tile
-  int32_t mat;    // compressed matrix index, or -1 for an uncompressed tensor
-  int32_t pad_;
-};
-
 struct QTile {
   int32_t mat, blk, col_begin, col_end;
 };
 
-// Update pass tiles: for a compressed matrix, rows [row_begin, row_end) x a strip of
-// kQThreads*4 (cols % 4 == 0) or kQThreads columns from col_begin; for an uncompressed
-// tensor (mat < 0), the flat element range [begin, end) as in a StreamTile.
+// Tiles of the worker and update passes: for a compressed matrix, rows
+// [row_begin, row_end) x a column strip starting at col_begin; for an uncompressed
+// tensor (mat < 0), the flat element range [begin, end) (begin a multiple of 4).
 struct UpdTile {
   int64_t begin, end;
   int32_t mat, row_begin, row_end, col_begin;
 };
-constexpr int kUpdRowsPerTile = 8;
 
 struct DeviceTables {
   void* base = nullptr;
   MatInfo* mats = nullptr;
-  StreamTile* stiles = nullptr;
   UpdTile* s2tiles = nullptr;
   QTile* qtiles = nullptr;
   UpdTile* utiles = nullptr;
@@ -102,7 +96,6 @@ struct psgd_plan {
   uint32_t flags = 0;
   std::vector<psgd_layer_info> layers;
   std::vector<psgd::MatInfo> mats;
-  std::vector<psgd::StreamTile> stiles;
   std::vector<psgd::UpdTile> s2tiles;
   std::vector<psgd::QTile> qtiles;
   std::vector<psgd::UpdTile> utiles;
@@ -110,7 +103,8 @@ struct psgd_plan {
   int64_t p_elems = 0, q_elems = 0, qpart_elems = 0, ppart_elems = 0;
   int64_t max_q_elems_per_matrix = 0;
   uint64_t ws_mbar = 0, ws_ppart = 0, ws_qpart = 0, ws_ebar = 0, ws_pprev = 0, ws_qprev = 0, workspace_bytes = 0;
-  int32_t mgs_threads = 64;  // Gram-Schmidt block size: enough for the tallest matrix, <= kMgsThreads
+  int32_t mgs_threads = 64;
+  int32_t worker_rows_per_tile = 1;  // Gram-Schmidt block size: enough for the tallest matrix, <= kMgsThreads
   uint64_t message_bytes = 0, model_bytes = 0, model_bytes_momentum = 0;
   std::map<int, psgd::DeviceTables> dev;  // per HIP device id
   // cross-step state: the carried error mean (PSGD_FLAG_CARRY_ERROR_MEAN) or the deferred
