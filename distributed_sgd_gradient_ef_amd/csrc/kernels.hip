@@ -365,7 +365,8 @@ __device__ __forceinline__ void momentum_masked(float* mom, float* x, int64_t c,
 }
 
 // ------------------------------------------------------------------ pass 1
-// One wave per tile: a run of rows [row_begin, row_end) x the lanes' V columns each.
+// One wave per row of a tile: row row_begin + blockIdx.y x the lanes' V columns each
+// (a tile spans several rows only for plans too large for one table entry per row).
 // FP selects the first-pass form:
 //   kFpMean  Mbar = mean_w (G_w + E_w)
 //   kFpCarry Mbar = mean_w G_w + ebar  (ebar = mean of the errors the previous step
@@ -387,7 +388,9 @@ __device__ __forceinline__ void first_matrix_tile(const UpdTile& t, const MatInf
   if constexpr (FP == kFpDefer) load_q_cols<V>(qp, Qprev + mi.q_off, j, R, active && offset_valid);
   const int strip = t.col_begin / (kStreamThreads * V);
   float* prow = Ppart + mi.ppart_off + int64_t(strip) * mi.rows * R;
-  for (int i = t.row_begin; i < t.row_end; ++i) {
+  {
+    const int i = t.row_begin + int(blockIdx.y);
+    if (i >= t.row_end) return;
     float part[4] = {0.f, 0.f, 0.f, 0.f};
     if (active) {
       const int64_t c = mi.offset + int64_t(i) * cols + j;
@@ -431,6 +434,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_first(const UpdTile* __restr
                                                           float inv_w, int offset_valid) {
   const UpdTile t = tiles[blockIdx.x];
   if (t.mat < 0) {  // uncompressed tensor: the worker mean of G
+    if (blockIdx.y != 0) return;
     const int64_t c = t.begin + int64_t(threadIdx.x) * 4;
     if (c < t.end) store4(Mbar + c, sum_g<4, GT, WT>(G, W, ld, c) * inv_w, t.end - c);
     return;
@@ -672,7 +676,9 @@ __device__ __forceinline__ void apply_matrix_tile(const UpdTile& t, const MatInf
   if (j >= cols) return;
   float qv[V][4];
   load_q_cols<V>(qv, Q + mi.q_off, j, R, true);
-  for (int i = t.row_begin; i < t.row_end; ++i) {
+  {
+    const int i = t.row_begin + int(blockIdx.y);
+    if (i >= t.row_end) return;
     float pr[4];
     load_p_row(pr, P + mi.p_off, i, R);
     const vec_t<V> u = pq_row<V>(pr, qv, R);
@@ -693,6 +699,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_apply(
     float mu, float inv_w) {
   const UpdTile t = tiles[blockIdx.x];
   if (t.mat < 0) {
+    if (blockIdx.y != 0) return;
     const int64_t c = t.begin + int64_t(threadIdx.x) * 4;
     if (c >= t.end) return;
     const int64_t valid = t.end - c;
@@ -768,7 +775,9 @@ __device__ __forceinline__ void materialize_tile(const UpdTile& t, const MatInfo
   if (j >= cols) return;
   float qp[V][4];
   load_q_cols<V>(qp, Qprev + mi.q_off, j, R, offset_valid != 0);
-  for (int i = t.row_begin; i < t.row_end; ++i) {
+  {
+    const int i = t.row_begin + int(blockIdx.y);
+    if (i >= t.row_end) return;
     float pp[4] = {0.f, 0.f, 0.f, 0.f};
     if (offset_valid) load_p_row(pp, Pprev + mi.p_off, i, R);
     const vec_t<V> up = pq_row<V>(pp, qp, R);
@@ -935,6 +944,7 @@ struct StepArgs {
   int W, R, mode;
   int64_t ld;
   unsigned n_s2;  // worker-pass tiles
+  unsigned rows_per_tile;  // grid.y of the worker passes: one workgroup per row of a tile
   hipStream_t st;
 };
 
@@ -943,7 +953,7 @@ enum PassKind { kPassFirst = 0, kPassApply = 1 };
 template <typename GT, int WT>
 void launch_pass(int which, int fp, const DeviceTables& dt, const StepArgs& a) {
   const GT* g = static_cast<const GT*>(a.grads);
-  const dim3 grid(a.n_s2), block(kStreamThreads);
+  const dim3 grid(a.n_s2, a.rows_per_tile), block(kStreamThreads);
   if (which == kPassApply) {
     hipLaunchKernelGGL((k_apply<GT, WT>), grid, block, 0, a.st, dt.s2tiles, dt.mats, g, a.errors, a.Mbar, a.p,
                        a.q, a.update, a.mom, a.x, a.ebar_out, a.W, a.ld, a.R, a.mode, a.lr, a.mu, a.inv_w);
@@ -1110,6 +1120,7 @@ psgd_status run_step(const char* fn, psgd_plan* plan, const void* grads, float* 
   a.mode = mode;
   a.ld = plan->worker_stride;
   a.n_s2 = unsigned(plan->s2tiles.size());
+  a.rows_per_tile = unsigned(plan->worker_rows_per_tile);
   a.st = static_cast<hipStream_t>(stream);
   switch (plan->rank) {
     case 1: s = launch_all<1>(plan, *dt, a); break;
@@ -1200,7 +1211,8 @@ extern "C" psgd_status psgd_errors_materialize(psgd_plan* plan, const float* err
   char* ws = static_cast<char*>(workspace);
   const float* Pprev = deferred ? reinterpret_cast<const float*>(ws + plan->ws_pprev) : nullptr;
   const float* Qprev = deferred ? reinterpret_cast<const float*>(ws + plan->ws_qprev) : nullptr;
-  hipLaunchKernelGGL(k_materialize, dim3(unsigned(plan->s2tiles.size())), dim3(kStreamThreads), 0,
+  hipLaunchKernelGGL(k_materialize, dim3(unsigned(plan->s2tiles.size()), unsigned(plan->worker_rows_per_tile)),
+                     dim3(kStreamThreads), 0,
                      static_cast<hipStream_t>(stream), dt->s2tiles, dt->mats, errors, out, Pprev, Qprev,
                      plan->n_workers, plan->worker_stride, plan->rank, offset ? 1 : 0);
   hipError_t e = hipGetLastError();

@@ -15,10 +15,11 @@ namespace psgd {
 constexpr int64_t kAlignElems = 64;  // every tensor starts on a 256-byte boundary
 
 // Worker passes (the first pass and the eager error/update pass): one workgroup is one
-// wave of kStreamThreads lanes.  Over a compressed matrix it handles a run of rows x a
-// strip of kStreamThreads*4 columns (kStreamThreads columns when cols % 4 != 0); over a
-// 1-D tensor, kStreamTileElems consecutive elements, one float4 chunk per lane.  A
-// plan uses as many rows per tile as keep its tile count under kMaxWorkerTiles.
+// wave of kStreamThreads lanes.  Over a compressed matrix it handles one row x a strip
+// of kStreamThreads*4 columns (kStreamThreads columns when cols % 4 != 0); over a 1-D
+// tensor, kStreamTileElems consecutive elements, one float4 chunk per lane.  A tile
+// table entry covers as many rows as keep the table under kMaxWorkerTiles entries, and
+// the launch's second grid dimension walks those rows, one workgroup each.
 constexpr int kStreamThreads = 64;
 constexpr int kStreamTileElems = kStreamThreads * 4;
 constexpr int64_t kMaxWorkerTiles = 65536;
@@ -30,7 +31,7 @@ constexpr int kUpdRowsPerTile = 8;
 
 // Q partials = Mbar^T P over a block of rows and a strip of columns.
 constexpr int kQThreads = 256;
-constexpr int kQTargetRowsPerBlock = 32;
+constexpr int kQTargetRowsPerBlock = 64;
 constexpr int kQMaxRowBlocks = 32;
 
 // Gram-Schmidt: one workgroup per matrix.
