@@ -28,6 +28,7 @@
 // thread keeps Q of its four columns in registers, reads P one row at a time (the same
 // address across the wave), and has every worker's float4 of a row in flight at once.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -891,9 +892,12 @@ psgd_status take_event(psgd_plan* plan, hipEvent_t* ev) {
   return e == hipSuccess ? PSGD_OK : hip_fail("hipEventCreate", e);
 }
 
-// Launch through `launch()`; with timing enabled, bracket it with two events on `st`.
-template <typename F>
-psgd_status launch_timed(psgd_plan* plan, hipStream_t st, int kid, F&& launch) {
+// Launch `kernel` on `st`.  With timing enabled the launch goes through
+// hipExtLaunchKernelGGL with a start and a stop event, which the runtime records with
+// the kernel's own dispatch, so the elapsed time is the kernel's execution alone.
+template <typename... KArgs, typename... Args>
+psgd_status launch_k(psgd_plan* plan, int kid, void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t st,
+                     Args... args) {
   hipEvent_t a = nullptr, b = nullptr;
   if (plan->timing) {
     psgd_status s = take_event(plan, &a);
@@ -902,16 +906,11 @@ psgd_status launch_timed(psgd_plan* plan, hipStream_t st, int kid, F&& launch) {
       if (a) plan->event_pool.push_back(a);
       return s;
     }
-    hipError_t e = hipEventRecord(a, st);
-    if (e != hipSuccess) {
-      plan->event_pool.push_back(a);
-      plan->event_pool.push_back(b);
-      return hip_fail("hipEventRecord", e);
-    }
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, a, b, 0, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
   }
-  launch();
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess && plan->timing) e = hipEventRecord(b, st);
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     if (plan->timing) {
       plan->event_pool.push_back(a);
@@ -951,37 +950,29 @@ struct StepArgs {
 enum PassKind { kPassFirst = 0, kPassApply = 1 };
 
 template <typename GT, int WT>
-void launch_pass(int which, int fp, const DeviceTables& dt, const StepArgs& a) {
+psgd_status launch_pass(psgd_plan* plan, int which, int fp, const DeviceTables& dt, const StepArgs& a) {
   const GT* g = static_cast<const GT*>(a.grads);
   const dim3 grid(a.n_s2, a.rows_per_tile), block(kStreamThreads);
-  if (which == kPassApply) {
-    hipLaunchKernelGGL((k_apply<GT, WT>), grid, block, 0, a.st, dt.s2tiles, dt.mats, g, a.errors, a.Mbar, a.p,
-                       a.q, a.update, a.mom, a.x, a.ebar_out, a.W, a.ld, a.R, a.mode, a.lr, a.mu, a.inv_w);
-    return;
-  }
-#define PSGD_FIRST(FP)                                                                                     \
-  hipLaunchKernelGGL((k_first<GT, WT, FP>), grid, block, 0, a.st, dt.s2tiles, dt.mats, g, a.errors, a.ebar_in, \
-                     a.Pprev, a.Qprev, a.q, a.Mbar, a.Ppart, a.W, a.ld, a.R, a.inv_w, a.offset_valid)
-  if (fp == kFpDefer)
-    PSGD_FIRST(kFpDefer);
-  else if (fp == kFpCarry)
-    PSGD_FIRST(kFpCarry);
-  else
-    PSGD_FIRST(kFpMean);
-#undef PSGD_FIRST
+  if (which == kPassApply)
+    return launch_k(plan, kKApply, k_apply<GT, WT>, grid, block, a.st, dt.s2tiles, dt.mats, g, a.errors, a.Mbar, a.p,
+                    a.q, a.update, a.mom, a.x, a.ebar_out, a.W, a.ld, a.R, a.mode, a.lr, a.mu, a.inv_w);
+  auto first = fp == kFpDefer ? k_first<GT, WT, kFpDefer> : fp == kFpCarry ? k_first<GT, WT, kFpCarry>
+                                                                           : k_first<GT, WT, kFpMean>;
+  return launch_k(plan, kKFirst, first, grid, block, a.st, dt.s2tiles, dt.mats, g, a.errors, a.ebar_in, a.Pprev,
+                  a.Qprev, a.q, a.Mbar, a.Ppart, a.W, a.ld, a.R, a.inv_w, a.offset_valid);
 }
 
-// Worker-count specialisations of the streaming passes: W in {1,2,4,8,16} unrolls fully,
+// Worker-count specialisations of the worker passes: W in {1,2,4,8,16} unrolls fully,
 // anything else takes the generic loop.
 template <typename GT>
-void launch_pass_w(int which, int fp, const DeviceTables& dt, const StepArgs& a) {
+psgd_status launch_pass_w(psgd_plan* plan, int which, int fp, const DeviceTables& dt, const StepArgs& a) {
   switch (a.W) {
-    case 1: launch_pass<GT, 1>(which, fp, dt, a); break;
-    case 2: launch_pass<GT, 2>(which, fp, dt, a); break;
-    case 4: launch_pass<GT, 4>(which, fp, dt, a); break;
-    case 8: launch_pass<GT, 8>(which, fp, dt, a); break;
-    case 16: launch_pass<GT, 16>(which, fp, dt, a); break;
-    default: launch_pass<GT, 0>(which, fp, dt, a); break;
+    case 1: return launch_pass<GT, 1>(plan, which, fp, dt, a);
+    case 2: return launch_pass<GT, 2>(plan, which, fp, dt, a);
+    case 4: return launch_pass<GT, 4>(plan, which, fp, dt, a);
+    case 8: return launch_pass<GT, 8>(plan, which, fp, dt, a);
+    case 16: return launch_pass<GT, 16>(plan, which, fp, dt, a);
+    default: return launch_pass<GT, 0>(plan, which, fp, dt, a);
   }
 }
 
@@ -994,39 +985,27 @@ psgd_status launch_all(psgd_plan* plan, const DeviceTables& dt, const StepArgs& 
   hipStream_t stream = a.st;
   psgd_status s;
   auto pass = [&](int which) {
-    if (bf)
-      launch_pass_w<bf16>(which, fp, dt, a);
-    else
-      launch_pass_w<float>(which, fp, dt, a);
+    return bf ? launch_pass_w<bf16>(plan, which, fp, dt, a) : launch_pass_w<float>(plan, which, fp, dt, a);
   };
 
-  s = launch_timed(plan, stream, kKFirst, [&] { pass(kPassFirst); });
-  if (s != PSGD_OK) return s;
-
+  if ((s = pass(kPassFirst)) != PSGD_OK) return s;
   if (n_mats > 0) {
-    s = launch_timed(plan, stream, kKMgs, [&] {
-      hipLaunchKernelGGL(k_mgs<R>, dim3(n_mats), dim3(plan->mgs_threads), 0, stream, dt.mats, a.Ppart, a.p,
-                         deferred ? a.Pprev : nullptr);
-    });
+    s = launch_k(plan, kKMgs, k_mgs<R>, dim3(n_mats), dim3(plan->mgs_threads), stream, dt.mats,
+                 static_cast<const float*>(a.Ppart), a.p, deferred ? a.Pprev : nullptr);
     if (s != PSGD_OK) return s;
-    s = launch_timed(plan, stream, kKQPartial, [&] {
-      hipLaunchKernelGGL(k_q_partial<R>, dim3(unsigned(plan->qtiles.size())), dim3(kQThreads), 0, stream,
-                         dt.qtiles, dt.mats, a.Mbar, a.p, a.Qpart);
-    });
+    s = launch_k(plan, kKQPartial, k_q_partial<R>, dim3(unsigned(plan->qtiles.size())), dim3(kQThreads), stream,
+                 dt.qtiles, dt.mats, static_cast<const float*>(a.Mbar), static_cast<const float*>(a.p), a.Qpart);
     if (s != PSGD_OK) return s;
     const unsigned gx = unsigned((plan->max_q_elems_per_matrix + kQRedThreads - 1) / kQRedThreads);
-    s = launch_timed(plan, stream, kKQReduce, [&] {
-      hipLaunchKernelGGL(k_q_reduce, dim3(gx, n_mats), dim3(kQRedThreads), 0, stream, dt.mats, a.Qpart, a.q,
-                         deferred ? a.Qprev : nullptr, R);
-    });
+    s = launch_k(plan, kKQReduce, k_q_reduce, dim3(gx, n_mats), dim3(kQRedThreads), stream, dt.mats,
+                 static_cast<const float*>(a.Qpart), a.q, deferred ? a.Qprev : nullptr, R);
     if (s != PSGD_OK) return s;
   }
   if (deferred)
-    return launch_timed(plan, stream, kKUpdate, [&] {
-      hipLaunchKernelGGL(k_update, dim3(unsigned(plan->utiles.size())), dim3(kUpdThreads), 0, stream, dt.utiles,
-                         dt.mats, a.Mbar, a.p, a.q, a.update, a.mom, a.x, R, a.mode, a.lr, a.mu);
-    });
-  return launch_timed(plan, stream, kKApply, [&] { pass(kPassApply); });
+    return launch_k(plan, kKUpdate, k_update, dim3(unsigned(plan->utiles.size())), dim3(kUpdThreads), stream,
+                    dt.utiles, dt.mats, static_cast<const float*>(a.Mbar), static_cast<const float*>(a.p),
+                    static_cast<const float*>(a.q), a.update, a.mom, a.x, R, a.mode, a.lr, a.mu);
+  return pass(kPassApply);
 }
 
 // Same device, same error and workspace buffers as the step that left the state.
