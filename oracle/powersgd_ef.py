@@ -121,21 +121,28 @@ class MatrixStep:
 
 
 def compress_matrix(g: np.ndarray, e: np.ndarray, q_in: np.ndarray,
-                    tol: float = DROP_TOL, local_q_error: bool = False) -> MatrixStep:
+                    tol: float = DROP_TOL, local_q_error: bool = False,
+                    iterations: int = 1) -> MatrixStep:
     """One warm-started compression step with error feedback for one matrix.
 
     g, e: (W, n, m) gradients and error memories; q_in: (m, r) shared warm start.
     Steps, in the page's order: EF add; P_w = M_w Q; all-reduce P; orthonormalise;
     Q_w = M_w^T P; all-reduce Q; decompress P Q^T; keep the error M_w - P Q^T.
     ``local_q_error`` switches the error to M_w - P Q_w^T (each worker's own Q).
+    ``iterations`` > 1 repeats the power-iteration half steps (P, all-reduce,
+    orthonormalise, Q, all-reduce) that many times from the previous Q before the
+    decompression; the page uses one step per gradient (warm start replaces more).
     """
     g, e = _f64(g), _f64(e)
     W = g.shape[0]
     m_w = [ef_add(g[w], e[w]) for w in range(W)]
-    p_bar = all_reduce_mean([worker_p(m_w[w], q_in) for w in range(W)])
-    p_hat = orthonormalise(p_bar, tol)
-    q_w = [worker_q(m_w[w], p_hat) for w in range(W)]
-    q_bar = all_reduce_mean(q_w)
+    q_cur = _f64(q_in)
+    for _ in range(max(1, iterations)):
+        p_bar = all_reduce_mean([worker_p(m_w[w], q_cur) for w in range(W)])
+        p_hat = orthonormalise(p_bar, tol)
+        q_w = [worker_q(m_w[w], p_hat) for w in range(W)]
+        q_bar = all_reduce_mean(q_w)
+        q_cur = q_bar
     u = decompress(p_hat, q_bar)
     if local_q_error:
         err = np.stack([new_error(m_w[w], decompress(p_hat, q_w[w])) for w in range(W)])

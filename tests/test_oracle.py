@@ -221,6 +221,25 @@ def pin_momentum_closed_form(mod, seed=12):
         assert _rel(xn, x0 - lr * accn) < 1e-12
 
 
+def pin_power_iterations_reach_svd(mod, n=40, m=30, r=3, seed=13):
+    """Many power iterations inside one step from a random Q converge to the top-r
+    singular subspace: U is then the SVD-optimal rank-r approximation (Eckart-Young
+    equality), and one iteration is the plain step."""
+    rng = np.random.default_rng(seed)
+    U0, _ = np.linalg.qr(_rand(n, n, rng=rng))
+    V0, _ = np.linalg.qr(_rand(m, m, rng=rng))
+    s = 0.5 ** np.arange(m)
+    M = (U0[:, :m] * s) @ V0.T
+    q = _rand(m, r, rng=rng)
+    z = np.zeros((1, n, m))
+    many = mod.compress_matrix(M[None], z, q, iterations=60)
+    best = (U0[:, :r] * s[:r]) @ V0[:, :r].T
+    assert _rel(many.update, best) < 1e-10
+    one = mod.compress_matrix(M[None], z, q, iterations=1)
+    plain = mod.compress_matrix(M[None], z, q)
+    assert _rel(one.update, plain.update) == 0.0
+
+
 PINS = [
     pin_single_worker_is_thin_qr,
     pin_rank1_is_power_iteration,
@@ -234,6 +253,7 @@ PINS = [
     pin_local_q_error,
     pin_uncompressed_mean,
     pin_momentum_closed_form,
+    pin_power_iterations_reach_svd,
 ]
 
 
