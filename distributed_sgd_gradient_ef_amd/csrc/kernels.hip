@@ -449,6 +449,54 @@ __global__ __launch_bounds__(kStreamThreads) void k_first(const UpdTile* __restr
                                      offset_valid);
 }
 
+// ------------------------------------------------------------------ extra power iterations
+// P-bar partial row sums of Mbar Q for one row x the wave's column strip, exactly as the
+// first pass forms them, but reading the stored Mbar (extra power iterations).
+template <int V>
+__device__ __forceinline__ void pbar_mbar_tile(const UpdTile& t, const MatInfo& mi, const float* Mbar,
+                                               const float* Qin, float* Ppart, int R) {
+  const int cols = mi.cols;
+  const int j = t.col_begin + int(threadIdx.x) * V;
+  const bool active = j < cols;
+  const int i = t.row_begin + int(blockIdx.y);
+  if (i >= t.row_end) return;
+  float qv[V][4];
+  load_q_cols<V>(qv, Qin + mi.q_off, j, R, active);
+  float part[4] = {0.f, 0.f, 0.f, 0.f};
+  if (active) {
+    const vec_t<V> mb = ldv<V>(Mbar + mi.offset + int64_t(i) * cols + j);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float s = 0.f;
+#pragma unroll
+      for (int q = 0; q < V; ++q) s += lane(mb, q) * qv[q][k];
+      part[k] = s;
+    }
+  }
+  const int strip = t.col_begin / (kStreamThreads * V);
+  float* prow = Ppart + mi.ppart_off + int64_t(strip) * mi.rows * R;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (k < R) {
+      const float v = wave_sum(part[k]);
+      if (threadIdx.x == 0) prow[int64_t(i) * R + k] = v;
+    }
+}
+
+__global__ __launch_bounds__(kStreamThreads) void k_p_mbar(const UpdTile* __restrict__ tiles,
+                                                           const MatInfo* __restrict__ mats,
+                                                           const float* __restrict__ Mbar,
+                                                           const float* __restrict__ Qin,
+                                                           float* __restrict__ Ppart, int R) {
+  const UpdTile t = tiles[blockIdx.x];
+  if (t.mat < 0) return;
+  const MatInfo mi = mats[t.mat];
+  if (mi.vec4)
+    pbar_mbar_tile<4>(t, mi, Mbar, Qin, Ppart, R);
+  else
+    pbar_mbar_tile<1>(t, mi, Mbar, Qin, Ppart, R);
+}
+
 // ------------------------------------------------------------------ Gram-Schmidt
 // P-bar = sum over column strips of the partial row sums (fixed strip order), then
 // modified Gram-Schmidt over its R columns in column order.  Dot products and norms
@@ -989,7 +1037,15 @@ psgd_status launch_all(psgd_plan* plan, const DeviceTables& dt, const StepArgs& 
   };
 
   if ((s = pass(kPassFirst)) != PSGD_OK) return s;
-  if (n_mats > 0) {
+  // Each round: orthonormalise P-bar, Q = Mbar^T P; rounds after the first recompute
+  // the P-bar partials from the stored Mbar and the Q of the previous round.
+  for (int round = 0; n_mats > 0 && round < plan->power_iterations; ++round) {
+    if (round > 0) {
+      s = launch_k(plan, kKPMbar, k_p_mbar, dim3(a.n_s2, a.rows_per_tile), dim3(kStreamThreads), stream,
+                   dt.s2tiles, dt.mats, static_cast<const float*>(a.Mbar), static_cast<const float*>(a.q),
+                   a.Ppart, R);
+      if (s != PSGD_OK) return s;
+    }
     s = launch_k(plan, kKMgs, k_mgs<R>, dim3(n_mats), dim3(plan->mgs_threads), stream, dt.mats,
                  static_cast<const float*>(a.Ppart), a.p, deferred ? a.Pprev : nullptr);
     if (s != PSGD_OK) return s;

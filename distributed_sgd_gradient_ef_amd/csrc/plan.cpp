@@ -16,8 +16,8 @@ namespace psgd {
 
 static thread_local std::string g_last_error;
 
-const char* const kKernelNames[kNumKernels] = {"k_first",    "k_mgs",   "k_q_partial",
-                                               "k_q_reduce", "k_apply", "k_update"};
+const char* const kKernelNames[kNumKernels] = {"k_first", "k_mgs",    "k_q_partial", "k_q_reduce",
+                                               "k_apply", "k_update", "k_p_mbar"};
 
 void set_error(const std::string& msg) { g_last_error = msg; }
 
@@ -306,4 +306,12 @@ extern "C" psgd_status psgd_plan_kernel_stats(psgd_plan* plan, psgd_kernel_stat*
   if (reset)
     for (auto& k : plan->stats) k = KernelStat{};
   return st;
+}
+
+extern "C" psgd_status psgd_plan_set_power_iterations(psgd_plan* plan, int32_t iterations) {
+  if (plan == nullptr) return fail(PSGD_ERR_INVALID_ARG, "psgd_plan_set_power_iterations: plan is NULL");
+  if (iterations < 1 || iterations > 16)
+    return fail(PSGD_ERR_INVALID_ARG, "psgd_plan_set_power_iterations: iterations must be in 1..16");
+  plan->power_iterations = iterations;
+  return PSGD_OK;
 }

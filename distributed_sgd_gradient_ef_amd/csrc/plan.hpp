@@ -75,7 +75,7 @@ struct DeviceTables {
 
 void set_error(const std::string& msg);
 
-enum KernelId { kKFirst = 0, kKMgs, kKQPartial, kKQReduce, kKApply, kKUpdate, kNumKernels };
+enum KernelId { kKFirst = 0, kKMgs, kKQPartial, kKQReduce, kKApply, kKUpdate, kKPMbar, kNumKernels };
 extern const char* const kKernelNames[kNumKernels];
 
 struct PendingTiming {
@@ -105,7 +105,8 @@ struct psgd_plan {
   int64_t max_q_elems_per_matrix = 0;
   uint64_t ws_mbar = 0, ws_ppart = 0, ws_qpart = 0, ws_ebar = 0, ws_pprev = 0, ws_qprev = 0, workspace_bytes = 0;
   int32_t mgs_threads = 64;
-  int32_t worker_rows_per_tile = 1;  // Gram-Schmidt block size: enough for the tallest matrix, <= kMgsThreads
+  int32_t worker_rows_per_tile = 1;
+  int32_t power_iterations = 1;  // power-iteration half-step pairs per step (psgd_plan_set_power_iterations)  // Gram-Schmidt block size: enough for the tallest matrix, <= kMgsThreads
   uint64_t message_bytes = 0, model_bytes = 0, model_bytes_momentum = 0;
   std::map<int, psgd::DeviceTables> dev;  // per HIP device id
   // cross-step state: the carried error mean (PSGD_FLAG_CARRY_ERROR_MEAN) or the deferred

@@ -36,7 +36,7 @@ EXPORTED = [
     "psgd_plan_create", "psgd_plan_sizes", "psgd_plan_layer_info", "psgd_plan_destroy",
     "psgd_compress_step", "psgd_ef_momentum_apply", "psgd_plan_set_timing",
     "psgd_plan_kernel_stats", "psgd_plan_reset_carry", "psgd_errors_materialize", "psgd_stream_copy",
-    "psgd_status_string", "psgd_last_error",
+    "psgd_plan_set_power_iterations", "psgd_status_string", "psgd_last_error",
 ]
 
 
@@ -100,7 +100,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.psgd_plan_reset_carry.argtypes = [vp]
     lib.psgd_stream_copy.argtypes = [vp, vp, ctypes.c_uint64, vp]
     lib.psgd_errors_materialize.argtypes = [vp, vp, vp, vp, vp]
-    for name in EXPORTED[:11]:
+    lib.psgd_plan_set_power_iterations.argtypes = [vp, i32]
+    for name in EXPORTED[:12]:
         getattr(lib, name).restype = ctypes.c_int
     lib.psgd_status_string.argtypes = [ctypes.c_int]
     lib.psgd_status_string.restype = ctypes.c_char_p
@@ -184,6 +185,10 @@ def psgd_plan_kernel_stats(plan: Plan, reset: bool = False) -> dict:
     n = ctypes.c_int32()
     _check(load_library().psgd_plan_kernel_stats(plan.handle, arr, 16, ctypes.byref(n), 1 if reset else 0))
     return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(n.value)}
+
+
+def psgd_plan_set_power_iterations(plan: Plan, iterations: int) -> None:
+    _check(load_library().psgd_plan_set_power_iterations(plan.handle, int(iterations)))
 
 
 def psgd_plan_reset_carry(plan: Plan) -> None:

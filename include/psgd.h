@@ -188,12 +188,23 @@ psgd_status psgd_ef_momentum_apply(psgd_plan* plan, const void* grads, float* er
                                    float* p, float* momentum, float* params, float lr, float mu,
                                    float* update, void* workspace, void* stream);
 
+/* Power-iteration steps per compression step (default 1, the page's method: one
+ * warm-started step per gradient).  With k > 1, after the first P, orthonormalise, Q
+ * round the step repeats P = mean_w M_w Q, orthonormalise, Q = mean_w M_w^T P another
+ * k - 1 times from the Q just computed, before decompressing; the worker mean of M is
+ * kept in the workspace, so each extra round reads only that mean twice.  This is the
+ * warm-start ablation the page's research question RQ3 and its warm-start finding
+ * ("Main findings") speak of: more iterations (or a fresh Q each step, passed in `q`)
+ * against one warm-started step.  Returns PSGD_ERR_INVALID_ARG outside 1..16.  Applies
+ * to later steps; host only. */
+psgd_status psgd_plan_set_power_iterations(psgd_plan* plan, int32_t iterations);
+
 /* Kernel timing, for benchmarks and profiling (off by default).  While enabled, every
  * kernel a step launches is bracketed by two HIP events recorded on the launch stream;
  * psgd_plan_kernel_stats waits for the recorded events and accumulates their elapsed
  * times per kernel.  Timing adds two event records per launch.  Kernel names:
- * "k_ef_mean", "k_p_rows", "k_mgs", "k_q_partial", "k_q_reduce", "k_apply", and in the
- * deferred mode "k_ef_defer" and "k_update" in place of "k_ef_mean" and "k_apply". */
+ * "k_first", "k_mgs", "k_q_partial", "k_q_reduce", "k_apply" (eager modes) or "k_update"
+ * (deferred mode), and "k_p_mbar" for extra power iterations. */
 typedef struct psgd_kernel_stat {
   char name[32];    /* kernel name */
   int64_t launches; /* launches timed since the last reset */

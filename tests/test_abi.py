@@ -148,6 +148,16 @@ def test_deferred_flag_rules():
     assert lib.psgd_errors_materialize(plan.handle, 0x1000, 0x1010, 0x200000, None) == psgd.PSGD_ERR_INVALID_ARG
 
 
+def test_power_iterations_setter():
+    lib = psgd.load_library()
+    plan = psgd.psgd_plan_create([(32, 32)], 2, 2)
+    for k in (1, 4, 16):
+        psgd.psgd_plan_set_power_iterations(plan, k)
+    for bad in (0, 17, -1):
+        assert lib.psgd_plan_set_power_iterations(plan.handle, bad) == psgd.PSGD_ERR_INVALID_ARG
+    assert lib.psgd_plan_set_power_iterations(None, 2) == psgd.PSGD_ERR_INVALID_ARG
+
+
 def test_timing_calls_without_gpu():
     plan = psgd.psgd_plan_create([(8, 8)], 2, 2)
     psgd.psgd_plan_set_timing(plan, True)
