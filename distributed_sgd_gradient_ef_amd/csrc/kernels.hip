@@ -502,8 +502,9 @@ __global__ __launch_bounds__(kStreamThreads) void k_p_mbar(const UpdTile* __rest
 // modified Gram-Schmidt over its R columns in column order.  Dot products and norms
 // accumulate in double; the working column is rounded to float after each
 // projection.  A column whose residual norm is at most 1e-4 of its norm before
-// orthogonalisation (or zero) becomes zero.  The norm of a fresh column and its
-// projection on column 0 share one reduction (both use the unmodified column).
+// orthogonalisation (or zero, or not a number) becomes exactly zero.  The norm of a
+// fresh column and its projection on column 0 share one reduction (both use the
+// unmodified column).
 // Matrices with at most kMgsRowsPerThread rows per thread keep their rows in registers;
 // taller ones work through the output buffer, each thread on its own rows.  `P2`, if
 // set, receives a copy of the result.
@@ -575,7 +576,7 @@ __global__ __launch_bounds__(kMgsThreads) void k_mgs(const MatInfo* __restrict__
       }
       const double scale = (after > 0.0 && after > 1e-4 * before) ? 1.0 / after : 0.0;
 #pragma unroll
-      for (int r = 0; r < kMgsRowsPerThread; ++r) v[r][k] = float(double(v[r][k]) * scale);
+      for (int r = 0; r < kMgsRowsPerThread; ++r) v[r][k] = scale > 0.0 ? float(double(v[r][k]) * scale) : 0.f;
     }
 #pragma unroll
     for (int r = 0; r < kMgsRowsPerThread; ++r) {
@@ -632,7 +633,7 @@ __global__ __launch_bounds__(kMgsThreads) void k_mgs(const MatInfo* __restrict__
     const double scale = (after > 0.0 && after > 1e-4 * before) ? 1.0 / after : 0.0;
     for (int i = threadIdx.x; i < n; i += bs) {
       const int64_t o = int64_t(i) * R + k;
-      const float v = float(double(dst[o]) * scale);
+      const float v = scale > 0.0 ? float(double(dst[o]) * scale) : 0.f;
       dst[o] = v;
       if (P2 != nullptr) P2[mi.p_off + o] = v;
     }

@@ -27,7 +27,9 @@
  *   - the orthonormalisation drops (sets to zero) a column whose residual norm is at
  *     most 1e-4 times its norm before orthogonalisation, or is zero;
  *   - the error uses the aggregated Q (one decompressed U per matrix);
- *   - momentum is heavy-ball, mom <- mu*mom + U, x <- x - lr*mom (Nesterov by flag).
+ *   - momentum is heavy-ball, mom <- mu*mom + U, x <- x - lr*mom (Nesterov by flag);
+ *   - non-finite inputs are not checked: they propagate into every output that depends
+ *     on them, and a P column whose norm is not a number is dropped (set to zero).
  *
  * Memory layout.  A plan fixes a packed layout for a list of tensors:
  *   - every tensor starts at an element offset that is a multiple of 64 (256 bytes)
