@@ -104,9 +104,9 @@ struct psgd_plan {
   int64_t p_elems = 0, q_elems = 0, qpart_elems = 0, ppart_elems = 0;
   int64_t max_q_elems_per_matrix = 0;
   uint64_t ws_mbar = 0, ws_ppart = 0, ws_qpart = 0, ws_ebar = 0, ws_pprev = 0, ws_qprev = 0, workspace_bytes = 0;
-  int32_t mgs_threads = 64;
+  int32_t mgs_threads = 64;  // Gram-Schmidt block size: enough for the tallest matrix, <= kMgsThreads
   int32_t worker_rows_per_tile = 1;
-  int32_t power_iterations = 1;  // power-iteration half-step pairs per step (psgd_plan_set_power_iterations)  // Gram-Schmidt block size: enough for the tallest matrix, <= kMgsThreads
+  int32_t power_iterations = 1;  // power-iteration rounds per step (psgd_plan_set_power_iterations)
   uint64_t message_bytes = 0, model_bytes = 0, model_bytes_momentum = 0;
   std::map<int, psgd::DeviceTables> dev;  // per HIP device id
   // cross-step state: the carried error mean (PSGD_FLAG_CARRY_ERROR_MEAN) or the deferred
