@@ -1,4 +1,5 @@
-"""Build libpsgd.so (host plan code + gfx950 HIP kernels) in-tree with hipcc.
+"""Build libpsgd.so (host plan code + gfx950 HIP kernels of the PowerSGD and rTop-k
+compressors) in-tree with hipcc.
 
     python -m distributed_sgd_gradient_ef_amd.build
 
@@ -15,7 +16,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_PATH = os.path.join(HERE, "libpsgd.so")
-SOURCES = [os.path.join(HERE, "csrc", "plan.cpp"), os.path.join(HERE, "csrc", "kernels.hip")]
+SOURCES = [os.path.join(HERE, "csrc", name) for name in ("plan.cpp", "kernels.hip", "rtopk.hip")]
 INCLUDE = [os.path.join(ROOT, "include"), os.path.join(HERE, "csrc")]
 ARCH = "gfx950"
 

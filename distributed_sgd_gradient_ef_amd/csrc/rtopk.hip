@@ -1,0 +1,971 @@
+// rTop-k sparsification with error feedback: the gfx950 kernels and the host side of
+// psgd_rtopk.h.  Operation: the review page "rTop-k: A Statistical Estimation Approach
+// to Distributed SGD", section "Proposed method" -- a random subset of the entries of
+// largest magnitude is sent, and what is not sent stays in the error memory.
+//
+// A segment is one tensor of one worker.  A tile is kTile consecutive elements of one
+// tensor (the last tile of a tensor may be shorter); the launches of the streaming
+// passes cover every tile of every worker at once (grid.x = tile, grid.y = worker).
+// Magnitudes are compared as the 31-bit key bits(|m|); within a segment the 63-bit
+// value key << 32 | ~index orders entries by magnitude, then by lower index, and is
+// unique, so "the r largest" is one set.
+//
+//   rk_zero       clear the level-1 histograms and the candidate counters
+//   rk_ef_hist    M = G + E, stored into E; per segment a histogram of key >> 20
+//                 (2048 bins in LDS per workgroup, flushed with atomics)
+//   rk_select     per segment: the bin b1 holding the r-th largest key, and how many
+//                 of that bin's entries still belong to the top set
+//   rk_mark       re-read M: entries above b1 -> top mask (one bit per element); entries
+//                 in b1 -> candidate list (their 63-bit keys); per-tile mask counts
+//   rk_refine     per segment: radix selection among the candidates, 11 bits a level,
+//                 then the chosen candidates join the mask
+//   rk_scan_top   per segment: exclusive scan of the per-tile mask counts (slot bases)
+//   rk_keep       per tile: each top entry's slot (its position in index order) gives
+//                 its rank; rank < k -> kept mask; per-tile kept counts
+//   rk_scan_kept  per segment: exclusive scan of the kept counts; unused output slots
+//                 get index -1, value 0
+//   rk_emit       per tile: index/value lists in index order (first k kept), E' = 0 at
+//                 the sent entries, the kept mask trimmed to what was sent, and each
+//                 mask word's first list position
+//   rk_update     U = (1/W) * sum over workers, in worker order, of the sent entries
+//
+// Every reduction that produces a float has a fixed order; every other result is an
+// integer count or a set, so a step is bitwise reproducible.
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <map>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "plan.hpp"
+#include "psgd_rtopk.h"
+
+namespace psgd {
+namespace rtk {
+
+constexpr int kTile = 4096;            // elements per tile
+constexpr int kTileThreads = 256;      // rk_ef_hist / rk_mark: 16 elements per thread
+constexpr int kWordThreads = kTile / 32;  // rk_keep / rk_emit: one thread per mask word
+constexpr int kDenseThreads = kTile / 4;    // rk_update: 4 elements per thread
+constexpr int kBins = 2048;            // 11-bit radix digits
+constexpr int kSegThreads = 1024;      // per-segment kernels
+constexpr int kLevel1Shift = 52;       // level-1 digit: bits 62..52 of the value key (key >> 20)
+constexpr int64_t kMinCandCap = 2048;  // candidate list capacity: max(this, numel / 16), at most numel
+
+struct RkLayer {
+  int64_t offset;    // element offset in a worker slice
+  int64_t numel;
+  int64_t top, keep;
+  int64_t top_off, keep_off;
+  int64_t cand_off;  // offset of the candidate list in one worker's candidate area
+  int64_t cand_cap;
+  int32_t tile_off;  // first tile of the tensor
+  int32_t ntiles;
+};
+
+struct RkTile {
+  int64_t begin;  // element offset of the tile in a worker slice
+  int32_t layer;
+  int32_t len;    // elements in the tile (kTile except at a tensor's end)
+  int32_t chunk;  // tile number inside its tensor
+  int32_t pad;
+};
+
+struct RkSeg {
+  uint32_t b1;         // level-1 bin of the r-th largest key
+  uint32_t need;       // entries of bin b1 that belong to the top set
+  uint32_t ncand;      // entries in bin b1
+  uint32_t from_list;  // 1: candidates were listed (ncand <= cap); 0: rescan the segment
+  uint32_t ntop;       // top-set size found (r)
+  uint32_t nkept;      // entries with rank < k
+  uint32_t pad0, pad1;
+};
+
+enum KernelId { kZero = 0, kEfHist, kSelect, kMark, kRefine, kScanTop, kKeep, kScanKept, kEmit, kUpdate, kNumK };
+const char* const kNames[kNumK] = {"rk_zero",     "rk_ef_hist", "rk_select",    "rk_mark", "rk_refine",
+                                   "rk_scan_top", "rk_keep",    "rk_scan_kept", "rk_emit", "rk_update"};
+
+}  // namespace rtk
+}  // namespace psgd
+
+struct psgd_rtopk_plan {
+  int32_t n_workers = 0;
+  psgd_dtype dtype = PSGD_F32;
+  std::vector<psgd_rtopk_layer_info> info;
+  std::vector<psgd::rtk::RkLayer> layers;
+  std::vector<psgd::rtk::RkTile> tiles;
+  int64_t worker_stride = 0, numel = 0, top_total = 0, keep_total = 0, cand_total = 0;
+  int64_t n_seg = 0;
+  uint64_t ws_hist = 0, ws_candcnt = 0, ws_seg = 0, ws_cand = 0, ws_mask = 0, ws_kmask = 0, ws_kpos = 0;
+  uint64_t ws_tcnt = 0, ws_tbase = 0, ws_kcnt = 0, ws_kbase = 0, workspace_bytes = 0;
+  uint64_t message_bytes = 0, model_bytes = 0;
+  std::map<int, void*> dev;  // device copy of the layer and tile tables, per HIP device
+  bool timing = false;
+  std::vector<psgd::PendingTiming> pending;
+  std::vector<hipEvent_t> event_pool;
+  psgd::KernelStat stats[psgd::rtk::kNumK];
+};
+
+namespace psgd {
+namespace rtk {
+namespace {
+
+// ------------------------------------------------------------------ device helpers
+__device__ __forceinline__ uint32_t mag_key(float m) { return __float_as_uint(m) & 0x7fffffffu; }
+
+__device__ __forceinline__ uint64_t value_key(float m, uint32_t idx) {
+  return (uint64_t(mag_key(m)) << 32) | uint64_t(~idx);
+}
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ v4f load_nt4(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+}
+
+__device__ __forceinline__ void store_nt4(float* p, v4f v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(p));
+}
+
+__device__ __forceinline__ v4f load_g4(const float* p) { return load_nt4(p); }
+
+// Four bfloat16 values widened exactly to float32.
+__device__ __forceinline__ v4f load_g4(const uint16_t* p) {
+  const v2u u = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(p));
+  v4f r;
+  r.x = __uint_as_float(u.x << 16);
+  r.y = __uint_as_float(u.x & 0xffff0000u);
+  r.z = __uint_as_float(u.y << 16);
+  r.w = __uint_as_float(u.y & 0xffff0000u);
+  return r;
+}
+
+// Place bit q of an 8-bit value at bit 4q.
+__device__ __forceinline__ uint32_t spread4(uint32_t x) {
+  x = (x | (x << 12)) & 0x000F000Fu;
+  x = (x | (x << 6)) & 0x03030303u;
+  x = (x | (x << 3)) & 0x11111111u;
+  return x;
+}
+
+// Inclusive scan over the block (blockDim.x a multiple of 64, at most 1024); `lds`
+// holds 16 words.  Every thread must call it.
+__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* lds) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t n = __shfl_up(v, o, 64);
+    if (lane >= o) v += n;
+  }
+  if (lane == 63) lds[wid] = v;
+  __syncthreads();
+  if (wid == 0) {
+    uint32_t t = lane < nw ? lds[lane] : 0u;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const uint32_t n = __shfl_up(t, o, 64);
+      if (lane >= o) t += n;
+    }
+    if (lane < nw) lds[lane] = t;
+  }
+  __syncthreads();
+  if (wid > 0) v += lds[wid - 1];
+  __syncthreads();
+  return v;
+}
+
+// Block total of v (every thread gets it).
+__device__ __forceinline__ uint32_t block_total(uint32_t v, uint32_t* lds) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if (lane == 0) lds[wid] = v;
+  __syncthreads();
+  uint32_t t = 0;
+  for (int i = 0; i < nw; ++i) t += lds[i];
+  __syncthreads();
+  return t;
+}
+
+// ------------------------------------------------------------------ kernels
+__global__ __launch_bounds__(256) void rk_zero(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) p[i] = 0u;
+}
+
+template <typename GT>
+__global__ __launch_bounds__(kTileThreads) void rk_ef_hist(const RkTile* __restrict__ tiles, const GT* __restrict__ G,
+                                                           float* __restrict__ E, uint32_t* __restrict__ hist,
+                                                           int64_t stride, int n_layers) {
+  __shared__ uint32_t h[kBins];
+  for (int b = threadIdx.x; b < kBins; b += kTileThreads) h[b] = 0u;
+  __syncthreads();
+  const RkTile t = tiles[blockIdx.x];
+  const int w = blockIdx.y;
+  const int64_t base = int64_t(w) * stride + t.begin;
+#pragma unroll
+  for (int i = 0; i < kTile / (kTileThreads * 4); ++i) {
+    const int e = (i * kTileThreads + int(threadIdx.x)) * 4;
+    if (e < t.len) {
+      const v4f g = load_g4(G + base + e);
+      float* ep = E + base + e;
+      const v4f mv = g + load_nt4(ep);
+      const float m[4] = {mv.x, mv.y, mv.z, mv.w};
+      const int valid = min(4, t.len - e);
+      if (valid == 4) {
+        store_nt4(ep, mv);
+      } else {
+        for (int j = 0; j < valid; ++j) ep[j] = m[j];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j < valid) atomicAdd(&h[mag_key(m[j]) >> 20], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t* gh = hist + (int64_t(w) * n_layers + t.layer) * kBins;
+  for (int b = threadIdx.x; b < kBins; b += kTileThreads) {
+    const uint32_t c = h[b];
+    if (c) atomicAdd(gh + b, c);
+  }
+}
+
+// One workgroup per segment; thread t owns the 8 bins below kBins - 8t.
+__global__ __launch_bounds__(256) void rk_select(const RkLayer* __restrict__ layers, const uint32_t* __restrict__ hist,
+                                                 RkSeg* __restrict__ seg, int n_layers) {
+  __shared__ uint32_t lds[16];
+  const int l = blockIdx.x, w = blockIdx.y;
+  const int64_t s = int64_t(w) * n_layers + l;
+  const RkLayer L = layers[l];
+  const uint32_t* h = hist + s * kBins;
+  const int hi = kBins - 8 * int(threadIdx.x);
+  uint32_t c[8], tsum = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    c[j] = h[hi - 1 - j];
+    tsum += c[j];
+  }
+  const uint32_t incl = block_incl_scan(tsum, lds);
+  const uint32_t above = incl - tsum;
+  const uint32_t r = uint32_t(L.top);
+  if (above < r && r <= incl) {
+    uint32_t acc = above;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (acc + c[j] >= r) {
+        RkSeg st{};
+        st.b1 = uint32_t(hi - 1 - j);
+        st.need = r - acc;
+        st.ncand = c[j];
+        st.from_list = int64_t(c[j]) <= L.cand_cap ? 1u : 0u;
+        seg[s] = st;
+        break;
+      }
+      acc += c[j];
+    }
+  }
+}
+
+// Tile of 16 groups of 256 elements; wave v handles groups v, v+4, v+8, v+12; lane l
+// holds elements 4l..4l+3 of its group, so mask word q of a group (32 elements) comes
+// from lanes 8q..8q+7 and is assembled by lane q from four ballots.
+__global__ __launch_bounds__(kTileThreads) void rk_mark(const RkTile* __restrict__ tiles,
+                                                        const RkLayer* __restrict__ layers,
+                                                        const float* __restrict__ E, const RkSeg* __restrict__ seg,
+                                                        uint32_t* __restrict__ mask, uint32_t* __restrict__ tcnt,
+                                                        uint64_t* __restrict__ cand, uint32_t* __restrict__ candcnt,
+                                                        int64_t stride, int64_t cand_stride, int n_layers,
+                                                        int ntiles) {
+  __shared__ uint32_t lds[16];
+  __shared__ uint32_t s_base;
+  const RkTile t = tiles[blockIdx.x];
+  const int w = blockIdx.y;
+  const int64_t s = int64_t(w) * n_layers + t.layer;
+  const uint32_t b1 = seg[s].b1;
+  const bool listing = seg[s].from_list != 0u;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t base = int64_t(w) * stride + t.begin;
+  const int64_t wbase = base >> 5;  // begin and stride are multiples of 64
+  float m[4][4];
+  uint32_t nsure = 0, ncand = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int g = i * 4 + wv;
+    const int e = g * 256 + lane * 4;
+    const int valid = max(0, min(4, t.len - e));
+    v4f v = {0.f, 0.f, 0.f, 0.f};
+    if (valid > 0) v = *reinterpret_cast<const v4f*>(E + base + e);
+    m[i][0] = v.x;
+    m[i][1] = v.y;
+    m[i][2] = v.z;
+    m[i][3] = v.w;
+    uint64_t B[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t bin = mag_key(m[i][j]) >> 20;
+      B[j] = __ballot(j < valid && bin > b1);
+      ncand += (j < valid && bin == b1) ? 1u : 0u;
+    }
+    if (lane < 8 && (g * 256 + lane * 32) < t.len) {
+      const int sh = lane * 8;
+      const uint32_t word = spread4(uint32_t(B[0] >> sh) & 0xffu) | (spread4(uint32_t(B[1] >> sh) & 0xffu) << 1) |
+                            (spread4(uint32_t(B[2] >> sh) & 0xffu) << 2) |
+                            (spread4(uint32_t(B[3] >> sh) & 0xffu) << 3);
+      mask[wbase + g * 8 + lane] = word;
+      nsure += __popc(word);
+    }
+  }
+  const uint32_t tot = block_total(nsure, lds);
+  if (threadIdx.x == 0) tcnt[int64_t(w) * ntiles + blockIdx.x] = tot;
+  if (!listing) return;  // uniform across the block
+  const uint32_t incl = block_incl_scan(ncand, lds);
+  if (threadIdx.x == kTileThreads - 1) s_base = incl > 0 ? atomicAdd(candcnt + s, incl) : 0u;
+  __syncthreads();
+  if (ncand == 0) return;
+  const RkLayer L = layers[t.layer];
+  uint64_t* out = cand + int64_t(w) * cand_stride + L.cand_off;
+  uint32_t pos = s_base + incl - ncand;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int g = i * 4 + wv;
+    const int e = g * 256 + lane * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (e + j < t.len && (mag_key(m[i][j]) >> 20) == b1) {
+        if (int64_t(pos) < L.cand_cap) out[pos] = value_key(m[i][j], uint32_t(t.chunk * kTile + e + j));
+        ++pos;
+      }
+    }
+  }
+}
+
+// One workgroup of kSegThreads per segment.  Items are the candidate list, or every
+// entry of the segment when the list would have overflowed (filtered to bin b1).
+__global__ __launch_bounds__(kSegThreads) void rk_refine(const RkLayer* __restrict__ layers,
+                                                         const float* __restrict__ E, const RkSeg* __restrict__ seg,
+                                                         const uint64_t* __restrict__ cand,
+                                                         const uint32_t* __restrict__ candcnt,
+                                                         uint32_t* __restrict__ mask, uint32_t* __restrict__ tcnt,
+                                                         int64_t stride, int64_t cand_stride, int n_layers,
+                                                         int ntiles) {
+  __shared__ uint32_t h[kBins];
+  __shared__ uint32_t lds[16];
+  __shared__ uint32_t s_b, s_above, s_count;
+  const int l = blockIdx.x, w = blockIdx.y;
+  const int64_t s = int64_t(w) * n_layers + l;
+  const RkLayer L = layers[l];
+  const RkSeg st = seg[s];
+  const bool listing = st.from_list != 0u;
+  const uint64_t* list = cand + int64_t(w) * cand_stride + L.cand_off;
+  const float* M = E + int64_t(w) * stride + L.offset;
+  const int64_t n_items = listing ? min(int64_t(candcnt[s]), L.cand_cap) : L.numel;
+  auto item = [&](int64_t i) -> uint64_t { return listing ? list[i] : value_key(M[i], uint32_t(i)); };
+
+  const uint64_t b1 = st.b1;
+  uint64_t prefix = b1;
+  uint32_t need = st.need;
+  uint64_t thr = b1 << kLevel1Shift;  // every entry of bin b1
+  if (need < st.ncand) {
+    const int shs[5] = {41, 30, 19, 8, 0};
+    const int wbs[5] = {11, 11, 11, 11, 8};
+    for (int lvl = 0; lvl < 5; ++lvl) {
+      const int sh = shs[lvl], wb = wbs[lvl];
+      const int nb = 1 << wb;
+      for (int b = threadIdx.x; b < nb; b += kSegThreads) h[b] = 0u;
+      __syncthreads();
+      for (int64_t i = threadIdx.x; i < n_items; i += kSegThreads) {
+        const uint64_t ck = item(i);
+        if ((ck >> (sh + wb)) == prefix) atomicAdd(&h[uint32_t(ck >> sh) & uint32_t(nb - 1)], 1u);
+      }
+      __syncthreads();
+      // thread t owns bins nb-1-2t and nb-2-2t (from the top)
+      const int hb = nb - 1 - 2 * int(threadIdx.x);
+      const uint32_t c0 = hb >= 0 ? h[hb] : 0u;
+      const uint32_t c1 = hb >= 1 ? h[hb - 1] : 0u;
+      const uint32_t incl = block_incl_scan(c0 + c1, lds);
+      const uint32_t above = incl - c0 - c1;
+      if (above < need && need <= incl) {
+        if (above + c0 >= need) {
+          s_b = uint32_t(hb);
+          s_above = above;
+          s_count = c0;
+        } else {
+          s_b = uint32_t(hb - 1);
+          s_above = above + c0;
+          s_count = c1;
+        }
+      }
+      __syncthreads();
+      prefix = (prefix << wb) | uint64_t(s_b);
+      need -= s_above;
+      const uint32_t cnt = s_count;
+      __syncthreads();
+      if (cnt == need) {  // every entry of the chosen bin belongs to the top set
+        thr = prefix << sh;
+        break;
+      }
+    }
+  }
+  uint32_t* mseg = mask + ((int64_t(w) * stride + L.offset) >> 5);
+  uint32_t* tc = tcnt + int64_t(w) * ntiles + L.tile_off;
+  for (int64_t i = threadIdx.x; i < n_items; i += kSegThreads) {
+    const uint64_t ck = item(i);
+    if ((ck >> kLevel1Shift) == b1 && ck >= thr) {
+      const uint32_t idx = ~uint32_t(ck);
+      atomicOr(mseg + (idx >> 5), 1u << (idx & 31u));
+      atomicAdd(tc + idx / kTile, 1u);
+    }
+  }
+}
+
+// Exclusive scan over a segment's per-tile counts; the total goes to *total_out and,
+// when `pad` is set, output slots [min(total, k), k) get index -1, value 0.
+__global__ __launch_bounds__(kSegThreads) void rk_scan_tiles(const RkLayer* __restrict__ layers,
+                                                             const uint32_t* __restrict__ cnt,
+                                                             uint32_t* __restrict__ basev, RkSeg* __restrict__ seg,
+                                                             int32_t* __restrict__ index, float* __restrict__ value,
+                                                             int64_t keep_total, int n_layers, int ntiles,
+                                                             int kept_pass) {
+  __shared__ uint32_t lds[16];
+  const int l = blockIdx.x, w = blockIdx.y;
+  const int64_t s = int64_t(w) * n_layers + l;
+  const RkLayer L = layers[l];
+  const int64_t row = int64_t(w) * ntiles + L.tile_off;
+  uint32_t running = 0;
+  for (int c0 = 0; c0 < L.ntiles; c0 += kSegThreads) {
+    const int i = c0 + int(threadIdx.x);
+    const uint32_t v = i < L.ntiles ? cnt[row + i] : 0u;
+    const uint32_t incl = block_incl_scan(v, lds);
+    if (i < L.ntiles) basev[row + i] = running + incl - v;
+    running += block_total(v, lds);
+  }
+  if (!kept_pass) {
+    if (threadIdx.x == 0) seg[s].ntop = running;
+    return;
+  }
+  if (threadIdx.x == 0) seg[s].nkept = running;
+  int32_t* ix = index + int64_t(w) * keep_total + L.keep_off;
+  float* vx = value + int64_t(w) * keep_total + L.keep_off;
+  for (int64_t p = int64_t(running) + threadIdx.x; p < L.keep; p += kSegThreads) {
+    ix[p] = -1;
+    vx[p] = 0.f;
+  }
+}
+
+// One thread per mask word of a tile: top entries in index order get consecutive slots
+// from the tile's base; those whose rank is below k are kept.
+__global__ __launch_bounds__(kWordThreads) void rk_keep(const RkTile* __restrict__ tiles,
+                                                        const RkLayer* __restrict__ layers,
+                                                        const uint32_t* __restrict__ mask,
+                                                        const uint32_t* __restrict__ tbase,
+                                                        const uint32_t* __restrict__ ranks,
+                                                        uint32_t* __restrict__ kmask, uint32_t* __restrict__ kcnt,
+                                                        int64_t stride, int64_t top_total, int ntiles) {
+  __shared__ uint32_t lds[16];
+  const RkTile t = tiles[blockIdx.x];
+  const int w = blockIdx.y;
+  const RkLayer L = layers[t.layer];
+  const int nwords = (t.len + 31) >> 5;
+  const int q = threadIdx.x;
+  const int64_t wi = ((int64_t(w) * stride + t.begin) >> 5) + q;
+  const uint32_t word = q < nwords ? mask[wi] : 0u;
+  const uint32_t c = __popc(word);
+  uint32_t slot = tbase[int64_t(w) * ntiles + blockIdx.x] + block_incl_scan(c, lds) - c;
+  const uint32_t* rk = ranks + int64_t(w) * top_total + L.top_off;
+  uint32_t kept = 0;
+  for (uint32_t bits = word; bits != 0u; bits &= bits - 1u) {
+    const int j = __builtin_ctz(bits);
+    if (int64_t(slot) < L.top && int64_t(rk[slot]) < L.keep) kept |= 1u << j;
+    ++slot;
+  }
+  if (q < nwords) kmask[wi] = kept;
+  const uint32_t tot = block_total(__popc(kept), lds);
+  if (threadIdx.x == 0) kcnt[int64_t(w) * ntiles + blockIdx.x] = tot;
+}
+
+__global__ __launch_bounds__(kWordThreads) void rk_emit(const RkTile* __restrict__ tiles,
+                                                        const RkLayer* __restrict__ layers,
+                                                        uint32_t* __restrict__ kmask, const uint32_t* __restrict__ kbase,
+                                                        float* __restrict__ E, int32_t* __restrict__ index,
+                                                        float* __restrict__ value, uint32_t* __restrict__ kpos,
+                                                        int64_t stride, int64_t keep_total, int ntiles) {
+  __shared__ uint32_t lds[16];
+  const RkTile t = tiles[blockIdx.x];
+  const int w = blockIdx.y;
+  const RkLayer L = layers[t.layer];
+  const int nwords = (t.len + 31) >> 5;
+  const int q = threadIdx.x;
+  const int64_t wi = ((int64_t(w) * stride + t.begin) >> 5) + q;
+  const uint32_t word = q < nwords ? kmask[wi] : 0u;
+  const uint32_t c = __popc(word);
+  const uint32_t first = kbase[int64_t(w) * ntiles + blockIdx.x] + block_incl_scan(c, lds) - c;
+  if (q >= nwords) return;
+  int32_t* ix = index + int64_t(w) * keep_total + L.keep_off;
+  float* vx = value + int64_t(w) * keep_total + L.keep_off;
+  float* M = E + int64_t(w) * stride + L.offset;
+  uint32_t pos = first, sent = 0;
+  for (uint32_t bits = word; bits != 0u; bits &= bits - 1u) {
+    const int j = __builtin_ctz(bits);
+    if (int64_t(pos) < L.keep) {
+      const int32_t idx = t.chunk * kTile + q * 32 + j;
+      ix[pos] = idx;
+      vx[pos] = M[idx];
+      M[idx] = 0.f;
+      sent |= 1u << j;
+    }
+    ++pos;
+  }
+  if (sent != word) kmask[wi] = sent;
+  kpos[wi] = first;
+}
+
+// Dense update: lane handles 4 elements; for each worker in order, the sent entries
+// among them are read from the worker's value list (position = the word's first list
+// position + the sent bits below).
+__global__ __launch_bounds__(kDenseThreads) void rk_update(const RkTile* __restrict__ tiles,
+                                                         const RkLayer* __restrict__ layers,
+                                                         const uint32_t* __restrict__ kmask,
+                                                         const uint32_t* __restrict__ kpos,
+                                                         const float* __restrict__ value, float* __restrict__ update,
+                                                         int W, int64_t stride, int64_t keep_total, float inv_w) {
+  const RkTile t = tiles[blockIdx.x];
+  const int e = int(threadIdx.x) * 4;
+  if (e >= t.len) return;
+  const RkLayer L = layers[t.layer];
+  const int valid = min(4, t.len - e);
+  const int64_t wi = (t.begin + e) >> 5;
+  const int sh = e & 31;
+  const int64_t wstride = stride >> 5;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int w = 0; w < W; ++w) {
+    const uint32_t kw = kmask[int64_t(w) * wstride + wi];
+    uint32_t nib = (kw >> sh) & 0xfu;
+    if (nib == 0u) continue;
+    uint32_t pos = kpos[int64_t(w) * wstride + wi] + __popc(kw & ((1u << sh) - 1u));
+    const float* vx = value + int64_t(w) * keep_total + L.keep_off;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if ((nib >> j) & 1u) {
+        acc[j] += vx[pos];
+        ++pos;
+      }
+    }
+  }
+  float* u = update + t.begin + e;
+  if (valid == 4) {
+    v4f o;
+    o.x = acc[0] * inv_w;
+    o.y = acc[1] * inv_w;
+    o.z = acc[2] * inv_w;
+    o.w = acc[3] * inv_w;
+    store_nt4(u, o);
+  } else {
+    for (int j = 0; j < valid; ++j) u[j] = acc[j] * inv_w;
+  }
+}
+
+// ------------------------------------------------------------------ host helpers
+psgd_status fail(psgd_status s, const std::string& msg) {
+  set_error(msg);
+  return s;
+}
+
+psgd_status hip_fail(const char* what, hipError_t e) {
+  return fail(PSGD_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+uint64_t a256(uint64_t x) { return (x + 255) / 256 * 256; }
+
+psgd_status device_tables(psgd_rtopk_plan* plan, RkLayer** layers, RkTile** tiles) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+  const uint64_t bl = a256(plan->layers.size() * sizeof(RkLayer) + 1);
+  auto it = plan->dev.find(dev);
+  if (it == plan->dev.end()) {
+    const uint64_t bt = plan->tiles.size() * sizeof(RkTile);
+    void* base = nullptr;
+    e = hipMalloc(&base, bl + bt + 256);
+    if (e != hipSuccess) return fail(PSGD_ERR_NO_MEMORY, std::string("hipMalloc of the plan's device tables: ") +
+                                                             hipGetErrorString(e));
+    char* b = static_cast<char*>(base);
+    e = hipMemcpy(b, plan->layers.data(), plan->layers.size() * sizeof(RkLayer), hipMemcpyHostToDevice);
+    if (e == hipSuccess && bt > 0) e = hipMemcpy(b + bl, plan->tiles.data(), bt, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      (void)hipFree(base);
+      return hip_fail("hipMemcpy of the plan's device tables", e);
+    }
+    it = plan->dev.emplace(dev, base).first;
+  }
+  char* b = static_cast<char*>(it->second);
+  *layers = reinterpret_cast<RkLayer*>(b);
+  *tiles = reinterpret_cast<RkTile*>(b + bl);
+  return PSGD_OK;
+}
+
+psgd_status take_event(psgd_rtopk_plan* plan, hipEvent_t* ev) {
+  if (!plan->event_pool.empty()) {
+    *ev = plan->event_pool.back();
+    plan->event_pool.pop_back();
+    return PSGD_OK;
+  }
+  const hipError_t e = hipEventCreate(ev);
+  return e == hipSuccess ? PSGD_OK : hip_fail("hipEventCreate", e);
+}
+
+// Launch on `st`; with timing on, through hipExtLaunchKernelGGL with events the runtime
+// records with the dispatch itself.
+template <typename... KArgs, typename... Args>
+psgd_status launch(psgd_rtopk_plan* plan, int kid, void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t st,
+                   Args... args) {
+  hipEvent_t a = nullptr, b = nullptr;
+  if (plan->timing) {
+    psgd_status s = take_event(plan, &a);
+    if (s == PSGD_OK) s = take_event(plan, &b);
+    if (s != PSGD_OK) {
+      if (a) plan->event_pool.push_back(a);
+      return s;
+    }
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, a, b, 0, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    if (plan->timing) {
+      plan->event_pool.push_back(a);
+      plan->event_pool.push_back(b);
+    }
+    return hip_fail((std::string("launch ") + kNames[kid]).c_str(), e);
+  }
+  if (plan->timing) plan->pending.push_back(PendingTiming{kid, a, b});
+  return PSGD_OK;
+}
+
+struct Span {
+  const char* name;
+  uintptr_t lo, hi;
+};
+
+}  // namespace
+}  // namespace rtk
+}  // namespace psgd
+
+using namespace psgd;
+using namespace psgd::rtk;
+
+extern "C" psgd_status psgd_rtopk_plan_create(const psgd_layer* layers, int32_t n_layers, const int64_t* top,
+                                              const int64_t* keep, int32_t n_workers, psgd_dtype grad_dtype,
+                                              uint32_t flags, psgd_rtopk_plan** out) {
+  if (out == nullptr) return fail(PSGD_ERR_INVALID_ARG, "psgd_rtopk_plan_create: out is NULL");
+  *out = nullptr;
+  if (n_layers < 1) return fail(PSGD_ERR_INVALID_ARG, "psgd_rtopk_plan_create: n_layers must be >= 1");
+  if (layers == nullptr || top == nullptr || keep == nullptr)
+    return fail(PSGD_ERR_INVALID_ARG, "psgd_rtopk_plan_create: layers, top or keep is NULL");
+  if (n_workers < 1 || n_workers > 65535)
+    return fail(PSGD_ERR_INVALID_ARG, "psgd_rtopk_plan_create: n_workers must be in 1..65535");
+  if (grad_dtype != PSGD_F32 && grad_dtype != PSGD_BF16)
+    return fail(PSGD_ERR_UNSUPPORTED, "psgd_rtopk_plan_create: unknown grad_dtype");
+  if (flags != 0u) return fail(PSGD_ERR_UNSUPPORTED, "psgd_rtopk_plan_create: flags must be 0");
+  psgd_rtopk_plan* plan = nullptr;
+  try {
+    plan = new psgd_rtopk_plan();
+    plan->n_workers = n_workers;
+    plan->dtype = grad_dtype;
+    int64_t off = 0, tile_count = 0;
+    for (int32_t i = 0; i < n_layers; ++i) {
+      const int64_t rows = layers[i].rows, cols = layers[i].cols;
+      if (rows < 1 || cols < 1 || rows > (int64_t(1) << 31) || cols > (int64_t(1) << 31) ||
+          rows * cols > int64_t(0x7fffffff)) {
+        delete plan;
+        return fail(PSGD_ERR_INVALID_ARG, "psgd_rtopk_plan_create: layer " + std::to_string(i) +
+                                              " needs 1 <= rows*cols < 2^31");
+      }
+      const int64_t numel = rows * cols;
+      if (keep[i] < 1 || keep[i] > top[i] || top[i] > numel) {
+        delete plan;
+        return fail(PSGD_ERR_INVALID_ARG, "psgd_rtopk_plan_create: layer " + std::to_string(i) +
+                                              " needs 1 <= keep <= top <= rows*cols");
+      }
+      psgd_rtopk_layer_info li{};
+      li.rows = rows;
+      li.cols = cols;
+      li.numel = numel;
+      li.offset = off;
+      li.top = top[i];
+      li.keep = keep[i];
+      li.top_offset = plan->top_total;
+      li.keep_offset = plan->keep_total;
+      RkLayer L{};
+      L.offset = off;
+      L.numel = numel;
+      L.top = top[i];
+      L.keep = keep[i];
+      L.top_off = plan->top_total;
+      L.keep_off = plan->keep_total;
+      L.cand_cap = std::min(numel, std::max(kMinCandCap, (numel + 15) / 16));
+      L.cand_off = plan->cand_total;
+      L.ntiles = int32_t((numel + kTile - 1) / kTile);
+      L.tile_off = int32_t(tile_count);
+      for (int32_t c = 0; c < L.ntiles; ++c) {
+        RkTile t{};
+        t.begin = off + int64_t(c) * kTile;
+        t.layer = i;
+        t.len = int32_t(std::min<int64_t>(kTile, numel - int64_t(c) * kTile));
+        t.chunk = c;
+        plan->tiles.push_back(t);
+      }
+      tile_count += L.ntiles;
+      if (tile_count > int64_t(0x7fffffff)) {
+        delete plan;
+        return fail(PSGD_ERR_INVALID_ARG, "psgd_rtopk_plan_create: too many tiles");
+      }
+      plan->cand_total += L.cand_cap;
+      plan->top_total += top[i];
+      plan->keep_total += keep[i];
+      plan->numel += numel;
+      plan->info.push_back(li);
+      plan->layers.push_back(L);
+      off = (off + numel + kAlignElems - 1) / kAlignElems * kAlignElems;
+    }
+    plan->worker_stride = off;
+    plan->n_seg = int64_t(n_workers) * n_layers;
+    const uint64_t W = uint64_t(n_workers);
+    const uint64_t ntiles = plan->tiles.size();
+    const uint64_t words = uint64_t(plan->worker_stride / 32);
+    uint64_t ws = 0;
+    plan->ws_hist = ws;  // histograms and candidate counters are cleared together
+    ws += uint64_t(plan->n_seg) * kBins * 4;
+    plan->ws_candcnt = ws;
+    ws = a256(ws + uint64_t(plan->n_seg) * 4);
+    plan->ws_seg = ws;
+    ws = a256(ws + uint64_t(plan->n_seg) * sizeof(RkSeg));
+    plan->ws_cand = ws;
+    ws = a256(ws + W * uint64_t(plan->cand_total) * 8);
+    plan->ws_mask = ws;
+    ws = a256(ws + W * words * 4);
+    plan->ws_kmask = ws;
+    ws = a256(ws + W * words * 4);
+    plan->ws_kpos = ws;
+    ws = a256(ws + W * words * 4);
+    plan->ws_tcnt = ws;
+    ws = a256(ws + W * ntiles * 4);
+    plan->ws_tbase = ws;
+    ws = a256(ws + W * ntiles * 4);
+    plan->ws_kcnt = ws;
+    ws = a256(ws + W * ntiles * 4);
+    plan->ws_kbase = ws;
+    ws = a256(ws + W * ntiles * 4);
+    plan->workspace_bytes = ws;
+    const uint64_t gb = grad_dtype == PSGD_BF16 ? 2 : 4;
+    plan->message_bytes = uint64_t(plan->keep_total) * 8;
+    plan->model_bytes = (W * (gb + 8) + 4) * uint64_t(plan->numel);
+  } catch (const std::bad_alloc&) {
+    delete plan;
+    return fail(PSGD_ERR_NO_MEMORY, "psgd_rtopk_plan_create: out of host memory");
+  }
+  *out = plan;
+  return PSGD_OK;
+}
+
+extern "C" psgd_status psgd_rtopk_plan_sizes(const psgd_rtopk_plan* plan, psgd_rtopk_sizes* out) {
+  if (plan == nullptr || out == nullptr) return fail(PSGD_ERR_INVALID_ARG, "psgd_rtopk_plan_sizes: NULL argument");
+  psgd_rtopk_sizes s{};
+  s.n_layers = int32_t(plan->info.size());
+  s.n_workers = plan->n_workers;
+  s.grad_dtype = int32_t(plan->dtype);
+  s.worker_stride = plan->worker_stride;
+  s.numel = plan->numel;
+  s.top_total = plan->top_total;
+  s.keep_total = plan->keep_total;
+  s.workspace_bytes = plan->workspace_bytes;
+  s.message_bytes = plan->message_bytes;
+  s.model_bytes = plan->model_bytes;
+  *out = s;
+  return PSGD_OK;
+}
+
+extern "C" psgd_status psgd_rtopk_plan_layer_info(const psgd_rtopk_plan* plan, int32_t layer,
+                                             psgd_rtopk_layer_info* out) {
+  if (plan == nullptr || out == nullptr) return fail(PSGD_ERR_INVALID_ARG, "psgd_rtopk_plan_layer_info: NULL argument");
+  if (layer < 0 || size_t(layer) >= plan->info.size())
+    return fail(PSGD_ERR_INVALID_ARG, "psgd_rtopk_plan_layer_info: layer index out of range");
+  *out = plan->info[size_t(layer)];
+  return PSGD_OK;
+}
+
+extern "C" psgd_status psgd_rtopk_plan_destroy(psgd_rtopk_plan* plan) {
+  if (plan == nullptr) return PSGD_OK;
+  psgd_status st = PSGD_OK;
+  for (const PendingTiming& t : plan->pending) {
+    (void)hipEventDestroy(t.start);
+    (void)hipEventDestroy(t.stop);
+  }
+  for (hipEvent_t ev : plan->event_pool) (void)hipEventDestroy(ev);
+  for (auto& kv : plan->dev) {
+    int cur = 0;
+    const bool have = hipGetDevice(&cur) == hipSuccess;
+    if (have && cur != kv.first) (void)hipSetDevice(kv.first);
+    if (hipFree(kv.second) != hipSuccess) {
+      set_error("psgd_rtopk_plan_destroy: hipFree of the device tables failed");
+      st = PSGD_ERR_HIP;
+    }
+    if (have && cur != kv.first) (void)hipSetDevice(cur);
+  }
+  delete plan;
+  return st;
+}
+
+extern "C" psgd_status psgd_rtopk_plan_set_timing(psgd_rtopk_plan* plan, int32_t enable) {
+  if (plan == nullptr) return fail(PSGD_ERR_INVALID_ARG, "psgd_rtopk_plan_set_timing: plan is NULL");
+  plan->timing = enable != 0;
+  return PSGD_OK;
+}
+
+extern "C" psgd_status psgd_rtopk_plan_kernel_stats(psgd_rtopk_plan* plan, psgd_kernel_stat* out, int32_t capacity,
+                                                    int32_t* count, int32_t reset) {
+  if (plan == nullptr) return fail(PSGD_ERR_INVALID_ARG, "psgd_rtopk_plan_kernel_stats: plan is NULL");
+  if (capacity > 0 && out == nullptr) return fail(PSGD_ERR_INVALID_ARG, "psgd_rtopk_plan_kernel_stats: out is NULL");
+  psgd_status st = PSGD_OK;
+  for (const PendingTiming& t : plan->pending) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(t.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.start, t.stop);
+    if (e != hipSuccess) {
+      set_error(std::string("psgd_rtopk_plan_kernel_stats: ") + hipGetErrorString(e));
+      st = PSGD_ERR_HIP;
+    } else {
+      plan->stats[t.kernel].launches += 1;
+      plan->stats[t.kernel].total_ms += double(ms);
+    }
+    plan->event_pool.push_back(t.start);
+    plan->event_pool.push_back(t.stop);
+  }
+  plan->pending.clear();
+  int32_t n = 0;
+  for (int k = 0; k < kNumK; ++k) {
+    if (plan->stats[k].launches == 0) continue;
+    if (n < capacity) {
+      psgd_kernel_stat ks{};
+      std::snprintf(ks.name, sizeof(ks.name), "%s", kNames[k]);
+      ks.launches = plan->stats[k].launches;
+      ks.total_ms = plan->stats[k].total_ms;
+      out[n] = ks;
+    }
+    ++n;
+  }
+  if (count != nullptr) *count = std::min(n, std::max<int32_t>(capacity, 0));
+  if (reset)
+    for (auto& k : plan->stats) k = KernelStat{};
+  return st;
+}
+
+extern "C" psgd_status psgd_rtopk_step(psgd_rtopk_plan* plan, const void* grads, float* errors,
+                                       const uint32_t* ranks, int32_t* index, float* value, float* update,
+                                       void* workspace, void* stream) {
+  static const char* fn = "psgd_rtopk_step";
+  if (plan == nullptr) return fail(PSGD_ERR_INVALID_ARG, "psgd_rtopk_step: plan is NULL");
+  const uint64_t W = uint64_t(plan->n_workers);
+  const uint64_t gb = plan->dtype == PSGD_BF16 ? 2 : 4;
+  const uint64_t stride = uint64_t(plan->worker_stride);
+  const Span spans[] = {
+      {"grads", uintptr_t(grads), uintptr_t(grads) + W * stride * gb},
+      {"errors", uintptr_t(errors), uintptr_t(errors) + W * stride * 4},
+      {"ranks", uintptr_t(ranks), uintptr_t(ranks) + W * uint64_t(plan->top_total) * 4},
+      {"index", uintptr_t(index), uintptr_t(index) + W * uint64_t(plan->keep_total) * 4},
+      {"value", uintptr_t(value), uintptr_t(value) + W * uint64_t(plan->keep_total) * 4},
+      {"update", uintptr_t(update), uintptr_t(update) + stride * 4},
+      {"workspace", uintptr_t(workspace), uintptr_t(workspace) + plan->workspace_bytes},
+  };
+  for (const Span& sp : spans) {
+    const bool nullable = std::string(sp.name) == "update";
+    if (sp.lo == 0) {
+      if (nullable) continue;
+      return fail(PSGD_ERR_INVALID_ARG, std::string(fn) + ": " + sp.name + " is NULL");
+    }
+    if (sp.lo % 16 != 0) return fail(PSGD_ERR_INVALID_ARG, std::string(fn) + ": " + sp.name + " is not 16-byte aligned");
+  }
+  for (size_t i = 0; i < sizeof(spans) / sizeof(spans[0]); ++i)
+    for (size_t j = i + 1; j < sizeof(spans) / sizeof(spans[0]); ++j) {
+      const Span &a = spans[i], &b = spans[j];
+      if (a.lo == 0 || b.lo == 0) continue;
+      if (a.lo < b.hi && b.lo < a.hi)
+        return fail(PSGD_ERR_INVALID_ARG, std::string(fn) + ": " + a.name + " and " + b.name + " overlap");
+    }
+  RkLayer* dl = nullptr;
+  RkTile* dt = nullptr;
+  psgd_status s = device_tables(plan, &dl, &dt);
+  if (s != PSGD_OK) return s;
+
+  char* ws = static_cast<char*>(workspace);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(ws + plan->ws_hist);
+  uint32_t* candcnt = reinterpret_cast<uint32_t*>(ws + plan->ws_candcnt);
+  RkSeg* seg = reinterpret_cast<RkSeg*>(ws + plan->ws_seg);
+  uint64_t* cand = reinterpret_cast<uint64_t*>(ws + plan->ws_cand);
+  uint32_t* mask = reinterpret_cast<uint32_t*>(ws + plan->ws_mask);
+  uint32_t* kmask = reinterpret_cast<uint32_t*>(ws + plan->ws_kmask);
+  uint32_t* kpos = reinterpret_cast<uint32_t*>(ws + plan->ws_kpos);
+  uint32_t* tcnt = reinterpret_cast<uint32_t*>(ws + plan->ws_tcnt);
+  uint32_t* tbase = reinterpret_cast<uint32_t*>(ws + plan->ws_tbase);
+  uint32_t* kcnt = reinterpret_cast<uint32_t*>(ws + plan->ws_kcnt);
+  uint32_t* kbase = reinterpret_cast<uint32_t*>(ws + plan->ws_kbase);
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int nl = int(plan->layers.size());
+  const int ntiles = int(plan->tiles.size());
+  const int64_t sstride = int64_t(stride);
+  const int64_t cstride = plan->cand_total;
+  const dim3 tgrid(static_cast<unsigned>(ntiles), static_cast<unsigned>(W));
+  const dim3 sgrid(static_cast<unsigned>(nl), static_cast<unsigned>(W));
+  const int64_t nzero = (int64_t(plan->ws_candcnt) - int64_t(plan->ws_hist)) / 4 + plan->n_seg;
+  const unsigned zblocks = unsigned(std::min<int64_t>((nzero + 255) / 256, 4096));
+
+  if ((s = launch(plan, kZero, rk_zero, dim3(zblocks), dim3(256), st, hist, nzero)) != PSGD_OK) return s;
+  if (plan->dtype == PSGD_BF16)
+    s = launch(plan, kEfHist, rk_ef_hist<uint16_t>, tgrid, dim3(kTileThreads), st, static_cast<const RkTile*>(dt),
+               static_cast<const uint16_t*>(grads), errors, hist, sstride, nl);
+  else
+    s = launch(plan, kEfHist, rk_ef_hist<float>, tgrid, dim3(kTileThreads), st, static_cast<const RkTile*>(dt),
+               static_cast<const float*>(grads), errors, hist, sstride, nl);
+  if (s != PSGD_OK) return s;
+  if ((s = launch(plan, kSelect, rk_select, sgrid, dim3(256), st, static_cast<const RkLayer*>(dl),
+                  static_cast<const uint32_t*>(hist), seg, nl)) != PSGD_OK)
+    return s;
+  if ((s = launch(plan, kMark, rk_mark, tgrid, dim3(kTileThreads), st, static_cast<const RkTile*>(dt),
+                  static_cast<const RkLayer*>(dl), static_cast<const float*>(errors), static_cast<const RkSeg*>(seg),
+                  mask, tcnt, cand, candcnt, sstride, cstride, nl, ntiles)) != PSGD_OK)
+    return s;
+  if ((s = launch(plan, kRefine, rk_refine, sgrid, dim3(kSegThreads), st, static_cast<const RkLayer*>(dl),
+                  static_cast<const float*>(errors), static_cast<const RkSeg*>(seg), static_cast<const uint64_t*>(cand),
+                  static_cast<const uint32_t*>(candcnt), mask, tcnt, sstride, cstride, nl, ntiles)) != PSGD_OK)
+    return s;
+  if ((s = launch(plan, kScanTop, rk_scan_tiles, sgrid, dim3(kSegThreads), st, static_cast<const RkLayer*>(dl),
+                  static_cast<const uint32_t*>(tcnt), tbase, seg, index, value, plan->keep_total, nl, ntiles, 0)) !=
+      PSGD_OK)
+    return s;
+  if ((s = launch(plan, kKeep, rk_keep, tgrid, dim3(kWordThreads), st, static_cast<const RkTile*>(dt),
+                  static_cast<const RkLayer*>(dl), static_cast<const uint32_t*>(mask),
+                  static_cast<const uint32_t*>(tbase), ranks, kmask, kcnt, sstride, plan->top_total, ntiles)) !=
+      PSGD_OK)
+    return s;
+  if ((s = launch(plan, kScanKept, rk_scan_tiles, sgrid, dim3(kSegThreads), st, static_cast<const RkLayer*>(dl),
+                  static_cast<const uint32_t*>(kcnt), kbase, seg, index, value, plan->keep_total, nl, ntiles, 1)) !=
+      PSGD_OK)
+    return s;
+  if ((s = launch(plan, kEmit, rk_emit, tgrid, dim3(kWordThreads), st, static_cast<const RkTile*>(dt),
+                  static_cast<const RkLayer*>(dl), kmask, static_cast<const uint32_t*>(kbase), errors, index, value,
+                  kpos, sstride, plan->keep_total, ntiles)) != PSGD_OK)
+    return s;
+  if (update != nullptr)
+    s = launch(plan, kUpdate, rk_update, dim3(unsigned(ntiles)), dim3(kDenseThreads), st,
+               static_cast<const RkTile*>(dt), static_cast<const RkLayer*>(dl), static_cast<const uint32_t*>(kmask),
+               static_cast<const uint32_t*>(kpos), static_cast<const float*>(value), update, int(W), sstride,
+               plan->keep_total, 1.0f / float(W));
+  return s;
+}

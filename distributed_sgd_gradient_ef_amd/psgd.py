@@ -1,4 +1,5 @@
-"""Thin ctypes binding of libpsgd (C ABI declared in include/psgd.h).
+"""Thin ctypes binding of libpsgd (C ABI declared in include/psgd.h and
+include/psgd_rtopk.h).
 
 Functions carry the C names.  The step functions take torch tensors on a ROCm device
 and pass their device pointers and the current HIP stream; every step of the
@@ -37,7 +38,10 @@ EXPORTED = [
     "psgd_compress_step", "psgd_ef_momentum_apply", "psgd_plan_set_timing",
     "psgd_plan_kernel_stats", "psgd_plan_reset_carry", "psgd_errors_materialize", "psgd_stream_copy",
     "psgd_plan_set_power_iterations", "psgd_status_string", "psgd_last_error",
+    "psgd_rtopk_plan_create", "psgd_rtopk_plan_sizes", "psgd_rtopk_plan_layer_info", "psgd_rtopk_plan_destroy",
+    "psgd_rtopk_step", "psgd_rtopk_plan_set_timing", "psgd_rtopk_plan_kernel_stats",
 ]
+_STRING_FUNCS = ("psgd_status_string", "psgd_last_error")
 
 
 class PsgdError(RuntimeError):
@@ -71,6 +75,21 @@ class _Sizes(ctypes.Structure):
                 ("model_bytes", ctypes.c_uint64), ("model_bytes_momentum", ctypes.c_uint64)]
 
 
+class _RtopkLayerInfo(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("numel", ctypes.c_int64),
+                ("offset", ctypes.c_int64), ("top", ctypes.c_int64), ("keep", ctypes.c_int64),
+                ("top_offset", ctypes.c_int64), ("keep_offset", ctypes.c_int64)]
+
+
+class _RtopkSizes(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("n_workers", ctypes.c_int32),
+                ("grad_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("worker_stride", ctypes.c_int64), ("numel", ctypes.c_int64),
+                ("top_total", ctypes.c_int64), ("keep_total", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_uint64), ("message_bytes", ctypes.c_uint64),
+                ("model_bytes", ctypes.c_uint64)]
+
+
 _lib = None
 
 
@@ -101,8 +120,18 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.psgd_stream_copy.argtypes = [vp, vp, ctypes.c_uint64, vp]
     lib.psgd_errors_materialize.argtypes = [vp, vp, vp, vp, vp]
     lib.psgd_plan_set_power_iterations.argtypes = [vp, i32]
-    for name in EXPORTED[:12]:
-        getattr(lib, name).restype = ctypes.c_int
+    i64p = ctypes.POINTER(i64)
+    lib.psgd_rtopk_plan_create.argtypes = [ctypes.POINTER(_Layer), i32, i64p, i64p, i32, i32, ctypes.c_uint32,
+                                           ctypes.POINTER(vp)]
+    lib.psgd_rtopk_plan_sizes.argtypes = [vp, ctypes.POINTER(_RtopkSizes)]
+    lib.psgd_rtopk_plan_layer_info.argtypes = [vp, i32, ctypes.POINTER(_RtopkLayerInfo)]
+    lib.psgd_rtopk_plan_destroy.argtypes = [vp]
+    lib.psgd_rtopk_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.psgd_rtopk_plan_set_timing.argtypes = [vp, i32]
+    lib.psgd_rtopk_plan_kernel_stats.argtypes = [vp, ctypes.POINTER(_KernelStat), i32, ctypes.POINTER(i32), i32]
+    for name in EXPORTED:
+        if name not in _STRING_FUNCS:
+            getattr(lib, name).restype = ctypes.c_int
     lib.psgd_status_string.argtypes = [ctypes.c_int]
     lib.psgd_status_string.restype = ctypes.c_char_p
     lib.psgd_last_error.argtypes = []
@@ -245,8 +274,91 @@ def psgd_ef_momentum_apply(plan: Plan, grads, errors, q, p, momentum, params, lr
             float(lr), float(mu), _ptr(update), _ptr(workspace), _stream(stream, grads)))
 
 
+# ------------------------------------------------------------------------ rTop-k
+@dataclass
+class RtopkLayerInfo:
+    rows: int
+    cols: int
+    numel: int
+    offset: int
+    top: int
+    keep: int
+    top_offset: int
+    keep_offset: int
+
+
+class RtopkPlan:
+    """Owns a psgd_rtopk_plan*; freed by psgd_rtopk_plan_destroy (or when collected)."""
+
+    def __init__(self, handle: int, shapes: Sequence[Tuple[int, int]]):
+        self.handle = handle
+        self.shapes = [tuple(int(v) for v in s) for s in shapes]
+        self.sizes = psgd_rtopk_plan_sizes(self)
+        self.layers: List[RtopkLayerInfo] = [psgd_rtopk_plan_layer_info(self, i) for i in range(len(shapes))]
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            try:
+                psgd_rtopk_plan_destroy(self)
+            except Exception:
+                pass
+
+
+def psgd_rtopk_plan_create(shapes: Sequence[Tuple[int, int]], top: Sequence[int], keep: Sequence[int],
+                           n_workers: int, grad_dtype: int = PSGD_F32, flags: int = 0) -> RtopkPlan:
+    lib = load_library()
+    n = len(shapes)
+    arr = (_Layer * max(1, n))(*[_Layer(int(r), int(c)) for r, c in shapes])
+    tops = (ctypes.c_int64 * max(1, n))(*[int(v) for v in top])
+    keeps = (ctypes.c_int64 * max(1, n))(*[int(v) for v in keep])
+    h = ctypes.c_void_p()
+    _check(lib.psgd_rtopk_plan_create(arr, n, tops, keeps, int(n_workers), int(grad_dtype), int(flags),
+                                      ctypes.byref(h)))
+    return RtopkPlan(h.value, shapes)
+
+
+def psgd_rtopk_plan_sizes(plan: RtopkPlan) -> dict:
+    s = _RtopkSizes()
+    _check(load_library().psgd_rtopk_plan_sizes(plan.handle, ctypes.byref(s)))
+    return {name: getattr(s, name) for name, _ in _RtopkSizes._fields_}
+
+
+def psgd_rtopk_plan_layer_info(plan: RtopkPlan, layer: int) -> RtopkLayerInfo:
+    li = _RtopkLayerInfo()
+    _check(load_library().psgd_rtopk_plan_layer_info(plan.handle, int(layer), ctypes.byref(li)))
+    return RtopkLayerInfo(*(getattr(li, name) for name, _ in _RtopkLayerInfo._fields_))
+
+
+def psgd_rtopk_plan_destroy(plan: RtopkPlan) -> None:
+    h, plan.handle = plan.handle, None
+    if h:
+        _check(load_library().psgd_rtopk_plan_destroy(h))
+
+
+def psgd_rtopk_plan_set_timing(plan: RtopkPlan, enable: bool) -> None:
+    _check(load_library().psgd_rtopk_plan_set_timing(plan.handle, 1 if enable else 0))
+
+
+def psgd_rtopk_plan_kernel_stats(plan: RtopkPlan, reset: bool = False) -> dict:
+    """{kernel name: (launches, total_ms)}; waits for every timed launch so far."""
+    arr = (_KernelStat * 16)()
+    n = ctypes.c_int32()
+    _check(load_library().psgd_rtopk_plan_kernel_stats(plan.handle, arr, 16, ctypes.byref(n), 1 if reset else 0))
+    return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(n.value)}
+
+
+def psgd_rtopk_step(plan: RtopkPlan, grads, errors, ranks, index, value, update, workspace, stream=None) -> None:
+    """Enqueue one rTop-k step (tensors on a ROCm device; see include/psgd_rtopk.h)."""
+    import torch
+
+    with torch.cuda.device(grads.device):
+        _check(load_library().psgd_rtopk_step(
+            plan.handle, _ptr(grads), _ptr(errors), _ptr(ranks), _ptr(index), _ptr(value), _ptr(update),
+            _ptr(workspace), _stream(stream, grads)))
+
+
 # ------------------------------------------------------------------------ layout helpers
-def pack(plan: Plan, per_layer: Sequence[np.ndarray], dtype=np.float32, workers: Optional[int] = None,
+def pack(plan, per_layer: Sequence[np.ndarray], dtype=np.float32, workers: Optional[int] = None,
          layers: Optional[Sequence[int]] = None) -> np.ndarray:
     """Place per-tensor arrays into the packed layout.
 
@@ -267,7 +379,7 @@ def pack(plan: Plan, per_layer: Sequence[np.ndarray], dtype=np.float32, workers:
     return out
 
 
-def unpack(plan: Plan, flat: np.ndarray, layer: int) -> np.ndarray:
+def unpack(plan, flat: np.ndarray, layer: int) -> np.ndarray:
     """Inverse of ``pack`` for one tensor: (W, rows, cols) or (rows, cols)."""
     L = plan.layers[layer]
     n = L.rows * L.cols
@@ -296,3 +408,22 @@ def pack_factors(plan: Plan, per_matrix: dict, which: str) -> np.ndarray:
         k = (L.rows if which == "p" else L.cols) * r
         out[off:off + k] = np.asarray(a, dtype=np.float32).reshape(k)
     return out
+
+
+def pack_rows(plan: RtopkPlan, per_layer: Sequence[np.ndarray], which: str, dtype) -> np.ndarray:
+    """Concatenate per-tensor (W, top) or (W, keep) arrays into the [W][top_total] or
+    [W][keep_total] rows of an rTop-k plan."""
+    W = plan.sizes["n_workers"]
+    total = plan.sizes["top_total" if which == "top" else "keep_total"]
+    out = np.zeros((W, total), dtype=dtype)
+    for a, L in zip(per_layer, plan.layers):
+        off, n = (L.top_offset, L.top) if which == "top" else (L.keep_offset, L.keep)
+        out[:, off:off + n] = np.asarray(a).reshape(W, n)
+    return out
+
+
+def row_slice(plan: RtopkPlan, rows: np.ndarray, layer: int, which: str) -> np.ndarray:
+    """One tensor's (W, top) or (W, keep) block of a [W][total] row array."""
+    L = plan.layers[layer]
+    off, n = (L.top_offset, L.top) if which == "top" else (L.keep_offset, L.keep)
+    return rows[:, off:off + n]

@@ -1,7 +1,7 @@
-"""Seeded synthetic workloads for the PowerSGD compression step.
+"""Seeded synthetic workloads for the PowerSGD and rTop-k compression steps.
 
-This module only draws inputs (gradients, the initial Q, parameters) and lists layer
-shapes.  It holds none of the compression arithmetic, so both the GPU library's tests
+This module only draws inputs (gradients, the initial Q, parameters, the random ranks
+that pick rTop-k's subset) and lists layer shapes.  It holds none of the compression arithmetic, so both the GPU library's tests
 and the CPU oracle can consume what it produces.
 
 Every draw comes from a Philox4x32-10 counter-based stream (numpy's ``Philox`` bit
@@ -27,7 +27,7 @@ import numpy as np
 Shape = Tuple[int, int]  # (rows, cols); a 1-D tensor of length d is (1, d)
 
 # purpose tags for the stream keys
-_P_FACTOR_U, _P_FACTOR_V, _P_NOISE, _P_Q0, _P_PARAM, _P_ROWS, _P_DRIFT = range(7)
+_P_FACTOR_U, _P_FACTOR_V, _P_NOISE, _P_Q0, _P_PARAM, _P_ROWS, _P_DRIFT, _P_RANKS = range(8)
 
 
 # --------------------------------------------------------------------------- shapes
@@ -107,6 +107,8 @@ class Workload:
     drift_rad: float = 0.0  # per-step rotation of the planted subspaces
     lr: float = 0.0
     mu: float = 0.0
+    keep_frac: float = 0.01  # rTop-k: entries sent per tensor, as a fraction of its size
+    top_factor: int = 2      # rTop-k: top-set size as a multiple of the sent count
 
     @property
     def matrix_shapes(self) -> List[Shape]:
@@ -136,6 +138,13 @@ def workload(name: str, **overrides) -> Workload:
         # bandwidth stress, W=4, r in {1,2,4}
         "stress": dict(name="stress", shapes=tuple(stress_shapes()), rank=2, workers=4,
                        steps=2, seed=1004, signal="stress"),
+        # rTop-k on ResNet-18 shapes: same gradient recipe, 16 workers, 1% of each
+        # tensor sent, drawn from its top 2%
+        "resnet18_rtopk": dict(name="resnet18_rtopk", shapes=tuple(resnet18_cifar_shapes()), rank=2,
+                               workers=16, steps=3, seed=1006, signal="resnet"),
+        # rTop-k on the LSTM shapes (a 5%-row-sparse embedding gradient), 8 workers
+        "lstm_rtopk": dict(name="lstm_rtopk", shapes=tuple(lstm_wikitext2_shapes()), rank=4, workers=8,
+                           steps=2, seed=1007, signal="lstm"),
         # full EF-SGD with momentum on ResNet-18 shapes, drifting subspace
         "resnet18_momentum": dict(name="resnet18_momentum", shapes=tuple(resnet18_cifar_shapes()),
                                   rank=4, workers=16, steps=200, seed=1005, signal="resnet",
@@ -285,6 +294,23 @@ def grads(wl: Workload, step: int, layers: Optional[Sequence[int]] = None) -> Li
             a[w] = grad_layer(wl, li, step, w, lr)
         out.append(a)
     return out
+
+
+def rtopk_counts(wl: Workload) -> Tuple[List[int], List[int]]:
+    """Per-tensor (top, keep) counts: keep = max(1, ceil(keep_frac * numel)) and
+    top = min(numel, top_factor * keep)."""
+    tops, keeps = [], []
+    for _, (n, m) in wl.shapes:
+        d = n * m
+        k = max(1, int(math.ceil(wl.keep_frac * d)))
+        tops.append(min(d, wl.top_factor * k))
+        keeps.append(k)
+    return tops, keeps
+
+
+def rtopk_ranks(wl: Workload, step: int, worker: int, layer: int, top: int) -> np.ndarray:
+    """Random ranks of one tensor's top set: a uniform permutation of 0..top-1 (uint32)."""
+    return stream(wl.seed, _P_RANKS, step, worker, layer).permutation(top).astype(np.uint32)
 
 
 def q0(wl: Workload, layer: int) -> np.ndarray:

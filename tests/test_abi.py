@@ -1,4 +1,4 @@
-"""The C ABI without a GPU: the library loads, exports every function include/psgd.h
+"""The C ABI without a GPU: the library loads, exports every function include/*.h
 declares, validates its arguments before touching the device, and its plan reproduces
 the layout and byte accounting the workloads need."""
 
@@ -13,15 +13,18 @@ from distributed_sgd_gradient_ef_amd import psgd
 from distributed_sgd_gradient_ef_amd import workloads as WL
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "psgd.h")
+HEADERS = [os.path.join(ROOT, "include", name) for name in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if name.endswith(".h")]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(psgd.LIB_PATH), reason="libpsgd.so not built")
 
 
 def _declared():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(psgd_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(psgd_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol():

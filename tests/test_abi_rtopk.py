@@ -1,0 +1,135 @@
+"""The rTop-k half of the C ABI without a GPU: plan validation, the packed layout and
+row offsets, byte accounting, and argument checks of psgd_rtopk_step that happen before
+any device call (the fake addresses below are never dereferenced)."""
+
+import math
+import os
+
+import numpy as np
+import pytest
+
+from distributed_sgd_gradient_ef_amd import psgd
+from distributed_sgd_gradient_ef_amd import workloads as WL
+
+pytestmark = pytest.mark.skipif(not os.path.exists(psgd.LIB_PATH), reason="libpsgd.so not built")
+
+SHAPES = [(64, 27), (1, 64), (10, 512), (3, 5)]
+TOPS = [35, 2, 103, 15]
+KEEPS = [18, 1, 52, 1]
+
+
+def _plan(W=4, dtype=psgd.PSGD_F32, shapes=SHAPES, tops=TOPS, keeps=KEEPS):
+    return psgd.psgd_rtopk_plan_create(shapes, tops, keeps, W, dtype)
+
+
+@pytest.mark.parametrize("tops,keeps", [
+    ([35, 2, 103, 16], KEEPS),      # top > numel
+    ([35, 2, 103, 15], [18, 3, 52, 1]),  # keep > top
+    ([35, 2, 103, 15], [18, 0, 52, 1]),  # keep < 1
+    ([35, 0, 103, 15], [18, 0, 52, 1]),  # top < 1
+])
+def test_plan_create_rejects_bad_counts(tops, keeps):
+    with pytest.raises(psgd.PsgdError) as e:
+        _plan(tops=tops, keeps=keeps)
+    assert e.value.status == psgd.PSGD_ERR_INVALID_ARG
+
+
+def test_plan_create_rejects_bad_arguments():
+    lib = psgd.load_library()
+    with pytest.raises(psgd.PsgdError) as e:
+        _plan(W=0)
+    assert e.value.status == psgd.PSGD_ERR_INVALID_ARG
+    with pytest.raises(psgd.PsgdError) as e:
+        _plan(dtype=7)
+    assert e.value.status == psgd.PSGD_ERR_UNSUPPORTED
+    with pytest.raises(psgd.PsgdError) as e:
+        psgd.psgd_rtopk_plan_create(SHAPES, TOPS, KEEPS, 2, psgd.PSGD_F32, flags=1)
+    assert e.value.status == psgd.PSGD_ERR_UNSUPPORTED
+    with pytest.raises(psgd.PsgdError) as e:
+        psgd.psgd_rtopk_plan_create([(65536, 32768)], [1], [1], 1)   # 2^31 elements
+    assert e.value.status == psgd.PSGD_ERR_INVALID_ARG
+    with pytest.raises(psgd.PsgdError):
+        psgd.psgd_rtopk_plan_create([(0, 5)], [1], [1], 1)
+    assert lib.psgd_rtopk_plan_create(None, 1, None, None, 1, 0, 0, None) == psgd.PSGD_ERR_INVALID_ARG
+
+
+def test_layout_and_rows():
+    plan = _plan()
+    s = plan.sizes
+    assert s["n_layers"] == 4 and s["n_workers"] == 4
+    assert s["numel"] == sum(r * c for r, c in SHAPES)
+    assert s["top_total"] == sum(TOPS) and s["keep_total"] == sum(KEEPS)
+    assert s["worker_stride"] % 64 == 0
+    end = 0
+    for L, (r, c), t, k in zip(plan.layers, SHAPES, TOPS, KEEPS):
+        assert L.offset % 64 == 0 and L.offset >= end
+        assert (L.rows, L.cols, L.numel, L.top, L.keep) == (r, c, r * c, t, k)
+        end = L.offset + L.numel
+    assert end <= s["worker_stride"]
+    assert [L.top_offset for L in plan.layers] == list(np.cumsum([0] + TOPS[:-1]))
+    assert [L.keep_offset for L in plan.layers] == list(np.cumsum([0] + KEEPS[:-1]))
+    assert s["message_bytes"] == 8 * sum(KEEPS)
+
+
+@pytest.mark.parametrize("dtype,gb", [(psgd.PSGD_F32, 4), (psgd.PSGD_BF16, 2)])
+def test_model_bytes(dtype, gb):
+    W = 16
+    plan = _plan(W=W, dtype=dtype)
+    assert plan.sizes["model_bytes"] == (W * (gb + 8) + 4) * plan.sizes["numel"]
+
+
+def test_workload_counts_plan():
+    wl = WL.workload("resnet18_rtopk")
+    tops, keeps = WL.rtopk_counts(wl)
+    plan = psgd.psgd_rtopk_plan_create([s for _, s in wl.shapes], tops, keeps, wl.workers)
+    for L in plan.layers:
+        assert L.keep == max(1, math.ceil(0.01 * L.numel)) and L.top == min(L.numel, 2 * L.keep)
+    # each row of ranks is a permutation of its top set
+    for li in (0, 5, 61):
+        r = WL.rtopk_ranks(wl, 0, 3, li, tops[li])
+        assert r.dtype == np.uint32 and np.array_equal(np.sort(r), np.arange(tops[li]))
+
+
+def _args(plan, **over):
+    ws = plan.sizes["workspace_bytes"]
+    a = dict(grads=0x10000000, errors=0x20000000, ranks=0x30000000, index=0x40000000, value=0x50000000,
+             update=0x60000000, workspace=0x70000000)
+    a.update(over)
+    assert ws < 0x10000000
+    return a
+
+
+@pytest.mark.parametrize("bad", [dict(grads=None), dict(errors=None), dict(ranks=None), dict(index=None),
+                                 dict(value=None), dict(workspace=None), dict(grads=0x10000004),
+                                 dict(index=0x40000008), dict(value=0x40000000), dict(update=0x20000010)])
+def test_step_rejects_bad_pointers_before_any_device_call(bad):
+    lib = psgd.load_library()
+    plan = _plan()
+    a = _args(plan, **bad)
+    st = lib.psgd_rtopk_step(plan.handle, a["grads"], a["errors"], a["ranks"], a["index"], a["value"], a["update"],
+                             a["workspace"], None)
+    assert st == psgd.PSGD_ERR_INVALID_ARG
+    assert lib.psgd_last_error()
+
+
+def test_step_rejects_null_plan():
+    lib = psgd.load_library()
+    assert lib.psgd_rtopk_step(None, 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, None, 0x6000, None) == \
+        psgd.PSGD_ERR_INVALID_ARG
+
+
+def test_timing_calls_without_gpu():
+    plan = _plan()
+    psgd.psgd_rtopk_plan_set_timing(plan, True)
+    assert psgd.psgd_rtopk_plan_kernel_stats(plan) == {}
+    psgd.psgd_rtopk_plan_set_timing(plan, False)
+
+
+def test_pack_rows_roundtrip():
+    plan = _plan(W=3)
+    rng = np.random.default_rng(0)
+    per = [rng.integers(0, 100, size=(3, t)).astype(np.uint32) for t in TOPS]
+    rows = psgd.pack_rows(plan, per, "top", np.uint32)
+    assert rows.shape == (3, sum(TOPS))
+    for li, a in enumerate(per):
+        assert np.array_equal(psgd.row_slice(plan, rows, li, "top"), a)

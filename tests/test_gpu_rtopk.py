@@ -1,0 +1,333 @@
+"""GPU parity of the rTop-k step (libpsgd through its C ABI) against the CPU oracle.
+
+Indices, sent values and the new error memory are compared bit for bit (the selection
+is decided on the same float32 M on both sides); the update, a float32 sum of at most W
+sent values per element, is compared against the oracle's float64 mean within the
+rounding bound of that sum.  Every case prints what names it before touching the GPU.
+"""
+
+import numpy as np
+import pytest
+
+from distributed_sgd_gradient_ef_amd import psgd as P
+from distributed_sgd_gradient_ef_amd import workloads as WL
+from oracle import rtopk_ef as O
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+DEV = "cuda:0"
+
+
+class RtopkRun:
+    """Device buffers of one rTop-k plan, filled with garbage where the step must write."""
+
+    def __init__(self, shapes, tops, keeps, W, bf16=False):
+        self.plan = P.psgd_rtopk_plan_create(shapes, tops, keeps, W, P.PSGD_BF16 if bf16 else P.PSGD_F32)
+        s = self.plan.sizes
+        self.W, self.bf16 = W, bf16
+        self.stride = s["worker_stride"]
+        self.g = torch.zeros((W, self.stride), dtype=torch.bfloat16 if bf16 else torch.float32, device=DEV)
+        self.e = torch.zeros((W, self.stride), dtype=torch.float32, device=DEV)
+        self.ranks = torch.zeros((W, max(1, s["top_total"])), dtype=torch.int32, device=DEV)
+        self.index = torch.full((W, max(1, s["keep_total"])), 0x7EADBEEF, dtype=torch.int32, device=DEV)
+        self.value = torch.full((W, max(1, s["keep_total"])), float("nan"), dtype=torch.float32, device=DEV)
+        self.update = torch.full((self.stride,), float("nan"), dtype=torch.float32, device=DEV)
+        self.ws = torch.full((max(256, s["workspace_bytes"]),), 0xAB, dtype=torch.uint8, device=DEV)
+
+    def set_grads(self, per_layer):
+        flat = P.pack(self.plan, [np.asarray(a, np.float32) for a in per_layer])
+        t = torch.from_numpy(flat).to(DEV)
+        self.g.copy_(t.to(torch.bfloat16) if self.bf16 else t)
+
+    def set_errors(self, per_layer):
+        self.e.copy_(torch.from_numpy(P.pack(self.plan, per_layer)).to(DEV))
+
+    def set_ranks(self, per_layer):
+        rows = P.pack_rows(self.plan, per_layer, "top", np.uint32).view(np.int32)
+        self.ranks[:, :rows.shape[1]].copy_(torch.from_numpy(rows).to(DEV))
+
+    def step(self, update=True):
+        P.psgd_rtopk_step(self.plan, self.g, self.e, self.ranks, self.index, self.value,
+                          self.update if update else None, self.ws)
+        torch.cuda.synchronize()
+
+    def grads_f32(self, li):
+        return P.unpack(self.plan, self.g.float().cpu().numpy(), li).reshape(self.W, -1)
+
+    def errors(self, li):
+        return P.unpack(self.plan, self.e.cpu().numpy(), li).reshape(self.W, -1)
+
+    def sent(self, li):
+        idx = P.row_slice(self.plan, self.index.cpu().numpy(), li, "keep")
+        val = P.row_slice(self.plan, self.value.cpu().numpy(), li, "keep")
+        return idx, val
+
+    def upd(self, li):
+        return P.unpack(self.plan, self.update.cpu().numpy(), li).reshape(-1)
+
+
+def _bits(a):
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
+def compare(run, li, st, nan_ok=False, check_update=True):
+    """Exact index/value/error parity and the update within its rounding bound."""
+    idx, val = run.sent(li)
+    assert np.array_equal(idx.astype(np.int64), st.index), f"layer {li}: indices differ"
+    e = run.errors(li)
+    if nan_ok:
+        assert np.array_equal(val, st.value, equal_nan=True)
+        assert np.array_equal(e, st.errors, equal_nan=True)
+    else:
+        assert np.array_equal(_bits(val), _bits(st.value)), f"layer {li}: sent values differ"
+        assert np.array_equal(_bits(e), _bits(st.errors)), f"layer {li}: errors differ"
+    if check_update:
+        u = run.upd(li).astype(np.float64)
+        W = run.W
+        absum = np.zeros_like(st.update)
+        for w in range(W):
+            ok = st.index[w] >= 0
+            np.add.at(absum, st.index[w][ok], np.abs(st.value[w][ok].astype(np.float64)))
+        bound = (W + 2) * 2.0 ** -24 * absum / W
+        if nan_ok:
+            fin = np.isfinite(st.update)
+            assert np.array_equal(np.isnan(u), np.isnan(st.update))
+            assert np.all(np.abs(u[fin] - st.update[fin]) <= bound[fin])
+        else:
+            assert np.all(np.abs(u - st.update) <= bound), f"layer {li}: update outside the rounding bound"
+
+
+def oracle_step(run, G, E, tops, keeps, ranks, layers):
+    return {li: O.compress_tensor(G[li], E[li], tops[li], keeps[li], ranks[li]) for li in layers}
+
+
+def _counts(shapes, keep_frac=0.01, factor=2):
+    tops, keeps = [], []
+    for r, c in shapes:
+        d = r * c
+        k = max(1, int(np.ceil(keep_frac * d)))
+        tops.append(min(d, factor * k))
+        keeps.append(k)
+    return tops, keeps
+
+
+def _ranks(rng, W, tops):
+    return [np.stack([rng.permutation(t) for _ in range(W)]).astype(np.uint32) for t in tops]
+
+
+# ragged sizes: tiny, not a multiple of 4 or 32, exactly one tile, several tiles + tail
+RAGGED = [(64, 27), (1, 64), (10, 512), (3, 5), (1, 1), (5, 4099), (4096, 1), (1, 2 * 4096 + 33)]
+
+
+@pytest.mark.parametrize("W", [1, 3, 4])
+def test_ragged_multilayer_three_steps(W):
+    print(f"\n[case] ragged multilayer W={W}", flush=True)
+    rng = np.random.default_rng(100 + W)
+    tops, keeps = _counts(RAGGED, 0.05, 3)
+    tops[4], keeps[4] = 1, 1            # a single element
+    tops[3], keeps[3] = 15, 15          # everything sent
+    run = RtopkRun(RAGGED, tops, keeps, W)
+    E = [np.zeros((W, r * c), np.float32) for r, c in RAGGED]
+    for step in range(3):
+        G = [rng.standard_normal((W, r * c)).astype(np.float32) for r, c in RAGGED]
+        R = _ranks(rng, W, tops)
+        run.set_grads(G)
+        run.set_ranks(R)
+        run.step()
+        ref = oracle_step(run, G, E, tops, keeps, R, range(len(RAGGED)))
+        for li, st in ref.items():
+            compare(run, li, st)
+        E = [ref[li].errors for li in range(len(RAGGED))]
+
+
+def test_ties_zeros_and_one_bin():
+    """Many exact ties (index order decides), a top set larger than the nonzeros (ties at
+    zero), and a tensor whose values all share one level-1 bin, so its candidates do not
+    fit the list and the segment is rescanned."""
+    print("\n[case] ties / zeros / one bin", flush=True)
+    W = 2
+    shapes = [(1, 3000), (1, 5000), (1, 50000), (1, 40000)]
+    rng = np.random.default_rng(7)
+    G0 = rng.choice(np.float32([-2, -1, 0, 1, 2, 3]), size=(W, 3000)).astype(np.float32)
+    G1 = np.zeros((W, 5000), np.float32)
+    G1[:, rng.choice(5000, 40, replace=False)] = rng.standard_normal((W, 40)).astype(np.float32)
+    G2 = (1.0 + 0.0625 * rng.random((W, 50000))).astype(np.float32)   # one bin: [1, 1.0625)
+    G3 = rng.choice(np.float32([1.0, 1.03125, -1.03125]), size=(W, 40000)).astype(np.float32)  # one bin, ties
+    G = [G0, G1, G2, G3]
+    tops, keeps = [700, 300, 20000, 9000], [350, 100, 5000, 4000]
+    R = _ranks(rng, W, tops)
+    run = RtopkRun(shapes, tops, keeps, W)
+    run.set_grads(G)
+    run.set_ranks(R)
+    run.step()
+    E = [np.zeros((W, r * c), np.float32) for r, c in shapes]
+    for li, st in oracle_step(run, G, E, tops, keeps, R, range(4)).items():
+        compare(run, li, st)
+
+
+def test_bf16_gradients():
+    print("\n[case] bf16 gradients W=4", flush=True)
+    W = 4
+    rng = np.random.default_rng(8)
+    shapes = RAGGED[:6]
+    tops, keeps = _counts(shapes, 0.03, 2)
+    run = RtopkRun(shapes, tops, keeps, W, bf16=True)
+    E = [(0.1 * rng.standard_normal((W, r * c))).astype(np.float32) for r, c in shapes]
+    G = [WL.to_bf16_values(rng.standard_normal((W, r * c)).astype(np.float32)) for r, c in shapes]
+    R = _ranks(rng, W, tops)
+    run.set_grads(G)
+    run.set_errors(E)
+    run.set_ranks(R)
+    run.step()
+    for li, st in oracle_step(run, G, E, tops, keeps, R, range(len(shapes))).items():
+        compare(run, li, st)
+
+
+def test_invalid_ranks_follow_the_oracle():
+    print("\n[case] ranks that are not permutations", flush=True)
+    W = 3
+    rng = np.random.default_rng(9)
+    shapes = [(1, 500), (20, 30), (1, 7000)]
+    tops, keeps = [40, 60, 300], [10, 20, 100]
+    G = [rng.standard_normal((W, r * c)).astype(np.float32) for r, c in shapes]
+    R = [np.zeros((W, 40), np.uint32),                               # every rank below k
+         np.full((W, 60), 0xFFFFFFFF, np.uint32),                    # none below k
+         rng.integers(0, 150, size=(W, 300)).astype(np.uint32)]      # duplicates, about 2/3 below k
+    run = RtopkRun(shapes, tops, keeps, W)
+    run.set_grads(G)
+    run.set_ranks(R)
+    run.step()
+    E = [np.zeros((W, r * c), np.float32) for r, c in shapes]
+    for li, st in oracle_step(run, G, E, tops, keeps, R, range(3)).items():
+        compare(run, li, st)
+
+
+def test_nonfinite_values():
+    print("\n[case] NaN and infinities", flush=True)
+    W = 2
+    rng = np.random.default_rng(10)
+    shapes = [(1, 300), (10, 100)]
+    tops, keeps = [20, 50], [10, 25]
+    G = [rng.standard_normal((W, r * c)).astype(np.float32) for r, c in shapes]
+    G[0][0, 5] = np.nan
+    G[0][1, 7] = np.inf
+    G[0][1, 8] = -np.inf
+    G[1][0, 3:6] = np.inf
+    R = _ranks(rng, W, tops)
+    run = RtopkRun(shapes, tops, keeps, W)
+    run.set_grads(G)
+    run.set_ranks(R)
+    run.step()
+    E = [np.zeros((W, r * c), np.float32) for r, c in shapes]
+    for li, st in oracle_step(run, G, E, tops, keeps, R, range(2)).items():
+        compare(run, li, st, nan_ok=True)
+
+
+def test_update_null_and_determinism():
+    print("\n[case] update=NULL and run-to-run determinism", flush=True)
+    W = 4
+    rng = np.random.default_rng(11)
+    tops, keeps = _counts(RAGGED, 0.02, 2)
+    G = [rng.standard_normal((W, r * c)).astype(np.float32) for r, c in RAGGED]
+    E = [(0.5 * rng.standard_normal((W, r * c))).astype(np.float32) for r, c in RAGGED]
+    R = _ranks(rng, W, tops)
+    outs = []
+    for update in (True, True, False):
+        run = RtopkRun(RAGGED, tops, keeps, W)
+        run.set_grads(G)
+        run.set_errors(E)
+        run.set_ranks(R)
+        run.step(update=update)
+        outs.append((run.index.cpu().numpy(), _bits(run.value.cpu().numpy()), _bits(run.e.cpu().numpy()),
+                     _bits(run.update.cpu().numpy())))
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a, b)
+    for a, b in zip(outs[0][:3], outs[2][:3]):
+        assert np.array_equal(a, b)
+    assert np.all(np.isnan(run.update.cpu().numpy()))  # not written without an update buffer
+
+
+def test_timing_reports_every_kernel():
+    print("\n[case] kernel timing", flush=True)
+    W = 2
+    tops, keeps = _counts(RAGGED, 0.02, 2)
+    run = RtopkRun(RAGGED, tops, keeps, W)
+    rng = np.random.default_rng(12)
+    run.set_grads([rng.standard_normal((W, r * c)).astype(np.float32) for r, c in RAGGED])
+    run.set_ranks(_ranks(rng, W, tops))
+    P.psgd_rtopk_plan_set_timing(run.plan, True)
+    run.step()
+    run.step()
+    stats = P.psgd_rtopk_plan_kernel_stats(run.plan, reset=True)
+    assert set(stats) == {"rk_zero", "rk_ef_hist", "rk_select", "rk_mark", "rk_refine", "rk_scan_top",
+                          "rk_keep", "rk_scan_kept", "rk_emit", "rk_update"}
+    assert all(n == 2 and ms > 0 for n, ms in stats.values())
+
+
+def _device_workload_run(name, steps, layers_checked):
+    wl = WL.workload(name)
+    shapes = [s for _, s in wl.shapes]
+    tops, keeps = WL.rtopk_counts(wl)
+    W = wl.workers
+    run = RtopkRun(shapes, tops, keeps, W)
+    layout = [(L.offset, L.rows, L.cols) for L in run.plan.layers]
+    cache = {}
+    for step in range(steps):
+        print(f"[case] {name} step {step}", flush=True)
+        E = {li: run.errors(li) for li in layers_checked}
+        WL.device_grads(wl, step, layout, run.g, cache)
+        R = [np.stack([WL.rtopk_ranks(wl, step, w, li, tops[li]) for w in range(W)]) for li in range(len(shapes))]
+        run.set_ranks(R)
+        run.step()
+        G = {li: run.grads_f32(li) for li in layers_checked}
+        for li in layers_checked:
+            st = O.compress_tensor(G[li], E[li], tops[li], keeps[li], R[li])
+            compare(run, li, st)
+    return run
+
+
+def test_resnet18_rtopk_workload():
+    """ResNet-18 shapes, W=16, 1% sent from the top 2%, two steps with error feedback;
+    the oracle checks the largest matrices, a middle one and small tensors."""
+    _device_workload_run("resnet18_rtopk", 2, [0, 1, 2, 14, 17, 19, 20, 21, 40, 61])
+
+
+def test_lstm_rtopk_workload():
+    """Tall LSTM shapes with the 5%-row-sparse embedding gradient, W=8, one step; the
+    tied embedding (21.6M entries) and one dense matrix against the oracle."""
+    _device_workload_run("lstm_rtopk", 1, [0, 3])
+
+
+def test_largest_tensor():
+    """One 8192 x 8192 tensor (the largest of the bandwidth stress set), W=2: worker 0
+    against the oracle; worker 1 against the threshold definition of the top set."""
+    print("\n[case] 8192 x 8192, W=2", flush=True)
+    W, n = 2, 8192 * 8192
+    k = n // 100
+    run = RtopkRun([(8192, 8192)], [2 * k], [k], W)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(1234)
+    torch.randn((W, run.stride), generator=gen, device=DEV, out=run.g)
+    rng = np.random.default_rng(13)
+    R = [np.stack([rng.permutation(2 * k) for _ in range(W)]).astype(np.uint32)]
+    run.set_ranks(R)
+    G = run.grads_f32(0)
+    run.step()
+    st = O.compress_tensor(G[:1], np.zeros((1, n), np.float32), 2 * k, k, R[0][:1])
+    idx, val = run.sent(0)
+    assert np.array_equal(idx[0].astype(np.int64), st.index[0])
+    assert np.array_equal(_bits(val[0]), _bits(st.value[0]))
+    e1 = run.errors(0)[1]
+    m = G[1]
+    a = np.abs(m.astype(np.float64))
+    t = np.partition(a, n - 2 * k)[n - 2 * k]
+    top = np.flatnonzero(a > t)
+    top = np.sort(np.concatenate([top, np.flatnonzero(a == t)[: 2 * k - top.size]]))
+    want = np.sort(top[R[0][1] < k])
+    assert np.array_equal(idx[1].astype(np.int64), want)
+    assert np.array_equal(_bits(val[1]), _bits(m[want]))
+    assert np.all(e1[want] == 0)
+    rest = np.ones(n, bool)
+    rest[want] = False
+    assert np.array_equal(_bits(e1[rest]), _bits(m[rest]))
