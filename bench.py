@@ -13,6 +13,11 @@ subtracted in the next step's pass), "carry" (PSGD_FLAG_CARRY_ERROR_MEAN: the pl
 E'_w is written every step, and the next step's first pass reads only G plus the
 carried error mean) and "plain" (no cross-step state).  `value` is the --primary one.
 
+A second compressor is timed beside it ("rtopk" in the output): rTop-k with error
+feedback on the same shapes and W = 16, 1% of each tensor sent, drawn from its top 2%
+(psgd_rtopk_step: EF add, top-set selection, random subset from seeded ranks, sparse
+lists, new errors, dense mean update).
+
 Prints one JSON line:
   value          gradient GB/s = W * numel * 4 bytes / step time (whole job, one GPU)
   pct_hbm_peak   minimal HBM bytes of a step / step time / 8 TB/s
@@ -37,6 +42,9 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 METRIC = "PowerSGD step gradient GB/s (ResNet-18 shapes, r=2, W=16) & % HBM peak"
 KERNEL_SRC = os.path.join(ROOT, "distributed_sgd_gradient_ef_amd", "csrc", "kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_resnet18_r2_w16.json")
+RTOPK_SRC = os.path.join(ROOT, "distributed_sgd_gradient_ef_amd", "csrc", "rtopk.hip")
+RTOPK_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_rtopk_resnet18_w16.json")
+RTOPK_METRIC = "rTop-k step gradient GB/s (ResNet-18 shapes, 1% sent from the top 2%, W=16) & % HBM peak"
 
 
 def kernel_bytes(plan, dtype_bytes: int, variant: str) -> dict:
@@ -66,13 +74,32 @@ def kernel_bytes(plan, dtype_bytes: int, variant: str) -> dict:
     }
 
 
-def traffic_for(kernel: str):
+def rtopk_kernel_bytes(plan, dtype_bytes: int) -> dict:
+    """Algorithmic HBM bytes per launch of the streaming rTop-k kernels (the selection
+    kernels in between move a few bytes per segment or per candidate)."""
+    s = plan.sizes
+    W, n = s["n_workers"], s["numel"]
+    return {
+        # read G_w and E_w, write M_w on every worker
+        "rk_ef_hist": W * (dtype_bytes + 8) * n,
+        # read M_w, write one mask bit per entry on every worker
+        "rk_mark": W * 4 * n + W * n // 8,
+        # read the top mask and the ranks of the top set, write the kept mask
+        "rk_keep": W * n // 4 + W * 4 * s["top_total"],
+        # read the kept mask, write the list positions and the lists
+        "rk_emit": W * n // 4 + W * 8 * s["keep_total"],
+        # read every worker's kept mask, write U once
+        "rk_update": W * n // 8 + 4 * n,
+    }
+
+
+def traffic_for(kernel: str, traffic_file: str = TRAFFIC_FILE, source: str = KERNEL_SRC):
     """Measured HBM bytes per launch from committed rocprofv3 counter runs, if they
     were taken on the current kernel source; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file) as f:
             t = json.load(f)
-        with open(KERNEL_SRC, "rb") as f:
+        with open(source, "rb") as f:
             sha = hashlib.sha256(f.read()).hexdigest()
     except (OSError, ValueError):
         return None
@@ -117,8 +144,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline sample length")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["all", "carry", "plain", "deferred"], default="all",
-                    help="plan variants to time (profiling runs use one)")
+    ap.add_argument("--mode", choices=["all", "carry", "plain", "deferred", "rtopk"], default="all",
+                    help="plan variants to time (profiling runs use one); rtopk times only the rTop-k step")
     ap.add_argument("--primary", choices=["carry", "deferred", "plain"], default="deferred",
                     help="variant reported as `value` when several are timed")
     args = ap.parse_args()
@@ -128,6 +155,7 @@ def main() -> int:
               "one GPU's HBM, and no multi-GPU path is built. Use --gpus 1.", file=sys.stderr)
         return 2
 
+    import numpy as np
     import torch
 
     from distributed_sgd_gradient_ef_amd import psgd
@@ -215,6 +243,82 @@ def main() -> int:
     copy_gbs = 2 * cbytes * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
 
+    def measure_rtopk() -> dict:
+        wr = WL.workload("resnet18_rtopk")
+        tops, keeps = WL.rtopk_counts(wr)
+        plan = psgd.psgd_rtopk_plan_create(shapes, tops, keeps, W, psgd.PSGD_F32)
+        s = plan.sizes
+        ld = s["worker_stride"]
+        grads = torch.zeros((W, ld), dtype=torch.float32, device=dev)
+        errors = torch.zeros((W, ld), dtype=torch.float32, device=dev)
+        index = torch.zeros((W, s["keep_total"]), dtype=torch.int32, device=dev)
+        value = torch.zeros((W, s["keep_total"]), dtype=torch.float32, device=dev)
+        update = torch.zeros(ld, dtype=torch.float32, device=dev)
+        workspace = torch.empty(s["workspace_bytes"], dtype=torch.uint8, device=dev)
+        WL.device_grads(wr, 0, [(L.offset, L.rows, L.cols) for L in plan.layers], grads)
+        ranks_h = psgd.pack_rows(plan, [np.stack([WL.rtopk_ranks(wr, 0, w, li, tops[li]) for w in range(W)])
+                                        for li in range(len(shapes))], "top", np.uint32)
+        ranks = torch.from_numpy(ranks_h.view(np.int32)).to(dev)
+        stream = torch.cuda.current_stream(dev)
+
+        def step():
+            psgd.psgd_rtopk_step(plan, grads, errors, ranks, index, value, update, workspace, stream)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize(dev)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(args.steps):
+            step()
+        t1.record(stream)
+        torch.cuda.synchronize(dev)
+        ms = t0.elapsed_time(t1) / args.steps
+        psgd.psgd_rtopk_plan_set_timing(plan, True)
+        psgd.psgd_rtopk_plan_kernel_stats(plan, reset=True)
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize(dev)
+        stats = psgd.psgd_rtopk_plan_kernel_stats(plan, reset=True)
+        psgd.psgd_rtopk_plan_set_timing(plan, False)
+        kb = rtopk_kernel_bytes(plan, 4)
+        kernels = {}
+        for name, (n, tot) in stats.items():
+            us = 1e3 * tot / max(n, 1)
+            entry = {"mean_us": round(us, 2), "launches": n}
+            if name in kb:
+                entry["alg_bytes"] = kb[name]
+                entry["alg_GBps"] = round(kb[name] / (us * 1e-6) / 1e9, 1)
+            kernels[name] = entry
+        dom = max((k for k in kernels if k in kb), key=lambda k: kernels[k]["mean_us"])
+        dom_us = kernels[dom]["mean_us"]
+        achieved = kb[dom] / (dom_us * 1e-6) / 1e9
+        grad_bytes = W * s["numel"] * 4
+        del grads, errors, workspace
+        return {
+            "metric": RTOPK_METRIC,
+            "value": round(grad_bytes / (ms * 1e-3) / 1e9, 2),
+            "unit": "GB/s",
+            "ms_per_step": round(ms, 4),
+            "pct_hbm_peak": round(100.0 * s["model_bytes"] / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 2),
+            "model_bytes_per_step": s["model_bytes"],
+            "config": {"workload": "resnet18_cifar_shapes", "workers": W, "tensors": s["n_layers"],
+                       "keep_frac": wr.keep_frac, "top_factor": wr.top_factor, "keep_total": s["keep_total"],
+                       "top_total": s["top_total"], "grad_bytes_per_step": grad_bytes},
+            "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": traffic_for(dom, RTOPK_TRAFFIC_FILE, RTOPK_SRC),
+                         "alg_bytes_per_launch": kb[dom], "mean_us": dom_us},
+            "kernels": kernels,
+        }
+
+    if args.mode == "rtopk":
+        out = measure_rtopk()
+        out.update({"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+                    "scaling": "weak", "vs_baseline": None, "dtype": "f32", "stream_copy_GBps": round(copy_gbs, 1)})
+        print(json.dumps(out), flush=True)
+        return 0
+
     names = ["plain", "carry", "deferred"] if args.mode == "all" else [args.mode]
     results = {n: measure(n) for n in names}
     primary = args.primary if args.primary in results else names[0]
@@ -257,6 +361,8 @@ def main() -> int:
                            "pct_hbm_peak": round(r["pct"], 2),
                            "kernels_mean_us": {k: v["mean_us"] for k, v in r["kernels"].items()}}
                        for n, r in results.items() if n != primary}
+    if args.mode == "all":
+        out["rtopk"] = measure_rtopk()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)

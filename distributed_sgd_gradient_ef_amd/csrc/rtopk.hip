@@ -4,22 +4,27 @@
 // largest magnitude is sent, and what is not sent stays in the error memory.
 //
 // A segment is one tensor of one worker.  A tile is kTile consecutive elements of one
-// tensor (the last tile of a tensor may be shorter); the launches of the streaming
-// passes cover every tile of every worker at once (grid.x = tile, grid.y = worker).
-// Magnitudes are compared as the 31-bit key bits(|m|); within a segment the 63-bit
-// value key << 32 | ~index orders entries by magnitude, then by lower index, and is
-// unique, so "the r largest" is one set.
+// tensor (the last tile of a tensor may be shorter); the streaming launches cover every
+// tile of every worker at once (grid.x = tile, grid.y = worker).  Magnitudes compare as
+// the 31-bit key bits(|m|).  The top set of a segment is every entry with key above the
+// r-th largest key T, plus the lowest-index entries with key T that complete r; T is
+// found by a radix selection over the key in three digits (bits 30..20, 19..9, 8..0).
 //
-//   rk_zero       clear the level-1 histograms and the candidate counters
-//   rk_ef_hist    M = G + E, stored into E; per segment a histogram of key >> 20
-//                 (2048 bins in LDS per workgroup, flushed with atomics)
-//   rk_select     per segment: the bin b1 holding the r-th largest key, and how many
-//                 of that bin's entries still belong to the top set
+//   rk_zero       clear the three digit histograms
+//   rk_ef_hist    M = G + E, stored into E; per segment, a histogram of digit 1
+//                 (LDS per workgroup, flushed with atomics)
+//   rk_select     per segment: the digit-1 bin b1 holding T, and how many of its
+//                 entries belong to the top set
 //   rk_mark       re-read M: entries above b1 -> top mask (one bit per element); entries
-//                 in b1 -> candidate list (their 63-bit keys); per-tile mask counts
-//   rk_refine     per segment: radix selection among the candidates, 11 bits a level,
-//                 then the chosen candidates join the mask
-//   rk_scan_top   per segment: exclusive scan of the per-tile mask counts (slot bases)
+//                 in b1 -> the tile's candidate region (key bits 19..0 | tile offset),
+//                 and a histogram of their digit 2; per-tile counts
+//   rk_level3     per chunk of tiles: digit-2 bin b2 (recomputed from the histogram),
+//                 then a histogram of digit 3 of the candidates in b2
+//   rk_final      per chunk of tiles: T and the rule (keys >= a bound are in; when the
+//                 entries equal to T are only partly in, they are tie-marked), applied
+//                 to the candidates
+//   rk_scan_top   per segment: scans of the per-tile tie counts (the first ties in
+//                 index order are in) and of the per-tile top counts (slot bases)
 //   rk_keep       per tile: each top entry's slot (its position in index order) gives
 //                 its rank; rank < k -> kept mask; per-tile kept counts
 //   rk_scan_kept  per segment: exclusive scan of the kept counts; unused output slots
@@ -49,23 +54,23 @@
 namespace psgd {
 namespace rtk {
 
-constexpr int kTile = 4096;            // elements per tile
-constexpr int kTileThreads = 256;      // rk_ef_hist / rk_mark: 16 elements per thread
-constexpr int kWordThreads = kTile / 32;  // rk_keep / rk_emit: one thread per mask word
-constexpr int kDenseThreads = kTile / 4;    // rk_update: 4 elements per thread
-constexpr int kBins = 2048;            // 11-bit radix digits
-constexpr int kSegThreads = 1024;      // per-segment kernels
-constexpr int kLevel1Shift = 52;       // level-1 digit: bits 62..52 of the value key (key >> 20)
-constexpr int64_t kMinCandCap = 2048;  // candidate list capacity: max(this, numel / 16), at most numel
+constexpr int kTile = 4096;               // elements per tile
+constexpr int kLocalBits = 12;            // log2(kTile): offset of an entry inside its tile
+constexpr int kTileThreads = 256;         // rk_ef_hist / rk_mark: 16 elements per thread
+constexpr int kWordThreads = kTile / 32;  // rk_keep / rk_emit / rk_update: one thread per mask word
+constexpr int kSelThreads = 256;          // rk_select / rk_level3 / rk_final
+constexpr int kSegThreads = 1024;         // per-segment scans
+constexpr int kBins1 = 2048;              // digit 1: key bits 30..20
+constexpr int kBins2 = 2048;              // digit 2: key bits 19..9
+constexpr int kBins3 = 512;               // digit 3: key bits 8..0
+constexpr int kChunkTiles = 16;           // tiles per workgroup in rk_level3 / rk_final
 
 struct RkLayer {
-  int64_t offset;    // element offset in a worker slice
+  int64_t offset;  // element offset in a worker slice
   int64_t numel;
   int64_t top, keep;
   int64_t top_off, keep_off;
-  int64_t cand_off;  // offset of the candidate list in one worker's candidate area
-  int64_t cand_cap;
-  int32_t tile_off;  // first tile of the tensor
+  int32_t tile_off;  // first tile of the tensor in the tile table
   int32_t ntiles;
 };
 
@@ -77,19 +82,31 @@ struct RkTile {
   int32_t pad;
 };
 
-struct RkSeg {
-  uint32_t b1;         // level-1 bin of the r-th largest key
-  uint32_t need;       // entries of bin b1 that belong to the top set
-  uint32_t ncand;      // entries in bin b1
-  uint32_t from_list;  // 1: candidates were listed (ncand <= cap); 0: rescan the segment
-  uint32_t ntop;       // top-set size found (r)
-  uint32_t nkept;      // entries with rank < k
-  uint32_t pad0, pad1;
+struct RkChunk {
+  int32_t layer;
+  int32_t t0, t1;  // tiles [t0, t1) of the tensor
+  int32_t first;   // 1 for the tensor's first chunk (it records the segment's rule)
 };
 
-enum KernelId { kZero = 0, kEfHist, kSelect, kMark, kRefine, kScanTop, kKeep, kScanKept, kEmit, kUpdate, kNumK };
-const char* const kNames[kNumK] = {"rk_zero",     "rk_ef_hist", "rk_select",    "rk_mark", "rk_refine",
-                                   "rk_scan_top", "rk_keep",    "rk_scan_kept", "rk_emit", "rk_update"};
+struct RkSeg {
+  uint32_t b1;      // digit-1 bin holding T
+  uint32_t need1;   // entries of bin b1 in the top set
+  uint32_t count1;  // entries in bin b1
+  uint32_t pad0;
+  uint32_t sel_lo;   // every entry with key >= sel_lo is in the top set
+  uint32_t tie_key;  // partial: the first need_t entries (index order) with this key are in
+  uint32_t need_t;
+  uint32_t partial;
+  uint32_t ntop;   // top-set size found (r)
+  uint32_t nkept;  // entries with rank < k
+  uint32_t pad1, pad2;
+};
+
+enum KernelId {
+  kZero = 0, kEfHist, kSelect, kMark, kLevel3, kFinal, kScanTop, kKeep, kScanKept, kEmit, kUpdate, kNumK
+};
+const char* const kNames[kNumK] = {"rk_zero",  "rk_ef_hist",  "rk_select", "rk_mark",      "rk_level3", "rk_final",
+                                   "rk_scan_top", "rk_keep", "rk_scan_kept", "rk_emit", "rk_update"};
 
 }  // namespace rtk
 }  // namespace psgd
@@ -100,12 +117,15 @@ struct psgd_rtopk_plan {
   std::vector<psgd_rtopk_layer_info> info;
   std::vector<psgd::rtk::RkLayer> layers;
   std::vector<psgd::rtk::RkTile> tiles;
-  int64_t worker_stride = 0, numel = 0, top_total = 0, keep_total = 0, cand_total = 0;
+  std::vector<psgd::rtk::RkChunk> chunks;
+  int64_t worker_stride = 0, numel = 0, top_total = 0, keep_total = 0;
   int64_t n_seg = 0;
-  uint64_t ws_hist = 0, ws_candcnt = 0, ws_seg = 0, ws_cand = 0, ws_mask = 0, ws_kmask = 0, ws_kpos = 0;
-  uint64_t ws_tcnt = 0, ws_tbase = 0, ws_kcnt = 0, ws_kbase = 0, workspace_bytes = 0;
+  uint64_t ws_hist1 = 0, ws_hist2 = 0, ws_hist3 = 0, ws_seg = 0, ws_cand = 0, ws_ccnt = 0;
+  uint64_t ws_mask = 0, ws_tmask = 0, ws_kmask = 0, ws_kpos = 0;
+  uint64_t ws_tcnt = 0, ws_ttie = 0, ws_tiebase = 0, ws_tbase = 0, ws_kcnt = 0, ws_kbase = 0;
+  uint64_t workspace_bytes = 0;
   uint64_t message_bytes = 0, model_bytes = 0;
-  std::map<int, void*> dev;  // device copy of the layer and tile tables, per HIP device
+  std::map<int, void*> dev;  // device copy of the layer, tile and chunk tables, per HIP device
   bool timing = false;
   std::vector<psgd::PendingTiming> pending;
   std::vector<hipEvent_t> event_pool;
@@ -118,10 +138,6 @@ namespace {
 
 // ------------------------------------------------------------------ device helpers
 __device__ __forceinline__ uint32_t mag_key(float m) { return __float_as_uint(m) & 0x7fffffffu; }
-
-__device__ __forceinline__ uint64_t value_key(float m, uint32_t idx) {
-  return (uint64_t(mag_key(m)) << 32) | uint64_t(~idx);
-}
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
@@ -194,6 +210,74 @@ __device__ __forceinline__ uint32_t block_total(uint32_t v, uint32_t* lds) {
   return t;
 }
 
+struct Pick {
+  uint32_t bin;    // the bin holding the need-th largest entry
+  uint32_t above;  // entries in the bins above it
+  uint32_t count;  // entries in it
+};
+
+// Walk a histogram of NB bins from the top (kSelThreads threads, NB / kSelThreads bins
+// each) to the bin where the count reaches `need`.  Every thread must call it.
+template <int NB>
+__device__ Pick pick_bin(const uint32_t* __restrict__ h, uint32_t need, uint32_t* lds, uint32_t* sh) {
+  constexpr int PER = NB / kSelThreads;
+  if (threadIdx.x == 0) sh[0] = sh[1] = sh[2] = 0u;
+  const int hi = NB - PER * int(threadIdx.x);
+  uint32_t c[PER], tsum = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    c[j] = h[hi - 1 - j];
+    tsum += c[j];
+  }
+  const uint32_t incl = block_incl_scan(tsum, lds);
+  const uint32_t above = incl - tsum;
+  if (above < need && need <= incl) {
+    uint32_t acc = above;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (acc + c[j] >= need) {
+        sh[0] = uint32_t(hi - 1 - j);
+        sh[1] = acc;
+        sh[2] = c[j];
+        break;
+      }
+      acc += c[j];
+    }
+  }
+  __syncthreads();
+  const Pick p{sh[0], sh[1], sh[2]};
+  __syncthreads();
+  return p;
+}
+
+// The selection rule of a segment from its three histograms: keys >= lo are in; with
+// `partial`, the first need_t entries (index order) with key tie are in as well.
+struct Rule {
+  uint32_t lo, tie, need_t, partial;
+};
+
+__device__ Rule segment_rule(const RkSeg& st, const uint32_t* h2, const uint32_t* h3, uint32_t* lds, uint32_t* sh) {
+  Rule r{st.b1 << 20, 0u, 0u, 0u};
+  if (st.need1 == st.count1) return r;
+  const Pick p2 = pick_bin<kBins2>(h2, st.need1, lds, sh);
+  const uint32_t need2 = st.need1 - p2.above;
+  const uint32_t k2 = (st.b1 << 20) | (p2.bin << 9);
+  r.lo = k2;
+  if (need2 == p2.count) return r;
+  const Pick p3 = pick_bin<kBins3>(h3, need2, lds, sh);
+  const uint32_t need3 = need2 - p3.above;
+  const uint32_t t = k2 | p3.bin;
+  if (need3 == p3.count) {
+    r.lo = t;
+  } else {
+    r.lo = t + 1u;
+    r.tie = t;
+    r.need_t = need3;
+    r.partial = 1u;
+  }
+  return r;
+}
+
 // ------------------------------------------------------------------ kernels
 __global__ __launch_bounds__(256) void rk_zero(uint32_t* __restrict__ p, int64_t n) {
   for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) p[i] = 0u;
@@ -201,10 +285,10 @@ __global__ __launch_bounds__(256) void rk_zero(uint32_t* __restrict__ p, int64_t
 
 template <typename GT>
 __global__ __launch_bounds__(kTileThreads) void rk_ef_hist(const RkTile* __restrict__ tiles, const GT* __restrict__ G,
-                                                           float* __restrict__ E, uint32_t* __restrict__ hist,
+                                                           float* __restrict__ E, uint32_t* __restrict__ hist1,
                                                            int64_t stride, int n_layers) {
-  __shared__ uint32_t h[kBins];
-  for (int b = threadIdx.x; b < kBins; b += kTileThreads) h[b] = 0u;
+  __shared__ uint32_t h[kBins1];
+  for (int b = threadIdx.x; b < kBins1; b += kTileThreads) h[b] = 0u;
   __syncthreads();
   const RkTile t = tiles[blockIdx.x];
   const int w = blockIdx.y;
@@ -229,69 +313,53 @@ __global__ __launch_bounds__(kTileThreads) void rk_ef_hist(const RkTile* __restr
     }
   }
   __syncthreads();
-  uint32_t* gh = hist + (int64_t(w) * n_layers + t.layer) * kBins;
-  for (int b = threadIdx.x; b < kBins; b += kTileThreads) {
+  uint32_t* gh = hist1 + (int64_t(w) * n_layers + t.layer) * kBins1;
+  for (int b = threadIdx.x; b < kBins1; b += kTileThreads) {
     const uint32_t c = h[b];
     if (c) atomicAdd(gh + b, c);
   }
 }
 
-// One workgroup per segment; thread t owns the 8 bins below kBins - 8t.
-__global__ __launch_bounds__(256) void rk_select(const RkLayer* __restrict__ layers, const uint32_t* __restrict__ hist,
-                                                 RkSeg* __restrict__ seg, int n_layers) {
-  __shared__ uint32_t lds[16];
+__global__ __launch_bounds__(kSelThreads) void rk_select(const RkLayer* __restrict__ layers,
+                                                         const uint32_t* __restrict__ hist1, RkSeg* __restrict__ seg,
+                                                         int n_layers) {
+  __shared__ uint32_t lds[16], sh[3];
   const int l = blockIdx.x, w = blockIdx.y;
   const int64_t s = int64_t(w) * n_layers + l;
-  const RkLayer L = layers[l];
-  const uint32_t* h = hist + s * kBins;
-  const int hi = kBins - 8 * int(threadIdx.x);
-  uint32_t c[8], tsum = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    c[j] = h[hi - 1 - j];
-    tsum += c[j];
-  }
-  const uint32_t incl = block_incl_scan(tsum, lds);
-  const uint32_t above = incl - tsum;
-  const uint32_t r = uint32_t(L.top);
-  if (above < r && r <= incl) {
-    uint32_t acc = above;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (acc + c[j] >= r) {
-        RkSeg st{};
-        st.b1 = uint32_t(hi - 1 - j);
-        st.need = r - acc;
-        st.ncand = c[j];
-        st.from_list = int64_t(c[j]) <= L.cand_cap ? 1u : 0u;
-        seg[s] = st;
-        break;
-      }
-      acc += c[j];
-    }
+  const uint32_t r = uint32_t(layers[l].top);
+  const Pick p = pick_bin<kBins1>(hist1 + s * kBins1, r, lds, sh);
+  if (threadIdx.x == 0) {
+    RkSeg st{};
+    st.b1 = p.bin;
+    st.need1 = r - p.above;
+    st.count1 = p.count;
+    seg[s] = st;
   }
 }
 
 // Tile of 16 groups of 256 elements; wave v handles groups v, v+4, v+8, v+12; lane l
 // holds elements 4l..4l+3 of its group, so mask word q of a group (32 elements) comes
-// from lanes 8q..8q+7 and is assembled by lane q from four ballots.
+// from lanes 8q..8q+7 and is assembled by lane q from four ballots.  Candidates (digit 1
+// equal to b1) go to the tile's own region of `cand` (same layout as E) as
+// (key bits 19..0) << 12 | offset in the tile.
 __global__ __launch_bounds__(kTileThreads) void rk_mark(const RkTile* __restrict__ tiles,
-                                                        const RkLayer* __restrict__ layers,
                                                         const float* __restrict__ E, const RkSeg* __restrict__ seg,
-                                                        uint32_t* __restrict__ mask, uint32_t* __restrict__ tcnt,
-                                                        uint64_t* __restrict__ cand, uint32_t* __restrict__ candcnt,
-                                                        int64_t stride, int64_t cand_stride, int n_layers,
+                                                        uint32_t* __restrict__ hist2, uint32_t* __restrict__ mask,
+                                                        uint32_t* __restrict__ tmask, uint32_t* __restrict__ tcnt,
+                                                        uint32_t* __restrict__ ttie, uint32_t* __restrict__ cand,
+                                                        uint32_t* __restrict__ ccnt, int64_t stride, int n_layers,
                                                         int ntiles) {
+  __shared__ uint32_t h2[kBins2];
   __shared__ uint32_t lds[16];
-  __shared__ uint32_t s_base;
+  for (int b = threadIdx.x; b < kBins2; b += kTileThreads) h2[b] = 0u;
   const RkTile t = tiles[blockIdx.x];
   const int w = blockIdx.y;
   const int64_t s = int64_t(w) * n_layers + t.layer;
   const uint32_t b1 = seg[s].b1;
-  const bool listing = seg[s].from_list != 0u;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t base = int64_t(w) * stride + t.begin;
   const int64_t wbase = base >> 5;  // begin and stride are multiples of 64
+  __syncthreads();
   float m[4][4];
   uint32_t nsure = 0, ncand = 0;
 #pragma unroll
@@ -308,9 +376,12 @@ __global__ __launch_bounds__(kTileThreads) void rk_mark(const RkTile* __restrict
     uint64_t B[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t bin = mag_key(m[i][j]) >> 20;
-      B[j] = __ballot(j < valid && bin > b1);
-      ncand += (j < valid && bin == b1) ? 1u : 0u;
+      const uint32_t key = mag_key(m[i][j]);
+      B[j] = __ballot(j < valid && (key >> 20) > b1);
+      if (j < valid && (key >> 20) == b1) {
+        atomicAdd(&h2[(key >> 9) & 0x7ffu], 1u);
+        ++ncand;
+      }
     }
     if (lane < 8 && (g * 256 + lane * 32) < t.len) {
       const int sh = lane * 8;
@@ -318,120 +389,171 @@ __global__ __launch_bounds__(kTileThreads) void rk_mark(const RkTile* __restrict
                             (spread4(uint32_t(B[2] >> sh) & 0xffu) << 2) |
                             (spread4(uint32_t(B[3] >> sh) & 0xffu) << 3);
       mask[wbase + g * 8 + lane] = word;
+      tmask[wbase + g * 8 + lane] = 0u;
       nsure += __popc(word);
     }
   }
   const uint32_t tot = block_total(nsure, lds);
-  if (threadIdx.x == 0) tcnt[int64_t(w) * ntiles + blockIdx.x] = tot;
-  if (!listing) return;  // uniform across the block
   const uint32_t incl = block_incl_scan(ncand, lds);
-  if (threadIdx.x == kTileThreads - 1) s_base = incl > 0 ? atomicAdd(candcnt + s, incl) : 0u;
-  __syncthreads();
-  if (ncand == 0) return;
-  const RkLayer L = layers[t.layer];
-  uint64_t* out = cand + int64_t(w) * cand_stride + L.cand_off;
-  uint32_t pos = s_base + incl - ncand;
+  const int64_t trow = int64_t(w) * ntiles + blockIdx.x;
+  if (threadIdx.x == 0) {
+    tcnt[trow] = tot;
+    ttie[trow] = 0u;
+  }
+  if (threadIdx.x == kTileThreads - 1) ccnt[trow] = incl;
+  if (ncand > 0) {
+    uint32_t* out = cand + base;
+    uint32_t pos = incl - ncand;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int g = i * 4 + wv;
-    const int e = g * 256 + lane * 4;
+    for (int i = 0; i < 4; ++i) {
+      const int e = (i * 4 + wv) * 256 + lane * 4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (e + j < t.len && (mag_key(m[i][j]) >> 20) == b1) {
-        if (int64_t(pos) < L.cand_cap) out[pos] = value_key(m[i][j], uint32_t(t.chunk * kTile + e + j));
-        ++pos;
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t key = mag_key(m[i][j]);
+        if (e + j < t.len && (key >> 20) == b1) out[pos++] = ((key & 0xfffffu) << kLocalBits) | uint32_t(e + j);
       }
+    }
+  }
+  uint32_t* gh = hist2 + s * kBins2;
+  for (int b = threadIdx.x; b < kBins2; b += kTileThreads) {
+    const uint32_t c = h2[b];
+    if (c) atomicAdd(gh + b, c);
+  }
+}
+
+// Digit 3 over the candidates whose digit 2 is b2, for segments not settled by then.
+__global__ __launch_bounds__(kSelThreads) void rk_level3(const RkChunk* __restrict__ chunks,
+                                                         const RkTile* __restrict__ tiles,
+                                                         const RkLayer* __restrict__ layers,
+                                                         const RkSeg* __restrict__ seg,
+                                                         const uint32_t* __restrict__ hist2,
+                                                         uint32_t* __restrict__ hist3, const uint32_t* __restrict__ cand,
+                                                         const uint32_t* __restrict__ ccnt, int64_t stride,
+                                                         int n_layers, int ntiles) {
+  __shared__ uint32_t h3[kBins3];
+  __shared__ uint32_t lds[16], sh[3];
+  const RkChunk ch = chunks[blockIdx.x];
+  const int w = blockIdx.y;
+  const int64_t s = int64_t(w) * n_layers + ch.layer;
+  const RkSeg st = seg[s];
+  if (st.need1 == st.count1) return;  // uniform: settled by digit 1
+  const Pick p2 = pick_bin<kBins2>(hist2 + s * kBins2, st.need1, lds, sh);
+  if (st.need1 - p2.above == p2.count) return;  // uniform: settled by digit 2
+  for (int b = threadIdx.x; b < kBins3; b += kSelThreads) h3[b] = 0u;
+  __syncthreads();
+  const RkLayer L = layers[ch.layer];
+  for (int tt = ch.t0; tt < ch.t1; ++tt) {
+    const int ti = L.tile_off + tt;
+    const uint32_t n = ccnt[int64_t(w) * ntiles + ti];
+    const uint32_t* c = cand + int64_t(w) * stride + tiles[ti].begin;
+    for (uint32_t i = threadIdx.x; i < n; i += kSelThreads) {
+      const uint32_t e = c[i];
+      if ((e >> 21) == p2.bin) atomicAdd(&h3[(e >> kLocalBits) & 0x1ffu], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t* gh = hist3 + s * kBins3;
+  for (int b = threadIdx.x; b < kBins3; b += kSelThreads) {
+    const uint32_t c = h3[b];
+    if (c) atomicAdd(gh + b, c);
+  }
+}
+
+// Apply the segment's rule to the candidates of a chunk of tiles: top-mask bits and
+// tile counts for those in, tie-mask bits and tile tie counts for the partial ties.
+__global__ __launch_bounds__(kSelThreads) void rk_final(const RkChunk* __restrict__ chunks,
+                                                        const RkTile* __restrict__ tiles,
+                                                        const RkLayer* __restrict__ layers, RkSeg* __restrict__ seg,
+                                                        const uint32_t* __restrict__ hist2,
+                                                        const uint32_t* __restrict__ hist3,
+                                                        const uint32_t* __restrict__ cand,
+                                                        const uint32_t* __restrict__ ccnt, uint32_t* __restrict__ mask,
+                                                        uint32_t* __restrict__ tmask, uint32_t* __restrict__ tcnt,
+                                                        uint32_t* __restrict__ ttie, int64_t stride, int n_layers,
+                                                        int ntiles) {
+  __shared__ uint32_t lds[16], sh[3];
+  const RkChunk ch = chunks[blockIdx.x];
+  const int w = blockIdx.y;
+  const int64_t s = int64_t(w) * n_layers + ch.layer;
+  const RkSeg st = seg[s];
+  const Rule rule = segment_rule(st, hist2 + s * kBins2, hist3 + s * kBins3, lds, sh);
+  if (ch.first && threadIdx.x == 0) {
+    seg[s].sel_lo = rule.lo;
+    seg[s].tie_key = rule.tie;
+    seg[s].need_t = rule.need_t;
+    seg[s].partial = rule.partial;
+  }
+  const RkLayer L = layers[ch.layer];
+  const uint32_t hi = st.b1 << 20;
+  for (int tt = ch.t0; tt < ch.t1; ++tt) {
+    const int ti = L.tile_off + tt;
+    const int64_t trow = int64_t(w) * ntiles + ti;
+    const uint32_t n = ccnt[trow];
+    const int64_t ebase = int64_t(w) * stride + tiles[ti].begin;
+    const uint32_t* c = cand + ebase;
+    uint32_t nin = 0, ntie = 0;
+    for (uint32_t i = threadIdx.x; i < n; i += kSelThreads) {
+      const uint32_t e = c[i];
+      const uint32_t key = hi | (e >> kLocalBits);
+      const int64_t el = ebase + (e & uint32_t(kTile - 1));
+      if (key >= rule.lo) {
+        atomicOr(mask + (el >> 5), 1u << (el & 31));
+        ++nin;
+      } else if (rule.partial && key == rule.tie) {
+        atomicOr(tmask + (el >> 5), 1u << (el & 31));
+        ++ntie;
+      }
+    }
+    const uint32_t a = block_total(nin, lds);
+    const uint32_t b = block_total(ntie, lds);
+    if (threadIdx.x == 0) {
+      tcnt[trow] += a;
+      ttie[trow] = b;
     }
   }
 }
 
-// One workgroup of kSegThreads per segment.  Items are the candidate list, or every
-// entry of the segment when the list would have overflowed (filtered to bin b1).
-__global__ __launch_bounds__(kSegThreads) void rk_refine(const RkLayer* __restrict__ layers,
-                                                         const float* __restrict__ E, const RkSeg* __restrict__ seg,
-                                                         const uint64_t* __restrict__ cand,
-                                                         const uint32_t* __restrict__ candcnt,
-                                                         uint32_t* __restrict__ mask, uint32_t* __restrict__ tcnt,
-                                                         int64_t stride, int64_t cand_stride, int n_layers,
-                                                         int ntiles) {
-  __shared__ uint32_t h[kBins];
+// Per segment: the first need_t tie entries in index order join the top set, so each
+// tile takes min(its ties, what is left); then exclusive scans give every tile its
+// first tie rank and its first slot.
+__global__ __launch_bounds__(kSegThreads) void rk_scan_top(const RkLayer* __restrict__ layers,
+                                                           const uint32_t* __restrict__ tcnt,
+                                                           const uint32_t* __restrict__ ttie,
+                                                           uint32_t* __restrict__ tbase,
+                                                           uint32_t* __restrict__ tiebase, RkSeg* __restrict__ seg,
+                                                           int n_layers, int ntiles) {
   __shared__ uint32_t lds[16];
-  __shared__ uint32_t s_b, s_above, s_count;
   const int l = blockIdx.x, w = blockIdx.y;
   const int64_t s = int64_t(w) * n_layers + l;
   const RkLayer L = layers[l];
-  const RkSeg st = seg[s];
-  const bool listing = st.from_list != 0u;
-  const uint64_t* list = cand + int64_t(w) * cand_stride + L.cand_off;
-  const float* M = E + int64_t(w) * stride + L.offset;
-  const int64_t n_items = listing ? min(int64_t(candcnt[s]), L.cand_cap) : L.numel;
-  auto item = [&](int64_t i) -> uint64_t { return listing ? list[i] : value_key(M[i], uint32_t(i)); };
-
-  const uint64_t b1 = st.b1;
-  uint64_t prefix = b1;
-  uint32_t need = st.need;
-  uint64_t thr = b1 << kLevel1Shift;  // every entry of bin b1
-  if (need < st.ncand) {
-    const int shs[5] = {41, 30, 19, 8, 0};
-    const int wbs[5] = {11, 11, 11, 11, 8};
-    for (int lvl = 0; lvl < 5; ++lvl) {
-      const int sh = shs[lvl], wb = wbs[lvl];
-      const int nb = 1 << wb;
-      for (int b = threadIdx.x; b < nb; b += kSegThreads) h[b] = 0u;
-      __syncthreads();
-      for (int64_t i = threadIdx.x; i < n_items; i += kSegThreads) {
-        const uint64_t ck = item(i);
-        if ((ck >> (sh + wb)) == prefix) atomicAdd(&h[uint32_t(ck >> sh) & uint32_t(nb - 1)], 1u);
-      }
-      __syncthreads();
-      // thread t owns bins nb-1-2t and nb-2-2t (from the top)
-      const int hb = nb - 1 - 2 * int(threadIdx.x);
-      const uint32_t c0 = hb >= 0 ? h[hb] : 0u;
-      const uint32_t c1 = hb >= 1 ? h[hb - 1] : 0u;
-      const uint32_t incl = block_incl_scan(c0 + c1, lds);
-      const uint32_t above = incl - c0 - c1;
-      if (above < need && need <= incl) {
-        if (above + c0 >= need) {
-          s_b = uint32_t(hb);
-          s_above = above;
-          s_count = c0;
-        } else {
-          s_b = uint32_t(hb - 1);
-          s_above = above + c0;
-          s_count = c1;
-        }
-      }
-      __syncthreads();
-      prefix = (prefix << wb) | uint64_t(s_b);
-      need -= s_above;
-      const uint32_t cnt = s_count;
-      __syncthreads();
-      if (cnt == need) {  // every entry of the chosen bin belongs to the top set
-        thr = prefix << sh;
-        break;
-      }
+  const uint32_t need_t = seg[s].partial ? seg[s].need_t : 0u;
+  const int64_t row = int64_t(w) * ntiles + L.tile_off;
+  uint32_t run_tie = 0, run_top = 0;
+  for (int c0 = 0; c0 < L.ntiles; c0 += kSegThreads) {
+    const int i = c0 + int(threadIdx.x);
+    const bool ok = i < L.ntiles;
+    const uint32_t vt = ok ? ttie[row + i] : 0u;
+    const uint32_t tb = run_tie + block_incl_scan(vt, lds) - vt;
+    const uint32_t take = tb >= need_t ? 0u : min(vt, need_t - tb);
+    const uint32_t v = (ok ? tcnt[row + i] : 0u) + take;
+    const uint32_t incl = block_incl_scan(v, lds);
+    if (ok) {
+      tbase[row + i] = run_top + incl - v;
+      tiebase[row + i] = tb;
     }
+    run_tie += block_total(vt, lds);
+    run_top += block_total(v, lds);
   }
-  uint32_t* mseg = mask + ((int64_t(w) * stride + L.offset) >> 5);
-  uint32_t* tc = tcnt + int64_t(w) * ntiles + L.tile_off;
-  for (int64_t i = threadIdx.x; i < n_items; i += kSegThreads) {
-    const uint64_t ck = item(i);
-    if ((ck >> kLevel1Shift) == b1 && ck >= thr) {
-      const uint32_t idx = ~uint32_t(ck);
-      atomicOr(mseg + (idx >> 5), 1u << (idx & 31u));
-      atomicAdd(tc + idx / kTile, 1u);
-    }
-  }
+  if (threadIdx.x == 0) seg[s].ntop = run_top;
 }
 
-// Exclusive scan over a segment's per-tile counts; the total goes to *total_out and,
-// when `pad` is set, output slots [min(total, k), k) get index -1, value 0.
-__global__ __launch_bounds__(kSegThreads) void rk_scan_tiles(const RkLayer* __restrict__ layers,
-                                                             const uint32_t* __restrict__ cnt,
-                                                             uint32_t* __restrict__ basev, RkSeg* __restrict__ seg,
-                                                             int32_t* __restrict__ index, float* __restrict__ value,
-                                                             int64_t keep_total, int n_layers, int ntiles,
-                                                             int kept_pass) {
+// Exclusive scan of a segment's per-tile kept counts; output slots [min(total, k), k)
+// get index -1, value 0.
+__global__ __launch_bounds__(kSegThreads) void rk_scan_kept(const RkLayer* __restrict__ layers,
+                                                            const uint32_t* __restrict__ kcnt,
+                                                            uint32_t* __restrict__ kbase, RkSeg* __restrict__ seg,
+                                                            int32_t* __restrict__ index, float* __restrict__ value,
+                                                            int64_t keep_total, int n_layers, int ntiles) {
   __shared__ uint32_t lds[16];
   const int l = blockIdx.x, w = blockIdx.y;
   const int64_t s = int64_t(w) * n_layers + l;
@@ -440,14 +562,10 @@ __global__ __launch_bounds__(kSegThreads) void rk_scan_tiles(const RkLayer* __re
   uint32_t running = 0;
   for (int c0 = 0; c0 < L.ntiles; c0 += kSegThreads) {
     const int i = c0 + int(threadIdx.x);
-    const uint32_t v = i < L.ntiles ? cnt[row + i] : 0u;
+    const uint32_t v = i < L.ntiles ? kcnt[row + i] : 0u;
     const uint32_t incl = block_incl_scan(v, lds);
-    if (i < L.ntiles) basev[row + i] = running + incl - v;
+    if (i < L.ntiles) kbase[row + i] = running + incl - v;
     running += block_total(v, lds);
-  }
-  if (!kept_pass) {
-    if (threadIdx.x == 0) seg[s].ntop = running;
-    return;
   }
   if (threadIdx.x == 0) seg[s].nkept = running;
   int32_t* ix = index + int64_t(w) * keep_total + L.keep_off;
@@ -458,25 +576,38 @@ __global__ __launch_bounds__(kSegThreads) void rk_scan_tiles(const RkLayer* __re
   }
 }
 
-// One thread per mask word of a tile: top entries in index order get consecutive slots
-// from the tile's base; those whose rank is below k are kept.
+// One thread per mask word of a tile: the top set's words (mask, plus the tie entries
+// whose tie rank is below need_t) in index order get consecutive slots from the tile's
+// base; those whose rank is below k are kept.
 __global__ __launch_bounds__(kWordThreads) void rk_keep(const RkTile* __restrict__ tiles,
                                                         const RkLayer* __restrict__ layers,
+                                                        const RkSeg* __restrict__ seg,
                                                         const uint32_t* __restrict__ mask,
+                                                        const uint32_t* __restrict__ tmask,
                                                         const uint32_t* __restrict__ tbase,
+                                                        const uint32_t* __restrict__ tiebase,
                                                         const uint32_t* __restrict__ ranks,
                                                         uint32_t* __restrict__ kmask, uint32_t* __restrict__ kcnt,
-                                                        int64_t stride, int64_t top_total, int ntiles) {
+                                                        int64_t stride, int64_t top_total, int n_layers, int ntiles) {
   __shared__ uint32_t lds[16];
   const RkTile t = tiles[blockIdx.x];
   const int w = blockIdx.y;
   const RkLayer L = layers[t.layer];
+  const int64_t s = int64_t(w) * n_layers + t.layer;
+  const uint32_t need_t = seg[s].partial ? seg[s].need_t : 0u;
   const int nwords = (t.len + 31) >> 5;
   const int q = threadIdx.x;
   const int64_t wi = ((int64_t(w) * stride + t.begin) >> 5) + q;
-  const uint32_t word = q < nwords ? mask[wi] : 0u;
+  const int64_t trow = int64_t(w) * ntiles + blockIdx.x;
+  uint32_t word = q < nwords ? mask[wi] : 0u;
+  const uint32_t tw = q < nwords ? tmask[wi] : 0u;
+  uint32_t tr = tiebase[trow] + block_incl_scan(__popc(tw), lds) - __popc(tw);
+  for (uint32_t bits = tw; bits != 0u; bits &= bits - 1u) {
+    if (tr < need_t) word |= 1u << __builtin_ctz(bits);
+    ++tr;
+  }
   const uint32_t c = __popc(word);
-  uint32_t slot = tbase[int64_t(w) * ntiles + blockIdx.x] + block_incl_scan(c, lds) - c;
+  uint32_t slot = tbase[trow] + block_incl_scan(c, lds) - c;
   const uint32_t* rk = ranks + int64_t(w) * top_total + L.top_off;
   uint32_t kept = 0;
   for (uint32_t bits = word; bits != 0u; bits &= bits - 1u) {
@@ -486,7 +617,7 @@ __global__ __launch_bounds__(kWordThreads) void rk_keep(const RkTile* __restrict
   }
   if (q < nwords) kmask[wi] = kept;
   const uint32_t tot = block_total(__popc(kept), lds);
-  if (threadIdx.x == 0) kcnt[int64_t(w) * ntiles + blockIdx.x] = tot;
+  if (threadIdx.x == 0) kcnt[trow] = tot;
 }
 
 __global__ __launch_bounds__(kWordThreads) void rk_emit(const RkTile* __restrict__ tiles,
@@ -525,49 +656,37 @@ __global__ __launch_bounds__(kWordThreads) void rk_emit(const RkTile* __restrict
   kpos[wi] = first;
 }
 
-// Dense update: lane handles 4 elements; for each worker in order, the sent entries
-// among them are read from the worker's value list (position = the word's first list
-// position + the sent bits below).
-__global__ __launch_bounds__(kDenseThreads) void rk_update(const RkTile* __restrict__ tiles,
-                                                         const RkLayer* __restrict__ layers,
-                                                         const uint32_t* __restrict__ kmask,
-                                                         const uint32_t* __restrict__ kpos,
-                                                         const float* __restrict__ value, float* __restrict__ update,
-                                                         int W, int64_t stride, int64_t keep_total, float inv_w) {
+// Dense update, one thread per mask word: for each worker in order, the word's sent
+// entries are read from the worker's value list (position = the word's first list
+// position + the sent bits below) and added in LDS; the tile is then written with
+// coalesced stores.
+__global__ __launch_bounds__(kWordThreads) void rk_update(const RkTile* __restrict__ tiles,
+                                                          const RkLayer* __restrict__ layers,
+                                                          const uint32_t* __restrict__ kmask,
+                                                          const uint32_t* __restrict__ kpos,
+                                                          const float* __restrict__ value, float* __restrict__ update,
+                                                          int W, int64_t stride, int64_t keep_total, float inv_w) {
+  __shared__ float acc[kWordThreads][33];
   const RkTile t = tiles[blockIdx.x];
-  const int e = int(threadIdx.x) * 4;
-  if (e >= t.len) return;
   const RkLayer L = layers[t.layer];
-  const int valid = min(4, t.len - e);
-  const int64_t wi = (t.begin + e) >> 5;
-  const int sh = e & 31;
-  const int64_t wstride = stride >> 5;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int w = 0; w < W; ++w) {
-    const uint32_t kw = kmask[int64_t(w) * wstride + wi];
-    uint32_t nib = (kw >> sh) & 0xfu;
-    if (nib == 0u) continue;
-    uint32_t pos = kpos[int64_t(w) * wstride + wi] + __popc(kw & ((1u << sh) - 1u));
-    const float* vx = value + int64_t(w) * keep_total + L.keep_off;
+  const int nwords = (t.len + 31) >> 5;
+  const int q = threadIdx.x;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if ((nib >> j) & 1u) {
-        acc[j] += vx[pos];
-        ++pos;
-      }
+  for (int j = 0; j < 32; ++j) acc[q][j] = 0.f;
+  if (q < nwords) {
+    const int64_t wi = (t.begin >> 5) + q;
+    const int64_t wstride = stride >> 5;
+    for (int w = 0; w < W; ++w) {
+      const uint32_t kw = kmask[int64_t(w) * wstride + wi];
+      if (kw == 0u) continue;
+      uint32_t pos = kpos[int64_t(w) * wstride + wi];
+      const float* vx = value + int64_t(w) * keep_total + L.keep_off;
+      for (uint32_t bits = kw; bits != 0u; bits &= bits - 1u) acc[q][__builtin_ctz(bits)] += vx[pos++];
     }
   }
-  float* u = update + t.begin + e;
-  if (valid == 4) {
-    v4f o;
-    o.x = acc[0] * inv_w;
-    o.y = acc[1] * inv_w;
-    o.z = acc[2] * inv_w;
-    o.w = acc[3] * inv_w;
-    store_nt4(u, o);
-  } else {
-    for (int j = 0; j < valid; ++j) u[j] = acc[j] * inv_w;
-  }
+  __syncthreads();
+  float* u = update + t.begin;
+  for (int e = q; e < t.len; e += kWordThreads) u[e] = acc[e >> 5][e & 31] * inv_w;
 }
 
 // ------------------------------------------------------------------ host helpers
@@ -582,21 +701,31 @@ psgd_status hip_fail(const char* what, hipError_t e) {
 
 uint64_t a256(uint64_t x) { return (x + 255) / 256 * 256; }
 
-psgd_status device_tables(psgd_rtopk_plan* plan, RkLayer** layers, RkTile** tiles) {
+struct DevTables {
+  RkLayer* layers;
+  RkTile* tiles;
+  RkChunk* chunks;
+};
+
+psgd_status device_tables(psgd_rtopk_plan* plan, DevTables* out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail("hipGetDevice", e);
   const uint64_t bl = a256(plan->layers.size() * sizeof(RkLayer) + 1);
+  const uint64_t bt = a256(plan->tiles.size() * sizeof(RkTile) + 1);
+  const uint64_t bc = a256(plan->chunks.size() * sizeof(RkChunk) + 1);
   auto it = plan->dev.find(dev);
   if (it == plan->dev.end()) {
-    const uint64_t bt = plan->tiles.size() * sizeof(RkTile);
     void* base = nullptr;
-    e = hipMalloc(&base, bl + bt + 256);
+    e = hipMalloc(&base, bl + bt + bc);
     if (e != hipSuccess) return fail(PSGD_ERR_NO_MEMORY, std::string("hipMalloc of the plan's device tables: ") +
                                                              hipGetErrorString(e));
     char* b = static_cast<char*>(base);
     e = hipMemcpy(b, plan->layers.data(), plan->layers.size() * sizeof(RkLayer), hipMemcpyHostToDevice);
-    if (e == hipSuccess && bt > 0) e = hipMemcpy(b + bl, plan->tiles.data(), bt, hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+      e = hipMemcpy(b + bl, plan->tiles.data(), plan->tiles.size() * sizeof(RkTile), hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+      e = hipMemcpy(b + bl + bt, plan->chunks.data(), plan->chunks.size() * sizeof(RkChunk), hipMemcpyHostToDevice);
     if (e != hipSuccess) {
       (void)hipFree(base);
       return hip_fail("hipMemcpy of the plan's device tables", e);
@@ -604,8 +733,9 @@ psgd_status device_tables(psgd_rtopk_plan* plan, RkLayer** layers, RkTile** tile
     it = plan->dev.emplace(dev, base).first;
   }
   char* b = static_cast<char*>(it->second);
-  *layers = reinterpret_cast<RkLayer*>(b);
-  *tiles = reinterpret_cast<RkTile*>(b + bl);
+  out->layers = reinterpret_cast<RkLayer*>(b);
+  out->tiles = reinterpret_cast<RkTile*>(b + bl);
+  out->chunks = reinterpret_cast<RkChunk*>(b + bl + bt);
   return PSGD_OK;
 }
 
@@ -709,8 +839,6 @@ extern "C" psgd_status psgd_rtopk_plan_create(const psgd_layer* layers, int32_t 
       L.keep = keep[i];
       L.top_off = plan->top_total;
       L.keep_off = plan->keep_total;
-      L.cand_cap = std::min(numel, std::max(kMinCandCap, (numel + 15) / 16));
-      L.cand_off = plan->cand_total;
       L.ntiles = int32_t((numel + kTile - 1) / kTile);
       L.tile_off = int32_t(tile_count);
       for (int32_t c = 0; c < L.ntiles; ++c) {
@@ -721,12 +849,13 @@ extern "C" psgd_status psgd_rtopk_plan_create(const psgd_layer* layers, int32_t 
         t.chunk = c;
         plan->tiles.push_back(t);
       }
+      for (int32_t c = 0; c < L.ntiles; c += kChunkTiles)
+        plan->chunks.push_back(RkChunk{i, c, std::min(L.ntiles, c + kChunkTiles), c == 0 ? 1 : 0});
       tile_count += L.ntiles;
       if (tile_count > int64_t(0x7fffffff)) {
         delete plan;
         return fail(PSGD_ERR_INVALID_ARG, "psgd_rtopk_plan_create: too many tiles");
       }
-      plan->cand_total += L.cand_cap;
       plan->top_total += top[i];
       plan->keep_total += keep[i];
       plan->numel += numel;
@@ -740,28 +869,28 @@ extern "C" psgd_status psgd_rtopk_plan_create(const psgd_layer* layers, int32_t 
     const uint64_t ntiles = plan->tiles.size();
     const uint64_t words = uint64_t(plan->worker_stride / 32);
     uint64_t ws = 0;
-    plan->ws_hist = ws;  // histograms and candidate counters are cleared together
-    ws += uint64_t(plan->n_seg) * kBins * 4;
-    plan->ws_candcnt = ws;
-    ws = a256(ws + uint64_t(plan->n_seg) * 4);
+    // the three digit histograms are contiguous: one fill clears them
+    plan->ws_hist1 = ws;
+    ws += uint64_t(plan->n_seg) * kBins1 * 4;
+    plan->ws_hist2 = ws;
+    ws += uint64_t(plan->n_seg) * kBins2 * 4;
+    plan->ws_hist3 = ws;
+    ws = a256(ws + uint64_t(plan->n_seg) * kBins3 * 4);
     plan->ws_seg = ws;
     ws = a256(ws + uint64_t(plan->n_seg) * sizeof(RkSeg));
-    plan->ws_cand = ws;
-    ws = a256(ws + W * uint64_t(plan->cand_total) * 8);
-    plan->ws_mask = ws;
-    ws = a256(ws + W * words * 4);
-    plan->ws_kmask = ws;
-    ws = a256(ws + W * words * 4);
-    plan->ws_kpos = ws;
-    ws = a256(ws + W * words * 4);
-    plan->ws_tcnt = ws;
-    ws = a256(ws + W * ntiles * 4);
-    plan->ws_tbase = ws;
-    ws = a256(ws + W * ntiles * 4);
-    plan->ws_kcnt = ws;
-    ws = a256(ws + W * ntiles * 4);
-    plan->ws_kbase = ws;
-    ws = a256(ws + W * ntiles * 4);
+    plan->ws_cand = ws;  // same layout as the error buffer, one uint32 per element
+    ws = a256(ws + W * uint64_t(plan->worker_stride) * 4);
+    uint64_t* word_arrays[] = {&plan->ws_mask, &plan->ws_tmask, &plan->ws_kmask, &plan->ws_kpos};
+    for (uint64_t* a : word_arrays) {
+      *a = ws;
+      ws = a256(ws + W * words * 4);
+    }
+    uint64_t* tile_arrays[] = {&plan->ws_ccnt, &plan->ws_tcnt, &plan->ws_ttie, &plan->ws_tiebase,
+                               &plan->ws_tbase, &plan->ws_kcnt, &plan->ws_kbase};
+    for (uint64_t* a : tile_arrays) {
+      *a = ws;
+      ws = a256(ws + W * ntiles * 4);
+    }
     plan->workspace_bytes = ws;
     const uint64_t gb = grad_dtype == PSGD_BF16 ? 2 : 4;
     plan->message_bytes = uint64_t(plan->keep_total) * 8;
@@ -898,74 +1027,78 @@ extern "C" psgd_status psgd_rtopk_step(psgd_rtopk_plan* plan, const void* grads,
       if (a.lo < b.hi && b.lo < a.hi)
         return fail(PSGD_ERR_INVALID_ARG, std::string(fn) + ": " + a.name + " and " + b.name + " overlap");
     }
-  RkLayer* dl = nullptr;
-  RkTile* dt = nullptr;
-  psgd_status s = device_tables(plan, &dl, &dt);
+  DevTables dt{};
+  psgd_status s = device_tables(plan, &dt);
   if (s != PSGD_OK) return s;
 
   char* ws = static_cast<char*>(workspace);
-  uint32_t* hist = reinterpret_cast<uint32_t*>(ws + plan->ws_hist);
-  uint32_t* candcnt = reinterpret_cast<uint32_t*>(ws + plan->ws_candcnt);
+  auto u32 = [&](uint64_t off) { return reinterpret_cast<uint32_t*>(ws + off); };
+  uint32_t* hist1 = u32(plan->ws_hist1);
+  uint32_t* hist2 = u32(plan->ws_hist2);
+  uint32_t* hist3 = u32(plan->ws_hist3);
   RkSeg* seg = reinterpret_cast<RkSeg*>(ws + plan->ws_seg);
-  uint64_t* cand = reinterpret_cast<uint64_t*>(ws + plan->ws_cand);
-  uint32_t* mask = reinterpret_cast<uint32_t*>(ws + plan->ws_mask);
-  uint32_t* kmask = reinterpret_cast<uint32_t*>(ws + plan->ws_kmask);
-  uint32_t* kpos = reinterpret_cast<uint32_t*>(ws + plan->ws_kpos);
-  uint32_t* tcnt = reinterpret_cast<uint32_t*>(ws + plan->ws_tcnt);
-  uint32_t* tbase = reinterpret_cast<uint32_t*>(ws + plan->ws_tbase);
-  uint32_t* kcnt = reinterpret_cast<uint32_t*>(ws + plan->ws_kcnt);
-  uint32_t* kbase = reinterpret_cast<uint32_t*>(ws + plan->ws_kbase);
+  uint32_t* cand = u32(plan->ws_cand);
+  uint32_t *mask = u32(plan->ws_mask), *tmask = u32(plan->ws_tmask), *kmask = u32(plan->ws_kmask);
+  uint32_t* kpos = u32(plan->ws_kpos);
+  uint32_t *ccnt = u32(plan->ws_ccnt), *tcnt = u32(plan->ws_tcnt), *ttie = u32(plan->ws_ttie);
+  uint32_t *tiebase = u32(plan->ws_tiebase), *tbase = u32(plan->ws_tbase);
+  uint32_t *kcnt = u32(plan->ws_kcnt), *kbase = u32(plan->ws_kbase);
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int nl = int(plan->layers.size());
   const int ntiles = int(plan->tiles.size());
   const int64_t sstride = int64_t(stride);
-  const int64_t cstride = plan->cand_total;
   const dim3 tgrid(static_cast<unsigned>(ntiles), static_cast<unsigned>(W));
   const dim3 sgrid(static_cast<unsigned>(nl), static_cast<unsigned>(W));
-  const int64_t nzero = (int64_t(plan->ws_candcnt) - int64_t(plan->ws_hist)) / 4 + plan->n_seg;
+  const dim3 cgrid(static_cast<unsigned>(plan->chunks.size()), static_cast<unsigned>(W));
+  const int64_t nzero = int64_t(plan->n_seg) * (kBins1 + kBins2 + kBins3);
   const unsigned zblocks = unsigned(std::min<int64_t>((nzero + 255) / 256, 4096));
+  const RkLayer* L = dt.layers;
+  const RkTile* T = dt.tiles;
+  const RkChunk* C = dt.chunks;
 
-  if ((s = launch(plan, kZero, rk_zero, dim3(zblocks), dim3(256), st, hist, nzero)) != PSGD_OK) return s;
+  if ((s = launch(plan, kZero, rk_zero, dim3(zblocks), dim3(256), st, hist1, nzero)) != PSGD_OK) return s;
   if (plan->dtype == PSGD_BF16)
-    s = launch(plan, kEfHist, rk_ef_hist<uint16_t>, tgrid, dim3(kTileThreads), st, static_cast<const RkTile*>(dt),
-               static_cast<const uint16_t*>(grads), errors, hist, sstride, nl);
+    s = launch(plan, kEfHist, rk_ef_hist<uint16_t>, tgrid, dim3(kTileThreads), st, T,
+               static_cast<const uint16_t*>(grads), errors, hist1, sstride, nl);
   else
-    s = launch(plan, kEfHist, rk_ef_hist<float>, tgrid, dim3(kTileThreads), st, static_cast<const RkTile*>(dt),
-               static_cast<const float*>(grads), errors, hist, sstride, nl);
+    s = launch(plan, kEfHist, rk_ef_hist<float>, tgrid, dim3(kTileThreads), st, T, static_cast<const float*>(grads),
+               errors, hist1, sstride, nl);
   if (s != PSGD_OK) return s;
-  if ((s = launch(plan, kSelect, rk_select, sgrid, dim3(256), st, static_cast<const RkLayer*>(dl),
-                  static_cast<const uint32_t*>(hist), seg, nl)) != PSGD_OK)
+  if ((s = launch(plan, kSelect, rk_select, sgrid, dim3(kSelThreads), st, L, static_cast<const uint32_t*>(hist1), seg,
+                  nl)) != PSGD_OK)
     return s;
-  if ((s = launch(plan, kMark, rk_mark, tgrid, dim3(kTileThreads), st, static_cast<const RkTile*>(dt),
-                  static_cast<const RkLayer*>(dl), static_cast<const float*>(errors), static_cast<const RkSeg*>(seg),
-                  mask, tcnt, cand, candcnt, sstride, cstride, nl, ntiles)) != PSGD_OK)
-    return s;
-  if ((s = launch(plan, kRefine, rk_refine, sgrid, dim3(kSegThreads), st, static_cast<const RkLayer*>(dl),
-                  static_cast<const float*>(errors), static_cast<const RkSeg*>(seg), static_cast<const uint64_t*>(cand),
-                  static_cast<const uint32_t*>(candcnt), mask, tcnt, sstride, cstride, nl, ntiles)) != PSGD_OK)
-    return s;
-  if ((s = launch(plan, kScanTop, rk_scan_tiles, sgrid, dim3(kSegThreads), st, static_cast<const RkLayer*>(dl),
-                  static_cast<const uint32_t*>(tcnt), tbase, seg, index, value, plan->keep_total, nl, ntiles, 0)) !=
+  if ((s = launch(plan, kMark, rk_mark, tgrid, dim3(kTileThreads), st, T, static_cast<const float*>(errors),
+                  static_cast<const RkSeg*>(seg), hist2, mask, tmask, tcnt, ttie, cand, ccnt, sstride, nl, ntiles)) !=
       PSGD_OK)
     return s;
-  if ((s = launch(plan, kKeep, rk_keep, tgrid, dim3(kWordThreads), st, static_cast<const RkTile*>(dt),
-                  static_cast<const RkLayer*>(dl), static_cast<const uint32_t*>(mask),
-                  static_cast<const uint32_t*>(tbase), ranks, kmask, kcnt, sstride, plan->top_total, ntiles)) !=
-      PSGD_OK)
+  if ((s = launch(plan, kLevel3, rk_level3, cgrid, dim3(kSelThreads), st, C, T, L, static_cast<const RkSeg*>(seg),
+                  static_cast<const uint32_t*>(hist2), hist3, static_cast<const uint32_t*>(cand),
+                  static_cast<const uint32_t*>(ccnt), sstride, nl, ntiles)) != PSGD_OK)
     return s;
-  if ((s = launch(plan, kScanKept, rk_scan_tiles, sgrid, dim3(kSegThreads), st, static_cast<const RkLayer*>(dl),
-                  static_cast<const uint32_t*>(kcnt), kbase, seg, index, value, plan->keep_total, nl, ntiles, 1)) !=
-      PSGD_OK)
+  if ((s = launch(plan, kFinal, rk_final, cgrid, dim3(kSelThreads), st, C, T, L, seg,
+                  static_cast<const uint32_t*>(hist2), static_cast<const uint32_t*>(hist3),
+                  static_cast<const uint32_t*>(cand), static_cast<const uint32_t*>(ccnt), mask, tmask, tcnt, ttie,
+                  sstride, nl, ntiles)) != PSGD_OK)
     return s;
-  if ((s = launch(plan, kEmit, rk_emit, tgrid, dim3(kWordThreads), st, static_cast<const RkTile*>(dt),
-                  static_cast<const RkLayer*>(dl), kmask, static_cast<const uint32_t*>(kbase), errors, index, value,
-                  kpos, sstride, plan->keep_total, ntiles)) != PSGD_OK)
+  if ((s = launch(plan, kScanTop, rk_scan_top, sgrid, dim3(kSegThreads), st, L, static_cast<const uint32_t*>(tcnt),
+                  static_cast<const uint32_t*>(ttie), tbase, tiebase, seg, nl, ntiles)) != PSGD_OK)
+    return s;
+  if ((s = launch(plan, kKeep, rk_keep, tgrid, dim3(kWordThreads), st, T, L, static_cast<const RkSeg*>(seg),
+                  static_cast<const uint32_t*>(mask), static_cast<const uint32_t*>(tmask),
+                  static_cast<const uint32_t*>(tbase), static_cast<const uint32_t*>(tiebase), ranks, kmask, kcnt,
+                  sstride, plan->top_total, nl, ntiles)) != PSGD_OK)
+    return s;
+  if ((s = launch(plan, kScanKept, rk_scan_kept, sgrid, dim3(kSegThreads), st, L, static_cast<const uint32_t*>(kcnt),
+                  kbase, seg, index, value, plan->keep_total, nl, ntiles)) != PSGD_OK)
+    return s;
+  if ((s = launch(plan, kEmit, rk_emit, tgrid, dim3(kWordThreads), st, T, L, kmask,
+                  static_cast<const uint32_t*>(kbase), errors, index, value, kpos, sstride, plan->keep_total,
+                  ntiles)) != PSGD_OK)
     return s;
   if (update != nullptr)
-    s = launch(plan, kUpdate, rk_update, dim3(unsigned(ntiles)), dim3(kDenseThreads), st,
-               static_cast<const RkTile*>(dt), static_cast<const RkLayer*>(dl), static_cast<const uint32_t*>(kmask),
-               static_cast<const uint32_t*>(kpos), static_cast<const float*>(value), update, int(W), sstride,
-               plan->keep_total, 1.0f / float(W));
+    s = launch(plan, kUpdate, rk_update, dim3(unsigned(ntiles)), dim3(kWordThreads), st, T, L,
+               static_cast<const uint32_t*>(kmask), static_cast<const uint32_t*>(kpos),
+               static_cast<const float*>(value), update, int(W), sstride, plan->keep_total, 1.0f / float(W));
   return s;
 }

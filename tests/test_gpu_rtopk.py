@@ -143,8 +143,8 @@ def test_ragged_multilayer_three_steps(W):
 
 def test_ties_zeros_and_one_bin():
     """Many exact ties (index order decides), a top set larger than the nonzeros (ties at
-    zero), and a tensor whose values all share one level-1 bin, so its candidates do not
-    fit the list and the segment is rescanned."""
+    zero), and tensors whose values all share one digit-1 bin, so every entry is a
+    candidate (one of them with ties that only the index order breaks)."""
     print("\n[case] ties / zeros / one bin", flush=True)
     W = 2
     shapes = [(1, 3000), (1, 5000), (1, 50000), (1, 40000)]
@@ -164,6 +164,28 @@ def test_ties_zeros_and_one_bin():
     E = [np.zeros((W, r * c), np.float32) for r, c in shapes]
     for li, st in oracle_step(run, G, E, tops, keeps, R, range(4)).items():
         compare(run, li, st)
+
+
+def test_error_feedback_many_steps():
+    """Twelve steps with error feedback: entries that stay unsent pile up just under the
+    threshold, which crowds the boundary bins; every step is compared exactly."""
+    print("\n[case] 12 EF steps W=4", flush=True)
+    W = 4
+    shapes = [(512, 2304), (256, 1152), (64, 576), (1, 512), (10, 512)]
+    tops, keeps = _counts(shapes, 0.01, 2)
+    rng = np.random.default_rng(14)
+    run = RtopkRun(shapes, tops, keeps, W)
+    E = [np.zeros((W, r * c), np.float32) for r, c in shapes]
+    for step in range(12):
+        G = [(0.05 * rng.standard_normal((W, r * c))).astype(np.float32) for r, c in shapes]
+        R = _ranks(rng, W, tops)
+        run.set_grads(G)
+        run.set_ranks(R)
+        run.step()
+        ref = oracle_step(run, G, E, tops, keeps, R, range(len(shapes)))
+        for li, st in ref.items():
+            compare(run, li, st)
+        E = [ref[li].errors for li in range(len(shapes))]
 
 
 def test_bf16_gradients():
@@ -260,8 +282,8 @@ def test_timing_reports_every_kernel():
     run.step()
     run.step()
     stats = P.psgd_rtopk_plan_kernel_stats(run.plan, reset=True)
-    assert set(stats) == {"rk_zero", "rk_ef_hist", "rk_select", "rk_mark", "rk_refine", "rk_scan_top",
-                          "rk_keep", "rk_scan_kept", "rk_emit", "rk_update"}
+    assert set(stats) == {"rk_zero", "rk_ef_hist", "rk_select", "rk_mark", "rk_level3", "rk_final",
+                          "rk_scan_top", "rk_keep", "rk_scan_kept", "rk_emit", "rk_update"}
     assert all(n == 2 and ms > 0 for n, ms in stats.values())
 
 
