@@ -249,20 +249,29 @@ def main() -> int:
         plan = psgd.psgd_rtopk_plan_create(shapes, tops, keeps, W, psgd.PSGD_F32)
         s = plan.sizes
         ld = s["worker_stride"]
-        grads = torch.zeros((W, ld), dtype=torch.float32, device=dev)
+        # four gradient sets resident in HBM, one per step in turn, so the error memory
+        # evolves as under changing gradients rather than one repeated gradient
+        nsets = 4
+        grads = torch.zeros((nsets, W, ld), dtype=torch.float32, device=dev)
         errors = torch.zeros((W, ld), dtype=torch.float32, device=dev)
         index = torch.zeros((W, s["keep_total"]), dtype=torch.int32, device=dev)
         value = torch.zeros((W, s["keep_total"]), dtype=torch.float32, device=dev)
         update = torch.zeros(ld, dtype=torch.float32, device=dev)
         workspace = torch.empty(s["workspace_bytes"], dtype=torch.uint8, device=dev)
-        WL.device_grads(wr, 0, [(L.offset, L.rows, L.cols) for L in plan.layers], grads)
-        ranks_h = psgd.pack_rows(plan, [np.stack([WL.rtopk_ranks(wr, 0, w, li, tops[li]) for w in range(W)])
-                                        for li in range(len(shapes))], "top", np.uint32)
-        ranks = torch.from_numpy(ranks_h.view(np.int32)).to(dev)
+        layout = [(L.offset, L.rows, L.cols) for L in plan.layers]
+        ranks = torch.zeros((nsets, W, s["top_total"]), dtype=torch.int32, device=dev)
+        for k in range(nsets):
+            WL.device_grads(wr, k, layout, grads[k])
+            ranks_h = psgd.pack_rows(plan, [np.stack([WL.rtopk_ranks(wr, k, w, li, tops[li]) for w in range(W)])
+                                            for li in range(len(shapes))], "top", np.uint32)
+            ranks[k].copy_(torch.from_numpy(ranks_h.view(np.int32)))
         stream = torch.cuda.current_stream(dev)
+        turn = [0]
 
         def step():
-            psgd.psgd_rtopk_step(plan, grads, errors, ranks, index, value, update, workspace, stream)
+            k = turn[0] % nsets
+            turn[0] += 1
+            psgd.psgd_rtopk_step(plan, grads[k], errors, ranks[k], index, value, update, workspace, stream)
 
         for _ in range(args.warmup):
             step()
@@ -304,7 +313,8 @@ def main() -> int:
             "model_bytes_per_step": s["model_bytes"],
             "config": {"workload": "resnet18_cifar_shapes", "workers": W, "tensors": s["n_layers"],
                        "keep_frac": wr.keep_frac, "top_factor": wr.top_factor, "keep_total": s["keep_total"],
-                       "top_total": s["top_total"], "grad_bytes_per_step": grad_bytes},
+                       "top_total": s["top_total"], "grad_bytes_per_step": grad_bytes,
+                       "gradient_sets": nsets},
             "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "traffic": traffic_for(dom, RTOPK_TRAFFIC_FILE, RTOPK_SRC),

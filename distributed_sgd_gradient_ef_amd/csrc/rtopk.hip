@@ -12,12 +12,15 @@
 //
 //   rk_zero       clear the three digit histograms
 //   rk_ef_hist    M = G + E, stored into E; per segment, a histogram of digit 1
-//                 (LDS per workgroup, flushed with atomics)
+//                 (LDS per workgroup, flushed with atomics); and, for the digit-1 bin
+//                 predicted from the previous step, the marking below
 //   rk_select     per segment: the digit-1 bin b1 holding T, and how many of its
-//                 entries belong to the top set
-//   rk_mark       re-read M: entries above b1 -> top mask (one bit per element); entries
-//                 in b1 -> the tile's candidate region (key bits 19..0 | tile offset),
-//                 and a histogram of their digit 2; per-tile counts
+//                 entries belong to the top set; a wrong prediction sends the segment
+//                 to rk_mark (b1 becomes the next step's prediction)
+//   rk_mark       (mispredicted segments) re-read M: entries above b1 -> top mask (one
+//                 bit per element); entries in b1 -> the tile's candidate region (key
+//                 bits 19..0 | tile offset), and a histogram of their digit 2; per-tile
+//                 counts
 //   rk_level3     per chunk of tiles: digit-2 bin b2 (recomputed from the histogram),
 //                 then a histogram of digit 3 of the candidates in b2
 //   rk_final      per chunk of tiles: T and the rule (keys >= a bound are in; when the
@@ -35,7 +38,9 @@
 //   rk_update     U = (1/W) * sum over workers, in worker order, of the sent entries
 //
 // Every reduction that produces a float has a fixed order; every other result is an
-// integer count or a set, so a step is bitwise reproducible.
+// integer count or a set, so a step is bitwise reproducible.  The prediction only
+// decides which kernel does the marking: a stale or garbage prediction costs the
+// re-read, never a different result.
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
@@ -57,13 +62,14 @@ namespace rtk {
 constexpr int kTile = 4096;               // elements per tile
 constexpr int kLocalBits = 12;            // log2(kTile): offset of an entry inside its tile
 constexpr int kTileThreads = 256;         // rk_ef_hist / rk_mark: 16 elements per thread
-constexpr int kWordThreads = kTile / 32;  // rk_keep / rk_emit / rk_update: one thread per mask word
+constexpr int kWordThreads = kTile / 32;  // rk_update: one thread per mask word
 constexpr int kSelThreads = 256;          // rk_select / rk_level3 / rk_final
 constexpr int kSegThreads = 1024;         // per-segment scans
 constexpr int kBins1 = 2048;              // digit 1: key bits 30..20
 constexpr int kBins2 = 2048;              // digit 2: key bits 19..9
 constexpr int kBins3 = 512;               // digit 3: key bits 8..0
 constexpr int kChunkTiles = 16;           // tiles per workgroup in rk_level3 / rk_final
+constexpr int kWaveBlock = 256;           // rk_keep / rk_emit: one wave per tile, 4 tiles per workgroup
 
 struct RkLayer {
   int64_t offset;  // element offset in a worker slice
@@ -92,21 +98,25 @@ struct RkSeg {
   uint32_t b1;      // digit-1 bin holding T
   uint32_t need1;   // entries of bin b1 in the top set
   uint32_t count1;  // entries in bin b1
-  uint32_t pad0;
+  uint32_t redo;    // 1: the predicted bin was not b1; rk_mark marks this segment
+  uint32_t b2;       // digit-2 bin holding T
+  uint32_t need2;    // entries of (b1, b2) in the top set
+  uint32_t settled;  // 1: every entry of the last bin found is in (no digit 3)
   uint32_t sel_lo;   // every entry with key >= sel_lo is in the top set
   uint32_t tie_key;  // partial: the first need_t entries (index order) with this key are in
   uint32_t need_t;
   uint32_t partial;
   uint32_t ntop;   // top-set size found (r)
   uint32_t nkept;  // entries with rank < k
-  uint32_t pad1, pad2;
+  uint32_t pad1, pad2, pad3;
 };
 
 enum KernelId {
-  kZero = 0, kEfHist, kSelect, kMark, kLevel3, kFinal, kScanTop, kKeep, kScanKept, kEmit, kUpdate, kNumK
+  kZero = 0, kEfHist, kSelect, kMark, kPick2, kLevel3, kRule, kFinal, kScanTop, kKeep, kScanKept, kEmit, kUpdate, kNumK
 };
-const char* const kNames[kNumK] = {"rk_zero",  "rk_ef_hist",  "rk_select", "rk_mark",      "rk_level3", "rk_final",
-                                   "rk_scan_top", "rk_keep", "rk_scan_kept", "rk_emit", "rk_update"};
+const char* const kNames[kNumK] = {"rk_zero",     "rk_ef_hist", "rk_select",    "rk_mark", "rk_pick2",
+                                   "rk_level3",   "rk_rule",    "rk_final",     "rk_scan_top", "rk_keep",
+                                   "rk_scan_kept", "rk_emit",   "rk_update"};
 
 }  // namespace rtk
 }  // namespace psgd
@@ -120,9 +130,9 @@ struct psgd_rtopk_plan {
   std::vector<psgd::rtk::RkChunk> chunks;
   int64_t worker_stride = 0, numel = 0, top_total = 0, keep_total = 0;
   int64_t n_seg = 0;
-  uint64_t ws_hist1 = 0, ws_hist2 = 0, ws_hist3 = 0, ws_seg = 0, ws_cand = 0, ws_ccnt = 0;
-  uint64_t ws_mask = 0, ws_tmask = 0, ws_kmask = 0, ws_kpos = 0;
-  uint64_t ws_tcnt = 0, ws_ttie = 0, ws_tiebase = 0, ws_tbase = 0, ws_kcnt = 0, ws_kbase = 0;
+  uint64_t ws_hist1 = 0, ws_hist2 = 0, ws_hist3 = 0, ws_seg = 0, ws_pred = 0, ws_cand = 0;
+  uint64_t ws_mask = 0, ws_tmask = 0, ws_kmask = 0, ws_kpos = 0, ws_ccnt4 = 0, ws_tcnt4 = 0;
+  uint64_t ws_tfin = 0, ws_ttie = 0, ws_tiebase = 0, ws_tbase = 0, ws_kcnt = 0, ws_kbase = 0;
   uint64_t workspace_bytes = 0;
   uint64_t message_bytes = 0, model_bytes = 0;
   std::map<int, void*> dev;  // device copy of the layer, tile and chunk tables, per HIP device
@@ -210,6 +220,33 @@ __device__ __forceinline__ uint32_t block_total(uint32_t v, uint32_t* lds) {
   return t;
 }
 
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t n = __shfl_up(v, o, 64);
+    if (lane >= o) v += n;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Set bits of `bits` in order, given the running rank of the first one: those whose
+// rank is below `limit` are returned.
+__device__ __forceinline__ uint32_t bits_below(uint32_t bits, uint32_t& rank, uint32_t limit) {
+  uint32_t out = 0;
+  for (; bits != 0u; bits &= bits - 1u) {
+    if (rank < limit) out |= bits & (0u - bits);
+    ++rank;
+  }
+  return out;
+}
+
 struct Pick {
   uint32_t bin;    // the bin holding the need-th largest entry
   uint32_t above;  // entries in the bins above it
@@ -250,135 +287,44 @@ __device__ Pick pick_bin(const uint32_t* __restrict__ h, uint32_t need, uint32_t
   return p;
 }
 
-// The selection rule of a segment from its three histograms: keys >= lo are in; with
-// `partial`, the first need_t entries (index order) with key tie are in as well.
-struct Rule {
-  uint32_t lo, tie, need_t, partial;
-};
-
-__device__ Rule segment_rule(const RkSeg& st, const uint32_t* h2, const uint32_t* h3, uint32_t* lds, uint32_t* sh) {
-  Rule r{st.b1 << 20, 0u, 0u, 0u};
-  if (st.need1 == st.count1) return r;
-  const Pick p2 = pick_bin<kBins2>(h2, st.need1, lds, sh);
-  const uint32_t need2 = st.need1 - p2.above;
-  const uint32_t k2 = (st.b1 << 20) | (p2.bin << 9);
-  r.lo = k2;
-  if (need2 == p2.count) return r;
-  const Pick p3 = pick_bin<kBins3>(h3, need2, lds, sh);
-  const uint32_t need3 = need2 - p3.above;
-  const uint32_t t = k2 | p3.bin;
-  if (need3 == p3.count) {
-    r.lo = t;
-  } else {
-    r.lo = t + 1u;
-    r.tie = t;
-    r.need_t = need3;
-    r.partial = 1u;
-  }
-  return r;
-}
-
-// ------------------------------------------------------------------ kernels
-__global__ __launch_bounds__(256) void rk_zero(uint32_t* __restrict__ p, int64_t n) {
-  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) p[i] = 0u;
-}
-
-template <typename GT>
-__global__ __launch_bounds__(kTileThreads) void rk_ef_hist(const RkTile* __restrict__ tiles, const GT* __restrict__ G,
-                                                           float* __restrict__ E, uint32_t* __restrict__ hist1,
-                                                           int64_t stride, int n_layers) {
-  __shared__ uint32_t h[kBins1];
-  for (int b = threadIdx.x; b < kBins1; b += kTileThreads) h[b] = 0u;
-  __syncthreads();
-  const RkTile t = tiles[blockIdx.x];
-  const int w = blockIdx.y;
-  const int64_t base = int64_t(w) * stride + t.begin;
+// Start of wave v's part of a tile's candidate region: the number of tile elements the
+// waves before it hold (wave v holds groups v, v+4, v+8, v+12 of 256 elements), so every
+// part lies inside the tile's own len elements.
+__device__ __forceinline__ int wave_region(int len, int v) {
+  int off = 0;
+  for (int u = 0; u < v; ++u)
 #pragma unroll
-  for (int i = 0; i < kTile / (kTileThreads * 4); ++i) {
-    const int e = (i * kTileThreads + int(threadIdx.x)) * 4;
-    if (e < t.len) {
-      const v4f g = load_g4(G + base + e);
-      float* ep = E + base + e;
-      const v4f mv = g + load_nt4(ep);
-      const float m[4] = {mv.x, mv.y, mv.z, mv.w};
-      const int valid = min(4, t.len - e);
-      if (valid == 4) {
-        store_nt4(ep, mv);
-      } else {
-        for (int j = 0; j < valid; ++j) ep[j] = m[j];
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (j < valid) atomicAdd(&h[mag_key(m[j]) >> 20], 1u);
-    }
-  }
-  __syncthreads();
-  uint32_t* gh = hist1 + (int64_t(w) * n_layers + t.layer) * kBins1;
-  for (int b = threadIdx.x; b < kBins1; b += kTileThreads) {
-    const uint32_t c = h[b];
-    if (c) atomicAdd(gh + b, c);
-  }
+    for (int i = 0; i < 4; ++i) off += min(256, max(0, len - (4 * i + u) * 256));
+  return off;
 }
 
-__global__ __launch_bounds__(kSelThreads) void rk_select(const RkLayer* __restrict__ layers,
-                                                         const uint32_t* __restrict__ hist1, RkSeg* __restrict__ seg,
-                                                         int n_layers) {
-  __shared__ uint32_t lds[16], sh[3];
-  const int l = blockIdx.x, w = blockIdx.y;
-  const int64_t s = int64_t(w) * n_layers + l;
-  const uint32_t r = uint32_t(layers[l].top);
-  const Pick p = pick_bin<kBins1>(hist1 + s * kBins1, r, lds, sh);
-  if (threadIdx.x == 0) {
-    RkSeg st{};
-    st.b1 = p.bin;
-    st.need1 = r - p.above;
-    st.count1 = p.count;
-    seg[s] = st;
-  }
-}
-
-// Tile of 16 groups of 256 elements; wave v handles groups v, v+4, v+8, v+12; lane l
-// holds elements 4l..4l+3 of its group, so mask word q of a group (32 elements) comes
-// from lanes 8q..8q+7 and is assembled by lane q from four ballots.  Candidates (digit 1
-// equal to b1) go to the tile's own region of `cand` (same layout as E) as
-// (key bits 19..0) << 12 | offset in the tile.
-__global__ __launch_bounds__(kTileThreads) void rk_mark(const RkTile* __restrict__ tiles,
-                                                        const float* __restrict__ E, const RkSeg* __restrict__ seg,
-                                                        uint32_t* __restrict__ hist2, uint32_t* __restrict__ mask,
-                                                        uint32_t* __restrict__ tmask, uint32_t* __restrict__ tcnt,
-                                                        uint32_t* __restrict__ ttie, uint32_t* __restrict__ cand,
-                                                        uint32_t* __restrict__ ccnt, int64_t stride, int n_layers,
-                                                        int ntiles) {
-  __shared__ uint32_t h2[kBins2];
-  __shared__ uint32_t lds[16];
-  for (int b = threadIdx.x; b < kBins2; b += kTileThreads) h2[b] = 0u;
-  const RkTile t = tiles[blockIdx.x];
-  const int w = blockIdx.y;
-  const int64_t s = int64_t(w) * n_layers + t.layer;
-  const uint32_t b1 = seg[s].b1;
+// Marking of one tile against digit-1 bin b1, from the 16 values each thread holds
+// (m[i][j] is element (i * kTileThreads + threadIdx.x) * 4 + j of the tile).  The wave
+// with index v handles groups v, v+4, v+8, v+12 of 256 elements; lane l holds elements
+// 4l..4l+3 of its group, so mask word q of a group (32 elements) comes from lanes
+// 8q..8q+7 and is assembled by lane q from four ballots.  Entries above b1 set top-mask
+// bits; entries in b1 (the candidates) go to the wave's part of the tile's region of
+// `cand` (same layout as E) as (key bits 19..0) << 12 | offset in the tile, and into the
+// LDS histogram h2 of their digit 2.  Each wave writes its own top and candidate counts;
+// no barrier.
+__device__ __forceinline__ void mark_tile(const float (&m)[4][4], const RkTile& t, uint32_t b1, int64_t base,
+                                          int64_t trow, uint32_t* h2, uint32_t* __restrict__ mask,
+                                          uint32_t* __restrict__ tmask, uint32_t* __restrict__ tcnt4,
+                                          uint32_t* __restrict__ cand, uint32_t* __restrict__ ccnt4) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int64_t base = int64_t(w) * stride + t.begin;
   const int64_t wbase = base >> 5;  // begin and stride are multiples of 64
-  __syncthreads();
-  float m[4][4];
   uint32_t nsure = 0, ncand = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int g = i * 4 + wv;
     const int e = g * 256 + lane * 4;
-    const int valid = max(0, min(4, t.len - e));
-    v4f v = {0.f, 0.f, 0.f, 0.f};
-    if (valid > 0) v = *reinterpret_cast<const v4f*>(E + base + e);
-    m[i][0] = v.x;
-    m[i][1] = v.y;
-    m[i][2] = v.z;
-    m[i][3] = v.w;
     uint64_t B[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t key = mag_key(m[i][j]);
-      B[j] = __ballot(j < valid && (key >> 20) > b1);
-      if (j < valid && (key >> 20) == b1) {
+      const bool ok = e + j < t.len;
+      B[j] = __ballot(ok && (key >> 20) > b1);
+      if (ok && (key >> 20) == b1) {
         atomicAdd(&h2[(key >> 9) & 0x7ffu], 1u);
         ++ncand;
       }
@@ -393,16 +339,12 @@ __global__ __launch_bounds__(kTileThreads) void rk_mark(const RkTile* __restrict
       nsure += __popc(word);
     }
   }
-  const uint32_t tot = block_total(nsure, lds);
-  const uint32_t incl = block_incl_scan(ncand, lds);
-  const int64_t trow = int64_t(w) * ntiles + blockIdx.x;
-  if (threadIdx.x == 0) {
-    tcnt[trow] = tot;
-    ttie[trow] = 0u;
-  }
-  if (threadIdx.x == kTileThreads - 1) ccnt[trow] = incl;
+  const uint32_t tot = wave_sum(nsure);
+  const uint32_t incl = wave_incl_scan(ncand);
+  if (lane == 0) tcnt4[trow * 4 + wv] = tot;
+  if (lane == 63) ccnt4[trow * 4 + wv] = incl;
   if (ncand > 0) {
-    uint32_t* out = cand + base;
+    uint32_t* out = cand + base + wave_region(t.len, wv);
     uint32_t pos = incl - ncand;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -414,6 +356,130 @@ __global__ __launch_bounds__(kTileThreads) void rk_mark(const RkTile* __restrict
       }
     }
   }
+}
+
+// ------------------------------------------------------------------ kernels
+__global__ __launch_bounds__(256) void rk_zero(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) p[i] = 0u;
+}
+
+template <typename GT>
+__global__ __launch_bounds__(kTileThreads) void rk_ef_hist(const RkTile* __restrict__ tiles, const GT* __restrict__ G,
+                                                           float* __restrict__ E, const uint32_t* __restrict__ pred,
+                                                           uint32_t* __restrict__ hist1, uint32_t* __restrict__ hist2,
+                                                           uint32_t* __restrict__ mask, uint32_t* __restrict__ tmask,
+                                                           uint32_t* __restrict__ tcnt4, uint32_t* __restrict__ cand,
+                                                           uint32_t* __restrict__ ccnt4, int64_t stride, int n_layers,
+                                                           int ntiles) {
+  __shared__ uint32_t h1[kBins1];
+  __shared__ uint32_t h2[kBins2];
+  for (int b = threadIdx.x; b < kBins1; b += kTileThreads) {
+    h1[b] = 0u;
+    h2[b] = 0u;
+  }
+  const RkTile t = tiles[blockIdx.x];
+  const int w = blockIdx.y;
+  const int64_t s = int64_t(w) * n_layers + t.layer;
+  const uint32_t bp = pred[s];
+  const int64_t base = int64_t(w) * stride + t.begin;
+  // All eight loads are issued before any use: a chunk past the tile's end reads the
+  // tile's first chunk instead (always in bounds) and is then ignored.
+  v4f gv[4], ev[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = (i * kTileThreads + int(threadIdx.x)) * 4;
+    const int ec = e < t.len ? e : 0;
+    gv[i] = load_g4(G + base + ec);
+    ev[i] = load_nt4(E + base + ec);
+  }
+  __syncthreads();
+  float m[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = (i * kTileThreads + int(threadIdx.x)) * 4;
+    const int valid = max(0, min(4, t.len - e));
+    v4f mv = gv[i] + ev[i];
+    float* ep = E + base + e;
+    if (valid == 4) {
+      store_nt4(ep, mv);
+    } else {
+      for (int j = 0; j < valid; ++j) ep[j] = mv[j];
+      if (valid == 0) mv = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    m[i][0] = mv.x;
+    m[i][1] = mv.y;
+    m[i][2] = mv.z;
+    m[i][3] = mv.w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j < valid) atomicAdd(&h1[mag_key(m[i][j]) >> 20], 1u);
+  }
+  mark_tile(m, t, bp, base, int64_t(w) * ntiles + blockIdx.x, h2, mask, tmask, tcnt4, cand, ccnt4);
+  __syncthreads();
+  uint32_t* g1 = hist1 + s * kBins1;
+  uint32_t* g2 = hist2 + s * kBins2;
+  for (int b = threadIdx.x; b < kBins1; b += kTileThreads) {
+    const uint32_t c1 = h1[b], c2 = h2[b];
+    if (c1) atomicAdd(g1 + b, c1);
+    if (c2) atomicAdd(g2 + b, c2);
+  }
+}
+
+// Per segment: b1 from the digit-1 histogram.  If the prediction the first pass marked
+// with was not b1, its digit-2 counts are discarded and rk_mark redoes the segment.
+__global__ __launch_bounds__(kSelThreads) void rk_select(const RkLayer* __restrict__ layers,
+                                                         const uint32_t* __restrict__ hist1,
+                                                         uint32_t* __restrict__ hist2, uint32_t* __restrict__ pred,
+                                                         RkSeg* __restrict__ seg, int n_layers) {
+  __shared__ uint32_t lds[16], sh[3];
+  const int l = blockIdx.x, w = blockIdx.y;
+  const int64_t s = int64_t(w) * n_layers + l;
+  const uint32_t r = uint32_t(layers[l].top);
+  const Pick p = pick_bin<kBins1>(hist1 + s * kBins1, r, lds, sh);
+  const bool redo = pred[s] != p.bin;
+  if (redo)
+    for (int b = threadIdx.x; b < kBins2; b += kSelThreads) hist2[s * kBins2 + b] = 0u;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    RkSeg st{};
+    st.b1 = p.bin;
+    st.need1 = r - p.above;
+    st.count1 = p.count;
+    st.redo = redo ? 1u : 0u;
+    seg[s] = st;
+    pred[s] = p.bin;
+  }
+}
+
+// Mispredicted segments only: re-read M and mark against the true b1.
+__global__ __launch_bounds__(kTileThreads) void rk_mark(const RkTile* __restrict__ tiles,
+                                                        const float* __restrict__ E, const RkSeg* __restrict__ seg,
+                                                        uint32_t* __restrict__ hist2, uint32_t* __restrict__ mask,
+                                                        uint32_t* __restrict__ tmask, uint32_t* __restrict__ tcnt4,
+                                                        uint32_t* __restrict__ cand, uint32_t* __restrict__ ccnt4,
+                                                        int64_t stride, int n_layers, int ntiles) {
+  __shared__ uint32_t h2[kBins2];
+  const RkTile t = tiles[blockIdx.x];
+  const int w = blockIdx.y;
+  const int64_t s = int64_t(w) * n_layers + t.layer;
+  if (!seg[s].redo) return;  // uniform
+  const uint32_t b1 = seg[s].b1;
+  for (int b = threadIdx.x; b < kBins2; b += kTileThreads) h2[b] = 0u;
+  const int64_t base = int64_t(w) * stride + t.begin;
+  float m[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = (i * kTileThreads + int(threadIdx.x)) * 4;
+    v4f v = *reinterpret_cast<const v4f*>(E + base + (e < t.len ? e : 0));
+    if (e >= t.len) v = v4f{0.f, 0.f, 0.f, 0.f};
+    m[i][0] = v.x;
+    m[i][1] = v.y;
+    m[i][2] = v.z;
+    m[i][3] = v.w;
+  }
+  __syncthreads();
+  mark_tile(m, t, b1, base, int64_t(w) * ntiles + blockIdx.x, h2, mask, tmask, tcnt4, cand, ccnt4);
+  __syncthreads();
   uint32_t* gh = hist2 + s * kBins2;
   for (int b = threadIdx.x; b < kBins2; b += kTileThreads) {
     const uint32_t c = h2[b];
@@ -421,35 +487,93 @@ __global__ __launch_bounds__(kTileThreads) void rk_mark(const RkTile* __restrict
   }
 }
 
+// Per segment, once digit 2 is counted: the digit-2 bin b2 (or the segment is settled).
+__global__ __launch_bounds__(kSelThreads) void rk_pick2(const uint32_t* __restrict__ hist2, RkSeg* __restrict__ seg,
+                                                        int64_t n_seg) {
+  __shared__ uint32_t lds[16], sh[3];
+  const int64_t s = int64_t(blockIdx.y) * gridDim.x + blockIdx.x;
+  const RkSeg st = seg[s];
+  if (st.need1 == st.count1) {  // settled by digit 1: all of bin b1 is in
+    if (threadIdx.x == 0) {
+      seg[s].settled = 1u;
+      seg[s].sel_lo = st.b1 << 20;
+    }
+    return;
+  }
+  const Pick p2 = pick_bin<kBins2>(hist2 + s * kBins2, st.need1, lds, sh);
+  if (threadIdx.x == 0) {
+    const uint32_t need2 = st.need1 - p2.above;
+    seg[s].b2 = p2.bin;
+    seg[s].need2 = need2;
+    seg[s].settled = need2 == p2.count ? 1u : 0u;
+    seg[s].sel_lo = (st.b1 << 20) | (p2.bin << 9);
+  }
+}
+
+// The candidate ranges of a chunk (kChunkTiles tiles x 4 waves) flattened into one index
+// space: rbeg[r] is range r's element offset in `cand`, pre[r] the number of candidates
+// before it, pre[nr] the chunk's total.  Every thread must call it.
+struct ChunkRanges {
+  int64_t rbeg[kChunkTiles * 4];
+  int64_t tbeg[kChunkTiles * 4];  // element offset of the range's tile (entries hold offsets in it)
+  uint32_t pre[kChunkTiles * 4 + 1];
+};
+
+__device__ __forceinline__ uint32_t chunk_ranges(const RkChunk& ch, const RkLayer& L, const RkTile* __restrict__ tiles,
+                                                 const uint32_t* __restrict__ ccnt4, int w, int64_t stride, int ntiles,
+                                                 ChunkRanges& cr) {
+  const int nr = (ch.t1 - ch.t0) * 4;
+  if (threadIdx.x < 64) {  // one wave builds the table
+    const int r = threadIdx.x;
+    uint32_t n = 0;
+    if (r < nr) {
+      const int ti = L.tile_off + ch.t0 + (r >> 2);
+      const RkTile tl = tiles[ti];
+      n = ccnt4[(int64_t(w) * ntiles + ti) * 4 + (r & 3)];
+      cr.tbeg[r] = int64_t(w) * stride + tl.begin;
+      cr.rbeg[r] = cr.tbeg[r] + wave_region(tl.len, r & 3);
+    }
+    const uint32_t incl = wave_incl_scan(n);
+    if (r < nr) cr.pre[r] = incl - n;
+    if (r == 63) cr.pre[nr] = incl;
+  }
+  __syncthreads();
+  return cr.pre[nr];
+}
+
+// Range holding flattened item i (pre is non-decreasing; ranges may be empty).
+__device__ __forceinline__ int range_of(const ChunkRanges& cr, int nr, uint32_t i) {
+  int lo = 0, hi = nr - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cr.pre[mid] <= i) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
 // Digit 3 over the candidates whose digit 2 is b2, for segments not settled by then.
 __global__ __launch_bounds__(kSelThreads) void rk_level3(const RkChunk* __restrict__ chunks,
                                                          const RkTile* __restrict__ tiles,
                                                          const RkLayer* __restrict__ layers,
-                                                         const RkSeg* __restrict__ seg,
-                                                         const uint32_t* __restrict__ hist2,
-                                                         uint32_t* __restrict__ hist3, const uint32_t* __restrict__ cand,
-                                                         const uint32_t* __restrict__ ccnt, int64_t stride,
+                                                         const RkSeg* __restrict__ seg, uint32_t* __restrict__ hist3,
+                                                         const uint32_t* __restrict__ cand,
+                                                         const uint32_t* __restrict__ ccnt4, int64_t stride,
                                                          int n_layers, int ntiles) {
   __shared__ uint32_t h3[kBins3];
-  __shared__ uint32_t lds[16], sh[3];
   const RkChunk ch = chunks[blockIdx.x];
   const int w = blockIdx.y;
   const int64_t s = int64_t(w) * n_layers + ch.layer;
-  const RkSeg st = seg[s];
-  if (st.need1 == st.count1) return;  // uniform: settled by digit 1
-  const Pick p2 = pick_bin<kBins2>(hist2 + s * kBins2, st.need1, lds, sh);
-  if (st.need1 - p2.above == p2.count) return;  // uniform: settled by digit 2
+  if (seg[s].settled) return;  // uniform
+  const uint32_t b2 = seg[s].b2;
   for (int b = threadIdx.x; b < kBins3; b += kSelThreads) h3[b] = 0u;
-  __syncthreads();
+  __shared__ ChunkRanges cr;
   const RkLayer L = layers[ch.layer];
-  for (int tt = ch.t0; tt < ch.t1; ++tt) {
-    const int ti = L.tile_off + tt;
-    const uint32_t n = ccnt[int64_t(w) * ntiles + ti];
-    const uint32_t* c = cand + int64_t(w) * stride + tiles[ti].begin;
-    for (uint32_t i = threadIdx.x; i < n; i += kSelThreads) {
-      const uint32_t e = c[i];
-      if ((e >> 21) == p2.bin) atomicAdd(&h3[(e >> kLocalBits) & 0x1ffu], 1u);
-    }
+  const int nr = (ch.t1 - ch.t0) * 4;
+  const uint32_t total = chunk_ranges(ch, L, tiles, ccnt4, w, stride, ntiles, cr);
+  for (uint32_t i = threadIdx.x; i < total; i += kSelThreads) {
+    const int r = range_of(cr, nr, i);
+    const uint32_t e = cand[cr.rbeg[r] + (i - cr.pre[r])];
+    if ((e >> 21) == b2) atomicAdd(&h3[(e >> kLocalBits) & 0x1ffu], 1u);
   }
   __syncthreads();
   uint32_t* gh = hist3 + s * kBins3;
@@ -459,57 +583,76 @@ __global__ __launch_bounds__(kSelThreads) void rk_level3(const RkChunk* __restri
   }
 }
 
-// Apply the segment's rule to the candidates of a chunk of tiles: top-mask bits and
-// tile counts for those in, tie-mask bits and tile tie counts for the partial ties.
+// Per segment, once digit 3 is counted: the rule.  Keys >= sel_lo are in; when the
+// entries equal to T are only partly in, the first need_t of them in index order are.
+__global__ __launch_bounds__(kSelThreads) void rk_rule(const uint32_t* __restrict__ hist3, RkSeg* __restrict__ seg) {
+  __shared__ uint32_t lds[16], sh[3];
+  const int64_t s = int64_t(blockIdx.y) * gridDim.x + blockIdx.x;
+  const RkSeg st = seg[s];
+  if (st.settled) {
+    if (threadIdx.x == 0) seg[s].partial = 0u;
+    return;
+  }
+  const Pick p3 = pick_bin<kBins3>(hist3 + s * kBins3, st.need2, lds, sh);
+  if (threadIdx.x == 0) {
+    const uint32_t need3 = st.need2 - p3.above;
+    const uint32_t t = st.sel_lo | p3.bin;
+    if (need3 == p3.count) {
+      seg[s].sel_lo = t;
+      seg[s].partial = 0u;
+    } else {
+      seg[s].sel_lo = t + 1u;
+      seg[s].tie_key = t;
+      seg[s].need_t = need3;
+      seg[s].partial = 1u;
+    }
+  }
+}
+
+// Apply the segment's rule to the candidates of a chunk of tiles: top-mask bits and a
+// per-tile count for those in, tie-mask bits and a per-tile tie count for the partial
+// ties.
 __global__ __launch_bounds__(kSelThreads) void rk_final(const RkChunk* __restrict__ chunks,
                                                         const RkTile* __restrict__ tiles,
-                                                        const RkLayer* __restrict__ layers, RkSeg* __restrict__ seg,
-                                                        const uint32_t* __restrict__ hist2,
-                                                        const uint32_t* __restrict__ hist3,
+                                                        const RkLayer* __restrict__ layers,
+                                                        const RkSeg* __restrict__ seg,
                                                         const uint32_t* __restrict__ cand,
-                                                        const uint32_t* __restrict__ ccnt, uint32_t* __restrict__ mask,
-                                                        uint32_t* __restrict__ tmask, uint32_t* __restrict__ tcnt,
+                                                        const uint32_t* __restrict__ ccnt4, uint32_t* __restrict__ mask,
+                                                        uint32_t* __restrict__ tmask, uint32_t* __restrict__ tfin,
                                                         uint32_t* __restrict__ ttie, int64_t stride, int n_layers,
                                                         int ntiles) {
-  __shared__ uint32_t lds[16], sh[3];
+  __shared__ uint32_t c_in[kChunkTiles], c_tie[kChunkTiles];
+  __shared__ ChunkRanges cr;
   const RkChunk ch = chunks[blockIdx.x];
   const int w = blockIdx.y;
   const int64_t s = int64_t(w) * n_layers + ch.layer;
-  const RkSeg st = seg[s];
-  const Rule rule = segment_rule(st, hist2 + s * kBins2, hist3 + s * kBins3, lds, sh);
-  if (ch.first && threadIdx.x == 0) {
-    seg[s].sel_lo = rule.lo;
-    seg[s].tie_key = rule.tie;
-    seg[s].need_t = rule.need_t;
-    seg[s].partial = rule.partial;
+  const uint32_t hi = seg[s].b1 << 20, lo = seg[s].sel_lo, tie = seg[s].tie_key;
+  const bool partial = seg[s].partial != 0u;
+  if (threadIdx.x < kChunkTiles) {
+    c_in[threadIdx.x] = 0u;
+    c_tie[threadIdx.x] = 0u;
   }
   const RkLayer L = layers[ch.layer];
-  const uint32_t hi = st.b1 << 20;
-  for (int tt = ch.t0; tt < ch.t1; ++tt) {
-    const int ti = L.tile_off + tt;
-    const int64_t trow = int64_t(w) * ntiles + ti;
-    const uint32_t n = ccnt[trow];
-    const int64_t ebase = int64_t(w) * stride + tiles[ti].begin;
-    const uint32_t* c = cand + ebase;
-    uint32_t nin = 0, ntie = 0;
-    for (uint32_t i = threadIdx.x; i < n; i += kSelThreads) {
-      const uint32_t e = c[i];
-      const uint32_t key = hi | (e >> kLocalBits);
-      const int64_t el = ebase + (e & uint32_t(kTile - 1));
-      if (key >= rule.lo) {
-        atomicOr(mask + (el >> 5), 1u << (el & 31));
-        ++nin;
-      } else if (rule.partial && key == rule.tie) {
-        atomicOr(tmask + (el >> 5), 1u << (el & 31));
-        ++ntie;
-      }
+  const int nr = (ch.t1 - ch.t0) * 4;
+  const uint32_t total = chunk_ranges(ch, L, tiles, ccnt4, w, stride, ntiles, cr);
+  for (uint32_t i = threadIdx.x; i < total; i += kSelThreads) {
+    const int r = range_of(cr, nr, i);
+    const uint32_t e = cand[cr.rbeg[r] + (i - cr.pre[r])];
+    const uint32_t key = hi | (e >> kLocalBits);
+    const int64_t el = cr.tbeg[r] + (e & uint32_t(kTile - 1));
+    if (key >= lo) {
+      atomicOr(mask + (el >> 5), 1u << (el & 31));
+      atomicAdd(&c_in[r >> 2], 1u);
+    } else if (partial && key == tie) {
+      atomicOr(tmask + (el >> 5), 1u << (el & 31));
+      atomicAdd(&c_tie[r >> 2], 1u);
     }
-    const uint32_t a = block_total(nin, lds);
-    const uint32_t b = block_total(ntie, lds);
-    if (threadIdx.x == 0) {
-      tcnt[trow] += a;
-      ttie[trow] = b;
-    }
+  }
+  __syncthreads();
+  if (int(threadIdx.x) < ch.t1 - ch.t0) {
+    const int64_t trow = int64_t(w) * ntiles + L.tile_off + ch.t0 + threadIdx.x;
+    tfin[trow] = c_in[threadIdx.x];
+    ttie[trow] = c_tie[threadIdx.x];
   }
 }
 
@@ -517,7 +660,8 @@ __global__ __launch_bounds__(kSelThreads) void rk_final(const RkChunk* __restric
 // tile takes min(its ties, what is left); then exclusive scans give every tile its
 // first tie rank and its first slot.
 __global__ __launch_bounds__(kSegThreads) void rk_scan_top(const RkLayer* __restrict__ layers,
-                                                           const uint32_t* __restrict__ tcnt,
+                                                           const uint32_t* __restrict__ tcnt4,
+                                                           const uint32_t* __restrict__ tfin,
                                                            const uint32_t* __restrict__ ttie,
                                                            uint32_t* __restrict__ tbase,
                                                            uint32_t* __restrict__ tiebase, RkSeg* __restrict__ seg,
@@ -535,7 +679,11 @@ __global__ __launch_bounds__(kSegThreads) void rk_scan_top(const RkLayer* __rest
     const uint32_t vt = ok ? ttie[row + i] : 0u;
     const uint32_t tb = run_tie + block_incl_scan(vt, lds) - vt;
     const uint32_t take = tb >= need_t ? 0u : min(vt, need_t - tb);
-    const uint32_t v = (ok ? tcnt[row + i] : 0u) + take;
+    uint32_t v = take;
+    if (ok) {
+      const uint32_t* c4 = tcnt4 + (row + i) * 4;
+      v += c4[0] + c4[1] + c4[2] + c4[3] + tfin[row + i];
+    }
     const uint32_t incl = block_incl_scan(v, lds);
     if (ok) {
       tbase[row + i] = run_top + incl - v;
@@ -576,84 +724,103 @@ __global__ __launch_bounds__(kSegThreads) void rk_scan_kept(const RkLayer* __res
   }
 }
 
-// One thread per mask word of a tile: the top set's words (mask, plus the tie entries
-// whose tie rank is below need_t) in index order get consecutive slots from the tile's
-// base; those whose rank is below k are kept.
-__global__ __launch_bounds__(kWordThreads) void rk_keep(const RkTile* __restrict__ tiles,
-                                                        const RkLayer* __restrict__ layers,
-                                                        const RkSeg* __restrict__ seg,
-                                                        const uint32_t* __restrict__ mask,
-                                                        const uint32_t* __restrict__ tmask,
-                                                        const uint32_t* __restrict__ tbase,
-                                                        const uint32_t* __restrict__ tiebase,
-                                                        const uint32_t* __restrict__ ranks,
-                                                        uint32_t* __restrict__ kmask, uint32_t* __restrict__ kcnt,
-                                                        int64_t stride, int64_t top_total, int n_layers, int ntiles) {
-  __shared__ uint32_t lds[16];
-  const RkTile t = tiles[blockIdx.x];
+// One wave per tile, two mask words (64 elements) per lane; wave scans only.  The top
+// set's words (mask, plus the tie entries whose tie rank is below need_t) in index order
+// get consecutive slots from the tile's base; those whose rank is below k are kept.
+__global__ __launch_bounds__(kWaveBlock) void rk_keep(const RkTile* __restrict__ tiles,
+                                                      const RkLayer* __restrict__ layers,
+                                                      const RkSeg* __restrict__ seg, const uint32_t* __restrict__ mask,
+                                                      const uint32_t* __restrict__ tmask,
+                                                      const uint32_t* __restrict__ tbase,
+                                                      const uint32_t* __restrict__ tiebase,
+                                                      const uint32_t* __restrict__ ranks, uint32_t* __restrict__ kmask,
+                                                      uint32_t* __restrict__ kcnt, int64_t stride, int64_t top_total,
+                                                      int n_layers, int ntiles) {
+  const int ti = blockIdx.x * (kWaveBlock / 64) + (threadIdx.x >> 6);
+  if (ti >= ntiles) return;  // whole wave
+  const int lane = threadIdx.x & 63;
+  const RkTile t = tiles[ti];
   const int w = blockIdx.y;
   const RkLayer L = layers[t.layer];
   const int64_t s = int64_t(w) * n_layers + t.layer;
   const uint32_t need_t = seg[s].partial ? seg[s].need_t : 0u;
   const int nwords = (t.len + 31) >> 5;
-  const int q = threadIdx.x;
+  const int q = 2 * lane;
   const int64_t wi = ((int64_t(w) * stride + t.begin) >> 5) + q;
-  const int64_t trow = int64_t(w) * ntiles + blockIdx.x;
-  uint32_t word = q < nwords ? mask[wi] : 0u;
-  const uint32_t tw = q < nwords ? tmask[wi] : 0u;
-  uint32_t tr = tiebase[trow] + block_incl_scan(__popc(tw), lds) - __popc(tw);
-  for (uint32_t bits = tw; bits != 0u; bits &= bits - 1u) {
-    if (tr < need_t) word |= 1u << __builtin_ctz(bits);
-    ++tr;
+  const int64_t trow = int64_t(w) * ntiles + ti;
+  uint32_t m0 = 0, m1 = 0, t0 = 0, t1 = 0;
+  if (q < nwords) {
+    m0 = mask[wi];
+    t0 = tmask[wi];
   }
-  const uint32_t c = __popc(word);
-  uint32_t slot = tbase[trow] + block_incl_scan(c, lds) - c;
+  if (q + 1 < nwords) {
+    m1 = mask[wi + 1];
+    t1 = tmask[wi + 1];
+  }
+  const uint32_t ct = __popc(t0) + __popc(t1);
+  uint32_t tr = tiebase[trow] + wave_incl_scan(ct) - ct;
+  m0 |= bits_below(t0, tr, need_t);
+  m1 |= bits_below(t1, tr, need_t);
+  const uint32_t c = __popc(m0) + __popc(m1);
+  uint32_t slot = tbase[trow] + wave_incl_scan(c) - c;
   const uint32_t* rk = ranks + int64_t(w) * top_total + L.top_off;
-  uint32_t kept = 0;
-  for (uint32_t bits = word; bits != 0u; bits &= bits - 1u) {
-    const int j = __builtin_ctz(bits);
-    if (int64_t(slot) < L.top && int64_t(rk[slot]) < L.keep) kept |= 1u << j;
-    ++slot;
-  }
-  if (q < nwords) kmask[wi] = kept;
-  const uint32_t tot = block_total(__popc(kept), lds);
-  if (threadIdx.x == 0) kcnt[trow] = tot;
+  uint32_t k0 = 0, k1 = 0;
+  for (uint32_t bits = m0; bits != 0u; bits &= bits - 1u, ++slot)
+    if (int64_t(slot) < L.top && int64_t(rk[slot]) < L.keep) k0 |= bits & (0u - bits);
+  for (uint32_t bits = m1; bits != 0u; bits &= bits - 1u, ++slot)
+    if (int64_t(slot) < L.top && int64_t(rk[slot]) < L.keep) k1 |= bits & (0u - bits);
+  if (q < nwords) kmask[wi] = k0;
+  if (q + 1 < nwords) kmask[wi + 1] = k1;
+  const uint32_t tot = wave_sum(__popc(k0) + __popc(k1));
+  if (lane == 0) kcnt[trow] = tot;
 }
 
-__global__ __launch_bounds__(kWordThreads) void rk_emit(const RkTile* __restrict__ tiles,
-                                                        const RkLayer* __restrict__ layers,
-                                                        uint32_t* __restrict__ kmask, const uint32_t* __restrict__ kbase,
-                                                        float* __restrict__ E, int32_t* __restrict__ index,
-                                                        float* __restrict__ value, uint32_t* __restrict__ kpos,
-                                                        int64_t stride, int64_t keep_total, int ntiles) {
-  __shared__ uint32_t lds[16];
-  const RkTile t = tiles[blockIdx.x];
+// One wave per tile, two mask words per lane: the kept entries in index order take list
+// positions from the tile's base; the first k are sent (index, value), their error is
+// set to zero, and the kept mask keeps only them; each word records its first position.
+__global__ __launch_bounds__(kWaveBlock) void rk_emit(const RkTile* __restrict__ tiles,
+                                                      const RkLayer* __restrict__ layers, uint32_t* __restrict__ kmask,
+                                                      const uint32_t* __restrict__ kbase, float* __restrict__ E,
+                                                      int32_t* __restrict__ index, float* __restrict__ value,
+                                                      uint32_t* __restrict__ kpos, int64_t stride, int64_t keep_total,
+                                                      int ntiles) {
+  const int ti = blockIdx.x * (kWaveBlock / 64) + (threadIdx.x >> 6);
+  if (ti >= ntiles) return;  // whole wave
+  const int lane = threadIdx.x & 63;
+  const RkTile t = tiles[ti];
   const int w = blockIdx.y;
   const RkLayer L = layers[t.layer];
   const int nwords = (t.len + 31) >> 5;
-  const int q = threadIdx.x;
+  const int q = 2 * lane;
   const int64_t wi = ((int64_t(w) * stride + t.begin) >> 5) + q;
-  const uint32_t word = q < nwords ? kmask[wi] : 0u;
-  const uint32_t c = __popc(word);
-  const uint32_t first = kbase[int64_t(w) * ntiles + blockIdx.x] + block_incl_scan(c, lds) - c;
+  const uint32_t k0 = q < nwords ? kmask[wi] : 0u;
+  const uint32_t k1 = q + 1 < nwords ? kmask[wi + 1] : 0u;
+  const uint32_t c = __popc(k0) + __popc(k1);
+  const uint32_t first = kbase[int64_t(w) * ntiles + ti] + wave_incl_scan(c) - c;
   if (q >= nwords) return;
   int32_t* ix = index + int64_t(w) * keep_total + L.keep_off;
   float* vx = value + int64_t(w) * keep_total + L.keep_off;
   float* M = E + int64_t(w) * stride + L.offset;
-  uint32_t pos = first, sent = 0;
-  for (uint32_t bits = word; bits != 0u; bits &= bits - 1u) {
-    const int j = __builtin_ctz(bits);
-    if (int64_t(pos) < L.keep) {
-      const int32_t idx = t.chunk * kTile + q * 32 + j;
-      ix[pos] = idx;
-      vx[pos] = M[idx];
-      M[idx] = 0.f;
-      sent |= 1u << j;
+  const int32_t e0 = t.chunk * kTile + q * 32;
+  uint32_t pos = first;
+  uint32_t sent[2] = {0u, 0u};
+  const uint32_t kw[2] = {k0, k1};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (h == 1 && q + 1 < nwords) kpos[wi + 1] = pos;
+    for (uint32_t bits = kw[h]; bits != 0u; bits &= bits - 1u, ++pos) {
+      if (int64_t(pos) < L.keep) {
+        const int32_t idx = e0 + 32 * h + __builtin_ctz(bits);
+        ix[pos] = idx;
+        vx[pos] = M[idx];
+        M[idx] = 0.f;
+        sent[h] |= bits & (0u - bits);
+      }
     }
-    ++pos;
   }
-  if (sent != word) kmask[wi] = sent;
   kpos[wi] = first;
+  if (sent[0] != k0) kmask[wi] = sent[0];
+  if (q + 1 < nwords && sent[1] != k1) kmask[wi + 1] = sent[1];
 }
 
 // Dense update, one thread per mask word: for each worker in order, the word's sent
@@ -878,6 +1045,8 @@ extern "C" psgd_status psgd_rtopk_plan_create(const psgd_layer* layers, int32_t 
     ws = a256(ws + uint64_t(plan->n_seg) * kBins3 * 4);
     plan->ws_seg = ws;
     ws = a256(ws + uint64_t(plan->n_seg) * sizeof(RkSeg));
+    plan->ws_pred = ws;  // digit-1 bin of the previous step per segment (a hint only)
+    ws = a256(ws + uint64_t(plan->n_seg) * 4);
     plan->ws_cand = ws;  // same layout as the error buffer, one uint32 per element
     ws = a256(ws + W * uint64_t(plan->worker_stride) * 4);
     uint64_t* word_arrays[] = {&plan->ws_mask, &plan->ws_tmask, &plan->ws_kmask, &plan->ws_kpos};
@@ -885,8 +1054,13 @@ extern "C" psgd_status psgd_rtopk_plan_create(const psgd_layer* layers, int32_t 
       *a = ws;
       ws = a256(ws + W * words * 4);
     }
-    uint64_t* tile_arrays[] = {&plan->ws_ccnt, &plan->ws_tcnt, &plan->ws_ttie, &plan->ws_tiebase,
-                               &plan->ws_tbase, &plan->ws_kcnt, &plan->ws_kbase};
+    uint64_t* wave_arrays[] = {&plan->ws_ccnt4, &plan->ws_tcnt4};  // one count per wave of a tile
+    for (uint64_t* a : wave_arrays) {
+      *a = ws;
+      ws = a256(ws + W * ntiles * 16);
+    }
+    uint64_t* tile_arrays[] = {&plan->ws_tfin, &plan->ws_ttie, &plan->ws_tiebase, &plan->ws_tbase, &plan->ws_kcnt,
+                               &plan->ws_kbase};
     for (uint64_t* a : tile_arrays) {
       *a = ws;
       ws = a256(ws + W * ntiles * 4);
@@ -1037,10 +1211,12 @@ extern "C" psgd_status psgd_rtopk_step(psgd_rtopk_plan* plan, const void* grads,
   uint32_t* hist2 = u32(plan->ws_hist2);
   uint32_t* hist3 = u32(plan->ws_hist3);
   RkSeg* seg = reinterpret_cast<RkSeg*>(ws + plan->ws_seg);
+  uint32_t* pred = u32(plan->ws_pred);
   uint32_t* cand = u32(plan->ws_cand);
   uint32_t *mask = u32(plan->ws_mask), *tmask = u32(plan->ws_tmask), *kmask = u32(plan->ws_kmask);
   uint32_t* kpos = u32(plan->ws_kpos);
-  uint32_t *ccnt = u32(plan->ws_ccnt), *tcnt = u32(plan->ws_tcnt), *ttie = u32(plan->ws_ttie);
+  uint32_t *ccnt4 = u32(plan->ws_ccnt4), *tcnt4 = u32(plan->ws_tcnt4), *tfin = u32(plan->ws_tfin);
+  uint32_t* ttie = u32(plan->ws_ttie);
   uint32_t *tiebase = u32(plan->ws_tiebase), *tbase = u32(plan->ws_tbase);
   uint32_t *kcnt = u32(plan->ws_kcnt), *kbase = u32(plan->ws_kbase);
 
@@ -1058,33 +1234,42 @@ extern "C" psgd_status psgd_rtopk_step(psgd_rtopk_plan* plan, const void* grads,
   const RkChunk* C = dt.chunks;
 
   if ((s = launch(plan, kZero, rk_zero, dim3(zblocks), dim3(256), st, hist1, nzero)) != PSGD_OK) return s;
+  const uint32_t* cpred = pred;
   if (plan->dtype == PSGD_BF16)
     s = launch(plan, kEfHist, rk_ef_hist<uint16_t>, tgrid, dim3(kTileThreads), st, T,
-               static_cast<const uint16_t*>(grads), errors, hist1, sstride, nl);
+               static_cast<const uint16_t*>(grads), errors, cpred, hist1, hist2, mask, tmask, tcnt4, cand, ccnt4,
+               sstride, nl, ntiles);
   else
     s = launch(plan, kEfHist, rk_ef_hist<float>, tgrid, dim3(kTileThreads), st, T, static_cast<const float*>(grads),
-               errors, hist1, sstride, nl);
+               errors, cpred, hist1, hist2, mask, tmask, tcnt4, cand, ccnt4, sstride, nl, ntiles);
   if (s != PSGD_OK) return s;
-  if ((s = launch(plan, kSelect, rk_select, sgrid, dim3(kSelThreads), st, L, static_cast<const uint32_t*>(hist1), seg,
-                  nl)) != PSGD_OK)
+  if ((s = launch(plan, kSelect, rk_select, sgrid, dim3(kSelThreads), st, L, static_cast<const uint32_t*>(hist1),
+                  hist2, pred, seg, nl)) != PSGD_OK)
     return s;
   if ((s = launch(plan, kMark, rk_mark, tgrid, dim3(kTileThreads), st, T, static_cast<const float*>(errors),
-                  static_cast<const RkSeg*>(seg), hist2, mask, tmask, tcnt, ttie, cand, ccnt, sstride, nl, ntiles)) !=
+                  static_cast<const RkSeg*>(seg), hist2, mask, tmask, tcnt4, cand, ccnt4, sstride, nl, ntiles)) !=
       PSGD_OK)
     return s;
-  if ((s = launch(plan, kLevel3, rk_level3, cgrid, dim3(kSelThreads), st, C, T, L, static_cast<const RkSeg*>(seg),
-                  static_cast<const uint32_t*>(hist2), hist3, static_cast<const uint32_t*>(cand),
-                  static_cast<const uint32_t*>(ccnt), sstride, nl, ntiles)) != PSGD_OK)
+  if ((s = launch(plan, kPick2, rk_pick2, sgrid, dim3(kSelThreads), st, static_cast<const uint32_t*>(hist2), seg,
+                  plan->n_seg)) != PSGD_OK)
     return s;
-  if ((s = launch(plan, kFinal, rk_final, cgrid, dim3(kSelThreads), st, C, T, L, seg,
-                  static_cast<const uint32_t*>(hist2), static_cast<const uint32_t*>(hist3),
-                  static_cast<const uint32_t*>(cand), static_cast<const uint32_t*>(ccnt), mask, tmask, tcnt, ttie,
+  if ((s = launch(plan, kLevel3, rk_level3, cgrid, dim3(kSelThreads), st, C, T, L, static_cast<const RkSeg*>(seg),
+                  hist3, static_cast<const uint32_t*>(cand), static_cast<const uint32_t*>(ccnt4), sstride, nl,
+                  ntiles)) != PSGD_OK)
+    return s;
+  if ((s = launch(plan, kRule, rk_rule, sgrid, dim3(kSelThreads), st, static_cast<const uint32_t*>(hist3), seg)) !=
+      PSGD_OK)
+    return s;
+  if ((s = launch(plan, kFinal, rk_final, cgrid, dim3(kSelThreads), st, C, T, L, static_cast<const RkSeg*>(seg),
+                  static_cast<const uint32_t*>(cand), static_cast<const uint32_t*>(ccnt4), mask, tmask, tfin, ttie,
                   sstride, nl, ntiles)) != PSGD_OK)
     return s;
-  if ((s = launch(plan, kScanTop, rk_scan_top, sgrid, dim3(kSegThreads), st, L, static_cast<const uint32_t*>(tcnt),
-                  static_cast<const uint32_t*>(ttie), tbase, tiebase, seg, nl, ntiles)) != PSGD_OK)
+  if ((s = launch(plan, kScanTop, rk_scan_top, sgrid, dim3(kSegThreads), st, L, static_cast<const uint32_t*>(tcnt4),
+                  static_cast<const uint32_t*>(tfin), static_cast<const uint32_t*>(ttie), tbase, tiebase, seg, nl,
+                  ntiles)) != PSGD_OK)
     return s;
-  if ((s = launch(plan, kKeep, rk_keep, tgrid, dim3(kWordThreads), st, T, L, static_cast<const RkSeg*>(seg),
+  const dim3 wgrid(static_cast<unsigned>((ntiles + kWaveBlock / 64 - 1) / (kWaveBlock / 64)), static_cast<unsigned>(W));
+  if ((s = launch(plan, kKeep, rk_keep, wgrid, dim3(kWaveBlock), st, T, L, static_cast<const RkSeg*>(seg),
                   static_cast<const uint32_t*>(mask), static_cast<const uint32_t*>(tmask),
                   static_cast<const uint32_t*>(tbase), static_cast<const uint32_t*>(tiebase), ranks, kmask, kcnt,
                   sstride, plan->top_total, nl, ntiles)) != PSGD_OK)
@@ -1092,7 +1277,7 @@ extern "C" psgd_status psgd_rtopk_step(psgd_rtopk_plan* plan, const void* grads,
   if ((s = launch(plan, kScanKept, rk_scan_kept, sgrid, dim3(kSegThreads), st, L, static_cast<const uint32_t*>(kcnt),
                   kbase, seg, index, value, plan->keep_total, nl, ntiles)) != PSGD_OK)
     return s;
-  if ((s = launch(plan, kEmit, rk_emit, tgrid, dim3(kWordThreads), st, T, L, kmask,
+  if ((s = launch(plan, kEmit, rk_emit, wgrid, dim3(kWaveBlock), st, T, L, kmask,
                   static_cast<const uint32_t*>(kbase), errors, index, value, kpos, sstride, plan->keep_total,
                   ntiles)) != PSGD_OK)
     return s;

@@ -98,8 +98,8 @@ psgd_status psgd_rtopk_step(psgd_rtopk_plan* plan, const void* grads, float* err
                             int32_t* index, float* value, float* update, void* workspace, void* stream);
 
 /* Kernel timing as psgd_plan_set_timing / psgd_plan_kernel_stats.  Kernel names:
- * "rk_zero", "rk_ef_hist", "rk_select", "rk_mark", "rk_level3", "rk_final", "rk_scan_top",
- * "rk_keep", "rk_scan_kept", "rk_emit", "rk_update". */
+ * "rk_zero", "rk_ef_hist", "rk_select", "rk_mark", "rk_pick2", "rk_level3", "rk_rule",
+ * "rk_final", "rk_scan_top", "rk_keep", "rk_scan_kept", "rk_emit", "rk_update". */
 psgd_status psgd_rtopk_plan_set_timing(psgd_rtopk_plan* plan, int32_t enable);
 psgd_status psgd_rtopk_plan_kernel_stats(psgd_rtopk_plan* plan, psgd_kernel_stat* out, int32_t capacity,
                                          int32_t* count, int32_t reset);

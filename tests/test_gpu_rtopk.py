@@ -282,8 +282,8 @@ def test_timing_reports_every_kernel():
     run.step()
     run.step()
     stats = P.psgd_rtopk_plan_kernel_stats(run.plan, reset=True)
-    assert set(stats) == {"rk_zero", "rk_ef_hist", "rk_select", "rk_mark", "rk_level3", "rk_final",
-                          "rk_scan_top", "rk_keep", "rk_scan_kept", "rk_emit", "rk_update"}
+    assert set(stats) == {"rk_zero", "rk_ef_hist", "rk_select", "rk_mark", "rk_pick2", "rk_level3", "rk_rule",
+                          "rk_final", "rk_scan_top", "rk_keep", "rk_scan_kept", "rk_emit", "rk_update"}
     assert all(n == 2 and ms > 0 for n, ms in stats.values())
 
 
