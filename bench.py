@@ -132,9 +132,69 @@ def cpu_baseline(wl, seconds: float) -> dict:
     t_step = el / steps
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     gbytes = wl.workers * wl.numel() * 4 / 1e9
+    # the same oracle on one thread, one whole step
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        t1 = time.perf_counter()
+        O.compress_layers(layers)
+        t_one = time.perf_counter() - t1
     return {"value": round(gbytes / t_step, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "value_1thread": round(gbytes / t_one, 4),
             "sample": f"{steps} whole step(s) of the same workload (all 21 matrices and 41 tensors, "
-                      f"W=16, r=2), numpy float64 oracle, {t_step:.2f} s per step; BLAS threads = cores"}
+                      f"W=16, r=2), numpy float64 oracle, {t_step:.2f} s per step; BLAS threads = cores; "
+                      f"value_1thread: one more step on one thread, {t_one:.2f} s"}
+
+
+def timed_steps(torch, step, steps: int, stream):
+    """Run `steps` calls of step() with an event recorded on `stream` between calls.
+    Returns (mean ms over the whole region, median ms, minimum ms)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    return ev[0].elapsed_time(ev[steps]) / steps, per[len(per) // 2], per[0]
+
+
+def config_timings(torch, psgd, WL, dev, steps: int) -> dict:
+    """Context lines for the other configurations (not the metric): the single small
+    matrix as latency, the LSTM shapes and the bandwidth-stress set, deferred mode."""
+    out = {}
+    for name, rank, nsteps in (("single", 1, 10 * steps), ("lstm", 4, steps), ("stress", 2, max(3, steps // 10))):
+        wl = WL.workload(name, rank=rank)
+        shapes = [s for _, s in wl.shapes]
+        W = wl.workers
+        plan = psgd.psgd_plan_create(shapes, wl.rank, W, psgd.PSGD_F32, psgd.PSGD_FLAG_DEFERRED_ERROR)
+        s = plan.sizes
+        ld = s["worker_stride"]
+        grads = torch.zeros((W, ld), dtype=torch.float32, device=dev)
+        errors = torch.zeros((W, ld), dtype=torch.float32, device=dev)
+        q = torch.zeros(s["q_elems"], dtype=torch.float32, device=dev)
+        p = torch.zeros(s["p_elems"], dtype=torch.float32, device=dev)
+        update = torch.zeros(ld, dtype=torch.float32, device=dev)
+        workspace = torch.empty(s["workspace_bytes"], dtype=torch.uint8, device=dev)
+        WL.device_grads(wl, 0, [(L.offset, L.rows, L.cols) for L in plan.layers], grads)
+        qh = psgd.pack_factors(plan, {i: WL.q0(wl, i) for i, L in enumerate(plan.layers) if L.compressed}, "q")
+        q.copy_(torch.from_numpy(qh).to(dev))
+        stream = torch.cuda.current_stream(dev)
+
+        def step():
+            psgd.psgd_compress_step(plan, grads, errors, q, p, update, workspace, stream)
+
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize(dev)
+        ms, med, mn = timed_steps(torch, step, nsteps, stream)
+        out[name] = {"workers": W, "rank": wl.rank, "params": s["numel"], "steps": nsteps,
+                     "ms_per_step": round(ms, 4), "ms_median": round(med, 4), "ms_min": round(mn, 4),
+                     "grad_GBps": round(W * s["numel"] * 4 / (ms * 1e-3) / 1e9, 1),
+                     "pct_hbm_peak": round(100.0 * s["model_bytes"] / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 2)}
+        del grads, errors, q, p, update, workspace, plan
+        torch.cuda.empty_cache()
+    out["single"]["role"] = "latency (one 256x128 matrix, W=1, r=1; launch-bound)"
+    return out
 
 
 def main() -> int:
@@ -144,6 +204,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline sample length")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the context timings of the other configurations")
     ap.add_argument("--mode", choices=["all", "carry", "plain", "deferred", "rtopk"], default="all",
                     help="plan variants to time (profiling runs use one); rtopk times only the rTop-k step")
     ap.add_argument("--primary", choices=["carry", "deferred", "plain"], default="deferred",
@@ -193,14 +254,8 @@ def main() -> int:
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize(dev)
-        # timed region 1: the step as a caller runs it
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
-        for _ in range(args.steps):
-            step()
-        t1.record(stream)
-        torch.cuda.synchronize(dev)
-        ms = t0.elapsed_time(t1) / args.steps
+        # timed region 1: the step as a caller runs it (an event between steps)
+        ms, ms_med, ms_min = timed_steps(torch, step, args.steps, stream)
         # timed region 2: the same steps with every kernel bracketed by HIP events
         psgd.psgd_plan_set_timing(plan, True)
         psgd.psgd_plan_kernel_stats(plan, reset=True)
@@ -224,7 +279,8 @@ def main() -> int:
             kernels[name] = entry
         grad_bytes = W * s["numel"] * 4
         del grads, errors, workspace
-        return {"ms": ms, "ms_timed": ms_timed, "kernels": kernels, "kb": kb, "sizes": s,
+        return {"ms": ms, "ms_med": ms_med, "ms_min": ms_min, "ms_timed": ms_timed, "kernels": kernels, "kb": kb,
+                "sizes": s,
                 "value": grad_bytes / (ms * 1e-3) / 1e9, "grad_bytes": grad_bytes,
                 "pct": 100.0 * s["model_bytes"] / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9)}
 
@@ -276,13 +332,7 @@ def main() -> int:
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize(dev)
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
-        for _ in range(args.steps):
-            step()
-        t1.record(stream)
-        torch.cuda.synchronize(dev)
-        ms = t0.elapsed_time(t1) / args.steps
+        ms, ms_med, ms_min = timed_steps(torch, step, args.steps, stream)
         psgd.psgd_rtopk_plan_set_timing(plan, True)
         psgd.psgd_rtopk_plan_kernel_stats(plan, reset=True)
         for _ in range(args.steps):
@@ -309,6 +359,8 @@ def main() -> int:
             "value": round(grad_bytes / (ms * 1e-3) / 1e9, 2),
             "unit": "GB/s",
             "ms_per_step": round(ms, 4),
+            "ms_per_step_median": round(ms_med, 4),
+            "ms_per_step_min": round(ms_min, 4),
             "pct_hbm_peak": round(100.0 * s["model_bytes"] / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 2),
             "model_bytes_per_step": s["model_bytes"],
             "config": {"workload": "resnet18_cifar_shapes", "workers": W, "tensors": s["n_layers"],
@@ -348,6 +400,8 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_median": round(main_run["ms_med"], 4),
+        "ms_per_step_min": round(main_run["ms_min"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -373,6 +427,8 @@ def main() -> int:
                        for n, r in results.items() if n != primary}
     if args.mode == "all":
         out["rtopk"] = measure_rtopk()
+        if not args.no_configs:
+            out["other_configs"] = config_timings(torch, psgd, WL, dev, args.steps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)

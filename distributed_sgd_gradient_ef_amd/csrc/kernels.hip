@@ -42,7 +42,9 @@ namespace psgd {
 namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 struct bf16 {
   unsigned short bits;
@@ -55,10 +57,13 @@ enum FirstPass { kFpMean = 0, kFpCarry = 1, kFpDefer = 2 };
 // Gradients and errors are touched once per pass and never reused from cache, so the
 // worker passes load and store them non-temporally; buffers that a later kernel of the
 // same step reads again (Mbar, the carried error mean) use ordinary accesses.
+// V elements per lane: 4 when a matrix's column count is a multiple of 4 (rows 16-byte
+// aligned), 2 when it is even (rows 8-byte aligned), else 1.
 template <int V>
-using vec_t = std::conditional_t<V == 4, f4, float>;
+using vec_t = std::conditional_t<V == 4, f4, std::conditional_t<V == 2, f2, float>>;
 
 __device__ __forceinline__ float lane(const f4& x, int q) { return x[q]; }
+__device__ __forceinline__ float lane(const f2& x, int q) { return x[q]; }
 __device__ __forceinline__ float lane(const float& x, int) { return x; }
 
 __device__ __forceinline__ f4 widen(const u16x4 v) {
@@ -70,10 +75,19 @@ __device__ __forceinline__ f4 widen(const u16x4 v) {
   return r;
 }
 
+__device__ __forceinline__ f2 widen(const u16x2 v) {
+  f2 r;
+  r.x = __uint_as_float(uint32_t(v.x) << 16);
+  r.y = __uint_as_float(uint32_t(v.y) << 16);
+  return r;
+}
+
 template <int V>
 __device__ __forceinline__ vec_t<V> ldv(const float* p) {
   if constexpr (V == 4)
     return *reinterpret_cast<const f4*>(p);
+  else if constexpr (V == 2)
+    return *reinterpret_cast<const f2*>(p);
   else
     return *p;
 }
@@ -82,6 +96,8 @@ template <int V>
 __device__ __forceinline__ vec_t<V> ld_nt(const float* p) {
   if constexpr (V == 4)
     return __builtin_nontemporal_load(reinterpret_cast<const f4*>(p));
+  else if constexpr (V == 2)
+    return __builtin_nontemporal_load(reinterpret_cast<const f2*>(p));
   else
     return __builtin_nontemporal_load(p);
 }
@@ -90,6 +106,8 @@ template <int V>
 __device__ __forceinline__ vec_t<V> ld_nt(const bf16* p) {
   if constexpr (V == 4)
     return widen(__builtin_nontemporal_load(reinterpret_cast<const u16x4*>(p)));
+  else if constexpr (V == 2)
+    return widen(__builtin_nontemporal_load(reinterpret_cast<const u16x2*>(p)));
   else
     return __uint_as_float(uint32_t(__builtin_nontemporal_load(reinterpret_cast<const unsigned short*>(p))) << 16);
 }
@@ -98,6 +116,8 @@ template <int V>
 __device__ __forceinline__ void st(float* p, const vec_t<V> v) {
   if constexpr (V == 4)
     *reinterpret_cast<f4*>(p) = v;
+  else if constexpr (V == 2)
+    *reinterpret_cast<f2*>(p) = v;
   else
     *p = v;
 }
@@ -106,6 +126,8 @@ template <int V>
 __device__ __forceinline__ void st_nt(float* p, const vec_t<V> v) {
   if constexpr (V == 4)
     __builtin_nontemporal_store(v, reinterpret_cast<f4*>(p));
+  else if constexpr (V == 2)
+    __builtin_nontemporal_store(v, reinterpret_cast<f2*>(p));
   else
     __builtin_nontemporal_store(v, p);
 }
@@ -240,6 +262,8 @@ template <int V>
 __device__ __forceinline__ vec_t<V> pq_row(const float (&pr)[4], const float (&qv)[V][4], int R) {
   if constexpr (V == 4)
     return f4{pq_dot(pr, qv[0], R), pq_dot(pr, qv[1], R), pq_dot(pr, qv[2], R), pq_dot(pr, qv[3], R)};
+  else if constexpr (V == 2)
+    return f2{pq_dot(pr, qv[0], R), pq_dot(pr, qv[1], R)};
   else
     return pq_dot(pr, qv[0], R);
 }
@@ -441,12 +465,14 @@ __global__ __launch_bounds__(kStreamThreads) void k_first(const UpdTile* __restr
     return;
   }
   const MatInfo mi = mats[t.mat];
-  if (mi.vec4)
-    first_matrix_tile<4, GT, WT, FP>(t, mi, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, W, ld, R, inv_w,
-                                     offset_valid);
-  else
-    first_matrix_tile<1, GT, WT, FP>(t, mi, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, W, ld, R, inv_w,
-                                     offset_valid);
+  switch (mi.vw) {
+    case 4: first_matrix_tile<4, GT, WT, FP>(t, mi, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, W, ld, R, inv_w,
+                                     offset_valid); break;
+    case 2: first_matrix_tile<2, GT, WT, FP>(t, mi, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, W, ld, R, inv_w,
+                                     offset_valid); break;
+    default: first_matrix_tile<1, GT, WT, FP>(t, mi, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, W, ld, R, inv_w,
+                                     offset_valid); break;
+  }
 }
 
 // ------------------------------------------------------------------ extra power iterations
@@ -491,10 +517,11 @@ __global__ __launch_bounds__(kStreamThreads) void k_p_mbar(const UpdTile* __rest
   const UpdTile t = tiles[blockIdx.x];
   if (t.mat < 0) return;
   const MatInfo mi = mats[t.mat];
-  if (mi.vec4)
-    pbar_mbar_tile<4>(t, mi, Mbar, Qin, Ppart, R);
-  else
-    pbar_mbar_tile<1>(t, mi, Mbar, Qin, Ppart, R);
+  switch (mi.vw) {
+    case 4: pbar_mbar_tile<4>(t, mi, Mbar, Qin, Ppart, R); break;
+    case 2: pbar_mbar_tile<2>(t, mi, Mbar, Qin, Ppart, R); break;
+    default: pbar_mbar_tile<1>(t, mi, Mbar, Qin, Ppart, R); break;
+  }
 }
 
 // ------------------------------------------------------------------ Gram-Schmidt
@@ -506,8 +533,8 @@ __global__ __launch_bounds__(kStreamThreads) void k_p_mbar(const UpdTile* __rest
 // fresh column and its projection on column 0 share one reduction (both use the
 // unmodified column).
 // Matrices with at most kMgsRowsPerThread rows per thread keep their rows in registers;
-// taller ones work through the output buffer, each thread on its own rows.  `P2`, if
-// set, receives a copy of the result.
+// taller ones take two passes through the output buffer (below).  `P2`, if set,
+// receives a copy of the result.
 constexpr int kMgsRowsPerThread = 4;
 
 template <int R>
@@ -592,50 +619,72 @@ __global__ __launch_bounds__(kMgsThreads) void k_mgs(const MatInfo* __restrict__
     return;
   }
 
-  // Tall matrices: the same steps through the output buffer.
+  // Tall matrices: two passes over the rows.  Pass 1 forms P-bar (kept in the output)
+  // and its Gram matrix in double.  One thread then takes the same Gram-Schmidt in the
+  // R x R Gram space -- the projection coefficients R_lk on the kept columns l < k and the
+  // residual norm sqrt(G_kk - sum_l R_lk^2), with the same drop rule -- and forms
+  // T = R^-1 (zero columns for dropped ones).  Pass 2 writes P = P-bar T.
+  constexpr int NG = R * (R + 1) / 2;
+  double g[NG];
+#pragma unroll
+  for (int a = 0; a < NG; ++a) g[a] = 0.0;
   for (int i = threadIdx.x; i < n; i += bs) {
     float acc[R];
     pbar_row<R>(acc, src, strip_stride, nst, i);
+    int a = 0;
 #pragma unroll
-    for (int k = 0; k < R; ++k) dst[int64_t(i) * R + k] = acc[k];
+    for (int k = 0; k < R; ++k) {
+      dst[int64_t(i) * R + k] = acc[k];
+#pragma unroll
+      for (int l = k; l < R; ++l) g[a++] += double(acc[k]) * double(acc[l]);
+    }
   }
-  for (int k = 0; k < R; ++k) {
-    double s = 0.0, c = 0.0;
-    for (int i = threadIdx.x; i < n; i += bs) {
-      const int64_t o = int64_t(i) * R;
-      const double v = dst[o + k];
-      s += v * v;
-      if (k > 0) c += double(dst[o]) * v;
-    }
-    block_sum2(s, c, red);
-    const double before = sqrt(s);
-    double after = before;
-    if (k > 0) {
+#pragma unroll
+  for (int a = 0; a < NG; ++a) g[a] = block_sum(g[a], red);
+  __shared__ double T[R][R];
+  if (threadIdx.x == 0) {
+    auto G = [&](int k, int l) {  // Gram entry (k <= l) in the packed upper triangle
+      return g[k * R - k * (k - 1) / 2 + (l - k)];
+    };
+    double Rm[R][R];
+    bool kept[R];
+    for (int k = 0; k < R; ++k) {
+      const double before = sqrt(G(k, k));
+      double ss = G(k, k);
       for (int l = 0; l < k; ++l) {
-        if (l > 0) {
-          c = 0.0;
-          for (int i = threadIdx.x; i < n; i += bs)
-            c += double(dst[int64_t(i) * R + l]) * double(dst[int64_t(i) * R + k]);
-          c = block_sum(c, red);
+        double r = 0.0;
+        if (kept[l]) {
+          r = G(l, k);
+          for (int m = 0; m < l; ++m) r -= Rm[m][l] * Rm[m][k];
+          r /= Rm[l][l];
         }
-        for (int i = threadIdx.x; i < n; i += bs) {
-          const int64_t o = int64_t(i) * R;
-          dst[o + k] = float(double(dst[o + k]) - c * double(dst[o + l]));
-        }
+        Rm[l][k] = r;
+        ss -= r * r;
       }
-      double s2 = 0.0;
-      for (int i = threadIdx.x; i < n; i += bs) {
-        const double v = dst[int64_t(i) * R + k];
-        s2 += v * v;
+      const double after = sqrt(ss > 0.0 ? ss : 0.0);
+      kept[k] = after > 0.0 && after > 1e-4 * before;
+      Rm[k][k] = after;
+      for (int l = 0; l < R; ++l) T[l][k] = 0.0;
+      if (kept[k]) {
+        T[k][k] = 1.0 / after;
+        for (int l = 0; l < k; ++l)
+          for (int m = 0; m < R; ++m) T[m][k] -= Rm[l][k] * T[m][l] / after;
       }
-      after = sqrt(block_sum(s2, red));
     }
-    const double scale = (after > 0.0 && after > 1e-4 * before) ? 1.0 / after : 0.0;
-    for (int i = threadIdx.x; i < n; i += bs) {
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += bs) {
+    double pb[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k) pb[k] = dst[int64_t(i) * R + k];
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      double v = 0.0;
+#pragma unroll
+      for (int l = 0; l <= k; ++l) v += pb[l] * T[l][k];
       const int64_t o = int64_t(i) * R + k;
-      const float v = scale > 0.0 ? float(double(dst[o]) * scale) : 0.f;
-      dst[o] = v;
-      if (P2 != nullptr) P2[mi.p_off + o] = v;
+      dst[o] = float(v);
+      if (P2 != nullptr) P2[mi.p_off + o] = float(v);
     }
   }
 }
@@ -655,7 +704,7 @@ __global__ __launch_bounds__(kQThreads) void k_q_partial(const QTile* __restrict
   const float* Pm = P + mi.p_off;
   const float* base = Mbar + mi.offset;
   float* out = Qpart + mi.qpart_off + int64_t(t.blk) * cols * R;
-  if (mi.vec4) {
+  if (mi.vw == 4) {
     const int j = t.col_begin + int(threadIdx.x) * 4;
     if (j >= t.col_end) return;
     float acc[4][R];
@@ -759,10 +808,11 @@ __global__ __launch_bounds__(kStreamThreads) void k_apply(
     return;
   }
   const MatInfo mi = mats[t.mat];
-  if (mi.vec4)
-    apply_matrix_tile<4, GT, WT>(t, mi, G, E, P, Q, update, mom, x, ebar, W, ld, R, mode, lr, mu, inv_w);
-  else
-    apply_matrix_tile<1, GT, WT>(t, mi, G, E, P, Q, update, mom, x, ebar, W, ld, R, mode, lr, mu, inv_w);
+  switch (mi.vw) {
+    case 4: apply_matrix_tile<4, GT, WT>(t, mi, G, E, P, Q, update, mom, x, ebar, W, ld, R, mode, lr, mu, inv_w); break;
+    case 2: apply_matrix_tile<2, GT, WT>(t, mi, G, E, P, Q, update, mom, x, ebar, W, ld, R, mode, lr, mu, inv_w); break;
+    default: apply_matrix_tile<1, GT, WT>(t, mi, G, E, P, Q, update, mom, x, ebar, W, ld, R, mode, lr, mu, inv_w); break;
+  }
 }
 
 // ------------------------------------------------------------------ deferred-error mode
@@ -806,10 +856,11 @@ __global__ __launch_bounds__(kUpdThreads) void k_update(
     return;
   }
   const MatInfo mi = mats[t.mat];
-  if (mi.vec4)
-    update_matrix_tile<4>(t, mi, P, Q, update, mom, x, R, mode, lr, mu);
-  else
-    update_matrix_tile<1>(t, mi, P, Q, update, mom, x, R, mode, lr, mu);
+  switch (mi.vw) {
+    case 4: update_matrix_tile<4>(t, mi, P, Q, update, mom, x, R, mode, lr, mu); break;
+    case 2: update_matrix_tile<2>(t, mi, P, Q, update, mom, x, R, mode, lr, mu); break;
+    default: update_matrix_tile<1>(t, mi, P, Q, update, mom, x, R, mode, lr, mu); break;
+  }
 }
 
 // out_w = errors_w - P_prev Q_prev^T for every compressed matrix (the plain error memory
@@ -843,10 +894,11 @@ __global__ __launch_bounds__(kStreamThreads) void k_materialize(
   const UpdTile t = tiles[blockIdx.x];
   if (t.mat < 0) return;
   const MatInfo mi = mats[t.mat];
-  if (mi.vec4)
-    materialize_tile<4>(t, mi, E, out, Pprev, Qprev, W, ld, R, offset_valid);
-  else
-    materialize_tile<1>(t, mi, E, out, Pprev, Qprev, W, ld, R, offset_valid);
+  switch (mi.vw) {
+    case 4: materialize_tile<4>(t, mi, E, out, Pprev, Qprev, W, ld, R, offset_valid); break;
+    case 2: materialize_tile<2>(t, mi, E, out, Pprev, Qprev, W, ld, R, offset_valid); break;
+    default: materialize_tile<1>(t, mi, E, out, Pprev, Qprev, W, ld, R, offset_valid); break;
+  }
 }
 
 // ------------------------------------------------------------------ calibration copy

@@ -108,10 +108,10 @@ extern "C" psgd_status psgd_plan_create(const psgd_layer* layers, int32_t n_laye
         nblk = std::min<int64_t>(nblk, kQMaxRowBlocks);
         mi.rows_per_blk = int32_t((rows + nblk - 1) / nblk);
         mi.nblk = int32_t((rows + mi.rows_per_blk - 1) / mi.rows_per_blk);
-        mi.vec4 = (cols % 4 == 0) ? 1 : 0;
+        mi.vw = (cols % 4 == 0) ? 4 : (cols % 2 == 0) ? 2 : 1;
         mi.qpart_off = qpart;
         qpart += int64_t(mi.nblk) * cols * r;
-        const int64_t strip_cols = int64_t(kStreamThreads) * (mi.vec4 ? 4 : 1);
+        const int64_t strip_cols = int64_t(kStreamThreads) * mi.vw;
         mi.nstrips = int32_t((cols + strip_cols - 1) / strip_cols);
         mi.ppart_off = plan->ppart_elems;
         plan->ppart_elems += int64_t(mi.nstrips) * rows * r;
@@ -144,7 +144,7 @@ extern "C" psgd_status psgd_plan_create(const psgd_layer* layers, int32_t n_laye
       for (const psgd_layer_info& li : plan->layers) {
         if (li.compressed) {
           const MatInfo& m = plan->mats[size_t(li.matrix_index)];
-          const int32_t strip = threads * (m.vec4 ? 4 : 1);
+          const int32_t strip = threads * m.vw;
           for (int32_t r0 = 0; r0 < m.rows; r0 += rows_per_tile)
             for (int32_t c0 = 0; c0 < m.cols; c0 += strip) {
               UpdTile u{};
@@ -173,7 +173,7 @@ extern "C" psgd_status psgd_plan_create(const psgd_layer* layers, int32_t n_laye
     build_tiles(plan->utiles, kUpdRowsPerTile, kUpdThreads);
     for (size_t mi = 0; mi < plan->mats.size(); ++mi) {
       const MatInfo& m = plan->mats[mi];
-      const int32_t strip = kQThreads * (m.vec4 ? 4 : 1);
+      const int32_t strip = kQThreads * (m.vw == 4 ? 4 : 1);  // the Q pass has no 2-wide form
       for (int32_t b = 0; b < m.nblk; ++b)
         for (int32_t c = 0; c < m.cols; c += strip)
           plan->qtiles.push_back(QTile{int32_t(mi), b, c, std::min(m.cols, c + strip)});

@@ -49,7 +49,7 @@ struct MatInfo {
   int32_t rows, cols;
   int32_t rows_per_blk;  // rows summed into one Q partial
   int32_t nblk;          // number of Q partials (row blocks)
-  int32_t vec4;          // 1 if cols % 4 == 0 (rows are 16-byte aligned)
+  int32_t vw;            // elements per lane in the row passes: 4 if cols % 4 == 0, 2 if even, else 1
   int32_t nstrips;       // column strips of the worker passes (P-bar partials per row)
 };
 
