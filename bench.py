@@ -7,11 +7,12 @@ HBM, fp32.  One step = one psgd_compress_step over all tensors (EF add, P = M Q,
 mean, Gram-Schmidt, Q = M^T P, worker mean, decompress, new errors).  Inputs are
 synthetic (planted low-rank part + worker noise), drawn on the device before timing.
 
-Three plan variants are timed: "deferred" (PSGD_FLAG_DEFERRED_ERROR: one pass over the
+Four plan variants are timed: "deferred" (PSGD_FLAG_DEFERRED_ERROR: one pass over the
 workers' G and E per step; the error buffer holds M_w and the previous step's P Q^T is
 subtracted in the next step's pass), "carry" (PSGD_FLAG_CARRY_ERROR_MEAN: the plain error
 E'_w is written every step, and the next step's first pass reads only G plus the
-carried error mean) and "plain" (no cross-step state).  `value` is the --primary one.
+carried error mean), "plain" (no cross-step state) and "local" (PSGD_FLAG_LOCAL_Q_ERROR:
+each worker's error uses its own Q_w).  `value` is the --primary one.
 
 A second compressor is timed beside it ("rtopk" in the output): rTop-k with error
 feedback on the same shapes and W = 16, 1% of each tensor sent, drawn from its top 2%
@@ -60,6 +61,8 @@ def kernel_bytes(plan, dtype_bytes: int, variant: str) -> dict:
         "carry": W * gb + 8,
         # read G_w and E_w, write M_w on every worker, write Mbar once
         "deferred": W * (gb + 8) + 4,
+        # as plain
+        "local": W * (gb + 4) + 4,
     }[variant]
     return {
         # 1-D tensors: read G_w on every worker, write the mean once
@@ -71,6 +74,8 @@ def kernel_bytes(plan, dtype_bytes: int, variant: str) -> dict:
         "k_apply": (W * (gb + 8) + (8 if variant == "carry" else 4)) * mn + 8 * vn,
         # write U once; 1-D tensors: read the mean, write the update
         "k_update": 4 * mn + 8 * vn,
+        # local-Q error: read G_w and E_w on every worker for its own Q_w
+        "k_qw_partial": W * (gb + 4) * mn,
     }
 
 
@@ -205,9 +210,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline sample length")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the context timings of the other configurations")
-    ap.add_argument("--mode", choices=["all", "carry", "plain", "deferred", "rtopk"], default="all",
+    ap.add_argument("--mode", choices=["all", "carry", "plain", "deferred", "local", "rtopk"], default="all",
                     help="plan variants to time (profiling runs use one); rtopk times only the rTop-k step")
-    ap.add_argument("--primary", choices=["carry", "deferred", "plain"], default="deferred",
+    ap.add_argument("--primary", choices=["carry", "deferred", "plain", "local"], default="deferred",
                     help="variant reported as `value` when several are timed")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -230,7 +235,8 @@ def main() -> int:
     wl = WL.workload("resnet18")
     shapes = [s for _, s in wl.shapes]
     W = wl.workers
-    flag_of = {"plain": 0, "carry": psgd.PSGD_FLAG_CARRY_ERROR_MEAN, "deferred": psgd.PSGD_FLAG_DEFERRED_ERROR}
+    flag_of = {"plain": 0, "carry": psgd.PSGD_FLAG_CARRY_ERROR_MEAN, "deferred": psgd.PSGD_FLAG_DEFERRED_ERROR,
+               "local": psgd.PSGD_FLAG_LOCAL_Q_ERROR}
 
     def measure(variant: str) -> dict:
         flags = flag_of[variant]
@@ -381,7 +387,7 @@ def main() -> int:
         print(json.dumps(out), flush=True)
         return 0
 
-    names = ["plain", "carry", "deferred"] if args.mode == "all" else [args.mode]
+    names = ["plain", "carry", "deferred", "local"] if args.mode == "all" else [args.mode]
     results = {n: measure(n) for n in names}
     primary = args.primary if args.primary in results else names[0]
     main_run = results[primary]
@@ -411,7 +417,8 @@ def main() -> int:
                    "matrices": s["n_matrices"], "uncompressed_tensors": s["n_vectors"],
                    "params": s["numel"], "grad_bytes_per_step": main_run["grad_bytes"],
                    "plan_flags": {"plain": "0", "carry": "PSGD_FLAG_CARRY_ERROR_MEAN",
-                                  "deferred": "PSGD_FLAG_DEFERRED_ERROR"}[primary]},
+                                  "deferred": "PSGD_FLAG_DEFERRED_ERROR",
+                                  "local": "PSGD_FLAG_LOCAL_Q_ERROR"}[primary]},
         "pct_hbm_peak": round(main_run["pct"], 2),
         "model_bytes_per_step": s["model_bytes"],
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,

@@ -370,6 +370,35 @@ __device__ __forceinline__ vec_t<V> update_workers(const GT* G, float* E, int W,
   return acc;
 }
 
+// PSGD_FLAG_LOCAL_Q_ERROR: E_w <- (G_w + E_w) - P_i Q_w^T with each worker's own Q_w
+// (its columns at j read from Qw + w * q_ws + q_off); returns sum_w of the stored values.
+template <int V, typename GT, int WT>
+__device__ __forceinline__ vec_t<V> update_workers_local(const GT* G, float* E, int W, int64_t ld, int64_t c,
+                                                         const float (&pr)[4], const float* Qw, int64_t q_ws,
+                                                         int64_t q_off, int j, int R) {
+  vec_t<V> acc{};
+  constexpr int B = 4;  // four workers in flight: each also needs its own Q_w columns
+  for (int w0 = 0; w0 < W; w0 += B) {
+    vec_t<V> g[B], e[B];
+#pragma unroll
+    for (int k = 0; k < B; ++k)
+      if ((WT > 0 && WT % B == 0) || w0 + k < W) {
+        g[k] = ld_nt<V>(G + (w0 + k) * ld + c);
+        e[k] = ld_nt<V>(E + (w0 + k) * ld + c);
+      }
+#pragma unroll
+    for (int k = 0; k < B; ++k)
+      if ((WT > 0 && WT % B == 0) || w0 + k < W) {
+        float qw[V][4];
+        load_q_cols<V>(qw, Qw + int64_t(w0 + k) * q_ws + q_off, j, R, true);
+        const vec_t<V> n = (g[k] + e[k]) - pq_row<V>(pr, qw, R);
+        st_nt<V>(E + (w0 + k) * ld + c, n);
+        acc += n;
+      }
+  }
+  return acc;
+}
+
 template <int V>
 __device__ __forceinline__ void momentum_v(float* mom, float* x, int64_t c, const vec_t<V> u, int mode, float lr,
                                            float mu) {
@@ -745,19 +774,83 @@ __global__ __launch_bounds__(kQThreads) void k_q_partial(const QTile* __restrict
   }
 }
 
+// grid.z walks workers when reducing the per-worker Q_w partials (strides part_ws and
+// q_ws between workers; both 0 for the Q pass over Mbar).
 __global__ __launch_bounds__(kQRedThreads) void k_q_reduce(const MatInfo* __restrict__ mats,
                                                            const float* __restrict__ Qpart,
                                                            float* __restrict__ Q, float* __restrict__ Q2,
-                                                           int R) {
+                                                           int R, int64_t part_ws, int64_t q_ws) {
   const MatInfo mi = mats[blockIdx.y];
   const int64_t n = int64_t(mi.cols) * R;
-  const float* part = Qpart + mi.qpart_off;
+  const float* part = Qpart + int64_t(blockIdx.z) * part_ws + mi.qpart_off;
+  float* out = Q + int64_t(blockIdx.z) * q_ws + mi.q_off;
   for (int64_t idx = int64_t(blockIdx.x) * kQRedThreads + threadIdx.x; idx < n;
        idx += int64_t(gridDim.x) * kQRedThreads) {
     float s = 0.f;
     for (int b = 0; b < mi.nblk; ++b) s += part[int64_t(b) * n + idx];
-    Q[mi.q_off + idx] = s;
+    out[idx] = s;
     if (Q2 != nullptr) Q2[mi.q_off + idx] = s;
+  }
+}
+
+// Per-worker Q partials for PSGD_FLAG_LOCAL_Q_ERROR: Q_w = (G_w + E_w)^T P, one worker
+// per grid.y, over the same row blocks and column strips as the Q pass over Mbar.
+template <int R, typename GT>
+__global__ __launch_bounds__(kQThreads) void k_qw_partial(const QTile* __restrict__ tiles,
+                                                          const MatInfo* __restrict__ mats,
+                                                          const GT* __restrict__ G, const float* __restrict__ E,
+                                                          int64_t ld, const float* __restrict__ P,
+                                                          float* __restrict__ Qwpart, int64_t qpart_elems) {
+  const QTile t = tiles[blockIdx.x];
+  const int w = blockIdx.y;
+  const MatInfo mi = mats[t.mat];
+  const int cols = mi.cols;
+  const int r0 = t.blk * mi.rows_per_blk;
+  const int r1 = min(mi.rows, r0 + mi.rows_per_blk);
+  const float* Pm = P + mi.p_off;
+  const GT* gb = G + int64_t(w) * ld + mi.offset;
+  const float* eb = E + int64_t(w) * ld + mi.offset;
+  float* out = Qwpart + int64_t(w) * qpart_elems + mi.qpart_off + int64_t(t.blk) * cols * R;
+  if (mi.vw == 4) {
+    const int j = t.col_begin + int(threadIdx.x) * 4;
+    if (j >= t.col_end) return;
+    float acc[4][R];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int k = 0; k < R; ++k) acc[q][k] = 0.f;
+#pragma unroll 4
+    for (int i = r0; i < r1; ++i) {
+      const int64_t c = int64_t(i) * cols + j;
+      const f4 v = ld_nt<4>(gb + c) + ld_nt<4>(eb + c);
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const float pk = Pm[int64_t(i) * R + k];
+        acc[0][k] += v.x * pk;
+        acc[1][k] += v.y * pk;
+        acc[2][k] += v.z * pk;
+        acc[3][k] += v.w * pk;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int k = 0; k < R; ++k) out[int64_t(j + q) * R + k] = acc[q][k];
+  } else {
+    const int j = t.col_begin + int(threadIdx.x);
+    if (j >= t.col_end) return;
+    float acc[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k) acc[k] = 0.f;
+#pragma unroll 4
+    for (int i = r0; i < r1; ++i) {
+      const int64_t c = int64_t(i) * cols + j;
+      const float v = ld_nt<1>(gb + c) + ld_nt<1>(eb + c);
+#pragma unroll
+      for (int k = 0; k < R; ++k) acc[k] += v * Pm[int64_t(i) * R + k];
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k) out[int64_t(j) * R + k] = acc[k];
   }
 }
 
@@ -765,11 +858,11 @@ __global__ __launch_bounds__(kQRedThreads) void k_q_reduce(const MatInfo* __rest
 // Matrix tile: u = P Q^T for the thread's columns of each row; E'_w = (G_w + E_w) - u
 // on every worker, the mean of the stored E'_w into `ebar` (carry mode), U once, and
 // the momentum-SGD update in the momentum modes.  1-D tensors: the update is the mean.
-template <int V, typename GT, int WT>
+template <int V, typename GT, int WT, bool LOCAL>
 __device__ __forceinline__ void apply_matrix_tile(const UpdTile& t, const MatInfo& mi, const GT* G, float* E,
-                                                  const float* P, const float* Q, float* update, float* mom,
-                                                  float* x, float* ebar, int W, int64_t ld, int R, int mode,
-                                                  float lr, float mu, float inv_w) {
+                                                  const float* P, const float* Q, const float* Qw, int64_t q_ws,
+                                                  float* update, float* mom, float* x, float* ebar, int W,
+                                                  int64_t ld, int R, int mode, float lr, float mu, float inv_w) {
   const int cols = mi.cols;
   const int j = t.col_begin + int(threadIdx.x) * V;
   if (j >= cols) return;
@@ -782,20 +875,24 @@ __device__ __forceinline__ void apply_matrix_tile(const UpdTile& t, const MatInf
     load_p_row(pr, P + mi.p_off, i, R);
     const vec_t<V> u = pq_row<V>(pr, qv, R);
     const int64_t c = mi.offset + int64_t(i) * cols + j;
-    const vec_t<V> es = update_workers<V, GT, WT>(G, E, W, ld, c, u);
+    vec_t<V> es;
+    if constexpr (LOCAL)
+      es = update_workers_local<V, GT, WT>(G, E, W, ld, c, pr, Qw, q_ws, mi.q_off, j, R);
+    else
+      es = update_workers<V, GT, WT>(G, E, W, ld, c, u);
     if (ebar != nullptr) st<V>(ebar + c, es * inv_w);
     if (update != nullptr) st_nt<V>(update + c, u);
     if (mode != kCompress) momentum_v<V>(mom, x, c, u, mode, lr, mu);
   }
 }
 
-template <typename GT, int WT>
+template <typename GT, int WT, bool LOCAL>
 __global__ __launch_bounds__(kStreamThreads) void k_apply(
     const UpdTile* __restrict__ tiles, const MatInfo* __restrict__ mats, const GT* __restrict__ G,
     float* __restrict__ E, const float* __restrict__ Mbar, const float* __restrict__ P,
-    const float* __restrict__ Q, float* __restrict__ update, float* __restrict__ mom,
-    float* __restrict__ x, float* __restrict__ ebar, int W, int64_t ld, int R, int mode, float lr,
-    float mu, float inv_w) {
+    const float* __restrict__ Q, const float* __restrict__ Qw, int64_t q_ws, float* __restrict__ update,
+    float* __restrict__ mom, float* __restrict__ x, float* __restrict__ ebar, int W, int64_t ld, int R, int mode,
+    float lr, float mu, float inv_w) {
   const UpdTile t = tiles[blockIdx.x];
   if (t.mat < 0) {
     if (blockIdx.y != 0) return;
@@ -809,9 +906,9 @@ __global__ __launch_bounds__(kStreamThreads) void k_apply(
   }
   const MatInfo mi = mats[t.mat];
   switch (mi.vw) {
-    case 4: apply_matrix_tile<4, GT, WT>(t, mi, G, E, P, Q, update, mom, x, ebar, W, ld, R, mode, lr, mu, inv_w); break;
-    case 2: apply_matrix_tile<2, GT, WT>(t, mi, G, E, P, Q, update, mom, x, ebar, W, ld, R, mode, lr, mu, inv_w); break;
-    default: apply_matrix_tile<1, GT, WT>(t, mi, G, E, P, Q, update, mom, x, ebar, W, ld, R, mode, lr, mu, inv_w); break;
+    case 4: apply_matrix_tile<4, GT, WT, LOCAL>(t, mi, G, E, P, Q, Qw, q_ws, update, mom, x, ebar, W, ld, R, mode, lr, mu, inv_w); break;
+    case 2: apply_matrix_tile<2, GT, WT, LOCAL>(t, mi, G, E, P, Q, Qw, q_ws, update, mom, x, ebar, W, ld, R, mode, lr, mu, inv_w); break;
+    default: apply_matrix_tile<1, GT, WT, LOCAL>(t, mi, G, E, P, Q, Qw, q_ws, update, mom, x, ebar, W, ld, R, mode, lr, mu, inv_w); break;
   }
 }
 
@@ -1040,6 +1137,9 @@ struct StepArgs {
   float* ebar_out;       // error mean to write (carry mode)
   float* Pprev;          // previous P, Q (deferred mode)
   float* Qprev;
+  float* Qwpart;         // per-worker Q partials and Q_w (local-Q error), else null
+  float* Qw;
+  int64_t q_ws;          // floats between workers' Q_w
   int offset_valid;      // deferred mode: errors hold M of the previous step
   int W, R, mode;
   int64_t ld;
@@ -1055,8 +1155,9 @@ psgd_status launch_pass(psgd_plan* plan, int which, int fp, const DeviceTables& 
   const GT* g = static_cast<const GT*>(a.grads);
   const dim3 grid(a.n_s2, a.rows_per_tile), block(kStreamThreads);
   if (which == kPassApply)
-    return launch_k(plan, kKApply, k_apply<GT, WT>, grid, block, a.st, dt.s2tiles, dt.mats, g, a.errors, a.Mbar, a.p,
-                    a.q, a.update, a.mom, a.x, a.ebar_out, a.W, a.ld, a.R, a.mode, a.lr, a.mu, a.inv_w);
+    return launch_k(plan, kKApply, a.Qw != nullptr ? k_apply<GT, WT, true> : k_apply<GT, WT, false>, grid, block, a.st,
+                    dt.s2tiles, dt.mats, g, a.errors, a.Mbar, a.p, a.q, static_cast<const float*>(a.Qw), a.q_ws,
+                    a.update, a.mom, a.x, a.ebar_out, a.W, a.ld, a.R, a.mode, a.lr, a.mu, a.inv_w);
   auto first = fp == kFpDefer ? k_first<GT, WT, kFpDefer> : fp == kFpCarry ? k_first<GT, WT, kFpCarry>
                                                                            : k_first<GT, WT, kFpMean>;
   return launch_k(plan, kKFirst, first, grid, block, a.st, dt.s2tiles, dt.mats, g, a.errors, a.ebar_in, a.Pprev,
@@ -1107,7 +1208,24 @@ psgd_status launch_all(psgd_plan* plan, const DeviceTables& dt, const StepArgs& 
     if (s != PSGD_OK) return s;
     const unsigned gx = unsigned((plan->max_q_elems_per_matrix + kQRedThreads - 1) / kQRedThreads);
     s = launch_k(plan, kKQReduce, k_q_reduce, dim3(gx, n_mats), dim3(kQRedThreads), stream, dt.mats,
-                 static_cast<const float*>(a.Qpart), a.q, deferred ? a.Qprev : nullptr, R);
+                 static_cast<const float*>(a.Qpart), a.q, deferred ? a.Qprev : nullptr, R, int64_t(0), int64_t(0));
+    if (s != PSGD_OK) return s;
+  }
+  if (a.Qw != nullptr && n_mats > 0) {  // local-Q error: every worker's own Q_w = (G_w + E_w)^T P
+    const dim3 qg(unsigned(plan->qtiles.size()), unsigned(a.W));
+    if (bf)
+      s = launch_k(plan, kKQwPartial, k_qw_partial<R, bf16>, qg, dim3(kQThreads), stream, dt.qtiles, dt.mats,
+                   static_cast<const bf16*>(a.grads), static_cast<const float*>(a.errors), a.ld,
+                   static_cast<const float*>(a.p), a.Qwpart, plan->qpart_elems);
+    else
+      s = launch_k(plan, kKQwPartial, k_qw_partial<R, float>, qg, dim3(kQThreads), stream, dt.qtiles, dt.mats,
+                   static_cast<const float*>(a.grads), static_cast<const float*>(a.errors), a.ld,
+                   static_cast<const float*>(a.p), a.Qwpart, plan->qpart_elems);
+    if (s != PSGD_OK) return s;
+    const unsigned gx = unsigned((plan->max_q_elems_per_matrix + kQRedThreads - 1) / kQRedThreads);
+    s = launch_k(plan, kKQwReduce, k_q_reduce, dim3(gx, n_mats, unsigned(a.W)), dim3(kQRedThreads), stream, dt.mats,
+                 static_cast<const float*>(a.Qwpart), a.Qw, static_cast<float*>(nullptr), R, plan->qpart_elems,
+                 a.q_ws);
     if (s != PSGD_OK) return s;
   }
   if (deferred)
@@ -1203,6 +1321,10 @@ psgd_status run_step(const char* fn, psgd_plan* plan, const void* grads, float* 
   a.Pprev = deferred ? reinterpret_cast<float*>(ws + plan->ws_pprev) : nullptr;
   a.Qprev = deferred ? reinterpret_cast<float*>(ws + plan->ws_qprev) : nullptr;
   a.offset_valid = (deferred && use_state) ? 1 : 0;
+  const bool local_q = (plan->flags & PSGD_FLAG_LOCAL_Q_ERROR) != 0;
+  a.Qwpart = local_q ? reinterpret_cast<float*>(ws + plan->ws_qwpart) : nullptr;
+  a.Qw = local_q ? reinterpret_cast<float*>(ws + plan->ws_qw) : nullptr;
+  a.q_ws = plan->q_elems;
   a.W = plan->n_workers;
   a.R = plan->rank;
   a.mode = mode;

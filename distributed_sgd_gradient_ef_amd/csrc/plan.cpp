@@ -16,8 +16,9 @@ namespace psgd {
 
 static thread_local std::string g_last_error;
 
-const char* const kKernelNames[kNumKernels] = {"k_first", "k_mgs",    "k_q_partial", "k_q_reduce",
-                                               "k_apply", "k_update", "k_p_mbar"};
+const char* const kKernelNames[kNumKernels] = {"k_first",  "k_mgs",    "k_q_partial",  "k_q_reduce",
+                                               "k_apply",  "k_update", "k_p_mbar",     "k_qw_partial",
+                                               "k_qw_reduce"};
 
 void set_error(const std::string& msg) { g_last_error = msg; }
 
@@ -64,10 +65,14 @@ extern "C" psgd_status psgd_plan_create(const psgd_layer* layers, int32_t n_laye
     return fail(PSGD_ERR_INVALID_ARG, "psgd_plan_create: n_workers must be in 1..65536");
   if (grad_dtype != PSGD_F32 && grad_dtype != PSGD_BF16)
     return fail(PSGD_ERR_UNSUPPORTED, "psgd_plan_create: unknown gradient dtype");
-  if (flags & ~uint32_t(PSGD_FLAG_NESTEROV | PSGD_FLAG_CARRY_ERROR_MEAN | PSGD_FLAG_DEFERRED_ERROR))
+  if (flags & ~uint32_t(PSGD_FLAG_NESTEROV | PSGD_FLAG_CARRY_ERROR_MEAN | PSGD_FLAG_DEFERRED_ERROR |
+                        PSGD_FLAG_LOCAL_Q_ERROR))
     return fail(PSGD_ERR_UNSUPPORTED, "psgd_plan_create: unknown flag bits");
   if ((flags & PSGD_FLAG_CARRY_ERROR_MEAN) && (flags & PSGD_FLAG_DEFERRED_ERROR))
     return fail(PSGD_ERR_UNSUPPORTED, "psgd_plan_create: PSGD_FLAG_CARRY_ERROR_MEAN and PSGD_FLAG_DEFERRED_ERROR exclude each other");
+  if ((flags & PSGD_FLAG_LOCAL_Q_ERROR) && (flags & (PSGD_FLAG_CARRY_ERROR_MEAN | PSGD_FLAG_DEFERRED_ERROR)))
+    return fail(PSGD_ERR_UNSUPPORTED,
+                "psgd_plan_create: PSGD_FLAG_LOCAL_Q_ERROR excludes PSGD_FLAG_CARRY_ERROR_MEAN and PSGD_FLAG_DEFERRED_ERROR");
 
   psgd_plan* plan = new (std::nothrow) psgd_plan();
   if (plan == nullptr) return fail(PSGD_ERR_NO_MEMORY, "psgd_plan_create: out of host memory");
@@ -193,6 +198,11 @@ extern "C" psgd_status psgd_plan_create(const psgd_layer* layers, int32_t n_laye
     if (flags & PSGD_FLAG_DEFERRED_ERROR) ws += uint64_t(round_up(std::max<int64_t>(plan->p_elems, 1) * 4, 256));
     plan->ws_qprev = ws;
     if (flags & PSGD_FLAG_DEFERRED_ERROR) ws += uint64_t(round_up(std::max<int64_t>(plan->q_elems, 1) * 4, 256));
+    plan->ws_qwpart = ws;
+    if (flags & PSGD_FLAG_LOCAL_Q_ERROR)
+      ws += uint64_t(round_up(std::max<int64_t>(plan->qpart_elems, 1) * 4 * n_workers, 256));
+    plan->ws_qw = ws;
+    if (flags & PSGD_FLAG_LOCAL_Q_ERROR) ws += uint64_t(round_up(std::max<int64_t>(plan->q_elems, 1) * 4 * n_workers, 256));
     plan->workspace_bytes = ws;
     int32_t max_rows = 1;
     for (const MatInfo& m : plan->mats) max_rows = std::max(max_rows, m.rows);

@@ -75,7 +75,7 @@ struct DeviceTables {
 
 void set_error(const std::string& msg);
 
-enum KernelId { kKFirst = 0, kKMgs, kKQPartial, kKQReduce, kKApply, kKUpdate, kKPMbar, kNumKernels };
+enum KernelId { kKFirst = 0, kKMgs, kKQPartial, kKQReduce, kKApply, kKUpdate, kKPMbar, kKQwPartial, kKQwReduce, kNumKernels };
 extern const char* const kKernelNames[kNumKernels];
 
 struct PendingTiming {
@@ -104,6 +104,7 @@ struct psgd_plan {
   int64_t p_elems = 0, q_elems = 0, qpart_elems = 0, ppart_elems = 0;
   int64_t max_q_elems_per_matrix = 0;
   uint64_t ws_mbar = 0, ws_ppart = 0, ws_qpart = 0, ws_ebar = 0, ws_pprev = 0, ws_qprev = 0, workspace_bytes = 0;
+  uint64_t ws_qwpart = 0, ws_qw = 0;  // per-worker Q partials and Q_w (PSGD_FLAG_LOCAL_Q_ERROR)
   int32_t mgs_threads = 64;  // Gram-Schmidt block size: enough for the tallest matrix, <= kMgsThreads
   int32_t worker_rows_per_tile = 1;
   int32_t power_iterations = 1;  // power-iteration rounds per step (psgd_plan_set_power_iterations)

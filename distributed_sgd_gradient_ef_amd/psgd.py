@@ -32,6 +32,7 @@ PSGD_BF16 = 1
 PSGD_FLAG_NESTEROV = 0x1
 PSGD_FLAG_CARRY_ERROR_MEAN = 0x2
 PSGD_FLAG_DEFERRED_ERROR = 0x4
+PSGD_FLAG_LOCAL_Q_ERROR = 0x8
 
 EXPORTED = [
     "psgd_plan_create", "psgd_plan_sizes", "psgd_plan_layer_info", "psgd_plan_destroy",

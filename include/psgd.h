@@ -26,7 +26,8 @@
  *     (not re-normalised);
  *   - the orthonormalisation drops (sets to zero) a column whose residual norm is at
  *     most 1e-4 times its norm before orthogonalisation, or is zero;
- *   - the error uses the aggregated Q (one decompressed U per matrix);
+ *   - the error uses the aggregated Q (one decompressed U per matrix), or, with
+ *     PSGD_FLAG_LOCAL_Q_ERROR, each worker's own Q_w;
  *   - momentum is heavy-ball, mom <- mu*mom + U, x <- x - lr*mom (Nesterov by flag);
  *   - non-finite inputs are not checked: they propagate into every output that depends
  *     on them, and a P column whose norm is not a number is dropped (set to zero).
@@ -110,6 +111,14 @@ typedef enum psgd_dtype {
  * declares that `errors` now holds plain errors).  Excludes
  * PSGD_FLAG_CARRY_ERROR_MEAN.  The workspace grows by p_elems + q_elems floats. */
 #define PSGD_FLAG_DEFERRED_ERROR 0x4u
+/* Local-Q error: each worker keeps E'_w = M_w - P Q_w^T with its own Q_w = M_w^T P
+ * (the projection of M_w off span(P)) instead of M_w - P Qbar^T.  P, Qbar (the output q
+ * and next warm start) and the update U = P Qbar^T are unchanged, and so is the workers'
+ * mean error.  This is the form that lets a multi-GPU step finish its error locally
+ * before the Q all-reduce.  One GPU pays an extra pass over every worker's G and E to form
+ * the Q_w.  Excludes PSGD_FLAG_CARRY_ERROR_MEAN and PSGD_FLAG_DEFERRED_ERROR.  The
+ * workspace grows by n_workers * (q_elems + Q-partial) floats. */
+#define PSGD_FLAG_LOCAL_Q_ERROR 0x8u
 
 /* One tensor of the layer list.  rows == 1 or cols == 1 marks a 1-D tensor. */
 typedef struct psgd_layer {
@@ -206,7 +215,8 @@ psgd_status psgd_plan_set_power_iterations(psgd_plan* plan, int32_t iterations);
  * psgd_plan_kernel_stats waits for the recorded events and accumulates their elapsed
  * times per kernel.  Timing adds two event records per launch.  Kernel names:
  * "k_first", "k_mgs", "k_q_partial", "k_q_reduce", "k_apply" (eager modes) or "k_update"
- * (deferred mode), and "k_p_mbar" for extra power iterations. */
+ * (deferred mode), "k_p_mbar" for extra power iterations, and "k_qw_partial" /
+ * "k_qw_reduce" for PSGD_FLAG_LOCAL_Q_ERROR. */
 typedef struct psgd_kernel_stat {
   char name[32];    /* kernel name */
   int64_t launches; /* launches timed since the last reset */

@@ -154,7 +154,7 @@ def snapshot(run: DeviceRun, layers: Sequence[int], errors_source=None) -> Dict[
 
 def compare_step(run: DeviceRun, snap: Dict[int, LayerSnapshot], oracle_mod, tol: float,
                  check_p: bool = True, what: str = "", errors_source=None,
-                 iterations: int = 1) -> Dict[str, float]:
+                 iterations: int = 1, local_q: bool = False) -> Dict[str, float]:
     """Run the oracle on the snapshot and compare with the GPU outputs of the step that
     followed it.  Returns the worst relative error per output kind; asserts <= tol."""
     run.torch.cuda.synchronize(run.dev)
@@ -167,7 +167,7 @@ def compare_step(run: DeviceRun, snap: Dict[int, LayerSnapshot], oracle_mod, tol
             worst["v"] = max(worst["v"], err)
             assert err <= tol, f"{what} layer {li} mean: rel {err:.3e}"
             continue
-        ref = oracle_mod.compress_matrix(s.g, s.e, s.q, iterations=iterations)
+        ref = oracle_mod.compress_matrix(s.g, s.e, s.q, iterations=iterations, local_q_error=local_q)
         mbar = np.linalg.norm((s.g.astype(np.float64) + s.e).mean(axis=0))
         errs = {
             "p": rel(run.p_layer(li), ref.p_hat, 1.0) if check_p else 0.0,

@@ -223,3 +223,18 @@ def test_pack_unpack_roundtrip():
     qflat = psgd.pack_factors(plan, qs, "q")
     for li, a in qs.items():
         assert np.allclose(psgd.factor_slice(plan, qflat, li, "q"), a)
+
+
+def test_local_q_flag_rules():
+    shapes = [(64, 27), (1, 64), (128, 576)]
+    base = psgd.psgd_plan_create(shapes, 2, 4)
+    loc = psgd.psgd_plan_create(shapes, 2, 4, flags=psgd.PSGD_FLAG_LOCAL_Q_ERROR)
+    grow = loc.sizes["workspace_bytes"] - base.sizes["workspace_bytes"]
+    # per-worker Q partials and per-worker Q_w (each region rounded to 256 bytes)
+    assert grow >= 4 * 4 * loc.sizes["q_elems"] and grow % 256 == 0
+    for other in (psgd.PSGD_FLAG_CARRY_ERROR_MEAN, psgd.PSGD_FLAG_DEFERRED_ERROR):
+        with pytest.raises(psgd.PsgdError) as e:
+            psgd.psgd_plan_create(shapes, 2, 4, flags=psgd.PSGD_FLAG_LOCAL_Q_ERROR | other)
+        assert e.value.status == psgd.PSGD_ERR_UNSUPPORTED
+    nest = psgd.psgd_plan_create(shapes, 2, 4, flags=psgd.PSGD_FLAG_LOCAL_Q_ERROR | psgd.PSGD_FLAG_NESTEROV)
+    assert nest.sizes["workspace_bytes"] == loc.sizes["workspace_bytes"]

@@ -670,3 +670,61 @@ def test_momentum_200_steps(torch_gpu):
         if t % 50 == 0 or t == wl.steps - 1:
             log(f"step {t}: worst " + " ".join(f"{k}={v:.2e}" for k, v in worst.items())
                 + f" mom/x={worst_all:.2e}")
+
+
+# ----------------------------------------------------------------------- local-Q error
+@pytest.mark.parametrize("W,r,bf16", [(1, 2, False), (3, 1, False), (4, 3, False), (16, 2, False), (5, 4, True)])
+def test_local_q_error_matches_oracle(torch_gpu, W, r, bf16):
+    """PSGD_FLAG_LOCAL_Q_ERROR: every worker keeps M_w - P Q_w^T with its own Q_w; P, Q-bar
+    and U are those of the aggregated-Q step.  Three steps against the oracle's local-Q
+    reading, ragged shapes including the 2-wide and tall row paths."""
+    from distributed_sgd_gradient_ef_amd import psgd
+
+    log(f"[case] local-Q W={W} r={r} bf16={bf16}")
+    shapes = [(37, 29), (1, 10), (130, 1030), (64, 27), (256, 2304), (4100, 6), (1, 65)]
+    rng = np.random.default_rng(100 + W * 7 + r)
+    run = DeviceRun(shapes, r, W, bf16=bf16, flags=psgd.PSGD_FLAG_LOCAL_Q_ERROR)
+    e = [0.3 * rng.standard_normal((W,) + s).astype(np.float32) for s in shapes]
+    run.set_errors_host(e)
+    qs = {i: rng.standard_normal((s[1], r)).astype(np.float32) for i, s in enumerate(shapes) if WL.is_matrix(s, r)}
+    run.set_q_host(qs)
+    for step in range(3):
+        g = [rng.standard_normal((W,) + s).astype(np.float32) for s in shapes]
+        if bf16:
+            g = [WL.to_bf16_values(a) for a in g]
+        run.set_grads_host(g)
+        snap = snapshot(run, range(len(shapes)))
+        run.compress()
+        compare_step(run, snap, O, TOL, what=f"local-Q step {step}", local_q=True)
+
+
+def test_local_q_error_mean_equals_aggregated(torch_gpu):
+    """The two error readings differ per worker but share the workers' mean error and
+    produce the same P, Q-bar and U (up to float rounding)."""
+    from distributed_sgd_gradient_ef_amd import psgd
+
+    log("[case] local-Q vs aggregated-Q")
+    shapes = [(200, 96), (1, 17), (300, 1030)]
+    W, r = 4, 2
+    rng = np.random.default_rng(5)
+    g = [rng.standard_normal((W,) + s).astype(np.float32) for s in shapes]
+    e = [0.3 * rng.standard_normal((W,) + s).astype(np.float32) for s in shapes]
+    qs = {i: rng.standard_normal((s[1], r)).astype(np.float32) for i, s in enumerate(shapes) if WL.is_matrix(s, r)}
+    runs = []
+    for flags in (0, psgd.PSGD_FLAG_LOCAL_Q_ERROR):
+        run = DeviceRun(shapes, r, W, flags=flags)
+        run.set_grads_host(g)
+        run.set_errors_host(e)
+        run.set_q_host(qs)
+        run.compress()
+        torch_gpu.cuda.synchronize()
+        runs.append(run)
+    for li in (0, 2):
+        a, b = runs[0], runs[1]
+        scale = np.abs(a.vec_layer(a.update, li)).max()
+        assert np.allclose(a.p_layer(li), b.p_layer(li), atol=1e-6)
+        assert np.allclose(a.q_layer(li), b.q_layer(li), atol=1e-5 * scale)
+        assert np.allclose(a.vec_layer(a.update, li), b.vec_layer(b.update, li), atol=1e-6 * scale)
+        ea, eb = a.errors_layer(li), b.errors_layer(li)
+        assert np.allclose(ea.mean(axis=0), eb.mean(axis=0), atol=1e-5 * scale)
+        assert not np.allclose(ea, eb, atol=1e-3 * scale)  # per worker they differ
