@@ -298,21 +298,29 @@ __device__ __forceinline__ int wave_region(int len, int v) {
   return off;
 }
 
+// Number of set bits of a wave-wide mask below this lane (no LDS involved).
+__device__ __forceinline__ uint32_t lanes_below(uint64_t b) {
+  return __builtin_amdgcn_mbcnt_hi(uint32_t(b >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(b), 0u));
+}
+
 // Marking of one tile against digit-1 bin b1, from the 16 values each thread holds
 // (m[i][j] is element (i * kTileThreads + threadIdx.x) * 4 + j of the tile).  The wave
 // with index v handles groups v, v+4, v+8, v+12 of 256 elements; lane l holds elements
 // 4l..4l+3 of its group, so mask word q of a group (32 elements) comes from lanes
 // 8q..8q+7 and is assembled by lane q from four ballots.  Entries above b1 set top-mask
 // bits; entries in b1 (the candidates) go to the wave's part of the tile's region of
-// `cand` (same layout as E) as (key bits 19..0) << 12 | offset in the tile, and into the
-// LDS histogram h2 of their digit 2.  Each wave writes its own top and candidate counts;
-// no barrier.
+// `cand` (same layout as E) as (key bits 19..0) << 12 | offset in the tile, placed by
+// ballot and lane count, and are then counted into the LDS histogram h2 of their digit
+// 2.  Counts come from ballot popcounts and positions from mbcnt, so no LDS operation
+// sits between the stores (the histogram atomics come last).  Each wave writes its own
+// top and candidate counts; no barrier.
 __device__ __forceinline__ void mark_tile(const float (&m)[4][4], const RkTile& t, uint32_t b1, int64_t base,
                                           int64_t trow, uint32_t* h2, uint32_t* __restrict__ mask,
                                           uint32_t* __restrict__ tmask, uint32_t* __restrict__ tcnt4,
                                           uint32_t* __restrict__ cand, uint32_t* __restrict__ ccnt4) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t wbase = base >> 5;  // begin and stride are multiples of 64
+  uint32_t* out = cand + base + wave_region(t.len, wv);
   uint32_t nsure = 0, ncand = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -324,10 +332,11 @@ __device__ __forceinline__ void mark_tile(const float (&m)[4][4], const RkTile& 
       const uint32_t key = mag_key(m[i][j]);
       const bool ok = e + j < t.len;
       B[j] = __ballot(ok && (key >> 20) > b1);
-      if (ok && (key >> 20) == b1) {
-        atomicAdd(&h2[(key >> 9) & 0x7ffu], 1u);
-        ++ncand;
-      }
+      nsure += uint32_t(__popcll(B[j]));
+      const bool c = ok && (key >> 20) == b1;
+      const uint64_t bc = __ballot(c);
+      if (c) out[ncand + lanes_below(bc)] = ((key & 0xfffffu) << kLocalBits) | uint32_t(e + j);
+      ncand += uint32_t(__popcll(bc));
     }
     if (lane < 8 && (g * 256 + lane * 32) < t.len) {
       const int sh = lane * 8;
@@ -336,24 +345,19 @@ __device__ __forceinline__ void mark_tile(const float (&m)[4][4], const RkTile& 
                             (spread4(uint32_t(B[3] >> sh) & 0xffu) << 3);
       mask[wbase + g * 8 + lane] = word;
       tmask[wbase + g * 8 + lane] = 0u;
-      nsure += __popc(word);
     }
   }
-  const uint32_t tot = wave_sum(nsure);
-  const uint32_t incl = wave_incl_scan(ncand);
-  if (lane == 0) tcnt4[trow * 4 + wv] = tot;
-  if (lane == 63) ccnt4[trow * 4 + wv] = incl;
-  if (ncand > 0) {
-    uint32_t* out = cand + base + wave_region(t.len, wv);
-    uint32_t pos = incl - ncand;
+  if (lane == 0) {
+    tcnt4[trow * 4 + wv] = nsure;
+    ccnt4[trow * 4 + wv] = ncand;
+  }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = (i * 4 + wv) * 256 + lane * 4;
+  for (int i = 0; i < 4; ++i) {
+    const int e = (i * 4 + wv) * 256 + lane * 4;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t key = mag_key(m[i][j]);
-        if (e + j < t.len && (key >> 20) == b1) out[pos++] = ((key & 0xfffffu) << kLocalBits) | uint32_t(e + j);
-      }
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t key = mag_key(m[i][j]);
+      if (e + j < t.len && (key >> 20) == b1) atomicAdd(&h2[(key >> 9) & 0x7ffu], 1u);
     }
   }
 }
@@ -410,11 +414,15 @@ __global__ __launch_bounds__(kTileThreads) void rk_ef_hist(const RkTile* __restr
     m[i][1] = mv.y;
     m[i][2] = mv.z;
     m[i][3] = mv.w;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (j < valid) atomicAdd(&h1[mag_key(m[i][j]) >> 20], 1u);
   }
   mark_tile(m, t, bp, base, int64_t(w) * ntiles + blockIdx.x, h2, mask, tmask, tcnt4, cand, ccnt4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = (i * kTileThreads + int(threadIdx.x)) * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (e + j < t.len) atomicAdd(&h1[mag_key(m[i][j]) >> 20], 1u);
+  }
   __syncthreads();
   uint32_t* g1 = hist1 + s * kBins1;
   uint32_t* g2 = hist2 + s * kBins2;
@@ -843,12 +851,20 @@ __global__ __launch_bounds__(kWordThreads) void rk_update(const RkTile* __restri
   if (q < nwords) {
     const int64_t wi = (t.begin >> 5) + q;
     const int64_t wstride = stride >> 5;
-    for (int w = 0; w < W; ++w) {
-      const uint32_t kw = kmask[int64_t(w) * wstride + wi];
-      if (kw == 0u) continue;
-      uint32_t pos = kpos[int64_t(w) * wstride + wi];
-      const float* vx = value + int64_t(w) * keep_total + L.keep_off;
-      for (uint32_t bits = kw; bits != 0u; bits &= bits - 1u) acc[q][__builtin_ctz(bits)] += vx[pos++];
+    // workers in groups of 8: all mask words (then all list positions) of a group are
+    // loaded before any is used
+    for (int w0 = 0; w0 < W; w0 += 8) {
+      uint32_t kw[8], kp[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) kw[k] = w0 + k < W ? kmask[int64_t(w0 + k) * wstride + wi] : 0u;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) kp[k] = kw[k] != 0u ? kpos[int64_t(w0 + k) * wstride + wi] : 0u;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float* vx = value + int64_t(w0 + k) * keep_total + L.keep_off;
+        uint32_t pos = kp[k];
+        for (uint32_t bits = kw[k]; bits != 0u; bits &= bits - 1u) acc[q][__builtin_ctz(bits)] += vx[pos++];
+      }
     }
   }
   __syncthreads();
