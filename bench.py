@@ -164,41 +164,75 @@ def timed_steps(torch, step, steps: int, stream):
 
 
 def config_timings(torch, psgd, WL, dev, steps: int) -> dict:
-    """Context lines for the other configurations (not the metric): the single small
-    matrix as latency, the LSTM shapes and the bandwidth-stress set, deferred mode."""
+    """Context lines for the other configurations (not the metric), deferred mode: the
+    single small matrix as latency, the LSTM shapes, the bandwidth-stress set at r = 1, 2,
+    4 and with bf16 gradients, and the fused momentum step on the ResNet-18 shapes."""
     out = {}
-    for name, rank, nsteps in (("single", 1, 10 * steps), ("lstm", 4, steps), ("stress", 2, max(3, steps // 10))):
-        wl = WL.workload(name, rank=rank)
-        shapes = [s for _, s in wl.shapes]
+
+    def run(name, wl, grads, gbytes, nsteps, momentum=False, dtype=None):
         W = wl.workers
-        plan = psgd.psgd_plan_create(shapes, wl.rank, W, psgd.PSGD_F32, psgd.PSGD_FLAG_DEFERRED_ERROR)
+        shapes = [s for _, s in wl.shapes]
+        plan = psgd.psgd_plan_create(shapes, wl.rank, W, dtype if dtype is not None else psgd.PSGD_F32,
+                                     psgd.PSGD_FLAG_DEFERRED_ERROR)
         s = plan.sizes
         ld = s["worker_stride"]
-        grads = torch.zeros((W, ld), dtype=torch.float32, device=dev)
         errors = torch.zeros((W, ld), dtype=torch.float32, device=dev)
         q = torch.zeros(s["q_elems"], dtype=torch.float32, device=dev)
         p = torch.zeros(s["p_elems"], dtype=torch.float32, device=dev)
         update = torch.zeros(ld, dtype=torch.float32, device=dev)
         workspace = torch.empty(s["workspace_bytes"], dtype=torch.uint8, device=dev)
-        WL.device_grads(wl, 0, [(L.offset, L.rows, L.cols) for L in plan.layers], grads)
         qh = psgd.pack_factors(plan, {i: WL.q0(wl, i) for i, L in enumerate(plan.layers) if L.compressed}, "q")
         q.copy_(torch.from_numpy(qh).to(dev))
         stream = torch.cuda.current_stream(dev)
+        if momentum:
+            mom = torch.zeros(ld, dtype=torch.float32, device=dev)
+            x = torch.zeros(ld, dtype=torch.float32, device=dev)
 
-        def step():
-            psgd.psgd_compress_step(plan, grads, errors, q, p, update, workspace, stream)
-
+            def step():
+                psgd.psgd_ef_momentum_apply(plan, grads, errors, q, p, mom, x, wl.lr, wl.mu, None, workspace, stream)
+            model = s["model_bytes_momentum"]
+        else:
+            def step():
+                psgd.psgd_compress_step(plan, grads, errors, q, p, update, workspace, stream)
+            model = s["model_bytes"]
         for _ in range(3):
             step()
         torch.cuda.synchronize(dev)
         ms, med, mn = timed_steps(torch, step, nsteps, stream)
         out[name] = {"workers": W, "rank": wl.rank, "params": s["numel"], "steps": nsteps,
                      "ms_per_step": round(ms, 4), "ms_median": round(med, 4), "ms_min": round(mn, 4),
-                     "grad_GBps": round(W * s["numel"] * 4 / (ms * 1e-3) / 1e9, 1),
-                     "pct_hbm_peak": round(100.0 * s["model_bytes"] / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 2)}
-        del grads, errors, q, p, update, workspace, plan
-        torch.cuda.empty_cache()
+                     "grad_GBps": round(W * s["numel"] * gbytes / (ms * 1e-3) / 1e9, 1),
+                     "pct_hbm_peak": round(100.0 * model / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 2)}
+        del errors, q, p, update, workspace, plan
+
+    def draw(wl):
+        plan = psgd.psgd_plan_create([s for _, s in wl.shapes], wl.rank, wl.workers)
+        g = torch.zeros((wl.workers, plan.sizes["worker_stride"]), dtype=torch.float32, device=dev)
+        WL.device_grads(wl, 0, [(L.offset, L.rows, L.cols) for L in plan.layers], g)
+        return g
+
+    wl = WL.workload("single")
+    run("single", wl, draw(wl), 4, 10 * steps)
     out["single"]["role"] = "latency (one 256x128 matrix, W=1, r=1; launch-bound)"
+    wl = WL.workload("lstm")
+    g = draw(wl)
+    run("lstm", wl, g, 4, steps)
+    del g
+    wl = WL.workload("resnet18_momentum")
+    g = draw(wl)
+    run("resnet18_momentum", wl, g, 4, steps, momentum=True)
+    del g
+    wl = WL.workload("stress", rank=2)
+    g = draw(wl)
+    nstress = max(3, steps // 10)
+    for r in (1, 2, 4):
+        run(f"stress_r{r}", WL.workload("stress", rank=r), g, 4, nstress)
+    gb = g.to(torch.bfloat16)
+    del g
+    torch.cuda.empty_cache()
+    run("stress_r2_bf16", wl, gb, 2, nstress, dtype=psgd.PSGD_BF16)
+    del gb
+    torch.cuda.empty_cache()
     return out
 
 
