@@ -82,9 +82,17 @@ __device__ __forceinline__ f2 widen(const u16x2 v) {
   return r;
 }
 
-template <int V>
-__device__ __forceinline__ vec_t<V> ldv(const float* p) {
-  if constexpr (V == 4)
+// A: the alignment of p in floats.  V = 4 with A = 2 (rows whose column count is even but
+// not a multiple of 4 are only 8-byte aligned) reads and writes the four floats as two
+// 8-byte halves.  Such a row ends two columns into its last lane: there hi is false and
+// the upper half is neither read (it reads as zero) nor written.
+template <int V, int A = V>
+__device__ __forceinline__ vec_t<V> ldv(const float* p, bool hi = true) {
+  if constexpr (V == 4 && A == 2) {
+    const f2 a = *reinterpret_cast<const f2*>(p);
+    const f2 b = hi ? *reinterpret_cast<const f2*>(p + 2) : f2{0.f, 0.f};
+    return f4{a.x, a.y, b.x, b.y};
+  } else if constexpr (V == 4)
     return *reinterpret_cast<const f4*>(p);
   else if constexpr (V == 2)
     return *reinterpret_cast<const f2*>(p);
@@ -92,9 +100,13 @@ __device__ __forceinline__ vec_t<V> ldv(const float* p) {
     return *p;
 }
 
-template <int V>
-__device__ __forceinline__ vec_t<V> ld_nt(const float* p) {
-  if constexpr (V == 4)
+template <int V, int A = V>
+__device__ __forceinline__ vec_t<V> ld_nt(const float* p, bool hi = true) {
+  if constexpr (V == 4 && A == 2) {
+    const f2 a = __builtin_nontemporal_load(reinterpret_cast<const f2*>(p));
+    const f2 b = hi ? __builtin_nontemporal_load(reinterpret_cast<const f2*>(p + 2)) : f2{0.f, 0.f};
+    return f4{a.x, a.y, b.x, b.y};
+  } else if constexpr (V == 4)
     return __builtin_nontemporal_load(reinterpret_cast<const f4*>(p));
   else if constexpr (V == 2)
     return __builtin_nontemporal_load(reinterpret_cast<const f2*>(p));
@@ -102,9 +114,13 @@ __device__ __forceinline__ vec_t<V> ld_nt(const float* p) {
     return __builtin_nontemporal_load(p);
 }
 
-template <int V>
-__device__ __forceinline__ vec_t<V> ld_nt(const bf16* p) {
-  if constexpr (V == 4)
+template <int V, int A = V>
+__device__ __forceinline__ vec_t<V> ld_nt(const bf16* p, bool hi = true) {
+  if constexpr (V == 4 && A == 2) {
+    const f2 a = widen(__builtin_nontemporal_load(reinterpret_cast<const u16x2*>(p)));
+    const f2 b = hi ? widen(__builtin_nontemporal_load(reinterpret_cast<const u16x2*>(p + 2))) : f2{0.f, 0.f};
+    return f4{a.x, a.y, b.x, b.y};
+  } else if constexpr (V == 4)
     return widen(__builtin_nontemporal_load(reinterpret_cast<const u16x4*>(p)));
   else if constexpr (V == 2)
     return widen(__builtin_nontemporal_load(reinterpret_cast<const u16x2*>(p)));
@@ -112,9 +128,12 @@ __device__ __forceinline__ vec_t<V> ld_nt(const bf16* p) {
     return __uint_as_float(uint32_t(__builtin_nontemporal_load(reinterpret_cast<const unsigned short*>(p))) << 16);
 }
 
-template <int V>
-__device__ __forceinline__ void st(float* p, const vec_t<V> v) {
-  if constexpr (V == 4)
+template <int V, int A = V>
+__device__ __forceinline__ void st(float* p, const vec_t<V> v, bool hi = true) {
+  if constexpr (V == 4 && A == 2) {
+    *reinterpret_cast<f2*>(p) = f2{v.x, v.y};
+    if (hi) *reinterpret_cast<f2*>(p + 2) = f2{v.z, v.w};
+  } else if constexpr (V == 4)
     *reinterpret_cast<f4*>(p) = v;
   else if constexpr (V == 2)
     *reinterpret_cast<f2*>(p) = v;
@@ -122,9 +141,12 @@ __device__ __forceinline__ void st(float* p, const vec_t<V> v) {
     *p = v;
 }
 
-template <int V>
-__device__ __forceinline__ void st_nt(float* p, const vec_t<V> v) {
-  if constexpr (V == 4)
+template <int V, int A = V>
+__device__ __forceinline__ void st_nt(float* p, const vec_t<V> v, bool hi = true) {
+  if constexpr (V == 4 && A == 2) {
+    __builtin_nontemporal_store(f2{v.x, v.y}, reinterpret_cast<f2*>(p));
+    if (hi) __builtin_nontemporal_store(f2{v.z, v.w}, reinterpret_cast<f2*>(p + 2));
+  } else if constexpr (V == 4)
     __builtin_nontemporal_store(v, reinterpret_cast<f4*>(p));
   else if constexpr (V == 2)
     __builtin_nontemporal_store(v, reinterpret_cast<f2*>(p));
@@ -235,9 +257,10 @@ __device__ __forceinline__ void load_q4(float (&qv)[4][4], const float* base) {
 // inactive).  With V = 4, j is a multiple of 4 and every Q block starts on a 16-byte
 // boundary, so the 4R floats are R aligned float4 loads.
 template <int V>
-__device__ __forceinline__ void load_q_cols(float (&qv)[V][4], const float* Qm, int j, int R, bool active) {
+__device__ __forceinline__ void load_q_cols(float (&qv)[V][4], const float* Qm, int j, int R, bool active,
+                                            bool hi = true) {
   if constexpr (V == 4) {
-    if (active) {
+    if (active && hi) {
       const float* base = Qm + int64_t(j) * R;
       switch (R) {
         case 1: load_q4<1>(qv, base); return;
@@ -250,7 +273,7 @@ __device__ __forceinline__ void load_q_cols(float (&qv)[V][4], const float* Qm, 
 #pragma unroll
   for (int q = 0; q < V; ++q)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) qv[q][k] = (active && k < R) ? Qm[int64_t(j + q) * R + k] : 0.f;
+    for (int k = 0; k < 4; ++k) qv[q][k] = (active && k < R && (q < 2 || hi)) ? Qm[int64_t(j + q) * R + k] : 0.f;
 }
 
 __device__ __forceinline__ void load_p_row(float (&pr)[4], const float* Pm, int i, int R) {
@@ -274,15 +297,16 @@ __device__ __forceinline__ vec_t<V> pq_row(const float (&pr)[4], const float (&q
 // any worker count, four at a time.
 
 // sum_w (G_w + E_w)
-template <int V, typename GT, int WT>
-__device__ __forceinline__ vec_t<V> sum_ge(const GT* G, const float* E, int W, int64_t ld, int64_t c) {
+template <int V, typename GT, int WT, int A = V>
+__device__ __forceinline__ vec_t<V> sum_ge(const GT* G, const float* E, int W, int64_t ld, int64_t c,
+                                          bool hi = true) {
   vec_t<V> acc{};
   if constexpr (WT > 0) {
     vec_t<V> g[WT], e[WT];
 #pragma unroll
     for (int w = 0; w < WT; ++w) {
-      g[w] = ld_nt<V>(G + w * ld + c);
-      e[w] = ld_nt<V>(E + w * ld + c);
+      g[w] = ld_nt<V, A>(G + w * ld + c, hi);
+      e[w] = ld_nt<V, A>(E + w * ld + c, hi);
     }
 #pragma unroll
     for (int w = 0; w < WT; ++w) acc += g[w] + e[w];
@@ -292,25 +316,25 @@ __device__ __forceinline__ vec_t<V> sum_ge(const GT* G, const float* E, int W, i
       vec_t<V> g[4], e[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        g[k] = ld_nt<V>(G + (w + k) * ld + c);
-        e[k] = ld_nt<V>(E + (w + k) * ld + c);
+        g[k] = ld_nt<V, A>(G + (w + k) * ld + c, hi);
+        e[k] = ld_nt<V, A>(E + (w + k) * ld + c, hi);
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) acc += g[k] + e[k];
     }
-    for (; w < W; ++w) acc += ld_nt<V>(G + w * ld + c) + ld_nt<V>(E + w * ld + c);
+    for (; w < W; ++w) acc += ld_nt<V, A>(G + w * ld + c, hi) + ld_nt<V, A>(E + w * ld + c, hi);
   }
   return acc;
 }
 
 // sum_w G_w
-template <int V, typename GT, int WT>
-__device__ __forceinline__ vec_t<V> sum_g(const GT* G, int W, int64_t ld, int64_t c) {
+template <int V, typename GT, int WT, int A = V>
+__device__ __forceinline__ vec_t<V> sum_g(const GT* G, int W, int64_t ld, int64_t c, bool hi = true) {
   vec_t<V> acc{};
   if constexpr (WT > 0) {
     vec_t<V> g[WT];
 #pragma unroll
-    for (int w = 0; w < WT; ++w) g[w] = ld_nt<V>(G + w * ld + c);
+    for (int w = 0; w < WT; ++w) g[w] = ld_nt<V, A>(G + w * ld + c, hi);
 #pragma unroll
     for (int w = 0; w < WT; ++w) acc += g[w];
   } else {
@@ -318,31 +342,31 @@ __device__ __forceinline__ vec_t<V> sum_g(const GT* G, int W, int64_t ld, int64_
     for (; w + 4 <= W; w += 4) {
       vec_t<V> g[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) g[k] = ld_nt<V>(G + (w + k) * ld + c);
+      for (int k = 0; k < 4; ++k) g[k] = ld_nt<V, A>(G + (w + k) * ld + c, hi);
 #pragma unroll
       for (int k = 0; k < 4; ++k) acc += g[k];
     }
-    for (; w < W; ++w) acc += ld_nt<V>(G + w * ld + c);
+    for (; w < W; ++w) acc += ld_nt<V, A>(G + w * ld + c, hi);
   }
   return acc;
 }
 
 // E_w <- (G_w + E_w) - u for every worker; returns sum_w of the stored values.
-template <int V, typename GT, int WT>
+template <int V, typename GT, int WT, int A = V>
 __device__ __forceinline__ vec_t<V> update_workers(const GT* G, float* E, int W, int64_t ld, int64_t c,
-                                                   const vec_t<V> u) {
+                                                   const vec_t<V> u, bool hi = true) {
   vec_t<V> acc{};
   if constexpr (WT > 0) {
     vec_t<V> g[WT], e[WT];
 #pragma unroll
     for (int w = 0; w < WT; ++w) {
-      g[w] = ld_nt<V>(G + w * ld + c);
-      e[w] = ld_nt<V>(E + w * ld + c);
+      g[w] = ld_nt<V, A>(G + w * ld + c, hi);
+      e[w] = ld_nt<V, A>(E + w * ld + c, hi);
     }
 #pragma unroll
     for (int w = 0; w < WT; ++w) {
       const vec_t<V> n = (g[w] + e[w]) - u;
-      st_nt<V>(E + w * ld + c, n);
+      st_nt<V, A>(E + w * ld + c, n, hi);
       acc += n;
     }
   } else {
@@ -351,19 +375,19 @@ __device__ __forceinline__ vec_t<V> update_workers(const GT* G, float* E, int W,
       vec_t<V> g[4], e[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        g[k] = ld_nt<V>(G + (w + k) * ld + c);
-        e[k] = ld_nt<V>(E + (w + k) * ld + c);
+        g[k] = ld_nt<V, A>(G + (w + k) * ld + c, hi);
+        e[k] = ld_nt<V, A>(E + (w + k) * ld + c, hi);
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const vec_t<V> n = (g[k] + e[k]) - u;
-        st_nt<V>(E + (w + k) * ld + c, n);
+        st_nt<V, A>(E + (w + k) * ld + c, n, hi);
         acc += n;
       }
     }
     for (; w < W; ++w) {
-      const vec_t<V> n = (ld_nt<V>(G + w * ld + c) + ld_nt<V>(E + w * ld + c)) - u;
-      st_nt<V>(E + w * ld + c, n);
+      const vec_t<V> n = (ld_nt<V, A>(G + w * ld + c, hi) + ld_nt<V, A>(E + w * ld + c, hi)) - u;
+      st_nt<V, A>(E + w * ld + c, n, hi);
       acc += n;
     }
   }
@@ -372,10 +396,10 @@ __device__ __forceinline__ vec_t<V> update_workers(const GT* G, float* E, int W,
 
 // PSGD_FLAG_LOCAL_Q_ERROR: E_w <- (G_w + E_w) - P_i Q_w^T with each worker's own Q_w
 // (its columns at j read from Qw + w * q_ws + q_off); returns sum_w of the stored values.
-template <int V, typename GT, int WT>
+template <int V, typename GT, int WT, int A = V>
 __device__ __forceinline__ vec_t<V> update_workers_local(const GT* G, float* E, int W, int64_t ld, int64_t c,
                                                          const float (&pr)[4], const float* Qw, int64_t q_ws,
-                                                         int64_t q_off, int j, int R) {
+                                                         int64_t q_off, int j, int R, bool hi = true) {
   vec_t<V> acc{};
   constexpr int B = 4;  // four workers in flight: each also needs its own Q_w columns
   for (int w0 = 0; w0 < W; w0 += B) {
@@ -383,30 +407,30 @@ __device__ __forceinline__ vec_t<V> update_workers_local(const GT* G, float* E, 
 #pragma unroll
     for (int k = 0; k < B; ++k)
       if ((WT > 0 && WT % B == 0) || w0 + k < W) {
-        g[k] = ld_nt<V>(G + (w0 + k) * ld + c);
-        e[k] = ld_nt<V>(E + (w0 + k) * ld + c);
+        g[k] = ld_nt<V, A>(G + (w0 + k) * ld + c, hi);
+        e[k] = ld_nt<V, A>(E + (w0 + k) * ld + c, hi);
       }
 #pragma unroll
     for (int k = 0; k < B; ++k)
       if ((WT > 0 && WT % B == 0) || w0 + k < W) {
         float qw[V][4];
-        load_q_cols<V>(qw, Qw + int64_t(w0 + k) * q_ws + q_off, j, R, true);
+        load_q_cols<V>(qw, Qw + int64_t(w0 + k) * q_ws + q_off, j, R, true, hi);
         const vec_t<V> n = (g[k] + e[k]) - pq_row<V>(pr, qw, R);
-        st_nt<V>(E + (w0 + k) * ld + c, n);
+        st_nt<V, A>(E + (w0 + k) * ld + c, n, hi);
         acc += n;
       }
   }
   return acc;
 }
 
-template <int V>
+template <int V, int A = V>
 __device__ __forceinline__ void momentum_v(float* mom, float* x, int64_t c, const vec_t<V> u, int mode, float lr,
-                                           float mu) {
-  const vec_t<V> m0 = ld_nt<V>(mom + c), x0 = ld_nt<V>(x + c);
+                                           float mu, bool hi = true) {
+  const vec_t<V> m0 = ld_nt<V, A>(mom + c, hi), x0 = ld_nt<V, A>(x + c, hi);
   const vec_t<V> m1 = mu * m0 + u;
   const vec_t<V> x1 = (mode == kNesterov) ? x0 - lr * (u + mu * m1) : x0 - lr * m1;
-  st_nt<V>(mom + c, m1);
-  st_nt<V>(x + c, x1);
+  st_nt<V, A>(mom + c, m1, hi);
+  st_nt<V, A>(x + c, x1, hi);
 }
 
 __device__ __forceinline__ void momentum_masked(float* mom, float* x, int64_t c, const f4 u, int64_t valid,
@@ -428,7 +452,7 @@ __device__ __forceinline__ void momentum_masked(float* mom, float* x, int64_t c,
 //   kFpDefer M_w = (G_w + E_w) - P_prev Q_prev^T is stored back into E; Mbar = mean_w M_w
 // For every row, each lane's share of P-bar = Mbar Q over its columns is summed across
 // the wave (fixed butterfly order) and lane 0 writes the strip's partial row sum.
-template <int V, typename GT, int WT, int FP>
+template <int V, typename GT, int WT, int FP, int A = V>
 __device__ __forceinline__ void first_matrix_tile(const UpdTile& t, const MatInfo& mi, const GT* G, float* E,
                                                   const float* ebar, const float* Pprev, const float* Qprev,
                                                   const float* Qin, float* Mbar, float* Ppart, int W, int64_t ld,
@@ -436,10 +460,11 @@ __device__ __forceinline__ void first_matrix_tile(const UpdTile& t, const MatInf
   const int cols = mi.cols;
   const int j = t.col_begin + int(threadIdx.x) * V;
   const bool active = j < cols;
+  const bool hi = A == V || j + 4 <= cols;
   float qv[V][4];
-  load_q_cols<V>(qv, Qin + mi.q_off, j, R, active);
+  load_q_cols<V>(qv, Qin + mi.q_off, j, R, active, hi);
   float qp[V][4];
-  if constexpr (FP == kFpDefer) load_q_cols<V>(qp, Qprev + mi.q_off, j, R, active && offset_valid);
+  if constexpr (FP == kFpDefer) load_q_cols<V>(qp, Qprev + mi.q_off, j, R, active && offset_valid, hi);
   const int strip = t.col_begin / (kStreamThreads * V);
   float* prow = Ppart + mi.ppart_off + int64_t(strip) * mi.rows * R;
   {
@@ -452,13 +477,13 @@ __device__ __forceinline__ void first_matrix_tile(const UpdTile& t, const MatInf
       if constexpr (FP == kFpDefer) {
         float pp[4] = {0.f, 0.f, 0.f, 0.f};
         if (offset_valid) load_p_row(pp, Pprev + mi.p_off, i, R);
-        mb = update_workers<V, GT, WT>(G, E, W, ld, c, pq_row<V>(pp, qp, R)) * inv_w;
+        mb = update_workers<V, GT, WT, A>(G, E, W, ld, c, pq_row<V>(pp, qp, R), hi) * inv_w;
       } else if constexpr (FP == kFpCarry) {
-        mb = sum_g<V, GT, WT>(G, W, ld, c) * inv_w + ldv<V>(ebar + c);
+        mb = sum_g<V, GT, WT, A>(G, W, ld, c, hi) * inv_w + ldv<V, A>(ebar + c, hi);
       } else {
-        mb = sum_ge<V, GT, WT>(G, E, W, ld, c) * inv_w;
+        mb = sum_ge<V, GT, WT, A>(G, E, W, ld, c, hi) * inv_w;
       }
-      st<V>(Mbar + c, mb);
+      st<V, A>(Mbar + c, mb, hi);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         float s = 0.f;
@@ -497,7 +522,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_first(const UpdTile* __restr
   switch (mi.vw) {
     case 4: first_matrix_tile<4, GT, WT, FP>(t, mi, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, W, ld, R, inv_w,
                                      offset_valid); break;
-    case 2: first_matrix_tile<2, GT, WT, FP>(t, mi, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, W, ld, R, inv_w,
+    case 2: first_matrix_tile<4, GT, WT, FP, 2>(t, mi, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, W, ld, R, inv_w,
                                      offset_valid); break;
     default: first_matrix_tile<1, GT, WT, FP>(t, mi, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, W, ld, R, inv_w,
                                      offset_valid); break;
@@ -507,19 +532,20 @@ __global__ __launch_bounds__(kStreamThreads) void k_first(const UpdTile* __restr
 // ------------------------------------------------------------------ extra power iterations
 // P-bar partial row sums of Mbar Q for one row x the wave's column strip, exactly as the
 // first pass forms them, but reading the stored Mbar (extra power iterations).
-template <int V>
+template <int V, int A = V>
 __device__ __forceinline__ void pbar_mbar_tile(const UpdTile& t, const MatInfo& mi, const float* Mbar,
                                                const float* Qin, float* Ppart, int R) {
   const int cols = mi.cols;
   const int j = t.col_begin + int(threadIdx.x) * V;
   const bool active = j < cols;
+  const bool hi = A == V || j + 4 <= cols;
   const int i = t.row_begin + int(blockIdx.y);
   if (i >= t.row_end) return;
   float qv[V][4];
-  load_q_cols<V>(qv, Qin + mi.q_off, j, R, active);
+  load_q_cols<V>(qv, Qin + mi.q_off, j, R, active, hi);
   float part[4] = {0.f, 0.f, 0.f, 0.f};
   if (active) {
-    const vec_t<V> mb = ldv<V>(Mbar + mi.offset + int64_t(i) * cols + j);
+    const vec_t<V> mb = ldv<V, A>(Mbar + mi.offset + int64_t(i) * cols + j, hi);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       float s = 0.f;
@@ -548,7 +574,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_p_mbar(const UpdTile* __rest
   const MatInfo mi = mats[t.mat];
   switch (mi.vw) {
     case 4: pbar_mbar_tile<4>(t, mi, Mbar, Qin, Ppart, R); break;
-    case 2: pbar_mbar_tile<2>(t, mi, Mbar, Qin, Ppart, R); break;
+    case 2: pbar_mbar_tile<4, 2>(t, mi, Mbar, Qin, Ppart, R); break;
     default: pbar_mbar_tile<1>(t, mi, Mbar, Qin, Ppart, R); break;
   }
 }
@@ -719,6 +745,35 @@ __global__ __launch_bounds__(kMgsThreads) void k_mgs(const MatInfo* __restrict__
 }
 
 // ------------------------------------------------------------------ Q = Mbar^T P
+// One lane's four columns j..j+3 of the row-block partial: sum over rows r0..r1-1 of
+// row(i) (four floats) times P[i, :].  hi false: the row ends at j + 2 (row(i) reads the
+// upper two as zero) and only columns j, j + 1 are written.
+template <int R, typename RowLoad>
+__device__ __forceinline__ void q_cols4(float* out, const float* Pm, int r0, int r1, int j, bool hi,
+                                        RowLoad row) {
+  float acc[4][R];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int k = 0; k < R; ++k) acc[q][k] = 0.f;
+#pragma unroll 8
+  for (int i = r0; i < r1; ++i) {
+    const f4 v = row(i);
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const float pk = Pm[int64_t(i) * R + k];
+      acc[0][k] += v.x * pk;
+      acc[1][k] += v.y * pk;
+      acc[2][k] += v.z * pk;
+      acc[3][k] += v.w * pk;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (q < 2 || hi)
+#pragma unroll
+      for (int k = 0; k < R; ++k) out[int64_t(j + q) * R + k] = acc[q][k];
+}
 template <int R>
 __global__ __launch_bounds__(kQThreads) void k_q_partial(const QTile* __restrict__ tiles,
                                                          const MatInfo* __restrict__ mats,
@@ -733,30 +788,14 @@ __global__ __launch_bounds__(kQThreads) void k_q_partial(const QTile* __restrict
   const float* Pm = P + mi.p_off;
   const float* base = Mbar + mi.offset;
   float* out = Qpart + mi.qpart_off + int64_t(t.blk) * cols * R;
-  if (mi.vw == 4) {
+  if (mi.vw != 1) {
     const int j = t.col_begin + int(threadIdx.x) * 4;
     if (j >= t.col_end) return;
-    float acc[4][R];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int k = 0; k < R; ++k) acc[q][k] = 0.f;
-#pragma unroll 8
-    for (int i = r0; i < r1; ++i) {
-      const f4 v = *reinterpret_cast<const f4*>(base + int64_t(i) * cols + j);
-#pragma unroll
-      for (int k = 0; k < R; ++k) {
-        const float pk = Pm[int64_t(i) * R + k];
-        acc[0][k] += v.x * pk;
-        acc[1][k] += v.y * pk;
-        acc[2][k] += v.z * pk;
-        acc[3][k] += v.w * pk;
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int k = 0; k < R; ++k) out[int64_t(j + q) * R + k] = acc[q][k];
+    const bool hi = j + 4 <= cols;
+    if (mi.vw == 4)
+      q_cols4<R>(out, Pm, r0, r1, j, true, [&](int i) { return ldv<4>(base + int64_t(i) * cols + j); });
+    else
+      q_cols4<R>(out, Pm, r0, r1, j, hi, [&](int i) { return ldv<4, 2>(base + int64_t(i) * cols + j, hi); });
   } else {
     const int j = t.col_begin + int(threadIdx.x);
     if (j >= t.col_end) return;
@@ -811,31 +850,20 @@ __global__ __launch_bounds__(kQThreads) void k_qw_partial(const QTile* __restric
   const GT* gb = G + int64_t(w) * ld + mi.offset;
   const float* eb = E + int64_t(w) * ld + mi.offset;
   float* out = Qwpart + int64_t(w) * qpart_elems + mi.qpart_off + int64_t(t.blk) * cols * R;
-  if (mi.vw == 4) {
+  if (mi.vw != 1) {
     const int j = t.col_begin + int(threadIdx.x) * 4;
     if (j >= t.col_end) return;
-    float acc[4][R];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int k = 0; k < R; ++k) acc[q][k] = 0.f;
-#pragma unroll 4
-    for (int i = r0; i < r1; ++i) {
-      const int64_t c = int64_t(i) * cols + j;
-      const f4 v = ld_nt<4>(gb + c) + ld_nt<4>(eb + c);
-#pragma unroll
-      for (int k = 0; k < R; ++k) {
-        const float pk = Pm[int64_t(i) * R + k];
-        acc[0][k] += v.x * pk;
-        acc[1][k] += v.y * pk;
-        acc[2][k] += v.z * pk;
-        acc[3][k] += v.w * pk;
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int k = 0; k < R; ++k) out[int64_t(j + q) * R + k] = acc[q][k];
+    const bool hi = j + 4 <= cols;
+    if (mi.vw == 4)
+      q_cols4<R>(out, Pm, r0, r1, j, true, [&](int i) {
+        const int64_t c = int64_t(i) * cols + j;
+        return ld_nt<4>(gb + c) + ld_nt<4>(eb + c);
+      });
+    else
+      q_cols4<R>(out, Pm, r0, r1, j, hi, [&](int i) {
+        const int64_t c = int64_t(i) * cols + j;
+        return ld_nt<4, 2>(gb + c, hi) + ld_nt<4, 2>(eb + c, hi);
+      });
   } else {
     const int j = t.col_begin + int(threadIdx.x);
     if (j >= t.col_end) return;
@@ -858,7 +886,7 @@ __global__ __launch_bounds__(kQThreads) void k_qw_partial(const QTile* __restric
 // Matrix tile: u = P Q^T for the thread's columns of each row; E'_w = (G_w + E_w) - u
 // on every worker, the mean of the stored E'_w into `ebar` (carry mode), U once, and
 // the momentum-SGD update in the momentum modes.  1-D tensors: the update is the mean.
-template <int V, typename GT, int WT, bool LOCAL>
+template <int V, typename GT, int WT, bool LOCAL, int A = V>
 __device__ __forceinline__ void apply_matrix_tile(const UpdTile& t, const MatInfo& mi, const GT* G, float* E,
                                                   const float* P, const float* Q, const float* Qw, int64_t q_ws,
                                                   float* update, float* mom, float* x, float* ebar, int W,
@@ -866,8 +894,9 @@ __device__ __forceinline__ void apply_matrix_tile(const UpdTile& t, const MatInf
   const int cols = mi.cols;
   const int j = t.col_begin + int(threadIdx.x) * V;
   if (j >= cols) return;
+  const bool hi = A == V || j + 4 <= cols;
   float qv[V][4];
-  load_q_cols<V>(qv, Q + mi.q_off, j, R, true);
+  load_q_cols<V>(qv, Q + mi.q_off, j, R, true, hi);
   {
     const int i = t.row_begin + int(blockIdx.y);
     if (i >= t.row_end) return;
@@ -877,12 +906,12 @@ __device__ __forceinline__ void apply_matrix_tile(const UpdTile& t, const MatInf
     const int64_t c = mi.offset + int64_t(i) * cols + j;
     vec_t<V> es;
     if constexpr (LOCAL)
-      es = update_workers_local<V, GT, WT>(G, E, W, ld, c, pr, Qw, q_ws, mi.q_off, j, R);
+      es = update_workers_local<V, GT, WT, A>(G, E, W, ld, c, pr, Qw, q_ws, mi.q_off, j, R, hi);
     else
-      es = update_workers<V, GT, WT>(G, E, W, ld, c, u);
-    if (ebar != nullptr) st<V>(ebar + c, es * inv_w);
-    if (update != nullptr) st_nt<V>(update + c, u);
-    if (mode != kCompress) momentum_v<V>(mom, x, c, u, mode, lr, mu);
+      es = update_workers<V, GT, WT, A>(G, E, W, ld, c, u, hi);
+    if (ebar != nullptr) st<V, A>(ebar + c, es * inv_w, hi);
+    if (update != nullptr) st_nt<V, A>(update + c, u, hi);
+    if (mode != kCompress) momentum_v<V, A>(mom, x, c, u, mode, lr, mu, hi);
   }
 }
 
@@ -907,7 +936,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_apply(
   const MatInfo mi = mats[t.mat];
   switch (mi.vw) {
     case 4: apply_matrix_tile<4, GT, WT, LOCAL>(t, mi, G, E, P, Q, Qw, q_ws, update, mom, x, ebar, W, ld, R, mode, lr, mu, inv_w); break;
-    case 2: apply_matrix_tile<2, GT, WT, LOCAL>(t, mi, G, E, P, Q, Qw, q_ws, update, mom, x, ebar, W, ld, R, mode, lr, mu, inv_w); break;
+    case 2: apply_matrix_tile<4, GT, WT, LOCAL, 2>(t, mi, G, E, P, Q, Qw, q_ws, update, mom, x, ebar, W, ld, R, mode, lr, mu, inv_w); break;
     default: apply_matrix_tile<1, GT, WT, LOCAL>(t, mi, G, E, P, Q, Qw, q_ws, update, mom, x, ebar, W, ld, R, mode, lr, mu, inv_w); break;
   }
 }
@@ -919,22 +948,23 @@ __global__ __launch_bounds__(kStreamThreads) void k_apply(
 // M_w(t) = G_w(t) + [M_w(t-1) - U(t-1)], stores M_w(t) back and writes Mbar.
 // k_update is the last pass: the decompressed update (P Q^T, or the mean for 1-D
 // tensors) and the momentum-SGD update; no worker data is touched.
-template <int V>
+template <int V, int A = V>
 __device__ __forceinline__ void update_matrix_tile(const UpdTile& t, const MatInfo& mi, const float* P,
                                                    const float* Q, float* update, float* mom, float* x, int R,
                                                    int mode, float lr, float mu) {
   const int cols = mi.cols;
   const int j = t.col_begin + int(threadIdx.x) * V;
   if (j >= cols) return;
+  const bool hi = A == V || j + 4 <= cols;
   float qv[V][4];
-  load_q_cols<V>(qv, Q + mi.q_off, j, R, true);
+  load_q_cols<V>(qv, Q + mi.q_off, j, R, true, hi);
   for (int i = t.row_begin; i < t.row_end; ++i) {
     float pr[4];
     load_p_row(pr, P + mi.p_off, i, R);
     const vec_t<V> u = pq_row<V>(pr, qv, R);
     const int64_t c = mi.offset + int64_t(i) * cols + j;
-    if (update != nullptr) st_nt<V>(update + c, u);
-    if (mode != kCompress) momentum_v<V>(mom, x, c, u, mode, lr, mu);
+    if (update != nullptr) st_nt<V, A>(update + c, u, hi);
+    if (mode != kCompress) momentum_v<V, A>(mom, x, c, u, mode, lr, mu, hi);
   }
 }
 
@@ -955,7 +985,7 @@ __global__ __launch_bounds__(kUpdThreads) void k_update(
   const MatInfo mi = mats[t.mat];
   switch (mi.vw) {
     case 4: update_matrix_tile<4>(t, mi, P, Q, update, mom, x, R, mode, lr, mu); break;
-    case 2: update_matrix_tile<2>(t, mi, P, Q, update, mom, x, R, mode, lr, mu); break;
+    case 2: update_matrix_tile<4, 2>(t, mi, P, Q, update, mom, x, R, mode, lr, mu); break;
     default: update_matrix_tile<1>(t, mi, P, Q, update, mom, x, R, mode, lr, mu); break;
   }
 }
@@ -964,15 +994,16 @@ __global__ __launch_bounds__(kUpdThreads) void k_update(
 // of a deferred-mode error buffer), on the worker-pass tiles; 1-D tensors are skipped.
 // The subtracted value is computed exactly as the first pass subtracts it.  E and out
 // may alias.
-template <int V>
+template <int V, int A = V>
 __device__ __forceinline__ void materialize_tile(const UpdTile& t, const MatInfo& mi, const float* E, float* out,
                                                  const float* Pprev, const float* Qprev, int W, int64_t ld, int R,
                                                  int offset_valid) {
   const int cols = mi.cols;
   const int j = t.col_begin + int(threadIdx.x) * V;
   if (j >= cols) return;
+  const bool hi = A == V || j + 4 <= cols;
   float qp[V][4];
-  load_q_cols<V>(qp, Qprev + mi.q_off, j, R, offset_valid != 0);
+  load_q_cols<V>(qp, Qprev + mi.q_off, j, R, offset_valid != 0, hi);
   {
     const int i = t.row_begin + int(blockIdx.y);
     if (i >= t.row_end) return;
@@ -980,7 +1011,7 @@ __device__ __forceinline__ void materialize_tile(const UpdTile& t, const MatInfo
     if (offset_valid) load_p_row(pp, Pprev + mi.p_off, i, R);
     const vec_t<V> up = pq_row<V>(pp, qp, R);
     const int64_t c = mi.offset + int64_t(i) * cols + j;
-    for (int w = 0; w < W; ++w) st_nt<V>(out + w * ld + c, ld_nt<V>(E + w * ld + c) - up);
+    for (int w = 0; w < W; ++w) st_nt<V, A>(out + w * ld + c, ld_nt<V, A>(E + w * ld + c, hi) - up, hi);
   }
 }
 
@@ -993,7 +1024,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_materialize(
   const MatInfo mi = mats[t.mat];
   switch (mi.vw) {
     case 4: materialize_tile<4>(t, mi, E, out, Pprev, Qprev, W, ld, R, offset_valid); break;
-    case 2: materialize_tile<2>(t, mi, E, out, Pprev, Qprev, W, ld, R, offset_valid); break;
+    case 2: materialize_tile<4, 2>(t, mi, E, out, Pprev, Qprev, W, ld, R, offset_valid); break;
     default: materialize_tile<1>(t, mi, E, out, Pprev, Qprev, W, ld, R, offset_valid); break;
   }
 }

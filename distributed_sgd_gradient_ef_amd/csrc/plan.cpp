@@ -116,7 +116,7 @@ extern "C" psgd_status psgd_plan_create(const psgd_layer* layers, int32_t n_laye
         mi.vw = (cols % 4 == 0) ? 4 : (cols % 2 == 0) ? 2 : 1;
         mi.qpart_off = qpart;
         qpart += int64_t(mi.nblk) * cols * r;
-        const int64_t strip_cols = int64_t(kStreamThreads) * mi.vw;
+        const int64_t strip_cols = int64_t(kStreamThreads) * (mi.vw == 1 ? 1 : 4);
         mi.nstrips = int32_t((cols + strip_cols - 1) / strip_cols);
         mi.ppart_off = plan->ppart_elems;
         plan->ppart_elems += int64_t(mi.nstrips) * rows * r;
@@ -149,7 +149,7 @@ extern "C" psgd_status psgd_plan_create(const psgd_layer* layers, int32_t n_laye
       for (const psgd_layer_info& li : plan->layers) {
         if (li.compressed) {
           const MatInfo& m = plan->mats[size_t(li.matrix_index)];
-          const int32_t strip = threads * m.vw;
+          const int32_t strip = threads * (m.vw == 1 ? 1 : 4);
           for (int32_t r0 = 0; r0 < m.rows; r0 += rows_per_tile)
             for (int32_t c0 = 0; c0 < m.cols; c0 += strip) {
               UpdTile u{};
@@ -178,7 +178,7 @@ extern "C" psgd_status psgd_plan_create(const psgd_layer* layers, int32_t n_laye
     build_tiles(plan->utiles, kUpdRowsPerTile, kUpdThreads);
     for (size_t mi = 0; mi < plan->mats.size(); ++mi) {
       const MatInfo& m = plan->mats[mi];
-      const int32_t strip = kQThreads * (m.vw == 4 ? 4 : 1);  // the Q pass has no 2-wide form
+      const int32_t strip = kQThreads * (m.vw == 1 ? 1 : 4);
       for (int32_t b = 0; b < m.nblk; ++b)
         for (int32_t c = 0; c < m.cols; c += strip)
           plan->qtiles.push_back(QTile{int32_t(mi), b, c, std::min(m.cols, c + strip)});

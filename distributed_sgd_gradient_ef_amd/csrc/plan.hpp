@@ -49,7 +49,8 @@ struct MatInfo {
   int32_t rows, cols;
   int32_t rows_per_blk;  // rows summed into one Q partial
   int32_t nblk;          // number of Q partials (row blocks)
-  int32_t vw;            // elements per lane in the row passes: 4 if cols % 4 == 0, 2 if even, else 1
+  int32_t vw;            // row alignment in floats: 4 if cols % 4 == 0, 2 if even, else 1 (4 and 2
+                         // run four columns per lane, 2 as two 8-byte halves; 1 one column)
   int32_t nstrips;       // column strips of the worker passes (P-bar partials per row)
 };
 
