@@ -1,7 +1,8 @@
-"""Seeded synthetic workloads for the PowerSGD and rTop-k compression steps.
+"""Seeded synthetic workloads for the PowerSGD, rTop-k and Spectral-ATOMO compression steps.
 
 This module only draws inputs (gradients, the initial Q, parameters, the random ranks
-that pick rTop-k's subset) and lists layer shapes.  It holds none of the compression arithmetic, so both the GPU library's tests
+that pick rTop-k's subset, the uniforms behind Spectral-ATOMO's Bernoulli draws) and
+lists layer shapes.  It holds none of the compression arithmetic, so both the GPU library's tests
 and the CPU oracle can consume what it produces.
 
 Every draw comes from a Philox4x32-10 counter-based stream (numpy's ``Philox`` bit
@@ -27,7 +28,7 @@ import numpy as np
 Shape = Tuple[int, int]  # (rows, cols); a 1-D tensor of length d is (1, d)
 
 # purpose tags for the stream keys
-_P_FACTOR_U, _P_FACTOR_V, _P_NOISE, _P_Q0, _P_PARAM, _P_ROWS, _P_DRIFT, _P_RANKS = range(8)
+_P_FACTOR_U, _P_FACTOR_V, _P_NOISE, _P_Q0, _P_PARAM, _P_ROWS, _P_DRIFT, _P_RANKS, _P_UNIFORM = range(9)
 
 
 # --------------------------------------------------------------------------- shapes
@@ -109,6 +110,7 @@ class Workload:
     mu: float = 0.0
     keep_frac: float = 0.01  # rTop-k: entries sent per tensor, as a fraction of its size
     top_factor: int = 2      # rTop-k: top-set size as a multiple of the sent count
+    atomo_budget: float = 2.0  # Spectral-ATOMO: expected atoms sent per matrix (sum of p_i)
 
     @property
     def matrix_shapes(self) -> List[Shape]:
@@ -145,6 +147,10 @@ def workload(name: str, **overrides) -> Workload:
         # rTop-k on the LSTM shapes (a 5%-row-sparse embedding gradient), 8 workers
         "lstm_rtopk": dict(name="lstm_rtopk", shapes=tuple(lstm_wikitext2_shapes()), rank=4, workers=8,
                            steps=2, seed=1007, signal="lstm"),
+        # Spectral-ATOMO on ResNet-18 shapes: same gradient recipe, 16 workers, an
+        # expected two atoms per matrix (about PowerSGD rank 2's message size)
+        "resnet18_atomo": dict(name="resnet18_atomo", shapes=tuple(resnet18_cifar_shapes()), rank=2,
+                               workers=16, steps=3, seed=1008, signal="resnet", atomo_budget=2.0),
         # full EF-SGD with momentum on ResNet-18 shapes, drifting subspace
         "resnet18_momentum": dict(name="resnet18_momentum", shapes=tuple(resnet18_cifar_shapes()),
                                   rank=4, workers=16, steps=200, seed=1005, signal="resnet",
@@ -311,6 +317,12 @@ def rtopk_counts(wl: Workload) -> Tuple[List[int], List[int]]:
 def rtopk_ranks(wl: Workload, step: int, worker: int, layer: int, top: int) -> np.ndarray:
     """Random ranks of one tensor's top set: a uniform permutation of 0..top-1 (uint32)."""
     return stream(wl.seed, _P_RANKS, step, worker, layer).permutation(top).astype(np.uint32)
+
+
+def atomo_uniforms(wl: Workload, step: int, worker: int, layer: int, k: int) -> np.ndarray:
+    """Spectral-ATOMO's Bernoulli draws for one worker's matrix: k uniforms in [0, 1)
+    (float32), one per singular value in descending order."""
+    return stream(wl.seed, _P_UNIFORM, step, worker, layer).random(k, dtype=np.float32)
 
 
 def q0(wl: Workload, layer: int) -> np.ndarray:
