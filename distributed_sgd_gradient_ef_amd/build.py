@@ -16,7 +16,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_PATH = os.path.join(HERE, "libpsgd.so")
-SOURCES = [os.path.join(HERE, "csrc", name) for name in ("plan.cpp", "kernels.hip", "rtopk.hip")]
+SOURCES = [os.path.join(HERE, "csrc", name) for name in ("plan.cpp", "kernels.hip", "rtopk.hip", "atomo.hip")]
 INCLUDE = [os.path.join(ROOT, "include"), os.path.join(HERE, "csrc")]
 ARCH = "gfx950"
 

@@ -1,0 +1,1233 @@
+// Spectral-ATOMO: the gfx950 kernels and the host side of psgd_atomo.h.  Operation: the
+// review page "ATOMO: Communication-efficient Learning via Atomic Sparsification",
+// section "Proposed method" -- the atoms of a layer gradient are the rank-one terms of
+// its singular value decomposition; atom i is kept with probability p_i = min(1, c
+// sigma_i) (sum p_i = s) and divided by p_i.
+//
+// A problem is one layer matrix of one worker; k = min(n, m) is its short side.  The
+// singular values are the square roots of the eigenvalues of the k x k Gram matrix of
+// the short side (G G^T when n <= m, else G^T G), and a sent atom needs only the one
+// eigenvector on that side: the other factor is G^T u / p (or G v / p), one more pass
+// over G.  Launches, each covering every problem of every worker:
+//
+//   at_gram       the Gram matrix, 64 x 64 output tiles of its lower block triangle
+//                 (mirrored into the upper one), the contraction over the long side
+//                 staged through LDS
+//   at_tridiag    one workgroup per problem: Householder reduction of the Gram matrix
+//                 to tridiagonal form.  Each step forms the next reflector from the
+//                 updated column, then one pass over the trailing block both applies
+//                 the previous rank-2 update and forms the product with the new
+//                 reflector; reflector q is kept in row q
+//   at_eig        every eigenvalue of the tridiagonal matrix by bisection on Sturm
+//                 counts (one per thread); sigma_i = sqrt(max(eigenvalue, 0))
+//   at_sample     the closed-form probabilities (the largest atoms saturate first),
+//                 the Bernoulli decisions x_i < p_i, and the list of sent atoms
+//   at_vectors    inverse iteration on the tridiagonal matrix (partial pivoting, float64)
+//                 for each sent atom, orthogonalised against the problem's earlier sent
+//                 atoms after every solve
+//   at_backxform  the sent eigenvectors back through the reflectors: the unit factor
+//   at_factor     the other factor, G^T u / p or G v / p, in one pass over G
+//   at_update     U = (1/W) sum over workers and their sent atoms of a b^T (and the
+//                 plain mean for tensors that are not compressed)
+//
+// Every reduction has a fixed order, so a step is bitwise reproducible.
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
+
+#include <algorithm>
+#include <cfloat>
+#include <cmath>
+#include <cstdio>
+#include <map>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "plan.hpp"
+#include "psgd_atomo.h"
+
+namespace psgd {
+namespace atm {
+
+constexpr int kMaxK = PSGD_ATOMO_MAX_K;
+constexpr int kGramTile = 64;
+constexpr int kGramKC = 16;
+constexpr int kGramThreads = 256;
+constexpr int kTriThreads = 1024;
+// rows per wave per batch of the trailing-block pass (fewer for the widest rows, whose
+// values would not fit in registers)
+template <int KT>
+constexpr int tri_rows() { return KT >= 16 ? 2 : 4; }
+constexpr int kEigThreads = 1024;
+constexpr int kSampleThreads = 1024;
+constexpr int kVecThreads = 256;
+constexpr int kBackThreads = 256;
+constexpr int kFactorThreads = 256;
+constexpr int kFactorGroup = 4;  // atoms per pass over G
+constexpr int kAtUpdThreads = 256;
+constexpr int kAtUpdRows = 8;
+
+struct AtMat {
+  int64_t offset;    // element offset inside a worker slice
+  int64_t sv_off;    // offset in a worker's row of uniforms / sigma / prob / index
+  int64_t atom_off;  // offset in a worker's row of atoms
+  int64_t b_off;     // offset of the k x k Gram matrix in a worker's Gram workspace
+  int32_t rows, cols, k, left;  // left: k == rows (G G^T), else k == cols (G^T G)
+  int32_t mat_index, pad;
+};
+
+struct GramTile {
+  int32_t mat, ti, tj, pad;
+};
+
+// at_factor: a column range [begin, end) of a left problem (k == rows), or a row range of
+// a right problem
+struct FactorTile {
+  int32_t mat, begin, end, pad;
+};
+
+// at_update: rows [row0, row1) x columns [col0, col0 + kAtUpdThreads) of matrix `mat`, or
+// for mat < 0 the flat range [begin, end) of an uncompressed tensor
+struct AtUpdTile {
+  int64_t begin, end;
+  int32_t mat, row0, row1, col0;
+};
+
+enum KernelId { kGram = 0, kTridiag, kEig, kSample, kVectors, kBack, kFactor, kUpdate, kNumK };
+const char* const kNames[kNumK] = {"at_gram",    "at_tridiag",   "at_eig",    "at_sample",
+                                   "at_vectors", "at_backxform", "at_factor", "at_update"};
+
+}  // namespace atm
+}  // namespace psgd
+
+struct psgd_atomo_plan {
+  int32_t n_workers = 0;
+  double budget = 0.0;
+  std::vector<psgd_atomo_layer_info> info;
+  std::vector<psgd::atm::AtMat> mats;
+  std::vector<psgd::atm::GramTile> gtiles;
+  std::vector<psgd::atm::FactorTile> ftiles;
+  std::vector<psgd::atm::AtUpdTile> utiles;
+  int64_t worker_stride = 0, numel = 0, sv_total = 0, atom_total = 0, gram_total = 0;
+  uint64_t ws_gram = 0, ws_y = 0, ws_tau = 0, ws_d = 0, ws_e = 0, ws_lam = 0, workspace_bytes = 0;
+  uint64_t model_bytes = 0;
+  std::map<int, void*> dev;  // device copy of the tables, per HIP device
+  bool timing = false;
+  std::vector<psgd::PendingTiming> pending;
+  std::vector<hipEvent_t> event_pool;
+  psgd::KernelStat stats[psgd::atm::kNumK];
+};
+
+namespace psgd {
+namespace atm {
+namespace {
+
+// ------------------------------------------------------------------ reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Sum over the workgroup; every thread gets the total (waves added in index order).
+template <typename T>
+__device__ T block_sum(T v, T* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  T s = T(0);
+  const int nw = int(blockDim.x) >> 6;
+  for (int i = 0; i < nw; ++i) s += red[i];
+  return s;
+}
+
+__device__ __forceinline__ float block_min(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  float s = red[0];
+  const int nw = int(blockDim.x) >> 6;
+  for (int i = 1; i < nw; ++i) s = fminf(s, red[i]);
+  return s;
+}
+
+__device__ __forceinline__ float block_max(float v, float* red) { return -block_min(-v, red); }
+
+// ------------------------------------------------------------------ at_gram
+__global__ __launch_bounds__(kGramThreads) void at_gram(const GramTile* __restrict__ tiles,
+                                                        const AtMat* __restrict__ mats,
+                                                        const float* __restrict__ G, int64_t ld,
+                                                        float* __restrict__ gram, int64_t gram_ws) {
+  const GramTile t = tiles[blockIdx.x];
+  const AtMat M = mats[t.mat];
+  const int w = blockIdx.y;
+  const float* g = G + int64_t(w) * ld + M.offset;
+  float* B = gram + int64_t(w) * gram_ws + M.b_off;
+  const int k = M.k, cols = M.cols;
+  const int L = M.left ? M.cols : M.rows;  // contraction length
+  const int a0 = t.ti * kGramTile, b0 = t.tj * kGramTile;
+  __shared__ float sa[kGramKC][kGramTile + 4];
+  __shared__ float sb[kGramKC][kGramTile + 4];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+  for (int c0 = 0; c0 < L; c0 += kGramKC) {
+    for (int e = threadIdx.x; e < kGramTile * kGramKC; e += kGramThreads) {
+      if (M.left) {  // element (short index a, long index c) = G[a][c]
+        const int a = e / kGramKC, c = e % kGramKC;
+        const bool cin = c0 + c < L;
+        sa[c][a] = (cin && a0 + a < k) ? g[int64_t(a0 + a) * cols + c0 + c] : 0.f;
+        sb[c][a] = (cin && b0 + a < k) ? g[int64_t(b0 + a) * cols + c0 + c] : 0.f;
+      } else {       // element (short index a, long index c) = G[c][a]
+        const int c = e / kGramTile, a = e % kGramTile;
+        const bool cin = c0 + c < L;
+        sa[c][a] = (cin && a0 + a < k) ? g[int64_t(c0 + c) * cols + a0 + a] : 0.f;
+        sb[c][a] = (cin && b0 + a < k) ? g[int64_t(c0 + c) * cols + b0 + a] : 0.f;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kGramKC; ++kk) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = sa[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bv[j] = sb[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  // A diagonal tile computes both (a, b) and (b, a) with the same products in the same
+  // order, so the stored matrix is exactly symmetric.
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int a = a0 + ty * 4 + i, b = b0 + tx * 4 + j;
+      if (a < k && b < k) {
+        B[int64_t(a) * k + b] = acc[i][j];
+        if (t.ti != t.tj) B[int64_t(b) * k + a] = acc[i][j];
+      }
+    }
+}
+
+// ------------------------------------------------------------------ at_tridiag
+// Reflector q (q = 0..k-3) is H_q = I - tau_q v_q v_q^T with v_q[q+1] = 1 and zeros above;
+// H_q maps column q of the current matrix below the diagonal to e[q] * e_{q+1}.  After
+// step q the trailing block (rows and columns > q) holds H_q A H_q there, applied as
+// A - v w^T - w v^T with w = tau A v - (tau^2 / 2)(v^T A v) v.
+constexpr int kTriWaves = kTriThreads / 64;
+
+struct TriShared {
+  float V[2][kMaxK], Wv[2][kMaxK], P[kMaxK];
+  float red[kTriWaves];
+};
+
+template <int KT>
+__device__ void tridiag_body(const AtMat& M, float* __restrict__ A, float* __restrict__ tau, float* __restrict__ d,
+                             float* __restrict__ e, TriShared& sh) {
+  const int k = M.k;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int kWaves = kTriWaves;
+  float (&V)[2][kMaxK] = sh.V;
+  float (&Wv)[2][kMaxK] = sh.Wv;
+  float* P = sh.P;
+  float* red = sh.red;
+  int cur = 0;
+  for (int i = tid; i < k; i += kTriThreads) {
+    V[0][i] = 0.f;
+    Wv[0][i] = 0.f;
+  }
+  __syncthreads();
+  for (int q = 0; q + 2 < k; ++q) {
+    const float* vp = V[cur];
+    const float* wp = Wv[cur];
+    float* vn = V[cur ^ 1];
+    float* wn = Wv[cur ^ 1];
+    // column q below the diagonal, with the previous reflector's update applied
+    const float vq = vp[q], wq = wp[q];
+    for (int i = q + 1 + tid; i < k; i += kTriThreads) vn[i] = A[int64_t(i) * k + q] - vp[i] * wq - wp[i] * vq;
+    if (tid == 0) d[q] = A[int64_t(q) * k + q] - 2.f * vq * wq;
+    __syncthreads();
+    float part = 0.f;
+    for (int i = q + 2 + tid; i < k; i += kTriThreads) part = fmaf(vn[i], vn[i], part);
+    const float ss = block_sum(part, red);
+    const float alpha = vn[q + 1];
+    float tq = 0.f, beta = alpha, inv = 0.f;
+    if (ss != 0.f) {
+      const float mu = sqrtf(fmaf(alpha, alpha, ss));
+      beta = alpha >= 0.f ? -mu : mu;
+      tq = (beta - alpha) / beta;
+      inv = 1.f / (alpha - beta);
+    }
+    __syncthreads();  // everyone has read alpha before vn is rescaled
+    for (int i = q + 1 + tid; i < k; i += kTriThreads) {
+      const float v = (i == q + 1) ? 1.f : vn[i] * inv;
+      vn[i] = v;
+      A[int64_t(q) * k + i] = v;
+    }
+    if (tid == 0) {
+      tau[q] = tq;
+      e[q] = beta;
+    }
+    __syncthreads();
+    // trailing block: apply the previous update (none at q = 0) and form A v_q
+    const int c0 = q + 1;
+    constexpr int kTriRows = tri_rows<KT>();
+    for (int rb = c0 + wave * kTriRows; rb < k; rb += kWaves * kTriRows) {
+      float a[kTriRows][KT];
+#pragma unroll
+      for (int u = 0; u < kTriRows; ++u)
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+          const int r = rb + u, c = c0 + lane + 64 * t;
+          a[u][t] = (r < k && c < k) ? A[int64_t(r) * k + c] : 0.f;
+        }
+#pragma unroll
+      for (int u = 0; u < kTriRows; ++u) {
+        const int r = rb + u;
+        if (r >= k) break;
+        const float vr = vp[r], wr = wp[r];
+        float s = 0.f;
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+          const int c = c0 + lane + 64 * t;
+          if (c < k) {
+            const float x = a[u][t] - vr * wp[c] - wr * vp[c];
+            if (q > 0) A[int64_t(r) * k + c] = x;
+            s = fmaf(x, vn[c], s);
+          }
+        }
+        s = wave_sum(s);
+        if (lane == 0) P[r] = s;
+      }
+    }
+    __syncthreads();
+    float part2 = 0.f;
+    for (int r = c0 + tid; r < k; r += kTriThreads) part2 = fmaf(P[r], vn[r], part2);
+    const float vav = block_sum(part2, red);  // v^T A v
+    const float half = 0.5f * tq * tq * vav;
+    for (int r = c0 + tid; r < k; r += kTriThreads) wn[r] = tq * P[r] - half * vn[r];
+    __syncthreads();
+    cur ^= 1;
+  }
+  // the last 2 x 2 block (rows and columns k-2, k-1) with the last reflector's update
+  if (tid == 0) {
+    const float* vp = V[cur];
+    const float* wp = Wv[cur];
+    const int i0 = k - 2, i1 = k - 1;
+    d[i0] = A[int64_t(i0) * k + i0] - 2.f * vp[i0] * wp[i0];
+    e[i0] = A[int64_t(i1) * k + i0] - vp[i1] * wp[i0] - wp[i1] * vp[i0];
+    d[i1] = A[int64_t(i1) * k + i1] - 2.f * vp[i1] * wp[i1];
+  }
+}
+
+__global__ __launch_bounds__(kTriThreads) void at_tridiag(const AtMat* __restrict__ mats, float* __restrict__ gram,
+                                                          int64_t gram_ws, float* __restrict__ tau_ws,
+                                                          float* __restrict__ d_ws, float* __restrict__ e_ws,
+                                                          int64_t sv_total) {
+  const AtMat M = mats[blockIdx.x];
+  const int64_t w = blockIdx.y;
+  float* A = gram + w * gram_ws + M.b_off;
+  float* tau = tau_ws + w * sv_total + M.sv_off;
+  float* d = d_ws + w * sv_total + M.sv_off;
+  float* e = e_ws + w * sv_total + M.sv_off;
+  __shared__ TriShared sh;
+  const int kt = (M.k + 63) / 64;
+  if (kt <= 1) tridiag_body<1>(M, A, tau, d, e, sh);
+  else if (kt <= 2) tridiag_body<2>(M, A, tau, d, e, sh);
+  else if (kt <= 4) tridiag_body<4>(M, A, tau, d, e, sh);
+  else if (kt <= 8) tridiag_body<8>(M, A, tau, d, e, sh);
+  else tridiag_body<16>(M, A, tau, d, e, sh);
+}
+
+// ------------------------------------------------------------------ at_eig
+// Number of eigenvalues of the tridiagonal (d, e^2) below x (Sturm sequence; a pivot
+// smaller than pivmin is replaced by -pivmin).
+__device__ __forceinline__ int sturm_below(const float* sd, const float* se2, int k, float x, float pivmin) {
+  float q = sd[0] - x;
+  if (fabsf(q) < pivmin) q = -pivmin;
+  int c = q < 0.f;
+  for (int t = 1; t < k; ++t) {
+    q = (sd[t] - x) - se2[t - 1] / q;
+    if (fabsf(q) < pivmin) q = -pivmin;
+    c += q < 0.f;
+  }
+  return c;
+}
+
+__global__ __launch_bounds__(kEigThreads) void at_eig(const AtMat* __restrict__ mats, const float* __restrict__ d_ws,
+                                                      const float* __restrict__ e_ws, float* __restrict__ lam_ws,
+                                                      float* __restrict__ sigma, int64_t sv_total) {
+  const AtMat M = mats[blockIdx.x];
+  const int64_t w = blockIdx.y;
+  const int k = M.k, tid = threadIdx.x;
+  const float* d = d_ws + w * sv_total + M.sv_off;
+  const float* e = e_ws + w * sv_total + M.sv_off;
+  float* lam = lam_ws + w * sv_total + M.sv_off;
+  float* sig = sigma + w * sv_total + M.sv_off;
+  __shared__ float sd[kMaxK], se2[kMaxK];
+  __shared__ float red[kEigThreads / 64];
+  float lo = FLT_MAX, hi = -FLT_MAX, e2max = 0.f;
+  for (int i = tid; i < k; i += kEigThreads) {
+    const float di = d[i];
+    const float el = i > 0 ? fabsf(e[i - 1]) : 0.f, er = i + 1 < k ? fabsf(e[i]) : 0.f;
+    sd[i] = di;
+    if (i + 1 < k) {
+      se2[i] = er * er;
+      e2max = fmaxf(e2max, er * er);
+    }
+    lo = fminf(lo, di - el - er);
+    hi = fmaxf(hi, di + el + er);
+  }
+  const float glo = block_min(lo, red);
+  const float ghi = block_max(hi, red);
+  const float gmax = block_max(e2max, red);
+  const float tnorm = fmaxf(fabsf(glo), fabsf(ghi));
+  const float pivmin = FLT_MIN * fmaxf(1.f, gmax);
+  const float slack = 4.f * FLT_EPSILON * tnorm + 2.f * pivmin;
+  const float abstol = 4.f * FLT_EPSILON * tnorm;
+  __syncthreads();
+  for (int idx = tid; idx < k; idx += kEigThreads) {
+    float a = glo - slack, b = ghi + slack;
+    for (int it = 0; it < 96; ++it) {
+      if (b - a <= abstol) break;
+      const float mid = 0.5f * (a + b);
+      if (mid <= a || mid >= b) break;
+      if (sturm_below(sd, se2, k, mid, pivmin) > idx) b = mid;
+      else a = mid;
+    }
+    const float l = 0.5f * (a + b);
+    lam[idx] = l;
+    sig[k - 1 - idx] = sqrtf(fmaxf(l, 0.f));
+  }
+}
+
+// ------------------------------------------------------------------ at_sample
+// p_i = 1 for the j* largest atoms and c sigma_i for the rest, where j* is the first j
+// (in descending order) with sigma_j (s - j) <= sum_{i >= j} sigma_i, and c = (s - j*) /
+// sum_{i >= j*} sigma_i; atoms with sigma_i = 0 get 0.
+__global__ __launch_bounds__(kSampleThreads) void at_sample(const AtMat* __restrict__ mats,
+                                                            const float* __restrict__ sigma,
+                                                            const float* __restrict__ uniforms,
+                                                            float* __restrict__ prob, int32_t* __restrict__ index,
+                                                            int32_t* __restrict__ count, int64_t sv_total,
+                                                            int32_t n_mats, float budget) {
+  const AtMat M = mats[blockIdx.x];
+  const int64_t w = blockIdx.y;
+  const int k = M.k, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int kWaves = kSampleThreads / 64;
+  const int64_t base = w * sv_total + M.sv_off;
+  __shared__ float ssum[kWaves];
+  __shared__ int sint[kWaves];
+  __shared__ int spos[kWaves];
+  const float sg = tid < k ? sigma[base + tid] : 0.f;
+  // suffix sums S_j = sum_{i >= j} sigma_i: an inclusive scan from the end, waves taken
+  // from the last one down, lanes from 63 down
+  float v = sg;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float n = __shfl_down(v, o, 64);
+    if (lane + o < 64) v += n;
+  }
+  if (lane == 0) ssum[wave] = v;  // the wave's total
+  __syncthreads();
+  float after = 0.f;
+  for (int i = kWaves - 1; i > wave; --i) after += ssum[i];
+  const float S = v + after;
+  // nnz and j*
+  const bool nz = tid < k && sg > 0.f;
+  const bool stop = nz && sg * (budget - float(tid)) <= S;
+  int cand = stop ? tid : k;
+  int nzc = nz ? 1 : 0;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    cand = min(cand, __shfl_xor(cand, o, 64));
+    nzc += __shfl_xor(nzc, o, 64);
+  }
+  __syncthreads();
+  if (lane == 0) {
+    sint[wave] = cand;
+    spos[wave] = nzc;
+  }
+  __syncthreads();
+  int jstar = k, nnz = 0;
+  for (int i = 0; i < kWaves; ++i) {
+    jstar = min(jstar, sint[i]);
+    nnz += spos[i];
+  }
+  jstar = min(jstar, nnz);
+  __shared__ float s_c;
+  if (tid == jstar && jstar < nnz) s_c = (budget - float(jstar)) / S;
+  __syncthreads();
+  const float c = jstar < nnz ? s_c : 0.f;
+  float p = 0.f;
+  if (tid < k && sg > 0.f) p = tid < jstar ? 1.f : fminf(1.f, c * sg);
+  const bool sent = tid < k && uniforms[base + tid] < p;
+  if (tid < k) prob[base + tid] = p;
+  // positions of the sent atoms (ascending)
+  const uint64_t ballot = __ballot(sent);
+  const int below = __popcll(ballot & ((uint64_t(1) << lane) - 1));
+  __syncthreads();
+  if (lane == 0) spos[wave] = __popcll(ballot);
+  __syncthreads();
+  int before = 0, total = 0;
+  for (int i = 0; i < kWaves; ++i) {
+    if (i < wave) before += spos[i];
+    total += spos[i];
+  }
+  if (tid < k) index[base + tid] = -1;
+  __syncthreads();
+  if (sent) index[base + before + below] = tid;
+  if (tid == 0) count[w * n_mats + M.mat_index] = total;
+}
+
+// ------------------------------------------------------------------ at_vectors
+// Inverse iteration for the eigenvector of the tridiagonal (d, e) at eigenvalue lam:
+// Gaussian elimination with partial pivoting of T - lam I (one thread, float64), three
+// solves, each followed by orthogonalisation against the problem's earlier sent atoms
+// and normalisation.
+__global__ __launch_bounds__(kVecThreads) void at_vectors(const AtMat* __restrict__ mats,
+                                                          const float* __restrict__ d_ws,
+                                                          const float* __restrict__ e_ws,
+                                                          const float* __restrict__ lam_ws,
+                                                          const int32_t* __restrict__ index,
+                                                          const int32_t* __restrict__ count, float* __restrict__ Y,
+                                                          int64_t gram_ws, int64_t sv_total, int32_t n_mats) {
+  const AtMat M = mats[blockIdx.x];
+  const int64_t w = blockIdx.y;
+  const int k = M.k, tid = threadIdx.x;
+  const int cnt = count[w * n_mats + M.mat_index];
+  if (cnt == 0) return;
+  const float* d = d_ws + w * sv_total + M.sv_off;
+  const float* e = e_ws + w * sv_total + M.sv_off;
+  const float* lam = lam_ws + w * sv_total + M.sv_off;
+  const int32_t* idx = index + w * sv_total + M.sv_off;
+  float* y_all = Y + w * gram_ws + M.b_off;  // sent atom j's vector at j * k
+  __shared__ double sd[kMaxK], se[kMaxK];
+  __shared__ double u0[kMaxK], u1[kMaxK], u2[kMaxK], ml[kMaxK];
+  __shared__ unsigned char sw[kMaxK];
+  __shared__ double y[kMaxK];
+  __shared__ double red[kVecThreads / 64];
+  __shared__ double s_tiny;
+  double tn = 0.0;
+  for (int i = tid; i < k; i += kVecThreads) {
+    sd[i] = double(d[i]);
+    se[i] = i + 1 < k ? double(e[i]) : 0.0;
+    tn = fmax(tn, fabs(sd[i]) + 2.0 * fabs(se[i]));
+  }
+  // the largest row sum bounds ||T||; pivots below 2^-24 ||T|| are raised to it
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) tn = fmax(tn, __shfl_xor(tn, o, 64));
+  if ((tid & 63) == 0) red[tid >> 6] = tn;
+  __syncthreads();
+  if (tid == 0) {
+    double m = 0.0;
+    for (int i = 0; i < kVecThreads / 64; ++i) m = fmax(m, red[i]);
+    s_tiny = fmax(m, 1e-300) * 0x1p-24;
+  }
+  __syncthreads();
+  const double tiny = s_tiny;
+  for (int j = 0; j < cnt; ++j) {
+    const int ei = k - 1 - idx[j];  // eigenvalue index, ascending
+    const double l = double(lam[ei]);
+    if (tid == 0) {
+      double cd = sd[0] - l, c1 = k > 1 ? se[0] : 0.0, c2 = 0.0;
+      for (int t = 0; t + 1 < k; ++t) {
+        const double sub = se[t], nd = sd[t + 1] - l, ns = t + 2 < k ? se[t + 1] : 0.0;
+        if (fabs(cd) >= fabs(sub)) {
+          double piv = cd;
+          if (fabs(piv) < tiny) piv = piv < 0.0 ? -tiny : tiny;
+          const double m = sub / piv;
+          u0[t] = piv;
+          u1[t] = c1;
+          u2[t] = c2;
+          ml[t] = m;
+          sw[t] = 0;
+          cd = nd - m * c1;
+          c1 = ns - m * c2;
+        } else {
+          const double m = cd / sub;
+          u0[t] = sub;
+          u1[t] = nd;
+          u2[t] = ns;
+          ml[t] = m;
+          sw[t] = 1;
+          cd = c1 - m * nd;
+          c1 = c2 - m * ns;
+        }
+        c2 = 0.0;
+      }
+      if (fabs(cd) < tiny) cd = cd < 0.0 ? -tiny : tiny;
+      u0[k - 1] = cd;
+      u1[k - 1] = 0.0;
+      u2[k - 1] = 0.0;
+    }
+    // a fixed start vector with entries in [0.5, 1.5)
+    for (int i = tid; i < k; i += kVecThreads) {
+      const uint32_t h = (uint32_t(i) + 1u) * 2654435761u ^ (uint32_t(j) + 1u) * 40503u;
+      y[i] = 0.5 + double((h >> 8) & 0xffffu) / 65536.0;
+    }
+    __syncthreads();
+    for (int it = 0; it < 3; ++it) {
+      if (tid == 0) {
+        // forward: apply the row operations to the right-hand side, in place
+        double cr = y[0];
+        for (int t = 0; t + 1 < k; ++t) {
+          const double nr = y[t + 1];
+          if (sw[t] == 0) {
+            y[t] = cr;
+            cr = nr - ml[t] * cr;
+          } else {
+            y[t] = nr;
+            cr = cr - ml[t] * nr;
+          }
+        }
+        y[k - 1] = cr;
+        // back substitution with the upper factor (diagonal and two above it)
+        double z1 = 0.0, z2 = 0.0;
+        for (int t = k - 1; t >= 0; --t) {
+          const double z = (y[t] - u1[t] * z1 - u2[t] * z2) / u0[t];
+          y[t] = z;
+          z2 = z1;
+          z1 = z;
+        }
+      }
+      __syncthreads();
+      for (int jj = 0; jj < j; ++jj) {
+        const float* yo = y_all + int64_t(jj) * k;
+        double part = 0.0;
+        for (int i = tid; i < k; i += kVecThreads) part += y[i] * double(yo[i]);
+        const double dot = block_sum(part, red);
+        for (int i = tid; i < k; i += kVecThreads) y[i] -= dot * double(yo[i]);
+        __syncthreads();
+      }
+      double part = 0.0;
+      for (int i = tid; i < k; i += kVecThreads) part += y[i] * y[i];
+      const double nrm = sqrt(block_sum(part, red));
+      const double inv = nrm > 0.0 ? 1.0 / nrm : 0.0;
+      for (int i = tid; i < k; i += kVecThreads) y[i] *= inv;
+      __syncthreads();
+    }
+    float* yo = y_all + int64_t(j) * k;
+    for (int i = tid; i < k; i += kVecThreads) yo[i] = float(y[i]);
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ at_backxform
+// x = H_0 H_1 ... H_{k-3} y for each sent atom (one wave per atom), written as the unit
+// factor of the message: a when k == rows, b when k == cols.
+template <int KT>
+__device__ void backxform_body(const AtMat& M, const float* __restrict__ A, const float* __restrict__ tau,
+                               const float* __restrict__ y_all, int cnt, float* __restrict__ atoms) {
+  const int k = M.k, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int kWaves = kBackThreads / 64;
+  const int64_t stride = int64_t(M.rows) + M.cols;
+  for (int j = wave; j < cnt; j += kWaves) {
+    const float* yin = y_all + int64_t(j) * k;
+    float y[KT];
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      const int c = lane + 64 * t;
+      y[t] = c < k ? yin[c] : 0.f;
+    }
+    float vn[KT];
+    int r = k - 3;
+    if (r >= 0) {
+#pragma unroll
+      for (int t = 0; t < KT; ++t) {
+        const int c = lane + 64 * t;
+        vn[t] = (c > r && c < k) ? A[int64_t(r) * k + c] : 0.f;
+      }
+    }
+    for (; r >= 0; --r) {
+      float v[KT];
+#pragma unroll
+      for (int t = 0; t < KT; ++t) v[t] = vn[t];
+      if (r > 0) {  // the next reflector's row, loaded ahead
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+          const int c = lane + 64 * t;
+          vn[t] = (c > r - 1 && c < k) ? A[int64_t(r - 1) * k + c] : 0.f;
+        }
+      }
+      const float tr = tau[r];
+      float part = 0.f;
+#pragma unroll
+      for (int t = 0; t < KT; ++t) part = fmaf(v[t], y[t], part);
+      const float f = tr * wave_sum(part);
+#pragma unroll
+      for (int t = 0; t < KT; ++t) y[t] = fmaf(-f, v[t], y[t]);
+    }
+    float* out = atoms + M.atom_off + int64_t(j) * stride + (M.left ? 0 : M.rows);
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      const int c = lane + 64 * t;
+      if (c < k) out[c] = y[t];
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBackThreads) void at_backxform(const AtMat* __restrict__ mats,
+                                                             const float* __restrict__ gram,
+                                                             const float* __restrict__ tau_ws,
+                                                             const float* __restrict__ Y,
+                                                             const int32_t* __restrict__ count,
+                                                             float* __restrict__ atoms, int64_t gram_ws,
+                                                             int64_t sv_total, int64_t atom_total, int32_t n_mats) {
+  const AtMat M = mats[blockIdx.x];
+  const int64_t w = blockIdx.y;
+  const int cnt = count[w * n_mats + M.mat_index];
+  if (cnt == 0) return;
+  const float* A = gram + w * gram_ws + M.b_off;
+  const float* tau = tau_ws + w * sv_total + M.sv_off;
+  const float* y_all = Y + w * gram_ws + M.b_off;
+  float* at = atoms + w * atom_total;
+  const int kt = (M.k + 63) / 64;
+  if (kt <= 1) backxform_body<1>(M, A, tau, y_all, cnt, at);
+  else if (kt <= 2) backxform_body<2>(M, A, tau, y_all, cnt, at);
+  else if (kt <= 4) backxform_body<4>(M, A, tau, y_all, cnt, at);
+  else if (kt <= 8) backxform_body<8>(M, A, tau, y_all, cnt, at);
+  else backxform_body<16>(M, A, tau, y_all, cnt, at);
+}
+
+// ------------------------------------------------------------------ at_factor
+// The second factor of each sent atom, kFactorGroup atoms per pass over the tile of G:
+//   left  (k == rows): b_j[c] = (sum_r G[r][c] u_j[r]) / p_j   (thread per column)
+//   right (k == cols): a_j[r] = (sum_c G[r][c] v_j[c]) / p_j   (wave per row)
+__global__ __launch_bounds__(kFactorThreads) void at_factor(const FactorTile* __restrict__ tiles,
+                                                            const AtMat* __restrict__ mats,
+                                                            const float* __restrict__ G, int64_t ld,
+                                                            const float* __restrict__ prob,
+                                                            const int32_t* __restrict__ index,
+                                                            const int32_t* __restrict__ count,
+                                                            float* __restrict__ atoms, int64_t sv_total,
+                                                            int64_t atom_total, int32_t n_mats) {
+  const FactorTile t = tiles[blockIdx.x];
+  const AtMat M = mats[t.mat];
+  const int64_t w = blockIdx.y;
+  const int cnt = count[w * n_mats + M.mat_index];
+  if (cnt == 0) return;
+  const int n = M.rows, m = M.cols, k = M.k;
+  const float* g = G + w * ld + M.offset;
+  const float* pw = prob + w * sv_total + M.sv_off;
+  const int32_t* iw = index + w * sv_total + M.sv_off;
+  float* at = atoms + w * atom_total + M.atom_off;
+  const int64_t stride = int64_t(n) + m;
+  __shared__ float unit[kFactorGroup][kMaxK];
+  __shared__ float rinv[kFactorGroup];
+  const int tid = threadIdx.x;
+  for (int j0 = 0; j0 < cnt; j0 += kFactorGroup) {
+    const int ng = min(kFactorGroup, cnt - j0);
+    __syncthreads();
+    for (int e = tid; e < kFactorGroup * k; e += kFactorThreads) {
+      const int jj = e / k, i = e % k;
+      unit[jj][i] = jj < ng ? at[int64_t(j0 + jj) * stride + (M.left ? 0 : n) + i] : 0.f;
+    }
+    if (tid < kFactorGroup) rinv[tid] = tid < ng ? 1.f / pw[iw[j0 + tid]] : 0.f;
+    __syncthreads();
+    if (M.left) {
+      const int c = t.begin + tid;
+      if (c < t.end) {
+        float acc[kFactorGroup] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+        for (int r = 0; r < n; ++r) {
+          const float gv = g[int64_t(r) * m + c];
+#pragma unroll
+          for (int jj = 0; jj < kFactorGroup; ++jj) acc[jj] = fmaf(gv, unit[jj][r], acc[jj]);
+        }
+        for (int jj = 0; jj < ng; ++jj) at[int64_t(j0 + jj) * stride + n + c] = acc[jj] * rinv[jj];
+      }
+    } else {
+      const int lane = tid & 63, wave = tid >> 6;
+      for (int r = t.begin + wave; r < t.end; r += kFactorThreads / 64) {
+        float acc[kFactorGroup] = {0.f, 0.f, 0.f, 0.f};
+        for (int c = lane; c < m; c += 64) {
+          const float gv = g[int64_t(r) * m + c];
+#pragma unroll
+          for (int jj = 0; jj < kFactorGroup; ++jj) acc[jj] = fmaf(gv, unit[jj][c], acc[jj]);
+        }
+#pragma unroll
+        for (int jj = 0; jj < kFactorGroup; ++jj) acc[jj] = wave_sum(acc[jj]);
+        if (lane == 0)
+          for (int jj = 0; jj < ng; ++jj) at[int64_t(j0 + jj) * stride + r] = acc[jj] * rinv[jj];
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ at_update
+__global__ __launch_bounds__(kAtUpdThreads) void at_update(const AtUpdTile* __restrict__ tiles,
+                                                         const AtMat* __restrict__ mats,
+                                                         const float* __restrict__ G, int64_t ld,
+                                                         const int32_t* __restrict__ count,
+                                                         const float* __restrict__ atoms, float* __restrict__ update,
+                                                         int W, int64_t atom_total, int32_t n_mats, float inv_w) {
+  const AtUpdTile t = tiles[blockIdx.x];
+  const int tid = threadIdx.x;
+  if (t.mat < 0) {
+    for (int64_t c = t.begin + tid; c < t.end; c += kAtUpdThreads) {
+      float s = 0.f;
+      for (int w = 0; w < W; ++w) s += G[int64_t(w) * ld + c];
+      update[c] = s * inv_w;
+    }
+    return;
+  }
+  const AtMat M = mats[t.mat];
+  const int n = M.rows, m = M.cols;
+  const int c = t.col0 + tid;
+  if (c >= m) return;
+  const int nr = t.row1 - t.row0;
+  const int64_t stride = int64_t(n) + m;
+  float acc[kAtUpdRows];
+#pragma unroll
+  for (int r = 0; r < kAtUpdRows; ++r) acc[r] = 0.f;
+  for (int w = 0; w < W; ++w) {
+    const int cnt = count[int64_t(w) * n_mats + M.mat_index];
+    const float* aw = atoms + int64_t(w) * atom_total + M.atom_off;
+    for (int j = 0; j < cnt; ++j) {
+      const float* a = aw + int64_t(j) * stride;
+      const float bv = a[n + c];
+#pragma unroll
+      for (int r = 0; r < kAtUpdRows; ++r)
+        if (r < nr) acc[r] = fmaf(a[t.row0 + r], bv, acc[r]);
+    }
+  }
+  float* u = update + M.offset;
+#pragma unroll
+  for (int r = 0; r < kAtUpdRows; ++r)
+    if (r < nr) u[int64_t(t.row0 + r) * m + c] = acc[r] * inv_w;
+}
+
+// ------------------------------------------------------------------ host helpers
+psgd_status fail(psgd_status s, const std::string& msg) {
+  set_error(msg);
+  return s;
+}
+
+psgd_status hip_fail(const char* what, hipError_t e) {
+  return fail(PSGD_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+uint64_t a256(uint64_t x) { return (x + 255) / 256 * 256; }
+
+struct DevTables {
+  AtMat* mats;
+  GramTile* gtiles;
+  FactorTile* ftiles;
+  AtUpdTile* utiles;
+};
+
+psgd_status device_tables(psgd_atomo_plan* plan, DevTables* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+  const uint64_t bm = a256(plan->mats.size() * sizeof(AtMat) + 1);
+  const uint64_t bg = a256(plan->gtiles.size() * sizeof(GramTile) + 1);
+  const uint64_t bf = a256(plan->ftiles.size() * sizeof(FactorTile) + 1);
+  const uint64_t bu = a256(plan->utiles.size() * sizeof(AtUpdTile) + 1);
+  auto it = plan->dev.find(dev);
+  if (it == plan->dev.end()) {
+    void* base = nullptr;
+    e = hipMalloc(&base, bm + bg + bf + bu);
+    if (e != hipSuccess)
+      return fail(PSGD_ERR_NO_MEMORY, std::string("hipMalloc of the plan's device tables: ") + hipGetErrorString(e));
+    char* b = static_cast<char*>(base);
+    e = hipMemcpy(b, plan->mats.data(), plan->mats.size() * sizeof(AtMat), hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+      e = hipMemcpy(b + bm, plan->gtiles.data(), plan->gtiles.size() * sizeof(GramTile), hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+      e = hipMemcpy(b + bm + bg, plan->ftiles.data(), plan->ftiles.size() * sizeof(FactorTile),
+                    hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+      e = hipMemcpy(b + bm + bg + bf, plan->utiles.data(), plan->utiles.size() * sizeof(AtUpdTile),
+                    hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      (void)hipFree(base);
+      return hip_fail("hipMemcpy of the plan's device tables", e);
+    }
+    it = plan->dev.emplace(dev, base).first;
+  }
+  char* b = static_cast<char*>(it->second);
+  out->mats = reinterpret_cast<AtMat*>(b);
+  out->gtiles = reinterpret_cast<GramTile*>(b + bm);
+  out->ftiles = reinterpret_cast<FactorTile*>(b + bm + bg);
+  out->utiles = reinterpret_cast<AtUpdTile*>(b + bm + bg + bf);
+  return PSGD_OK;
+}
+
+psgd_status take_event(psgd_atomo_plan* plan, hipEvent_t* ev) {
+  if (!plan->event_pool.empty()) {
+    *ev = plan->event_pool.back();
+    plan->event_pool.pop_back();
+    return PSGD_OK;
+  }
+  const hipError_t e = hipEventCreate(ev);
+  return e == hipSuccess ? PSGD_OK : hip_fail("hipEventCreate", e);
+}
+
+// Launch on `st`; with timing on, through hipExtLaunchKernelGGL with events the runtime
+// records with the dispatch itself.
+template <typename... KArgs, typename... Args>
+psgd_status launch(psgd_atomo_plan* plan, int kid, void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t st,
+                   Args... args) {
+  if (grid.x == 0 || grid.y == 0) return PSGD_OK;
+  hipEvent_t a = nullptr, b = nullptr;
+  if (plan->timing) {
+    psgd_status s = take_event(plan, &a);
+    if (s == PSGD_OK) s = take_event(plan, &b);
+    if (s != PSGD_OK) {
+      if (a) plan->event_pool.push_back(a);
+      return s;
+    }
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, a, b, 0, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    if (plan->timing) {
+      plan->event_pool.push_back(a);
+      plan->event_pool.push_back(b);
+    }
+    return hip_fail((std::string("launch ") + kNames[kid]).c_str(), e);
+  }
+  if (plan->timing) plan->pending.push_back(PendingTiming{kid, a, b});
+  return PSGD_OK;
+}
+
+struct Span {
+  const char* name;
+  uintptr_t lo, hi;
+};
+
+}  // namespace
+}  // namespace atm
+}  // namespace psgd
+
+using namespace psgd;
+using namespace psgd::atm;
+
+extern "C" psgd_status psgd_atomo_plan_create(const psgd_layer* layers, int32_t n_layers, double budget,
+                                              int32_t n_workers, uint32_t flags, psgd_atomo_plan** out) {
+  static const char* fn = "psgd_atomo_plan_create";
+  if (out == nullptr) return fail(PSGD_ERR_INVALID_ARG, std::string(fn) + ": out is NULL");
+  *out = nullptr;
+  if (n_layers < 1) return fail(PSGD_ERR_INVALID_ARG, std::string(fn) + ": n_layers must be >= 1");
+  if (layers == nullptr) return fail(PSGD_ERR_INVALID_ARG, std::string(fn) + ": layers is NULL");
+  if (n_workers < 1 || n_workers > 65535)
+    return fail(PSGD_ERR_INVALID_ARG, std::string(fn) + ": n_workers must be in 1..65535");
+  if (!(budget > 0.0) || !std::isfinite(budget) || budget > 1e30)
+    return fail(PSGD_ERR_INVALID_ARG, std::string(fn) + ": budget must be positive and finite");
+  if (flags != 0u) return fail(PSGD_ERR_UNSUPPORTED, std::string(fn) + ": flags must be 0");
+  psgd_atomo_plan* plan = nullptr;
+  try {
+    plan = new psgd_atomo_plan();
+    plan->n_workers = n_workers;
+    plan->budget = budget;
+    int64_t off = 0, sv = 0, atom = 0, gram = 0;
+    for (int32_t i = 0; i < n_layers; ++i) {
+      const int64_t rows = layers[i].rows, cols = layers[i].cols;
+      if (rows < 1 || cols < 1 || rows > (int64_t(1) << 31) || cols > (int64_t(1) << 31) ||
+          rows * cols > int64_t(0x7fffffff)) {
+        delete plan;
+        return fail(PSGD_ERR_INVALID_ARG, std::string(fn) + ": layer " + std::to_string(i) +
+                                              " must have 1 <= rows, cols and rows * cols < 2^31");
+      }
+      psgd_atomo_layer_info li{};
+      li.rows = rows;
+      li.cols = cols;
+      li.numel = rows * cols;
+      li.offset = off;
+      li.matrix_index = -1;
+      const int64_t k = std::min(rows, cols);
+      if (k >= 2) {
+        if (k > kMaxK) {
+          delete plan;
+          return fail(PSGD_ERR_UNSUPPORTED, std::string(fn) + ": layer " + std::to_string(i) +
+                                                " has min(rows, cols) above PSGD_ATOMO_MAX_K");
+        }
+        li.compressed = 1;
+        li.matrix_index = int32_t(plan->mats.size());
+        li.k = k;
+        li.sv_offset = sv;
+        li.atom_offset = atom;
+        AtMat m{};
+        m.offset = off;
+        m.sv_off = sv;
+        m.atom_off = atom;
+        m.b_off = gram;
+        m.rows = int32_t(rows);
+        m.cols = int32_t(cols);
+        m.k = int32_t(k);
+        m.left = rows <= cols ? 1 : 0;
+        m.mat_index = li.matrix_index;
+        plan->mats.push_back(m);
+        sv += k;
+        atom += k * (rows + cols);
+        gram += (k * k + 63) / 64 * 64;
+      }
+      plan->info.push_back(li);
+      off += (li.numel + 63) / 64 * 64;
+    }
+    plan->worker_stride = off;
+    plan->sv_total = sv;
+    plan->atom_total = atom;
+    plan->gram_total = gram;
+    plan->numel = 0;
+    const uint64_t W = uint64_t(n_workers);
+    uint64_t model = 0;
+    for (const auto& li : plan->info) {
+      plan->numel += li.numel;
+      model += (li.compressed ? 8 * W + 4 : 4 * W + 4) * uint64_t(li.numel);
+    }
+    plan->model_bytes = model;
+    // tiles
+    for (size_t mi = 0; mi < plan->mats.size(); ++mi) {
+      const AtMat& m = plan->mats[mi];
+      const int nt = (m.k + kGramTile - 1) / kGramTile;
+      for (int ti = 0; ti < nt; ++ti)
+        for (int tj = 0; tj <= ti; ++tj) plan->gtiles.push_back(GramTile{int32_t(mi), ti, tj, 0});
+      if (m.left) {
+        for (int c = 0; c < m.cols; c += kFactorThreads)
+          plan->ftiles.push_back(FactorTile{int32_t(mi), c, std::min(m.cols, c + kFactorThreads), 0});
+      } else {
+        const int rows_per = 4 * (kFactorThreads / 64);
+        for (int r = 0; r < m.rows; r += rows_per)
+          plan->ftiles.push_back(FactorTile{int32_t(mi), r, std::min(m.rows, r + rows_per), 0});
+      }
+      for (int r = 0; r < m.rows; r += kAtUpdRows)
+        for (int c = 0; c < m.cols; c += kAtUpdThreads)
+          plan->utiles.push_back(AtUpdTile{0, 0, int32_t(mi), r, std::min(m.rows, r + kAtUpdRows), c});
+    }
+    for (const auto& li : plan->info)
+      if (!li.compressed)
+        for (int64_t b = 0; b < li.numel; b += 4096)
+          plan->utiles.push_back(AtUpdTile{li.offset + b, li.offset + std::min(li.numel, b + 4096), -1, 0, 0, 0});
+    // workspace
+    uint64_t ws = 0;
+    plan->ws_gram = ws;
+    ws = a256(ws + W * uint64_t(gram) * 4);
+    plan->ws_y = ws;
+    ws = a256(ws + W * uint64_t(gram) * 4);
+    plan->ws_tau = ws;
+    ws = a256(ws + W * uint64_t(sv) * 4);
+    plan->ws_d = ws;
+    ws = a256(ws + W * uint64_t(sv) * 4);
+    plan->ws_e = ws;
+    ws = a256(ws + W * uint64_t(sv) * 4);
+    plan->ws_lam = ws;
+    ws = a256(ws + W * uint64_t(sv) * 4);
+    plan->workspace_bytes = std::max<uint64_t>(ws, 256);
+  } catch (const std::bad_alloc&) {
+    delete plan;
+    return fail(PSGD_ERR_NO_MEMORY, std::string(fn) + ": out of host memory");
+  }
+  *out = plan;
+  return PSGD_OK;
+}
+
+extern "C" psgd_status psgd_atomo_plan_sizes(const psgd_atomo_plan* plan, psgd_atomo_sizes* out) {
+  if (plan == nullptr || out == nullptr) return fail(PSGD_ERR_INVALID_ARG, "psgd_atomo_plan_sizes: NULL argument");
+  psgd_atomo_sizes s{};
+  s.n_layers = int32_t(plan->info.size());
+  s.n_workers = plan->n_workers;
+  s.n_matrices = int32_t(plan->mats.size());
+  s.worker_stride = plan->worker_stride;
+  s.numel = plan->numel;
+  s.sv_total = plan->sv_total;
+  s.atom_total = plan->atom_total;
+  s.workspace_bytes = plan->workspace_bytes;
+  s.model_bytes = plan->model_bytes;
+  s.budget = plan->budget;
+  *out = s;
+  return PSGD_OK;
+}
+
+extern "C" psgd_status psgd_atomo_plan_layer_info(const psgd_atomo_plan* plan, int32_t layer,
+                                                  psgd_atomo_layer_info* out) {
+  if (plan == nullptr || out == nullptr)
+    return fail(PSGD_ERR_INVALID_ARG, "psgd_atomo_plan_layer_info: NULL argument");
+  if (layer < 0 || size_t(layer) >= plan->info.size())
+    return fail(PSGD_ERR_INVALID_ARG, "psgd_atomo_plan_layer_info: layer index out of range");
+  *out = plan->info[size_t(layer)];
+  return PSGD_OK;
+}
+
+extern "C" psgd_status psgd_atomo_plan_destroy(psgd_atomo_plan* plan) {
+  if (plan == nullptr) return PSGD_OK;
+  psgd_status st = PSGD_OK;
+  for (const PendingTiming& t : plan->pending) {
+    (void)hipEventDestroy(t.start);
+    (void)hipEventDestroy(t.stop);
+  }
+  for (hipEvent_t ev : plan->event_pool) (void)hipEventDestroy(ev);
+  for (auto& kv : plan->dev) {
+    int cur = 0;
+    const bool have = hipGetDevice(&cur) == hipSuccess;
+    if (have && cur != kv.first) (void)hipSetDevice(kv.first);
+    if (hipFree(kv.second) != hipSuccess) {
+      set_error("psgd_atomo_plan_destroy: hipFree of the device tables failed");
+      st = PSGD_ERR_HIP;
+    }
+    if (have && cur != kv.first) (void)hipSetDevice(cur);
+  }
+  delete plan;
+  return st;
+}
+
+extern "C" psgd_status psgd_atomo_plan_set_timing(psgd_atomo_plan* plan, int32_t enable) {
+  if (plan == nullptr) return fail(PSGD_ERR_INVALID_ARG, "psgd_atomo_plan_set_timing: plan is NULL");
+  plan->timing = enable != 0;
+  return PSGD_OK;
+}
+
+extern "C" psgd_status psgd_atomo_plan_kernel_stats(psgd_atomo_plan* plan, psgd_kernel_stat* out, int32_t capacity,
+                                                    int32_t* count, int32_t reset) {
+  if (plan == nullptr) return fail(PSGD_ERR_INVALID_ARG, "psgd_atomo_plan_kernel_stats: plan is NULL");
+  if (capacity > 0 && out == nullptr) return fail(PSGD_ERR_INVALID_ARG, "psgd_atomo_plan_kernel_stats: out is NULL");
+  psgd_status st = PSGD_OK;
+  for (const PendingTiming& t : plan->pending) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(t.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.start, t.stop);
+    if (e != hipSuccess) {
+      set_error(std::string("psgd_atomo_plan_kernel_stats: ") + hipGetErrorString(e));
+      st = PSGD_ERR_HIP;
+    } else {
+      plan->stats[t.kernel].launches += 1;
+      plan->stats[t.kernel].total_ms += double(ms);
+    }
+    plan->event_pool.push_back(t.start);
+    plan->event_pool.push_back(t.stop);
+  }
+  plan->pending.clear();
+  int32_t n = 0;
+  for (int k = 0; k < kNumK; ++k) {
+    if (plan->stats[k].launches == 0) continue;
+    if (n < capacity) {
+      psgd_kernel_stat ks{};
+      std::snprintf(ks.name, sizeof(ks.name), "%s", kNames[k]);
+      ks.launches = plan->stats[k].launches;
+      ks.total_ms = plan->stats[k].total_ms;
+      out[n] = ks;
+    }
+    ++n;
+  }
+  if (count != nullptr) *count = std::min(n, std::max<int32_t>(capacity, 0));
+  if (reset)
+    for (auto& k : plan->stats) k = KernelStat{};
+  return st;
+}
+
+extern "C" psgd_status psgd_atomo_step(psgd_atomo_plan* plan, const float* grads, const float* uniforms,
+                                       float* sigma, float* prob, int32_t* index, int32_t* count, float* atoms,
+                                       float* update, void* workspace, void* stream) {
+  static const char* fn = "psgd_atomo_step";
+  if (plan == nullptr) return fail(PSGD_ERR_INVALID_ARG, std::string(fn) + ": plan is NULL");
+  const uint64_t W = uint64_t(plan->n_workers);
+  const uint64_t stride = uint64_t(plan->worker_stride);
+  const uint64_t sv = uint64_t(plan->sv_total);
+  const uint64_t nm = uint64_t(plan->mats.size());
+  const Span spans[] = {
+      {"grads", uintptr_t(grads), uintptr_t(grads) + W * stride * 4},
+      {"uniforms", uintptr_t(uniforms), uintptr_t(uniforms) + W * sv * 4},
+      {"sigma", uintptr_t(sigma), uintptr_t(sigma) + W * sv * 4},
+      {"prob", uintptr_t(prob), uintptr_t(prob) + W * sv * 4},
+      {"index", uintptr_t(index), uintptr_t(index) + W * sv * 4},
+      {"count", uintptr_t(count), uintptr_t(count) + W * nm * 4},
+      {"atoms", uintptr_t(atoms), uintptr_t(atoms) + W * uint64_t(plan->atom_total) * 4},
+      {"update", uintptr_t(update), uintptr_t(update) + stride * 4},
+      {"workspace", uintptr_t(workspace), uintptr_t(workspace) + plan->workspace_bytes},
+  };
+  constexpr size_t kSpans = sizeof(spans) / sizeof(spans[0]);
+  for (const Span& sp : spans) {
+    const std::string name(sp.name);
+    const bool empty = sp.hi == sp.lo;
+    const bool nullable = name == "update" || (empty && name != "grads" && name != "workspace");
+    if (sp.lo == 0) {
+      if (nullable) continue;
+      return fail(PSGD_ERR_INVALID_ARG, std::string(fn) + ": " + sp.name + " is NULL");
+    }
+    if (sp.lo % 16 != 0) return fail(PSGD_ERR_INVALID_ARG, std::string(fn) + ": " + sp.name + " is not 16-byte aligned");
+  }
+  for (size_t i = 0; i < kSpans; ++i)
+    for (size_t j = i + 1; j < kSpans; ++j) {
+      const Span &a = spans[i], &b = spans[j];
+      if (a.lo == 0 || b.lo == 0 || a.lo == a.hi || b.lo == b.hi) continue;
+      if (a.lo < b.hi && b.lo < a.hi)
+        return fail(PSGD_ERR_INVALID_ARG, std::string(fn) + ": " + a.name + " and " + b.name + " overlap");
+    }
+  DevTables dt{};
+  psgd_status s = device_tables(plan, &dt);
+  if (s != PSGD_OK) return s;
+
+  char* ws = static_cast<char*>(workspace);
+  float* gram = reinterpret_cast<float*>(ws + plan->ws_gram);
+  float* Y = reinterpret_cast<float*>(ws + plan->ws_y);
+  float* tau = reinterpret_cast<float*>(ws + plan->ws_tau);
+  float* dd = reinterpret_cast<float*>(ws + plan->ws_d);
+  float* ee = reinterpret_cast<float*>(ws + plan->ws_e);
+  float* lam = reinterpret_cast<float*>(ws + plan->ws_lam);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t ld = int64_t(stride);
+  const int64_t gws = plan->gram_total;
+  const int64_t svt = plan->sv_total;
+  const int64_t att = plan->atom_total;
+  const int32_t nmats = int32_t(nm);
+  const dim3 mgrid(static_cast<unsigned>(nm), static_cast<unsigned>(W));
+  const AtMat* M = dt.mats;
+
+  if (nm > 0) {
+    if ((s = launch(plan, kGram, at_gram, dim3(unsigned(plan->gtiles.size()), unsigned(W)), dim3(kGramThreads), st,
+                    static_cast<const GramTile*>(dt.gtiles), M, grads, ld, gram, gws)) != PSGD_OK)
+      return s;
+    if ((s = launch(plan, kTridiag, at_tridiag, mgrid, dim3(kTriThreads), st, M, gram, gws, tau, dd, ee, svt)) !=
+        PSGD_OK)
+      return s;
+    if ((s = launch(plan, kEig, at_eig, mgrid, dim3(kEigThreads), st, M, static_cast<const float*>(dd),
+                    static_cast<const float*>(ee), lam, sigma, svt)) != PSGD_OK)
+      return s;
+    if ((s = launch(plan, kSample, at_sample, mgrid, dim3(kSampleThreads), st, M, static_cast<const float*>(sigma),
+                    uniforms, prob, index, count, svt, nmats, float(plan->budget))) != PSGD_OK)
+      return s;
+    if ((s = launch(plan, kVectors, at_vectors, mgrid, dim3(kVecThreads), st, M, static_cast<const float*>(dd),
+                    static_cast<const float*>(ee), static_cast<const float*>(lam),
+                    static_cast<const int32_t*>(index), static_cast<const int32_t*>(count), Y, gws, svt, nmats)) !=
+        PSGD_OK)
+      return s;
+    if ((s = launch(plan, kBack, at_backxform, mgrid, dim3(kBackThreads), st, M, static_cast<const float*>(gram),
+                    static_cast<const float*>(tau), static_cast<const float*>(Y),
+                    static_cast<const int32_t*>(count), atoms, gws, svt, att, nmats)) != PSGD_OK)
+      return s;
+    if ((s = launch(plan, kFactor, at_factor, dim3(unsigned(plan->ftiles.size()), unsigned(W)),
+                    dim3(kFactorThreads), st, static_cast<const FactorTile*>(dt.ftiles), M, grads, ld,
+                    static_cast<const float*>(prob), static_cast<const int32_t*>(index),
+                    static_cast<const int32_t*>(count), atoms, svt, att, nmats)) != PSGD_OK)
+      return s;
+  }
+  if (update != nullptr)
+    s = launch(plan, kUpdate, at_update, dim3(unsigned(plan->utiles.size())), dim3(kAtUpdThreads), st,
+               static_cast<const AtUpdTile*>(dt.utiles), M, grads, ld, static_cast<const int32_t*>(count),
+               static_cast<const float*>(atoms), update, int(W), att, nmats, 1.0f / float(W));
+  return s;
+}

@@ -1,5 +1,5 @@
-"""Thin ctypes binding of libpsgd (C ABI declared in include/psgd.h and
-include/psgd_rtopk.h).
+"""Thin ctypes binding of libpsgd (C ABI declared in include/psgd.h,
+include/psgd_rtopk.h and include/psgd_atomo.h).
 
 Functions carry the C names.  The step functions take torch tensors on a ROCm device
 and pass their device pointers and the current HIP stream; every step of the
@@ -41,7 +41,10 @@ EXPORTED = [
     "psgd_plan_set_power_iterations", "psgd_status_string", "psgd_last_error",
     "psgd_rtopk_plan_create", "psgd_rtopk_plan_sizes", "psgd_rtopk_plan_layer_info", "psgd_rtopk_plan_destroy",
     "psgd_rtopk_step", "psgd_rtopk_plan_set_timing", "psgd_rtopk_plan_kernel_stats",
+    "psgd_atomo_plan_create", "psgd_atomo_plan_sizes", "psgd_atomo_plan_layer_info", "psgd_atomo_plan_destroy",
+    "psgd_atomo_step", "psgd_atomo_plan_set_timing", "psgd_atomo_plan_kernel_stats",
 ]
+PSGD_ATOMO_MAX_K = 1024
 _STRING_FUNCS = ("psgd_status_string", "psgd_last_error")
 
 
@@ -91,6 +94,21 @@ class _RtopkSizes(ctypes.Structure):
                 ("model_bytes", ctypes.c_uint64)]
 
 
+class _AtomoLayerInfo(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("numel", ctypes.c_int64),
+                ("offset", ctypes.c_int64), ("compressed", ctypes.c_int32), ("matrix_index", ctypes.c_int32),
+                ("k", ctypes.c_int64), ("sv_offset", ctypes.c_int64), ("atom_offset", ctypes.c_int64)]
+
+
+class _AtomoSizes(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("n_workers", ctypes.c_int32),
+                ("n_matrices", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("worker_stride", ctypes.c_int64), ("numel", ctypes.c_int64),
+                ("sv_total", ctypes.c_int64), ("atom_total", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_uint64), ("model_bytes", ctypes.c_uint64),
+                ("budget", ctypes.c_double)]
+
+
 _lib = None
 
 
@@ -130,6 +148,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.psgd_rtopk_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.psgd_rtopk_plan_set_timing.argtypes = [vp, i32]
     lib.psgd_rtopk_plan_kernel_stats.argtypes = [vp, ctypes.POINTER(_KernelStat), i32, ctypes.POINTER(i32), i32]
+    lib.psgd_atomo_plan_create.argtypes = [ctypes.POINTER(_Layer), i32, ctypes.c_double, i32, ctypes.c_uint32,
+                                           ctypes.POINTER(vp)]
+    lib.psgd_atomo_plan_sizes.argtypes = [vp, ctypes.POINTER(_AtomoSizes)]
+    lib.psgd_atomo_plan_layer_info.argtypes = [vp, i32, ctypes.POINTER(_AtomoLayerInfo)]
+    lib.psgd_atomo_plan_destroy.argtypes = [vp]
+    lib.psgd_atomo_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.psgd_atomo_plan_set_timing.argtypes = [vp, i32]
+    lib.psgd_atomo_plan_kernel_stats.argtypes = [vp, ctypes.POINTER(_KernelStat), i32, ctypes.POINTER(i32), i32]
     for name in EXPORTED:
         if name not in _STRING_FUNCS:
             getattr(lib, name).restype = ctypes.c_int
@@ -356,6 +382,113 @@ def psgd_rtopk_step(plan: RtopkPlan, grads, errors, ranks, index, value, update,
         _check(load_library().psgd_rtopk_step(
             plan.handle, _ptr(grads), _ptr(errors), _ptr(ranks), _ptr(index), _ptr(value), _ptr(update),
             _ptr(workspace), _stream(stream, grads)))
+
+
+# ------------------------------------------------------------------------ Spectral-ATOMO
+@dataclass
+class AtomoLayerInfo:
+    rows: int
+    cols: int
+    numel: int
+    offset: int
+    compressed: int
+    matrix_index: int
+    k: int
+    sv_offset: int
+    atom_offset: int
+
+
+class AtomoPlan:
+    """Owns a psgd_atomo_plan*; freed by psgd_atomo_plan_destroy (or when collected)."""
+
+    def __init__(self, handle: int, shapes: Sequence[Tuple[int, int]]):
+        self.handle = handle
+        self.shapes = [tuple(int(v) for v in s) for s in shapes]
+        self.sizes = psgd_atomo_plan_sizes(self)
+        self.layers: List[AtomoLayerInfo] = [psgd_atomo_plan_layer_info(self, i) for i in range(len(shapes))]
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            try:
+                psgd_atomo_plan_destroy(self)
+            except Exception:
+                pass
+
+
+def psgd_atomo_plan_create(shapes: Sequence[Tuple[int, int]], budget: float, n_workers: int,
+                           flags: int = 0) -> AtomoPlan:
+    lib = load_library()
+    n = len(shapes)
+    arr = (_Layer * max(1, n))(*[_Layer(int(r), int(c)) for r, c in shapes])
+    h = ctypes.c_void_p()
+    _check(lib.psgd_atomo_plan_create(arr, n, float(budget), int(n_workers), int(flags), ctypes.byref(h)))
+    return AtomoPlan(h.value, shapes)
+
+
+def psgd_atomo_plan_sizes(plan: AtomoPlan) -> dict:
+    s = _AtomoSizes()
+    _check(load_library().psgd_atomo_plan_sizes(plan.handle, ctypes.byref(s)))
+    return {name: getattr(s, name) for name, _ in _AtomoSizes._fields_}
+
+
+def psgd_atomo_plan_layer_info(plan: AtomoPlan, layer: int) -> AtomoLayerInfo:
+    li = _AtomoLayerInfo()
+    _check(load_library().psgd_atomo_plan_layer_info(plan.handle, int(layer), ctypes.byref(li)))
+    return AtomoLayerInfo(*(getattr(li, name) for name, _ in _AtomoLayerInfo._fields_))
+
+
+def psgd_atomo_plan_destroy(plan: AtomoPlan) -> None:
+    h, plan.handle = plan.handle, None
+    if h:
+        _check(load_library().psgd_atomo_plan_destroy(h))
+
+
+def psgd_atomo_plan_set_timing(plan: AtomoPlan, enable: bool) -> None:
+    _check(load_library().psgd_atomo_plan_set_timing(plan.handle, 1 if enable else 0))
+
+
+def psgd_atomo_plan_kernel_stats(plan: AtomoPlan, reset: bool = False) -> dict:
+    """{kernel name: (launches, total_ms)}; waits for every timed launch so far."""
+    arr = (_KernelStat * 16)()
+    n = ctypes.c_int32()
+    _check(load_library().psgd_atomo_plan_kernel_stats(plan.handle, arr, 16, ctypes.byref(n), 1 if reset else 0))
+    return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(n.value)}
+
+
+def psgd_atomo_step(plan: AtomoPlan, grads, uniforms, sigma, prob, index, count, atoms, update, workspace,
+                    stream=None) -> None:
+    """Enqueue one Spectral-ATOMO step (tensors on a ROCm device; see include/psgd_atomo.h)."""
+    import torch
+
+    with torch.cuda.device(grads.device):
+        _check(load_library().psgd_atomo_step(
+            plan.handle, _ptr(grads), _ptr(uniforms), _ptr(sigma), _ptr(prob), _ptr(index), _ptr(count),
+            _ptr(atoms), _ptr(update), _ptr(workspace), _stream(stream, grads)))
+
+
+def pack_sv(plan: AtomoPlan, per_layer: dict, dtype=np.float32) -> np.ndarray:
+    """Place per-matrix (W, k) arrays ({layer: array}) into the [W][sv_total] rows of an
+    ATOMO plan (zeros elsewhere)."""
+    W = plan.sizes["n_workers"]
+    out = np.zeros((W, plan.sizes["sv_total"]), dtype=dtype)
+    for li, a in per_layer.items():
+        L = plan.layers[li]
+        out[:, L.sv_offset:L.sv_offset + L.k] = np.asarray(a).reshape(W, L.k)
+    return out
+
+
+def sv_slice(plan: AtomoPlan, rows: np.ndarray, layer: int) -> np.ndarray:
+    """One matrix's (W, k) block of a [W][sv_total] array."""
+    L = plan.layers[layer]
+    return rows[:, L.sv_offset:L.sv_offset + L.k]
+
+
+def atom_factors(plan: AtomoPlan, atoms: np.ndarray, count: np.ndarray, layer: int, worker: int):
+    """The sent factors of one worker's matrix: (a [count, rows], b [count, cols])."""
+    L = plan.layers[layer]
+    cnt = int(count[worker, L.matrix_index])
+    blk = atoms[worker, L.atom_offset:L.atom_offset + cnt * (L.rows + L.cols)].reshape(cnt, L.rows + L.cols)
+    return blk[:, :L.rows], blk[:, L.rows:]
 
 
 # ------------------------------------------------------------------------ layout helpers
