@@ -11,13 +11,13 @@
 // over G.  Launches, each covering every problem of every worker:
 //
 //   at_gram       the Gram matrix, 64 x 64 output tiles of its lower block triangle
-//                 (mirrored into the upper one), the contraction over the long side
-//                 staged through LDS
+//                 (stored as the packed lower triangle), the contraction over the long
+//                 side staged through LDS
 //   at_tridiag    one workgroup per problem: Householder reduction of the Gram matrix
 //                 to tridiagonal form.  Each step forms the next reflector from the
-//                 updated column, then one pass over the trailing block both applies
-//                 the previous rank-2 update and forms the product with the new
-//                 reflector; reflector q is kept in row q
+//                 updated column, then one pass over the packed trailing block both
+//                 applies the previous rank-2 update and forms the product with the new
+//                 reflector; the last 190 rows are reduced in LDS
 //   at_eig        every eigenvalue of the tridiagonal matrix by bisection on Sturm
 //                 counts (one per thread); sigma_i = sqrt(max(eigenvalue, 0))
 //   at_sample     the closed-form probabilities (the largest atoms saturate first),
@@ -56,9 +56,9 @@ constexpr int kGramKC = 16;
 constexpr int kGramThreads = 256;
 constexpr int kTriThreads = 1024;
 // rows per wave per batch of the trailing-block pass (fewer for the widest rows, whose
-// values would not fit in registers)
+// values would not fit in the 128 registers a lane has at 1024 threads)
 template <int KT>
-constexpr int tri_rows() { return KT >= 16 ? 2 : 4; }
+constexpr int tri_rows() { return KT >= 16 ? 1 : KT >= 8 ? 3 : KT >= 4 ? 5 : 8; }
 constexpr int kEigThreads = 1024;
 constexpr int kSampleThreads = 1024;
 constexpr int kVecThreads = 256;
@@ -109,6 +109,8 @@ struct psgd_atomo_plan {
   std::vector<psgd::atm::GramTile> gtiles;
   std::vector<psgd::atm::FactorTile> ftiles;
   std::vector<psgd::atm::AtUpdTile> utiles;
+  std::vector<int32_t> tri_list;  // matrices in decreasing k (the largest start first)
+  int32_t tri_kt = 1;             // width class of the widest matrix
   int64_t worker_stride = 0, numel = 0, sv_total = 0, atom_total = 0, gram_total = 0;
   uint64_t ws_gram = 0, ws_y = 0, ws_tau = 0, ws_d = 0, ws_e = 0, ws_lam = 0, workspace_bytes = 0;
   uint64_t model_bytes = 0;
@@ -165,6 +167,15 @@ __device__ __forceinline__ float block_min(float v, float* red) {
 
 __device__ __forceinline__ float block_max(float v, float* red) { return -block_min(-v, red); }
 
+// ------------------------------------------------------------------ packed storage
+// A problem's k * k floats of workspace: the lower triangle of the symmetric matrix,
+// packed by rows (row r at tri_off(r), columns 0..r), then the Householder reflectors
+// (reflector q, entries q+1..k-1, at refl_off(k, q)); k (k + 1) / 2 + k (k - 1) / 2 = k^2.
+// (k <= 1024, so every offset inside a problem's k * k floats fits in 32 bits)
+__device__ __forceinline__ int tri_off(int r) { return (r * (r + 1)) >> 1; }
+
+__device__ __forceinline__ int refl_off(int k, int q) { return tri_off(k) + q * (k - 1) - ((q * (q - 1)) >> 1); }
+
 // ------------------------------------------------------------------ at_gram
 __global__ __launch_bounds__(kGramThreads) void at_gram(const GramTile* __restrict__ tiles,
                                                         const AtMat* __restrict__ mats,
@@ -215,17 +226,13 @@ __global__ __launch_bounds__(kGramThreads) void at_gram(const GramTile* __restri
     }
     __syncthreads();
   }
-  // A diagonal tile computes both (a, b) and (b, a) with the same products in the same
-  // order, so the stored matrix is exactly symmetric.
+  // the lower triangle only, packed
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int a = a0 + ty * 4 + i, b = b0 + tx * 4 + j;
-      if (a < k && b < k) {
-        B[int64_t(a) * k + b] = acc[i][j];
-        if (t.ti != t.tj) B[int64_t(b) * k + a] = acc[i][j];
-      }
+      if (a < k && b <= a) B[tri_off(a) + b] = acc[i][j];
     }
 }
 
@@ -234,140 +241,214 @@ __global__ __launch_bounds__(kGramThreads) void at_gram(const GramTile* __restri
 // H_q maps column q of the current matrix below the diagonal to e[q] * e_{q+1}.  After
 // step q the trailing block (rows and columns > q) holds H_q A H_q there, applied as
 // A - v w^T - w v^T with w = tau A v - (tau^2 / 2)(v^T A v) v.
+//
+// A problem's k * k floats of workspace hold the lower triangle of the symmetric
+// matrix, packed by rows (row r at r(r+1)/2, columns 0..r), followed by the reflectors
+// (reflector q, entries q+1..k-1, at refl_off(k, q)).  In the pass over the trailing
+// block, row r contributes sum_c a_rc v_c to (A v)_r directly and a_rc v_r to (A v)_c
+// for c < r; a lane keeps the latter for its own columns in registers, and the waves'
+// column sums are added in wave order.  Once the trailing block fits, it moves to LDS.
 constexpr int kTriWaves = kTriThreads / 64;
+constexpr int kTailRows = 190;                            // largest trailing block kept in LDS
+constexpr int kTailFloats = kTailRows * (kTailRows + 1) / 2;
 
 struct TriShared {
   float V[2][kMaxK], Wv[2][kMaxK], P[kMaxK];
+  float next[kMaxK];            // column q+1 as the pass of step q stores it
+  float col[kTriWaves][kMaxK];  // per-wave column sums of the pass
   float red[kTriWaves];
+  float tail[kTailFloats];      // the trailing block, packed, once it fits
 };
+
+// one Householder step q on packed storage: global (LOCAL = false) or the LDS copy of the
+// block from row/column `base` on
+template <int KT, bool LOCAL>
+__device__ __forceinline__ void tri_step(int q, int k, int base, float* __restrict__ A, float* __restrict__ Rf,
+                                         float* __restrict__ tau, float* __restrict__ d, float* __restrict__ e,
+                                         TriShared& sh, int cur) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int kWaves = kTriWaves;
+  auto at = [&](int r, int c) -> float& {
+    if constexpr (LOCAL) return sh.tail[tri_off(r - base) + (c - base)];
+    else return A[tri_off(r) + c];
+  };
+  const float* vp = sh.V[cur];
+  const float* wp = sh.Wv[cur];
+  float* vn = sh.V[cur ^ 1];
+  float* wn = sh.Wv[cur ^ 1];
+  float* P = sh.P;
+  // column q below the diagonal, with the previous reflector's update applied (the
+  // stored column comes from the previous pass, or from memory at the first step)
+  const float vq = vp[q], wq = wp[q];
+  const bool fresh = q == 0;
+  for (int i = q + 1 + tid; i < k; i += kTriThreads)
+    vn[i] = (fresh ? at(i, q) : sh.next[i]) - vp[i] * wq - wp[i] * vq;
+  if (tid == 0) d[q] = (fresh ? at(q, q) : sh.next[q]) - 2.f * vq * wq;
+  __syncthreads();
+  float part = 0.f;
+  for (int i = q + 2 + tid; i < k; i += kTriThreads) part = fmaf(vn[i], vn[i], part);
+  const float ss = block_sum(part, sh.red);
+  const float alpha = vn[q + 1];
+  float tq = 0.f, beta = alpha, inv = 0.f;
+  if (ss != 0.f) {
+    const float mu = sqrtf(fmaf(alpha, alpha, ss));
+    beta = alpha >= 0.f ? -mu : mu;
+    tq = (beta - alpha) / beta;
+    inv = 1.f / (alpha - beta);
+  }
+  __syncthreads();  // everyone has read alpha before vn is rescaled
+  float* rq = Rf + refl_off(k, q) - (q + 1);
+  for (int i = q + 1 + tid; i < k; i += kTriThreads) {
+    const float v = (i == q + 1) ? 1.f : vn[i] * inv;
+    vn[i] = v;
+    rq[i] = v;
+  }
+  if (tid == 0) {
+    tau[q] = tq;
+    e[q] = beta;
+  }
+  __syncthreads();
+  // trailing block: apply the previous update (none at q = 0) and form A v_q.  A wave
+  // takes kTriRows rows at a time, all their loads issued first, then walks the lane's
+  // columns (reflector entries read once per column for all the rows).
+  const int c0 = q + 1;
+  constexpr int kTriRows = tri_rows<KT>();
+  float colr[KT];
+#pragma unroll
+  for (int t = 0; t < KT; ++t) colr[t] = 0.f;
+  for (int rb = c0 + wave * kTriRows; rb < k; rb += kWaves * kTriRows) {
+    float a[kTriRows][KT];
+#pragma unroll
+    for (int u = 0; u < kTriRows; ++u)
+#pragma unroll
+      for (int t = 0; t < KT; ++t) {
+        const int r = rb + u, c = c0 + lane + 64 * t;
+        a[u][t] = (r < k && c <= r) ? at(r, c) : 0.f;
+      }
+    float vr[kTriRows], wr[kTriRows], nr[kTriRows], sr[kTriRows];
+#pragma unroll
+    for (int u = 0; u < kTriRows; ++u) {
+      const int r = min(rb + u, k - 1);
+      vr[u] = vp[r];
+      wr[u] = wp[r];
+      nr[u] = vn[r];
+      sr[u] = 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      const int c = c0 + lane + 64 * t;
+      const int cc = min(c, k - 1);
+      const float cw = wp[cc], cv = vp[cc], cn = vn[cc];
+#pragma unroll
+      for (int u = 0; u < kTriRows; ++u) {
+        const int r = rb + u;
+        if (r < k && c <= r) {
+          const float x = a[u][t] - vr[u] * cw - wr[u] * cv;
+          sr[u] = fmaf(x, cn, sr[u]);
+          if (c < r) colr[t] = fmaf(x, nr[u], colr[t]);
+          if (q > 0) at(r, c) = x;
+          if (c == c0) sh.next[r] = x;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kTriRows; ++u) {
+      const int r = rb + u;
+      if (r < k) {
+        const float s = wave_sum(sr[u]);
+        if (lane == 0) P[r] = s;
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    const int c = c0 + lane + 64 * t;
+    if (c < k) sh.col[wave][c] = colr[t];
+  }
+  __syncthreads();
+  float part2 = 0.f;
+  for (int r = c0 + tid; r < k; r += kTriThreads) {
+    float pr = P[r];
+#pragma unroll
+    for (int w2 = 0; w2 < kWaves; ++w2) pr += sh.col[w2][r];
+    P[r] = pr;
+    part2 = fmaf(pr, vn[r], part2);
+  }
+  const float vav = block_sum(part2, sh.red);  // v^T A v
+  const float half = 0.5f * tq * tq * vav;
+  for (int r = c0 + tid; r < k; r += kTriThreads) wn[r] = tq * P[r] - half * vn[r];
+  __syncthreads();
+}
 
 template <int KT>
 __device__ void tridiag_body(const AtMat& M, float* __restrict__ A, float* __restrict__ tau, float* __restrict__ d,
                              float* __restrict__ e, TriShared& sh) {
   const int k = M.k;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int kWaves = kTriWaves;
-  float (&V)[2][kMaxK] = sh.V;
-  float (&Wv)[2][kMaxK] = sh.Wv;
-  float* P = sh.P;
-  float* red = sh.red;
-  int cur = 0;
   for (int i = tid; i < k; i += kTriThreads) {
-    V[0][i] = 0.f;
-    Wv[0][i] = 0.f;
+    sh.V[0][i] = 0.f;
+    sh.Wv[0][i] = 0.f;
   }
   __syncthreads();
-  for (int q = 0; q + 2 < k; ++q) {
-    const float* vp = V[cur];
-    const float* wp = Wv[cur];
-    float* vn = V[cur ^ 1];
-    float* wn = Wv[cur ^ 1];
-    // column q below the diagonal, with the previous reflector's update applied
-    const float vq = vp[q], wq = wp[q];
-    for (int i = q + 1 + tid; i < k; i += kTriThreads) vn[i] = A[int64_t(i) * k + q] - vp[i] * wq - wp[i] * vq;
-    if (tid == 0) d[q] = A[int64_t(q) * k + q] - 2.f * vq * wq;
-    __syncthreads();
-    float part = 0.f;
-    for (int i = q + 2 + tid; i < k; i += kTriThreads) part = fmaf(vn[i], vn[i], part);
-    const float ss = block_sum(part, red);
-    const float alpha = vn[q + 1];
-    float tq = 0.f, beta = alpha, inv = 0.f;
-    if (ss != 0.f) {
-      const float mu = sqrtf(fmaf(alpha, alpha, ss));
-      beta = alpha >= 0.f ? -mu : mu;
-      tq = (beta - alpha) / beta;
-      inv = 1.f / (alpha - beta);
-    }
-    __syncthreads();  // everyone has read alpha before vn is rescaled
-    for (int i = q + 1 + tid; i < k; i += kTriThreads) {
-      const float v = (i == q + 1) ? 1.f : vn[i] * inv;
-      vn[i] = v;
-      A[int64_t(q) * k + i] = v;
-    }
-    if (tid == 0) {
-      tau[q] = tq;
-      e[q] = beta;
-    }
-    __syncthreads();
-    // trailing block: apply the previous update (none at q = 0) and form A v_q
-    const int c0 = q + 1;
-    constexpr int kTriRows = tri_rows<KT>();
-    for (int rb = c0 + wave * kTriRows; rb < k; rb += kWaves * kTriRows) {
-      float a[kTriRows][KT];
-#pragma unroll
-      for (int u = 0; u < kTriRows; ++u)
-#pragma unroll
-        for (int t = 0; t < KT; ++t) {
-          const int r = rb + u, c = c0 + lane + 64 * t;
-          a[u][t] = (r < k && c < k) ? A[int64_t(r) * k + c] : 0.f;
-        }
-#pragma unroll
-      for (int u = 0; u < kTriRows; ++u) {
-        const int r = rb + u;
-        if (r >= k) break;
-        const float vr = vp[r], wr = wp[r];
-        float s = 0.f;
-#pragma unroll
-        for (int t = 0; t < KT; ++t) {
-          const int c = c0 + lane + 64 * t;
-          if (c < k) {
-            const float x = a[u][t] - vr * wp[c] - wr * vp[c];
-            if (q > 0) A[int64_t(r) * k + c] = x;
-            s = fmaf(x, vn[c], s);
-          }
-        }
-        s = wave_sum(s);
-        if (lane == 0) P[r] = s;
-      }
-    }
-    __syncthreads();
-    float part2 = 0.f;
-    for (int r = c0 + tid; r < k; r += kTriThreads) part2 = fmaf(P[r], vn[r], part2);
-    const float vav = block_sum(part2, red);  // v^T A v
-    const float half = 0.5f * tq * tq * vav;
-    for (int r = c0 + tid; r < k; r += kTriThreads) wn[r] = tq * P[r] - half * vn[r];
-    __syncthreads();
-    cur ^= 1;
-  }
+  int cur = 0;
+  // global storage while the trailing block (rows and columns >= q) is too large for LDS
+  const int qlocal = max(0, k - kTailRows);
+  int q = 0;
+  for (; q + 2 < k && q < qlocal; ++q, cur ^= 1) tri_step<KT, false>(q, k, 0, A, A, tau, d, e, sh, cur);
+  // copy the block from row/column q on into LDS, then continue there
+  const int base = q;
+  for (int r = base + wave; r < k; r += kTriWaves)
+    for (int c = base + lane; c <= r; c += 64) sh.tail[tri_off(r - base) + (c - base)] = A[tri_off(r) + c];
+  __syncthreads();
+  for (; q + 2 < k; ++q, cur ^= 1) tri_step<KT, true>(q, k, base, A, A, tau, d, e, sh, cur);
   // the last 2 x 2 block (rows and columns k-2, k-1) with the last reflector's update
   if (tid == 0) {
-    const float* vp = V[cur];
-    const float* wp = Wv[cur];
+    const float* vp = sh.V[cur];
+    const float* wp = sh.Wv[cur];
     const int i0 = k - 2, i1 = k - 1;
-    d[i0] = A[int64_t(i0) * k + i0] - 2.f * vp[i0] * wp[i0];
-    e[i0] = A[int64_t(i1) * k + i0] - vp[i1] * wp[i0] - wp[i1] * vp[i0];
-    d[i1] = A[int64_t(i1) * k + i1] - 2.f * vp[i1] * wp[i1];
+    auto at = [&](int r, int c) { return sh.tail[tri_off(r - base) + (c - base)]; };
+    d[i0] = at(i0, i0) - 2.f * vp[i0] * wp[i0];
+    e[i0] = at(i1, i0) - vp[i1] * wp[i0] - wp[i1] * vp[i0];
+    d[i1] = at(i1, i1) - 2.f * vp[i1] * wp[i1];
   }
 }
 
-__global__ __launch_bounds__(kTriThreads) void at_tridiag(const AtMat* __restrict__ mats, float* __restrict__ gram,
+// One launch over every matrix of the plan (`list`), KT set by the widest one (k <= 64 KT):
+// narrower matrices leave slots idle, but every problem runs concurrently and the kernel
+// holds a single register allocation.
+template <int KT>
+__global__ __launch_bounds__(kTriThreads) void at_tridiag(const int32_t* __restrict__ list,
+                                                          const AtMat* __restrict__ mats, float* __restrict__ gram,
                                                           int64_t gram_ws, float* __restrict__ tau_ws,
                                                           float* __restrict__ d_ws, float* __restrict__ e_ws,
                                                           int64_t sv_total) {
-  const AtMat M = mats[blockIdx.x];
+  const AtMat M = mats[list[blockIdx.x]];
   const int64_t w = blockIdx.y;
   float* A = gram + w * gram_ws + M.b_off;
   float* tau = tau_ws + w * sv_total + M.sv_off;
   float* d = d_ws + w * sv_total + M.sv_off;
   float* e = e_ws + w * sv_total + M.sv_off;
   __shared__ TriShared sh;
-  const int kt = (M.k + 63) / 64;
-  if (kt <= 1) tridiag_body<1>(M, A, tau, d, e, sh);
-  else if (kt <= 2) tridiag_body<2>(M, A, tau, d, e, sh);
-  else if (kt <= 4) tridiag_body<4>(M, A, tau, d, e, sh);
-  else if (kt <= 8) tridiag_body<8>(M, A, tau, d, e, sh);
-  else tridiag_body<16>(M, A, tau, d, e, sh);
+  tridiag_body<KT>(M, A, tau, d, e, sh);
+}
+
+// the width class of a matrix: the smallest of 1, 2, 4, 8, 16 with k <= 64 * class
+inline int tri_class(int k) {
+  const int kt = (k + 63) / 64;
+  return kt > 8 ? 16 : kt > 4 ? 8 : kt > 2 ? 4 : kt > 1 ? 2 : 1;
 }
 
 // ------------------------------------------------------------------ at_eig
 // Number of eigenvalues of the tridiagonal (d, e^2) below x (Sturm sequence; a pivot
-// smaller than pivmin is replaced by -pivmin).
+// smaller than pivmin is replaced by -pivmin).  The hardware reciprocal (1 ulp) is
+// enough: only the signs of the pivots are used.
 __device__ __forceinline__ int sturm_below(const float* sd, const float* se2, int k, float x, float pivmin) {
   float q = sd[0] - x;
   if (fabsf(q) < pivmin) q = -pivmin;
   int c = q < 0.f;
+#pragma unroll 4
   for (int t = 1; t < k; ++t) {
-    q = (sd[t] - x) - se2[t - 1] / q;
+    q = (sd[t] - x) - se2[t - 1] * __builtin_amdgcn_rcpf(q);
     if (fabsf(q) < pivmin) q = -pivmin;
     c += q < 0.f;
   }
@@ -501,10 +582,16 @@ __global__ __launch_bounds__(kSampleThreads) void at_sample(const AtMat* __restr
 }
 
 // ------------------------------------------------------------------ at_vectors
-// Inverse iteration for the eigenvector of the tridiagonal (d, e) at eigenvalue lam:
-// Gaussian elimination with partial pivoting of T - lam I (one thread, float64), three
-// solves, each followed by orthogonalisation against the problem's earlier sent atoms
-// and normalisation.
+// Inverse iteration for the eigenvectors of the tridiagonal (d, e) at the sent atoms'
+// eigenvalues: Gaussian elimination with partial pivoting of T - lam I, then three
+// rounds of (solve; orthogonalise each vector, in atom order, against every earlier
+// atom's vector -- classical Gram-Schmidt applied twice --; normalise).  Up to kVecSlots
+// atoms are solved side by side, one lane each (the elimination is a sequential
+// recurrence); pivots below 2^-24 ||T|| are raised to that size.
+constexpr int kVecLdsBytes = 2048 * 21;  // slots * k * (5 floats + 1 byte) stays within this
+
+__device__ __forceinline__ int vec_slots(int k) { return max(1, min(8, 2048 / k)); }
+
 __global__ __launch_bounds__(kVecThreads) void at_vectors(const AtMat* __restrict__ mats,
                                                           const float* __restrict__ d_ws,
                                                           const float* __restrict__ e_ws,
@@ -514,7 +601,8 @@ __global__ __launch_bounds__(kVecThreads) void at_vectors(const AtMat* __restric
                                                           int64_t gram_ws, int64_t sv_total, int32_t n_mats) {
   const AtMat M = mats[blockIdx.x];
   const int64_t w = blockIdx.y;
-  const int k = M.k, tid = threadIdx.x;
+  const int k = M.k, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int kWaves = kVecThreads / 64;
   const int cnt = count[w * n_mats + M.mat_index];
   if (cnt == 0) return;
   const float* d = d_ws + w * sv_total + M.sv_off;
@@ -522,77 +610,85 @@ __global__ __launch_bounds__(kVecThreads) void at_vectors(const AtMat* __restric
   const float* lam = lam_ws + w * sv_total + M.sv_off;
   const int32_t* idx = index + w * sv_total + M.sv_off;
   float* y_all = Y + w * gram_ws + M.b_off;  // sent atom j's vector at j * k
-  __shared__ double sd[kMaxK], se[kMaxK];
-  __shared__ double u0[kMaxK], u1[kMaxK], u2[kMaxK], ml[kMaxK];
-  __shared__ unsigned char sw[kMaxK];
-  __shared__ double y[kMaxK];
-  __shared__ double red[kVecThreads / 64];
-  __shared__ double s_tiny;
-  double tn = 0.0;
+  __shared__ float sd[kMaxK], se[kMaxK], dots[kMaxK];
+  __shared__ float red[kWaves];
+  __shared__ __align__(16) unsigned char pool[kVecLdsBytes];
+  const int ns = vec_slots(k);
+  float* f0 = reinterpret_cast<float*>(pool);  // 1 / pivot
+  float* f1 = f0 + ns * k;                      // first entry right of the pivot
+  float* f2 = f1 + ns * k;                      // second entry right of the pivot
+  float* fm = f2 + ns * k;                      // multiplier
+  float* fy = fm + ns * k;                      // the slot's vector
+  unsigned char* fsw = reinterpret_cast<unsigned char*>(fy + ns * k);  // rows swapped
+  float tn = 0.f;
   for (int i = tid; i < k; i += kVecThreads) {
-    sd[i] = double(d[i]);
-    se[i] = i + 1 < k ? double(e[i]) : 0.0;
-    tn = fmax(tn, fabs(sd[i]) + 2.0 * fabs(se[i]));
+    sd[i] = d[i];
+    se[i] = i + 1 < k ? e[i] : 0.f;
+    tn = fmaxf(tn, fabsf(sd[i]) + 2.f * fabsf(se[i]));
   }
-  // the largest row sum bounds ||T||; pivots below 2^-24 ||T|| are raised to it
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) tn = fmax(tn, __shfl_xor(tn, o, 64));
-  if ((tid & 63) == 0) red[tid >> 6] = tn;
-  __syncthreads();
-  if (tid == 0) {
-    double m = 0.0;
-    for (int i = 0; i < kVecThreads / 64; ++i) m = fmax(m, red[i]);
-    s_tiny = fmax(m, 1e-300) * 0x1p-24;
-  }
-  __syncthreads();
-  const double tiny = s_tiny;
-  for (int j = 0; j < cnt; ++j) {
-    const int ei = k - 1 - idx[j];  // eigenvalue index, ascending
-    const double l = double(lam[ei]);
-    if (tid == 0) {
-      double cd = sd[0] - l, c1 = k > 1 ? se[0] : 0.0, c2 = 0.0;
+  const float tiny = fmaxf(block_max(tn, red), FLT_MIN) * 0x1p-24f;
+  for (int j0 = 0; j0 < cnt; j0 += ns) {
+    const int ng = min(ns, cnt - j0);
+    // factorisations, one lane per atom
+    if (tid < ng) {
+      const int s = tid;
+      const float l = lam[k - 1 - idx[j0 + s]];
+      float* u0 = f0 + s * k;
+      float* u1 = f1 + s * k;
+      float* u2 = f2 + s * k;
+      float* ml = fm + s * k;
+      unsigned char* sw = fsw + s * k;
+      float cd = sd[0] - l, c1 = k > 1 ? se[0] : 0.f, c2 = 0.f;
       for (int t = 0; t + 1 < k; ++t) {
-        const double sub = se[t], nd = sd[t + 1] - l, ns = t + 2 < k ? se[t + 1] : 0.0;
-        if (fabs(cd) >= fabs(sub)) {
-          double piv = cd;
-          if (fabs(piv) < tiny) piv = piv < 0.0 ? -tiny : tiny;
-          const double m = sub / piv;
-          u0[t] = piv;
+        const float sub = se[t], nd = sd[t + 1] - l, nsup = t + 2 < k ? se[t + 1] : 0.f;
+        if (fabsf(cd) >= fabsf(sub)) {
+          float piv = cd;
+          if (fabsf(piv) < tiny) piv = piv < 0.f ? -tiny : tiny;
+          const float r = 1.f / piv;
+          const float m = sub * r;
+          u0[t] = r;
           u1[t] = c1;
           u2[t] = c2;
           ml[t] = m;
           sw[t] = 0;
           cd = nd - m * c1;
-          c1 = ns - m * c2;
+          c1 = nsup - m * c2;
         } else {
-          const double m = cd / sub;
-          u0[t] = sub;
+          const float m = cd / sub;
+          u0[t] = 1.f / sub;
           u1[t] = nd;
-          u2[t] = ns;
+          u2[t] = nsup;
           ml[t] = m;
           sw[t] = 1;
           cd = c1 - m * nd;
-          c1 = c2 - m * ns;
+          c1 = c2 - m * nsup;
         }
-        c2 = 0.0;
+        c2 = 0.f;
       }
-      if (fabs(cd) < tiny) cd = cd < 0.0 ? -tiny : tiny;
-      u0[k - 1] = cd;
-      u1[k - 1] = 0.0;
-      u2[k - 1] = 0.0;
+      if (fabsf(cd) < tiny) cd = cd < 0.f ? -tiny : tiny;
+      u0[k - 1] = 1.f / cd;
+      u1[k - 1] = 0.f;
+      u2[k - 1] = 0.f;
     }
-    // a fixed start vector with entries in [0.5, 1.5)
-    for (int i = tid; i < k; i += kVecThreads) {
-      const uint32_t h = (uint32_t(i) + 1u) * 2654435761u ^ (uint32_t(j) + 1u) * 40503u;
-      y[i] = 0.5 + double((h >> 8) & 0xffffu) / 65536.0;
+    // fixed start vectors with entries in [0.5, 1.5)
+    for (int e2 = tid; e2 < ng * k; e2 += kVecThreads) {
+      const int s = e2 / k, i = e2 % k;
+      const uint32_t h = (uint32_t(i) + 1u) * 2654435761u ^ (uint32_t(j0 + s) + 1u) * 40503u;
+      fy[s * k + i] = 0.5f + float((h >> 8) & 0xffffu) / 65536.f;
     }
     __syncthreads();
     for (int it = 0; it < 3; ++it) {
-      if (tid == 0) {
-        // forward: apply the row operations to the right-hand side, in place
-        double cr = y[0];
+      if (tid < ng) {
+        const int s = tid;
+        const float* u0 = f0 + s * k;
+        const float* u1 = f1 + s * k;
+        const float* u2 = f2 + s * k;
+        const float* ml = fm + s * k;
+        const unsigned char* sw = fsw + s * k;
+        float* y = fy + s * k;
+        float cr = y[0];
         for (int t = 0; t + 1 < k; ++t) {
-          const double nr = y[t + 1];
+          const float nr = y[t + 1];
           if (sw[t] == 0) {
             y[t] = cr;
             cr = nr - ml[t] * cr;
@@ -602,34 +698,51 @@ __global__ __launch_bounds__(kVecThreads) void at_vectors(const AtMat* __restric
           }
         }
         y[k - 1] = cr;
-        // back substitution with the upper factor (diagonal and two above it)
-        double z1 = 0.0, z2 = 0.0;
+        float z1 = 0.f, z2 = 0.f, big = 0.f;
         for (int t = k - 1; t >= 0; --t) {
-          const double z = (y[t] - u1[t] * z1 - u2[t] * z2) / u0[t];
+          const float z = (y[t] - u1[t] * z1 - u2[t] * z2) * u0[t];
           y[t] = z;
           z2 = z1;
           z1 = z;
+          big = fmaxf(big, fabsf(z));
         }
+        // rescale so the next round cannot overflow
+        const float sc = big > 0.f ? 1.f / big : 0.f;
+        for (int t = 0; t < k; ++t) y[t] *= sc;
       }
       __syncthreads();
-      for (int jj = 0; jj < j; ++jj) {
-        const float* yo = y_all + int64_t(jj) * k;
-        double part = 0.0;
-        for (int i = tid; i < k; i += kVecThreads) part += y[i] * double(yo[i]);
-        const double dot = block_sum(part, red);
-        for (int i = tid; i < k; i += kVecThreads) y[i] -= dot * double(yo[i]);
+      for (int s = 0; s < ng; ++s) {
+        const int j = j0 + s;
+        float* y = fy + s * k;
+        for (int pass = 0; pass < 2; ++pass) {
+          for (int jj = wave; jj < j; jj += kWaves) {
+            const float* yo = y_all + int64_t(jj) * k;
+            float part = 0.f;
+            for (int i = lane; i < k; i += 64) part = fmaf(y[i], yo[i], part);
+            part = wave_sum(part);
+            if (lane == 0) dots[jj] = part;
+          }
+          __syncthreads();
+          for (int i = tid; i < k; i += kVecThreads) {
+            float v = y[i];
+            for (int jj = 0; jj < j; ++jj) v = fmaf(-dots[jj], y_all[int64_t(jj) * k + i], v);
+            y[i] = v;
+          }
+          __syncthreads();
+        }
+        float part = 0.f;
+        for (int i = tid; i < k; i += kVecThreads) part = fmaf(y[i], y[i], part);
+        const float nrm = sqrtf(block_sum(part, red));
+        const float inv = nrm > 0.f ? 1.f / nrm : 0.f;
+        float* yo = y_all + int64_t(j) * k;
+        for (int i = tid; i < k; i += kVecThreads) {
+          const float v = y[i] * inv;
+          y[i] = v;
+          yo[i] = v;
+        }
         __syncthreads();
       }
-      double part = 0.0;
-      for (int i = tid; i < k; i += kVecThreads) part += y[i] * y[i];
-      const double nrm = sqrt(block_sum(part, red));
-      const double inv = nrm > 0.0 ? 1.0 / nrm : 0.0;
-      for (int i = tid; i < k; i += kVecThreads) y[i] *= inv;
-      __syncthreads();
     }
-    float* yo = y_all + int64_t(j) * k;
-    for (int i = tid; i < k; i += kVecThreads) yo[i] = float(y[i]);
-    __syncthreads();
   }
 }
 
@@ -653,21 +766,23 @@ __device__ void backxform_body(const AtMat& M, const float* __restrict__ A, cons
     float vn[KT];
     int r = k - 3;
     if (r >= 0) {
+      const float* row = A + refl_off(k, r) - (r + 1);
 #pragma unroll
       for (int t = 0; t < KT; ++t) {
         const int c = lane + 64 * t;
-        vn[t] = (c > r && c < k) ? A[int64_t(r) * k + c] : 0.f;
+        vn[t] = (c > r && c < k) ? row[c] : 0.f;
       }
     }
     for (; r >= 0; --r) {
       float v[KT];
 #pragma unroll
       for (int t = 0; t < KT; ++t) v[t] = vn[t];
-      if (r > 0) {  // the next reflector's row, loaded ahead
+      if (r > 0) {  // the next reflector, loaded ahead
+        const float* row = A + refl_off(k, r - 1) - r;
 #pragma unroll
         for (int t = 0; t < KT; ++t) {
           const int c = lane + 64 * t;
-          vn[t] = (c > r - 1 && c < k) ? A[int64_t(r - 1) * k + c] : 0.f;
+          vn[t] = (c > r - 1 && c < k) ? row[c] : 0.f;
         }
       }
       const float tr = tau[r];
@@ -835,6 +950,7 @@ struct DevTables {
   GramTile* gtiles;
   FactorTile* ftiles;
   AtUpdTile* utiles;
+  int32_t* tri_list;
 };
 
 psgd_status device_tables(psgd_atomo_plan* plan, DevTables* out) {
@@ -845,10 +961,11 @@ psgd_status device_tables(psgd_atomo_plan* plan, DevTables* out) {
   const uint64_t bg = a256(plan->gtiles.size() * sizeof(GramTile) + 1);
   const uint64_t bf = a256(plan->ftiles.size() * sizeof(FactorTile) + 1);
   const uint64_t bu = a256(plan->utiles.size() * sizeof(AtUpdTile) + 1);
+  const uint64_t bl = a256(plan->tri_list.size() * sizeof(int32_t) + 1);
   auto it = plan->dev.find(dev);
   if (it == plan->dev.end()) {
     void* base = nullptr;
-    e = hipMalloc(&base, bm + bg + bf + bu);
+    e = hipMalloc(&base, bm + bg + bf + bu + bl);
     if (e != hipSuccess)
       return fail(PSGD_ERR_NO_MEMORY, std::string("hipMalloc of the plan's device tables: ") + hipGetErrorString(e));
     char* b = static_cast<char*>(base);
@@ -861,6 +978,9 @@ psgd_status device_tables(psgd_atomo_plan* plan, DevTables* out) {
     if (e == hipSuccess)
       e = hipMemcpy(b + bm + bg + bf, plan->utiles.data(), plan->utiles.size() * sizeof(AtUpdTile),
                     hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+      e = hipMemcpy(b + bm + bg + bf + bu, plan->tri_list.data(), plan->tri_list.size() * sizeof(int32_t),
+                    hipMemcpyHostToDevice);
     if (e != hipSuccess) {
       (void)hipFree(base);
       return hip_fail("hipMemcpy of the plan's device tables", e);
@@ -872,6 +992,7 @@ psgd_status device_tables(psgd_atomo_plan* plan, DevTables* out) {
   out->gtiles = reinterpret_cast<GramTile*>(b + bm);
   out->ftiles = reinterpret_cast<FactorTile*>(b + bm + bg);
   out->utiles = reinterpret_cast<AtUpdTile*>(b + bm + bg + bf);
+  out->tri_list = reinterpret_cast<int32_t*>(b + bm + bg + bf + bu);
   return PSGD_OK;
 }
 
@@ -1019,6 +1140,12 @@ extern "C" psgd_status psgd_atomo_plan_create(const psgd_layer* layers, int32_t 
         for (int c = 0; c < m.cols; c += kAtUpdThreads)
           plan->utiles.push_back(AtUpdTile{0, 0, int32_t(mi), r, std::min(m.rows, r + kAtUpdRows), c});
     }
+    for (size_t mi = 0; mi < plan->mats.size(); ++mi) {
+      plan->tri_list.push_back(int32_t(mi));
+      plan->tri_kt = std::max(plan->tri_kt, tri_class(plan->mats[mi].k));
+    }
+    std::stable_sort(plan->tri_list.begin(), plan->tri_list.end(),
+                     [&](int32_t x, int32_t y) { return plan->mats[size_t(x)].k > plan->mats[size_t(y)].k; });
     for (const auto& li : plan->info)
       if (!li.compressed)
         for (int64_t b = 0; b < li.numel; b += 4096)
@@ -1201,9 +1328,17 @@ extern "C" psgd_status psgd_atomo_step(psgd_atomo_plan* plan, const float* grads
     if ((s = launch(plan, kGram, at_gram, dim3(unsigned(plan->gtiles.size()), unsigned(W)), dim3(kGramThreads), st,
                     static_cast<const GramTile*>(dt.gtiles), M, grads, ld, gram, gws)) != PSGD_OK)
       return s;
-    if ((s = launch(plan, kTridiag, at_tridiag, mgrid, dim3(kTriThreads), st, M, gram, gws, tau, dd, ee, svt)) !=
-        PSGD_OK)
-      return s;
+    {
+      const int32_t* list = dt.tri_list;
+      switch (plan->tri_kt) {
+        case 16: s = launch(plan, kTridiag, at_tridiag<16>, mgrid, dim3(kTriThreads), st, list, M, gram, gws, tau, dd, ee, svt); break;
+        case 8: s = launch(plan, kTridiag, at_tridiag<8>, mgrid, dim3(kTriThreads), st, list, M, gram, gws, tau, dd, ee, svt); break;
+        case 4: s = launch(plan, kTridiag, at_tridiag<4>, mgrid, dim3(kTriThreads), st, list, M, gram, gws, tau, dd, ee, svt); break;
+        case 2: s = launch(plan, kTridiag, at_tridiag<2>, mgrid, dim3(kTriThreads), st, list, M, gram, gws, tau, dd, ee, svt); break;
+        default: s = launch(plan, kTridiag, at_tridiag<1>, mgrid, dim3(kTriThreads), st, list, M, gram, gws, tau, dd, ee, svt); break;
+      }
+      if (s != PSGD_OK) return s;
+    }
     if ((s = launch(plan, kEig, at_eig, mgrid, dim3(kEigThreads), st, M, static_cast<const float*>(dd),
                     static_cast<const float*>(ee), lam, sigma, svt)) != PSGD_OK)
       return s;
