@@ -46,6 +46,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_resnet18_r2_w16.json")
 RTOPK_SRC = os.path.join(ROOT, "distributed_sgd_gradient_ef_amd", "csrc", "rtopk.hip")
 RTOPK_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_rtopk_resnet18_w16.json")
 RTOPK_METRIC = "rTop-k step gradient GB/s (ResNet-18 shapes, 1% sent from the top 2%, W=16) & % HBM peak"
+ATOMO_METRIC = "Spectral-ATOMO step gradient GB/s (ResNet-18 shapes, budget s=2, W=16)"
+ATOMO_SRC = os.path.join(ROOT, "distributed_sgd_gradient_ef_amd", "csrc", "atomo.hip")
+ATOMO_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_atomo_resnet18_w16.json")
+FP32_VECTOR_PEAK_TFLOPS = 157.3
 
 
 def kernel_bytes(plan, dtype_bytes: int, variant: str) -> dict:
@@ -98,6 +102,22 @@ def rtopk_kernel_bytes(plan, dtype_bytes: int) -> dict:
     }
 
 
+def atomo_kernel_work(plan) -> dict:
+    """Algorithmic work per launch of the Spectral-ATOMO kernels: flops of the Gram
+    matrices (lower triangle, k (k + 1) L multiply-adds) and of the Householder
+    tridiagonalisation (4/3 k^3 per matrix and worker); HBM bytes of the passes over G."""
+    s = plan.sizes
+    W = s["n_workers"]
+    gram = tri = gbytes = 0
+    for L in plan.layers:
+        if L.compressed:
+            k, long = L.k, max(L.rows, L.cols)
+            gram += W * 2 * k * (k + 1) // 2 * long
+            tri += W * 4 * k ** 3 // 3
+            gbytes += W * 4 * L.rows * L.cols
+    return {"at_gram": ("flops", gram), "at_tridiag": ("flops", tri), "at_factor": ("bytes", gbytes)}
+
+
 def traffic_for(kernel: str, traffic_file: str = TRAFFIC_FILE, source: str = KERNEL_SRC):
     """Measured HBM bytes per launch from committed rocprofv3 counter runs, if they
     were taken on the current kernel source; else None."""
@@ -148,6 +168,37 @@ def cpu_baseline(wl, seconds: float) -> dict:
             "sample": f"{steps} whole step(s) of the same workload (all 21 matrices and 41 tensors, "
                       f"W=16, r=2), numpy float64 oracle, {t_step:.2f} s per step; BLAS threads = cores; "
                       f"value_1thread: one more step on one thread, {t_one:.2f} s"}
+
+
+def atomo_cpu_baseline(wl, seconds: float) -> dict:
+    """Time the Spectral-ATOMO oracle on whole workers of the same workload (every matrix
+    and tensor of one worker per round, at least one round), scaled to W workers."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from distributed_sgd_gradient_ef_amd import workloads as WL
+    from oracle import atomo as O
+
+    grads = WL.grads(wl, 0)
+    rounds, t0 = 0, time.perf_counter()
+    while True:
+        w = rounds % wl.workers
+        for li, g in enumerate(grads):
+            if O.is_matrix(g.shape[1:]):
+                x = WL.atomo_uniforms(wl, 0, w, li, min(g.shape[1:]))
+                O.compress_matrix(g[w].astype(np.float64), wl.atomo_budget, x)
+        rounds += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    t_worker = el / rounds
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    gbytes = wl.workers * wl.numel() * 4 / 1e9
+    return {"value": round(gbytes / (t_worker * wl.workers), 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{rounds} worker(s) of the same workload (all 21 matrices of one worker per round, "
+                      f"float64 numpy SVD oracle), {t_worker:.2f} s per worker, scaled to W={wl.workers}; "
+                      f"BLAS threads = cores"}
 
 
 def timed_steps(torch, step, steps: int, stream):
@@ -244,7 +295,7 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline sample length")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the context timings of the other configurations")
-    ap.add_argument("--mode", choices=["all", "carry", "plain", "deferred", "local", "rtopk"], default="all",
+    ap.add_argument("--mode", choices=["all", "carry", "plain", "deferred", "local", "rtopk", "atomo"], default="all",
                     help="plan variants to time (profiling runs use one); rtopk times only the rTop-k step")
     ap.add_argument("--primary", choices=["carry", "deferred", "plain", "local"], default="deferred",
                     help="variant reported as `value` when several are timed")
@@ -414,6 +465,102 @@ def main() -> int:
             "kernels": kernels,
         }
 
+    def measure_atomo() -> dict:
+        wa = WL.workload("resnet18_atomo")
+        plan = psgd.psgd_atomo_plan_create(shapes, wa.atomo_budget, W)
+        s = plan.sizes
+        ld, sv = s["worker_stride"], s["sv_total"]
+        nsets = 2
+        grads = torch.zeros((nsets, W, ld), dtype=torch.float32, device=dev)
+        unif = torch.zeros((nsets, W, sv), dtype=torch.float32, device=dev)
+        layout = [(L.offset, L.rows, L.cols) for L in plan.layers]
+        for k in range(nsets):
+            WL.device_grads(wa, k, layout, grads[k])
+            xs = {li: np.stack([WL.atomo_uniforms(wa, k, w, li, L.k) for w in range(W)])
+                  for li, L in enumerate(plan.layers) if L.compressed}
+            unif[k].copy_(torch.from_numpy(psgd.pack_sv(plan, xs)))
+        sigma = torch.zeros((W, sv), dtype=torch.float32, device=dev)
+        prob = torch.zeros_like(sigma)
+        index = torch.zeros((W, sv), dtype=torch.int32, device=dev)
+        count = torch.zeros((W, s["n_matrices"]), dtype=torch.int32, device=dev)
+        atoms = torch.zeros((W, s["atom_total"]), dtype=torch.float32, device=dev)
+        update = torch.zeros(ld, dtype=torch.float32, device=dev)
+        workspace = torch.empty(s["workspace_bytes"], dtype=torch.uint8, device=dev)
+        stream = torch.cuda.current_stream(dev)
+        turn = [0]
+
+        def step():
+            k = turn[0] % nsets
+            turn[0] += 1
+            psgd.psgd_atomo_step(plan, grads[k], unif[k], sigma, prob, index, count, atoms, update, workspace,
+                                 stream)
+
+        nsteps = max(1, min(args.steps, 20))
+        for _ in range(min(args.warmup, 3)):
+            step()
+        torch.cuda.synchronize(dev)
+        ms, ms_med, ms_min = timed_steps(torch, step, nsteps, stream)
+        psgd.psgd_atomo_plan_set_timing(plan, True)
+        psgd.psgd_atomo_plan_kernel_stats(plan, reset=True)
+        for _ in range(nsteps):
+            step()
+        torch.cuda.synchronize(dev)
+        stats = psgd.psgd_atomo_plan_kernel_stats(plan, reset=True)
+        psgd.psgd_atomo_plan_set_timing(plan, False)
+        sent = float(count.float().mean().item())
+        work = atomo_kernel_work(plan)
+        kernels = {}
+        for name, (n, tot) in stats.items():
+            us = 1e3 * tot / max(n, 1)
+            entry = {"mean_us": round(us, 2), "launches": n}
+            if name in work:
+                kind, amount = work[name]
+                entry["alg_" + kind] = amount
+                if kind == "flops":
+                    entry["alg_TFLOPs"] = round(amount / (us * 1e-6) / 1e12, 3)
+                else:
+                    entry["alg_GBps"] = round(amount / (us * 1e-6) / 1e9, 1)
+            kernels[name] = entry
+        dom = max(kernels, key=lambda k: kernels[k]["mean_us"])
+        dom_us = kernels[dom]["mean_us"]
+        kind, amount = work.get(dom, ("flops", 0))
+        if kind == "flops":
+            achieved = amount / (dom_us * 1e-6) / 1e12
+            roof = {"kernel": dom, "bound": "alu", "achieved": round(achieved, 3), "peak": FP32_VECTOR_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / FP32_VECTOR_PEAK_TFLOPS, 5)}
+        else:
+            achieved = amount / (dom_us * 1e-6) / 1e9
+            roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+        roof.update({"traffic": traffic_for(dom, ATOMO_TRAFFIC_FILE, ATOMO_SRC), "alg_" + kind + "_per_launch": amount,
+                     "mean_us": dom_us})
+        grad_bytes = W * s["numel"] * 4
+        del grads, workspace, atoms
+        out = {
+            "metric": ATOMO_METRIC,
+            "value": round(grad_bytes / (ms * 1e-3) / 1e9, 2),
+            "unit": "GB/s",
+            "ms_per_step": round(ms, 4),
+            "ms_per_step_median": round(ms_med, 4),
+            "ms_per_step_min": round(ms_min, 4),
+            "steps": nsteps,
+            "config": {"workload": "resnet18_cifar_shapes", "workers": W, "matrices": s["n_matrices"],
+                       "budget": wa.atomo_budget, "sv_total": sv, "grad_bytes_per_step": grad_bytes,
+                       "mean_atoms_sent_per_matrix": round(sent, 3), "gradient_sets": nsets},
+            "roofline": roof,
+            "kernels": kernels,
+        }
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = atomo_cpu_baseline(wa, args.cpu_seconds / 3)
+        return out
+
+    if args.mode == "atomo":
+        out = measure_atomo()
+        out.update({"n_gpus": 1, "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
+                    "vs_baseline": None, "dtype": "f32", "stream_copy_GBps": round(copy_gbs, 1)})
+        print(json.dumps(out), flush=True)
+        return 0
+
     if args.mode == "rtopk":
         out = measure_rtopk()
         out.update({"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
@@ -468,6 +615,7 @@ def main() -> int:
                        for n, r in results.items() if n != primary}
     if args.mode == "all":
         out["rtopk"] = measure_rtopk()
+        out["atomo"] = measure_atomo()
         if not args.no_configs:
             out["other_configs"] = config_timings(torch, psgd, WL, dev, args.steps)
     if not args.no_cpu_baseline:

@@ -108,12 +108,28 @@ def expected_square_norm(lam: np.ndarray, p: np.ndarray) -> float:
 
 
 def sparsify(lam: np.ndarray, atoms: Sequence[np.ndarray], p: np.ndarray, t: np.ndarray) -> np.ndarray:
-    """g_hat = sum_i (lam_i t_i / p_i) a_i for any list of atoms (arrays of one shape)."""
+    """g_hat = sum_i (lam_i t_i / p_i) a_i for any indexable sequence of atoms (arrays of
+    one shape), in index order; atoms that are not sent are never read."""
     out = np.zeros(np.shape(atoms[0]), dtype=np.float64)
-    for li, ai, pi, ti in zip(lam, atoms, p, t):
-        if ti:
-            out += (li / pi) * np.asarray(ai, dtype=np.float64)
+    for i in range(len(lam)):
+        if t[i]:
+            out += (lam[i] / p[i]) * np.asarray(atoms[i], dtype=np.float64)
     return out
+
+
+class OuterAtoms:
+    """The spectral atoms left[:, i] right[i, :] of a decomposition, each built when read."""
+
+    def __init__(self, left: np.ndarray, right: np.ndarray):
+        self.left, self.right = left, right
+
+    def __len__(self) -> int:
+        return self.left.shape[1]
+
+    def __getitem__(self, i: int) -> np.ndarray:
+        if not 0 <= i < len(self):
+            raise IndexError(i)
+        return np.outer(self.left[:, i], self.right[i, :])
 
 
 # ------------------------------------------------------------------ one matrix, one worker
@@ -142,7 +158,7 @@ def compress_matrix(g: np.ndarray, s: float, x: np.ndarray) -> AtomoMatrix:
     else:        # the unit factor is the right singular vector
         a = (sigma[index] / p[index])[:, None] * left[:, index].T
         b = right[index, :].copy()
-    estimate = sparsify(sigma, [np.outer(left[:, i], right[i, :]) for i in range(len(sigma))], p, t)
+    estimate = sparsify(sigma, OuterAtoms(left, right), p, t)
     return AtomoMatrix(sigma, p, index, a, b, estimate)
 
 
