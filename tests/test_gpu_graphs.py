@@ -1,0 +1,109 @@
+"""Every step of the library can be captured into a HIP graph (torch.cuda.CUDAGraph) once
+its plan has run one step eagerly (the first call uploads the plan's tables).  A
+captured step is replayed several times, with the program's own eager work and a
+synchronisation between replays, and every replay is compared bit for bit with a second
+plan stepped eagerly from the same state (the kernels are deterministic)."""
+
+import numpy as np
+import pytest
+
+from distributed_sgd_gradient_ef_amd import psgd as P
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+DEV = "cuda:0"
+REPLAYS = 4
+
+
+def _replay_and_compare(name, make, step, outputs):
+    """make() -> state dict of device tensors (and plan); step(state) enqueues one step;
+    outputs(state) -> list of tensors to compare."""
+    print(f"[graphs] case {name}", flush=True)
+    a, b = make(), make()
+    for _ in range(2):                      # eager warm-up on both (plan tables uploaded)
+        step(a)
+        step(b)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(a)
+    torch.cuda.synchronize()
+    scratch = torch.zeros(1 << 20, device=DEV)
+    for i in range(REPLAYS):
+        g.replay()
+        scratch.add_(1.0)                   # eager work between the replays
+        torch.cuda.synchronize()
+        step(b)
+        torch.cuda.synchronize()
+        for j, (x, y) in enumerate(zip(outputs(a), outputs(b))):
+            assert torch.equal(x, y), f"{name}: replay {i}, output {j} differs from the eager step"
+
+
+def test_powersgd_deferred_step_graph():
+    shapes = [(64, 27), (1, 64), (128, 130), (10, 512)]
+    W, r = 4, 2
+
+    def make():
+        plan = P.psgd_plan_create(shapes, r, W, P.PSGD_F32, P.PSGD_FLAG_DEFERRED_ERROR)
+        s = plan.sizes
+        rs = np.random.default_rng(601)
+        g = torch.from_numpy(rs.standard_normal((W, s["worker_stride"])).astype(np.float32)).to(DEV)
+        q = torch.from_numpy(rs.standard_normal(s["q_elems"]).astype(np.float32)).to(DEV)
+        return dict(plan=plan, g=g, e=torch.zeros_like(g), q=q,
+                    p=torch.zeros(s["p_elems"], device=DEV), u=torch.zeros(s["worker_stride"], device=DEV),
+                    ws=torch.zeros(s["workspace_bytes"], dtype=torch.uint8, device=DEV))
+
+    def step(st):
+        P.psgd_compress_step(st["plan"], st["g"], st["e"], st["q"], st["p"], st["u"], st["ws"])
+
+    _replay_and_compare("powersgd deferred", make, step, lambda st: [st["e"], st["q"], st["p"], st["u"]])
+
+
+def test_rtopk_step_graph():
+    shapes = [(64, 27), (1, 64), (10, 512), (3, 5)]
+    tops, keeps = [40, 4, 100, 15], [20, 1, 50, 15]
+    W = 3
+
+    def make():
+        plan = P.psgd_rtopk_plan_create(shapes, tops, keeps, W)
+        s = plan.sizes
+        rs = np.random.default_rng(602)
+        g = torch.from_numpy(rs.standard_normal((W, s["worker_stride"])).astype(np.float32)).to(DEV)
+        ranks = P.pack_rows(plan, [np.stack([rs.permutation(t) for _ in range(W)]) for t in tops], "top",
+                            np.uint32).view(np.int32)
+        return dict(plan=plan, g=g, e=torch.zeros_like(g), ranks=torch.from_numpy(ranks).to(DEV),
+                    index=torch.zeros((W, s["keep_total"]), dtype=torch.int32, device=DEV),
+                    value=torch.zeros((W, s["keep_total"]), device=DEV),
+                    u=torch.zeros(s["worker_stride"], device=DEV),
+                    ws=torch.zeros(s["workspace_bytes"], dtype=torch.uint8, device=DEV))
+
+    def step(st):
+        P.psgd_rtopk_step(st["plan"], st["g"], st["e"], st["ranks"], st["index"], st["value"], st["u"], st["ws"])
+
+    _replay_and_compare("rtopk", make, step, lambda st: [st["e"], st["index"], st["value"], st["u"]])
+
+
+def test_atomo_step_graph():
+    shapes = [(20, 33), (33, 20), (1, 9)]
+    W = 2
+
+    def make():
+        plan = P.psgd_atomo_plan_create(shapes, 1.5, W)
+        s = plan.sizes
+        rs = np.random.default_rng(603)
+        g = torch.from_numpy(rs.standard_normal((W, s["worker_stride"])).astype(np.float32)).to(DEV)
+        x = torch.from_numpy(rs.random((W, s["sv_total"])).astype(np.float32)).to(DEV)
+        return dict(plan=plan, g=g, x=x, sigma=torch.zeros((W, s["sv_total"]), device=DEV),
+                    prob=torch.zeros((W, s["sv_total"]), device=DEV),
+                    index=torch.zeros((W, s["sv_total"]), dtype=torch.int32, device=DEV),
+                    count=torch.zeros((W, s["n_matrices"]), dtype=torch.int32, device=DEV),
+                    atoms=torch.zeros((W, s["atom_total"]), device=DEV), u=torch.zeros(s["worker_stride"], device=DEV),
+                    ws=torch.zeros(s["workspace_bytes"], dtype=torch.uint8, device=DEV))
+
+    def step(st):
+        P.psgd_atomo_step(st["plan"], st["g"], st["x"], st["sigma"], st["prob"], st["index"], st["count"],
+                          st["atoms"], st["u"], st["ws"])
+
+    _replay_and_compare("atomo", make, step,
+                        lambda st: [st["sigma"], st["prob"], st["index"], st["count"], st["atoms"], st["u"]])
