@@ -359,6 +359,21 @@ def main() -> int:
         ms_timed = t2.elapsed_time(t3) / args.steps
         stats = psgd.psgd_plan_kernel_stats(plan, reset=True)
         psgd.psgd_plan_set_timing(plan, False)
+        # timed region 3 (context): one step captured into a HIP graph, replayed K times
+        ms_graph = None
+        if variant == args.primary:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                psgd.psgd_compress_step(plan, grads, errors, q, p, update, workspace)
+            torch.cuda.synchronize(dev)
+            g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            g0.record(stream)
+            for _ in range(args.steps):
+                graph.replay()
+            g1.record(stream)
+            torch.cuda.synchronize(dev)
+            ms_graph = g0.elapsed_time(g1) / args.steps
+            del graph
         kb = kernel_bytes(plan, 4, variant)
         kernels = {}
         for name, (n, tot) in stats.items():
@@ -370,7 +385,8 @@ def main() -> int:
             kernels[name] = entry
         grad_bytes = W * s["numel"] * 4
         del grads, errors, workspace
-        return {"ms": ms, "ms_med": ms_med, "ms_min": ms_min, "ms_timed": ms_timed, "kernels": kernels, "kb": kb,
+        return {"ms": ms, "ms_med": ms_med, "ms_min": ms_min, "ms_timed": ms_timed, "ms_graph": ms_graph,
+                "kernels": kernels, "kb": kb,
                 "sizes": s,
                 "value": grad_bytes / (ms * 1e-3) / 1e9, "grad_bytes": grad_bytes,
                 "pct": 100.0 * s["model_bytes"] / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9)}
@@ -607,6 +623,7 @@ def main() -> int:
                      "alg_bytes_per_launch": kb[dom], "mean_us": dom_us},
         "kernels": kernels,
         "ms_per_step_with_kernel_events": round(main_run["ms_timed"], 4),
+        "ms_per_step_graph_replay": round(main_run["ms_graph"], 4) if main_run["ms_graph"] else None,
         "stream_copy_GBps": round(copy_gbs, 1),
     }
     out["variants"] = {n: {"value": round(r["value"], 2), "ms_per_step": round(r["ms"], 4),

@@ -313,3 +313,16 @@ def test_step_is_reproducible_and_update_optional():
     for key in ("sigma", "prob", "index", "count", "atoms"):
         assert np.array_equal(first[key], second[key], equal_nan=True), key
     assert np.all(np.isnan(second["update"]))
+
+
+def test_lstm_shaped_matrices():
+    """k = 650 in both orientations (the widest width class, 1 < k / 512), with the
+    separated spectra of the parity cases."""
+    rng = np.random.default_rng(450)
+    shapes = [(2000, 650), (650, 1300)]
+    W = 2
+    grads = [np.stack([_spectral(rng, n, m, _separated_sigma(min(n, m), w)) for w in range(W)]) for n, m in shapes]
+    xs = [rng.random((W, 650)).astype(np.float32) for _ in shapes]
+    run, out, orc = _run_case("lstm-shaped", shapes, 3.0, W, grads, xs)
+    for li in orc:
+        _check_layer(run.plan, out, li, orc[li], grads[li], compare_vectors=False)
