@@ -326,3 +326,17 @@ def test_lstm_shaped_matrices():
     run, out, orc = _run_case("lstm-shaped", shapes, 3.0, W, grads, xs)
     for li in orc:
         _check_layer(run.plan, out, li, orc[li], grads[li], compare_vectors=False)
+
+
+def test_plan_without_matrices():
+    """Only 1-D tensors: no decomposition runs and the update is the workers' mean."""
+    rng = np.random.default_rng(460)
+    shapes = [(1, 300), (5, 1), (1, 4097)]
+    W = 3
+    grads = [rng.standard_normal((W, n, m)) for n, m in shapes]
+    print("[atomo] case vectors only", flush=True)
+    run = AtomoRun(shapes, 2.0, W)
+    assert run.plan.sizes["n_matrices"] == 0 and run.plan.sizes["sv_total"] == 0
+    run.set_grads(grads)
+    run.step()
+    _check_vectors(run, run.fetch(), grads)
