@@ -132,12 +132,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
 // Sum over the workgroup; every thread gets the total (waves added in index order).
 template <typename T>
 __device__ T block_sum(T v, T* red) {

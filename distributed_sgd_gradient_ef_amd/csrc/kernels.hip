@@ -57,13 +57,12 @@ enum FirstPass { kFpMean = 0, kFpCarry = 1, kFpDefer = 2 };
 // Gradients and errors are touched once per pass and never reused from cache, so the
 // worker passes load and store them non-temporally; buffers that a later kernel of the
 // same step reads again (Mbar, the carried error mean) use ordinary accesses.
-// V elements per lane: 4 when a matrix's column count is a multiple of 4 (rows 16-byte
-// aligned), 2 when it is even (rows 8-byte aligned), else 1.
+// V elements per lane: 4 when a matrix's column count is even (rows 16-byte aligned, or
+// 8-byte aligned and accessed as two halves), else 1.
 template <int V>
-using vec_t = std::conditional_t<V == 4, f4, std::conditional_t<V == 2, f2, float>>;
+using vec_t = std::conditional_t<V == 4, f4, float>;
 
 __device__ __forceinline__ float lane(const f4& x, int q) { return x[q]; }
-__device__ __forceinline__ float lane(const f2& x, int q) { return x[q]; }
 __device__ __forceinline__ float lane(const float& x, int) { return x; }
 
 __device__ __forceinline__ f4 widen(const u16x4 v) {
@@ -94,8 +93,6 @@ __device__ __forceinline__ vec_t<V> ldv(const float* p, bool hi = true) {
     return f4{a.x, a.y, b.x, b.y};
   } else if constexpr (V == 4)
     return *reinterpret_cast<const f4*>(p);
-  else if constexpr (V == 2)
-    return *reinterpret_cast<const f2*>(p);
   else
     return *p;
 }
@@ -108,8 +105,6 @@ __device__ __forceinline__ vec_t<V> ld_nt(const float* p, bool hi = true) {
     return f4{a.x, a.y, b.x, b.y};
   } else if constexpr (V == 4)
     return __builtin_nontemporal_load(reinterpret_cast<const f4*>(p));
-  else if constexpr (V == 2)
-    return __builtin_nontemporal_load(reinterpret_cast<const f2*>(p));
   else
     return __builtin_nontemporal_load(p);
 }
@@ -122,8 +117,6 @@ __device__ __forceinline__ vec_t<V> ld_nt(const bf16* p, bool hi = true) {
     return f4{a.x, a.y, b.x, b.y};
   } else if constexpr (V == 4)
     return widen(__builtin_nontemporal_load(reinterpret_cast<const u16x4*>(p)));
-  else if constexpr (V == 2)
-    return widen(__builtin_nontemporal_load(reinterpret_cast<const u16x2*>(p)));
   else
     return __uint_as_float(uint32_t(__builtin_nontemporal_load(reinterpret_cast<const unsigned short*>(p))) << 16);
 }
@@ -135,8 +128,6 @@ __device__ __forceinline__ void st(float* p, const vec_t<V> v, bool hi = true) {
     if (hi) *reinterpret_cast<f2*>(p + 2) = f2{v.z, v.w};
   } else if constexpr (V == 4)
     *reinterpret_cast<f4*>(p) = v;
-  else if constexpr (V == 2)
-    *reinterpret_cast<f2*>(p) = v;
   else
     *p = v;
 }
@@ -148,8 +139,6 @@ __device__ __forceinline__ void st_nt(float* p, const vec_t<V> v, bool hi = true
     if (hi) __builtin_nontemporal_store(f2{v.z, v.w}, reinterpret_cast<f2*>(p + 2));
   } else if constexpr (V == 4)
     __builtin_nontemporal_store(v, reinterpret_cast<f4*>(p));
-  else if constexpr (V == 2)
-    __builtin_nontemporal_store(v, reinterpret_cast<f2*>(p));
   else
     __builtin_nontemporal_store(v, p);
 }
@@ -285,8 +274,6 @@ template <int V>
 __device__ __forceinline__ vec_t<V> pq_row(const float (&pr)[4], const float (&qv)[V][4], int R) {
   if constexpr (V == 4)
     return f4{pq_dot(pr, qv[0], R), pq_dot(pr, qv[1], R), pq_dot(pr, qv[2], R), pq_dot(pr, qv[3], R)};
-  else if constexpr (V == 2)
-    return f2{pq_dot(pr, qv[0], R), pq_dot(pr, qv[1], R)};
   else
     return pq_dot(pr, qv[0], R);
 }
