@@ -10,9 +10,9 @@
 // eigenvector on that side: the other factor is G^T u / p (or G v / p), one more pass
 // over G.  Launches, each covering every problem of every worker:
 //
-//   at_gram       the Gram matrix, 64 x 64 output tiles of its lower block triangle
-//                 (stored as the packed lower triangle), the contraction over the long
-//                 side staged through LDS
+//   at_gram       the Gram matrix, 128 x 128 output tiles of its lower block triangle
+//                 (stored as the packed lower triangle) with fp32 MFMA, the contraction
+//                 over the long side staged through LDS
 //   at_tridiag    one workgroup per problem: Householder reduction of the Gram matrix
 //                 to tridiagonal form.  Each step forms the next reflector from the
 //                 updated column, then one pass over the packed trailing block both
@@ -51,8 +51,8 @@ namespace psgd {
 namespace atm {
 
 constexpr int kMaxK = PSGD_ATOMO_MAX_K;
-constexpr int kGramTile = 64;
-constexpr int kGramKC = 16;
+constexpr int kGramTile = 128;
+constexpr int kGramKC = 32;
 constexpr int kGramThreads = 256;
 constexpr int kTriThreads = 1024;
 // rows per wave per batch of the trailing-block pass (fewer for the widest rows, whose
@@ -171,6 +171,15 @@ __device__ __forceinline__ int tri_off(int r) { return (r * (r + 1)) >> 1; }
 __device__ __forceinline__ int refl_off(int k, int q) { return tri_off(k) + q * (k - 1) - ((q * (q - 1)) >> 1); }
 
 // ------------------------------------------------------------------ at_gram
+// One 128 x 128 tile of the lower block triangle per workgroup of four waves; each wave
+// computes a 64 x 64 quadrant as 2 x 2 blocks of the fp32 matrix instruction
+// v_mfma_f32_32x32x2_f32 (D += A B with A 32 x 2, B 2 x 32).  Its operands: lane l holds
+// A[l mod 32][l / 32] and B[l / 32][l mod 32]; result D[i][j] is accumulator
+// (i mod 4) + 4 (i / 8) of lane j + 32 ((i / 4) mod 2).  The long side is staged through
+// LDS in chunks of kGramKC, read as float4 where a matrix's rows are 16-byte aligned.
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+
 __global__ __launch_bounds__(kGramThreads) void at_gram(const GramTile* __restrict__ tiles,
                                                         const AtMat* __restrict__ mats,
                                                         const float* __restrict__ G, int64_t ld,
@@ -183,51 +192,119 @@ __global__ __launch_bounds__(kGramThreads) void at_gram(const GramTile* __restri
   const int k = M.k, cols = M.cols;
   const int L = M.left ? M.cols : M.rows;  // contraction length
   const int a0 = t.ti * kGramTile, b0 = t.tj * kGramTile;
-  __shared__ float sa[kGramKC][kGramTile + 4];
-  __shared__ float sb[kGramKC][kGramTile + 4];
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  float acc[4][4];
+  __shared__ __align__(16) float sa[kGramKC][kGramTile + 4];
+  __shared__ __align__(16) float sb[kGramKC][kGramTile + 4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wr = (wave >> 1) * 64, wc = (wave & 1) * 64;  // the wave's quadrant
+  const int half = lane >> 5, l32 = lane & 31;
+  const bool vec = (cols & 3) == 0;  // rows (and the offset, a multiple of 64) 16-byte aligned
+  f16v acc[2][2] = {};
+  auto mfma_chunk = [&]() {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int kk = 0; kk < kGramKC; kk += 2) {
+      const float x0 = sa[kk + half][wr + l32], x1 = sa[kk + half][wr + 32 + l32];
+      const float y0 = sb[kk + half][wc + l32], y1 = sb[kk + half][wc + 32 + l32];
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, y0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, y1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, y0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, y1, acc[1][1], 0, 0, 0);
+    }
+  };
+  if (vec) {
+    // four consecutive elements along the contiguous direction per thread and step; the
+    // next chunk is loaded into registers while the current one is multiplied
+    constexpr int kSteps = kGramTile * kGramKC / 4 / kGramThreads;
+    f4 ra[kSteps], rb[kSteps];
+    auto fetch = [&](int c0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-  for (int c0 = 0; c0 < L; c0 += kGramKC) {
-    for (int e = threadIdx.x; e < kGramTile * kGramKC; e += kGramThreads) {
-      if (M.left) {  // element (short index a, long index c) = G[a][c]
-        const int a = e / kGramKC, c = e % kGramKC;
-        const bool cin = c0 + c < L;
-        sa[c][a] = (cin && a0 + a < k) ? g[int64_t(a0 + a) * cols + c0 + c] : 0.f;
-        sb[c][a] = (cin && b0 + a < k) ? g[int64_t(b0 + a) * cols + c0 + c] : 0.f;
-      } else {       // element (short index a, long index c) = G[c][a]
-        const int c = e / kGramTile, a = e % kGramTile;
-        const bool cin = c0 + c < L;
-        sa[c][a] = (cin && a0 + a < k) ? g[int64_t(c0 + c) * cols + a0 + a] : 0.f;
-        sb[c][a] = (cin && b0 + a < k) ? g[int64_t(c0 + c) * cols + b0 + a] : 0.f;
+      for (int i = 0; i < kSteps; ++i) {
+        const int e = int(threadIdx.x) + i * kGramThreads;
+        f4 va = {0.f, 0.f, 0.f, 0.f}, vb = {0.f, 0.f, 0.f, 0.f};
+        if (M.left) {  // G[a][c0 + c .. +3]
+          const int a = e / (kGramKC / 4), c = (e % (kGramKC / 4)) * 4;
+          if (c0 + c + 3 < L) {
+            if (a0 + a < k) va = *reinterpret_cast<const f4*>(g + int64_t(a0 + a) * cols + c0 + c);
+            if (b0 + a < k) vb = *reinterpret_cast<const f4*>(g + int64_t(b0 + a) * cols + c0 + c);
+          } else {
+            for (int q = 0; q < 4; ++q)
+              if (c0 + c + q < L) {
+                if (a0 + a < k) va[q] = g[int64_t(a0 + a) * cols + c0 + c + q];
+                if (b0 + a < k) vb[q] = g[int64_t(b0 + a) * cols + c0 + c + q];
+              }
+          }
+        } else {       // G[c0 + c][a0 + a .. +3]
+          const int c = e / (kGramTile / 4), a = (e % (kGramTile / 4)) * 4;
+          if (c0 + c < L) {
+            const float* row = g + int64_t(c0 + c) * cols;
+            if (a0 + a + 3 < k) va = *reinterpret_cast<const f4*>(row + a0 + a);
+            else
+              for (int q = 0; q < 4; ++q)
+                if (a0 + a + q < k) va[q] = row[a0 + a + q];
+            if (b0 + a + 3 < k) vb = *reinterpret_cast<const f4*>(row + b0 + a);
+            else
+              for (int q = 0; q < 4; ++q)
+                if (b0 + a + q < k) vb[q] = row[b0 + a + q];
+          }
+        }
+        ra[i] = va;
+        rb[i] = vb;
       }
+    };
+    auto stage = [&]() {
+#pragma unroll
+      for (int i = 0; i < kSteps; ++i) {
+        const int e = int(threadIdx.x) + i * kGramThreads;
+        if (M.left) {
+          const int a = e / (kGramKC / 4), c = (e % (kGramKC / 4)) * 4;
+          for (int q = 0; q < 4; ++q) {
+            sa[c + q][a] = ra[i][q];
+            sb[c + q][a] = rb[i][q];
+          }
+        } else {
+          const int c = e / (kGramTile / 4), a = (e % (kGramTile / 4)) * 4;
+          *reinterpret_cast<f4*>(&sa[c][a]) = ra[i];
+          *reinterpret_cast<f4*>(&sb[c][a]) = rb[i];
+        }
+      }
+    };
+    fetch(0);
+    for (int c0 = 0; c0 < L; c0 += kGramKC) {
+      stage();
+      __syncthreads();
+      if (c0 + kGramKC < L) fetch(c0 + kGramKC);
+      mfma_chunk();
+      __syncthreads();
     }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < kGramKC; ++kk) {
-      float av[4], bv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = sa[kk][ty * 4 + i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bv[j] = sb[kk][tx * 4 + j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+  } else {
+    for (int c0 = 0; c0 < L; c0 += kGramKC) {
+      for (int e = threadIdx.x; e < kGramTile * kGramKC; e += kGramThreads) {
+        if (M.left) {  // element (short index a, long index c) = G[a][c]
+          const int a = e / kGramKC, c = e % kGramKC;
+          const bool cin = c0 + c < L;
+          sa[c][a] = (cin && a0 + a < k) ? g[int64_t(a0 + a) * cols + c0 + c] : 0.f;
+          sb[c][a] = (cin && b0 + a < k) ? g[int64_t(b0 + a) * cols + c0 + c] : 0.f;
+        } else {       // element (short index a, long index c) = G[c][a]
+          const int c = e / kGramTile, a = e % kGramTile;
+          const bool cin = c0 + c < L;
+          sa[c][a] = (cin && a0 + a < k) ? g[int64_t(c0 + c) * cols + a0 + a] : 0.f;
+          sb[c][a] = (cin && b0 + a < k) ? g[int64_t(c0 + c) * cols + b0 + a] : 0.f;
+        }
+      }
+      __syncthreads();
+      mfma_chunk();
+      __syncthreads();
     }
-    __syncthreads();
   }
   // the lower triangle only, packed
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int a = a0 + ty * 4 + i, b = b0 + tx * 4 + j;
-      if (a < k && b <= a) B[tri_off(a) + b] = acc[i][j];
-    }
+    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int a = a0 + wr + 32 * bi + 8 * (v >> 2) + 4 * half + (v & 3), b = b0 + wc + 32 * bj + l32;
+        if (a < k && b <= a) B[tri_off(a) + b] = acc[bi][bj][v];
+      }
 }
 
 // ------------------------------------------------------------------ at_tridiag
