@@ -445,7 +445,8 @@ __device__ __forceinline__ void first_matrix_tile(const UpdTile& t, const MatInf
                                                   const float* Qin, float* Mbar, float* Ppart, int W, int64_t ld,
                                                   int R, float inv_w, int offset_valid) {
   const int cols = mi.cols;
-  const int j = t.col_begin + int(threadIdx.x) * V;
+  const int ln = int(threadIdx.x) & 63;
+  const int j = t.col_begin + ln * V;
   const bool active = j < cols;
   const bool hi = A == V || j + 4 <= cols;
   float qv[V][4];
@@ -483,13 +484,13 @@ __device__ __forceinline__ void first_matrix_tile(const UpdTile& t, const MatInf
     for (int k = 0; k < 4; ++k)
       if (k < R) {
         const float v = wave_sum(part[k]);
-        if (threadIdx.x == 0) prow[int64_t(i) * R + k] = v;
+        if (ln == 0) prow[int64_t(i) * R + k] = v;
       }
   }
 }
 
-template <typename GT, int WT, int FP>
-__global__ __launch_bounds__(kStreamThreads) void k_first(const UpdTile* __restrict__ tiles,
+template <typename GT, int WT, int FP, int NW>
+__global__ __launch_bounds__(kStreamThreads * NW) void k_first(const UpdTile* __restrict__ tiles, int32_t ntiles,
                                                           const MatInfo* __restrict__ mats,
                                                           const GT* __restrict__ G, float* __restrict__ E,
                                                           const float* __restrict__ ebar,
@@ -498,10 +499,12 @@ __global__ __launch_bounds__(kStreamThreads) void k_first(const UpdTile* __restr
                                                           const float* __restrict__ Qin, float* __restrict__ Mbar,
                                                           float* __restrict__ Ppart, int W, int64_t ld, int R,
                                                           float inv_w, int offset_valid) {
-  const UpdTile t = tiles[blockIdx.x];
+  const int ti = int(blockIdx.x) * NW + int(threadIdx.x >> 6);  // one tile per wave
+  if (ti >= ntiles) return;
+  const UpdTile t = tiles[ti];
   if (t.mat < 0) {  // uncompressed tensor: the worker mean of G
     if (blockIdx.y != 0) return;
-    const int64_t c = t.begin + int64_t(threadIdx.x) * 4;
+    const int64_t c = t.begin + int64_t(threadIdx.x & 63) * 4;
     if (c < t.end) store4(Mbar + c, sum_g<4, GT, WT>(G, W, ld, c) * inv_w, t.end - c);
     return;
   }
@@ -879,7 +882,7 @@ __device__ __forceinline__ void apply_matrix_tile(const UpdTile& t, const MatInf
                                                   float* update, float* mom, float* x, float* ebar, int W,
                                                   int64_t ld, int R, int mode, float lr, float mu, float inv_w) {
   const int cols = mi.cols;
-  const int j = t.col_begin + int(threadIdx.x) * V;
+  const int j = t.col_begin + (int(threadIdx.x) & 63) * V;
   if (j >= cols) return;
   const bool hi = A == V || j + 4 <= cols;
   float qv[V][4];
@@ -902,17 +905,19 @@ __device__ __forceinline__ void apply_matrix_tile(const UpdTile& t, const MatInf
   }
 }
 
-template <typename GT, int WT, bool LOCAL>
-__global__ __launch_bounds__(kStreamThreads) void k_apply(
-    const UpdTile* __restrict__ tiles, const MatInfo* __restrict__ mats, const GT* __restrict__ G,
+template <typename GT, int WT, bool LOCAL, int NW>
+__global__ __launch_bounds__(kStreamThreads * NW) void k_apply(
+    const UpdTile* __restrict__ tiles, int32_t ntiles, const MatInfo* __restrict__ mats, const GT* __restrict__ G,
     float* __restrict__ E, const float* __restrict__ Mbar, const float* __restrict__ P,
     const float* __restrict__ Q, const float* __restrict__ Qw, int64_t q_ws, float* __restrict__ update,
     float* __restrict__ mom, float* __restrict__ x, float* __restrict__ ebar, int W, int64_t ld, int R, int mode,
     float lr, float mu, float inv_w) {
-  const UpdTile t = tiles[blockIdx.x];
+  const int ti = int(blockIdx.x) * NW + int(threadIdx.x >> 6);  // one tile per wave
+  if (ti >= ntiles) return;
+  const UpdTile t = tiles[ti];
   if (t.mat < 0) {
     if (blockIdx.y != 0) return;
-    const int64_t c = t.begin + int64_t(threadIdx.x) * 4;
+    const int64_t c = t.begin + int64_t(threadIdx.x & 63) * 4;
     if (c >= t.end) return;
     const int64_t valid = t.end - c;
     const f4 uv = *reinterpret_cast<const f4*>(Mbar + c);
@@ -1168,18 +1173,28 @@ struct StepArgs {
 
 enum PassKind { kPassFirst = 0, kPassApply = 1 };
 
+// NW waves per workgroup, one worker-pass tile each (one wave: measured, four waves per
+// workgroup were no faster at W = 4 or 8).
+template <typename GT, int WT, int NW>
+psgd_status launch_pass_nw(psgd_plan* plan, int which, int fp, const DeviceTables& dt, const StepArgs& a) {
+  const GT* g = static_cast<const GT*>(a.grads);
+  const int32_t ntiles = int32_t(a.n_s2);
+  const dim3 grid((a.n_s2 + NW - 1) / NW, a.rows_per_tile), block(kStreamThreads * NW);
+  if (which == kPassApply)
+    return launch_k(plan, kKApply, a.Qw != nullptr ? k_apply<GT, WT, true, NW> : k_apply<GT, WT, false, NW>, grid,
+                    block, a.st, dt.s2tiles, ntiles, dt.mats, g, a.errors, a.Mbar, a.p, a.q,
+                    static_cast<const float*>(a.Qw), a.q_ws, a.update, a.mom, a.x, a.ebar_out, a.W, a.ld, a.R,
+                    a.mode, a.lr, a.mu, a.inv_w);
+  auto first = fp == kFpDefer   ? k_first<GT, WT, kFpDefer, NW>
+               : fp == kFpCarry ? k_first<GT, WT, kFpCarry, NW>
+                                : k_first<GT, WT, kFpMean, NW>;
+  return launch_k(plan, kKFirst, first, grid, block, a.st, dt.s2tiles, ntiles, dt.mats, g, a.errors, a.ebar_in,
+                  a.Pprev, a.Qprev, a.q, a.Mbar, a.Ppart, a.W, a.ld, a.R, a.inv_w, a.offset_valid);
+}
+
 template <typename GT, int WT>
 psgd_status launch_pass(psgd_plan* plan, int which, int fp, const DeviceTables& dt, const StepArgs& a) {
-  const GT* g = static_cast<const GT*>(a.grads);
-  const dim3 grid(a.n_s2, a.rows_per_tile), block(kStreamThreads);
-  if (which == kPassApply)
-    return launch_k(plan, kKApply, a.Qw != nullptr ? k_apply<GT, WT, true> : k_apply<GT, WT, false>, grid, block, a.st,
-                    dt.s2tiles, dt.mats, g, a.errors, a.Mbar, a.p, a.q, static_cast<const float*>(a.Qw), a.q_ws,
-                    a.update, a.mom, a.x, a.ebar_out, a.W, a.ld, a.R, a.mode, a.lr, a.mu, a.inv_w);
-  auto first = fp == kFpDefer ? k_first<GT, WT, kFpDefer> : fp == kFpCarry ? k_first<GT, WT, kFpCarry>
-                                                                           : k_first<GT, WT, kFpMean>;
-  return launch_k(plan, kKFirst, first, grid, block, a.st, dt.s2tiles, dt.mats, g, a.errors, a.ebar_in, a.Pprev,
-                  a.Qprev, a.q, a.Mbar, a.Ppart, a.W, a.ld, a.R, a.inv_w, a.offset_valid);
+  return launch_pass_nw<GT, WT, 1>(plan, which, fp, dt, a);
 }
 
 // Worker-count specialisations of the worker passes: W in {1,2,4,8,16} unrolls fully,
