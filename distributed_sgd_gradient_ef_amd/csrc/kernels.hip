@@ -278,6 +278,147 @@ __device__ __forceinline__ vec_t<V> pq_row(const float (&pr)[4], const float (&q
     return pq_dot(pr, qv[0], R);
 }
 
+// ------------------------------------------------------------------ flat chunks
+// A flat matrix (rows that do not start on a 128-byte line) is streamed in runs of
+// consecutive elements, four per lane from a 16-byte boundary, so that no cache line is
+// split between two waves.  A lane's four elements can run from the end of one row into
+// the start of the next.
+struct Flat4 {
+  int i0, j0;  // row and column of the lane's first element
+  int nw;      // how many of the four lie in row i0; the rest continue row i0 + 1 from column 0
+  int valid;   // how many lie inside the matrix (0 past its end)
+};
+
+// c: absolute element offset of the lane's first element (a multiple of 4).
+__device__ __forceinline__ Flat4 flat4_at(const MatInfo& mi, int64_t c) {
+  const int64_t e = c - mi.offset;
+  const int64_t numel = int64_t(mi.rows) * mi.cols;
+  Flat4 f;
+  if (e >= numel) {
+    f.i0 = mi.rows;
+    f.j0 = 0;
+    f.nw = 4;
+    f.valid = 0;
+    return f;
+  }
+  const int ei = int(e);
+  f.i0 = ei / mi.cols;
+  f.j0 = ei - f.i0 * mi.cols;
+  f.nw = min(4, mi.cols - f.j0);
+  f.valid = int(min<int64_t>(4, numel - e));
+  return f;
+}
+
+// Q row of one column: R floats (one float4 or float2 load for R = 4 or 2; every Q
+// block starts on a 16-byte boundary), zeros past the rank.
+__device__ __forceinline__ void load_q_col(float (&qc)[4], const float* Qm, int col, int R) {
+  const float* b = Qm + int64_t(col) * R;
+  if (R == 4) {
+    const f4 v = *reinterpret_cast<const f4*>(b);
+    qc[0] = v.x;
+    qc[1] = v.y;
+    qc[2] = v.z;
+    qc[3] = v.w;
+  } else if (R == 2) {
+    const f2 v = *reinterpret_cast<const f2*>(b);
+    qc[0] = v.x;
+    qc[1] = v.y;
+    qc[2] = 0.f;
+    qc[3] = 0.f;
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) qc[k] = (k < R) ? b[k] : 0.f;
+  }
+}
+
+// P rows i0 and i0 + 1 of the lane's elements (zeros where the lane has none).
+__device__ __forceinline__ void load_flat_p_rows(float (&p0)[4], float (&p1)[4], const float* Pm, const Flat4& f,
+                                                 int R) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) p0[k] = p1[k] = 0.f;
+  if (f.valid > 0) load_p_row(p0, Pm, f.i0, R);
+  if (f.valid > f.nw) load_p_row(p1, Pm, f.i0 + 1, R);
+}
+
+// (P Q^T) at the lane's elements, each by pq_dot (0 past the matrix end).
+__device__ __forceinline__ f4 pq_flat(const float (&p0)[4], const float (&p1)[4], const float* Qm, const Flat4& f,
+                                      int R) {
+  f4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (q < f.valid) {
+      const bool first = q < f.nw;
+      float qc[4], pr[4];
+      load_q_col(qc, Qm, first ? f.j0 + q : q - f.nw, R);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) pr[k] = first ? p0[k] : p1[k];
+      u[q] = pq_dot(pr, qc, R);
+    }
+  return u;
+}
+
+// P-bar partial row sums of one flat chunk (chunk index `chunk` within the matrix; mb
+// is zero past the matrix end).  Each lane splits its share of mb Q between rows i0 and
+// i0 + 1; the part in row i0 + 1 moves to the next lane, whose first element is in that
+// row.  A segmented inclusive scan over the wave (lanes keyed by row, fixed order) then
+// leaves each row's sum over the chunk in the row's last lane, which writes it to slot
+// chunk - (first chunk of the row).  The part of the last lane in row i0 + 1 is that
+// row's whole share of the chunk and is written as it is.  Every lane must call this.
+__device__ __forceinline__ void flat_pbar_partial(const MatInfo& mi, const Flat4& f, const f4 mb, const float* Qm,
+                                                  float* Ppart, int chunk, int R) {
+  const int ln = int(threadIdx.x) & 63;
+  float a[4] = {0.f, 0.f, 0.f, 0.f}, b[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (q < f.valid) {
+      const bool first = q < f.nw;
+      float qc[4];
+      load_q_col(qc, Qm, first ? f.j0 + q : q - f.nw, R);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (first)
+          a[k] += mb[q] * qc[k];
+        else
+          b[k] += mb[q] * qc[k];
+      }
+    }
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (k < R) {
+      const float t = __shfl_up(b[k], 1, 64);
+      if (ln > 0) a[k] += t;
+    }
+  const int key = f.valid > 0 ? f.i0 : mi.rows;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int kk = __shfl_up(key, o, 64);
+    float t[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) t[k] = (k < R) ? __shfl_up(a[k], o, 64) : 0.f;
+    if (ln >= o && kk == key)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (k < R) a[k] += t[k];
+  }
+  const int next = __shfl_down(key, 1, 64);
+  float* base = Ppart + mi.ppart_off;
+  if ((ln == 63 || next != key) && key < mi.rows) {
+    const int slot = chunk - (key * mi.cols) / kStreamTileElems;
+    float* dst = base + (int64_t(slot) * mi.rows + key) * R;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (k < R) dst[k] = a[k];
+  }
+  if (ln == 63 && f.valid > f.nw) {
+    const int row = f.i0 + 1;
+    const int slot = chunk - (row * mi.cols) / kStreamTileElems;
+    float* dst = base + (int64_t(slot) * mi.rows + row) * R;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (k < R) dst[k] = b[k];
+  }
+}
+
 // ------------------------------------------------------------------ worker loops
 // Every worker's slice of one chunk (V consecutive elements at c) is loaded before any
 // is used.  WT > 0: the worker count is the compile-time WT (fully unrolled); WT == 0:
@@ -410,6 +551,52 @@ __device__ __forceinline__ vec_t<V> update_workers_local(const GT* G, float* E, 
   return acc;
 }
 
+// The last lane of a flat matrix whose size is not a multiple of 4: E_w <- (G_w + E_w) - u
+// on the first `valid` elements only (the loads past them stay inside the padding before
+// the next tensor); returns sum_w of the new values (unspecified past `valid`).
+template <typename GT>
+__device__ f4 update_workers_tail(const GT* G, float* E, int W, int64_t ld, int64_t c, const f4 u, int valid) {
+  f4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int w = 0; w < W; ++w) {
+    const f4 n = (ld_nt<4>(G + w * ld + c) + ld_nt<4>(E + w * ld + c)) - u;
+    store4_nt(E + w * ld + c, n, valid);
+    acc += n;
+  }
+  return acc;
+}
+
+// PSGD_FLAG_LOCAL_Q_ERROR over a flat chunk: E_w <- (G_w + E_w) - (P Q_w^T) at the
+// lane's elements, only the first `valid` of them stored; returns sum_w of the new values.
+template <typename GT, int WT>
+__device__ __forceinline__ f4 update_workers_local_flat(const GT* G, float* E, int W, int64_t ld, int64_t c,
+                                                        const float (&p0)[4], const float (&p1)[4],
+                                                        const float* Qw, int64_t q_ws, int64_t q_off,
+                                                        const Flat4& f, int R) {
+  f4 acc = {0.f, 0.f, 0.f, 0.f};
+  constexpr int B = 4;
+  for (int w0 = 0; w0 < W; w0 += B) {
+    f4 g[B], e[B];
+#pragma unroll
+    for (int k = 0; k < B; ++k)
+      if ((WT > 0 && WT % B == 0) || w0 + k < W) {
+        g[k] = ld_nt<4>(G + (w0 + k) * ld + c);
+        e[k] = ld_nt<4>(E + (w0 + k) * ld + c);
+      }
+#pragma unroll
+    for (int k = 0; k < B; ++k)
+      if ((WT > 0 && WT % B == 0) || w0 + k < W) {
+        const f4 uw = pq_flat(p0, p1, Qw + int64_t(w0 + k) * q_ws + q_off, f, R);
+        const f4 n = (g[k] + e[k]) - uw;
+        if (f.valid == 4)
+          st_nt<4>(E + (w0 + k) * ld + c, n);
+        else
+          store4_nt(E + (w0 + k) * ld + c, n, f.valid);
+        acc += n;
+      }
+  }
+  return acc;
+}
+
 template <int V, int A = V>
 __device__ __forceinline__ void momentum_v(float* mom, float* x, int64_t c, const vec_t<V> u, int mode, float lr,
                                            float mu, bool hi = true) {
@@ -489,6 +676,40 @@ __device__ __forceinline__ void first_matrix_tile(const UpdTile& t, const MatInf
   }
 }
 
+// The same for one flat chunk: chunk blockIdx.y of the tile, four elements per lane.
+template <typename GT, int WT, int FP>
+__device__ __forceinline__ void first_flat_tile(const UpdTile& t, const MatInfo& mi, const GT* G, float* E,
+                                                const float* ebar, const float* Pprev, const float* Qprev,
+                                                const float* Qin, float* Mbar, float* Ppart, int W, int64_t ld,
+                                                int R, float inv_w, int offset_valid) {
+  const int64_t c0 = t.begin + int64_t(blockIdx.y) * kStreamTileElems;
+  if (c0 >= t.end) return;
+  const int64_t c = c0 + int64_t(threadIdx.x & 63) * 4;
+  const Flat4 f = flat4_at(mi, c);
+  f4 mb = {0.f, 0.f, 0.f, 0.f};
+  if (f.valid > 0) {
+    if constexpr (FP == kFpDefer) {
+      f4 u = {0.f, 0.f, 0.f, 0.f};
+      if (offset_valid) {
+        float p0[4], p1[4];
+        load_flat_p_rows(p0, p1, Pprev + mi.p_off, f, R);
+        u = pq_flat(p0, p1, Qprev + mi.q_off, f, R);
+      }
+      mb = (f.valid == 4 ? update_workers<4, GT, WT>(G, E, W, ld, c, u)
+                         : update_workers_tail<GT>(G, E, W, ld, c, u, f.valid)) * inv_w;
+    } else if constexpr (FP == kFpCarry) {
+      mb = sum_g<4, GT, WT>(G, W, ld, c) * inv_w + ldv<4>(ebar + c);
+    } else {
+      mb = sum_ge<4, GT, WT>(G, E, W, ld, c) * inv_w;
+    }
+    store4(Mbar + c, mb, f.valid);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (q >= f.valid) mb[q] = 0.f;
+  }
+  flat_pbar_partial(mi, f, mb, Qin + mi.q_off, Ppart, int((c0 - mi.offset) / kStreamTileElems), R);
+}
+
 template <typename GT, int WT, int FP, int NW>
 __global__ __launch_bounds__(kStreamThreads * NW) void k_first(const UpdTile* __restrict__ tiles, int32_t ntiles,
                                                           const MatInfo* __restrict__ mats,
@@ -509,6 +730,10 @@ __global__ __launch_bounds__(kStreamThreads * NW) void k_first(const UpdTile* __
     return;
   }
   const MatInfo mi = mats[t.mat];
+  if (mi.flat) {
+    first_flat_tile<GT, WT, FP>(t, mi, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, W, ld, R, inv_w, offset_valid);
+    return;
+  }
   switch (mi.vw) {
     case 4: first_matrix_tile<4, GT, WT, FP>(t, mi, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, W, ld, R, inv_w,
                                      offset_valid); break;
@@ -562,6 +787,21 @@ __global__ __launch_bounds__(kStreamThreads) void k_p_mbar(const UpdTile* __rest
   const UpdTile t = tiles[blockIdx.x];
   if (t.mat < 0) return;
   const MatInfo mi = mats[t.mat];
+  if (mi.flat) {
+    const int64_t c0 = t.begin + int64_t(blockIdx.y) * kStreamTileElems;
+    if (c0 >= t.end) return;
+    const int64_t c = c0 + int64_t(threadIdx.x) * 4;
+    const Flat4 f = flat4_at(mi, c);
+    f4 mb = {0.f, 0.f, 0.f, 0.f};
+    if (f.valid > 0) {
+      mb = ldv<4>(Mbar + c);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (q >= f.valid) mb[q] = 0.f;
+    }
+    flat_pbar_partial(mi, f, mb, Qin + mi.q_off, Ppart, int((c0 - mi.offset) / kStreamTileElems), R);
+    return;
+  }
   switch (mi.vw) {
     case 4: pbar_mbar_tile<4>(t, mi, Mbar, Qin, Ppart, R); break;
     case 2: pbar_mbar_tile<4, 2>(t, mi, Mbar, Qin, Ppart, R); break;
@@ -578,45 +818,88 @@ __global__ __launch_bounds__(kStreamThreads) void k_p_mbar(const UpdTile* __rest
 // fresh column and its projection on column 0 share one reduction (both use the
 // unmodified column).
 // Matrices with at most kMgsRowsPerThread rows per thread keep their rows in registers;
-// taller ones take two passes through the output buffer (below).  `P2`, if set,
-// receives a copy of the result.
-constexpr int kMgsRowsPerThread = 4;
+// taller ones go through their Gram matrix (below).  `P2`, if set, receives a copy of
+// the result.
 
-template <int R>
-__device__ __forceinline__ void pbar_row(float (&acc)[R], const float* src, int64_t strip_stride, int nst,
-                                         int i) {
+// Partial slots of row i: every column strip, or for a flat matrix the chunks the row
+// overlaps.
+__device__ __forceinline__ int pbar_slots(const MatInfo& mi, int i) {
+  if (!mi.flat) return mi.nstrips;
+  return ((i + 1) * mi.cols - 1) / kStreamTileElems - (i * mi.cols) / kStreamTileElems + 1;
+}
+
+// P-bar rows i_first + u * step for u < U (zero rows from n on): each the sum of its
+// partial slots in slot order.  SU slots of all U rows are loaded at once, every load
+// unconditional (a slot a row does not have reads the matrix's first partial instead and
+// is not added), so that they overlap.
+template <int R, int U>
+__device__ __forceinline__ void pbar_rows(float (&acc)[U][R], const float* src, int64_t strip_stride,
+                                          const MatInfo& mi, int i_first, int step, int n) {
+  constexpr int SU = (U * R >= 16) ? 1 : 16 / (U * R);
+  int ns[U];
 #pragma unroll
-  for (int k = 0; k < R; ++k) acc[k] = 0.f;
-#pragma unroll 6
-  for (int sidx = 0; sidx < nst; ++sidx)
+  for (int u = 0; u < U; ++u) {
+    const int i = i_first + u * step;
+    ns[u] = i < n ? pbar_slots(mi, i) : 0;
 #pragma unroll
-    for (int k = 0; k < R; ++k) acc[k] += src[sidx * strip_stride + int64_t(i) * R + k];
+    for (int k = 0; k < R; ++k) acc[u][k] = 0.f;
+  }
+  for (int s0 = 0; s0 < mi.nstrips; s0 += SU) {
+    float tmp[SU][U][R];
+#pragma unroll
+    for (int j = 0; j < SU; ++j)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float* row =
+            (s0 + j < ns[u]) ? src + (s0 + j) * strip_stride + int64_t(i_first + u * step) * R : src;
+#pragma unroll
+        for (int k = 0; k < R; ++k) tmp[j][u][k] = row[k];
+      }
+#pragma unroll
+    for (int j = 0; j < SU; ++j)
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (s0 + j < ns[u])
+#pragma unroll
+          for (int k = 0; k < R; ++k) acc[u][k] += tmp[j][u][k];
+  }
 }
 
 template <int R>
 __global__ __launch_bounds__(kMgsThreads) void k_mgs(const MatInfo* __restrict__ mats,
                                                      const float* __restrict__ Ppart,
-                                                     float* __restrict__ P, float* __restrict__ P2) {
+                                                     float* __restrict__ P, float* __restrict__ P2,
+                                                     const double* __restrict__ gpart,
+                                                     double* __restrict__ tmat) {
   __shared__ double red[2 * (kMgsThreads / 64)];
   const MatInfo mi = mats[blockIdx.x];
   const float* src = Ppart + mi.ppart_off;
   float* dst = P + mi.p_off;
   const int n = mi.rows;
-  const int nst = mi.nstrips;
   const int64_t strip_stride = int64_t(n) * R;
   const int bs = blockDim.x;
 
-  if (n <= bs * kMgsRowsPerThread) {
+  if (mi.tall_blk0 < 0) {
+    // as many rows per thread as the matrix needs, so that a thread with one row has
+    // more of that row's partial slots in flight
     float v[kMgsRowsPerThread][R];
+    const int rpt = (n + bs - 1) / bs;
+    if (rpt == 1) {
+      float a[1][R];
+      pbar_rows<R, 1>(a, src, strip_stride, mi, int(threadIdx.x), bs, n);
 #pragma unroll
-    for (int r = 0; r < kMgsRowsPerThread; ++r) {
-      const int i = threadIdx.x + r * bs;
-      if (i < n) {
-        pbar_row<R>(v[r], src, strip_stride, nst, i);
-      } else {
+      for (int r = 0; r < kMgsRowsPerThread; ++r)
 #pragma unroll
-        for (int k = 0; k < R; ++k) v[r][k] = 0.f;
-      }
+        for (int k = 0; k < R; ++k) v[r][k] = r == 0 ? a[0][k] : 0.f;
+    } else if (rpt == 2) {
+      float a[2][R];
+      pbar_rows<R, 2>(a, src, strip_stride, mi, int(threadIdx.x), bs, n);
+#pragma unroll
+      for (int r = 0; r < kMgsRowsPerThread; ++r)
+#pragma unroll
+        for (int k = 0; k < R; ++k) v[r][k] = r < 2 ? a[r][k] : 0.f;
+    } else {
+      pbar_rows<R, kMgsRowsPerThread>(v, src, strip_stride, mi, int(threadIdx.x), bs, n);
     }
 #pragma unroll
     for (int k = 0; k < R; ++k) {
@@ -664,34 +947,25 @@ __global__ __launch_bounds__(kMgsThreads) void k_mgs(const MatInfo* __restrict__
     return;
   }
 
-  // Tall matrices: two passes over the rows.  Pass 1 forms P-bar (kept in the output)
-  // and its Gram matrix in double.  One thread then takes the same Gram-Schmidt in the
-  // R x R Gram space -- the projection coefficients R_lk on the kept columns l < k and the
-  // residual norm sqrt(G_kk - sum_l R_lk^2), with the same drop rule -- and forms
-  // T = R^-1 (zero columns for dropped ones).  Pass 2 writes P = P-bar T.
+  // Tall matrices: k_tall_rows has written P-bar into the output and one Gram partial
+  // (in double) per block of kTallRows rows.  The partials are summed in a fixed order;
+  // one thread takes the same Gram-Schmidt in the R x R Gram space -- the projection
+  // coefficients R_lk on the kept columns l < k and the residual norm
+  // sqrt(G_kk - sum_l R_lk^2), with the same drop rule -- and stores T = R^-1 (zero
+  // columns for dropped ones) for k_tall_apply, which writes P = P-bar T.
   constexpr int NG = R * (R + 1) / 2;
   double g[NG];
 #pragma unroll
-  for (int a = 0; a < NG; ++a) g[a] = 0.0;
-  for (int i = threadIdx.x; i < n; i += bs) {
-    float acc[R];
-    pbar_row<R>(acc, src, strip_stride, nst, i);
-    int a = 0;
-#pragma unroll
-    for (int k = 0; k < R; ++k) {
-      dst[int64_t(i) * R + k] = acc[k];
-#pragma unroll
-      for (int l = k; l < R; ++l) g[a++] += double(acc[k]) * double(acc[l]);
-    }
+  for (int a = 0; a < NG; ++a) {
+    double s = 0.0;
+    for (int b = int(threadIdx.x); b < mi.tall_nblk; b += bs) s += gpart[int64_t(mi.tall_blk0 + b) * 10 + a];
+    g[a] = block_sum(s, red);
   }
-#pragma unroll
-  for (int a = 0; a < NG; ++a) g[a] = block_sum(g[a], red);
-  __shared__ double T[R][R];
   if (threadIdx.x == 0) {
     auto G = [&](int k, int l) {  // Gram entry (k <= l) in the packed upper triangle
       return g[k * R - k * (k - 1) / 2 + (l - k)];
     };
-    double Rm[R][R];
+    double Rm[R][R], T[R][R];
     bool kept[R];
     for (int k = 0; k < R; ++k) {
       const double before = sqrt(G(k, k));
@@ -716,21 +990,72 @@ __global__ __launch_bounds__(kMgsThreads) void k_mgs(const MatInfo* __restrict__
           for (int m = 0; m < R; ++m) T[m][k] -= Rm[l][k] * T[m][l] / after;
       }
     }
+    double* out = tmat + int64_t(blockIdx.x) * 16;
+    for (int l = 0; l < R; ++l)
+      for (int k = 0; k < R; ++k) out[l * 4 + k] = T[l][k];
+  }
+}
+
+// Row pass 1 of a tall matrix, one row per thread over blocks of kTallRows rows: P-bar
+// rows into P and the block's Gram partial sum_i P-bar_i^T P-bar_i (upper triangle, in
+// double; thread sums across the workgroup in a fixed order).
+template <int R>
+__global__ __launch_bounds__(kTallRows) void k_tall_rows(const TallBlk* __restrict__ tblks,
+                                                         const MatInfo* __restrict__ mats,
+                                                         const float* __restrict__ Ppart, float* __restrict__ P,
+                                                         double* __restrict__ gpart) {
+  constexpr int NG = R * (R + 1) / 2;
+  __shared__ double red[kTallRows / 64][NG];
+  const TallBlk tb = tblks[blockIdx.x];
+  const MatInfo mi = mats[tb.mat];
+  const int n = mi.rows;
+  const int i = tb.blk * kTallRows + int(threadIdx.x);
+  float acc[1][R];
+  pbar_rows<R, 1>(acc, Ppart + mi.ppart_off, int64_t(n) * R, mi, i, 0, n);
+  double g[NG];
+  int a = 0;
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    if (i < n) P[mi.p_off + int64_t(i) * R + k] = acc[0][k];
+#pragma unroll
+    for (int l = k; l < R; ++l) g[a++] = double(acc[0][k]) * double(acc[0][l]);
+  }
+  const int ln = int(threadIdx.x) & 63, wave = int(threadIdx.x) >> 6;
+#pragma unroll
+  for (int b = 0; b < NG; ++b) {
+    const double v = wave_sum(g[b]);
+    if (ln == 0) red[wave][b] = v;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < n; i += bs) {
-    double pb[R];
+  if (int(threadIdx.x) < NG) {
+    double s = 0.0;
+    for (int w = 0; w < kTallRows / 64; ++w) s += red[w][threadIdx.x];
+    gpart[int64_t(blockIdx.x) * 10 + threadIdx.x] = s;
+  }
+}
+
+// Row pass 2 of a tall matrix: P = P-bar T (in double, l in order), and the copy in P2.
+template <int R>
+__global__ __launch_bounds__(kTallRows) void k_tall_apply(const TallBlk* __restrict__ tblks,
+                                                          const MatInfo* __restrict__ mats,
+                                                          const double* __restrict__ tmat, float* __restrict__ P,
+                                                          float* __restrict__ P2) {
+  const TallBlk tb = tblks[blockIdx.x];
+  const MatInfo mi = mats[tb.mat];
+  const int i = tb.blk * kTallRows + int(threadIdx.x);
+  if (i >= mi.rows) return;
+  const double* T = tmat + int64_t(tb.mat) * 16;
+  float pb[R];
 #pragma unroll
-    for (int k = 0; k < R; ++k) pb[k] = dst[int64_t(i) * R + k];
+  for (int k = 0; k < R; ++k) pb[k] = P[mi.p_off + int64_t(i) * R + k];
 #pragma unroll
-    for (int k = 0; k < R; ++k) {
-      double v = 0.0;
+  for (int k = 0; k < R; ++k) {
+    double v = 0.0;
 #pragma unroll
-      for (int l = 0; l <= k; ++l) v += pb[l] * T[l][k];
-      const int64_t o = int64_t(i) * R + k;
-      dst[o] = float(v);
-      if (P2 != nullptr) P2[mi.p_off + o] = float(v);
-    }
+    for (int l = 0; l <= k; ++l) v += double(pb[l]) * T[l * 4 + k];
+    const int64_t o = mi.p_off + int64_t(i) * R + k;
+    P[o] = float(v);
+    if (P2 != nullptr) P2[o] = float(v);
   }
 }
 
@@ -803,22 +1128,34 @@ __global__ __launch_bounds__(kQThreads) void k_q_partial(const QTile* __restrict
   }
 }
 
-// grid.z walks workers when reducing the per-worker Q_w partials (strides part_ws and
-// q_ws between workers; both 0 for the Q pass over Mbar).
-__global__ __launch_bounds__(kQRedThreads) void k_q_reduce(const MatInfo* __restrict__ mats,
-                                                           const float* __restrict__ Qpart,
-                                                           float* __restrict__ Q, float* __restrict__ Q2,
-                                                           int R, int64_t part_ws, int64_t q_ws) {
+// Q = sum of the row-block partials.  Workgroup (blockIdx.x, matrix blockIdx.y) takes
+// 64 elements of Q, one per lane; its waves split the row blocks (wave w sums blocks w,
+// w + waves, ... in order) and the first wave adds the waves' sums in wave order.  grid.z
+// walks workers when reducing the per-worker Q_w partials (strides part_ws and q_ws
+// between workers; both 0 for the Q pass over Mbar).
+__global__ __launch_bounds__(64 * kQRedMaxWaves) void k_q_reduce(const MatInfo* __restrict__ mats,
+                                                                 const float* __restrict__ Qpart,
+                                                                 float* __restrict__ Q, float* __restrict__ Q2,
+                                                                 int R, int64_t part_ws, int64_t q_ws) {
+  __shared__ float red[kQRedMaxWaves][64];
   const MatInfo mi = mats[blockIdx.y];
   const int64_t n = int64_t(mi.cols) * R;
+  if (int64_t(blockIdx.x) * 64 >= n) return;  // the whole workgroup
+  const int ln = int(threadIdx.x) & 63, wave = int(threadIdx.x) >> 6, nw = int(blockDim.x) >> 6;
+  const int64_t idx = int64_t(blockIdx.x) * 64 + ln;
   const float* part = Qpart + int64_t(blockIdx.z) * part_ws + mi.qpart_off;
-  float* out = Q + int64_t(blockIdx.z) * q_ws + mi.q_off;
-  for (int64_t idx = int64_t(blockIdx.x) * kQRedThreads + threadIdx.x; idx < n;
-       idx += int64_t(gridDim.x) * kQRedThreads) {
-    float s = 0.f;
-    for (int b = 0; b < mi.nblk; ++b) s += part[int64_t(b) * n + idx];
-    out[idx] = s;
-    if (Q2 != nullptr) Q2[mi.q_off + idx] = s;
+  float s = 0.f;
+  if (idx < n) {
+#pragma unroll 8
+    for (int b = wave; b < mi.nblk; b += nw) s += part[int64_t(b) * n + idx];
+  }
+  red[wave][ln] = s;
+  __syncthreads();
+  if (wave == 0 && idx < n) {
+    float t = red[0][ln];
+    for (int w = 1; w < nw; ++w) t += red[w][ln];
+    Q[int64_t(blockIdx.z) * q_ws + mi.q_off + idx] = t;
+    if (Q2 != nullptr) Q2[mi.q_off + idx] = t;
   }
 }
 
@@ -905,6 +1242,37 @@ __device__ __forceinline__ void apply_matrix_tile(const UpdTile& t, const MatInf
   }
 }
 
+// The same for one flat chunk (chunk blockIdx.y of the tile).
+template <typename GT, int WT, bool LOCAL>
+__device__ __forceinline__ void apply_flat_tile(const UpdTile& t, const MatInfo& mi, const GT* G, float* E,
+                                                const float* P, const float* Q, const float* Qw, int64_t q_ws,
+                                                float* update, float* mom, float* x, float* ebar, int W,
+                                                int64_t ld, int R, int mode, float lr, float mu, float inv_w) {
+  const int64_t c0 = t.begin + int64_t(blockIdx.y) * kStreamTileElems;
+  if (c0 >= t.end) return;
+  const int64_t c = c0 + int64_t(threadIdx.x & 63) * 4;
+  const Flat4 f = flat4_at(mi, c);
+  if (f.valid == 0) return;
+  float p0[4], p1[4];
+  load_flat_p_rows(p0, p1, P + mi.p_off, f, R);
+  const f4 u = pq_flat(p0, p1, Q + mi.q_off, f, R);
+  f4 es;
+  if constexpr (LOCAL)
+    es = update_workers_local_flat<GT, WT>(G, E, W, ld, c, p0, p1, Qw, q_ws, mi.q_off, f, R);
+  else
+    es = f.valid == 4 ? update_workers<4, GT, WT>(G, E, W, ld, c, u)
+                      : update_workers_tail<GT>(G, E, W, ld, c, u, f.valid);
+  if (f.valid == 4) {
+    if (ebar != nullptr) st<4>(ebar + c, es * inv_w);
+    if (update != nullptr) st_nt<4>(update + c, u);
+    if (mode != kCompress) momentum_v<4>(mom, x, c, u, mode, lr, mu);
+  } else {
+    if (ebar != nullptr) store4(ebar + c, es * inv_w, f.valid);
+    if (update != nullptr) store4_nt(update + c, u, f.valid);
+    if (mode != kCompress) momentum_masked(mom, x, c, u, f.valid, mode, lr, mu);
+  }
+}
+
 template <typename GT, int WT, bool LOCAL, int NW>
 __global__ __launch_bounds__(kStreamThreads * NW) void k_apply(
     const UpdTile* __restrict__ tiles, int32_t ntiles, const MatInfo* __restrict__ mats, const GT* __restrict__ G,
@@ -926,6 +1294,10 @@ __global__ __launch_bounds__(kStreamThreads * NW) void k_apply(
     return;
   }
   const MatInfo mi = mats[t.mat];
+  if (mi.flat) {
+    apply_flat_tile<GT, WT, LOCAL>(t, mi, G, E, P, Q, Qw, q_ws, update, mom, x, ebar, W, ld, R, mode, lr, mu, inv_w);
+    return;
+  }
   switch (mi.vw) {
     case 4: apply_matrix_tile<4, GT, WT, LOCAL>(t, mi, G, E, P, Q, Qw, q_ws, update, mom, x, ebar, W, ld, R, mode, lr, mu, inv_w); break;
     case 2: apply_matrix_tile<4, GT, WT, LOCAL, 2>(t, mi, G, E, P, Q, Qw, q_ws, update, mom, x, ebar, W, ld, R, mode, lr, mu, inv_w); break;
@@ -960,10 +1332,46 @@ __device__ __forceinline__ void update_matrix_tile(const UpdTile& t, const MatIn
   }
 }
 
+// The same over a flat run: kUpdFlatRuns chunks of kUpdThreads * 4 elements.  A lane's
+// next element position is its previous one moved on by the chunk length (one integer
+// division per lane in all).
+__device__ __forceinline__ void update_flat_tile(const UpdTile& t, const MatInfo& mi, const float* P,
+                                                 const float* Q, float* update, float* mom, float* x, int R,
+                                                 int mode, float lr, float mu) {
+  constexpr int kStep = kUpdThreads * 4;
+  const int dq = kStep / mi.cols, dr = kStep - dq * mi.cols;
+  const int64_t numel = int64_t(mi.rows) * mi.cols;
+  Flat4 f = flat4_at(mi, t.begin + int64_t(threadIdx.x) * 4);
+  for (int64_t c = t.begin + int64_t(threadIdx.x) * 4; c < t.end; c += kStep) {
+    if (c != t.begin + int64_t(threadIdx.x) * 4) {
+      int j = f.j0 + dr, i = f.i0 + dq;
+      if (j >= mi.cols) {
+        j -= mi.cols;
+        ++i;
+      }
+      f.i0 = i;
+      f.j0 = j;
+      f.nw = min(4, mi.cols - j);
+      f.valid = int(min<int64_t>(4, numel - (c - mi.offset)));
+    }
+    float p0[4], p1[4];
+    load_flat_p_rows(p0, p1, P + mi.p_off, f, R);
+    const f4 u = pq_flat(p0, p1, Q + mi.q_off, f, R);
+    if (f.valid == 4) {
+      if (update != nullptr) st_nt<4>(update + c, u);
+      if (mode != kCompress) momentum_v<4>(mom, x, c, u, mode, lr, mu);
+    } else {
+      if (update != nullptr) store4_nt(update + c, u, f.valid);
+      if (mode != kCompress) momentum_masked(mom, x, c, u, f.valid, mode, lr, mu);
+    }
+  }
+}
+
+template <int R>
 __global__ __launch_bounds__(kUpdThreads) void k_update(
     const UpdTile* __restrict__ tiles, const MatInfo* __restrict__ mats, const float* __restrict__ Mbar,
     const float* __restrict__ P, const float* __restrict__ Q, float* __restrict__ update,
-    float* __restrict__ mom, float* __restrict__ x, int R, int mode, float lr, float mu) {
+    float* __restrict__ mom, float* __restrict__ x, int mode, float lr, float mu) {
   const UpdTile t = tiles[blockIdx.x];
   if (t.mat < 0) {
     const int64_t c = t.begin + int64_t(threadIdx.x) * 4;
@@ -975,6 +1383,10 @@ __global__ __launch_bounds__(kUpdThreads) void k_update(
     return;
   }
   const MatInfo mi = mats[t.mat];
+  if (mi.flat) {
+    update_flat_tile(t, mi, P, Q, update, mom, x, R, mode, lr, mu);
+    return;
+  }
   switch (mi.vw) {
     case 4: update_matrix_tile<4>(t, mi, P, Q, update, mom, x, R, mode, lr, mu); break;
     case 2: update_matrix_tile<4, 2>(t, mi, P, Q, update, mom, x, R, mode, lr, mu); break;
@@ -1007,6 +1419,30 @@ __device__ __forceinline__ void materialize_tile(const UpdTile& t, const MatInfo
   }
 }
 
+// The same for one flat chunk.
+__device__ __forceinline__ void materialize_flat_tile(const UpdTile& t, const MatInfo& mi, const float* E,
+                                                      float* out, const float* Pprev, const float* Qprev, int W,
+                                                      int64_t ld, int R, int offset_valid) {
+  const int64_t c0 = t.begin + int64_t(blockIdx.y) * kStreamTileElems;
+  if (c0 >= t.end) return;
+  const int64_t c = c0 + int64_t(threadIdx.x) * 4;
+  const Flat4 f = flat4_at(mi, c);
+  if (f.valid == 0) return;
+  f4 up = {0.f, 0.f, 0.f, 0.f};
+  if (offset_valid) {
+    float p0[4], p1[4];
+    load_flat_p_rows(p0, p1, Pprev + mi.p_off, f, R);
+    up = pq_flat(p0, p1, Qprev + mi.q_off, f, R);
+  }
+  for (int w = 0; w < W; ++w) {
+    const f4 v = ld_nt<4>(E + w * ld + c) - up;
+    if (f.valid == 4)
+      st_nt<4>(out + w * ld + c, v);
+    else
+      store4_nt(out + w * ld + c, v, f.valid);
+  }
+}
+
 __global__ __launch_bounds__(kStreamThreads) void k_materialize(
     const UpdTile* __restrict__ tiles, const MatInfo* __restrict__ mats, const float* E, float* out,
     const float* __restrict__ Pprev, const float* __restrict__ Qprev, int W, int64_t ld, int R,
@@ -1014,6 +1450,10 @@ __global__ __launch_bounds__(kStreamThreads) void k_materialize(
   const UpdTile t = tiles[blockIdx.x];
   if (t.mat < 0) return;
   const MatInfo mi = mats[t.mat];
+  if (mi.flat) {
+    materialize_flat_tile(t, mi, E, out, Pprev, Qprev, W, ld, R, offset_valid);
+    return;
+  }
   switch (mi.vw) {
     case 4: materialize_tile<4>(t, mi, E, out, Pprev, Qprev, W, ld, R, offset_valid); break;
     case 2: materialize_tile<4, 2>(t, mi, E, out, Pprev, Qprev, W, ld, R, offset_valid); break;
@@ -1049,8 +1489,9 @@ psgd_status ensure_tables(psgd_plan* plan, DeviceTables** out) {
   const uint64_t b_rt = align256(plan->s2tiles.size() * sizeof(UpdTile) + 1);
   const uint64_t b_qt = align256(plan->qtiles.size() * sizeof(QTile) + 1);
   const uint64_t b_ut = align256(plan->utiles.size() * sizeof(UpdTile) + 1);
+  const uint64_t b_tb = align256(plan->tblks.size() * sizeof(TallBlk) + 1);
   void* base = nullptr;
-  e = hipMalloc(&base, b_mats + b_rt + b_qt + b_ut);
+  e = hipMalloc(&base, b_mats + b_rt + b_qt + b_ut + b_tb);
   if (e != hipSuccess) {
     set_error(std::string("hipMalloc of the plan's device tables: ") + hipGetErrorString(e));
     return PSGD_ERR_NO_MEMORY;
@@ -1062,6 +1503,7 @@ psgd_status ensure_tables(psgd_plan* plan, DeviceTables** out) {
   t.s2tiles = reinterpret_cast<UpdTile*>(b + b_mats);
   t.qtiles = reinterpret_cast<QTile*>(b + b_mats + b_rt);
   t.utiles = reinterpret_cast<UpdTile*>(b + b_mats + b_rt + b_qt);
+  t.tblks = reinterpret_cast<TallBlk*>(b + b_mats + b_rt + b_qt + b_ut);
   struct {
     void* dst;
     const void* src;
@@ -1071,6 +1513,7 @@ psgd_status ensure_tables(psgd_plan* plan, DeviceTables** out) {
       {t.s2tiles, plan->s2tiles.data(), plan->s2tiles.size() * sizeof(UpdTile)},
       {t.qtiles, plan->qtiles.data(), plan->qtiles.size() * sizeof(QTile)},
       {t.utiles, plan->utiles.data(), plan->utiles.size() * sizeof(UpdTile)},
+      {t.tblks, plan->tblks.data(), plan->tblks.size() * sizeof(TallBlk)},
   };
   for (const auto& c : copies) {
     if (c.bytes == 0) continue;
@@ -1156,6 +1599,8 @@ struct StepArgs {
   float* Mbar;
   float* Ppart;
   float* Qpart;
+  double* gpart;         // tall matrices: per-block Gram partials and per-matrix T
+  double* tmat;
   const float* ebar_in;  // carried error mean to read (carry mode, valid carry)
   float* ebar_out;       // error mean to write (carry mode)
   float* Pprev;          // previous P, Q (deferred mode)
@@ -1222,6 +1667,8 @@ psgd_status launch_all(psgd_plan* plan, const DeviceTables& dt, const StepArgs& 
   auto pass = [&](int which) {
     return bf ? launch_pass_w<bf16>(plan, which, fp, dt, a) : launch_pass_w<float>(plan, which, fp, dt, a);
   };
+  const unsigned qred_gx = unsigned((plan->max_q_elems_per_matrix + 63) / 64);
+  const dim3 qred_block(unsigned(64 * plan->qred_waves));
 
   if ((s = pass(kPassFirst)) != PSGD_OK) return s;
   // Each round: orthonormalise P-bar, Q = Mbar^T P; rounds after the first recompute
@@ -1233,14 +1680,25 @@ psgd_status launch_all(psgd_plan* plan, const DeviceTables& dt, const StepArgs& 
                    a.Ppart, R);
       if (s != PSGD_OK) return s;
     }
+    const unsigned n_tall = unsigned(plan->tblks.size());
+    if (n_tall > 0) {
+      s = launch_k(plan, kKTallRows, k_tall_rows<R>, dim3(n_tall), dim3(kTallRows), stream, dt.tblks, dt.mats,
+                   static_cast<const float*>(a.Ppart), a.p, a.gpart);
+      if (s != PSGD_OK) return s;
+    }
     s = launch_k(plan, kKMgs, k_mgs<R>, dim3(n_mats), dim3(plan->mgs_threads), stream, dt.mats,
-                 static_cast<const float*>(a.Ppart), a.p, deferred ? a.Pprev : nullptr);
+                 static_cast<const float*>(a.Ppart), a.p, deferred ? a.Pprev : nullptr,
+                 static_cast<const double*>(a.gpart), a.tmat);
     if (s != PSGD_OK) return s;
+    if (n_tall > 0) {
+      s = launch_k(plan, kKTallApply, k_tall_apply<R>, dim3(n_tall), dim3(kTallRows), stream, dt.tblks, dt.mats,
+                   static_cast<const double*>(a.tmat), a.p, deferred ? a.Pprev : nullptr);
+      if (s != PSGD_OK) return s;
+    }
     s = launch_k(plan, kKQPartial, k_q_partial<R>, dim3(unsigned(plan->qtiles.size())), dim3(kQThreads), stream,
                  dt.qtiles, dt.mats, static_cast<const float*>(a.Mbar), static_cast<const float*>(a.p), a.Qpart);
     if (s != PSGD_OK) return s;
-    const unsigned gx = unsigned((plan->max_q_elems_per_matrix + kQRedThreads - 1) / kQRedThreads);
-    s = launch_k(plan, kKQReduce, k_q_reduce, dim3(gx, n_mats), dim3(kQRedThreads), stream, dt.mats,
+    s = launch_k(plan, kKQReduce, k_q_reduce, dim3(qred_gx, n_mats), qred_block, stream, dt.mats,
                  static_cast<const float*>(a.Qpart), a.q, deferred ? a.Qprev : nullptr, R, int64_t(0), int64_t(0));
     if (s != PSGD_OK) return s;
   }
@@ -1255,16 +1713,15 @@ psgd_status launch_all(psgd_plan* plan, const DeviceTables& dt, const StepArgs& 
                    static_cast<const float*>(a.grads), static_cast<const float*>(a.errors), a.ld,
                    static_cast<const float*>(a.p), a.Qwpart, plan->qpart_elems);
     if (s != PSGD_OK) return s;
-    const unsigned gx = unsigned((plan->max_q_elems_per_matrix + kQRedThreads - 1) / kQRedThreads);
-    s = launch_k(plan, kKQwReduce, k_q_reduce, dim3(gx, n_mats, unsigned(a.W)), dim3(kQRedThreads), stream, dt.mats,
+    s = launch_k(plan, kKQwReduce, k_q_reduce, dim3(qred_gx, n_mats, unsigned(a.W)), qred_block, stream, dt.mats,
                  static_cast<const float*>(a.Qwpart), a.Qw, static_cast<float*>(nullptr), R, plan->qpart_elems,
                  a.q_ws);
     if (s != PSGD_OK) return s;
   }
   if (deferred)
-    return launch_k(plan, kKUpdate, k_update, dim3(unsigned(plan->utiles.size())), dim3(kUpdThreads), stream,
+    return launch_k(plan, kKUpdate, k_update<R>, dim3(unsigned(plan->utiles.size())), dim3(kUpdThreads), stream,
                     dt.utiles, dt.mats, static_cast<const float*>(a.Mbar), static_cast<const float*>(a.p),
-                    static_cast<const float*>(a.q), a.update, a.mom, a.x, R, a.mode, a.lr, a.mu);
+                    static_cast<const float*>(a.q), a.update, a.mom, a.x, a.mode, a.lr, a.mu);
   return pass(kPassApply);
 }
 
@@ -1349,6 +1806,8 @@ psgd_status run_step(const char* fn, psgd_plan* plan, const void* grads, float* 
   a.Mbar = reinterpret_cast<float*>(ws + plan->ws_mbar);
   a.Ppart = reinterpret_cast<float*>(ws + plan->ws_ppart);
   a.Qpart = reinterpret_cast<float*>(ws + plan->ws_qpart);
+  a.gpart = reinterpret_cast<double*>(ws + plan->ws_gpart);
+  a.tmat = reinterpret_cast<double*>(ws + plan->ws_tmat);
   a.ebar_out = carry ? reinterpret_cast<float*>(ws + plan->ws_ebar) : nullptr;
   a.ebar_in = (carry && use_state) ? a.ebar_out : nullptr;
   a.Pprev = deferred ? reinterpret_cast<float*>(ws + plan->ws_pprev) : nullptr;

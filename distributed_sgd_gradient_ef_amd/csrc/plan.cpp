@@ -16,9 +16,9 @@ namespace psgd {
 
 static thread_local std::string g_last_error;
 
-const char* const kKernelNames[kNumKernels] = {"k_first",  "k_mgs",    "k_q_partial",  "k_q_reduce",
-                                               "k_apply",  "k_update", "k_p_mbar",     "k_qw_partial",
-                                               "k_qw_reduce"};
+const char* const kKernelNames[kNumKernels] = {"k_first",      "k_mgs",         "k_q_partial",  "k_q_reduce",
+                                               "k_apply",      "k_update",      "k_p_mbar",     "k_qw_partial",
+                                               "k_qw_reduce",  "k_tall_rows",   "k_tall_apply"};
 
 void set_error(const std::string& msg) { g_last_error = msg; }
 
@@ -109,15 +109,16 @@ extern "C" psgd_status psgd_plan_create(const psgd_layer* layers, int32_t n_laye
         mi.q_off = q_off;
         mi.rows = int32_t(rows);
         mi.cols = int32_t(cols);
-        int64_t nblk = (rows + kQTargetRowsPerBlock - 1) / kQTargetRowsPerBlock;
-        nblk = std::min<int64_t>(nblk, kQMaxRowBlocks);
-        mi.rows_per_blk = int32_t((rows + nblk - 1) / nblk);
-        mi.nblk = int32_t((rows + mi.rows_per_blk - 1) / mi.rows_per_blk);
         mi.vw = (cols % 4 == 0) ? 4 : (cols % 2 == 0) ? 2 : 1;
-        mi.qpart_off = qpart;
-        qpart += int64_t(mi.nblk) * cols * r;
-        const int64_t strip_cols = int64_t(kStreamThreads) * (mi.vw == 1 ? 1 : 4);
-        mi.nstrips = int32_t((cols + strip_cols - 1) / strip_cols);
+        mi.flat = (cols >= kFlatMinCols && cols % 32 != 0) ? 1 : 0;
+        if (mi.flat) {
+          // a row of cols elements starting at offset o < kStreamTileElems within a chunk
+          // overlaps ceil((o + cols) / kStreamTileElems) chunks
+          mi.nstrips = int32_t((cols + 2 * kStreamTileElems - 2) / kStreamTileElems);
+        } else {
+          const int64_t strip_cols = int64_t(kStreamThreads) * (mi.vw == 1 ? 1 : 4);
+          mi.nstrips = int32_t((cols + strip_cols - 1) / strip_cols);
+        }
         mi.ppart_off = plan->ppart_elems;
         plan->ppart_elems += int64_t(mi.nstrips) * rows * r;
         plan->mats.push_back(mi);
@@ -141,13 +142,54 @@ extern "C" psgd_status psgd_plan_create(const psgd_layer* layers, int32_t n_laye
     plan->worker_stride = off;
     plan->p_elems = p_off;
     plan->q_elems = q_off;
+
+    // Q-pass row blocks: at most kQMaxRowBlocks, unless the matrix's share of the plan's
+    // elements asks for more of the launch's kQTargetTiles tiles (a single tall, narrow
+    // matrix would otherwise stream through a few workgroups).
+    for (MatInfo& mi : plan->mats) {
+      const int64_t rows = mi.rows, cols = mi.cols;
+      const int64_t most = (rows + kQTargetRowsPerBlock - 1) / kQTargetRowsPerBlock;
+      const int64_t strip = int64_t(kQThreads) * (mi.vw == 1 ? 1 : 4);
+      const int64_t strips = (cols + strip - 1) / strip;
+      const int64_t share = (kQTargetTiles * rows * cols + plan->matrix_numel * strips - 1) /
+                            (plan->matrix_numel * strips);
+      const int64_t nblk = std::min(most, std::max<int64_t>(std::min<int64_t>(most, kQMaxRowBlocks), share));
+      mi.rows_per_blk = int32_t((rows + nblk - 1) / nblk);
+      mi.nblk = int32_t((rows + mi.rows_per_blk - 1) / mi.rows_per_blk);
+      mi.qpart_off = qpart;
+      qpart += int64_t(mi.nblk) * cols * r;
+      // about eight partials per wave
+      plan->qred_waves = std::max(plan->qred_waves, std::min((mi.nblk + 7) / 8, kQRedMaxWaves));
+    }
     plan->qpart_elems = qpart;
+
+    // Tall matrices: blocks of kTallRows rows for the two row passes of their Gram route.
+    for (size_t m = 0; m < plan->mats.size(); ++m) {
+      MatInfo& mi = plan->mats[m];
+      mi.tall_blk0 = -1;
+      mi.tall_nblk = 0;
+      if (mi.rows <= kMgsThreads * kMgsRowsPerThread) continue;
+      mi.tall_blk0 = int32_t(plan->tblks.size());
+      mi.tall_nblk = (mi.rows + kTallRows - 1) / kTallRows;
+      for (int32_t b = 0; b < mi.tall_nblk; ++b) plan->tblks.push_back(TallBlk{int32_t(m), b});
+    }
 
     // Work-lists: row x column-strip tiles over the compressed matrices, flat ranges
     // over the 1-D tensors.
-    auto build_tiles = [&](std::vector<UpdTile>& out, int32_t rows_per_tile, int32_t threads) {
+    auto build_tiles = [&](std::vector<UpdTile>& out, int32_t rows_per_tile, int32_t flat_runs, int32_t threads) {
       for (const psgd_layer_info& li : plan->layers) {
-        if (li.compressed) {
+        if (li.compressed && plan->mats[size_t(li.matrix_index)].flat) {
+          // flat_runs runs of threads * 4 elements per entry
+          const int64_t end = li.offset + li.rows * li.cols;
+          const int64_t span = int64_t(flat_runs) * threads * 4;
+          for (int64_t b = li.offset; b < end; b += span) {
+            UpdTile u{};
+            u.begin = b;
+            u.end = std::min<int64_t>(end, b + span);
+            u.mat = li.matrix_index;
+            out.push_back(u);
+          }
+        } else if (li.compressed) {
           const MatInfo& m = plan->mats[size_t(li.matrix_index)];
           const int32_t strip = threads * (m.vw == 1 ? 1 : 4);
           for (int32_t r0 = 0; r0 < m.rows; r0 += rows_per_tile)
@@ -172,10 +214,12 @@ extern "C" psgd_status psgd_plan_create(const psgd_layer* layers, int32_t n_laye
       }
     };
     int64_t row_strips = 0;
-    for (const MatInfo& m : plan->mats) row_strips += int64_t(m.rows) * m.nstrips;
+    for (const MatInfo& m : plan->mats)
+      row_strips += m.flat ? (int64_t(m.rows) * m.cols + kStreamTileElems - 1) / kStreamTileElems
+                           : int64_t(m.rows) * m.nstrips;
     plan->worker_rows_per_tile = int32_t(std::max<int64_t>(1, (row_strips + kMaxWorkerTiles - 1) / kMaxWorkerTiles));
-    build_tiles(plan->s2tiles, plan->worker_rows_per_tile, kStreamThreads);
-    build_tiles(plan->utiles, kUpdRowsPerTile, kUpdThreads);
+    build_tiles(plan->s2tiles, plan->worker_rows_per_tile, plan->worker_rows_per_tile, kStreamThreads);
+    build_tiles(plan->utiles, kUpdRowsPerTile, kUpdFlatRuns, kUpdThreads);
     for (size_t mi = 0; mi < plan->mats.size(); ++mi) {
       const MatInfo& m = plan->mats[mi];
       const int32_t strip = kQThreads * (m.vw == 1 ? 1 : 4);
@@ -203,6 +247,10 @@ extern "C" psgd_status psgd_plan_create(const psgd_layer* layers, int32_t n_laye
       ws += uint64_t(round_up(std::max<int64_t>(plan->qpart_elems, 1) * 4 * n_workers, 256));
     plan->ws_qw = ws;
     if (flags & PSGD_FLAG_LOCAL_Q_ERROR) ws += uint64_t(round_up(std::max<int64_t>(plan->q_elems, 1) * 4 * n_workers, 256));
+    plan->ws_gpart = ws;
+    ws += uint64_t(round_up(int64_t(plan->tblks.size()) * 10 * 8, 256));
+    plan->ws_tmat = ws;
+    if (!plan->tblks.empty()) ws += uint64_t(round_up(int64_t(plan->mats.size()) * 16 * 8, 256));
     plan->workspace_bytes = ws;
     int32_t max_rows = 1;
     for (const MatInfo& m : plan->mats) max_rows = std::max(max_rows, m.rows);

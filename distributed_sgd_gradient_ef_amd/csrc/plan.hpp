@@ -15,30 +15,47 @@ namespace psgd {
 constexpr int64_t kAlignElems = 64;  // every tensor starts on a 256-byte boundary
 
 // Worker passes (the first pass and the eager error/update pass): one workgroup is one
-// wave of kStreamThreads lanes.  Over a compressed matrix it handles one row x a strip
-// of kStreamThreads*4 columns (kStreamThreads columns when cols % 4 != 0); over a 1-D
-// tensor, kStreamTileElems consecutive elements, one float4 chunk per lane.  A tile
-// table entry covers as many rows as keep the table under kMaxWorkerTiles entries, and
-// the launch's second grid dimension walks those rows, one workgroup each.
+// wave of kStreamThreads lanes.  Over a compressed matrix whose rows start on 128-byte
+// lines it handles one row x a strip of kStreamThreads*4 columns (kStreamThreads
+// columns when cols % 4 != 0).  Over a 1-D tensor, and over a "flat" matrix (at least
+// kFlatMinCols columns, not a multiple of 32, so its rows start anywhere in a line), it
+// handles kStreamTileElems consecutive elements, one float4 chunk per lane.  A tile
+// table entry covers as many rows (flat chunks) as keep the table under
+// kMaxWorkerTiles entries, and the launch's second grid dimension walks them, one
+// workgroup each.
 constexpr int kStreamThreads = 64;
 constexpr int kStreamTileElems = kStreamThreads * 4;
 constexpr int64_t kMaxWorkerTiles = 65536;
+constexpr int kFlatMinCols = 32;
 
 // Update-only pass (deferred mode): workgroups of kUpdThreads over kUpdRowsPerTile rows
-// x a strip of kUpdThreads*4 columns, or kUpdThreads*4 elements of a 1-D tensor.
+// x a strip of kUpdThreads*4 columns, or kUpdFlatRuns runs of kUpdThreads*4 elements
+// of a flat matrix, or kUpdThreads*4 elements of a 1-D tensor.
 constexpr int kUpdThreads = 256;
 constexpr int kUpdRowsPerTile = 8;
+constexpr int kUpdFlatRuns = 8;
 
-// Q partials = Mbar^T P over a block of rows and a strip of columns.
+// Q partials = Mbar^T P over a block of rows and a strip of columns.  A matrix gets
+// ceil(rows / kQTargetRowsPerBlock) row blocks, at most kQMaxRowBlocks, or more (up to
+// that ceiling) when its share of the plan's elements calls for more than
+// kQMaxRowBlocks of the kQTargetTiles tiles of the launch.
 constexpr int kQThreads = 256;
 constexpr int kQTargetRowsPerBlock = 64;
 constexpr int kQMaxRowBlocks = 32;
+constexpr int64_t kQTargetTiles = 2048;
 
-// Gram-Schmidt: one workgroup per matrix.
+// Gram-Schmidt: one workgroup per matrix.  A matrix taller than kMgsThreads *
+// kMgsRowsPerThread rows is orthonormalised through its Gram matrix instead: P-bar rows
+// and per-block Gram partials over blocks of kTallRows rows (one per thread), the
+// coefficients in that matrix's Gram-Schmidt workgroup, and P = P-bar T over the same
+// blocks.
 constexpr int kMgsThreads = 1024;
+constexpr int kMgsRowsPerThread = 4;
+constexpr int kTallRows = 256;
 
-// Reduction of the Q partials: one thread per element of Q.
-constexpr int kQRedThreads = 256;
+// Reduction of the Q partials: a workgroup takes 64 elements of Q (one per lane) and up
+// to kQRedMaxWaves waves, which split the row blocks between them.
+constexpr int kQRedMaxWaves = 16;
 
 struct MatInfo {
   int64_t offset;     // element offset of the matrix in a worker slice / Mbar / update
@@ -51,7 +68,15 @@ struct MatInfo {
   int32_t nblk;          // number of Q partials (row blocks)
   int32_t vw;            // row alignment in floats: 4 if cols % 4 == 0, 2 if even, else 1 (4 and 2
                          // run four columns per lane, 2 as two 8-byte halves; 1 one column)
-  int32_t nstrips;       // column strips of the worker passes (P-bar partials per row)
+  int32_t nstrips;       // P-bar partial slots per row: the column strips of the worker passes, or
+                         // for a flat matrix the most flat chunks one row can overlap
+  int32_t flat;          // 1: the worker passes stream the matrix in flat chunks
+  int32_t tall_blk0;     // first entry of the matrix in the tall-block list, -1 if not tall
+  int32_t tall_nblk;     // its number of tall blocks
+};
+
+struct TallBlk {
+  int32_t mat, blk;
 };
 
 struct QTile {
@@ -59,8 +84,9 @@ struct QTile {
 };
 
 // Tiles of the worker and update passes: for a compressed matrix, rows
-// [row_begin, row_end) x a column strip starting at col_begin; for an uncompressed
-// tensor (mat < 0), the flat element range [begin, end) (begin a multiple of 4).
+// [row_begin, row_end) x a column strip starting at col_begin; for a flat matrix and
+// for an uncompressed tensor (mat < 0), the element range [begin, end) (begin a
+// multiple of 4).
 struct UpdTile {
   int64_t begin, end;
   int32_t mat, row_begin, row_end, col_begin;
@@ -72,11 +98,15 @@ struct DeviceTables {
   UpdTile* s2tiles = nullptr;
   QTile* qtiles = nullptr;
   UpdTile* utiles = nullptr;
+  TallBlk* tblks = nullptr;
 };
 
 void set_error(const std::string& msg);
 
-enum KernelId { kKFirst = 0, kKMgs, kKQPartial, kKQReduce, kKApply, kKUpdate, kKPMbar, kKQwPartial, kKQwReduce, kNumKernels };
+enum KernelId {
+  kKFirst = 0, kKMgs, kKQPartial, kKQReduce, kKApply, kKUpdate, kKPMbar, kKQwPartial, kKQwReduce,
+  kKTallRows, kKTallApply, kNumKernels
+};
 extern const char* const kKernelNames[kNumKernels];
 
 struct PendingTiming {
@@ -101,12 +131,15 @@ struct psgd_plan {
   std::vector<psgd::UpdTile> s2tiles;
   std::vector<psgd::QTile> qtiles;
   std::vector<psgd::UpdTile> utiles;
+  std::vector<psgd::TallBlk> tblks;
   int64_t worker_stride = 0, numel = 0, matrix_numel = 0, vector_numel = 0;
   int64_t p_elems = 0, q_elems = 0, qpart_elems = 0, ppart_elems = 0;
   int64_t max_q_elems_per_matrix = 0;
   uint64_t ws_mbar = 0, ws_ppart = 0, ws_qpart = 0, ws_ebar = 0, ws_pprev = 0, ws_qprev = 0, workspace_bytes = 0;
   uint64_t ws_qwpart = 0, ws_qw = 0;  // per-worker Q partials and Q_w (PSGD_FLAG_LOCAL_Q_ERROR)
+  uint64_t ws_gpart = 0, ws_tmat = 0;  // tall matrices: per-block Gram partials, per-matrix T (doubles)
   int32_t mgs_threads = 64;  // Gram-Schmidt block size: enough for the tallest matrix, <= kMgsThreads
+  int32_t qred_waves = 1;    // waves per workgroup of the Q-partial reduction (about 8 row blocks each, <= 16)
   int32_t worker_rows_per_tile = 1;
   int32_t power_iterations = 1;  // power-iteration rounds per step (psgd_plan_set_power_iterations)
   uint64_t message_bytes = 0, model_bytes = 0, model_bytes_momentum = 0;

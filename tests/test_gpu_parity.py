@@ -698,6 +698,78 @@ def test_local_q_error_matches_oracle(torch_gpu, W, r, bf16):
         compare_step(run, snap, O, TOL, what=f"local-Q step {step}", local_q=True)
 
 
+# ----------------------------------------------------------------------- flat rows
+# Matrices with at least 32 columns that are not a multiple of 32 start their rows
+# anywhere in a 128-byte line; the worker passes stream them as flat runs whose lanes
+# can straddle two rows.  33x35, 7x1001 and 50x257 end inside a float4; 5000x35 takes
+# the two-pass orthonormalisation; 64x64 and 64x27 keep the row-strip tiles.
+FLAT_SHAPES = [(33, 35), (1, 40), (7, 1001), (64, 64), (50, 257), (5000, 35), (130, 650), (64, 27)]
+
+
+@pytest.mark.parametrize("mode", ["plain", "carry", "deferred", "local", "iter2", "bf16", "momentum"])
+def test_flat_rows_every_mode(torch_gpu, mode):
+    from distributed_sgd_gradient_ef_amd import psgd
+
+    W, r = (4, 2) if mode == "bf16" else (3, 3)
+    flags = {"carry": psgd.PSGD_FLAG_CARRY_ERROR_MEAN, "deferred": psgd.PSGD_FLAG_DEFERRED_ERROR,
+             "local": psgd.PSGD_FLAG_LOCAL_Q_ERROR, "bf16": psgd.PSGD_FLAG_DEFERRED_ERROR,
+             "momentum": psgd.PSGD_FLAG_DEFERRED_ERROR}.get(mode, 0)
+    log(f"[case] flat rows mode={mode} W={W} r={r}")
+    rng = np.random.default_rng(90 + len(mode))
+    run = DeviceRun(FLAT_SHAPES, r, W, bf16=(mode == "bf16"), flags=flags, momentum=(mode == "momentum"))
+    iters = 2 if mode == "iter2" else 1
+    if iters > 1:
+        psgd.psgd_plan_set_power_iterations(run.plan, iters)
+    run.set_q_host({i: rng.standard_normal((s[1], r)).astype(np.float32)
+                    for i, s in enumerate(FLAT_SHAPES) if WL.is_matrix(s, r)})
+    if mode != "carry":  # carry mode must start from the errors it has seen (zero)
+        run.set_errors_host([0.3 * rng.standard_normal((W,) + s).astype(np.float32) for s in FLAT_SHAPES])
+        psgd.psgd_plan_reset_carry(run.plan)
+    for t in range(3):
+        g = [rng.standard_normal((W,) + s).astype(np.float32) for s in FLAT_SHAPES]
+        if mode == "bf16":
+            g = [WL.to_bf16_values(a) for a in g]
+        run.set_grads_host(g)
+        before = run.plain_errors()
+        snap = snapshot(run, range(len(FLAT_SHAPES)), errors_source=before)
+        if mode == "momentum":
+            run.momentum_step(0.1, 0.9)
+        else:
+            run.compress()
+        compare_step(run, snap, O, TOL, what=f"flat {mode} step {t}", errors_source=run.plain_errors(),
+                     iterations=iters, local_q=(mode == "local"))
+
+
+def test_flat_rows_deterministic_and_update_matches_subtraction(torch_gpu):
+    """Two plans stepped from the same state give bit-identical outputs; in deferred mode
+    the U written by the update pass is exactly what the next first pass subtracts (the
+    materialised errors equal M_w - U bit for bit)."""
+    from distributed_sgd_gradient_ef_amd import psgd
+
+    log("[case] flat rows determinism")
+    W, r = 4, 2
+    rng = np.random.default_rng(77)
+    g = [rng.standard_normal((W,) + s).astype(np.float32) for s in FLAT_SHAPES]
+    qs = {i: rng.standard_normal((s[1], r)).astype(np.float32) for i, s in enumerate(FLAT_SHAPES) if WL.is_matrix(s, r)}
+    outs = []
+    for _ in range(2):
+        run = DeviceRun(FLAT_SHAPES, r, W, flags=psgd.PSGD_FLAG_DEFERRED_ERROR)
+        run.set_q_host(qs)
+        run.set_grads_host(g)
+        run.compress()
+        m = run.host(run.errors).copy()        # M_w (deferred: the buffer holds M_w)
+        u = run.host(run.update).copy()
+        plain = run.host(run.plain_errors())
+        outs.append([m, u, plain, run.host(run.p).copy(), run.host(run.q).copy()])
+        for li, L in enumerate(run.plan.layers):
+            if L.compressed:
+                n = L.rows * L.cols
+                seg = slice(L.offset, L.offset + n)
+                assert np.array_equal(plain[:, seg], (m[:, seg] - u[None, seg]).astype(np.float32)), li
+    for a, b in zip(*outs):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
 def test_local_q_error_mean_equals_aggregated(torch_gpu):
     """The two error readings differ per worker but share the workers' mean error and
     produce the same P, Q-bar and U (up to float rounding)."""
