@@ -62,6 +62,7 @@ namespace rtk {
 constexpr int kTile = 4096;               // elements per tile
 constexpr int kLocalBits = 12;            // log2(kTile): offset of an entry inside its tile
 constexpr int kTileThreads = 256;         // rk_ef_hist / rk_mark: 16 elements per thread
+constexpr int kEfTiles = 4;               // rk_ef_hist: consecutive tiles per workgroup
 constexpr int kWordThreads = kTile / 32;  // rk_update: one thread per mask word
 constexpr int kSelThreads = 256;          // rk_select / rk_level3 / rk_final
 constexpr int kSegThreads = 1024;         // per-segment scans
@@ -367,6 +368,24 @@ __global__ __launch_bounds__(256) void rk_zero(uint32_t* __restrict__ p, int64_t
   for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) p[i] = 0u;
 }
 
+// Loads of one tile's G and E chunks (16 elements per thread).  A chunk past the tile's
+// end reads the tile's first chunk instead (always in bounds) and is then ignored.
+template <typename GT>
+__device__ __forceinline__ void load_tile(const RkTile& t, const GT* G, const float* E, int64_t base, v4f (&gv)[4],
+                                          v4f (&ev)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = (i * kTileThreads + int(threadIdx.x)) * 4;
+    const int ec = e < t.len ? e : 0;
+    gv[i] = load_g4(G + base + ec);
+    ev[i] = load_nt4(E + base + ec);
+  }
+}
+
+// kEfTiles consecutive tiles of the tile table per workgroup (grid.y = worker).  The
+// next tile's loads are issued before the current tile is processed.  The LDS
+// histograms are flushed to the segment's global ones (and cleared) whenever the next
+// tile belongs to another tensor, and after the last tile.
 template <typename GT>
 __global__ __launch_bounds__(kTileThreads) void rk_ef_hist(const RkTile* __restrict__ tiles, const GT* __restrict__ G,
                                                            float* __restrict__ E, const uint32_t* __restrict__ pred,
@@ -377,59 +396,72 @@ __global__ __launch_bounds__(kTileThreads) void rk_ef_hist(const RkTile* __restr
                                                            int ntiles) {
   __shared__ uint32_t h1[kBins1];
   __shared__ uint32_t h2[kBins2];
+  const int w = blockIdx.y;
+  const int t_first = int(blockIdx.x) * kEfTiles;
+  const int t_end = min(ntiles, t_first + kEfTiles);
+  RkTile t = tiles[t_first];
+  v4f gv[4], ev[4];
+  load_tile(t, G, E, int64_t(w) * stride + t.begin, gv, ev);
   for (int b = threadIdx.x; b < kBins1; b += kTileThreads) {
     h1[b] = 0u;
     h2[b] = 0u;
   }
-  const RkTile t = tiles[blockIdx.x];
-  const int w = blockIdx.y;
-  const int64_t s = int64_t(w) * n_layers + t.layer;
-  const uint32_t bp = pred[s];
-  const int64_t base = int64_t(w) * stride + t.begin;
-  // All eight loads are issued before any use: a chunk past the tile's end reads the
-  // tile's first chunk instead (always in bounds) and is then ignored.
-  v4f gv[4], ev[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = (i * kTileThreads + int(threadIdx.x)) * 4;
-    const int ec = e < t.len ? e : 0;
-    gv[i] = load_g4(G + base + ec);
-    ev[i] = load_nt4(E + base + ec);
-  }
   __syncthreads();
-  float m[4][4];
+  for (int ti = t_first; ti < t_end; ++ti) {
+    const bool more = ti + 1 < t_end;
+    const RkTile tn = more ? tiles[ti + 1] : t;
+    v4f gn[4], en[4];
+    if (more) load_tile(tn, G, E, int64_t(w) * stride + tn.begin, gn, en);
+    const int64_t s = int64_t(w) * n_layers + t.layer;
+    const uint32_t bp = pred[s];
+    const int64_t base = int64_t(w) * stride + t.begin;
+    float m[4][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = (i * kTileThreads + int(threadIdx.x)) * 4;
-    const int valid = max(0, min(4, t.len - e));
-    v4f mv = gv[i] + ev[i];
-    float* ep = E + base + e;
-    if (valid == 4) {
-      store_nt4(ep, mv);
-    } else {
-      for (int j = 0; j < valid; ++j) ep[j] = mv[j];
-      if (valid == 0) mv = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 4; ++i) {
+      const int e = (i * kTileThreads + int(threadIdx.x)) * 4;
+      const int valid = max(0, min(4, t.len - e));
+      v4f mv = gv[i] + ev[i];
+      float* ep = E + base + e;
+      if (valid == 4) {
+        store_nt4(ep, mv);
+      } else {
+        for (int j = 0; j < valid; ++j) ep[j] = mv[j];
+        if (valid == 0) mv = v4f{0.f, 0.f, 0.f, 0.f};
+      }
+      m[i][0] = mv.x;
+      m[i][1] = mv.y;
+      m[i][2] = mv.z;
+      m[i][3] = mv.w;
     }
-    m[i][0] = mv.x;
-    m[i][1] = mv.y;
-    m[i][2] = mv.z;
-    m[i][3] = mv.w;
-  }
-  mark_tile(m, t, bp, base, int64_t(w) * ntiles + blockIdx.x, h2, mask, tmask, tcnt4, cand, ccnt4);
+    mark_tile(m, t, bp, base, int64_t(w) * ntiles + ti, h2, mask, tmask, tcnt4, cand, ccnt4);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = (i * kTileThreads + int(threadIdx.x)) * 4;
+    for (int i = 0; i < 4; ++i) {
+      const int e = (i * kTileThreads + int(threadIdx.x)) * 4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (e + j < t.len) atomicAdd(&h1[mag_key(m[i][j]) >> 20], 1u);
-  }
-  __syncthreads();
-  uint32_t* g1 = hist1 + s * kBins1;
-  uint32_t* g2 = hist2 + s * kBins2;
-  for (int b = threadIdx.x; b < kBins1; b += kTileThreads) {
-    const uint32_t c1 = h1[b], c2 = h2[b];
-    if (c1) atomicAdd(g1 + b, c1);
-    if (c2) atomicAdd(g2 + b, c2);
+      for (int j = 0; j < 4; ++j)
+        if (e + j < t.len) atomicAdd(&h1[mag_key(m[i][j]) >> 20], 1u);
+    }
+    if (!more || tn.layer != t.layer) {
+      __syncthreads();
+      uint32_t* g1 = hist1 + s * kBins1;
+      uint32_t* g2 = hist2 + s * kBins2;
+      for (int b = threadIdx.x; b < kBins1; b += kTileThreads) {
+        const uint32_t c1 = h1[b], c2 = h2[b];
+        if (c1) atomicAdd(g1 + b, c1);
+        if (c2) atomicAdd(g2 + b, c2);
+        h1[b] = 0u;
+        h2[b] = 0u;
+      }
+      __syncthreads();
+    }
+    if (more) {
+      t = tn;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        gv[i] = gn[i];
+        ev[i] = en[i];
+      }
+    }
   }
 }
 
@@ -810,13 +842,46 @@ __global__ __launch_bounds__(kWaveBlock) void rk_emit(const RkTile* __restrict__
   float* vx = value + int64_t(w) * keep_total + L.keep_off;
   float* M = E + int64_t(w) * stride + L.offset;
   const int32_t e0 = t.chunk * kTile + q * 32;
-  uint32_t pos = first;
   uint32_t sent[2] = {0u, 0u};
   const uint32_t kw[2] = {k0, k1};
+  const uint32_t wpos[2] = {first, first + uint32_t(__popc(k0))};  // list position of each word's first bit
+  if (q + 1 < nwords) kpos[wi + 1] = wpos[1];
+  // The first two set bits of each word (nearly every word has at most two): their
+  // values are loaded together, then listed.  Distinct bits are distinct entries, so
+  // the loads may all precede the stores.
+  bool cok[4];
+  int32_t cidx[4];
+  float cval[4];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    if (h == 1 && q + 1 < nwords) kpos[wi + 1] = pos;
-    for (uint32_t bits = kw[h]; bits != 0u; bits &= bits - 1u, ++pos) {
+    uint32_t b = kw[h];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int c = 2 * h + r;
+      cok[c] = b != 0u && int64_t(wpos[h] + r) < L.keep;
+      cidx[c] = e0 + 32 * h + (b != 0u ? __builtin_ctz(b) : 0);
+      b &= b - 1u;
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) cval[c] = cok[c] ? M[cidx[c]] : 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    if (cok[c]) {
+      const uint32_t pos = wpos[c >> 1] + (c & 1);
+      ix[pos] = cidx[c];
+      vx[pos] = cval[c];
+      M[cidx[c]] = 0.f;
+      sent[c >> 1] |= 1u << (cidx[c] - e0 - 32 * (c >> 1));
+    }
+  // any further set bits, one at a time
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t pos = wpos[h] + 2;
+    uint32_t bits = kw[h];
+    bits &= bits - 1u;
+    bits &= bits - 1u;
+    for (; bits != 0u; bits &= bits - 1u, ++pos) {
       if (int64_t(pos) < L.keep) {
         const int32_t idx = e0 + 32 * h + __builtin_ctz(bits);
         ix[pos] = idx;
@@ -859,11 +924,33 @@ __global__ __launch_bounds__(kWordThreads) void rk_update(const RkTile* __restri
       for (int k = 0; k < 8; ++k) kw[k] = w0 + k < W ? kmask[int64_t(w0 + k) * wstride + wi] : 0u;
 #pragma unroll
       for (int k = 0; k < 8; ++k) kp[k] = kw[k] != 0u ? kpos[int64_t(w0 + k) * wstride + wi] : 0u;
+      // the values of the first two sent entries of each word are loaded together (nearly
+      // every word has at most two); they are added in worker order as before
+      float v[8][2];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const float* vx = value + int64_t(w0 + k) * keep_total + L.keep_off;
+        uint32_t b = kw[k];
+        v[k][0] = b != 0u ? vx[kp[k]] : 0.f;
+        b &= b - 1u;
+        v[k][1] = b != 0u ? vx[kp[k] + 1] : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float* vx = value + int64_t(w0 + k) * keep_total + L.keep_off;
+        uint32_t bits = kw[k];
         uint32_t pos = kp[k];
-        for (uint32_t bits = kw[k]; bits != 0u; bits &= bits - 1u) acc[q][__builtin_ctz(bits)] += vx[pos++];
+        if (bits != 0u) {
+          acc[q][__builtin_ctz(bits)] += v[k][0];
+          bits &= bits - 1u;
+          ++pos;
+        }
+        if (bits != 0u) {
+          acc[q][__builtin_ctz(bits)] += v[k][1];
+          bits &= bits - 1u;
+          ++pos;
+        }
+        for (; bits != 0u; bits &= bits - 1u) acc[q][__builtin_ctz(bits)] += vx[pos++];
       }
     }
   }
@@ -1241,6 +1328,7 @@ extern "C" psgd_status psgd_rtopk_step(psgd_rtopk_plan* plan, const void* grads,
   const int ntiles = int(plan->tiles.size());
   const int64_t sstride = int64_t(stride);
   const dim3 tgrid(static_cast<unsigned>(ntiles), static_cast<unsigned>(W));
+  const dim3 egrid(static_cast<unsigned>((ntiles + kEfTiles - 1) / kEfTiles), static_cast<unsigned>(W));
   const dim3 sgrid(static_cast<unsigned>(nl), static_cast<unsigned>(W));
   const dim3 cgrid(static_cast<unsigned>(plan->chunks.size()), static_cast<unsigned>(W));
   const int64_t nzero = int64_t(plan->n_seg) * (kBins1 + kBins2 + kBins3);
@@ -1252,11 +1340,11 @@ extern "C" psgd_status psgd_rtopk_step(psgd_rtopk_plan* plan, const void* grads,
   if ((s = launch(plan, kZero, rk_zero, dim3(zblocks), dim3(256), st, hist1, nzero)) != PSGD_OK) return s;
   const uint32_t* cpred = pred;
   if (plan->dtype == PSGD_BF16)
-    s = launch(plan, kEfHist, rk_ef_hist<uint16_t>, tgrid, dim3(kTileThreads), st, T,
+    s = launch(plan, kEfHist, rk_ef_hist<uint16_t>, egrid, dim3(kTileThreads), st, T,
                static_cast<const uint16_t*>(grads), errors, cpred, hist1, hist2, mask, tmask, tcnt4, cand, ccnt4,
                sstride, nl, ntiles);
   else
-    s = launch(plan, kEfHist, rk_ef_hist<float>, tgrid, dim3(kTileThreads), st, T, static_cast<const float*>(grads),
+    s = launch(plan, kEfHist, rk_ef_hist<float>, egrid, dim3(kTileThreads), st, T, static_cast<const float*>(grads),
                errors, cpred, hist1, hist2, mask, tmask, tcnt4, cand, ccnt4, sstride, nl, ntiles);
   if (s != PSGD_OK) return s;
   if ((s = launch(plan, kSelect, rk_select, sgrid, dim3(kSelThreads), st, L, static_cast<const uint32_t*>(hist1),
