@@ -651,7 +651,8 @@ __global__ __launch_bounds__(kSelThreads) void rk_rule(const uint32_t* __restric
 
 // Apply the segment's rule to the candidates of a chunk of tiles: top-mask bits and a
 // per-tile count for those in, tie-mask bits and a per-tile tie count for the partial
-// ties.
+// ties.  The bits are gathered in LDS bitmaps of the chunk's tiles and then ORed into
+// the masks word by word (no other workgroup touches these tiles' words).
 __global__ __launch_bounds__(kSelThreads) void rk_final(const RkChunk* __restrict__ chunks,
                                                         const RkTile* __restrict__ tiles,
                                                         const RkLayer* __restrict__ layers,
@@ -661,7 +662,9 @@ __global__ __launch_bounds__(kSelThreads) void rk_final(const RkChunk* __restric
                                                         uint32_t* __restrict__ tmask, uint32_t* __restrict__ tfin,
                                                         uint32_t* __restrict__ ttie, int64_t stride, int n_layers,
                                                         int ntiles) {
+  constexpr int kTileWords = kTile / 32;
   __shared__ uint32_t c_in[kChunkTiles], c_tie[kChunkTiles];
+  __shared__ uint32_t lm[kChunkTiles * kTileWords], lt[kChunkTiles * kTileWords];
   __shared__ ChunkRanges cr;
   const RkChunk ch = chunks[blockIdx.x];
   const int w = blockIdx.y;
@@ -672,23 +675,36 @@ __global__ __launch_bounds__(kSelThreads) void rk_final(const RkChunk* __restric
     c_in[threadIdx.x] = 0u;
     c_tie[threadIdx.x] = 0u;
   }
+  for (int i = threadIdx.x; i < kChunkTiles * kTileWords; i += kSelThreads) {
+    lm[i] = 0u;
+    lt[i] = 0u;
+  }
   const RkLayer L = layers[ch.layer];
   const int nr = (ch.t1 - ch.t0) * 4;
-  const uint32_t total = chunk_ranges(ch, L, tiles, ccnt4, w, stride, ntiles, cr);
+  const uint32_t total = chunk_ranges(ch, L, tiles, ccnt4, w, stride, ntiles, cr);  // (a barrier)
   for (uint32_t i = threadIdx.x; i < total; i += kSelThreads) {
     const int r = range_of(cr, nr, i);
     const uint32_t e = cand[cr.rbeg[r] + (i - cr.pre[r])];
     const uint32_t key = hi | (e >> kLocalBits);
-    const int64_t el = cr.tbeg[r] + (e & uint32_t(kTile - 1));
+    const uint32_t off = e & uint32_t(kTile - 1);
+    const int word = (r >> 2) * kTileWords + int(off >> 5);
     if (key >= lo) {
-      atomicOr(mask + (el >> 5), 1u << (el & 31));
+      atomicOr(&lm[word], 1u << (off & 31));
       atomicAdd(&c_in[r >> 2], 1u);
     } else if (partial && key == tie) {
-      atomicOr(tmask + (el >> 5), 1u << (el & 31));
+      atomicOr(&lt[word], 1u << (off & 31));
       atomicAdd(&c_tie[r >> 2], 1u);
     }
   }
   __syncthreads();
+  // tile begins are multiples of 64 elements, so a tile's mask words are its own
+  for (int i = threadIdx.x; i < (ch.t1 - ch.t0) * kTileWords; i += kSelThreads) {
+    const uint32_t a = lm[i], b = lt[i];
+    if ((a | b) == 0u) continue;
+    const int64_t gw = (cr.tbeg[(i / kTileWords) * 4] >> 5) + (i % kTileWords);
+    if (a) mask[gw] |= a;
+    if (b) tmask[gw] |= b;
+  }
   if (int(threadIdx.x) < ch.t1 - ch.t0) {
     const int64_t trow = int64_t(w) * ntiles + L.tile_off + ch.t0 + threadIdx.x;
     tfin[trow] = c_in[threadIdx.x];
@@ -804,11 +820,39 @@ __global__ __launch_bounds__(kWaveBlock) void rk_keep(const RkTile* __restrict__
   const uint32_t c = __popc(m0) + __popc(m1);
   uint32_t slot = tbase[trow] + wave_incl_scan(c) - c;
   const uint32_t* rk = ranks + int64_t(w) * top_total + L.top_off;
-  uint32_t k0 = 0, k1 = 0;
-  for (uint32_t bits = m0; bits != 0u; bits &= bits - 1u, ++slot)
-    if (int64_t(slot) < L.top && int64_t(rk[slot]) < L.keep) k0 |= bits & (0u - bits);
-  for (uint32_t bits = m1; bits != 0u; bits &= bits - 1u, ++slot)
-    if (int64_t(slot) < L.top && int64_t(rk[slot]) < L.keep) k1 |= bits & (0u - bits);
+  const uint32_t mw[2] = {m0, m1};
+  const uint32_t sw[2] = {slot, slot + uint32_t(__popc(m0))};  // slot of each word's first bit
+  uint32_t kw[2] = {0u, 0u};
+  // The ranks of the first two set bits of each word (nearly every word has at most
+  // two) are loaded together; further bits one at a time, in order.
+  bool ok[4];
+  uint32_t bit[4], rv[4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t b = mw[h];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int c = 2 * h + r;
+      ok[c] = b != 0u && int64_t(sw[h] + r) < L.top;
+      bit[c] = b & (0u - b);
+      b &= b - 1u;
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) rv[c] = ok[c] ? rk[sw[c >> 1] + (c & 1)] : 0u;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    if (ok[c] && int64_t(rv[c]) < L.keep) kw[c >> 1] |= bit[c];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t sl = sw[h] + 2;
+    uint32_t bits = mw[h];
+    bits &= bits - 1u;
+    bits &= bits - 1u;
+    for (; bits != 0u; bits &= bits - 1u, ++sl)
+      if (int64_t(sl) < L.top && int64_t(rk[sl]) < L.keep) kw[h] |= bits & (0u - bits);
+  }
+  const uint32_t k0 = kw[0], k1 = kw[1];
   if (q < nwords) kmask[wi] = k0;
   if (q + 1 < nwords) kmask[wi + 1] = k1;
   const uint32_t tot = wave_sum(__popc(k0) + __popc(k1));
