@@ -24,9 +24,10 @@
 // the subtraction of the previous step's P Q^T into the next step's k_first.
 //
 // The worker passes are HBM-bound (about one flop per byte), so no MFMA is used.  They
-// work on tiles of a few rows by a strip of 1024 columns (256 threads x float4): each
-// thread keeps Q of its four columns in registers, reads P one row at a time (the same
-// address across the wave), and has every worker's float4 of a row in flight at once.
+// run one 64-lane wave per matrix row by a strip of 256 columns (float4 per lane), or per
+// few rows when the worker count is small: each lane keeps Q of its four columns in
+// registers, reads P one row at a time (the same address across the wave), and has every
+// worker's float4 of a row in flight at once.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -676,13 +677,106 @@ __device__ __forceinline__ void first_matrix_tile(const UpdTile& t, const MatInf
   }
 }
 
-// The same for one flat chunk: chunk blockIdx.y of the tile, four elements per lane.
+// The same over RP consecutive rows per wave, for small compile-time worker counts
+// (WT > 0): the strip's Q rows are loaded once for all RP rows, and every worker's chunk
+// of every row is in flight before the first store.  Rows past the tile's end load row
+// i0 again (a valid address) and store nothing.  Per row, the arithmetic and its order
+// are those of first_matrix_tile.
+template <int V, typename GT, int WT, int FP, int RP, int A = V>
+__device__ __forceinline__ void first_matrix_rows(const UpdTile& t, const MatInfo& mi, const GT* G, float* E,
+                                                  const float* ebar, const float* Pprev, const float* Qprev,
+                                                  const float* Qin, float* Mbar, float* Ppart, int64_t ld,
+                                                  int R, float inv_w, int offset_valid) {
+  static_assert(WT > 0, "the multi-row first pass needs a compile-time worker count");
+  const int cols = mi.cols;
+  const int ln = int(threadIdx.x) & 63;
+  const int j = t.col_begin + ln * V;
+  const bool active = j < cols;
+  const bool hi = A == V || j + 4 <= cols;
+  const int i0 = t.row_begin + int(blockIdx.y) * RP;
+  if (i0 >= t.row_end) return;
+  const int nr = min(RP, t.row_end - i0);
+  float qv[V][4];
+  load_q_cols<V>(qv, Qin + mi.q_off, j, R, active, hi);
+  float qp[V][4];
+  if constexpr (FP == kFpDefer) load_q_cols<V>(qp, Qprev + mi.q_off, j, R, active && offset_valid, hi);
+  const int strip = t.col_begin / (kStreamThreads * V);
+  float* prow = Ppart + mi.ppart_off + int64_t(strip) * mi.rows * R;
+  float part[RP][4];
+#pragma unroll
+  for (int rr = 0; rr < RP; ++rr)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) part[rr][k] = 0.f;
+  if (active) {
+    const int64_t c0 = mi.offset + int64_t(i0) * cols + j;
+    vec_t<V> g[RP][WT], e[RP][WT];
+#pragma unroll
+    for (int rr = 0; rr < RP; ++rr) {
+      const int64_t c = c0 + int64_t(rr < nr ? rr : 0) * cols;
+#pragma unroll
+      for (int w = 0; w < WT; ++w) {
+        g[rr][w] = ld_nt<V, A>(G + w * ld + c, hi);
+        if constexpr (FP == kFpCarry) {
+          if (w == 0) e[rr][0] = ldv<V, A>(ebar + c, hi);
+        } else {
+          e[rr][w] = ld_nt<V, A>(E + w * ld + c, hi);
+        }
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < RP; ++rr) {
+      if (rr >= nr) break;
+      const int64_t c = c0 + int64_t(rr) * cols;
+      vec_t<V> acc{};
+      if constexpr (FP == kFpDefer) {
+        float pp[4] = {0.f, 0.f, 0.f, 0.f};
+        if (offset_valid) load_p_row(pp, Pprev + mi.p_off, i0 + rr, R);
+        const vec_t<V> u = pq_row<V>(pp, qp, R);
+#pragma unroll
+        for (int w = 0; w < WT; ++w) {
+          const vec_t<V> n = (g[rr][w] + e[rr][w]) - u;
+          st_nt<V, A>(E + w * ld + c, n, hi);
+          acc += n;
+        }
+        acc = acc * inv_w;
+      } else if constexpr (FP == kFpCarry) {
+#pragma unroll
+        for (int w = 0; w < WT; ++w) acc += g[rr][w];
+        acc = acc * inv_w + e[rr][0];
+      } else {
+#pragma unroll
+        for (int w = 0; w < WT; ++w) acc += g[rr][w] + e[rr][w];
+        acc = acc * inv_w;
+      }
+      st<V, A>(Mbar + c, acc, hi);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float s = 0.f;
+#pragma unroll
+        for (int q = 0; q < V; ++q) s += lane(acc, q) * qv[q][k];
+        part[rr][k] = s;
+      }
+    }
+  }
+#pragma unroll
+  for (int rr = 0; rr < RP; ++rr) {
+    if (rr >= nr) break;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (k < R) {
+        const float v = wave_sum(part[rr][k]);
+        if (ln == 0) prow[int64_t(i0 + rr) * R + k] = v;
+      }
+  }
+}
+
+// The same for one flat chunk (chunk `chunk` of the tile), four elements per lane.
 template <typename GT, int WT, int FP>
 __device__ __forceinline__ void first_flat_tile(const UpdTile& t, const MatInfo& mi, const GT* G, float* E,
                                                 const float* ebar, const float* Pprev, const float* Qprev,
                                                 const float* Qin, float* Mbar, float* Ppart, int W, int64_t ld,
-                                                int R, float inv_w, int offset_valid) {
-  const int64_t c0 = t.begin + int64_t(blockIdx.y) * kStreamTileElems;
+                                                int R, float inv_w, int offset_valid, int chunk) {
+  const int64_t c0 = t.begin + int64_t(chunk) * kStreamTileElems;
   if (c0 >= t.end) return;
   const int64_t c = c0 + int64_t(threadIdx.x & 63) * 4;
   const Flat4 f = flat4_at(mi, c);
@@ -710,7 +804,9 @@ __device__ __forceinline__ void first_flat_tile(const UpdTile& t, const MatInfo&
   flat_pbar_partial(mi, f, mb, Qin + mi.q_off, Ppart, int((c0 - mi.offset) / kStreamTileElems), R);
 }
 
-template <typename GT, int WT, int FP, int NW>
+// RP > 1 (small compile-time worker counts): each workgroup takes RP rows of its tile, or
+// RP flat chunks, and the launch's grid.y is the tile's row count over RP.
+template <typename GT, int WT, int FP, int NW, int RP>
 __global__ __launch_bounds__(kStreamThreads * NW) void k_first(const UpdTile* __restrict__ tiles, int32_t ntiles,
                                                           const MatInfo* __restrict__ mats,
                                                           const GT* __restrict__ G, float* __restrict__ E,
@@ -731,7 +827,20 @@ __global__ __launch_bounds__(kStreamThreads * NW) void k_first(const UpdTile* __
   }
   const MatInfo mi = mats[t.mat];
   if (mi.flat) {
-    first_flat_tile<GT, WT, FP>(t, mi, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, W, ld, R, inv_w, offset_valid);
+    for (int rr = 0; rr < RP; ++rr)
+      first_flat_tile<GT, WT, FP>(t, mi, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, W, ld, R, inv_w, offset_valid,
+                                  int(blockIdx.y) * RP + rr);
+    return;
+  }
+  if constexpr (RP > 1) {
+    switch (mi.vw) {
+      case 4: first_matrix_rows<4, GT, WT, FP, RP>(t, mi, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, ld, R, inv_w,
+                                                 offset_valid); break;
+      case 2: first_matrix_rows<4, GT, WT, FP, RP, 2>(t, mi, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, ld, R,
+                                                    inv_w, offset_valid); break;
+      default: first_matrix_rows<1, GT, WT, FP, RP>(t, mi, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, ld, R,
+                                                  inv_w, offset_valid); break;
+    }
     return;
   }
   switch (mi.vw) {
@@ -1625,15 +1734,17 @@ psgd_status launch_pass_nw(psgd_plan* plan, int which, int fp, const DeviceTable
   const GT* g = static_cast<const GT*>(a.grads);
   const int32_t ntiles = int32_t(a.n_s2);
   const dim3 grid((a.n_s2 + NW - 1) / NW, a.rows_per_tile), block(kStreamThreads * NW);
+  constexpr int RP = WT > 0 ? first_pass_rows(WT, std::is_same<GT, bf16>::value) : 1;
   if (which == kPassApply)
     return launch_k(plan, kKApply, a.Qw != nullptr ? k_apply<GT, WT, true, NW> : k_apply<GT, WT, false, NW>, grid,
                     block, a.st, dt.s2tiles, ntiles, dt.mats, g, a.errors, a.Mbar, a.p, a.q,
                     static_cast<const float*>(a.Qw), a.q_ws, a.update, a.mom, a.x, a.ebar_out, a.W, a.ld, a.R,
                     a.mode, a.lr, a.mu, a.inv_w);
-  auto first = fp == kFpDefer   ? k_first<GT, WT, kFpDefer, NW>
-               : fp == kFpCarry ? k_first<GT, WT, kFpCarry, NW>
-                                : k_first<GT, WT, kFpMean, NW>;
-  return launch_k(plan, kKFirst, first, grid, block, a.st, dt.s2tiles, ntiles, dt.mats, g, a.errors, a.ebar_in,
+  auto first = fp == kFpDefer   ? k_first<GT, WT, kFpDefer, NW, RP>
+               : fp == kFpCarry ? k_first<GT, WT, kFpCarry, NW, RP>
+                                : k_first<GT, WT, kFpMean, NW, RP>;
+  const dim3 grid_first(grid.x, (a.rows_per_tile + RP - 1) / RP);
+  return launch_k(plan, kKFirst, first, grid_first, block, a.st, dt.s2tiles, ntiles, dt.mats, g, a.errors, a.ebar_in,
                   a.Pprev, a.Qprev, a.q, a.Mbar, a.Ppart, a.W, a.ld, a.R, a.inv_w, a.offset_valid);
 }
 

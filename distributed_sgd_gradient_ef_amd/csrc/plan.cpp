@@ -217,7 +217,8 @@ extern "C" psgd_status psgd_plan_create(const psgd_layer* layers, int32_t n_laye
     for (const MatInfo& m : plan->mats)
       row_strips += m.flat ? (int64_t(m.rows) * m.cols + kStreamTileElems - 1) / kStreamTileElems
                            : int64_t(m.rows) * m.nstrips;
-    plan->worker_rows_per_tile = int32_t(std::max<int64_t>(1, (row_strips + kMaxWorkerTiles - 1) / kMaxWorkerTiles));
+    plan->worker_rows_per_tile = int32_t(std::max<int64_t>(first_pass_rows(n_workers, grad_dtype == PSGD_BF16),
+                                                            (row_strips + kMaxWorkerTiles - 1) / kMaxWorkerTiles));
     build_tiles(plan->s2tiles, plan->worker_rows_per_tile, plan->worker_rows_per_tile, kStreamThreads);
     build_tiles(plan->utiles, kUpdRowsPerTile, kUpdFlatRuns, kUpdThreads);
     for (size_t mi = 0; mi < plan->mats.size(); ++mi) {

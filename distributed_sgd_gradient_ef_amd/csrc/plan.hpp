@@ -27,6 +27,14 @@ constexpr int kStreamThreads = 64;
 constexpr int kStreamTileElems = kStreamThreads * 4;
 constexpr int64_t kMaxWorkerTiles = 65536;
 constexpr int kFlatMinCols = 32;
+// Rows (or flat chunks) per first-pass wave at small worker counts: with few workers a
+// row's loads are few, so a wave takes several rows, loads the strip's Q once for all of
+// them and has every row's loads in flight together (W = 4 on the 4096- and 8192-column
+// stress matrices: 2 rows for float32 gradients, 4 for bf16, measured best of 1, 2, 4 on
+// one allocation).  The tile lists then hold at least this many rows per entry.
+constexpr int first_pass_rows(int w, bool bf16_grads) {
+  return w == 1 || w == 2 ? 4 : w == 4 ? (bf16_grads ? 4 : 2) : 1;
+}
 
 // Update-only pass (deferred mode): workgroups of kUpdThreads over kUpdRowsPerTile rows
 // x a strip of kUpdThreads*4 columns, or kUpdFlatRuns runs of kUpdThreads*4 elements

@@ -437,6 +437,37 @@ def test_bf16_in_cross_step_modes(torch_gpu, mode, W):
         compare_step(run, snap, O, TOL, what=f"bf16 {mode} step {t}", errors_source=run.plain_errors())
 
 
+# Row counts that are not multiples of 2 or 4 end a multi-row first-pass wave early; the
+# set also has a 2-wide row (518 columns), a 1-wide row (29 columns), a flat matrix (66
+# columns), a matrix over one 256-column strip and 1-D tensors.
+MULTIROW_SHAPES = [(37, 29), (1, 10), (130, 518), (17, 1024), (203, 66), (6, 300), (1, 7)]
+
+
+@pytest.mark.parametrize("mode", ["plain", "carry", "deferred"])
+@pytest.mark.parametrize("W,bf16", [(1, False), (2, False), (4, False), (4, True), (2, True)])
+def test_multi_row_first_pass(torch_gpu, mode, W, bf16):
+    """Worker counts 1, 2 and 4 run the first pass over several rows per wave: every
+    first-pass form matches the oracle at every step (bf16: on the values the GPU read)."""
+    from distributed_sgd_gradient_ef_amd import psgd
+
+    log(f"[case] multi-row first pass mode={mode} W={W} bf16={bf16}")
+    shapes = MULTIROW_SHAPES
+    r = 2
+    rng = np.random.default_rng(61 + 7 * W + bf16)
+    flags = {"plain": 0, "carry": psgd.PSGD_FLAG_CARRY_ERROR_MEAN, "deferred": psgd.PSGD_FLAG_DEFERRED_ERROR}[mode]
+    run = DeviceRun(shapes, r, W, bf16=bf16, flags=flags)
+    run.set_q_host({i: rng.standard_normal((s[1], r)).astype(np.float32)
+                    for i, s in enumerate(shapes) if WL.is_matrix(s, r)})
+    run.set_errors_host([0.2 * rng.standard_normal((W,) + s).astype(np.float32) for s in shapes])
+    for t in range(3):
+        g = [rng.standard_normal((W,) + s).astype(np.float32) for s in shapes]
+        run.set_grads_host([WL.to_bf16_values(x) for x in g] if bf16 else g)
+        before = run.plain_errors()
+        snap = snapshot(run, range(len(shapes)), errors_source=before)
+        run.compress()
+        compare_step(run, snap, O, TOL, what=f"multi-row {mode} W={W} step {t}", errors_source=run.plain_errors())
+
+
 @pytest.mark.parametrize("mode", ["plain", "deferred"])
 def test_nesterov_and_update_null(torch_gpu, mode):
     """Nesterov momentum against the oracle's closed step, and a run with update=NULL
