@@ -618,8 +618,9 @@ __device__ __forceinline__ void momentum_masked(float* mom, float* x, int64_t c,
 }
 
 // ------------------------------------------------------------------ pass 1
-// One wave per row of a tile: row row_begin + blockIdx.y x the lanes' V columns each
-// (a tile spans several rows only for plans too large for one table entry per row).
+// One wave per row of a tile: row row_begin + rb x the lanes' V columns each (a tile
+// spans several rows for plans too large for one table entry per row, and at small
+// worker counts).
 // FP selects the first-pass form:
 //   kFpMean  Mbar = mean_w (G_w + E_w)
 //   kFpCarry Mbar = mean_w G_w + ebar  (ebar = mean of the errors the previous step
@@ -631,7 +632,7 @@ template <int V, typename GT, int WT, int FP, int A = V>
 __device__ __forceinline__ void first_matrix_tile(const UpdTile& t, const MatInfo& mi, const GT* G, float* E,
                                                   const float* ebar, const float* Pprev, const float* Qprev,
                                                   const float* Qin, float* Mbar, float* Ppart, int W, int64_t ld,
-                                                  int R, float inv_w, int offset_valid) {
+                                                  int R, float inv_w, int offset_valid, int rb) {
   const int cols = mi.cols;
   const int ln = int(threadIdx.x) & 63;
   const int j = t.col_begin + ln * V;
@@ -644,7 +645,7 @@ __device__ __forceinline__ void first_matrix_tile(const UpdTile& t, const MatInf
   const int strip = t.col_begin / (kStreamThreads * V);
   float* prow = Ppart + mi.ppart_off + int64_t(strip) * mi.rows * R;
   {
-    const int i = t.row_begin + int(blockIdx.y);
+    const int i = t.row_begin + rb;
     if (i >= t.row_end) return;
     float part[4] = {0.f, 0.f, 0.f, 0.f};
     if (active) {
@@ -686,14 +687,14 @@ template <int V, typename GT, int WT, int FP, int RP, int A = V>
 __device__ __forceinline__ void first_matrix_rows(const UpdTile& t, const MatInfo& mi, const GT* G, float* E,
                                                   const float* ebar, const float* Pprev, const float* Qprev,
                                                   const float* Qin, float* Mbar, float* Ppart, int64_t ld,
-                                                  int R, float inv_w, int offset_valid) {
+                                                  int R, float inv_w, int offset_valid, int rb) {
   static_assert(WT > 0, "the multi-row first pass needs a compile-time worker count");
   const int cols = mi.cols;
   const int ln = int(threadIdx.x) & 63;
   const int j = t.col_begin + ln * V;
   const bool active = j < cols;
   const bool hi = A == V || j + 4 <= cols;
-  const int i0 = t.row_begin + int(blockIdx.y) * RP;
+  const int i0 = t.row_begin + rb * RP;
   if (i0 >= t.row_end) return;
   const int nr = min(RP, t.row_end - i0);
   float qv[V][4];
@@ -804,23 +805,40 @@ __device__ __forceinline__ void first_flat_tile(const UpdTile& t, const MatInfo&
   flat_pbar_partial(mi, f, mb, Qin + mi.q_off, Ppart, int((c0 - mi.offset) / kStreamTileElems), R);
 }
 
+// Worker passes run a 1-D grid of ntiles x rgroups workgroups, one wave each, with the
+// row group fastest: consecutive workgroups walk down one tile's rows, so the launch
+// sweeps every buffer in address order (a tile-fastest order visits one row of every
+// tile first, across the whole multi-GB buffers, before the next).  A plan with 2^32 or
+// more worker-pass threads takes a 2-D grid instead (tile = blockIdx.x, row group =
+// blockIdx.y).
+struct TileRow {
+  int tile, rb;
+};
+__device__ __forceinline__ TileRow tile_row(int rgroups) {
+  if (gridDim.y > 1) return TileRow{int(blockIdx.x), int(blockIdx.y)};
+  const int id = int(blockIdx.x);
+  const int ti = id / rgroups;
+  return TileRow{ti, id - ti * rgroups};
+}
+
 // RP > 1 (small compile-time worker counts): each workgroup takes RP rows of its tile, or
-// RP flat chunks, and the launch's grid.y is the tile's row count over RP.
-template <typename GT, int WT, int FP, int NW, int RP>
-__global__ __launch_bounds__(kStreamThreads * NW) void k_first(const UpdTile* __restrict__ tiles, int32_t ntiles,
-                                                          const MatInfo* __restrict__ mats,
-                                                          const GT* __restrict__ G, float* __restrict__ E,
-                                                          const float* __restrict__ ebar,
-                                                          const float* __restrict__ Pprev,
-                                                          const float* __restrict__ Qprev,
-                                                          const float* __restrict__ Qin, float* __restrict__ Mbar,
-                                                          float* __restrict__ Ppart, int W, int64_t ld, int R,
-                                                          float inv_w, int offset_valid) {
-  const int ti = int(blockIdx.x) * NW + int(threadIdx.x >> 6);  // one tile per wave
-  if (ti >= ntiles) return;
-  const UpdTile t = tiles[ti];
+// RP flat chunks, and rgroups is the tile's row count over RP.
+template <typename GT, int WT, int FP, int RP>
+__global__ __launch_bounds__(kStreamThreads) void k_first(const UpdTile* __restrict__ tiles, int32_t ntiles,
+                                                     int32_t rgroups, const MatInfo* __restrict__ mats,
+                                                     const GT* __restrict__ G, float* __restrict__ E,
+                                                     const float* __restrict__ ebar,
+                                                     const float* __restrict__ Pprev,
+                                                     const float* __restrict__ Qprev,
+                                                     const float* __restrict__ Qin, float* __restrict__ Mbar,
+                                                     float* __restrict__ Ppart, int W, int64_t ld, int R,
+                                                     float inv_w, int offset_valid) {
+  const TileRow tr = tile_row(rgroups);
+  if (tr.tile >= ntiles) return;
+  const UpdTile t = tiles[tr.tile];
+  const int rb = tr.rb;
   if (t.mat < 0) {  // uncompressed tensor: the worker mean of G
-    if (blockIdx.y != 0) return;
+    if (rb != 0) return;
     const int64_t c = t.begin + int64_t(threadIdx.x & 63) * 4;
     if (c < t.end) store4(Mbar + c, sum_g<4, GT, WT>(G, W, ld, c) * inv_w, t.end - c);
     return;
@@ -829,27 +847,27 @@ __global__ __launch_bounds__(kStreamThreads * NW) void k_first(const UpdTile* __
   if (mi.flat) {
     for (int rr = 0; rr < RP; ++rr)
       first_flat_tile<GT, WT, FP>(t, mi, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, W, ld, R, inv_w, offset_valid,
-                                  int(blockIdx.y) * RP + rr);
+                                  rb * RP + rr);
     return;
   }
   if constexpr (RP > 1) {
     switch (mi.vw) {
       case 4: first_matrix_rows<4, GT, WT, FP, RP>(t, mi, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, ld, R, inv_w,
-                                                 offset_valid); break;
+                                                 offset_valid, rb); break;
       case 2: first_matrix_rows<4, GT, WT, FP, RP, 2>(t, mi, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, ld, R,
-                                                    inv_w, offset_valid); break;
+                                                    inv_w, offset_valid, rb); break;
       default: first_matrix_rows<1, GT, WT, FP, RP>(t, mi, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, ld, R,
-                                                  inv_w, offset_valid); break;
+                                                  inv_w, offset_valid, rb); break;
     }
     return;
   }
   switch (mi.vw) {
     case 4: first_matrix_tile<4, GT, WT, FP>(t, mi, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, W, ld, R, inv_w,
-                                     offset_valid); break;
+                                     offset_valid, rb); break;
     case 2: first_matrix_tile<4, GT, WT, FP, 2>(t, mi, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, W, ld, R, inv_w,
-                                     offset_valid); break;
+                                     offset_valid, rb); break;
     default: first_matrix_tile<1, GT, WT, FP>(t, mi, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, W, ld, R, inv_w,
-                                     offset_valid); break;
+                                     offset_valid, rb); break;
   }
 }
 
@@ -1326,7 +1344,8 @@ template <int V, typename GT, int WT, bool LOCAL, int A = V>
 __device__ __forceinline__ void apply_matrix_tile(const UpdTile& t, const MatInfo& mi, const GT* G, float* E,
                                                   const float* P, const float* Q, const float* Qw, int64_t q_ws,
                                                   float* update, float* mom, float* x, float* ebar, int W,
-                                                  int64_t ld, int R, int mode, float lr, float mu, float inv_w) {
+                                                  int64_t ld, int R, int mode, float lr, float mu, float inv_w,
+                                                  int rb) {
   const int cols = mi.cols;
   const int j = t.col_begin + (int(threadIdx.x) & 63) * V;
   if (j >= cols) return;
@@ -1334,7 +1353,7 @@ __device__ __forceinline__ void apply_matrix_tile(const UpdTile& t, const MatInf
   float qv[V][4];
   load_q_cols<V>(qv, Q + mi.q_off, j, R, true, hi);
   {
-    const int i = t.row_begin + int(blockIdx.y);
+    const int i = t.row_begin + rb;
     if (i >= t.row_end) return;
     float pr[4];
     load_p_row(pr, P + mi.p_off, i, R);
@@ -1351,13 +1370,14 @@ __device__ __forceinline__ void apply_matrix_tile(const UpdTile& t, const MatInf
   }
 }
 
-// The same for one flat chunk (chunk blockIdx.y of the tile).
+// The same for one flat chunk (chunk rb of the tile).
 template <typename GT, int WT, bool LOCAL>
 __device__ __forceinline__ void apply_flat_tile(const UpdTile& t, const MatInfo& mi, const GT* G, float* E,
                                                 const float* P, const float* Q, const float* Qw, int64_t q_ws,
                                                 float* update, float* mom, float* x, float* ebar, int W,
-                                                int64_t ld, int R, int mode, float lr, float mu, float inv_w) {
-  const int64_t c0 = t.begin + int64_t(blockIdx.y) * kStreamTileElems;
+                                                int64_t ld, int R, int mode, float lr, float mu, float inv_w,
+                                                int rb) {
+  const int64_t c0 = t.begin + int64_t(rb) * kStreamTileElems;
   if (c0 >= t.end) return;
   const int64_t c = c0 + int64_t(threadIdx.x & 63) * 4;
   const Flat4 f = flat4_at(mi, c);
@@ -1382,18 +1402,20 @@ __device__ __forceinline__ void apply_flat_tile(const UpdTile& t, const MatInfo&
   }
 }
 
-template <typename GT, int WT, bool LOCAL, int NW>
-__global__ __launch_bounds__(kStreamThreads * NW) void k_apply(
-    const UpdTile* __restrict__ tiles, int32_t ntiles, const MatInfo* __restrict__ mats, const GT* __restrict__ G,
+template <typename GT, int WT, bool LOCAL>
+__global__ __launch_bounds__(kStreamThreads) void k_apply(
+    const UpdTile* __restrict__ tiles, int32_t ntiles, int32_t rgroups, const MatInfo* __restrict__ mats,
+    const GT* __restrict__ G,
     float* __restrict__ E, const float* __restrict__ Mbar, const float* __restrict__ P,
     const float* __restrict__ Q, const float* __restrict__ Qw, int64_t q_ws, float* __restrict__ update,
     float* __restrict__ mom, float* __restrict__ x, float* __restrict__ ebar, int W, int64_t ld, int R, int mode,
     float lr, float mu, float inv_w) {
-  const int ti = int(blockIdx.x) * NW + int(threadIdx.x >> 6);  // one tile per wave
-  if (ti >= ntiles) return;
-  const UpdTile t = tiles[ti];
+  const TileRow tr = tile_row(rgroups);
+  if (tr.tile >= ntiles) return;
+  const UpdTile t = tiles[tr.tile];
+  const int rb = tr.rb;
   if (t.mat < 0) {
-    if (blockIdx.y != 0) return;
+    if (rb != 0) return;
     const int64_t c = t.begin + int64_t(threadIdx.x & 63) * 4;
     if (c >= t.end) return;
     const int64_t valid = t.end - c;
@@ -1404,13 +1426,14 @@ __global__ __launch_bounds__(kStreamThreads * NW) void k_apply(
   }
   const MatInfo mi = mats[t.mat];
   if (mi.flat) {
-    apply_flat_tile<GT, WT, LOCAL>(t, mi, G, E, P, Q, Qw, q_ws, update, mom, x, ebar, W, ld, R, mode, lr, mu, inv_w);
+    apply_flat_tile<GT, WT, LOCAL>(t, mi, G, E, P, Q, Qw, q_ws, update, mom, x, ebar, W, ld, R, mode, lr, mu, inv_w,
+                                   rb);
     return;
   }
   switch (mi.vw) {
-    case 4: apply_matrix_tile<4, GT, WT, LOCAL>(t, mi, G, E, P, Q, Qw, q_ws, update, mom, x, ebar, W, ld, R, mode, lr, mu, inv_w); break;
-    case 2: apply_matrix_tile<4, GT, WT, LOCAL, 2>(t, mi, G, E, P, Q, Qw, q_ws, update, mom, x, ebar, W, ld, R, mode, lr, mu, inv_w); break;
-    default: apply_matrix_tile<1, GT, WT, LOCAL>(t, mi, G, E, P, Q, Qw, q_ws, update, mom, x, ebar, W, ld, R, mode, lr, mu, inv_w); break;
+    case 4: apply_matrix_tile<4, GT, WT, LOCAL>(t, mi, G, E, P, Q, Qw, q_ws, update, mom, x, ebar, W, ld, R, mode, lr, mu, inv_w, rb); break;
+    case 2: apply_matrix_tile<4, GT, WT, LOCAL, 2>(t, mi, G, E, P, Q, Qw, q_ws, update, mom, x, ebar, W, ld, R, mode, lr, mu, inv_w, rb); break;
+    default: apply_matrix_tile<1, GT, WT, LOCAL>(t, mi, G, E, P, Q, Qw, q_ws, update, mom, x, ebar, W, ld, R, mode, lr, mu, inv_w, rb); break;
   }
 }
 
@@ -1727,30 +1750,34 @@ struct StepArgs {
 
 enum PassKind { kPassFirst = 0, kPassApply = 1 };
 
-// NW waves per workgroup, one worker-pass tile each (one wave: measured, four waves per
-// workgroup were no faster at W = 4 or 8).
-template <typename GT, int WT, int NW>
-psgd_status launch_pass_nw(psgd_plan* plan, int which, int fp, const DeviceTables& dt, const StepArgs& a) {
-  const GT* g = static_cast<const GT*>(a.grads);
-  const int32_t ntiles = int32_t(a.n_s2);
-  const dim3 grid((a.n_s2 + NW - 1) / NW, a.rows_per_tile), block(kStreamThreads * NW);
-  constexpr int RP = WT > 0 ? first_pass_rows(WT, std::is_same<GT, bf16>::value) : 1;
-  if (which == kPassApply)
-    return launch_k(plan, kKApply, a.Qw != nullptr ? k_apply<GT, WT, true, NW> : k_apply<GT, WT, false, NW>, grid,
-                    block, a.st, dt.s2tiles, ntiles, dt.mats, g, a.errors, a.Mbar, a.p, a.q,
-                    static_cast<const float*>(a.Qw), a.q_ws, a.update, a.mom, a.x, a.ebar_out, a.W, a.ld, a.R,
-                    a.mode, a.lr, a.mu, a.inv_w);
-  auto first = fp == kFpDefer   ? k_first<GT, WT, kFpDefer, NW, RP>
-               : fp == kFpCarry ? k_first<GT, WT, kFpCarry, NW, RP>
-                                : k_first<GT, WT, kFpMean, NW, RP>;
-  const dim3 grid_first(grid.x, (a.rows_per_tile + RP - 1) / RP);
-  return launch_k(plan, kKFirst, first, grid_first, block, a.st, dt.s2tiles, ntiles, dt.mats, g, a.errors, a.ebar_in,
-                  a.Pprev, a.Qprev, a.q, a.Mbar, a.Ppart, a.W, a.ld, a.R, a.inv_w, a.offset_valid);
+// One wave per workgroup (measured: four waves per workgroup were no faster at W = 4 or
+// 8), one workgroup per (tile, row group); k_first takes first_pass_rows rows per group.
+inline dim3 pass_grid(int32_t ntiles, int32_t rgroups) {
+  if (uint64_t(ntiles) * uint64_t(rgroups) * kStreamThreads <= uint64_t(UINT32_MAX))
+    return dim3(unsigned(ntiles) * unsigned(rgroups));
+  return dim3(unsigned(ntiles), unsigned(rgroups));
 }
 
 template <typename GT, int WT>
 psgd_status launch_pass(psgd_plan* plan, int which, int fp, const DeviceTables& dt, const StepArgs& a) {
-  return launch_pass_nw<GT, WT, 1>(plan, which, fp, dt, a);
+  const GT* g = static_cast<const GT*>(a.grads);
+  const int32_t ntiles = int32_t(a.n_s2);
+  const dim3 block(kStreamThreads);
+  if (which == kPassApply) {
+    const int32_t rgroups = int32_t(a.rows_per_tile);
+    return launch_k(plan, kKApply, a.Qw != nullptr ? k_apply<GT, WT, true> : k_apply<GT, WT, false>,
+                    pass_grid(ntiles, rgroups), block, a.st, dt.s2tiles, ntiles, rgroups, dt.mats, g,
+                    a.errors, a.Mbar, a.p, a.q, static_cast<const float*>(a.Qw), a.q_ws, a.update, a.mom, a.x,
+                    a.ebar_out, a.W, a.ld, a.R, a.mode, a.lr, a.mu, a.inv_w);
+  }
+  constexpr int RP = WT > 0 ? first_pass_rows(WT, std::is_same<GT, bf16>::value) : 1;
+  const int32_t rgroups = int32_t((a.rows_per_tile + RP - 1) / RP);
+  auto first = fp == kFpDefer   ? k_first<GT, WT, kFpDefer, RP>
+               : fp == kFpCarry ? k_first<GT, WT, kFpCarry, RP>
+                                : k_first<GT, WT, kFpMean, RP>;
+  return launch_k(plan, kKFirst, first, pass_grid(ntiles, rgroups), block, a.st, dt.s2tiles, ntiles,
+                  rgroups, dt.mats, g, a.errors, a.ebar_in, a.Pprev, a.Qprev, a.q, a.Mbar, a.Ppart, a.W, a.ld, a.R,
+                  a.inv_w, a.offset_valid);
 }
 
 // Worker-count specialisations of the worker passes: W in {1,2,4,8,16} unrolls fully,
