@@ -344,6 +344,20 @@ __device__ __forceinline__ void load_flat_p_rows(float (&p0)[4], float (&p1)[4],
 // (P Q^T) at the lane's elements, each by pq_dot (0 past the matrix end).
 __device__ __forceinline__ f4 pq_flat(const float (&p0)[4], const float (&p1)[4], const float* Qm, const Flat4& f,
                                       int R) {
+  // Four elements of one row whose Q rows start on a 16-byte boundary (nearly every lane):
+  // the 4R floats are R aligned float4 loads and every element uses p0.  Same products
+  // and order as the column-by-column form below.
+  if (f.nw == 4 && f.valid == 4 && ((f.j0 * R) & 3) == 0) {
+    float qv[4][4];
+    const float* base = Qm + int64_t(f.j0) * R;
+    switch (R) {
+      case 1: load_q4<1>(qv, base); break;
+      case 2: load_q4<2>(qv, base); break;
+      case 3: load_q4<3>(qv, base); break;
+      default: load_q4<4>(qv, base); break;
+    }
+    return f4{pq_dot(p0, qv[0], R), pq_dot(p0, qv[1], R), pq_dot(p0, qv[2], R), pq_dot(p0, qv[3], R)};
+  }
   f4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int q = 0; q < 4; ++q)

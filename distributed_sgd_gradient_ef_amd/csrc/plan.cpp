@@ -228,6 +228,15 @@ extern "C" psgd_status psgd_plan_create(const psgd_layer* layers, int32_t n_laye
         for (int32_t c = 0; c < m.cols; c += strip)
           plan->qtiles.push_back(QTile{int32_t(mi), b, c, std::min(m.cols, c + strip)});
     }
+    // Longest row blocks first, so that they do not form the launch's tail (the Q
+    // partials do not depend on the order in which tiles run).
+    std::stable_sort(plan->qtiles.begin(), plan->qtiles.end(), [&](const QTile& a, const QTile& b) {
+      auto len = [&](const QTile& t) {
+        const MatInfo& m = plan->mats[size_t(t.mat)];
+        return std::min(m.rows, (t.blk + 1) * m.rows_per_blk) - t.blk * m.rows_per_blk;
+      };
+      return len(a) > len(b);
+    });
 
     // Workspace: Mbar (same layout as update), P-bar partials, Q partials; 256-byte aligned.
     uint64_t ws = 0;
