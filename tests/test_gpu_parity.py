@@ -668,6 +668,48 @@ def test_largest_tensor_sampled(torch_gpu):
     assert np.abs(Us - np.outer(P[rows], Q[cols])).max() <= 1e-5 * np.abs(Us).max()
 
 
+def test_grid_fallback_past_2_32_threads(torch_gpu):
+    """A 69,000,000 x 31 matrix at W=3: over 2^32 worker-pass threads, so k_first and
+    k_apply take the 2-D grid.  The worker mean of the new errors plus U equals the mean
+    gradient everywhere; P, Q and U are checked on sampled rows (and all 31 columns)
+    against the oracle's per-element definitions."""
+    n, m, W = 69_000_000, 31, 3
+    log(f"[case] 2-D grid fallback {n}x{m} r=1 W={W}")
+    torch = torch_gpu
+    run = DeviceRun([(n, m)], 1, W)
+    g = torch.Generator(device=run.dev)
+    g.manual_seed(78)
+    col = torch.randn(m, generator=g, device=run.dev)
+    for w in range(W):
+        torch.randn(n * m, generator=g, device=run.dev, out=run.grads[w, : n * m])
+        run.grads[w, : n * m].view(n, m).add_(torch.randn(n, 1, generator=g, device=run.dev) * col[None])
+    q = np.random.default_rng(5).standard_normal((m, 1)).astype(np.float32)
+    run.set_q_host({0: q})
+    run.compress()
+    torch.cuda.synchronize()
+    Gm = run.grads[:, : n * m].view(W, n, m).mean(0)
+    Em = run.errors[:, : n * m].view(W, n, m).mean(0)
+    U = run.update[: n * m].view(n, m)
+    assert (Em + U - Gm).abs().max().item() <= 1e-5 * Gm.abs().max().item()
+    del Em
+    P = run.p_layer(0).astype(np.float64)[:, 0]
+    Q = run.q_layer(0).astype(np.float64)[:, 0]
+    assert abs(np.dot(P, P) - 1.0) < 1e-5
+    rows = np.sort(np.random.default_rng(3).choice(n, 64, replace=False))
+    ridx = torch.as_tensor(rows, device=run.dev)
+    Gr = run.grads[:, : n * m].view(W, n, m)[:, ridx].double().mean(0).cpu().numpy()
+    ratio = (Gr @ q.astype(np.float64)[:, 0]) / P[rows]
+    assert np.abs(ratio / ratio.mean() - 1).max() < 1e-4
+    Pd = torch.as_tensor(P, device=run.dev)
+    q_ref = torch.zeros(m, dtype=torch.float64, device=run.dev)  # Q = Mbar^T P, by row chunks
+    for r0 in range(0, n, 1 << 23):
+        q_ref += Gm[r0:r0 + (1 << 23)].double().T @ Pd[r0:r0 + (1 << 23)]
+    q_ref = q_ref.cpu().numpy()
+    assert np.abs(q_ref - Q).max() <= 1e-4 * np.abs(Q).max()
+    Us = U[ridx].double().cpu().numpy()
+    assert np.abs(Us - np.outer(P[rows], Q)).max() <= 1e-5 * np.abs(Us).max()
+
+
 def test_momentum_200_steps(torch_gpu):
     """EF-SGD with momentum (mu=0.9, lr=0.1) on ResNet-18 shapes, r=4, W=16, drifting
     subspace, 200 steps.  Every step: a fixed sample of tensors against the oracle fed
