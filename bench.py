@@ -22,6 +22,9 @@ lists, new errors, dense mean update).
 Prints one JSON line:
   value          gradient GB/s = W * numel * 4 bytes / step time (whole job, one GPU)
   pct_hbm_peak   minimal HBM bytes of a step / step time / 8 TB/s
+  pct_hbm_peak_kernel_bytes
+                 the bytes the variant's kernels must move (Mbar written and read again,
+                 a second pass over the workers) / step time / 8 TB/s
   roofline       the longest kernel: algorithmic bytes per launch / its mean duration
                  (HIP events recorded on the launch stream around every launch)
   cpu_baseline   the CPU oracle timed on a bounded sample of the same workload
@@ -384,9 +387,13 @@ def main() -> int:
                 entry["alg_GBps"] = round(kb[name] / (us * 1e-6) / 1e9, 1)
             kernels[name] = entry
         grad_bytes = W * s["numel"] * 4
+        # the variant's own bytes: what its kernels must move per step (reads of Mbar and
+        # of a second pass included), beside the minimal-bytes model of the step
+        own = sum(kb[k] * n for k, (n, _) in stats.items() if k in kb) / max(args.steps, 1)
         del grads, errors, workspace
         return {"ms": ms, "ms_med": ms_med, "ms_min": ms_min, "ms_timed": ms_timed, "ms_graph": ms_graph,
-                "kernels": kernels, "kb": kb,
+                "kernels": kernels, "kb": kb, "own_bytes": int(own),
+                "pct_own": 100.0 * own / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
                 "sizes": s,
                 "value": grad_bytes / (ms * 1e-3) / 1e9, "grad_bytes": grad_bytes,
                 "pct": 100.0 * s["model_bytes"] / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9)}
@@ -618,6 +625,8 @@ def main() -> int:
                                   "local": "PSGD_FLAG_LOCAL_Q_ERROR"}[primary]},
         "pct_hbm_peak": round(main_run["pct"], 2),
         "model_bytes_per_step": s["model_bytes"],
+        "kernel_bytes_per_step": main_run["own_bytes"],
+        "pct_hbm_peak_kernel_bytes": round(main_run["pct_own"], 2),
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "alg_bytes_per_launch": kb[dom], "mean_us": dom_us},
@@ -628,6 +637,8 @@ def main() -> int:
     }
     out["variants"] = {n: {"value": round(r["value"], 2), "ms_per_step": round(r["ms"], 4),
                            "pct_hbm_peak": round(r["pct"], 2),
+                           "kernel_bytes_per_step": r["own_bytes"],
+                           "pct_hbm_peak_kernel_bytes": round(r["pct_own"], 2),
                            "kernels_mean_us": {k: v["mean_us"] for k, v in r["kernels"].items()}}
                        for n, r in results.items() if n != primary}
     if args.mode == "all":
