@@ -223,7 +223,7 @@ def config_timings(torch, psgd, WL, dev, steps: int) -> dict:
     4 and with bf16 gradients, and the fused momentum step on the ResNet-18 shapes."""
     out = {}
 
-    def run(name, wl, grads, gbytes, nsteps, momentum=False, dtype=None):
+    def run(name, wl, grads, gbytes, nsteps, momentum=False, dtype=None, graph=False):
         W = wl.workers
         shapes = [s for _, s in wl.shapes]
         plan = psgd.psgd_plan_create(shapes, wl.rank, W, dtype if dtype is not None else psgd.PSGD_F32,
@@ -257,6 +257,14 @@ def config_timings(torch, psgd, WL, dev, steps: int) -> dict:
                      "ms_per_step": round(ms, 4), "ms_median": round(med, 4), "ms_min": round(mn, 4),
                      "grad_GBps": round(W * s["numel"] * gbytes / (ms * 1e-3) / 1e9, 1),
                      "pct_hbm_peak": round(100.0 * model / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 2)}
+        if graph:  # the same step captured once into a HIP graph and replayed
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):  # on the capture stream (the current one inside)
+                psgd.psgd_compress_step(plan, grads, errors, q, p, update, workspace)
+            torch.cuda.synchronize(dev)
+            ms_g, _, _ = timed_steps(torch, g.replay, nsteps, stream)
+            out[name]["ms_per_step_graph_replay"] = round(ms_g, 4)
+            del g
         del errors, q, p, update, workspace, plan
 
     def draw(wl):
@@ -266,7 +274,7 @@ def config_timings(torch, psgd, WL, dev, steps: int) -> dict:
         return g
 
     wl = WL.workload("single")
-    run("single", wl, draw(wl), 4, 10 * steps)
+    run("single", wl, draw(wl), 4, 10 * steps, graph=True)
     out["single"]["role"] = "latency (one 256x128 matrix, W=1, r=1; launch-bound)"
     wl = WL.workload("lstm")
     g = draw(wl)
