@@ -12,8 +12,11 @@
 //                mean_w M_w Q = Mbar Q and mean_w M_w^T P = Mbar^T P: the all-reduce of
 //                P and Q becomes this one pass over the worker slices.  1-D tensors get
 //                the worker mean of G.
-//   k_mgs        sums the P-bar partials and runs modified Gram-Schmidt, one workgroup
-//                per matrix.
+//   k_mgs        sums the P-bar partials and orthonormalises the columns, one
+//                workgroup per matrix: Gram-Schmidt taken in the r x r Gram space of
+//                P-bar (one fixed-order fp64 reduction of the Gram entries, then the
+//                column-by-column coefficients and drop rule), which is modified
+//                Gram-Schmidt in exact arithmetic.
 //   k_q_partial  Q partials = Mbar^T P over row blocks and column strips.
 //   k_q_reduce   Q = sum of the partials (fixed order, deterministic).
 //   k_apply      streams G and E again: E'_w = (G_w + E_w) - P Q^T, writes the
@@ -178,38 +181,25 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
-// Sum over the workgroup; every thread gets the same value (same order everywhere).
-__device__ double block_sum(double v, double* red) {
-  v = wave_sum(v);
+// N sums over the workgroup in one round of barriers (red holds N * waves doubles);
+// every thread gets the same values.
+template <int N>
+__device__ void block_sum_n(double (&v)[N], double* red) {
   const int lane_id = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int a = 0; a < N; ++a) v[a] = wave_sum(v[a]);
   __syncthreads();
-  if (lane_id == 0) red[wave] = v;
+  if (lane_id == 0)
+#pragma unroll
+    for (int a = 0; a < N; ++a) red[N * wave + a] = v[a];
   __syncthreads();
-  double s = 0.0;
   const int nw = blockDim.x >> 6;
-  for (int i = 0; i < nw; ++i) s += red[i];
-  return s;
-}
-
-// Two sums over the workgroup in one round of barriers.
-__device__ void block_sum2(double& a, double& b, double* red) {
-  a = wave_sum(a);
-  b = wave_sum(b);
-  const int lane_id = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __syncthreads();
-  if (lane_id == 0) {
-    red[2 * wave] = a;
-    red[2 * wave + 1] = b;
+#pragma unroll
+  for (int a = 0; a < N; ++a) {
+    double t = 0.0;
+    for (int i = 0; i < nw; ++i) t += red[N * i + a];
+    v[a] = t;
   }
-  __syncthreads();
-  double sa = 0.0, sb = 0.0;
-  const int nw = blockDim.x >> 6;
-  for (int i = 0; i < nw; ++i) {
-    sa += red[2 * i];
-    sb += red[2 * i + 1];
-  }
-  a = sa;
-  b = sb;
 }
 
 // ------------------------------------------------------------------ P Q^T
@@ -1006,13 +996,56 @@ __device__ __forceinline__ void pbar_rows(float (&acc)[U][R], const float* src, 
   }
 }
 
+// Gram-Schmidt of the columns of P-bar taken in its R x R Gram space (g: the packed
+// upper triangle, entry (k, l), k <= l, at k R - k (k - 1) / 2 + l - k): column by
+// column, the projection coefficients R_lk on the kept earlier columns and the residual
+// norm sqrt(G_kk - sum_l R_lk^2), with the drop rule (a residual norm that is zero, not a
+// number, or at most 1e-4 times the column's norm before orthogonalisation drops the
+// column).  In exact arithmetic this is column-by-column modified Gram-Schmidt.  Writes
+// T = R^-1 with zero columns for dropped columns, so that P = P-bar T.
+template <int R>
+__device__ __forceinline__ void gram_gs_coeffs(const double (&g)[R * (R + 1) / 2], double (&T)[R][R]) {
+  auto G = [&](int k, int l) { return g[k * R - k * (k - 1) / 2 + (l - k)]; };
+  double Rm[R][R];
+  bool kept[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const double before = sqrt(G(k, k));
+    double ss = G(k, k);
+#pragma unroll
+    for (int l = 0; l < k; ++l) {
+      double r = 0.0;
+      if (kept[l]) {
+        r = G(l, k);
+#pragma unroll
+        for (int m = 0; m < l; ++m) r -= Rm[m][l] * Rm[m][k];
+        r /= Rm[l][l];
+      }
+      Rm[l][k] = r;
+      ss -= r * r;
+    }
+    const double after = sqrt(ss > 0.0 ? ss : 0.0);
+    kept[k] = after > 0.0 && after > 1e-4 * before;
+    Rm[k][k] = after;
+#pragma unroll
+    for (int l = 0; l < R; ++l) T[l][k] = 0.0;
+    if (kept[k]) {
+      T[k][k] = 1.0 / after;
+#pragma unroll
+      for (int l = 0; l < k; ++l)
+#pragma unroll
+        for (int m = 0; m < R; ++m) T[m][k] -= Rm[l][k] * T[m][l] / after;
+    }
+  }
+}
+
 template <int R>
 __global__ __launch_bounds__(kMgsThreads) void k_mgs(const MatInfo* __restrict__ mats,
                                                      const float* __restrict__ Ppart,
                                                      float* __restrict__ P, float* __restrict__ P2,
                                                      const double* __restrict__ gpart,
                                                      double* __restrict__ tmat) {
-  __shared__ double red[2 * (kMgsThreads / 64)];
+  __shared__ double red[10 * (kMgsThreads / 64)];
   const MatInfo mi = mats[blockIdx.x];
   const float* src = Ppart + mi.ppart_off;
   float* dst = P + mi.p_off;
@@ -1042,37 +1075,37 @@ __global__ __launch_bounds__(kMgsThreads) void k_mgs(const MatInfo* __restrict__
     } else {
       pbar_rows<R, kMgsRowsPerThread>(v, src, strip_stride, mi, int(threadIdx.x), bs, n);
     }
+    // The R (R + 1) / 2 Gram entries of the rows in registers, summed over the
+    // workgroup in one fixed-order reduction; every thread then derives the same
+    // coefficients and applies them to its rows (terms with a zero coefficient are
+    // skipped, so a dropped column, even one that is not a number, leaves no trace).
+    constexpr int NG = R * (R + 1) / 2;
+    double g[NG];
 #pragma unroll
-    for (int k = 0; k < R; ++k) {
-      double s = 0.0, c = 0.0;
+    for (int k = 0, a = 0; k < R; ++k)
 #pragma unroll
-      for (int r = 0; r < kMgsRowsPerThread; ++r) {
-        s += double(v[r][k]) * double(v[r][k]);
-        if (k > 0) c += double(v[r][0]) * double(v[r][k]);
+      for (int l = k; l < R; ++l, ++a) {
+        double t = 0.0;
+#pragma unroll
+        for (int r = 0; r < kMgsRowsPerThread; ++r) t += double(v[r][k]) * double(v[r][l]);
+        g[a] = t;
       }
-      block_sum2(s, c, red);
-      const double before = sqrt(s);
-      double after = before;
-      if (k > 0) {
+    block_sum_n<NG>(g, red);
+    double T[R][R];
+    gram_gs_coeffs<R>(g, T);
 #pragma unroll
-        for (int l = 0; l < k; ++l) {
-          if (l > 0) {
-            c = 0.0;
+    for (int r = 0; r < kMgsRowsPerThread; ++r) {
+      float o[R];
 #pragma unroll
-            for (int r = 0; r < kMgsRowsPerThread; ++r) c += double(v[r][l]) * double(v[r][k]);
-            c = block_sum(c, red);
-          }
+      for (int k = 0; k < R; ++k) {
+        double t = 0.0;
 #pragma unroll
-          for (int r = 0; r < kMgsRowsPerThread; ++r) v[r][k] = float(double(v[r][k]) - c * double(v[r][l]));
-        }
-        double s2 = 0.0;
-#pragma unroll
-        for (int r = 0; r < kMgsRowsPerThread; ++r) s2 += double(v[r][k]) * double(v[r][k]);
-        after = sqrt(block_sum(s2, red));
+        for (int l = 0; l <= k; ++l)
+          if (T[l][k] != 0.0) t += double(v[r][l]) * T[l][k];
+        o[k] = float(t);
       }
-      const double scale = (after > 0.0 && after > 1e-4 * before) ? 1.0 / after : 0.0;
 #pragma unroll
-      for (int r = 0; r < kMgsRowsPerThread; ++r) v[r][k] = scale > 0.0 ? float(double(v[r][k]) * scale) : 0.f;
+      for (int k = 0; k < R; ++k) v[r][k] = o[k];
     }
 #pragma unroll
     for (int r = 0; r < kMgsRowsPerThread; ++r) {
@@ -1090,47 +1123,19 @@ __global__ __launch_bounds__(kMgsThreads) void k_mgs(const MatInfo* __restrict__
 
   // Tall matrices: k_tall_rows has written P-bar into the output and one Gram partial
   // (in double) per block of kTallRows rows.  The partials are summed in a fixed order;
-  // one thread takes the same Gram-Schmidt in the R x R Gram space -- the projection
-  // coefficients R_lk on the kept columns l < k and the residual norm
-  // sqrt(G_kk - sum_l R_lk^2), with the same drop rule -- and stores T = R^-1 (zero
-  // columns for dropped ones) for k_tall_apply, which writes P = P-bar T.
+  // one thread takes the same Gram-space Gram-Schmidt and stores T = R^-1 (zero columns
+  // for dropped ones) for k_tall_apply, which writes P = P-bar T.
   constexpr int NG = R * (R + 1) / 2;
   double g[NG];
 #pragma unroll
-  for (int a = 0; a < NG; ++a) {
-    double s = 0.0;
-    for (int b = int(threadIdx.x); b < mi.tall_nblk; b += bs) s += gpart[int64_t(mi.tall_blk0 + b) * 10 + a];
-    g[a] = block_sum(s, red);
-  }
+  for (int a = 0; a < NG; ++a) g[a] = 0.0;
+  for (int b = int(threadIdx.x); b < mi.tall_nblk; b += bs)
+#pragma unroll
+    for (int a = 0; a < NG; ++a) g[a] += gpart[int64_t(mi.tall_blk0 + b) * 10 + a];
+  block_sum_n<NG>(g, red);
   if (threadIdx.x == 0) {
-    auto G = [&](int k, int l) {  // Gram entry (k <= l) in the packed upper triangle
-      return g[k * R - k * (k - 1) / 2 + (l - k)];
-    };
-    double Rm[R][R], T[R][R];
-    bool kept[R];
-    for (int k = 0; k < R; ++k) {
-      const double before = sqrt(G(k, k));
-      double ss = G(k, k);
-      for (int l = 0; l < k; ++l) {
-        double r = 0.0;
-        if (kept[l]) {
-          r = G(l, k);
-          for (int m = 0; m < l; ++m) r -= Rm[m][l] * Rm[m][k];
-          r /= Rm[l][l];
-        }
-        Rm[l][k] = r;
-        ss -= r * r;
-      }
-      const double after = sqrt(ss > 0.0 ? ss : 0.0);
-      kept[k] = after > 0.0 && after > 1e-4 * before;
-      Rm[k][k] = after;
-      for (int l = 0; l < R; ++l) T[l][k] = 0.0;
-      if (kept[k]) {
-        T[k][k] = 1.0 / after;
-        for (int l = 0; l < k; ++l)
-          for (int m = 0; m < R; ++m) T[m][k] -= Rm[l][k] * T[m][l] / after;
-      }
-    }
+    double T[R][R];
+    gram_gs_coeffs<R>(g, T);
     double* out = tmat + int64_t(blockIdx.x) * 16;
     for (int l = 0; l < R; ++l)
       for (int k = 0; k < R; ++k) out[l * 4 + k] = T[l][k];
@@ -1193,7 +1198,8 @@ __global__ __launch_bounds__(kTallRows) void k_tall_apply(const TallBlk* __restr
   for (int k = 0; k < R; ++k) {
     double v = 0.0;
 #pragma unroll
-    for (int l = 0; l <= k; ++l) v += double(pb[l]) * T[l * 4 + k];
+    for (int l = 0; l <= k; ++l)
+      if (T[l * 4 + k] != 0.0) v += double(pb[l]) * T[l * 4 + k];  // a dropped column leaves no trace
     const int64_t o = mi.p_off + int64_t(i) * R + k;
     P[o] = float(v);
     if (P2 != nullptr) P2[o] = float(v);
