@@ -9,7 +9,9 @@
  *   previous step:
  *     M_w  = G_w + E_w                          error feedback
  *     P    = mean_w M_w Q                       one power-iteration half step, all-reduced
- *     P    = orthonormalise(P)                  modified Gram-Schmidt, column order
+ *     P    = orthonormalise(P)                  Gram-Schmidt, column order (taken in
+ *                                               P's r x r Gram space in fp64: the
+ *                                               modified Gram-Schmidt factor)
  *     Q    = mean_w M_w^T P                     second half step, all-reduced
  *     U    = P Q^T                              decompressed update
  *     E_w  = M_w - U                            error kept for the next step
