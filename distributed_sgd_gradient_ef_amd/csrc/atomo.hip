@@ -126,10 +126,24 @@ namespace atm {
 namespace {
 
 // ------------------------------------------------------------------ reductions
+// Sum over the 64 lanes by DPP moves (two quad permutes, two row rotates, two row
+// broadcasts), a few cycles each where the shuffle butterfly waits on the LDS crossbar
+// six times; lane 63 ends with the total, which every lane reads back.  All 64 lanes
+// must be active (every caller is in wave-uniform control flow).  Rows that a broadcast
+// does not write add zero.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_mov<0xB1, 0xf>(v);   // quad_perm [1,0,3,2]: pairs
+  v += dpp_mov<0x4E, 0xf>(v);   // quad_perm [2,3,0,1]: quads
+  v += dpp_mov<0x124, 0xf>(v);  // row_ror:4: two quads
+  v += dpp_mov<0x128, 0xf>(v);  // row_ror:8: the 16-lane row
+  v += dpp_mov<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3: rows 0+1, 2+3
+  v += dpp_mov<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3: lane 63 has all four
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // Sum over the workgroup; every thread gets the total (waves added in index order).
@@ -819,7 +833,22 @@ __global__ __launch_bounds__(kVecThreads) void at_vectors(const AtMat* __restric
 
 // ------------------------------------------------------------------ at_backxform
 // x = H_0 H_1 ... H_{k-3} y for each sent atom (one wave per atom), written as the unit
-// factor of the message: a when k == rows, b when k == cols.
+// factor of the message: a when k == rows, b when k == cols.  The reflectors are applied
+// from the last to the first; a ring of kBackAhead of them is kept in registers, and the
+// slot a reflector leaves is refilled at once with the one kBackAhead places further on,
+// so each load has kBackAhead - 1 reflector applications to arrive.
+constexpr int kBackAhead = 4;
+
+template <int KT>
+__device__ __forceinline__ void load_reflector(float (&v)[KT], const float* __restrict__ A, int k, int r, int lane) {
+  const float* row = A + refl_off(k, r < 0 ? 0 : r) - ((r < 0 ? 0 : r) + 1);
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    const int c = lane + 64 * t;
+    v[t] = (r >= 0 && c > r && c < k) ? row[c] : 0.f;
+  }
+}
+
 template <int KT>
 __device__ void backxform_body(const AtMat& M, const float* __restrict__ A, const float* __restrict__ tau,
                                const float* __restrict__ y_all, int cnt, float* __restrict__ atoms) {
@@ -834,35 +863,31 @@ __device__ void backxform_body(const AtMat& M, const float* __restrict__ A, cons
       const int c = lane + 64 * t;
       y[t] = c < k ? yin[c] : 0.f;
     }
-    float vn[KT];
-    int r = k - 3;
-    if (r >= 0) {
-      const float* row = A + refl_off(k, r) - (r + 1);
+    // ring slot d holds reflector r0 - d of the current group (zeros below reflector 0)
+    float ring[kBackAhead][KT], tring[kBackAhead];
 #pragma unroll
-      for (int t = 0; t < KT; ++t) {
-        const int c = lane + 64 * t;
-        vn[t] = (c > r && c < k) ? row[c] : 0.f;
-      }
+    for (int d = 0; d < kBackAhead; ++d) {
+      load_reflector<KT>(ring[d], A, k, k - 3 - d, lane);
+      tring[d] = k - 3 - d >= 0 ? tau[k - 3 - d] : 0.f;
     }
-    for (; r >= 0; --r) {
-      float v[KT];
+    for (int r0 = k - 3; r0 >= 0; r0 -= kBackAhead) {
 #pragma unroll
-      for (int t = 0; t < KT; ++t) v[t] = vn[t];
-      if (r > 0) {  // the next reflector, loaded ahead
-        const float* row = A + refl_off(k, r - 1) - r;
+      for (int d = 0; d < kBackAhead; ++d) {
+        const int r = r0 - d;
+        if (r < 0) break;  // wave-uniform
+        float v[KT];
 #pragma unroll
-        for (int t = 0; t < KT; ++t) {
-          const int c = lane + 64 * t;
-          vn[t] = (c > r - 1 && c < k) ? row[c] : 0.f;
-        }
+        for (int t = 0; t < KT; ++t) v[t] = ring[d][t];
+        const float tr = tring[d];
+        load_reflector<KT>(ring[d], A, k, r - kBackAhead, lane);
+        tring[d] = r - kBackAhead >= 0 ? tau[r - kBackAhead] : 0.f;
+        float part = 0.f;
+#pragma unroll
+        for (int t = 0; t < KT; ++t) part = fmaf(v[t], y[t], part);
+        const float f = tr * wave_sum(part);
+#pragma unroll
+        for (int t = 0; t < KT; ++t) y[t] = fmaf(-f, v[t], y[t]);
       }
-      const float tr = tau[r];
-      float part = 0.f;
-#pragma unroll
-      for (int t = 0; t < KT; ++t) part = fmaf(v[t], y[t], part);
-      const float f = tr * wave_sum(part);
-#pragma unroll
-      for (int t = 0; t < KT; ++t) y[t] = fmaf(-f, v[t], y[t]);
     }
     float* out = atoms + M.atom_off + int64_t(j) * stride + (M.left ? 0 : M.rows);
 #pragma unroll
