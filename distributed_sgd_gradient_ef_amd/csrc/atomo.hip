@@ -19,7 +19,8 @@
 //                 applies the previous rank-2 update and forms the product with the new
 //                 reflector; the last 190 rows are reduced in LDS
 //   at_eig        every eigenvalue of the tridiagonal matrix by bisection on Sturm
-//                 counts (one per thread); sigma_i = sqrt(max(eigenvalue, 0))
+//                 counts (one per thread, 128 per workgroup, so a large matrix spans
+//                 several compute units); sigma_i = sqrt(max(eigenvalue, 0))
 //   at_sample     the closed-form probabilities (the largest atoms saturate first),
 //                 the Bernoulli decisions x_i < p_i, and the list of sent atoms
 //   at_vectors    inverse iteration on the tridiagonal matrix (partial pivoting, float64)
@@ -59,7 +60,7 @@ constexpr int kTriThreads = 1024;
 // values would not fit in the 128 registers a lane has at 1024 threads)
 template <int KT>
 constexpr int tri_rows() { return KT >= 16 ? 1 : KT >= 8 ? 3 : KT >= 4 ? 5 : 8; }
-constexpr int kEigThreads = 1024;
+constexpr int kEigThreads = 128;  // eigenvalues per at_eig workgroup (grid.z splits a matrix)
 constexpr int kSampleThreads = 1024;
 constexpr int kVecThreads = 256;
 constexpr int kBackThreads = 256;
@@ -546,6 +547,7 @@ __global__ __launch_bounds__(kEigThreads) void at_eig(const AtMat* __restrict__ 
   const AtMat M = mats[blockIdx.x];
   const int64_t w = blockIdx.y;
   const int k = M.k, tid = threadIdx.x;
+  if (int(blockIdx.z) * kEigThreads >= k) return;  // the whole workgroup: no eigenvalue here
   const float* d = d_ws + w * sv_total + M.sv_off;
   const float* e = e_ws + w * sv_total + M.sv_off;
   float* lam = lam_ws + w * sv_total + M.sv_off;
@@ -572,7 +574,8 @@ __global__ __launch_bounds__(kEigThreads) void at_eig(const AtMat* __restrict__ 
   const float slack = 4.f * FLT_EPSILON * tnorm + 2.f * pivmin;
   const float abstol = 4.f * FLT_EPSILON * tnorm;
   __syncthreads();
-  for (int idx = tid; idx < k; idx += kEigThreads) {
+  for (int idx = int(blockIdx.z) * kEigThreads + tid; idx < min(k, int(blockIdx.z + 1) * kEigThreads);
+       idx += kEigThreads) {
     float a = glo - slack, b = ghi + slack;
     for (int it = 0; it < 96; ++it) {
       if (b - a <= abstol) break;
@@ -1435,7 +1438,10 @@ extern "C" psgd_status psgd_atomo_step(psgd_atomo_plan* plan, const float* grads
       }
       if (s != PSGD_OK) return s;
     }
-    if ((s = launch(plan, kEig, at_eig, mgrid, dim3(kEigThreads), st, M, static_cast<const float*>(dd),
+    // eigenvalues in slices of kEigThreads per workgroup: a large matrix's bisections
+    // spread over several compute units
+    const dim3 egrid(mgrid.x, mgrid.y, unsigned((64 * plan->tri_kt + kEigThreads - 1) / kEigThreads));
+    if ((s = launch(plan, kEig, at_eig, egrid, dim3(kEigThreads), st, M, static_cast<const float*>(dd),
                     static_cast<const float*>(ee), lam, sigma, svt)) != PSGD_OK)
       return s;
     if ((s = launch(plan, kSample, at_sample, mgrid, dim3(kSampleThreads), st, M, static_cast<const float*>(sigma),
