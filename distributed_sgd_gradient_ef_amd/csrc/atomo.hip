@@ -19,7 +19,7 @@
 //                 applies the previous rank-2 update and forms the product with the new
 //                 reflector; the last 190 rows are reduced in LDS
 //   at_eig        every eigenvalue of the tridiagonal matrix by bisection on Sturm
-//                 counts (one per thread, 128 per workgroup, so a large matrix spans
+//                 counts (one per thread, 64 per workgroup, so a large matrix spans
 //                 several compute units); sigma_i = sqrt(max(eigenvalue, 0))
 //   at_sample     the closed-form probabilities (the largest atoms saturate first),
 //                 the Bernoulli decisions x_i < p_i, and the list of sent atoms
@@ -60,7 +60,7 @@ constexpr int kTriThreads = 1024;
 // values would not fit in the 128 registers a lane has at 1024 threads)
 template <int KT>
 constexpr int tri_rows() { return KT >= 16 ? 1 : KT >= 8 ? 3 : KT >= 4 ? 5 : 8; }
-constexpr int kEigThreads = 128;  // eigenvalues per at_eig workgroup (grid.z splits a matrix)
+constexpr int kEigThreads = 64;  // eigenvalues per at_eig workgroup (grid.z splits a matrix)
 constexpr int kSampleThreads = 1024;
 constexpr int kVecThreads = 256;
 constexpr int kBackThreads = 256;
