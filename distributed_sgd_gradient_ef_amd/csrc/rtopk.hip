@@ -182,24 +182,37 @@ __device__ __forceinline__ uint32_t spread4(uint32_t x) {
   return x;
 }
 
+// Wave scans and sums by DPP moves: row shifts within each 16-lane row (lanes without a
+// source read zero), then the row broadcasts of lanes 15 and 31 into the rows after them.
+// All 64 lanes must be active; integer sums, so the result does not depend on the order.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, ROW_MASK, 0xf, true));
+}
+
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += dpp_u32<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_u32<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_u32<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_u32<0x118, 0xf>(v);  // row_shr:8: inclusive scan of each row
+  v += dpp_u32<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_u32<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_readlane(int(wave_incl_scan(v)), 63));
+}
+
 // Inclusive scan over the block (blockDim.x a multiple of 64, at most 1024); `lds`
 // holds 16 words.  Every thread must call it.
 __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* lds) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t n = __shfl_up(v, o, 64);
-    if (lane >= o) v += n;
-  }
+  v = wave_incl_scan(v);
   if (lane == 63) lds[wid] = v;
   __syncthreads();
   if (wid == 0) {
-    uint32_t t = lane < nw ? lds[lane] : 0u;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const uint32_t n = __shfl_up(t, o, 64);
-      if (lane >= o) t += n;
-    }
+    const uint32_t t = wave_incl_scan(lane < nw ? lds[lane] : 0u);
     if (lane < nw) lds[lane] = t;
   }
   __syncthreads();
@@ -211,8 +224,7 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* lds) {
 // Block total of v (every thread gets it).
 __device__ __forceinline__ uint32_t block_total(uint32_t v, uint32_t* lds) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  v = wave_sum(v);
   if (lane == 0) lds[wid] = v;
   __syncthreads();
   uint32_t t = 0;
@@ -221,21 +233,6 @@ __device__ __forceinline__ uint32_t block_total(uint32_t v, uint32_t* lds) {
   return t;
 }
 
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t n = __shfl_up(v, o, 64);
-    if (lane >= o) v += n;
-  }
-  return v;
-}
-
-__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
 
 // Set bits of `bits` in order, given the running rank of the first one: those whose
 // rank is below `limit` are returned.
