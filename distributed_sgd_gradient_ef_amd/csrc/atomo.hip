@@ -148,11 +148,13 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // Sum over the workgroup; every thread gets the total (waves added in index order).
-template <typename T>
+// GUARDED = false skips the barrier that protects `red` from the previous sum's readers:
+// for a caller that passes a buffer no thread has read since the last barrier.
+template <typename T, bool GUARDED = true>
 __device__ T block_sum(T v, T* red) {
   v = wave_sum(v);
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  __syncthreads();
+  if constexpr (GUARDED) __syncthreads();
   if (lane == 0) red[wid] = v;
   __syncthreads();
   T s = T(0);
@@ -342,7 +344,7 @@ struct TriShared {
   float V[2][kMaxK], Wv[2][kMaxK], P[kMaxK];
   float next[kMaxK];            // column q+1 as the pass of step q stores it
   float col[kTriWaves][kMaxK];  // per-wave column sums of the pass
-  float red[kTriWaves];
+  float red[kTriWaves], red2[kTriWaves];  // the step's two sums use one each
   float tail[kTailFloats];      // the trailing block, packed, once it fits
 };
 
@@ -373,7 +375,7 @@ __device__ __forceinline__ void tri_step(int q, int k, int base, float* __restri
   __syncthreads();
   float part = 0.f;
   for (int i = q + 2 + tid; i < k; i += kTriThreads) part = fmaf(vn[i], vn[i], part);
-  const float ss = block_sum(part, sh.red);
+  const float ss = block_sum<float, false>(part, sh.red);
   const float alpha = vn[q + 1];
   float tq = 0.f, beta = alpha, inv = 0.f;
   if (ss != 0.f) {
@@ -460,7 +462,7 @@ __device__ __forceinline__ void tri_step(int q, int k, int base, float* __restri
     P[r] = pr;
     part2 = fmaf(pr, vn[r], part2);
   }
-  const float vav = block_sum(part2, sh.red);  // v^T A v
+  const float vav = block_sum<float, false>(part2, sh.red2);  // v^T A v
   const float half = 0.5f * tq * tq * vav;
   for (int r = c0 + tid; r < k; r += kTriThreads) wn[r] = tq * P[r] - half * vn[r];
   __syncthreads();
