@@ -373,10 +373,12 @@ __device__ __forceinline__ void tri_step(int q, int k, int base, float* __restri
     vn[i] = (fresh ? at(i, q) : sh.next[i]) - vp[i] * wq - wp[i] * vq;
   if (tid == 0) d[q] = (fresh ? at(q, q) : sh.next[q]) - 2.f * vq * wq;
   __syncthreads();
+  // alpha is read before the sum's barrier, so that once the sum returns nobody reads vn
+  // any more and it can be rescaled in place
+  const float alpha = vn[q + 1];
   float part = 0.f;
   for (int i = q + 2 + tid; i < k; i += kTriThreads) part = fmaf(vn[i], vn[i], part);
   const float ss = block_sum<float, false>(part, sh.red);
-  const float alpha = vn[q + 1];
   float tq = 0.f, beta = alpha, inv = 0.f;
   if (ss != 0.f) {
     const float mu = sqrtf(fmaf(alpha, alpha, ss));
@@ -384,7 +386,6 @@ __device__ __forceinline__ void tri_step(int q, int k, int base, float* __restri
     tq = (beta - alpha) / beta;
     inv = 1.f / (alpha - beta);
   }
-  __syncthreads();  // everyone has read alpha before vn is rescaled
   float* rq = Rf + refl_off(k, q) - (q + 1);
   for (int i = q + 1 + tid; i < k; i += kTriThreads) {
     const float v = (i == q + 1) ? 1.f : vn[i] * inv;
