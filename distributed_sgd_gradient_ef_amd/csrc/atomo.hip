@@ -735,7 +735,7 @@ __global__ __launch_bounds__(kVecThreads) void at_vectors(const AtMat* __restric
         if (fabsf(cd) >= fabsf(sub)) {
           float piv = cd;
           if (fabsf(piv) < tiny) piv = piv < 0.f ? -tiny : tiny;
-          const float r = 1.f / piv;
+          const float r = __builtin_amdgcn_rcpf(piv);
           const float m = sub * r;
           u0[t] = r;
           u1[t] = c1;
@@ -745,8 +745,9 @@ __global__ __launch_bounds__(kVecThreads) void at_vectors(const AtMat* __restric
           cd = nd - m * c1;
           c1 = nsup - m * c2;
         } else {
-          const float m = cd / sub;
-          u0[t] = 1.f / sub;
+          const float rs = __builtin_amdgcn_rcpf(sub);
+          const float m = cd * rs;
+          u0[t] = rs;
           u1[t] = nd;
           u2[t] = nsup;
           ml[t] = m;
@@ -757,7 +758,7 @@ __global__ __launch_bounds__(kVecThreads) void at_vectors(const AtMat* __restric
         c2 = 0.f;
       }
       if (fabsf(cd) < tiny) cd = cd < 0.f ? -tiny : tiny;
-      u0[k - 1] = 1.f / cd;
+      u0[k - 1] = __builtin_amdgcn_rcpf(cd);
       u1[k - 1] = 0.f;
       u2[k - 1] = 0.f;
     }
