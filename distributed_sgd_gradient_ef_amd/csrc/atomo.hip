@@ -703,6 +703,7 @@ __global__ __launch_bounds__(kVecThreads) void at_vectors(const AtMat* __restric
   float* y_all = Y + w * gram_ws + M.b_off;  // sent atom j's vector at j * k
   __shared__ float sd[kMaxK], se[kMaxK], dots[kMaxK];
   __shared__ float red[kWaves];
+  __shared__ float vscale[8];
   __shared__ __align__(16) unsigned char pool[kVecLdsBytes];
   const int ns = vec_slots(k);
   float* f0 = reinterpret_cast<float*>(pool);  // 1 / pivot
@@ -798,10 +799,12 @@ __global__ __launch_bounds__(kVecThreads) void at_vectors(const AtMat* __restric
           z1 = z;
           big = fmaxf(big, fabsf(z));
         }
-        // rescale so the next round cannot overflow
-        const float sc = big > 0.f ? 1.f / big : 0.f;
-        for (int t = 0; t < k; ++t) y[t] *= sc;
+        // the scale that keeps the next round from overflowing, applied below by the
+        // whole workgroup
+        vscale[s] = big > 0.f ? 1.f / big : 0.f;
       }
+      __syncthreads();
+      for (int e2 = tid; e2 < ng * k; e2 += kVecThreads) fy[e2] *= vscale[e2 / k];
       __syncthreads();
       for (int s = 0; s < ng; ++s) {
         const int j = j0 + s;
