@@ -849,13 +849,19 @@ __global__ __launch_bounds__(kVecThreads) void at_vectors(const AtMat* __restric
 // so each load has kBackAhead - 1 reflector applications to arrive.
 constexpr int kBackAhead = 4;
 
+// Every lane loads unconditionally from a clamped column (c <= r reaches back into the
+// previous reflector, or the last element of the packed triangle for r = 0; c >= k reads
+// column k - 1: all inside the problem's k * k floats) and keeps zero where the reflector
+// has no entry, so the loads need no branches.
 template <int KT>
 __device__ __forceinline__ void load_reflector(float (&v)[KT], const float* __restrict__ A, int k, int r, int lane) {
-  const float* row = A + refl_off(k, r < 0 ? 0 : r) - ((r < 0 ? 0 : r) + 1);
+  const int rr = r < 0 ? 0 : r;
+  const float* row = A + refl_off(k, rr) - (rr + 1);
 #pragma unroll
   for (int t = 0; t < KT; ++t) {
     const int c = lane + 64 * t;
-    v[t] = (r >= 0 && c > r && c < k) ? row[c] : 0.f;
+    const float x = row[c < k ? c : k - 1];
+    v[t] = (r >= 0 && c > r && c < k) ? x : 0.f;
   }
 }
 
