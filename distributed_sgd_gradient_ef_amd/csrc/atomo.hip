@@ -337,15 +337,20 @@ __global__ __launch_bounds__(kGramThreads) void at_gram(const GramTile* __restri
 // for c < r; a lane keeps the latter for its own columns in registers, and the waves'
 // column sums are added in wave order.  Once the trailing block fits, it moves to LDS.
 constexpr int kTriWaves = kTriThreads / 64;
-constexpr int kTailRows = 190;                            // largest trailing block kept in LDS
-constexpr int kTailFloats = kTailRows * (kTailRows + 1) / 2;
+// LDS per problem: the reflector and product vectors and the per-wave column sums sized
+// for the width class (64 KT columns), and as large a packed trailing block as the rest of
+// the 160 KB allows (width classes up to 4, k <= 256, hold the whole matrix).
+template <int KT>
+constexpr int tail_rows() { return KT >= 16 ? 190 : KT >= 8 ? 240 : 64 * KT; }
 
+template <int KT>
 struct TriShared {
-  float V[2][kMaxK], Wv[2][kMaxK], P[kMaxK];
-  float next[kMaxK];            // column q+1 as the pass of step q stores it
-  float col[kTriWaves][kMaxK];  // per-wave column sums of the pass
+  static constexpr int N = 64 * KT;
+  float V[2][N], Wv[2][N], P[N];
+  float next[N];            // column q+1 as the pass of step q stores it
+  float col[kTriWaves][N];  // per-wave column sums of the pass
   float red[kTriWaves], red2[kTriWaves];  // the step's two sums use one each
-  float tail[kTailFloats];      // the trailing block, packed, once it fits
+  float tail[tail_rows<KT>() * (tail_rows<KT>() + 1) / 2];  // the trailing block, packed, once it fits
 };
 
 // one Householder step q on packed storage: global (LOCAL = false) or the LDS copy of the
@@ -353,7 +358,7 @@ struct TriShared {
 template <int KT, bool LOCAL>
 __device__ __forceinline__ void tri_step(int q, int k, int base, float* __restrict__ A, float* __restrict__ Rf,
                                          float* __restrict__ tau, float* __restrict__ d, float* __restrict__ e,
-                                         TriShared& sh, int cur) {
+                                         TriShared<KT>& sh, int cur) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int kWaves = kTriWaves;
   auto at = [&](int r, int c) -> float& {
@@ -471,7 +476,7 @@ __device__ __forceinline__ void tri_step(int q, int k, int base, float* __restri
 
 template <int KT>
 __device__ void tridiag_body(const AtMat& M, float* __restrict__ A, float* __restrict__ tau, float* __restrict__ d,
-                             float* __restrict__ e, TriShared& sh) {
+                             float* __restrict__ e, TriShared<KT>& sh) {
   const int k = M.k;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < k; i += kTriThreads) {
@@ -481,7 +486,7 @@ __device__ void tridiag_body(const AtMat& M, float* __restrict__ A, float* __res
   __syncthreads();
   int cur = 0;
   // global storage while the trailing block (rows and columns >= q) is too large for LDS
-  const int qlocal = max(0, k - kTailRows);
+  const int qlocal = max(0, k - tail_rows<KT>());
   int q = 0;
   for (; q + 2 < k && q < qlocal; ++q, cur ^= 1) tri_step<KT, false>(q, k, 0, A, A, tau, d, e, sh, cur);
   // copy the block from row/column q on into LDS, then continue there
@@ -517,7 +522,7 @@ __global__ __launch_bounds__(kTriThreads) void at_tridiag(const int32_t* __restr
   float* tau = tau_ws + w * sv_total + M.sv_off;
   float* d = d_ws + w * sv_total + M.sv_off;
   float* e = e_ws + w * sv_total + M.sv_off;
-  __shared__ TriShared sh;
+  __shared__ TriShared<KT> sh;
   tridiag_body<KT>(M, A, tau, d, e, sh);
 }
 
