@@ -17,7 +17,10 @@ each worker's error uses its own Q_w).  `value` is the --primary one.
 A second compressor is timed beside it ("rtopk" in the output): rTop-k with error
 feedback on the same shapes and W = 16, 1% of each tensor sent, drawn from its top 2%
 (psgd_rtopk_step: EF add, top-set selection, random subset from seeded ranks, sparse
-lists, new errors, dense mean update).
+lists, new errors, dense mean update), and a third ("atomo"): Spectral-ATOMO on the same
+shapes and workers with budget s = 2 (psgd_atomo_step: Gram matrices, tridiagonalisation,
+eigenvalues, closed-form probabilities, Bernoulli draws from seeded uniforms, inverse
+iteration and back-transformation for the sent atoms, their second factors, the mean).
 
 Prints one JSON line:
   value          gradient GB/s = W * numel * 4 bytes / step time (whole job, one GPU)
