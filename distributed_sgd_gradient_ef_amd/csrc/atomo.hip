@@ -201,9 +201,9 @@ __global__ __launch_bounds__(kGramThreads) void at_gram(const GramTile* __restri
                                                         const AtMat* __restrict__ mats,
                                                         const float* __restrict__ G, int64_t ld,
                                                         float* __restrict__ gram, int64_t gram_ws) {
-  const GramTile t = tiles[blockIdx.x];
-  const AtMat M = mats[t.mat];
-  const int w = blockIdx.y;
+  const GramTile t = tiles[blockIdx.y];  // grid.x walks the workers: a tile of every worker
+  const AtMat M = mats[t.mat];            // is dispatched before the next tile
+  const int w = blockIdx.x;
   const float* g = G + int64_t(w) * ld + M.offset;
   float* B = gram + int64_t(w) * gram_ws + M.b_off;
   const int k = M.k, cols = M.cols;
@@ -1257,6 +1257,17 @@ extern "C" psgd_status psgd_atomo_plan_create(const psgd_layer* layers, int32_t 
         for (int c = 0; c < m.cols; c += kAtUpdThreads)
           plan->utiles.push_back(AtUpdTile{0, 0, int32_t(mi), r, std::min(m.rows, r + kAtUpdRows), c});
     }
+    // the longest contractions first, so that they do not form the launch's tail (each
+    // tile writes its own block of the Gram matrix; the order changes no result)
+    std::stable_sort(plan->gtiles.begin(), plan->gtiles.end(), [&](const GramTile& a, const GramTile& b) {
+      const AtMat& ma = plan->mats[size_t(a.mat)];
+      const AtMat& mb = plan->mats[size_t(b.mat)];
+      return (ma.left ? ma.cols : ma.rows) > (mb.left ? mb.cols : mb.rows);
+    });
+    if (plan->gtiles.size() > 65535) {  // the Gram launch's second grid dimension
+      delete plan;
+      return fail(PSGD_ERR_UNSUPPORTED, std::string(fn) + ": more than 65535 Gram tiles (128 x 128) in one plan");
+    }
     for (size_t mi = 0; mi < plan->mats.size(); ++mi) {
       plan->tri_list.push_back(int32_t(mi));
       plan->tri_kt = std::max(plan->tri_kt, tri_class(plan->mats[mi].k));
@@ -1442,7 +1453,7 @@ extern "C" psgd_status psgd_atomo_step(psgd_atomo_plan* plan, const float* grads
   const AtMat* M = dt.mats;
 
   if (nm > 0) {
-    if ((s = launch(plan, kGram, at_gram, dim3(unsigned(plan->gtiles.size()), unsigned(W)), dim3(kGramThreads), st,
+    if ((s = launch(plan, kGram, at_gram, dim3(unsigned(W), unsigned(plan->gtiles.size())), dim3(kGramThreads), st,
                     static_cast<const GramTile*>(dt.gtiles), M, grads, ld, gram, gws)) != PSGD_OK)
       return s;
     {
