@@ -516,8 +516,10 @@ __global__ __launch_bounds__(kTriThreads) void at_tridiag(const int32_t* __restr
                                                           int64_t gram_ws, float* __restrict__ tau_ws,
                                                           float* __restrict__ d_ws, float* __restrict__ e_ws,
                                                           int64_t sv_total) {
-  const AtMat M = mats[list[blockIdx.x]];
-  const int64_t w = blockIdx.y;
+  // grid.x walks the workers, grid.y the matrices in decreasing k: every worker's largest
+  // problems are dispatched first
+  const AtMat M = mats[list[blockIdx.y]];
+  const int64_t w = blockIdx.x;
   float* A = gram + w * gram_ws + M.b_off;
   float* tau = tau_ws + w * sv_total + M.sv_off;
   float* d = d_ws + w * sv_total + M.sv_off;
@@ -1458,12 +1460,13 @@ extern "C" psgd_status psgd_atomo_step(psgd_atomo_plan* plan, const float* grads
       return s;
     {
       const int32_t* list = dt.tri_list;
+      const dim3 tgrid(mgrid.y, mgrid.x);  // (workers, matrices)
       switch (plan->tri_kt) {
-        case 16: s = launch(plan, kTridiag, at_tridiag<16>, mgrid, dim3(kTriThreads), st, list, M, gram, gws, tau, dd, ee, svt); break;
-        case 8: s = launch(plan, kTridiag, at_tridiag<8>, mgrid, dim3(kTriThreads), st, list, M, gram, gws, tau, dd, ee, svt); break;
-        case 4: s = launch(plan, kTridiag, at_tridiag<4>, mgrid, dim3(kTriThreads), st, list, M, gram, gws, tau, dd, ee, svt); break;
-        case 2: s = launch(plan, kTridiag, at_tridiag<2>, mgrid, dim3(kTriThreads), st, list, M, gram, gws, tau, dd, ee, svt); break;
-        default: s = launch(plan, kTridiag, at_tridiag<1>, mgrid, dim3(kTriThreads), st, list, M, gram, gws, tau, dd, ee, svt); break;
+        case 16: s = launch(plan, kTridiag, at_tridiag<16>, tgrid, dim3(kTriThreads), st, list, M, gram, gws, tau, dd, ee, svt); break;
+        case 8: s = launch(plan, kTridiag, at_tridiag<8>, tgrid, dim3(kTriThreads), st, list, M, gram, gws, tau, dd, ee, svt); break;
+        case 4: s = launch(plan, kTridiag, at_tridiag<4>, tgrid, dim3(kTriThreads), st, list, M, gram, gws, tau, dd, ee, svt); break;
+        case 2: s = launch(plan, kTridiag, at_tridiag<2>, tgrid, dim3(kTriThreads), st, list, M, gram, gws, tau, dd, ee, svt); break;
+        default: s = launch(plan, kTridiag, at_tridiag<1>, tgrid, dim3(kTriThreads), st, list, M, gram, gws, tau, dd, ee, svt); break;
       }
       if (s != PSGD_OK) return s;
     }
