@@ -19,8 +19,9 @@
 //                 applies the previous rank-2 update and forms the product with the new
 //                 reflector; the last 190 rows are reduced in LDS
 //   at_eig        every eigenvalue of the tridiagonal matrix by bisection on Sturm
-//                 counts (one per thread, 64 per workgroup, so a large matrix spans
-//                 several compute units); sigma_i = sqrt(max(eigenvalue, 0))
+//                 counts: 64 per workgroup (one per lane; a large matrix spans several
+//                 compute units), four probe points per round (one per wave);
+//                 sigma_i = sqrt(max(eigenvalue, 0))
 //   at_sample     the closed-form probabilities (the largest atoms saturate first),
 //                 the Bernoulli decisions x_i < p_i, and the list of sent atoms
 //   at_vectors    inverse iteration on the tridiagonal matrix (partial pivoting, float64)
@@ -60,7 +61,9 @@ constexpr int kTriThreads = 1024;
 // values would not fit in the 128 registers a lane has at 1024 threads)
 template <int KT>
 constexpr int tri_rows() { return KT >= 16 ? 1 : KT >= 8 ? 3 : KT >= 4 ? 5 : 8; }
-constexpr int kEigThreads = 64;  // eigenvalues per at_eig workgroup (grid.z splits a matrix)
+constexpr int kEigSlots = 64;    // eigenvalues per at_eig workgroup, one per lane (grid.z splits a matrix)
+constexpr int kEigWaves = 4;     // probe points per round, one per wave: each round leaves a fifth
+constexpr int kEigThreads = 64 * kEigWaves;
 constexpr int kSampleThreads = 1024;
 constexpr int kVecThreads = 256;
 constexpr int kBackThreads = 256;
@@ -557,7 +560,7 @@ __global__ __launch_bounds__(kEigThreads) void at_eig(const AtMat* __restrict__ 
   const AtMat M = mats[blockIdx.x];
   const int64_t w = blockIdx.y;
   const int k = M.k, tid = threadIdx.x;
-  if (int(blockIdx.z) * kEigThreads >= k) return;  // the whole workgroup: no eigenvalue here
+  if (int(blockIdx.z) * kEigSlots >= k) return;  // the whole workgroup: no eigenvalue here
   const float* d = d_ws + w * sv_total + M.sv_off;
   const float* e = e_ws + w * sv_total + M.sv_off;
   float* lam = lam_ws + w * sv_total + M.sv_off;
@@ -584,16 +587,37 @@ __global__ __launch_bounds__(kEigThreads) void at_eig(const AtMat* __restrict__ 
   const float slack = 4.f * FLT_EPSILON * tnorm + 2.f * pivmin;
   const float abstol = 4.f * FLT_EPSILON * tnorm;
   __syncthreads();
-  for (int idx = int(blockIdx.z) * kEigThreads + tid; idx < min(k, int(blockIdx.z + 1) * kEigThreads);
-       idx += kEigThreads) {
-    float a = glo - slack, b = ghi + slack;
-    for (int it = 0; it < 96; ++it) {
-      if (b - a <= abstol) break;
-      const float mid = 0.5f * (a + b);
-      if (mid <= a || mid >= b) break;
-      if (sturm_below(sd, se2, k, mid, pivmin) > idx) b = mid;
-      else a = mid;
+  // multisection: lane l owns eigenvalue idx; in each round wave p counts the eigenvalues
+  // below a + (p + 1) h, h = (b - a) / (kEigWaves + 1), and every wave narrows (a, b) to
+  // the fifth between the last probe with at most idx below it and the next one, from the
+  // same counts with the same arithmetic, so all waves hold the same interval
+  __shared__ int cnt[kEigWaves][64];
+  const int lane = tid & 63, wave = tid >> 6;
+  const int idx = int(blockIdx.z) * kEigSlots + lane;
+  const bool mine = idx < k;
+  float a = glo - slack, b = ghi + slack;
+  for (int it = 0; it < 96; ++it) {
+    const float h = (b - a) * (1.f / float(kEigWaves + 1));
+    float xs[kEigWaves];
+    bool split = true;
+#pragma unroll
+    for (int p = 0; p < kEigWaves; ++p) {
+      xs[p] = a + h * float(p + 1);
+      split = split && xs[p] > (p == 0 ? a : xs[p - 1]);
     }
+    split = split && xs[kEigWaves - 1] < b;
+    const bool active = mine && b - a > abstol && split;
+    if (!__syncthreads_or(active)) break;  // the same decision in every thread
+    cnt[wave][lane] = active ? sturm_below(sd, se2, k, xs[wave], pivmin) : 0;
+    __syncthreads();
+    if (active) {
+      int p = 0;
+      while (p < kEigWaves && cnt[p][lane] <= idx) ++p;
+      if (p > 0) a = xs[p - 1];
+      if (p < kEigWaves) b = xs[p];
+    }
+  }
+  if (mine && wave == 0) {
     const float l = 0.5f * (a + b);
     lam[idx] = l;
     sig[k - 1 - idx] = sqrtf(fmaxf(l, 0.f));
@@ -1470,9 +1494,9 @@ extern "C" psgd_status psgd_atomo_step(psgd_atomo_plan* plan, const float* grads
       }
       if (s != PSGD_OK) return s;
     }
-    // eigenvalues in slices of kEigThreads per workgroup: a large matrix's bisections
+    // eigenvalues in slices of kEigSlots per workgroup: a large matrix's bisections
     // spread over several compute units
-    const dim3 egrid(mgrid.x, mgrid.y, unsigned((64 * plan->tri_kt + kEigThreads - 1) / kEigThreads));
+    const dim3 egrid(mgrid.x, mgrid.y, unsigned((64 * plan->tri_kt + kEigSlots - 1) / kEigSlots));
     if ((s = launch(plan, kEig, at_eig, egrid, dim3(kEigThreads), st, M, static_cast<const float*>(dd),
                     static_cast<const float*>(ee), lam, sigma, svt)) != PSGD_OK)
       return s;
