@@ -980,9 +980,9 @@ __global__ __launch_bounds__(kFactorThreads) void at_factor(const FactorTile* __
                                                             const int32_t* __restrict__ count,
                                                             float* __restrict__ atoms, int64_t sv_total,
                                                             int64_t atom_total, int32_t n_mats) {
-  const FactorTile t = tiles[blockIdx.x];
-  const AtMat M = mats[t.mat];
-  const int64_t w = blockIdx.y;
+  const FactorTile t = tiles[blockIdx.y];  // grid.x walks the workers, grid.y the tiles,
+  const AtMat M = mats[t.mat];              // largest first
+  const int64_t w = blockIdx.x;
   const int cnt = count[w * n_mats + M.mat_index];
   if (cnt == 0) return;
   const int n = M.rows, m = M.cols, k = M.k;
@@ -1294,6 +1294,18 @@ extern "C" psgd_status psgd_atomo_plan_create(const psgd_layer* layers, int32_t 
       delete plan;
       return fail(PSGD_ERR_UNSUPPORTED, std::string(fn) + ": more than 65535 Gram tiles (128 x 128) in one plan");
     }
+    // the largest factor tiles first (rows x columns each covers), for the same reason
+    std::stable_sort(plan->ftiles.begin(), plan->ftiles.end(), [&](const FactorTile& a, const FactorTile& b) {
+      const AtMat& ma = plan->mats[size_t(a.mat)];
+      const AtMat& mb = plan->mats[size_t(b.mat)];
+      const int64_t wa = int64_t(a.end - a.begin) * (ma.left ? ma.rows : ma.cols);
+      const int64_t wb = int64_t(b.end - b.begin) * (mb.left ? mb.rows : mb.cols);
+      return wa > wb;
+    });
+    if (plan->ftiles.size() > 65535) {  // the factor launch's second grid dimension
+      delete plan;
+      return fail(PSGD_ERR_UNSUPPORTED, std::string(fn) + ": more than 65535 factor tiles in one plan");
+    }
     for (size_t mi = 0; mi < plan->mats.size(); ++mi) {
       plan->tri_list.push_back(int32_t(mi));
       plan->tri_kt = std::max(plan->tri_kt, tri_class(plan->mats[mi].k));
@@ -1512,7 +1524,7 @@ extern "C" psgd_status psgd_atomo_step(psgd_atomo_plan* plan, const float* grads
                     static_cast<const float*>(tau), static_cast<const float*>(Y),
                     static_cast<const int32_t*>(count), atoms, gws, svt, att, nmats)) != PSGD_OK)
       return s;
-    if ((s = launch(plan, kFactor, at_factor, dim3(unsigned(plan->ftiles.size()), unsigned(W)),
+    if ((s = launch(plan, kFactor, at_factor, dim3(unsigned(W), unsigned(plan->ftiles.size())),
                     dim3(kFactorThreads), st, static_cast<const FactorTile*>(dt.ftiles), M, grads, ld,
                     static_cast<const float*>(prob), static_cast<const int32_t*>(index),
                     static_cast<const int32_t*>(count), atoms, svt, att, nmats)) != PSGD_OK)

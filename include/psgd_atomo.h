@@ -95,7 +95,9 @@ typedef struct psgd_atomo_sizes {
  * finite), W = n_workers in 1..65535 and float32 gradients.  Matrices with
  * min(rows, cols) > PSGD_ATOMO_MAX_K are rejected (PSGD_ERR_UNSUPPORTED), and so is a
  * plan with more than 65535 Gram tiles (the sum over matrices of T (T + 1) / 2 with
- * T = ceil(min(rows, cols) / 128)).  flags must be 0.  Host only. */
+ * T = ceil(min(rows, cols) / 128)) or more than 65535 factor tiles (a matrix with
+ * rows <= cols has ceil(cols / 256) of them, any other ceil(rows / 16)).  flags must be
+ * 0.  Host only. */
 psgd_status psgd_atomo_plan_create(const psgd_layer* layers, int32_t n_layers, double budget, int32_t n_workers,
                                    uint32_t flags, psgd_atomo_plan** out);
 psgd_status psgd_atomo_plan_sizes(const psgd_atomo_plan* plan, psgd_atomo_sizes* out);
