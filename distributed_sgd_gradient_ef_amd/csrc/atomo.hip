@@ -54,7 +54,7 @@ namespace atm {
 
 constexpr int kMaxK = PSGD_ATOMO_MAX_K;
 constexpr int kGramTile = 128;
-constexpr int kGramKC = 32;
+constexpr int kGramKC = 16;
 constexpr int kGramThreads = 256;
 constexpr int kTriThreads = 1024;
 // rows per wave per batch of the trailing-block pass (fewer for the widest rows, whose
