@@ -1,5 +1,5 @@
-"""Build libpsgd.so (host plan code + gfx950 HIP kernels of the PowerSGD and rTop-k
-compressors) in-tree with hipcc.
+"""Build libpsgd.so (host plan code + gfx950 HIP kernels of the PowerSGD, rTop-k and
+Spectral-ATOMO compressors) in-tree with hipcc.
 
     python -m distributed_sgd_gradient_ef_amd.build
 

@@ -24,7 +24,7 @@
 //                 sigma_i = sqrt(max(eigenvalue, 0))
 //   at_sample     the closed-form probabilities (the largest atoms saturate first),
 //                 the Bernoulli decisions x_i < p_i, and the list of sent atoms
-//   at_vectors    inverse iteration on the tridiagonal matrix (partial pivoting, float64)
+//   at_vectors    inverse iteration on the tridiagonal matrix (partial pivoting, float32)
 //                 for each sent atom, orthogonalised against the problem's earlier sent
 //                 atoms after every solve
 //   at_backxform  the sent eigenvectors back through the reflectors: the unit factor

@@ -11,7 +11,7 @@ import pytest
 from distributed_sgd_gradient_ef_amd import psgd
 from distributed_sgd_gradient_ef_amd import workloads as WL
 
-pytestmark = pytest.mark.skipif(not os.path.exists(psgd.LIB_PATH), reason="libpsgd.so not built")
+pytestmark = pytest.mark.usefixtures("built_library")
 
 SHAPES = [(64, 27), (1, 64), (10, 512), (3, 5)]
 TOPS = [35, 2, 103, 15]
