@@ -37,6 +37,8 @@
 
 #include <cmath>
 #include <cstdint>
+#include <map>
+#include <mutex>
 #include <string>
 #include <type_traits>
 
@@ -828,15 +830,13 @@ __device__ __forceinline__ TileRow tile_row(int rgroups) {
 // RP > 1 (small compile-time worker counts): each workgroup takes RP rows of its tile, or
 // RP flat chunks, and rgroups is the tile's row count over RP.
 template <typename GT, int WT, int FP, int RP>
-__global__ __launch_bounds__(kStreamThreads) void k_first(const UpdTile* __restrict__ tiles, int32_t ntiles,
-                                                     int32_t rgroups, const MatInfo* __restrict__ mats,
-                                                     const GT* __restrict__ G, float* __restrict__ E,
-                                                     const float* __restrict__ ebar,
-                                                     const float* __restrict__ Pprev,
-                                                     const float* __restrict__ Qprev,
-                                                     const float* __restrict__ Qin, float* __restrict__ Mbar,
-                                                     float* __restrict__ Ppart, int W, int64_t ld, int R,
-                                                     float inv_w, int offset_valid) {
+__device__ __forceinline__ void first_body(const UpdTile* __restrict__ tiles, int32_t ntiles, int32_t rgroups,
+                                           const MatInfo* __restrict__ mats, const GT* __restrict__ G,
+                                           float* __restrict__ E, const float* __restrict__ ebar,
+                                           const float* __restrict__ Pprev, const float* __restrict__ Qprev,
+                                           const float* __restrict__ Qin, float* __restrict__ Mbar,
+                                           float* __restrict__ Ppart, int W, int64_t ld, int R, float inv_w,
+                                           int offset_valid) {
   const TileRow tr = tile_row(rgroups);
   if (tr.tile >= ntiles) return;
   const UpdTile t = tiles[tr.tile];
@@ -873,6 +873,46 @@ __global__ __launch_bounds__(kStreamThreads) void k_first(const UpdTile* __restr
     default: first_matrix_tile<1, GT, WT, FP>(t, mi, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, W, ld, R, inv_w,
                                      offset_valid, rb); break;
   }
+}
+
+// Cross-step state (the carried error mean, or the deferred offset) is used when the
+// host allows it (use_state: the plan's previous step ran on these buffers and nothing
+// reset it since) and the workspace's state word holds this plan's key for this error
+// buffer (written by the last pass of the step that left the state; cleared by
+// in-place materialisation and by the stream-ordered reset).  The word is read on the
+// device, so a step replayed from a captured graph still sees what happened between
+// replays.  Without valid state, a carry-mode pass reads every error (the plain form)
+// and a deferred-mode pass subtracts nothing.
+__device__ __forceinline__ int state_valid(const uint64_t* state, uint64_t key, int use_state) {
+  return use_state != 0 && state != nullptr && *state == key;
+}
+
+template <typename GT, int WT, int FP, int RP>
+__global__ __launch_bounds__(kStreamThreads) void k_first(const UpdTile* __restrict__ tiles, int32_t ntiles,
+                                                     int32_t rgroups, const MatInfo* __restrict__ mats,
+                                                     const GT* __restrict__ G, float* __restrict__ E,
+                                                     const float* __restrict__ ebar,
+                                                     const float* __restrict__ Pprev,
+                                                     const float* __restrict__ Qprev,
+                                                     const float* __restrict__ Qin, float* __restrict__ Mbar,
+                                                     float* __restrict__ Ppart, int W, int64_t ld, int R,
+                                                     float inv_w, const uint64_t* __restrict__ state, uint64_t key,
+                                                     int use_state) {
+  const int valid = state_valid(state, key, use_state);
+  if constexpr (FP == kFpCarry) {
+    if (!valid) {
+      first_body<GT, WT, kFpMean, RP>(tiles, ntiles, rgroups, mats, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, W,
+                                      ld, R, inv_w, 0);
+      return;
+    }
+  }
+  first_body<GT, WT, FP, RP>(tiles, ntiles, rgroups, mats, G, E, ebar, Pprev, Qprev, Qin, Mbar, Ppart, W, ld, R,
+                             inv_w, FP == kFpDefer ? valid : 0);
+}
+
+// One thread stores `value` into the workspace's state word (a plain vector store).
+__global__ __launch_bounds__(64) void k_state_store(uint64_t* __restrict__ state, uint64_t value) {
+  if (threadIdx.x == 0) *state = value;
 }
 
 // ------------------------------------------------------------------ extra power iterations
@@ -1429,7 +1469,8 @@ __global__ __launch_bounds__(kStreamThreads) void k_apply(
     float* __restrict__ E, const float* __restrict__ Mbar, const float* __restrict__ P,
     const float* __restrict__ Q, const float* __restrict__ Qw, int64_t q_ws, float* __restrict__ update,
     float* __restrict__ mom, float* __restrict__ x, float* __restrict__ ebar, int W, int64_t ld, int R, int mode,
-    float lr, float mu, float inv_w) {
+    float lr, float mu, float inv_w, uint64_t* __restrict__ state, uint64_t key) {
+  if (state != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *state = key;
   const TileRow tr = tile_row(rgroups);
   if (tr.tile >= ntiles) return;
   const UpdTile t = tiles[tr.tile];
@@ -1523,7 +1564,9 @@ template <int R>
 __global__ __launch_bounds__(kUpdThreads) void k_update(
     const UpdTile* __restrict__ tiles, const MatInfo* __restrict__ mats, const float* __restrict__ Mbar,
     const float* __restrict__ P, const float* __restrict__ Q, float* __restrict__ update,
-    float* __restrict__ mom, float* __restrict__ x, int mode, float lr, float mu) {
+    float* __restrict__ mom, float* __restrict__ x, int mode, float lr, float mu, uint64_t* __restrict__ state,
+    uint64_t key) {
+  if (state != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *state = key;
   const UpdTile t = tiles[blockIdx.x];
   if (t.mat < 0) {
     const int64_t c = t.begin + int64_t(threadIdx.x) * 4;
@@ -1598,7 +1641,8 @@ __device__ __forceinline__ void materialize_flat_tile(const UpdTile& t, const Ma
 __global__ __launch_bounds__(kStreamThreads) void k_materialize(
     const UpdTile* __restrict__ tiles, const MatInfo* __restrict__ mats, const float* E, float* out,
     const float* __restrict__ Pprev, const float* __restrict__ Qprev, int W, int64_t ld, int R,
-    int offset_valid) {
+    const uint64_t* __restrict__ state, uint64_t key, int use_state) {
+  const int offset_valid = state_valid(state, key, use_state);
   const UpdTile t = tiles[blockIdx.x];
   if (t.mat < 0) return;
   const MatInfo mi = mats[t.mat];
@@ -1628,34 +1672,28 @@ psgd_status hip_fail(const char* what, hipError_t e) {
 
 uint64_t align256(uint64_t x) { return (x + 255) / 256 * 256; }
 
-psgd_status ensure_tables(psgd_plan* plan, DeviceTables** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
-  auto it = plan->dev.find(dev);
-  if (it != plan->dev.end()) {
-    *out = &it->second;
-    return PSGD_OK;
-  }
+// Layout of the plan's device tables from `base` (each table 256-byte aligned); returns
+// their total size in bytes.  base may be null to only measure.
+uint64_t layout_tables(const psgd_plan* plan, char* base, DeviceTables* t) {
   const uint64_t b_mats = align256(plan->mats.size() * sizeof(MatInfo) + 1);
   const uint64_t b_rt = align256(plan->s2tiles.size() * sizeof(UpdTile) + 1);
   const uint64_t b_qt = align256(plan->qtiles.size() * sizeof(QTile) + 1);
   const uint64_t b_ut = align256(plan->utiles.size() * sizeof(UpdTile) + 1);
   const uint64_t b_tb = align256(plan->tblks.size() * sizeof(TallBlk) + 1);
-  void* base = nullptr;
-  e = hipMalloc(&base, b_mats + b_rt + b_qt + b_ut + b_tb);
-  if (e != hipSuccess) {
-    set_error(std::string("hipMalloc of the plan's device tables: ") + hipGetErrorString(e));
-    return PSGD_ERR_NO_MEMORY;
+  if (t != nullptr) {
+    t->base = base;
+    t->mats = reinterpret_cast<MatInfo*>(base);
+    t->s2tiles = reinterpret_cast<UpdTile*>(base + b_mats);
+    t->qtiles = reinterpret_cast<QTile*>(base + b_mats + b_rt);
+    t->utiles = reinterpret_cast<UpdTile*>(base + b_mats + b_rt + b_qt);
+    t->tblks = reinterpret_cast<TallBlk*>(base + b_mats + b_rt + b_qt + b_ut);
   }
-  DeviceTables t;
-  t.base = base;
-  char* b = static_cast<char*>(base);
-  t.mats = reinterpret_cast<MatInfo*>(b);
-  t.s2tiles = reinterpret_cast<UpdTile*>(b + b_mats);
-  t.qtiles = reinterpret_cast<QTile*>(b + b_mats + b_rt);
-  t.utiles = reinterpret_cast<UpdTile*>(b + b_mats + b_rt + b_qt);
-  t.tblks = reinterpret_cast<TallBlk*>(b + b_mats + b_rt + b_qt + b_ut);
+  return b_mats + b_rt + b_qt + b_ut + b_tb;
+}
+
+// Copy the plan's host tables to the device tables t: synchronously (stream null) or
+// enqueued on `st`.
+psgd_status copy_tables(const psgd_plan* plan, const DeviceTables& t, bool async, hipStream_t st) {
   struct {
     void* dst;
     const void* src;
@@ -1669,11 +1707,34 @@ psgd_status ensure_tables(psgd_plan* plan, DeviceTables** out) {
   };
   for (const auto& c : copies) {
     if (c.bytes == 0) continue;
-    e = hipMemcpy(c.dst, c.src, c.bytes, hipMemcpyHostToDevice);
-    if (e != hipSuccess) {
-      (void)hipFree(base);
-      return hip_fail("hipMemcpy of the plan's device tables", e);
-    }
+    const hipError_t e = async ? hipMemcpyAsync(c.dst, c.src, c.bytes, hipMemcpyHostToDevice, st)
+                               : hipMemcpy(c.dst, c.src, c.bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail("copy of the plan's device tables", e);
+  }
+  return PSGD_OK;
+}
+
+psgd_status ensure_tables(psgd_plan* plan, DeviceTables** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+  auto it = plan->dev.find(dev);
+  if (it != plan->dev.end()) {
+    *out = &it->second;
+    return PSGD_OK;
+  }
+  void* base = nullptr;
+  e = hipMalloc(&base, layout_tables(plan, nullptr, nullptr));
+  if (e != hipSuccess) {
+    set_error(std::string("hipMalloc of the plan's device tables: ") + hipGetErrorString(e));
+    return PSGD_ERR_NO_MEMORY;
+  }
+  DeviceTables t;
+  layout_tables(plan, static_cast<char*>(base), &t);
+  const psgd_status s = copy_tables(plan, t, false, nullptr);
+  if (s != PSGD_OK) {
+    (void)hipFree(base);
+    return s;
   }
   auto ins = plan->dev.emplace(dev, t);
   *out = &ins.first->second;
@@ -1753,14 +1814,16 @@ struct StepArgs {
   float* Qpart;
   double* gpart;         // tall matrices: per-block Gram partials and per-matrix T
   double* tmat;
-  const float* ebar_in;  // carried error mean to read (carry mode, valid carry)
+  const float* ebar_in;  // carried error mean to read (carry mode, when the state is valid)
   float* ebar_out;       // error mean to write (carry mode)
   float* Pprev;          // previous P, Q (deferred mode)
   float* Qprev;
   float* Qwpart;         // per-worker Q partials and Q_w (local-Q error), else null
   float* Qw;
   int64_t q_ws;          // floats between workers' Q_w
-  int offset_valid;      // deferred mode: errors hold M of the previous step
+  uint64_t* state;       // workspace state word (carry and deferred modes), else null
+  uint64_t key;          // this plan's key for these errors
+  int use_state;         // host allows the cross-step state (same buffers, not reset)
   int W, R, mode;
   int64_t ld;
   unsigned n_s2;  // worker-pass tiles
@@ -1788,7 +1851,8 @@ psgd_status launch_pass(psgd_plan* plan, int which, int fp, const DeviceTables& 
     return launch_k(plan, kKApply, a.Qw != nullptr ? k_apply<GT, WT, true> : k_apply<GT, WT, false>,
                     pass_grid(ntiles, rgroups), block, a.st, dt.s2tiles, ntiles, rgroups, dt.mats, g,
                     a.errors, a.Mbar, a.p, a.q, static_cast<const float*>(a.Qw), a.q_ws, a.update, a.mom, a.x,
-                    a.ebar_out, a.W, a.ld, a.R, a.mode, a.lr, a.mu, a.inv_w);
+                    a.ebar_out, a.W, a.ld, a.R, a.mode, a.lr, a.mu, a.inv_w, a.ebar_out != nullptr ? a.state : nullptr,
+                    a.key);
   }
   constexpr int RP = WT > 0 ? first_pass_rows(WT, std::is_same<GT, bf16>::value) : 1;
   const int32_t rgroups = int32_t((a.rows_per_tile + RP - 1) / RP);
@@ -1797,7 +1861,7 @@ psgd_status launch_pass(psgd_plan* plan, int which, int fp, const DeviceTables& 
                                 : k_first<GT, WT, kFpMean, RP>;
   return launch_k(plan, kKFirst, first, pass_grid(ntiles, rgroups), block, a.st, dt.s2tiles, ntiles,
                   rgroups, dt.mats, g, a.errors, a.ebar_in, a.Pprev, a.Qprev, a.q, a.Mbar, a.Ppart, a.W, a.ld, a.R,
-                  a.inv_w, a.offset_valid);
+                  a.inv_w, static_cast<const uint64_t*>(a.state), a.key, a.use_state);
 }
 
 // Worker-count specialisations of the worker passes: W in {1,2,4,8,16} unrolls fully,
@@ -1817,7 +1881,7 @@ psgd_status launch_pass_w(psgd_plan* plan, int which, int fp, const DeviceTables
 template <int R>
 psgd_status launch_all(psgd_plan* plan, const DeviceTables& dt, const StepArgs& a) {
   const bool deferred = (plan->flags & PSGD_FLAG_DEFERRED_ERROR) != 0;
-  const int fp = deferred ? kFpDefer : (a.ebar_in != nullptr ? kFpCarry : kFpMean);
+  const int fp = deferred ? kFpDefer : (a.ebar_in != nullptr ? kFpCarry : kFpMean);  // carry: decided on device
   const bool bf = plan->dtype == PSGD_BF16;
   const unsigned n_mats = unsigned(plan->mats.size());
   hipStream_t stream = a.st;
@@ -1879,7 +1943,7 @@ psgd_status launch_all(psgd_plan* plan, const DeviceTables& dt, const StepArgs& 
   if (deferred)
     return launch_k(plan, kKUpdate, k_update<R>, dim3(unsigned(plan->utiles.size())), dim3(kUpdThreads), stream,
                     dt.utiles, dt.mats, static_cast<const float*>(a.Mbar), static_cast<const float*>(a.p),
-                    static_cast<const float*>(a.q), a.update, a.mom, a.x, a.mode, a.lr, a.mu);
+                    static_cast<const float*>(a.q), a.update, a.mom, a.x, a.mode, a.lr, a.mu, a.state, a.key);
   return pass(kPassApply);
 }
 
@@ -1889,9 +1953,46 @@ bool state_matches(const psgd_plan* plan, const void* errors, const void* worksp
          plan->state_device == dev;
 }
 
+// The value the workspace's state word holds while `errors` carries this plan's
+// cross-step state: the plan's random nonce mixed with the buffer address (the
+// splitmix64 finaliser), never 0, the cleared value.
+uint64_t state_key(const psgd_plan* plan, const void* errors) {
+  uint64_t z = plan->nonce ^ (uint64_t(reinterpret_cast<uintptr_t>(errors)) * 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return (z ^ (z >> 31)) | 1u;
+}
+
+bool stream_capturing(hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(st, &cs) == hipSuccess && cs == hipStreamCaptureStatusActive;
+}
+
+// A call captured into a graph keeps the host's decision (use the state or not) for every
+// replay.  Captured without the state, replays would never use the state that earlier
+// replays leave, so such a capture is refused: capture only after an eager step of the
+// plan on the same buffers.
+psgd_status check_capture(const char* fn, bool needs_state, bool use_state, hipStream_t st) {
+  if (needs_state && !use_state && stream_capturing(st)) {
+    set_error(std::string(fn) + ": a carry or deferred plan can be captured into a graph only after an eager "
+              "step of the plan on the same errors and workspace");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  return PSGD_OK;
+}
+
+// Device tables supplied by the caller instead of the plan's own: `tables` holds the
+// plan's tables when *owner == nonce, else they are copied there on the step's stream
+// (after the arguments are checked) and *owner becomes nonce.
+struct TableSlot {
+  DeviceTables tables;
+  uint64_t* owner;
+};
+
+// slot: NULL for the plan's own tables (uploaded on its first step on a device).
 psgd_status run_step(const char* fn, psgd_plan* plan, const void* grads, float* errors, float* q,
                      float* p, float* update, float* mom, float* x, float lr, float mu, void* workspace,
-                     void* stream, int mode) {
+                     void* stream, int mode, TableSlot* slot = nullptr) {
   if (plan == nullptr) {
     set_error(std::string(fn) + ": plan is NULL");
     return PSGD_ERR_INVALID_ARG;
@@ -1938,16 +2039,30 @@ psgd_status run_step(const char* fn, psgd_plan* plan, const void* grads, float* 
         return PSGD_ERR_INVALID_ARG;
       }
 
-  DeviceTables* dt = nullptr;
-  if ((s = ensure_tables(plan, &dt)) != PSGD_OK) return s;
   int dev = 0;
-  (void)hipGetDevice(&dev);
-  char* ws = static_cast<char*>(workspace);
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) return hip_fail("hipGetDevice", he);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
   const bool carry = (plan->flags & PSGD_FLAG_CARRY_ERROR_MEAN) != 0;
   const bool deferred = (plan->flags & PSGD_FLAG_DEFERRED_ERROR) != 0;
-  // Cross-step state (carried error mean, or the deferred offset) is used only if the
-  // previous step of this plan left it on this device in these error/workspace buffers.
-  const bool use_state = (carry || deferred) && state_matches(plan, errors, workspace, dev);
+  const bool cross = (carry || deferred) && has_mats;
+  // Cross-step state (carried error mean, or the deferred offset) may be used only if the
+  // previous step of this plan left it on this device in these error/workspace buffers;
+  // the kernels also check the workspace's state word.
+  const bool use_state = cross && state_matches(plan, errors, workspace, dev);
+  if ((s = check_capture(fn, cross, use_state, st)) != PSGD_OK) return s;
+  DeviceTables* dt = nullptr;
+  if (slot == nullptr) {
+    if ((s = ensure_tables(plan, &dt)) != PSGD_OK) return s;
+  } else {
+    dt = &slot->tables;
+    if (*slot->owner != plan->nonce) {
+      *slot->owner = 0;
+      if ((s = copy_tables(plan, *dt, true, st)) != PSGD_OK) return s;
+      *slot->owner = plan->nonce;
+    }
+  }
+  char* ws = static_cast<char*>(workspace);
   plan->state_valid = false;
 
   StepArgs a{};
@@ -1967,10 +2082,12 @@ psgd_status run_step(const char* fn, psgd_plan* plan, const void* grads, float* 
   a.gpart = reinterpret_cast<double*>(ws + plan->ws_gpart);
   a.tmat = reinterpret_cast<double*>(ws + plan->ws_tmat);
   a.ebar_out = carry ? reinterpret_cast<float*>(ws + plan->ws_ebar) : nullptr;
-  a.ebar_in = (carry && use_state) ? a.ebar_out : nullptr;
+  a.ebar_in = a.ebar_out;
   a.Pprev = deferred ? reinterpret_cast<float*>(ws + plan->ws_pprev) : nullptr;
   a.Qprev = deferred ? reinterpret_cast<float*>(ws + plan->ws_qprev) : nullptr;
-  a.offset_valid = (deferred && use_state) ? 1 : 0;
+  a.state = cross ? reinterpret_cast<uint64_t*>(ws + plan->ws_state) : nullptr;
+  a.key = state_key(plan, errors);
+  a.use_state = use_state ? 1 : 0;
   const bool local_q = (plan->flags & PSGD_FLAG_LOCAL_Q_ERROR) != 0;
   a.Qwpart = local_q ? reinterpret_cast<float*>(ws + plan->ws_qwpart) : nullptr;
   a.Qw = local_q ? reinterpret_cast<float*>(ws + plan->ws_qw) : nullptr;
@@ -1981,7 +2098,7 @@ psgd_status run_step(const char* fn, psgd_plan* plan, const void* grads, float* 
   a.ld = plan->worker_stride;
   a.n_s2 = unsigned(plan->s2tiles.size());
   a.rows_per_tile = unsigned(plan->worker_rows_per_tile);
-  a.st = static_cast<hipStream_t>(stream);
+  a.st = st;
   switch (plan->rank) {
     case 1: s = launch_all<1>(plan, *dt, a); break;
     case 2: s = launch_all<2>(plan, *dt, a); break;
@@ -1991,13 +2108,12 @@ psgd_status run_step(const char* fn, psgd_plan* plan, const void* grads, float* 
       set_error(std::string(fn) + ": rank outside 1..4");
       return PSGD_ERR_UNSUPPORTED;
   }
-  if (s == PSGD_OK && (carry || deferred) && has_mats) {
+  if (s == PSGD_OK && cross) {
     plan->state_valid = true;
     plan->state_errors = errors;
     plan->state_workspace = workspace;
     plan->state_device = dev;
   }
-  plan->last_step_used_state = use_state;
   return s;
 }
 
@@ -2062,23 +2178,51 @@ extern "C" psgd_status psgd_errors_materialize(psgd_plan* plan, const float* err
   }
   if (plan->mats.empty()) return PSGD_OK;
   int dev = 0;
-  (void)hipGetDevice(&dev);
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
   const bool deferred = (plan->flags & PSGD_FLAG_DEFERRED_ERROR) != 0;
-  const bool offset = deferred && state_matches(plan, errors, workspace, dev);
-  if (!offset && out == errors) return PSGD_OK;  // already plain, nothing to write
+  // The host rules out a subtraction when the plan's last step did not run on these
+  // buffers (or was reset); otherwise the kernel reads the workspace's state word.
+  const bool use_state = deferred && state_matches(plan, errors, workspace, dev);
+  if (!use_state && out == errors) return PSGD_OK;  // already plain, nothing to write
+  if ((s = check_capture(fn, deferred, use_state, st)) != PSGD_OK) return s;
   DeviceTables* dt = nullptr;
   if ((s = ensure_tables(plan, &dt)) != PSGD_OK) return s;
   char* ws = static_cast<char*>(workspace);
   const float* Pprev = deferred ? reinterpret_cast<const float*>(ws + plan->ws_pprev) : nullptr;
   const float* Qprev = deferred ? reinterpret_cast<const float*>(ws + plan->ws_qprev) : nullptr;
+  uint64_t* state = deferred ? reinterpret_cast<uint64_t*>(ws + plan->ws_state) : nullptr;
   hipLaunchKernelGGL(k_materialize, dim3(unsigned(plan->s2tiles.size()), unsigned(plan->worker_rows_per_tile)),
-                     dim3(kStreamThreads), 0,
-                     static_cast<hipStream_t>(stream), dt->s2tiles, dt->mats, errors, out, Pprev, Qprev,
-                     plan->n_workers, plan->worker_stride, plan->rank, offset ? 1 : 0);
-  hipError_t e = hipGetLastError();
+                     dim3(kStreamThreads), 0, st, dt->s2tiles, dt->mats, errors, out, Pprev, Qprev,
+                     plan->n_workers, plan->worker_stride, plan->rank, static_cast<const uint64_t*>(state),
+                     state_key(plan, errors), use_state ? 1 : 0);
+  e = hipGetLastError();
   if (e != hipSuccess) return hip_fail("launch k_materialize", e);
-  if (offset && out == errors) plan->state_valid = false;  // the buffer now holds plain errors
+  if (use_state && out == errors) {  // the buffer now holds plain errors
+    plan->state_valid = false;
+    hipLaunchKernelGGL(k_state_store, dim3(1), dim3(64), 0, st, state, uint64_t(0));
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail("launch k_state_store", e);
+  }
   return PSGD_OK;
+}
+
+extern "C" psgd_status psgd_plan_reset_carry_stream(psgd_plan* plan, void* workspace, void* stream) {
+  const char* fn = "psgd_plan_reset_carry_stream";
+  if (plan == nullptr) {
+    set_error(std::string(fn) + ": plan is NULL");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  psgd_status s;
+  if ((s = check_ptr(fn, "workspace", workspace, false)) != PSGD_OK) return s;
+  plan->state_valid = false;
+  const bool cross = (plan->flags & (PSGD_FLAG_CARRY_ERROR_MEAN | PSGD_FLAG_DEFERRED_ERROR)) != 0;
+  if (!cross || plan->mats.empty()) return PSGD_OK;
+  hipLaunchKernelGGL(k_state_store, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
+                     reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + plan->ws_state), uint64_t(0));
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PSGD_OK : hip_fail("launch k_state_store", e);
 }
 
 extern "C" psgd_status psgd_ef_momentum_apply(psgd_plan* plan, const void* grads, float* errors,
@@ -2089,3 +2233,4 @@ extern "C" psgd_status psgd_ef_momentum_apply(psgd_plan* plan, const void* grads
   return run_step("psgd_ef_momentum_apply", plan, grads, errors, q, p, update, momentum, params, lr, mu,
                   workspace, stream, mode);
 }
+

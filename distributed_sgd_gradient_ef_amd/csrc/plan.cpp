@@ -5,9 +5,12 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdio>
 #include <new>
+#include <random>
 #include <string>
 
 #include "plan.hpp"
@@ -81,6 +84,17 @@ extern "C" psgd_status psgd_plan_create(const psgd_layer* layers, int32_t n_laye
     plan->n_workers = n_workers;
     plan->dtype = grad_dtype;
     plan->flags = flags;
+    {  // a key no other plan's state word is likely to hold: random bits, the clock, a counter
+      static std::atomic<uint64_t> counter{0};
+      uint64_t nonce = (++counter) * 0x9E3779B97F4A7C15ull ^
+                       uint64_t(std::chrono::steady_clock::now().time_since_epoch().count());
+      try {
+        std::random_device rd;
+        nonce ^= uint64_t(rd()) << 32 | rd();
+      } catch (...) {
+      }
+      plan->nonce = nonce;
+    }
     const int64_t r = rank;
     int64_t off = 0, p_off = 0, q_off = 0, qpart = 0;
     for (int32_t i = 0; i < n_layers; ++i) {
@@ -261,6 +275,8 @@ extern "C" psgd_status psgd_plan_create(const psgd_layer* layers, int32_t n_laye
     ws += uint64_t(round_up(int64_t(plan->tblks.size()) * 10 * 8, 256));
     plan->ws_tmat = ws;
     if (!plan->tblks.empty()) ws += uint64_t(round_up(int64_t(plan->mats.size()) * 16 * 8, 256));
+    plan->ws_state = ws;  // one 64-bit state word (carry and deferred modes)
+    if (flags & (PSGD_FLAG_CARRY_ERROR_MEAN | PSGD_FLAG_DEFERRED_ERROR)) ws += 256;
     plan->workspace_bytes = ws;
     int32_t max_rows = 1;
     for (const MatInfo& m : plan->mats) max_rows = std::max(max_rows, m.rows);

@@ -156,8 +156,11 @@ struct psgd_plan {
   std::map<int, psgd::DeviceTables> dev;  // per HIP device id
   // cross-step state: the carried error mean (PSGD_FLAG_CARRY_ERROR_MEAN) or the deferred
   // offset (PSGD_FLAG_DEFERRED_ERROR), valid for these error/workspace buffers on this device
+  // (the host's view; the workspace's state word at ws_state holds the device's, keyed by
+  // nonce and the errors address)
   bool state_valid = false;
-  bool last_step_used_state = false;
+  uint64_t nonce = 0;
+  uint64_t ws_state = 0;
   const void* state_errors = nullptr;
   const void* state_workspace = nullptr;
   int state_device = -1;

@@ -37,7 +37,8 @@ PSGD_FLAG_LOCAL_Q_ERROR = 0x8
 EXPORTED = [
     "psgd_plan_create", "psgd_plan_sizes", "psgd_plan_layer_info", "psgd_plan_destroy",
     "psgd_compress_step", "psgd_ef_momentum_apply", "psgd_plan_set_timing",
-    "psgd_plan_kernel_stats", "psgd_plan_reset_carry", "psgd_errors_materialize", "psgd_stream_copy",
+    "psgd_plan_kernel_stats", "psgd_plan_reset_carry", "psgd_plan_reset_carry_stream", "psgd_errors_materialize",
+    "psgd_stream_copy",
     "psgd_plan_set_power_iterations", "psgd_status_string", "psgd_last_error",
     "psgd_rtopk_plan_create", "psgd_rtopk_plan_sizes", "psgd_rtopk_plan_layer_info", "psgd_rtopk_plan_destroy",
     "psgd_rtopk_step", "psgd_rtopk_plan_set_timing", "psgd_rtopk_plan_kernel_stats",
@@ -136,6 +137,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.psgd_plan_set_timing.argtypes = [vp, i32]
     lib.psgd_plan_kernel_stats.argtypes = [vp, ctypes.POINTER(_KernelStat), i32, ctypes.POINTER(i32), i32]
     lib.psgd_plan_reset_carry.argtypes = [vp]
+    lib.psgd_plan_reset_carry_stream.argtypes = [vp, vp, vp]
     lib.psgd_stream_copy.argtypes = [vp, vp, ctypes.c_uint64, vp]
     lib.psgd_errors_materialize.argtypes = [vp, vp, vp, vp, vp]
     lib.psgd_plan_set_power_iterations.argtypes = [vp, i32]
@@ -249,6 +251,15 @@ def psgd_plan_set_power_iterations(plan: Plan, iterations: int) -> None:
 
 def psgd_plan_reset_carry(plan: Plan) -> None:
     _check(load_library().psgd_plan_reset_carry(plan.handle))
+
+
+def psgd_plan_reset_carry_stream(plan: Plan, workspace, stream=None) -> None:
+    """Stream-ordered reset of the cross-step state held in `workspace`."""
+    import torch
+
+    with torch.cuda.device(workspace.device):
+        _check(load_library().psgd_plan_reset_carry_stream(plan.handle, _ptr(workspace),
+                                                           _stream(stream, workspace)))
 
 
 def psgd_errors_materialize(plan: Plan, errors, out, workspace, stream=None) -> None:

@@ -99,7 +99,8 @@ typedef enum psgd_dtype {
  * the same `errors` and `workspace` pointers and modifies neither.  A step falls back to
  * reading all errors when it is the plan's first, follows psgd_plan_reset_carry, or
  * sees other errors/workspace pointers or another device than the previous step; a
- * failed step also forces the fallback.  The workspace grows by worker_stride floats. */
+ * failed step also forces the fallback.  The workspace grows by worker_stride floats
+ * and a 256-byte state block (see "Cross-step state and graphs" below). */
 #define PSGD_FLAG_CARRY_ERROR_MEAN 0x2u
 /* Deferred error subtraction.  The step reads every worker's G and E once: the error
  * buffer keeps M_w = G_w + E_w of the step that wrote it (the error before subtracting
@@ -111,7 +112,23 @@ typedef enum psgd_dtype {
  * writes it out.  Contract and fallback as for PSGD_FLAG_CARRY_ERROR_MEAN: the same
  * errors and workspace pointers, unmodified, between steps (psgd_plan_reset_carry
  * declares that `errors` now holds plain errors).  Excludes
- * PSGD_FLAG_CARRY_ERROR_MEAN.  The workspace grows by p_elems + q_elems floats. */
+ * PSGD_FLAG_CARRY_ERROR_MEAN.  The workspace grows by p_elems + q_elems floats and the
+ * 256-byte state block.
+ *
+ * Cross-step state and graphs.  Whether a step of a carry or deferred plan uses the
+ * state the previous step left is decided twice: on the host (the plan's previous step
+ * ran on this device with the same errors and workspace pointers and nothing reset it
+ * since) and on the device, from a state word in the workspace.  The last pass of a
+ * step writes the word (a key of the plan and the errors address); in-place
+ * psgd_errors_materialize and psgd_plan_reset_carry_stream clear it on the stream.  A
+ * step captured into a HIP graph therefore keeps working when the buffers change
+ * between replays, as long as the change goes through those stream-ordered calls:
+ *   - capture a step of such a plan only after one eager step on the same errors and
+ *     workspace (a capture without usable state is refused with PSGD_ERR_INVALID_ARG;
+ *     so is a capture of psgd_errors_materialize on a deferred plan in that case);
+ *   - after writing errors or the workspace yourself, call psgd_plan_reset_carry_stream
+ *     on the stream before the next replay (psgd_plan_reset_carry is host-only and
+ *     reaches eager steps, not replays). */
 #define PSGD_FLAG_DEFERRED_ERROR 0x4u
 /* Local-Q error: each worker keeps E'_w = M_w - P Q_w^T with its own Q_w = M_w^T P
  * (the projection of M_w off span(P)) instead of M_w - P Qbar^T.  P, Qbar (the output q
@@ -241,12 +258,22 @@ psgd_status psgd_plan_kernel_stats(psgd_plan* plan, psgd_kernel_stat* out, int32
  * yourself, e.g. when restoring a checkpoint. */
 psgd_status psgd_plan_reset_carry(psgd_plan* plan);
 
+/* The stream-ordered form of psgd_plan_reset_carry: clears the state word in
+ * `workspace` (a device pointer, the plan's workspace) with a one-thread kernel on
+ * `stream`, so that every later step on that workspace, eager or replayed from a graph,
+ * treats `errors` as plain errors, and also does what psgd_plan_reset_carry does.  It
+ * may itself be captured into a graph.  Plans without PSGD_FLAG_CARRY_ERROR_MEAN or
+ * PSGD_FLAG_DEFERRED_ERROR (or without compressed matrices) enqueue nothing.
+ * PSGD_ERR_INVALID_ARG for a NULL plan or a NULL or misaligned workspace. */
+psgd_status psgd_plan_reset_carry_stream(psgd_plan* plan, void* workspace, void* stream);
+
 /* Write the plain error memory of every compressed matrix to `out` ([n_workers]
  * [worker_stride] float32): for a PSGD_FLAG_DEFERRED_ERROR plan whose last step left
  * `errors` and `workspace` in the deferred form, out_w = errors_w - P Q^T of that step;
  * otherwise out_w = errors_w.  `out` may be `errors` (in place; the plan then treats the
- * buffer as plain) or a separate buffer (the plan's state is kept).  Elements of 1-D
- * tensors and padding are not written.  Asynchronous on `stream`. */
+ * buffer as plain, and clears the workspace's state word on the stream) or a separate
+ * buffer (the plan's state is kept).  Elements of 1-D tensors and padding are not
+ * written.  Asynchronous on `stream`. */
 psgd_status psgd_errors_materialize(psgd_plan* plan, const float* errors, float* out, void* workspace,
                                     void* stream);
 

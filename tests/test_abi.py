@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADERS = [os.path.join(ROOT, "include", name) for name in sorted(os.listdir(os.path.join(ROOT, "include")))
            if name.endswith(".h")]
 
-pytestmark = pytest.mark.skipif(not os.path.exists(psgd.LIB_PATH), reason="libpsgd.so not built")
+pytestmark = pytest.mark.usefixtures("built_library")
 
 
 def _declared():
@@ -126,14 +126,22 @@ def test_plan_model_bytes(dtype, gb):
         assert abs(s["model_bytes"] / 1e9 - 2.189) < 0.001
 
 
-def test_carry_flag_grows_workspace_by_one_slice():
+def test_carry_flag_grows_workspace_by_one_slice_and_the_state_block():
     shapes = [s for _, s in WL.resnet18_cifar_shapes()]
     a = psgd.psgd_plan_create(shapes, 2, 16).sizes
     b = psgd.psgd_plan_create(shapes, 2, 16, flags=psgd.PSGD_FLAG_CARRY_ERROR_MEAN).sizes
-    assert b["workspace_bytes"] - a["workspace_bytes"] == -(-a["worker_stride"] * 4 // 256) * 256
+    assert b["workspace_bytes"] - a["workspace_bytes"] == -(-a["worker_stride"] * 4 // 256) * 256 + 256
     plan = psgd.psgd_plan_create(shapes, 2, 16, flags=psgd.PSGD_FLAG_CARRY_ERROR_MEAN | psgd.PSGD_FLAG_NESTEROV)
     psgd.psgd_plan_reset_carry(plan)
-    assert psgd.load_library().psgd_plan_reset_carry(None) == psgd.PSGD_ERR_INVALID_ARG
+    lib = psgd.load_library()
+    assert lib.psgd_plan_reset_carry(None) == psgd.PSGD_ERR_INVALID_ARG
+    # the stream-ordered reset checks its arguments before any device call
+    assert lib.psgd_plan_reset_carry_stream(None, 0x1000, None) == psgd.PSGD_ERR_INVALID_ARG
+    assert lib.psgd_plan_reset_carry_stream(plan.handle, None, None) == psgd.PSGD_ERR_INVALID_ARG
+    assert lib.psgd_plan_reset_carry_stream(plan.handle, 0x1008, None) == psgd.PSGD_ERR_INVALID_ARG
+    # a plan without cross-step state enqueues nothing (no device call is made)
+    plain = psgd.psgd_plan_create(shapes, 2, 16)
+    assert lib.psgd_plan_reset_carry_stream(plain.handle, 0x1000, None) == psgd.PSGD_OK
 
 
 def test_deferred_flag_rules():
@@ -143,7 +151,7 @@ def test_deferred_flag_rules():
         psgd.PSGD_ERR_UNSUPPORTED
     a = psgd.psgd_plan_create(shapes, 2, 4).sizes
     b = psgd.psgd_plan_create(shapes, 2, 4, flags=psgd.PSGD_FLAG_DEFERRED_ERROR).sizes
-    assert b["workspace_bytes"] - a["workspace_bytes"] == 2 * 512  # P (64x2) and Q (64x2), 256-B rounded
+    assert b["workspace_bytes"] - a["workspace_bytes"] == 2 * 512 + 256  # P, Q (64x2 each, 256-B rounded), state
     lib = psgd.load_library()
     plan = psgd.psgd_plan_create(shapes, 2, 4, flags=psgd.PSGD_FLAG_DEFERRED_ERROR)
     assert lib.psgd_errors_materialize(None, 0x1000, 0x1000, 0x2000, None) == psgd.PSGD_ERR_INVALID_ARG

@@ -107,3 +107,79 @@ def test_atomo_step_graph():
 
     _replay_and_compare("atomo", make, step,
                         lambda st: [st["sigma"], st["prob"], st["index"], st["count"], st["atoms"], st["u"]])
+
+
+@pytest.mark.parametrize("mode", ["deferred", "carry"])
+def test_cross_step_state_changes_between_replays(mode):
+    """A captured step of a deferred (carry) plan, replayed while its cross-step state is
+    changed between replays: new gradients every replay, an in-place materialisation of
+    the errors (deferred), and errors written anew followed by the stream-ordered reset.
+    The state is read on the device, so every replay equals (bit for bit) an eager plan
+    given the same calls (which may use the host-only reset)."""
+    flags = P.PSGD_FLAG_DEFERRED_ERROR if mode == "deferred" else P.PSGD_FLAG_CARRY_ERROR_MEAN
+    shapes = [(64, 27), (1, 64), (128, 130), (10, 512), (300, 96)]
+    W, r = 4, 2
+    rs = np.random.default_rng(604)
+    print(f"[graphs] case cross-step state between replays ({mode})", flush=True)
+
+    def make():
+        plan = P.psgd_plan_create(shapes, r, W, P.PSGD_F32, flags)
+        s = plan.sizes
+        return dict(plan=plan, g=torch.zeros((W, s["worker_stride"]), device=DEV),
+                    e=torch.zeros((W, s["worker_stride"]), device=DEV),
+                    q=torch.ones(s["q_elems"], device=DEV), p=torch.zeros(s["p_elems"], device=DEV),
+                    u=torch.zeros(s["worker_stride"], device=DEV),
+                    ws=torch.zeros(s["workspace_bytes"], dtype=torch.uint8, device=DEV))
+
+    a, b = make(), make()
+    ld = a["plan"].sizes["worker_stride"]
+    q0 = torch.from_numpy(rs.standard_normal(a["plan"].sizes["q_elems"]).astype(np.float32)).to(DEV)
+
+    def new_grads():
+        g = torch.from_numpy(rs.standard_normal((W, ld)).astype(np.float32)).to(DEV)
+        a["g"].copy_(g)
+        b["g"].copy_(g)
+
+    def step(st):
+        P.psgd_compress_step(st["plan"], st["g"], st["e"], st["q"], st["p"], st["u"], st["ws"])
+
+    # a capture without usable state (no eager step yet) is refused before enqueuing
+    g0 = torch.cuda.CUDAGraph()
+    refused = False
+    with torch.cuda.graph(g0):
+        try:
+            step(a)
+        except P.PsgdError as err:
+            refused = err.status == P.PSGD_ERR_INVALID_ARG
+    assert refused
+    del g0
+    for st in (a, b):
+        st["q"].copy_(q0)
+    for _ in range(2):
+        new_grads()
+        step(a)
+        step(b)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(a)
+    torch.cuda.synchronize()
+    for i in range(7):
+        if i == 2 and mode == "deferred":  # the buffers now hold plain errors
+            P.psgd_errors_materialize(a["plan"], a["e"], a["e"], a["ws"])
+            P.psgd_errors_materialize(b["plan"], b["e"], b["e"], b["ws"])
+        if i in (4, 5):  # errors written from outside
+            e = torch.from_numpy(0.3 * rs.standard_normal((W, ld)).astype(np.float32)).to(DEV)
+            a["e"].copy_(e)
+            b["e"].copy_(e)
+            P.psgd_plan_reset_carry_stream(a["plan"], a["ws"])
+            if i == 4:
+                P.psgd_plan_reset_carry(b["plan"])
+            else:
+                P.psgd_plan_reset_carry_stream(b["plan"], b["ws"])
+        new_grads()
+        g.replay()
+        step(b)
+        torch.cuda.synchronize()
+        for j, (x, y) in enumerate(zip([a["e"], a["q"], a["p"], a["u"]], [b["e"], b["q"], b["p"], b["u"]])):
+            assert torch.equal(x, y), f"{mode}: replay {i}, output {j} differs from the eager step"
