@@ -2234,3 +2234,60 @@ extern "C" psgd_status psgd_ef_momentum_apply(psgd_plan* plan, const void* grads
                   workspace, stream, mode);
 }
 
+// ------------------------------------------------------------------ no-allocation entry point
+// psgd_compress_step_noalloc is for callers that cannot allocate device memory (code
+// under graph capture, tight serving loops, harnesses that forbid hipMalloc).  It runs the
+// kernels of psgd_compress_step with the step's workspace and the plan's device tables in
+// `scratch`, one array of kNoAllocScratchBytes per GPU that the code object holds until
+// the process ends.  Host code never passes `scratch` itself to a kernel or a copy (on the
+// host the name is a stand-in, not a device address): on its first call on a GPU the
+// entry point looks up that GPU's address of the array and uses only that.
+constexpr uint64_t kNoAllocScratchBytes = uint64_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+struct NoAllocDevice {
+  char* base = nullptr;      // this GPU's address of `scratch`
+  uint64_t tables_of = 0;    // nonce of the plan whose device tables the array holds (0: none)
+};
+std::mutex g_noalloc_mutex;
+std::map<int, NoAllocDevice> g_noalloc;  // per HIP device id
+}  // namespace
+
+extern "C" psgd_status psgd_compress_step_noalloc(psgd_plan* plan, const void* grads, float* errors, float* q,
+                                                  float* p, float* update, void* stream) {
+  const char* fn = "psgd_compress_step_noalloc";
+  if (plan == nullptr) {
+    set_error(std::string(fn) + ": plan is NULL");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  if (plan->flags & (PSGD_FLAG_CARRY_ERROR_MEAN | PSGD_FLAG_DEFERRED_ERROR)) {
+    set_error(std::string(fn) + ": plans with PSGD_FLAG_CARRY_ERROR_MEAN or PSGD_FLAG_DEFERRED_ERROR keep state "
+              "between steps in their workspace, which this entry point shares between all calls on a GPU");
+    return PSGD_ERR_UNSUPPORTED;
+  }
+  const uint64_t tables = layout_tables(plan, nullptr, nullptr);
+  const uint64_t need = tables + plan->workspace_bytes;
+  if (need > kNoAllocScratchBytes) {
+    set_error(std::string(fn) + ": the plan needs " + std::to_string(need) + " bytes of scratch (tables " +
+              std::to_string(tables) + " + workspace " + std::to_string(plan->workspace_bytes) +
+              "), more than the " + std::to_string(kNoAllocScratchBytes) + " bytes of the static array");
+    return PSGD_ERR_INVALID_ARG;
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+  std::lock_guard<std::mutex> lock(g_noalloc_mutex);
+  NoAllocDevice& nd = g_noalloc[dev];
+  if (nd.base == nullptr) {  // set-up, once per GPU, with that GPU current
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail("hipGetSymbolAddress of the scratch array", e);
+    nd.base = static_cast<char*>(ptr);
+  }
+  TableSlot slot;
+  layout_tables(plan, nd.base, &slot.tables);
+  slot.owner = &nd.tables_of;
+  return run_step(fn, plan, grads, errors, q, p, update, nullptr, nullptr, 0.f, 0.f, nd.base + tables, stream,
+                  kCompress, &slot);
+}

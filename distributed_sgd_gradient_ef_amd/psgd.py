@@ -36,7 +36,7 @@ PSGD_FLAG_LOCAL_Q_ERROR = 0x8
 
 EXPORTED = [
     "psgd_plan_create", "psgd_plan_sizes", "psgd_plan_layer_info", "psgd_plan_destroy",
-    "psgd_compress_step", "psgd_ef_momentum_apply", "psgd_plan_set_timing",
+    "psgd_compress_step", "psgd_compress_step_noalloc", "psgd_ef_momentum_apply", "psgd_plan_set_timing",
     "psgd_plan_kernel_stats", "psgd_plan_reset_carry", "psgd_plan_reset_carry_stream", "psgd_errors_materialize",
     "psgd_stream_copy",
     "psgd_plan_set_power_iterations", "psgd_status_string", "psgd_last_error",
@@ -133,6 +133,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.psgd_plan_layer_info.argtypes = [vp, i32, ctypes.POINTER(_LayerInfo)]
     lib.psgd_plan_destroy.argtypes = [vp]
     lib.psgd_compress_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.psgd_compress_step_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     lib.psgd_ef_momentum_apply.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, f32, vp, vp, vp]
     lib.psgd_plan_set_timing.argtypes = [vp, i32]
     lib.psgd_plan_kernel_stats.argtypes = [vp, ctypes.POINTER(_KernelStat), i32, ctypes.POINTER(i32), i32]
@@ -299,6 +300,16 @@ def psgd_compress_step(plan: Plan, grads, errors, q, p, update, workspace, strea
         _check(load_library().psgd_compress_step(
             plan.handle, _ptr(grads), _ptr(errors), _ptr(q), _ptr(p), _ptr(update), _ptr(workspace),
             _stream(stream, grads)))
+
+
+def psgd_compress_step_noalloc(plan: Plan, grads, errors, q, p, update, stream=None) -> None:
+    """The same step with the workspace in the library's static device array (no
+    device allocation; see include/psgd.h)."""
+    import torch
+
+    with torch.cuda.device(grads.device):
+        _check(load_library().psgd_compress_step_noalloc(
+            plan.handle, _ptr(grads), _ptr(errors), _ptr(q), _ptr(p), _ptr(update), _stream(stream, grads)))
 
 
 def psgd_ef_momentum_apply(plan: Plan, grads, errors, q, p, momentum, params, lr: float, mu: float,

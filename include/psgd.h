@@ -277,6 +277,23 @@ psgd_status psgd_plan_reset_carry_stream(psgd_plan* plan, void* workspace, void*
 psgd_status psgd_errors_materialize(psgd_plan* plan, const float* errors, float* out, void* workspace,
                                     void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): psgd_compress_step without a workspace
+ * argument and without any device allocation.  The same kernels run with the workspace
+ * and the plan's device tables in a static array of the library, 64 MiB per GPU, which
+ * each GPU the library runs on holds until the process ends; the first call on a GPU
+ * looks up that GPU's copy of the array.  The plan's tables are copied into the array
+ * (hipMemcpyAsync on `stream`) whenever the previous call on that GPU used another plan.
+ * Arguments as for psgd_compress_step.  Returns PSGD_ERR_INVALID_ARG, enqueueing
+ * nothing, when the plan needs more than the array holds (its workspace_bytes plus its
+ * tables; ResNet-18 shapes at 16 workers and rank 2 need 46.5 MB), and PSGD_ERR_UNSUPPORTED for a
+ * plan with PSGD_FLAG_CARRY_ERROR_MEAN or PSGD_FLAG_DEFERRED_ERROR (their cross-step state
+ * would live in the shared array).  Every call on a GPU shares that GPU's array: calls
+ * that overlap on one GPU (other streams, other threads) race and give undefined
+ * results; serialise them.  No step of the plain plans needs the array cleared. */
+psgd_status psgd_compress_step_noalloc(psgd_plan* plan, const void* grads, float* errors, float* q,
+                                       float* p, float* update, void* stream);
+
 /* Calibration probe: copy `bytes` (a multiple of 16) from `src` to `dst` on `stream`
  * with the same non-temporal float4 accesses the streaming passes use.  It measures the
  * copy bandwidth the device reaches, and gives hardware counters a transfer of known
