@@ -207,6 +207,42 @@ def atomo_cpu_baseline(wl, seconds: float) -> dict:
                       f"BLAS threads = cores"}
 
 
+def rtopk_cpu_baseline(wl, seconds: float, workers: int = 2) -> dict:
+    """Time the rTop-k oracle on `workers` of the W workers (every tensor of each, rounds
+    until `seconds` have passed, at least one) and scale to a whole step of W workers:
+    each worker's selection is independent, the mean of the sparse messages is a small
+    share of the work."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from distributed_sgd_gradient_ef_amd import workloads as WL
+    from oracle import rtopk_ef as O
+
+    tops, keeps = WL.rtopk_counts(wl)
+    grads, ranks = [], []
+    for li in range(len(wl.shapes)):
+        p = WL.planted(wl, li, 0)
+        low = None if p is None else p.dense()
+        grads.append(np.stack([WL.grad_layer(wl, li, 0, w, low) for w in range(workers)]))
+        ranks.append(np.stack([WL.rtopk_ranks(wl, 0, w, li, tops[li]) for w in range(workers)]))
+    errors = [np.zeros_like(g) for g in grads]
+    rounds, t0 = 0, time.perf_counter()
+    while True:
+        O.compress_layers(grads, errors, tops, keeps, ranks)
+        rounds += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    t_step = el / rounds * wl.workers / workers
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    gbytes = wl.workers * wl.numel() * 4 / 1e9
+    return {"value": round(gbytes / t_step, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rounds} round(s) of {workers} of the {wl.workers} workers (all 62 tensors each, 1% sent "
+                      f"from the top 2%), numpy oracle (lexsort top set), {el / rounds:.2f} s per round, scaled "
+                      f"to a whole step of {wl.workers} workers ({t_step:.1f} s); BLAS threads = cores (the "
+                      f"selection itself runs on one thread)"}
+
+
 def timed_steps(torch, step, steps: int, stream):
     """Run `steps` calls of step() with an event recorded on `stream` between calls.
     Returns (mean ms over the whole region, median ms, minimum ms)."""
@@ -497,6 +533,7 @@ def main() -> int:
                          "traffic": traffic_for(dom, RTOPK_TRAFFIC_FILE, RTOPK_SRC),
                          "alg_bytes_per_launch": kb[dom], "mean_us": dom_us},
             "kernels": kernels,
+            **({} if args.no_cpu_baseline else {"cpu_baseline": rtopk_cpu_baseline(wr, args.cpu_seconds / 3)}),
         }
 
     def measure_atomo() -> dict:
