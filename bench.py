@@ -17,7 +17,8 @@ each worker's error uses its own Q_w).  `value` is the --primary one.
 A second compressor is timed beside it ("rtopk" in the output): rTop-k with error
 feedback on the same shapes and W = 16, 1% of each tensor sent, drawn from its top 2%
 (psgd_rtopk_step: EF add, top-set selection, random subset from seeded ranks, sparse
-lists, new errors, dense mean update), and a third ("atomo"): Spectral-ATOMO on the same
+lists, new errors, dense mean update; the deferred-zero plan, whose next step zeroes the
+sent entries as it reads the errors), and a third ("atomo"): Spectral-ATOMO on the same
 shapes and workers with budget s = 2 (psgd_atomo_step: Gram matrices, tridiagonalisation,
 eigenvalues, closed-form probabilities, Bernoulli draws from seeded uniforms, inverse
 iteration and back-transformation for the sent atoms, their second factors, the mean).
@@ -89,14 +90,15 @@ def kernel_bytes(plan, dtype_bytes: int, variant: str) -> dict:
     }
 
 
-def rtopk_kernel_bytes(plan, dtype_bytes: int) -> dict:
+def rtopk_kernel_bytes(plan, dtype_bytes: int, deferred: bool = True) -> dict:
     """Algorithmic HBM bytes per launch of the streaming rTop-k kernels (the selection
     kernels in between move a few bytes per segment or per candidate)."""
     s = plan.sizes
     W, n = s["n_workers"], s["numel"]
     return {
-        # read G_w and E_w, write M_w on every worker
-        "rk_ef_hist": W * (dtype_bytes + 8) * n,
+        # read G_w and E_w, write M_w on every worker (deferred zeros: and read the
+        # previous step's sent mask, one bit per element)
+        "rk_ef_hist": W * (dtype_bytes + 8) * n + (W * n // 8 if deferred else 0),
         # read M_w, write one mask bit per entry on every worker
         "rk_mark": W * 4 * n + W * n // 8,
         # read the top mask and the ranks of the top set, write the kept mask
@@ -463,7 +465,7 @@ def main() -> int:
     def measure_rtopk() -> dict:
         wr = WL.workload("resnet18_rtopk")
         tops, keeps = WL.rtopk_counts(wr)
-        plan = psgd.psgd_rtopk_plan_create(shapes, tops, keeps, W, psgd.PSGD_F32)
+        plan = psgd.psgd_rtopk_plan_create(shapes, tops, keeps, W, psgd.PSGD_F32, psgd.PSGD_RTOPK_FLAG_DEFERRED_ZERO)
         s = plan.sizes
         ld = s["worker_stride"]
         # four gradient sets resident in HBM, one per step in turn, so the error memory
@@ -527,7 +529,7 @@ def main() -> int:
             "config": {"workload": "resnet18_cifar_shapes", "workers": W, "tensors": s["n_layers"],
                        "keep_frac": wr.keep_frac, "top_factor": wr.top_factor, "keep_total": s["keep_total"],
                        "top_total": s["top_total"], "grad_bytes_per_step": grad_bytes,
-                       "gradient_sets": nsets},
+                       "gradient_sets": nsets, "plan_flags": "PSGD_RTOPK_FLAG_DEFERRED_ZERO"},
             "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "traffic": traffic_for(dom, RTOPK_TRAFFIC_FILE, RTOPK_SRC),

@@ -33,8 +33,9 @@
 //   rk_scan_kept  per segment: exclusive scan of the kept counts; unused output slots
 //                 get index -1, value 0
 //   rk_emit       per tile: index/value lists in index order (first k kept), E' = 0 at
-//                 the sent entries, the kept mask trimmed to what was sent, and each
-//                 mask word's first list position
+//                 the sent entries (deferred-zero plans leave that to the next step's
+//                 rk_ef_hist, which zeroes them as it reads E), the kept mask trimmed to
+//                 what was sent, and each mask word's first list position
 //   rk_update     U = (1/W) * sum over workers, in worker order, of the sent entries
 //
 // Every reduction that produces a float has a fixed order; every other result is an
@@ -46,10 +47,13 @@
 #include <hip/hip_ext.h>
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdio>
 #include <map>
 #include <new>
+#include <random>
 #include <string>
 #include <vector>
 
@@ -125,6 +129,16 @@ const char* const kNames[kNumK] = {"rk_zero",     "rk_ef_hist", "rk_select",    
 struct psgd_rtopk_plan {
   int32_t n_workers = 0;
   psgd_dtype dtype = PSGD_F32;
+  uint32_t flags = 0;
+  // deferred-zero plans: the sent mask of the last step (ws_kmask) is pending in the
+  // errors; the host's view of that state (these buffers, this device, not reset) and,
+  // on the device, the state word at ws_state keyed by nonce and the errors address
+  uint64_t nonce = 0;
+  bool state_valid = false;
+  const void* state_errors = nullptr;
+  const void* state_workspace = nullptr;
+  int state_device = -1;
+  uint64_t ws_state = 0;
   std::vector<psgd_rtopk_layer_info> info;
   std::vector<psgd::rtk::RkLayer> layers;
   std::vector<psgd::rtk::RkTile> tiles;
@@ -366,17 +380,38 @@ __global__ __launch_bounds__(256) void rk_zero(uint32_t* __restrict__ p, int64_t
 }
 
 // Loads of one tile's G and E chunks (16 elements per thread).  A chunk past the tile's
-// end reads the tile's first chunk instead (always in bounds) and is then ignored.
+// end reads the tile's first chunk instead (always in bounds) and is then ignored.  With
+// `zmask` (a deferred-zero plan whose previous step's zeros are pending) the entries the
+// previous step sent read as zero: their bits in that step's sent mask (base and the
+// chunk start are multiples of 4, so a chunk's four bits lie in one mask word).
 template <typename GT>
-__device__ __forceinline__ void load_tile(const RkTile& t, const GT* G, const float* E, int64_t base, v4f (&gv)[4],
-                                          v4f (&ev)[4]) {
+__device__ __forceinline__ void load_tile(const RkTile& t, const GT* G, const float* E, const uint32_t* zmask,
+                                          int64_t base, v4f (&gv)[4], v4f (&ev)[4], uint32_t (&zw)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = (i * kTileThreads + int(threadIdx.x)) * 4;
     const int ec = e < t.len ? e : 0;
     gv[i] = load_g4(G + base + ec);
     ev[i] = load_nt4(E + base + ec);
+    zw[i] = zmask != nullptr ? zmask[(base + ec) >> 5] : 0u;
   }
+}
+
+__device__ __forceinline__ v4f zero_sent(v4f v, uint32_t word, int e) {
+  const uint32_t b = word >> (e & 31);
+  v.x = (b & 1u) ? 0.f : v.x;
+  v.y = (b & 2u) ? 0.f : v.y;
+  v.z = (b & 4u) ? 0.f : v.z;
+  v.w = (b & 8u) ? 0.f : v.w;
+  return v;
+}
+
+// The state word of a deferred-zero plan's workspace holds the plan's key for the errors
+// buffer while the previous step's zeros are pending there (written by rk_emit; cleared
+// by in-place materialisation and the stream-ordered reset).  It is read on the device,
+// so a step replayed from a captured graph sees changes made between replays.
+__device__ __forceinline__ bool zeros_pending(const uint64_t* state, uint64_t key, int use_state) {
+  return use_state != 0 && state != nullptr && *state == key;
 }
 
 // kEfTiles consecutive tiles of the tile table per workgroup (grid.y = worker).  The
@@ -390,15 +425,19 @@ __global__ __launch_bounds__(kTileThreads) void rk_ef_hist(const RkTile* __restr
                                                            uint32_t* __restrict__ mask, uint32_t* __restrict__ tmask,
                                                            uint32_t* __restrict__ tcnt4, uint32_t* __restrict__ cand,
                                                            uint32_t* __restrict__ ccnt4, int64_t stride, int n_layers,
-                                                           int ntiles) {
+                                                           int ntiles, const uint32_t* __restrict__ sent_prev,
+                                                           const uint64_t* __restrict__ state, uint64_t key,
+                                                           int use_state) {
   __shared__ uint32_t h1[kBins1];
   __shared__ uint32_t h2[kBins2];
   const int w = blockIdx.y;
   const int t_first = int(blockIdx.x) * kEfTiles;
   const int t_end = min(ntiles, t_first + kEfTiles);
+  const uint32_t* zmask = zeros_pending(state, key, use_state) ? sent_prev : nullptr;
   RkTile t = tiles[t_first];
   v4f gv[4], ev[4];
-  load_tile(t, G, E, int64_t(w) * stride + t.begin, gv, ev);
+  uint32_t zw[4];
+  load_tile(t, G, E, zmask, int64_t(w) * stride + t.begin, gv, ev, zw);
   for (int b = threadIdx.x; b < kBins1; b += kTileThreads) {
     h1[b] = 0u;
     h2[b] = 0u;
@@ -408,7 +447,8 @@ __global__ __launch_bounds__(kTileThreads) void rk_ef_hist(const RkTile* __restr
     const bool more = ti + 1 < t_end;
     const RkTile tn = more ? tiles[ti + 1] : t;
     v4f gn[4], en[4];
-    if (more) load_tile(tn, G, E, int64_t(w) * stride + tn.begin, gn, en);
+    uint32_t zn[4];
+    if (more) load_tile(tn, G, E, zmask, int64_t(w) * stride + tn.begin, gn, en, zn);
     const int64_t s = int64_t(w) * n_layers + t.layer;
     const uint32_t bp = pred[s];
     const int64_t base = int64_t(w) * stride + t.begin;
@@ -417,7 +457,7 @@ __global__ __launch_bounds__(kTileThreads) void rk_ef_hist(const RkTile* __restr
     for (int i = 0; i < 4; ++i) {
       const int e = (i * kTileThreads + int(threadIdx.x)) * 4;
       const int valid = max(0, min(4, t.len - e));
-      v4f mv = gv[i] + ev[i];
+      v4f mv = gv[i] + (zmask != nullptr ? zero_sent(ev[i], zw[i], e) : ev[i]);
       float* ep = E + base + e;
       if (valid == 4) {
         store_nt4(ep, mv);
@@ -457,6 +497,7 @@ __global__ __launch_bounds__(kTileThreads) void rk_ef_hist(const RkTile* __restr
       for (int i = 0; i < 4; ++i) {
         gv[i] = gn[i];
         ev[i] = en[i];
+        zw[i] = zn[i];
       }
     }
   }
@@ -864,7 +905,11 @@ __global__ __launch_bounds__(kWaveBlock) void rk_emit(const RkTile* __restrict__
                                                       const uint32_t* __restrict__ kbase, float* __restrict__ E,
                                                       int32_t* __restrict__ index, float* __restrict__ value,
                                                       uint32_t* __restrict__ kpos, int64_t stride, int64_t keep_total,
-                                                      int ntiles) {
+                                                      int ntiles, uint64_t* __restrict__ state, uint64_t key) {
+  // deferred-zero plans (state != NULL): the sent entries keep their value in E, and the
+  // state word says that the trimmed sent mask of this step is pending there
+  const bool defer = state != nullptr;
+  if (defer && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *state = key;
   const int ti = blockIdx.x * (kWaveBlock / 64) + (threadIdx.x >> 6);
   if (ti >= ntiles) return;  // whole wave
   const int lane = threadIdx.x & 63;
@@ -912,7 +957,7 @@ __global__ __launch_bounds__(kWaveBlock) void rk_emit(const RkTile* __restrict__
       const uint32_t pos = wpos[c >> 1] + (c & 1);
       ix[pos] = cidx[c];
       vx[pos] = cval[c];
-      M[cidx[c]] = 0.f;
+      if (!defer) M[cidx[c]] = 0.f;
       sent[c >> 1] |= 1u << (cidx[c] - e0 - 32 * (c >> 1));
     }
   // any further set bits, one at a time
@@ -927,7 +972,7 @@ __global__ __launch_bounds__(kWaveBlock) void rk_emit(const RkTile* __restrict__
         const int32_t idx = e0 + 32 * h + __builtin_ctz(bits);
         ix[pos] = idx;
         vx[pos] = M[idx];
-        M[idx] = 0.f;
+        if (!defer) M[idx] = 0.f;
         sent[h] |= bits & (0u - bits);
       }
     }
@@ -998,6 +1043,38 @@ __global__ __launch_bounds__(kWordThreads) void rk_update(const RkTile* __restri
   __syncthreads();
   float* u = update + t.begin;
   for (int e = q; e < t.len; e += kWordThreads) u[e] = acc[e >> 5][e & 31] * inv_w;
+}
+
+// The plain error memory of a deferred-zero plan: out = E with the entries the last step
+// sent set to zero (when its zeros are pending), per tile and worker, 16 elements per
+// thread.  In place (out == E) only the sent entries are written.
+__global__ __launch_bounds__(kTileThreads) void rk_materialize(const RkTile* __restrict__ tiles,
+                                                               const uint32_t* __restrict__ sent,
+                                                               const float* E, float* out,
+                                                               const uint64_t* __restrict__ state, uint64_t key,
+                                                               int use_state, int64_t stride) {
+  const RkTile t = tiles[blockIdx.x];
+  const int64_t base = int64_t(blockIdx.y) * stride + t.begin;
+  const bool pend = zeros_pending(state, key, use_state);
+  const bool in_place = E == out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = (i * kTileThreads + int(threadIdx.x)) * 4;
+    if (e >= t.len) continue;
+    const int valid = min(4, t.len - e);
+    const uint32_t b = pend ? (sent[(base + e) >> 5] >> (e & 31)) & 0xfu : 0u;
+    if (in_place) {
+      for (int j = 0; j < valid; ++j)
+        if (b & (1u << j)) out[base + e + j] = 0.f;
+    } else {
+      for (int j = 0; j < valid; ++j) out[base + e + j] = (b & (1u << j)) ? 0.f : E[base + e + j];
+    }
+  }
+}
+
+// One thread stores `value` into the workspace's state word (a plain vector store).
+__global__ __launch_bounds__(64) void rk_state_store(uint64_t* __restrict__ state, uint64_t value) {
+  if (threadIdx.x == 0) *state = value;
 }
 
 // ------------------------------------------------------------------ host helpers
@@ -1094,6 +1171,32 @@ struct Span {
   uintptr_t lo, hi;
 };
 
+// Same device, same error and workspace buffers as the step that left pending zeros.
+bool state_matches(const psgd_rtopk_plan* plan, const void* errors, const void* workspace, int dev) {
+  return plan->state_valid && plan->state_errors == errors && plan->state_workspace == workspace &&
+         plan->state_device == dev;
+}
+
+// The value the state word holds while `errors` has this plan's pending zeros: the plan's
+// nonce mixed with the buffer address (the splitmix64 finaliser), never 0.
+uint64_t state_key(const psgd_rtopk_plan* plan, const void* errors) {
+  uint64_t z = plan->nonce ^ (uint64_t(reinterpret_cast<uintptr_t>(errors)) * 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return (z ^ (z >> 31)) | 1u;
+}
+
+// A captured call keeps the host's decision for every replay; without usable state the
+// replays would never apply the zeros earlier replays leave pending, so such a capture
+// is refused.
+psgd_status check_capture(const char* fn, bool deferred, bool use_state, hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (deferred && !use_state && hipStreamIsCapturing(st, &cs) == hipSuccess && cs == hipStreamCaptureStatusActive)
+    return fail(PSGD_ERR_INVALID_ARG, std::string(fn) + ": a deferred-zero plan can be captured into a graph only "
+                                          "after an eager step of the plan on the same errors and workspace");
+  return PSGD_OK;
+}
+
 }  // namespace
 }  // namespace rtk
 }  // namespace psgd
@@ -1113,12 +1216,25 @@ extern "C" psgd_status psgd_rtopk_plan_create(const psgd_layer* layers, int32_t 
     return fail(PSGD_ERR_INVALID_ARG, "psgd_rtopk_plan_create: n_workers must be in 1..65535");
   if (grad_dtype != PSGD_F32 && grad_dtype != PSGD_BF16)
     return fail(PSGD_ERR_UNSUPPORTED, "psgd_rtopk_plan_create: unknown grad_dtype");
-  if (flags != 0u) return fail(PSGD_ERR_UNSUPPORTED, "psgd_rtopk_plan_create: flags must be 0");
+  if (flags & ~uint32_t(PSGD_RTOPK_FLAG_DEFERRED_ZERO))
+    return fail(PSGD_ERR_UNSUPPORTED, "psgd_rtopk_plan_create: unknown flag bits");
   psgd_rtopk_plan* plan = nullptr;
   try {
     plan = new psgd_rtopk_plan();
     plan->n_workers = n_workers;
     plan->dtype = grad_dtype;
+    plan->flags = flags;
+    {  // a key no other plan's state word is likely to hold: random bits, the clock, a counter
+      static std::atomic<uint64_t> counter{0};
+      uint64_t nonce = (++counter) * 0xD1B54A32D192ED03ull ^
+                       uint64_t(std::chrono::steady_clock::now().time_since_epoch().count());
+      try {
+        std::random_device rd;
+        nonce ^= uint64_t(rd()) << 32 | rd();
+      } catch (...) {
+      }
+      plan->nonce = nonce;
+    }
     int64_t off = 0, tile_count = 0;
     for (int32_t i = 0; i < n_layers; ++i) {
       const int64_t rows = layers[i].rows, cols = layers[i].cols;
@@ -1209,6 +1325,8 @@ extern "C" psgd_status psgd_rtopk_plan_create(const psgd_layer* layers, int32_t 
       *a = ws;
       ws = a256(ws + W * ntiles * 4);
     }
+    plan->ws_state = ws;  // one 64-bit state word (deferred-zero plans)
+    ws += 256;
     plan->workspace_bytes = ws;
     const uint64_t gb = grad_dtype == PSGD_BF16 ? 2 : 4;
     plan->message_bytes = uint64_t(plan->keep_total) * 8;
@@ -1345,9 +1463,17 @@ extern "C" psgd_status psgd_rtopk_step(psgd_rtopk_plan* plan, const void* grads,
       if (a.lo < b.hi && b.lo < a.hi)
         return fail(PSGD_ERR_INVALID_ARG, std::string(fn) + ": " + a.name + " and " + b.name + " overlap");
     }
-  DevTables dt{};
-  psgd_status s = device_tables(plan, &dt);
+  int dev = 0;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) return hip_fail("hipGetDevice", he);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool deferred = (plan->flags & PSGD_RTOPK_FLAG_DEFERRED_ZERO) != 0;
+  const bool use_state = deferred && state_matches(plan, errors, workspace, dev);
+  psgd_status s = check_capture(fn, deferred, use_state, st);
   if (s != PSGD_OK) return s;
+  DevTables dt{};
+  if ((s = device_tables(plan, &dt)) != PSGD_OK) return s;
+  plan->state_valid = false;
 
   char* ws = static_cast<char*>(workspace);
   auto u32 = [&](uint64_t off) { return reinterpret_cast<uint32_t*>(ws + off); };
@@ -1363,8 +1489,10 @@ extern "C" psgd_status psgd_rtopk_step(psgd_rtopk_plan* plan, const void* grads,
   uint32_t* ttie = u32(plan->ws_ttie);
   uint32_t *tiebase = u32(plan->ws_tiebase), *tbase = u32(plan->ws_tbase);
   uint32_t *kcnt = u32(plan->ws_kcnt), *kbase = u32(plan->ws_kbase);
+  uint64_t* state = deferred ? reinterpret_cast<uint64_t*>(ws + plan->ws_state) : nullptr;
+  const uint64_t key = state_key(plan, errors);
+  const int ust = use_state ? 1 : 0;
 
-  hipStream_t st = static_cast<hipStream_t>(stream);
   const int nl = int(plan->layers.size());
   const int ntiles = int(plan->tiles.size());
   const int64_t sstride = int64_t(stride);
@@ -1383,10 +1511,12 @@ extern "C" psgd_status psgd_rtopk_step(psgd_rtopk_plan* plan, const void* grads,
   if (plan->dtype == PSGD_BF16)
     s = launch(plan, kEfHist, rk_ef_hist<uint16_t>, egrid, dim3(kTileThreads), st, T,
                static_cast<const uint16_t*>(grads), errors, cpred, hist1, hist2, mask, tmask, tcnt4, cand, ccnt4,
-               sstride, nl, ntiles);
+               sstride, nl, ntiles, static_cast<const uint32_t*>(kmask), static_cast<const uint64_t*>(state), key,
+               ust);
   else
     s = launch(plan, kEfHist, rk_ef_hist<float>, egrid, dim3(kTileThreads), st, T, static_cast<const float*>(grads),
-               errors, cpred, hist1, hist2, mask, tmask, tcnt4, cand, ccnt4, sstride, nl, ntiles);
+               errors, cpred, hist1, hist2, mask, tmask, tcnt4, cand, ccnt4, sstride, nl, ntiles,
+               static_cast<const uint32_t*>(kmask), static_cast<const uint64_t*>(state), key, ust);
   if (s != PSGD_OK) return s;
   if ((s = launch(plan, kSelect, rk_select, sgrid, dim3(kSelThreads), st, L, static_cast<const uint32_t*>(hist1),
                   hist2, pred, seg, nl)) != PSGD_OK)
@@ -1424,11 +1554,70 @@ extern "C" psgd_status psgd_rtopk_step(psgd_rtopk_plan* plan, const void* grads,
     return s;
   if ((s = launch(plan, kEmit, rk_emit, wgrid, dim3(kWaveBlock), st, T, L, kmask,
                   static_cast<const uint32_t*>(kbase), errors, index, value, kpos, sstride, plan->keep_total,
-                  ntiles)) != PSGD_OK)
+                  ntiles, state, key)) != PSGD_OK)
     return s;
   if (update != nullptr)
     s = launch(plan, kUpdate, rk_update, dim3(unsigned(ntiles)), dim3(kWordThreads), st, T, L,
                static_cast<const uint32_t*>(kmask), static_cast<const uint32_t*>(kpos),
                static_cast<const float*>(value), update, int(W), sstride, plan->keep_total, 1.0f / float(W));
+  if (s == PSGD_OK && deferred) {
+    plan->state_valid = true;
+    plan->state_errors = errors;
+    plan->state_workspace = workspace;
+    plan->state_device = dev;
+  }
   return s;
+}
+
+extern "C" psgd_status psgd_rtopk_errors_materialize(psgd_rtopk_plan* plan, const float* errors, float* out,
+                                                     void* workspace, void* stream) {
+  static const char* fn = "psgd_rtopk_errors_materialize";
+  if (plan == nullptr) return fail(PSGD_ERR_INVALID_ARG, std::string(fn) + ": plan is NULL");
+  const uintptr_t ptrs[] = {uintptr_t(errors), uintptr_t(out), uintptr_t(workspace)};
+  for (uintptr_t p : ptrs)
+    if (p == 0 || p % 16 != 0) return fail(PSGD_ERR_INVALID_ARG, std::string(fn) + ": NULL or misaligned pointer");
+  const uint64_t bytes = uint64_t(plan->n_workers) * uint64_t(plan->worker_stride) * 4;
+  const uintptr_t e0 = uintptr_t(errors), o0 = uintptr_t(out);
+  if (out != errors && e0 < o0 + bytes && o0 < e0 + bytes)
+    return fail(PSGD_ERR_INVALID_ARG, std::string(fn) + ": out partly overlaps errors (pass the same pointer for in place)");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool deferred = (plan->flags & PSGD_RTOPK_FLAG_DEFERRED_ZERO) != 0;
+  const bool use_state = deferred && state_matches(plan, errors, workspace, dev);
+  if (!use_state && out == errors) return PSGD_OK;  // nothing pending: already plain
+  psgd_status s = check_capture(fn, deferred, use_state, st);
+  if (s != PSGD_OK) return s;
+  DevTables dt{};
+  if ((s = device_tables(plan, &dt)) != PSGD_OK) return s;
+  char* ws = static_cast<char*>(workspace);
+  uint64_t* state = deferred ? reinterpret_cast<uint64_t*>(ws + plan->ws_state) : nullptr;
+  hipLaunchKernelGGL(rk_materialize, dim3(unsigned(plan->tiles.size()), unsigned(plan->n_workers)),
+                     dim3(kTileThreads), 0, st, static_cast<const RkTile*>(dt.tiles),
+                     reinterpret_cast<const uint32_t*>(ws + plan->ws_kmask), errors, out,
+                     static_cast<const uint64_t*>(state), state_key(plan, errors), use_state ? 1 : 0,
+                     plan->worker_stride);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail("launch rk_materialize", e);
+  if (use_state && out == errors) {  // the buffer now holds plain errors
+    plan->state_valid = false;
+    hipLaunchKernelGGL(rk_state_store, dim3(1), dim3(64), 0, st, state, uint64_t(0));
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail("launch rk_state_store", e);
+  }
+  return PSGD_OK;
+}
+
+extern "C" psgd_status psgd_rtopk_plan_reset_state(psgd_rtopk_plan* plan, void* workspace, void* stream) {
+  static const char* fn = "psgd_rtopk_plan_reset_state";
+  if (plan == nullptr) return fail(PSGD_ERR_INVALID_ARG, std::string(fn) + ": plan is NULL");
+  if (workspace == nullptr || uintptr_t(workspace) % 16 != 0)
+    return fail(PSGD_ERR_INVALID_ARG, std::string(fn) + ": workspace is NULL or misaligned");
+  plan->state_valid = false;
+  if (!(plan->flags & PSGD_RTOPK_FLAG_DEFERRED_ZERO)) return PSGD_OK;
+  hipLaunchKernelGGL(rk_state_store, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
+                     reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + plan->ws_state), uint64_t(0));
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PSGD_OK : hip_fail("launch rk_state_store", e);
 }

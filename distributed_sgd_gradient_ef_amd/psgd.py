@@ -33,6 +33,7 @@ PSGD_FLAG_NESTEROV = 0x1
 PSGD_FLAG_CARRY_ERROR_MEAN = 0x2
 PSGD_FLAG_DEFERRED_ERROR = 0x4
 PSGD_FLAG_LOCAL_Q_ERROR = 0x8
+PSGD_RTOPK_FLAG_DEFERRED_ZERO = 0x1
 
 EXPORTED = [
     "psgd_plan_create", "psgd_plan_sizes", "psgd_plan_layer_info", "psgd_plan_destroy",
@@ -42,6 +43,7 @@ EXPORTED = [
     "psgd_plan_set_power_iterations", "psgd_status_string", "psgd_last_error",
     "psgd_rtopk_plan_create", "psgd_rtopk_plan_sizes", "psgd_rtopk_plan_layer_info", "psgd_rtopk_plan_destroy",
     "psgd_rtopk_step", "psgd_rtopk_plan_set_timing", "psgd_rtopk_plan_kernel_stats",
+    "psgd_rtopk_errors_materialize", "psgd_rtopk_plan_reset_state",
     "psgd_atomo_plan_create", "psgd_atomo_plan_sizes", "psgd_atomo_plan_layer_info", "psgd_atomo_plan_destroy",
     "psgd_atomo_step", "psgd_atomo_plan_set_timing", "psgd_atomo_plan_kernel_stats",
 ]
@@ -151,6 +153,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.psgd_rtopk_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.psgd_rtopk_plan_set_timing.argtypes = [vp, i32]
     lib.psgd_rtopk_plan_kernel_stats.argtypes = [vp, ctypes.POINTER(_KernelStat), i32, ctypes.POINTER(i32), i32]
+    lib.psgd_rtopk_errors_materialize.argtypes = [vp, vp, vp, vp, vp]
+    lib.psgd_rtopk_plan_reset_state.argtypes = [vp, vp, vp]
     lib.psgd_atomo_plan_create.argtypes = [ctypes.POINTER(_Layer), i32, ctypes.c_double, i32, ctypes.c_uint32,
                                            ctypes.POINTER(vp)]
     lib.psgd_atomo_plan_sizes.argtypes = [vp, ctypes.POINTER(_AtomoSizes)]
@@ -405,6 +409,23 @@ def psgd_rtopk_step(plan: RtopkPlan, grads, errors, ranks, index, value, update,
             plan.handle, _ptr(grads), _ptr(errors), _ptr(ranks), _ptr(index), _ptr(value), _ptr(update),
             _ptr(workspace), _stream(stream, grads)))
 
+def psgd_rtopk_errors_materialize(plan: RtopkPlan, errors, out, workspace, stream=None) -> None:
+    """Plain error memory of a deferred-zero plan's error buffer into `out` (may be `errors`)."""
+    import torch
+
+    with torch.cuda.device(errors.device):
+        _check(load_library().psgd_rtopk_errors_materialize(plan.handle, _ptr(errors), _ptr(out), _ptr(workspace),
+                                                            _stream(stream, errors)))
+
+
+def psgd_rtopk_plan_reset_state(plan: RtopkPlan, workspace, stream=None) -> None:
+    """Forget the pending zeros of a deferred-zero plan (host view and, on the stream, the
+    workspace's state word)."""
+    import torch
+
+    with torch.cuda.device(workspace.device):
+        _check(load_library().psgd_rtopk_plan_reset_state(plan.handle, _ptr(workspace), _stream(stream, workspace)))
+
 
 # ------------------------------------------------------------------------ Spectral-ATOMO
 @dataclass
@@ -435,6 +456,7 @@ class AtomoPlan:
                 psgd_atomo_plan_destroy(self)
             except Exception:
                 pass
+
 
 
 def psgd_atomo_plan_create(shapes: Sequence[Tuple[int, int]], budget: float, n_workers: int,

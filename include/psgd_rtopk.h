@@ -52,6 +52,24 @@ extern "C" {
 
 typedef struct psgd_rtopk_plan psgd_rtopk_plan;
 
+/* Plan flag: deferred zeroing of the sent entries.  A step then leaves the error buffer
+ * holding M_w at the entries it sent (everything else is E'_w as usual), and keeps that
+ * step's sent mask in the workspace; the next step's first pass reads E with those
+ * entries as zero (one mask bit per element, read with E) instead of this step writing
+ * them one by one.  Only the error buffer's representation differs: the lists, the
+ * update and the next step's results are the same.  psgd_rtopk_errors_materialize
+ * writes the plain E'.  Contract: between consecutive steps the caller passes the same
+ * errors and workspace pointers and modifies neither (the workspace is then not
+ * scratch).  A step applies the pending zeros only when the plan's previous step ran on
+ * this device with these errors and workspace pointers and nothing reset it since (the
+ * host's view), and the workspace's state word holds the plan's key for these errors
+ * (the device's view: written by the step, cleared by in-place materialisation and by
+ * psgd_rtopk_plan_reset_state on the stream).  So a step captured into a HIP graph keeps
+ * working when the buffers change between replays through those calls; a capture
+ * without usable state (no eager step yet on these buffers) is refused with
+ * PSGD_ERR_INVALID_ARG. */
+#define PSGD_RTOPK_FLAG_DEFERRED_ZERO 0x1u
+
 typedef struct psgd_rtopk_layer_info {
   int64_t rows, cols;
   int64_t numel;       /* rows * cols */
@@ -77,7 +95,8 @@ typedef struct psgd_rtopk_sizes {
 
 /* Build a plan for `n_layers` tensors with per-tensor counts top[l] = r, keep[l] = k
  * (1 <= k <= r <= rows*cols < 2^31), W = n_workers in 1..65535 workers and gradients of
- * grad_dtype.  flags must be 0.  Host only. */
+ * grad_dtype.  flags: 0 or PSGD_RTOPK_FLAG_DEFERRED_ZERO (other bits:
+ * PSGD_ERR_UNSUPPORTED).  Host only. */
 psgd_status psgd_rtopk_plan_create(const psgd_layer* layers, int32_t n_layers, const int64_t* top,
                                    const int64_t* keep, int32_t n_workers, psgd_dtype grad_dtype,
                                    uint32_t flags, psgd_rtopk_plan** out);
@@ -87,15 +106,34 @@ psgd_status psgd_rtopk_plan_destroy(psgd_rtopk_plan* plan);
 
 /* One step for every tensor of the plan and every worker:
  *   grads     [W][worker_stride] grad_dtype, read only
- *   errors    [W][worker_stride] float32, E in, E' out
+ *   errors    [W][worker_stride] float32, E in, E' out (deferred-zero plans: see the flag)
  *   ranks     [W][top_total] uint32, read only
  *   index     [W][keep_total] int32 out
  *   value     [W][keep_total] float32 out
  *   update    [worker_stride] float32 out, or NULL (then not computed)
- *   workspace workspace_bytes of device memory, contents need not be preserved
+ *   workspace workspace_bytes of device memory; contents need not be preserved between
+ *             steps, except for deferred-zero plans (see the flag)
  * Asynchronous on `stream` (a hipStream_t; NULL = default stream). */
 psgd_status psgd_rtopk_step(psgd_rtopk_plan* plan, const void* grads, float* errors, const uint32_t* ranks,
                             int32_t* index, float* value, float* update, void* workspace, void* stream);
+
+/* The plain error memory E' of a deferred-zero plan: out = errors with the entries the
+ * last step sent set to zero, if that step's zeros are pending in these errors (see the
+ * flag), else a copy.  out may be errors (in place: only the pending entries are written,
+ * and the state word is cleared on the stream, so later steps treat the buffer as plain)
+ * or a separate [W][worker_stride] float32 buffer (the pending state is kept).  Elements
+ * of padding are not written.  For a plan without the flag, out is a copy of errors (in
+ * place: nothing to do).  Asynchronous on `stream`.  PSGD_ERR_INVALID_ARG for NULL or
+ * misaligned pointers or partly overlapping buffers. */
+psgd_status psgd_rtopk_errors_materialize(psgd_rtopk_plan* plan, const float* errors, float* out, void* workspace,
+                                          void* stream);
+
+/* Forget a deferred-zero plan's pending zeros (after writing errors or the workspace
+ * yourself): the host's view at once, and the workspace's state word by a one-thread
+ * kernel on `stream` (so replays of a captured step see it too; the call may itself be
+ * captured).  Plans without the flag enqueue nothing.  PSGD_ERR_INVALID_ARG for a NULL
+ * plan or a NULL or misaligned workspace. */
+psgd_status psgd_rtopk_plan_reset_state(psgd_rtopk_plan* plan, void* workspace, void* stream);
 
 /* Kernel timing as psgd_plan_set_timing / psgd_plan_kernel_stats.  Kernel names:
  * "rk_zero", "rk_ef_hist", "rk_select", "rk_mark", "rk_pick2", "rk_level3", "rk_rule",

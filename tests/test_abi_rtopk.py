@@ -43,7 +43,7 @@ def test_plan_create_rejects_bad_arguments():
         _plan(dtype=7)
     assert e.value.status == psgd.PSGD_ERR_UNSUPPORTED
     with pytest.raises(psgd.PsgdError) as e:
-        psgd.psgd_rtopk_plan_create(SHAPES, TOPS, KEEPS, 2, psgd.PSGD_F32, flags=1)
+        psgd.psgd_rtopk_plan_create(SHAPES, TOPS, KEEPS, 2, psgd.PSGD_F32, flags=2)
     assert e.value.status == psgd.PSGD_ERR_UNSUPPORTED
     with pytest.raises(psgd.PsgdError) as e:
         psgd.psgd_rtopk_plan_create([(65536, 32768)], [1], [1], 1)   # 2^31 elements
@@ -133,3 +133,21 @@ def test_pack_rows_roundtrip():
     assert rows.shape == (3, sum(TOPS))
     for li, a in enumerate(per):
         assert np.array_equal(psgd.row_slice(plan, rows, li, "top"), a)
+
+
+def test_deferred_zero_flag_and_its_calls_check_arguments_first():
+    plain = _plan()
+    lib = psgd.load_library()
+    d = psgd.psgd_rtopk_plan_create(SHAPES, TOPS, KEEPS, 4, psgd.PSGD_F32, flags=psgd.PSGD_RTOPK_FLAG_DEFERRED_ZERO)
+    assert d.sizes["workspace_bytes"] == plain.sizes["workspace_bytes"]  # the state block is always there
+    n = 4 * d.sizes["worker_stride"] * 4
+    for bad in [(None, 0x2000000, 0x3000000), (0x1000000, None, 0x3000000), (0x1000000, 0x2000000, None),
+                (0x1000008, 0x2000000, 0x3000000), (0x1000000, 0x1000000 + 16, 0x3000000)]:
+        assert lib.psgd_rtopk_errors_materialize(d.handle, *bad, None) == psgd.PSGD_ERR_INVALID_ARG
+    assert n > 16
+    assert lib.psgd_rtopk_errors_materialize(None, 0x1000000, 0x2000000, 0x3000000, None) == psgd.PSGD_ERR_INVALID_ARG
+    assert lib.psgd_rtopk_plan_reset_state(None, 0x1000, None) == psgd.PSGD_ERR_INVALID_ARG
+    assert lib.psgd_rtopk_plan_reset_state(d.handle, None, None) == psgd.PSGD_ERR_INVALID_ARG
+    assert lib.psgd_rtopk_plan_reset_state(d.handle, 0x1008, None) == psgd.PSGD_ERR_INVALID_ARG
+    # without the flag nothing is enqueued (no device call is made)
+    assert lib.psgd_rtopk_plan_reset_state(plain.handle, 0x1000, None) == psgd.PSGD_OK

@@ -183,3 +183,68 @@ def test_cross_step_state_changes_between_replays(mode):
         torch.cuda.synchronize()
         for j, (x, y) in enumerate(zip([a["e"], a["q"], a["p"], a["u"]], [b["e"], b["q"], b["p"], b["u"]])):
             assert torch.equal(x, y), f"{mode}: replay {i}, output {j} differs from the eager step"
+
+
+def test_rtopk_deferred_state_changes_between_replays():
+    """A captured step of a deferred-zero rTop-k plan, replayed while its pending zeros
+    change between replays (new gradients and ranks every replay, an in-place
+    materialisation, errors written anew with the stream-ordered reset): every replay
+    equals an eager plan given the same calls, bit for bit."""
+    shapes = [(64, 27), (1, 64), (10, 512), (3, 5), (1, 5000)]
+    tops, keeps = [40, 4, 100, 15, 120], [20, 1, 50, 15, 60]
+    W = 3
+    rs = np.random.default_rng(605)
+    print("[graphs] case rtopk deferred zeros between replays", flush=True)
+
+    def make():
+        plan = P.psgd_rtopk_plan_create(shapes, tops, keeps, W, P.PSGD_F32, P.PSGD_RTOPK_FLAG_DEFERRED_ZERO)
+        s = plan.sizes
+        return dict(plan=plan, g=torch.zeros((W, s["worker_stride"]), device=DEV),
+                    e=torch.zeros((W, s["worker_stride"]), device=DEV),
+                    ranks=torch.zeros((W, s["top_total"]), dtype=torch.int32, device=DEV),
+                    index=torch.zeros((W, s["keep_total"]), dtype=torch.int32, device=DEV),
+                    value=torch.zeros((W, s["keep_total"]), device=DEV),
+                    u=torch.zeros(s["worker_stride"], device=DEV),
+                    ws=torch.zeros(s["workspace_bytes"], dtype=torch.uint8, device=DEV))
+
+    a, b = make(), make()
+    ld = a["plan"].sizes["worker_stride"]
+
+    def new_inputs():
+        g = torch.from_numpy(rs.standard_normal((W, ld)).astype(np.float32)).to(DEV)
+        ranks = P.pack_rows(a["plan"], [np.stack([rs.permutation(t) for _ in range(W)]) for t in tops], "top",
+                            np.uint32).view(np.int32)
+        r = torch.from_numpy(ranks).to(DEV)
+        for st in (a, b):
+            st["g"].copy_(g)
+            st["ranks"].copy_(r)
+
+    def step(st):
+        P.psgd_rtopk_step(st["plan"], st["g"], st["e"], st["ranks"], st["index"], st["value"], st["u"], st["ws"])
+
+    for _ in range(2):
+        new_inputs()
+        step(a)
+        step(b)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(a)
+    torch.cuda.synchronize()
+    for i in range(7):
+        if i == 2:
+            P.psgd_rtopk_errors_materialize(a["plan"], a["e"], a["e"], a["ws"])
+            P.psgd_rtopk_errors_materialize(b["plan"], b["e"], b["e"], b["ws"])
+        if i == 4:
+            e = torch.from_numpy(0.3 * rs.standard_normal((W, ld)).astype(np.float32)).to(DEV)
+            for st in (a, b):
+                st["e"].copy_(e)
+                P.psgd_rtopk_plan_reset_state(st["plan"], st["ws"])
+        new_inputs()
+        g.replay()
+        step(b)
+        torch.cuda.synchronize()
+        outs_a = [a["e"], a["index"], a["value"], a["u"]]
+        outs_b = [b["e"], b["index"], b["value"], b["u"]]
+        for j, (x, y) in enumerate(zip(outs_a, outs_b)):
+            assert torch.equal(x, y), f"rtopk deferred: replay {i}, output {j} differs from the eager step"

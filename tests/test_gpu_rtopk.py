@@ -20,12 +20,15 @@ DEV = "cuda:0"
 
 
 class RtopkRun:
-    """Device buffers of one rTop-k plan, filled with garbage where the step must write."""
+    """Device buffers of one rTop-k plan, filled with garbage where the step must write.
+    deferred: a PSGD_RTOPK_FLAG_DEFERRED_ZERO plan, whose errors are read back through
+    psgd_rtopk_errors_materialize (into a separate buffer, so the plan's state is kept)."""
 
-    def __init__(self, shapes, tops, keeps, W, bf16=False):
-        self.plan = P.psgd_rtopk_plan_create(shapes, tops, keeps, W, P.PSGD_BF16 if bf16 else P.PSGD_F32)
+    def __init__(self, shapes, tops, keeps, W, bf16=False, deferred=False):
+        self.plan = P.psgd_rtopk_plan_create(shapes, tops, keeps, W, P.PSGD_BF16 if bf16 else P.PSGD_F32,
+                                             P.PSGD_RTOPK_FLAG_DEFERRED_ZERO if deferred else 0)
         s = self.plan.sizes
-        self.W, self.bf16 = W, bf16
+        self.W, self.bf16, self.deferred = W, bf16, deferred
         self.stride = s["worker_stride"]
         self.g = torch.zeros((W, self.stride), dtype=torch.bfloat16 if bf16 else torch.float32, device=DEV)
         self.e = torch.zeros((W, self.stride), dtype=torch.float32, device=DEV)
@@ -55,8 +58,16 @@ class RtopkRun:
     def grads_f32(self, li):
         return P.unpack(self.plan, self.g.float().cpu().numpy(), li).reshape(self.W, -1)
 
+    def plain_errors(self):
+        if not self.deferred:
+            return self.e
+        out = torch.full_like(self.e, float("nan"))
+        P.psgd_rtopk_errors_materialize(self.plan, self.e, out, self.ws)
+        torch.cuda.synchronize()
+        return out
+
     def errors(self, li):
-        return P.unpack(self.plan, self.e.cpu().numpy(), li).reshape(self.W, -1)
+        return P.unpack(self.plan, self.plain_errors().cpu().numpy(), li).reshape(self.W, -1)
 
     def sent(self, li):
         idx = P.row_slice(self.plan, self.index.cpu().numpy(), li, "keep")
@@ -120,14 +131,15 @@ def _ranks(rng, W, tops):
 RAGGED = [(64, 27), (1, 64), (10, 512), (3, 5), (1, 1), (5, 4099), (4096, 1), (1, 2 * 4096 + 33)]
 
 
+@pytest.mark.parametrize("deferred", [False, True], ids=["plain", "deferred"])
 @pytest.mark.parametrize("W", [1, 3, 4])
-def test_ragged_multilayer_three_steps(W):
-    print(f"\n[case] ragged multilayer W={W}", flush=True)
+def test_ragged_multilayer_three_steps(W, deferred):
+    print(f"\n[case] ragged multilayer W={W} deferred={deferred}", flush=True)
     rng = np.random.default_rng(100 + W)
     tops, keeps = _counts(RAGGED, 0.05, 3)
     tops[4], keeps[4] = 1, 1            # a single element
     tops[3], keeps[3] = 15, 15          # everything sent
-    run = RtopkRun(RAGGED, tops, keeps, W)
+    run = RtopkRun(RAGGED, tops, keeps, W, deferred=deferred)
     E = [np.zeros((W, r * c), np.float32) for r, c in RAGGED]
     for step in range(3):
         G = [rng.standard_normal((W, r * c)).astype(np.float32) for r, c in RAGGED]
@@ -166,15 +178,16 @@ def test_ties_zeros_and_one_bin():
         compare(run, li, st)
 
 
-def test_error_feedback_many_steps():
+@pytest.mark.parametrize("deferred", [False, True], ids=["plain", "deferred"])
+def test_error_feedback_many_steps(deferred):
     """Twelve steps with error feedback: entries that stay unsent pile up just under the
     threshold, which crowds the boundary bins; every step is compared exactly."""
-    print("\n[case] 12 EF steps W=4", flush=True)
+    print(f"\n[case] 12 EF steps W=4 deferred={deferred}", flush=True)
     W = 4
     shapes = [(512, 2304), (256, 1152), (64, 576), (1, 512), (10, 512)]
     tops, keeps = _counts(shapes, 0.01, 2)
     rng = np.random.default_rng(14)
-    run = RtopkRun(shapes, tops, keeps, W)
+    run = RtopkRun(shapes, tops, keeps, W, deferred=deferred)
     E = [np.zeros((W, r * c), np.float32) for r, c in shapes]
     for step in range(12):
         G = [(0.05 * rng.standard_normal((W, r * c))).astype(np.float32) for r, c in shapes]
@@ -188,22 +201,26 @@ def test_error_feedback_many_steps():
         E = [ref[li].errors for li in range(len(shapes))]
 
 
-def test_bf16_gradients():
-    print("\n[case] bf16 gradients W=4", flush=True)
+@pytest.mark.parametrize("deferred", [False, True], ids=["plain", "deferred"])
+def test_bf16_gradients(deferred):
+    print(f"\n[case] bf16 gradients W=4 deferred={deferred}", flush=True)
     W = 4
     rng = np.random.default_rng(8)
     shapes = RAGGED[:6]
     tops, keeps = _counts(shapes, 0.03, 2)
-    run = RtopkRun(shapes, tops, keeps, W, bf16=True)
+    run = RtopkRun(shapes, tops, keeps, W, bf16=True, deferred=deferred)
     E = [(0.1 * rng.standard_normal((W, r * c))).astype(np.float32) for r, c in shapes]
-    G = [WL.to_bf16_values(rng.standard_normal((W, r * c)).astype(np.float32)) for r, c in shapes]
-    R = _ranks(rng, W, tops)
-    run.set_grads(G)
     run.set_errors(E)
-    run.set_ranks(R)
-    run.step()
-    for li, st in oracle_step(run, G, E, tops, keeps, R, range(len(shapes))).items():
-        compare(run, li, st)
+    for step in range(2):
+        G = [WL.to_bf16_values(rng.standard_normal((W, r * c)).astype(np.float32)) for r, c in shapes]
+        R = _ranks(rng, W, tops)
+        run.set_grads(G)
+        run.set_ranks(R)
+        run.step()
+        ref = oracle_step(run, G, E, tops, keeps, R, range(len(shapes)))
+        for li, st in ref.items():
+            compare(run, li, st)
+        E = [ref[li].errors for li in range(len(shapes))]
 
 
 def test_invalid_ranks_follow_the_oracle():
@@ -225,25 +242,32 @@ def test_invalid_ranks_follow_the_oracle():
         compare(run, li, st)
 
 
-def test_nonfinite_values():
-    print("\n[case] NaN and infinities", flush=True)
+@pytest.mark.parametrize("deferred", [False, True], ids=["plain", "deferred"])
+def test_nonfinite_values(deferred):
+    """NaN and infinities are sent first (they sort on top); a NaN that was sent leaves a
+    zero error, which the next step (deferred: reading the pending zero) adds to."""
+    print(f"\n[case] NaN and infinities deferred={deferred}", flush=True)
     W = 2
     rng = np.random.default_rng(10)
     shapes = [(1, 300), (10, 100)]
     tops, keeps = [20, 50], [10, 25]
-    G = [rng.standard_normal((W, r * c)).astype(np.float32) for r, c in shapes]
-    G[0][0, 5] = np.nan
-    G[0][1, 7] = np.inf
-    G[0][1, 8] = -np.inf
-    G[1][0, 3:6] = np.inf
-    R = _ranks(rng, W, tops)
-    run = RtopkRun(shapes, tops, keeps, W)
-    run.set_grads(G)
-    run.set_ranks(R)
-    run.step()
+    run = RtopkRun(shapes, tops, keeps, W, deferred=deferred)
     E = [np.zeros((W, r * c), np.float32) for r, c in shapes]
-    for li, st in oracle_step(run, G, E, tops, keeps, R, range(2)).items():
-        compare(run, li, st, nan_ok=True)
+    for step in range(2):
+        G = [rng.standard_normal((W, r * c)).astype(np.float32) for r, c in shapes]
+        if step == 0:
+            G[0][0, 5] = np.nan
+            G[0][1, 7] = np.inf
+            G[0][1, 8] = -np.inf
+            G[1][0, 3:6] = np.inf
+        R = _ranks(rng, W, tops)
+        run.set_grads(G)
+        run.set_ranks(R)
+        run.step()
+        ref = oracle_step(run, G, E, tops, keeps, R, range(2))
+        for li, st in ref.items():
+            compare(run, li, st, nan_ok=True)
+        E = [ref[li].errors for li in range(2)]
 
 
 def test_update_null_and_determinism():
@@ -287,16 +311,16 @@ def test_timing_reports_every_kernel():
     assert all(n == 2 and ms > 0 for n, ms in stats.values())
 
 
-def _device_workload_run(name, steps, layers_checked):
+def _device_workload_run(name, steps, layers_checked, deferred=False):
     wl = WL.workload(name)
     shapes = [s for _, s in wl.shapes]
     tops, keeps = WL.rtopk_counts(wl)
     W = wl.workers
-    run = RtopkRun(shapes, tops, keeps, W)
+    run = RtopkRun(shapes, tops, keeps, W, deferred=deferred)
     layout = [(L.offset, L.rows, L.cols) for L in run.plan.layers]
     cache = {}
     for step in range(steps):
-        print(f"[case] {name} step {step}", flush=True)
+        print(f"[case] {name} step {step} deferred={deferred}", flush=True)
         E = {li: run.errors(li) for li in layers_checked}
         WL.device_grads(wl, step, layout, run.g, cache)
         R = [np.stack([WL.rtopk_ranks(wl, step, w, li, tops[li]) for w in range(W)]) for li in range(len(shapes))]
@@ -309,16 +333,60 @@ def _device_workload_run(name, steps, layers_checked):
     return run
 
 
-def test_resnet18_rtopk_workload():
-    """ResNet-18 shapes, W=16, 1% sent from the top 2%, two steps with error feedback;
-    the oracle checks the largest matrices, a middle one and small tensors."""
-    _device_workload_run("resnet18_rtopk", 2, [0, 1, 2, 14, 17, 19, 20, 21, 40, 61])
+@pytest.mark.parametrize("deferred", [False, True], ids=["plain", "deferred"])
+def test_resnet18_rtopk_workload(deferred):
+    """ResNet-18 shapes, W=16, 1% sent from the top 2%, with error feedback (two steps;
+    three for the deferred-zero plan the benchmark times, so two steps read pending
+    zeros); the oracle checks the largest matrices, a middle one and small tensors."""
+    _device_workload_run("resnet18_rtopk", 3 if deferred else 2, [0, 1, 2, 14, 17, 19, 20, 21, 40, 61], deferred)
 
 
-def test_lstm_rtopk_workload():
-    """Tall LSTM shapes with the 5%-row-sparse embedding gradient, W=8, one step; the
-    tied embedding (21.6M entries) and one dense matrix against the oracle."""
-    _device_workload_run("lstm_rtopk", 1, [0, 3])
+@pytest.mark.parametrize("deferred", [False, True], ids=["plain", "deferred"])
+def test_lstm_rtopk_workload(deferred):
+    """Tall LSTM shapes with the 5%-row-sparse embedding gradient, W=8 (one step; two for
+    the deferred-zero plan); the tied embedding (21.6M entries) and one dense matrix
+    against the oracle."""
+    _device_workload_run("lstm_rtopk", 2 if deferred else 1, [0, 3], deferred)
+
+
+def test_deferred_materialize_in_place_and_reset():
+    """In-place materialisation writes the pending zeros and makes the buffer plain (the
+    next step applies nothing more); errors written from outside followed by
+    psgd_rtopk_plan_reset_state are taken as plain; a new workspace also drops the
+    pending state (the host's view)."""
+    print("\n[case] rtopk deferred materialise in place / reset", flush=True)
+    W = 3
+    shapes = [(64, 27), (1, 5000), (20, 333)]
+    tops, keeps = _counts(shapes, 0.05, 2)
+    rng = np.random.default_rng(15)
+    run = RtopkRun(shapes, tops, keeps, W, deferred=True)
+    E = [np.zeros((W, r * c), np.float32) for r, c in shapes]
+
+    def step_and_check(E):
+        G = [rng.standard_normal((W, r * c)).astype(np.float32) for r, c in shapes]
+        R = _ranks(rng, W, tops)
+        run.set_grads(G)
+        run.set_ranks(R)
+        run.step()
+        ref = oracle_step(run, G, E, tops, keeps, R, range(len(shapes)))
+        for li, st in ref.items():
+            compare(run, li, st)
+        return [ref[li].errors for li in range(len(shapes))]
+
+    E = step_and_check(E)
+    P.psgd_rtopk_errors_materialize(run.plan, run.e, run.e, run.ws)  # in place
+    torch.cuda.synchronize()
+    got = [P.unpack(run.plan, run.e.cpu().numpy(), li).reshape(W, -1) for li in range(len(shapes))]
+    for a, b in zip(got, E):
+        assert np.array_equal(_bits(a), _bits(b))
+    E = step_and_check(E)
+    E = [(0.2 * rng.standard_normal((W, r * c))).astype(np.float32) for r, c in shapes]
+    run.set_errors(E)
+    P.psgd_rtopk_plan_reset_state(run.plan, run.ws)
+    E = step_and_check(E)
+    run.ws = torch.full_like(run.ws, 0xCD)  # another workspace: the pending zeros are lost, so
+    run.set_errors(E)                       # the caller passes plain errors, as the contract asks
+    E = step_and_check(E)
 
 
 def test_largest_tensor():
