@@ -112,18 +112,22 @@ def rtopk_kernel_bytes(plan, dtype_bytes: int, deferred: bool = True) -> dict:
 
 def atomo_kernel_work(plan) -> dict:
     """Algorithmic work per launch of the Spectral-ATOMO kernels: flops of the Gram
-    matrices (lower triangle, k (k + 1) L multiply-adds) and of the Householder
-    tridiagonalisation (4/3 k^3 per matrix and worker); HBM bytes of the passes over G."""
+    matrices (lower triangle, k (k + 1) L multiply-adds), of the reduction to a band of
+    half-bandwidth 16 (the classical count of a symmetric Householder reduction, 4/3 k^3
+    per matrix and worker) and of the bulge chasing (about 12 b^2 flops for each of the
+    k^2 / (2 b) reflectors, b = 16); HBM bytes of the passes over G."""
     s = plan.sizes
     W = s["n_workers"]
-    gram = tri = gbytes = 0
+    gram = band = chase = gbytes = 0
     for L in plan.layers:
         if L.compressed:
             k, long = L.k, max(L.rows, L.cols)
             gram += W * 2 * k * (k + 1) // 2 * long
-            tri += W * 4 * k ** 3 // 3
+            band += W * 4 * k ** 3 // 3
+            chase += W * 6 * 16 * k * k
             gbytes += W * 4 * L.rows * L.cols
-    return {"at_gram": ("flops", gram), "at_tridiag": ("flops", tri), "at_factor": ("bytes", gbytes)}
+    return {"at_gram": ("flops", gram), "at_band": ("flops", band), "at_chase": ("flops", chase),
+            "at_factor": ("bytes", gbytes)}
 
 
 def traffic_for(kernel: str, traffic_file: str = TRAFFIC_FILE, source: str = KERNEL_SRC):

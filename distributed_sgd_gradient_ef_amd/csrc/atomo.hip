@@ -11,13 +11,13 @@
 // over G.  Launches, each covering every problem of every worker:
 //
 //   at_gram       the Gram matrix, 128 x 128 output tiles of its lower block triangle
-//                 (stored as the packed lower triangle) with fp32 MFMA, the contraction
-//                 over the long side staged through LDS
-//   at_tridiag    one workgroup per problem: Householder reduction of the Gram matrix
-//                 to tridiagonal form.  Each step forms the next reflector from the
-//                 updated column, then one pass over the packed trailing block both
-//                 applies the previous rank-2 update and forms the product with the new
-//                 reflector; the last 190 rows are reduced in LDS
+//                 (stored in full, both triangles) with fp32 MFMA, the contraction over
+//                 the long side staged through LDS
+//   at_band       one workgroup per problem: reduction of the Gram matrix to a band of
+//                 half-bandwidth 16 by panels of 16 columns (Householder QR of the
+//                 panel in LDS, two-sided blocked update of the trailing matrix)
+//   at_chase      one workgroup per problem: the band to tridiagonal form by bulge
+//                 chasing in LDS, the sweeps pipelined three steps apart
 //   at_eig        every eigenvalue of the tridiagonal matrix by bisection on Sturm
 //                 counts: 64 per workgroup (one per lane; a large matrix spans several
 //                 compute units), four probe points per round (one per wave);
@@ -27,7 +27,8 @@
 //   at_vectors    inverse iteration on the tridiagonal matrix (partial pivoting, float32)
 //                 for each sent atom, orthogonalised against the problem's earlier sent
 //                 atoms after every solve
-//   at_backxform  the sent eigenvectors back through the reflectors: the unit factor
+//   at_backchase  the sent eigenvectors back through the chase's reflectors (stage 2)
+//   at_backband   and through the band reduction's panels (stage 1): the unit factor
 //   at_factor     the other factor, G^T u / p or G v / p, in one pass over G
 //   at_update     U = (1/W) sum over workers and their sent atoms of a b^T (and the
 //                 plain mean for tensors that are not compressed)
@@ -56,17 +57,12 @@ constexpr int kMaxK = PSGD_ATOMO_MAX_K;
 constexpr int kGramTile = 128;
 constexpr int kGramKC = 16;
 constexpr int kGramThreads = 256;
-constexpr int kTriThreads = 1024;
-// rows per wave per batch of the trailing-block pass (fewer for the widest rows, whose
-// values would not fit in the 128 registers a lane has at 1024 threads)
-template <int KT>
-constexpr int tri_rows() { return KT >= 16 ? 1 : KT >= 8 ? 3 : KT >= 4 ? 5 : 8; }
 constexpr int kEigSlots = 64;    // eigenvalues per at_eig workgroup, one per lane (grid.z splits a matrix)
 constexpr int kEigWaves = 4;     // probe points per round, one per wave: each round leaves a fifth
 constexpr int kEigThreads = 64 * kEigWaves;
 constexpr int kSampleThreads = 1024;
 constexpr int kVecThreads = 256;
-constexpr int kBackThreads = 256;
+constexpr int kBackThreads = 512;
 constexpr int kFactorThreads = 256;
 constexpr int kFactorGroup = 4;  // atoms per pass over G
 constexpr int kAtUpdThreads = 256;
@@ -77,6 +73,7 @@ struct AtMat {
   int64_t sv_off;    // offset in a worker's row of uniforms / sigma / prob / index
   int64_t atom_off;  // offset in a worker's row of atoms
   int64_t b_off;     // offset of the k x k Gram matrix in a worker's Gram workspace
+  int64_t r_off;     // offset of the chase reflectors in a worker's reflector workspace
   int32_t rows, cols, k, left;  // left: k == rows (G G^T), else k == cols (G^T G)
   int32_t mat_index, pad;
 };
@@ -98,9 +95,9 @@ struct AtUpdTile {
   int32_t mat, row0, row1, col0;
 };
 
-enum KernelId { kGram = 0, kTridiag, kEig, kSample, kVectors, kBack, kFactor, kUpdate, kNumK };
-const char* const kNames[kNumK] = {"at_gram",    "at_tridiag",   "at_eig",    "at_sample",
-                                   "at_vectors", "at_backxform", "at_factor", "at_update"};
+enum KernelId { kGram = 0, kBandK, kChase, kEig, kSample, kVectors, kBackChase, kBackBand, kFactor, kUpdate, kNumK };
+const char* const kNames[kNumK] = {"at_gram",    "at_band",      "at_chase",  "at_eig",   "at_sample",
+                                   "at_vectors", "at_backchase", "at_backband", "at_factor", "at_update"};
 
 }  // namespace atm
 }  // namespace psgd
@@ -114,9 +111,9 @@ struct psgd_atomo_plan {
   std::vector<psgd::atm::FactorTile> ftiles;
   std::vector<psgd::atm::AtUpdTile> utiles;
   std::vector<int32_t> tri_list;  // matrices in decreasing k (the largest start first)
-  int32_t tri_kt = 1;             // width class of the widest matrix
-  int64_t worker_stride = 0, numel = 0, sv_total = 0, atom_total = 0, gram_total = 0;
-  uint64_t ws_gram = 0, ws_y = 0, ws_tau = 0, ws_d = 0, ws_e = 0, ws_lam = 0, workspace_bytes = 0;
+  int32_t max_k = 0;
+  int64_t worker_stride = 0, numel = 0, sv_total = 0, atom_total = 0, gram_total = 0, refl_total = 0;
+  uint64_t ws_gram = 0, ws_y = 0, ws_refl = 0, ws_d = 0, ws_e = 0, ws_lam = 0, workspace_bytes = 0;
   uint64_t model_bytes = 0;
   std::map<int, void*> dev;  // device copy of the tables, per HIP device
   bool timing = false;
@@ -180,15 +177,6 @@ __device__ __forceinline__ float block_min(float v, float* red) {
 }
 
 __device__ __forceinline__ float block_max(float v, float* red) { return -block_min(-v, red); }
-
-// ------------------------------------------------------------------ packed storage
-// A problem's k * k floats of workspace: the lower triangle of the symmetric matrix,
-// packed by rows (row r at tri_off(r), columns 0..r), then the Householder reflectors
-// (reflector q, entries q+1..k-1, at refl_off(k, q)); k (k + 1) / 2 + k (k - 1) / 2 = k^2.
-// (k <= 1024, so every offset inside a problem's k * k floats fits in 32 bits)
-__device__ __forceinline__ int tri_off(int r) { return (r * (r + 1)) >> 1; }
-
-__device__ __forceinline__ int refl_off(int k, int q) { return tri_off(k) + q * (k - 1) - ((q * (q - 1)) >> 1); }
 
 // ------------------------------------------------------------------ at_gram
 // One 128 x 128 tile of the lower block triangle per workgroup of four waves; each wave
@@ -315,226 +303,473 @@ __global__ __launch_bounds__(kGramThreads) void at_gram(const GramTile* __restri
       __syncthreads();
     }
   }
-  // the lower triangle only, packed
+  // full storage (row-major, leading dimension k): the tile's lower-triangle entries and
+  // their mirror images; a lane's four consecutive accumulators are four consecutive
+  // columns of the mirror row, stored together where rows are 16-byte aligned
+  const bool mvec = (k & 3) == 0;
 #pragma unroll
   for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < 2; ++bj)
+    for (int bj = 0; bj < 2; ++bj) {
+      const int b = b0 + wc + 32 * bj + l32;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int a = a0 + wr + 32 * bi + 8 * (v >> 2) + 4 * half + (v & 3), b = b0 + wc + 32 * bj + l32;
-        if (a < k && b <= a) B[tri_off(a) + b] = acc[bi][bj][v];
+        const int a = a0 + wr + 32 * bi + 8 * (v >> 2) + 4 * half + (v & 3);
+        if (a < k && b <= a) B[int64_t(a) * k + b] = acc[bi][bj][v];
       }
-}
-
-// ------------------------------------------------------------------ at_tridiag
-// Reflector q (q = 0..k-3) is H_q = I - tau_q v_q v_q^T with v_q[q+1] = 1 and zeros above;
-// H_q maps column q of the current matrix below the diagonal to e[q] * e_{q+1}.  After
-// step q the trailing block (rows and columns > q) holds H_q A H_q there, applied as
-// A - v w^T - w v^T with w = tau A v - (tau^2 / 2)(v^T A v) v.
-//
-// A problem's k * k floats of workspace hold the lower triangle of the symmetric
-// matrix, packed by rows (row r at r(r+1)/2, columns 0..r), followed by the reflectors
-// (reflector q, entries q+1..k-1, at refl_off(k, q)).  In the pass over the trailing
-// block, row r contributes sum_c a_rc v_c to (A v)_r directly and a_rc v_r to (A v)_c
-// for c < r; a lane keeps the latter for its own columns in registers, and the waves'
-// column sums are added in wave order.  Once the trailing block fits, it moves to LDS.
-constexpr int kTriWaves = kTriThreads / 64;
-// LDS per problem: the reflector and product vectors and the per-wave column sums sized
-// for the width class (64 KT columns), and as large a packed trailing block as the rest of
-// the 160 KB allows (width classes up to 4, k <= 256, hold the whole matrix).
-template <int KT>
-constexpr int tail_rows() { return KT >= 16 ? 190 : KT >= 8 ? 240 : 64 * KT; }
-
-template <int KT>
-struct TriShared {
-  static constexpr int N = 64 * KT;
-  float V[2][N], Wv[2][N], P[N];
-  float next[N];            // column q+1 as the pass of step q stores it
-  float col[kTriWaves][N];  // per-wave column sums of the pass
-  float red[kTriWaves], red2[kTriWaves];  // the step's two sums use one each
-  float tail[tail_rows<KT>() * (tail_rows<KT>() + 1) / 2];  // the trailing block, packed, once it fits
-};
-
-// one Householder step q on packed storage: global (LOCAL = false) or the LDS copy of the
-// block from row/column `base` on
-template <int KT, bool LOCAL>
-__device__ __forceinline__ void tri_step(int q, int k, int base, float* __restrict__ A, float* __restrict__ Rf,
-                                         float* __restrict__ tau, float* __restrict__ d, float* __restrict__ e,
-                                         TriShared<KT>& sh, int cur) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int kWaves = kTriWaves;
-  auto at = [&](int r, int c) -> float& {
-    if constexpr (LOCAL) return sh.tail[tri_off(r - base) + (c - base)];
-    else return A[tri_off(r) + c];
-  };
-  const float* vp = sh.V[cur];
-  const float* wp = sh.Wv[cur];
-  float* vn = sh.V[cur ^ 1];
-  float* wn = sh.Wv[cur ^ 1];
-  float* P = sh.P;
-  // column q below the diagonal, with the previous reflector's update applied (the
-  // stored column comes from the previous pass, or from memory at the first step)
-  const float vq = vp[q], wq = wp[q];
-  const bool fresh = q == 0;
-  for (int i = q + 1 + tid; i < k; i += kTriThreads)
-    vn[i] = (fresh ? at(i, q) : sh.next[i]) - vp[i] * wq - wp[i] * vq;
-  if (tid == 0) d[q] = (fresh ? at(q, q) : sh.next[q]) - 2.f * vq * wq;
-  __syncthreads();
-  // alpha is read before the sum's barrier, so that once the sum returns nobody reads vn
-  // any more and it can be rescaled in place
-  const float alpha = vn[q + 1];
-  float part = 0.f;
-  for (int i = q + 2 + tid; i < k; i += kTriThreads) part = fmaf(vn[i], vn[i], part);
-  const float ss = block_sum<float, false>(part, sh.red);
-  float tq = 0.f, beta = alpha, inv = 0.f;
-  if (ss != 0.f) {
-    const float mu = sqrtf(fmaf(alpha, alpha, ss));
-    beta = alpha >= 0.f ? -mu : mu;
-    tq = (beta - alpha) / beta;
-    inv = 1.f / (alpha - beta);
-  }
-  float* rq = Rf + refl_off(k, q) - (q + 1);
-  for (int i = q + 1 + tid; i < k; i += kTriThreads) {
-    const float v = (i == q + 1) ? 1.f : vn[i] * inv;
-    vn[i] = v;
-    rq[i] = v;
-  }
-  if (tid == 0) {
-    tau[q] = tq;
-    e[q] = beta;
-  }
-  __syncthreads();
-  // trailing block: apply the previous update (none at q = 0) and form A v_q.  A wave
-  // takes kTriRows rows at a time, all their loads issued first, then walks the lane's
-  // columns (reflector entries read once per column for all the rows).
-  const int c0 = q + 1;
-  constexpr int kTriRows = tri_rows<KT>();
-  float colr[KT];
 #pragma unroll
-  for (int t = 0; t < KT; ++t) colr[t] = 0.f;
-  for (int rb = c0 + wave * kTriRows; rb < k; rb += kWaves * kTriRows) {
-    float a[kTriRows][KT];
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int a = a0 + wr + 32 * bi + 8 * g4 + 4 * half;
+        if (mvec && a + 3 < k && b < a) {
+          const f4 m4 = {acc[bi][bj][4 * g4], acc[bi][bj][4 * g4 + 1], acc[bi][bj][4 * g4 + 2], acc[bi][bj][4 * g4 + 3]};
+          *reinterpret_cast<f4*>(B + int64_t(b) * k + a) = m4;
+        } else {
 #pragma unroll
-    for (int u = 0; u < kTriRows; ++u)
-#pragma unroll
-      for (int t = 0; t < KT; ++t) {
-        const int r = rb + u, c = c0 + lane + 64 * t;
-        a[u][t] = (r < k && c <= r) ? at(r, c) : 0.f;
-      }
-    float vr[kTriRows], wr[kTriRows], nr[kTriRows], sr[kTriRows];
-#pragma unroll
-    for (int u = 0; u < kTriRows; ++u) {
-      const int r = min(rb + u, k - 1);
-      vr[u] = vp[r];
-      wr[u] = wp[r];
-      nr[u] = vn[r];
-      sr[u] = 0.f;
-    }
-#pragma unroll
-    for (int t = 0; t < KT; ++t) {
-      const int c = c0 + lane + 64 * t;
-      const int cc = min(c, k - 1);
-      const float cw = wp[cc], cv = vp[cc], cn = vn[cc];
-#pragma unroll
-      for (int u = 0; u < kTriRows; ++u) {
-        const int r = rb + u;
-        if (r < k && c <= r) {
-          const float x = a[u][t] - vr[u] * cw - wr[u] * cv;
-          sr[u] = fmaf(x, cn, sr[u]);
-          if (c < r) colr[t] = fmaf(x, nr[u], colr[t]);
-          if (q > 0) at(r, c) = x;
-          if (c == c0) sh.next[r] = x;
+          for (int q = 0; q < 4; ++q)
+            if (a + q < k && b < a + q) B[int64_t(b) * k + a + q] = acc[bi][bj][4 * g4 + q];
         }
       }
     }
+}
+
+// ------------------------------------------------------------------ at_band / at_chase
+// The Gram matrix is reduced to tridiagonal form in two stages.
+//
+// Stage 1 (at_band): to a band of half-bandwidth kBand, by panels of kBand columns.  For
+// the panel of columns [c, c + kBand), the rows below the band (r0 = c + kBand .. k-1)
+// get a Householder QR in LDS (one reflector per column, H_i = I - tau_i v_i v_i^T with
+// v_i[i] = 1), accumulated as Q = I - V T V^T (T upper triangular); the trailing matrix
+// A22 (rows and columns >= r0) becomes Q^T A22 Q = A22 - V Z^T - Z V^T with
+// W = A22 V T, S = T^T V^T W, Z = W - V S / 2.  The matrix is held in full (both
+// triangles), so the products over A22 read and write it along rows, coalesced.  The
+// panel's R (upper triangle, on the band) and its reflectors (below the band) stay in
+// the matrix, and T goes to the block above the band, the mirror of the panel, which
+// nothing reads afterwards.
+//
+// Stage 2 (at_chase): band to tridiagonal by bulge chasing in LDS (the lower band, with
+// room for the bulges below it: 2 kBand diagonals).  Sweep j annihilates column j below
+// its subdiagonal with a reflector on rows r0 = j + 1 .. j + kBand (step 0); applied from
+// both sides this fills a block below the band, whose first column the next reflector,
+// kBand rows further down, annihilates (step 1), and so on to the end of the matrix.
+// Step s of sweep j runs in round 3 j + s: two sweeps three rounds apart touch disjoint
+// elements, so every wave takes one sweep of a round and the round ends with one
+// barrier.  Every reflector (kBand entries and tau) is kept for the back-transform, where
+// the reflectors of one sweep (disjoint supports) are applied together and the sweeps in
+// reverse order.
+constexpr int kBand = 16;
+constexpr int kVS = kBand + 1;  // LDS row stride of the panel arrays
+constexpr int kBandThreads = 1024;
+constexpr int kChaseThreads = 1024;
+constexpr int kChaseWaves = kChaseThreads / 64;
+constexpr int kLag = 3;  // rounds between the starts of consecutive sweeps
+
+// the most chase steps a sweep of a k x k problem has, and the reflector block's floats
+__host__ __device__ constexpr int chase_steps_max(int k) { return (k + kBand - 1) / kBand; }
+__host__ __device__ constexpr int64_t chase_block(int k) {
+  return k < 3 ? 0 : int64_t(k - 2) * chase_steps_max(k) * (kBand + 1);
+}
+// steps of sweep j: reflectors on rows j + 1 + s kBand .. while at least two rows remain
+__device__ __forceinline__ int chase_steps(int k, int j) { return j > k - 3 ? 0 : (k - 3 - j) / kBand + 1; }
+// stage-1 panels: columns c = 0, kBand, ... while at least two rows lie below the band
+__device__ __forceinline__ int band_panels(int k) { return k < kBand + 2 ? 0 : (k - kBand - 2) / kBand + 1; }
+
+// A workgroup barrier that orders LDS only: the chase's global stores (the reflectors,
+// read by a later kernel) are not waited for at every round, as __syncthreads() would.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Sum over each 16-lane row of the wave (every lane of the row gets it): four row rotates.
+// All 64 lanes must be active.
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_mov<0x128, 0xf>(v);  // row_ror:8
+  v += dpp_mov<0x124, 0xf>(v);  // row_ror:4
+  v += dpp_mov<0x122, 0xf>(v);  // row_ror:2
+  v += dpp_mov<0x121, 0xf>(v);  // row_ror:1
+  return v;
+}
+
+// The reflector of a vector x (its first entry alpha, the squared norm of the rest sig2):
+// H x = beta e_1 with H = I - tau v v^T, v[0] = 1, v[i] = x[i] * scale.  sig2 = 0 gives
+// H = I (tau = 0, beta = alpha, scale = 0).
+struct Refl {
+  float tau, beta, scale;
+};
+// The hardware square root and reciprocal (about 1 ulp each) suffice: the reflector
+// stays orthogonal to rounding, whatever values tau and v take.
+__device__ __forceinline__ Refl make_refl(float alpha, float sig2) {
+  Refl h{0.f, alpha, 0.f};
+  if (sig2 != 0.f) {
+    const float mu = __builtin_amdgcn_sqrtf(fmaf(alpha, alpha, sig2));
+    h.beta = alpha >= 0.f ? -mu : mu;
+    h.tau = (h.beta - alpha) * __builtin_amdgcn_rcpf(h.beta);
+    h.scale = __builtin_amdgcn_rcpf(alpha - h.beta);
+  }
+  return h;
+}
+
+__global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restrict__ list,
+                                                        const AtMat* __restrict__ mats, float* __restrict__ gram,
+                                                        int64_t gram_ws) {
+  // grid.x walks the workers, grid.y the matrices in decreasing k
+  const AtMat M = mats[list[blockIdx.y]];
+  const int k = M.k;
+  const int np = band_panels(k);
+  if (np == 0) return;  // already a band
+  float* A = gram + int64_t(blockIdx.x) * gram_ws + M.b_off;
+  // P1 rows of kVS = kBand + 1 floats (rows read lane by lane fall in different banks):
+  // the panel, its reflectors, then A22 V (partial sums, then the sums).  P2 rows of kBand
+  // floats, 16-byte aligned for the broadcast reads of the products: V, then (P1) Z.
+  __shared__ __align__(16) float P1[kMaxK * kVS];
+  __shared__ __align__(16) float P2[kMaxK * kBand];
+  __shared__ float Tm[kBand][kBand + 1];
+  __shared__ float Gm[kBand][kBand + 1];  // V^T V, then V^T X
+  __shared__ float Sm[kBand][kBand + 1];
+  __shared__ float part[4][kBand * kBand];
+  __shared__ float vbuf[2][kMaxK];  // the current reflector, double-buffered
+  __shared__ float hbuf[2][3];      // its tau, scale, beta
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int kRegs = kMaxK / 64;  // a panel column in registers: row lane + 64 q
+  for (int p = 0; p < np; ++p) {
+    const int c = p * kBand, r0 = c + kBand, m = k - r0;
+    const int nref = min(kBand, m - 1);
+    for (int e = tid; e < m * kBand; e += kBandThreads)
+      P1[(e / kBand) * kVS + e % kBand] = A[int64_t(r0 + e / kBand) * k + c + e % kBand];
+    if (tid < kBand * kBand) Tm[tid / kBand][tid % kBand] = 0.f;
+    __syncthreads();
+    // QR of the panel: wave t holds column t in registers.  Reflector i is formed by wave
+    // i from its column (in the step before, by the wave that updated it last) and put in
+    // vbuf; after one barrier the waves t > i apply it, and wave i + 1 forms the next.
+    float col[kRegs];
 #pragma unroll
-    for (int u = 0; u < kTriRows; ++u) {
-      const int r = rb + u;
-      if (r < k) {
-        const float s = wave_sum(sr[u]);
-        if (lane == 0) P[r] = s;
+    for (int q = 0; q < kRegs; ++q) {
+      const int r = lane + 64 * q;
+      col[q] = r < m ? P1[r * kVS + wave] : 0.f;
+    }
+    // wave w forms reflector w from its column: v (rows > w), beta at row w
+    auto form = [&](int i) {
+      float s2 = 0.f, alpha = 0.f;
+#pragma unroll
+      for (int q = 0; q < kRegs; ++q) {
+        const int r = lane + 64 * q;
+        if (r > i) s2 = fmaf(col[q], col[q], s2);
+        if (r == i) alpha = col[q];
+      }
+      s2 = wave_sum(s2);
+      alpha = wave_sum(alpha);  // one lane holds it
+      const Refl h = make_refl(alpha, s2);
+#pragma unroll
+      for (int q = 0; q < kRegs; ++q) {
+        const int r = lane + 64 * q;
+        const float v = r > i ? col[q] * h.scale : (r == i ? 1.f : 0.f);
+        if (r < m) vbuf[i & 1][r] = v;
+        if (r > i) col[q] = v;
+        if (r == i) col[q] = h.beta;
+      }
+      if (lane == 0) {
+        hbuf[i & 1][0] = h.tau;
+        Tm[i][i] = h.tau;
+      }
+    };
+    if (wave == 0) form(0);
+    for (int i = 0; i < nref; ++i) {
+      __syncthreads();
+      if (wave > i) {
+        const float tau = hbuf[i & 1][0];
+        const float* v = vbuf[i & 1];
+        float y = 0.f;
+#pragma unroll
+        for (int q = 0; q < kRegs; ++q) {
+          const int r = lane + 64 * q;
+          if (r >= i && r < m) y = fmaf(v[r], col[q], y);
+        }
+        const float f = tau * wave_sum(y);
+#pragma unroll
+        for (int q = 0; q < kRegs; ++q) {
+          const int r = lane + 64 * q;
+          if (r >= i && r < m) col[q] = fmaf(-f, v[r], col[q]);
+        }
+        if (wave == i + 1 && i + 1 < nref) form(i + 1);
       }
     }
-  }
+    __syncthreads();
+    // the panel (R on the band, the reflectors below it) back into P1 and the matrix; P1
+    // and P2 become the unit lower trapezoidal matrix V of the reflectors
 #pragma unroll
-  for (int t = 0; t < KT; ++t) {
-    const int c = c0 + lane + 64 * t;
-    if (c < k) sh.col[wave][c] = colr[t];
-  }
-  __syncthreads();
-  float part2 = 0.f;
-  for (int r = c0 + tid; r < k; r += kTriThreads) {
-    float pr = P[r];
+    for (int q = 0; q < kRegs; ++q) {
+      const int r = lane + 64 * q;
+      if (r < m) P1[r * kVS + wave] = col[q];
+    }
+    __syncthreads();
+    for (int e = tid; e < m * kBand; e += kBandThreads) {
+      const int i = e / kBand, t = e % kBand;
+      const float x = P1[i * kVS + t];
+      A[int64_t(r0 + i) * k + c + t] = x;
+      const float v = t < nref ? (i > t ? x : (i == t ? 1.f : 0.f)) : 0.f;
+      P1[i * kVS + t] = v;
+      P2[e] = v;
+    }
+    __syncthreads();
+    // T: T[i][i] = tau_i, T[0:i, i] = -tau_i T[0:i, 0:i] (V^T v_i)[0:i]
+    for (int pr = wave; pr < kBand * kBand; pr += kBandThreads / 64) {
+      const int a = pr / kBand, b = pr % kBand;
+      if (a < b && b < nref) {
+        float g = 0.f;
+        for (int r = b + lane; r < m; r += 64) g = fmaf(P1[r * kVS + a], P1[r * kVS + b], g);
+        g = wave_sum(g);
+        if (lane == 0) Gm[a][b] = g;
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {  // lane a holds row a of T; column i needs the finished columns < i
+      float tr[kBand];
 #pragma unroll
-    for (int w2 = 0; w2 < kWaves; ++w2) pr += sh.col[w2][r];
-    P[r] = pr;
-    part2 = fmaf(pr, vn[r], part2);
+      for (int b = 0; b < kBand; ++b) tr[b] = (lane < kBand && b == lane) ? Tm[lane][lane] : 0.f;
+#pragma unroll
+      for (int i = 1; i < kBand; ++i) {
+        if (i >= nref) break;
+        float g = 0.f;
+#pragma unroll
+        for (int b = 0; b < i; ++b) g = fmaf(tr[b], Gm[b][i], g);
+        tr[i] = lane < i ? -Tm[i][i] * g : tr[i];
+      }
+      if (lane < kBand)
+#pragma unroll
+        for (int b = 0; b < kBand; ++b) Tm[lane][b] = tr[b];
+    }
+    __syncthreads();
+    if (tid < nref * nref) A[int64_t(c + tid / nref) * k + r0 + tid % nref] = Tm[tid / nref][tid % nref];
+    // X = A22 V: thread (r, part) sums rows [part * rl, ...) of column r of A22 (its row r
+    // by symmetry), reading along rows; the parts are added in a fixed order
+    const int nparts = max(1, kBandThreads / m);
+    const int rl = (m + nparts - 1) / nparts;
+    const int rr = tid % m, pi = tid / m;
+    const float* A22 = A + int64_t(r0) * k + r0;
+    const f4* V4 = reinterpret_cast<const f4*>(P2);
+    if (pi < nparts) {
+      float x[kBand];
+#pragma unroll
+      for (int q = 0; q < kBand; ++q) x[q] = 0.f;
+      const int l1 = min(m, (pi + 1) * rl);
+      for (int l = pi * rl; l < l1; ++l) {
+        const float a = A22[int64_t(l) * k + rr];
+#pragma unroll
+        for (int q4 = 0; q4 < kBand / 4; ++q4) {
+          const f4 v = V4[l * (kBand / 4) + q4];
+#pragma unroll
+          for (int z = 0; z < 4; ++z) x[4 * q4 + z] = fmaf(a, v[z], x[4 * q4 + z]);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < kBand; ++q) P1[(pi * m + rr) * kVS + q] = x[q];
+    }
+    __syncthreads();
+    for (int e = tid; e < m * kBand; e += kBandThreads) {
+      const int r = e / kBand, q = e % kBand;
+      float sum = P1[r * kVS + q];
+      for (int pp = 1; pp < nparts; ++pp) sum += P1[(pp * m + r) * kVS + q];
+      P1[r * kVS + q] = sum;
+    }
+    __syncthreads();
+    {  // V^T X, four row quarters per entry
+      const int en = tid % (kBand * kBand), qt = tid / (kBand * kBand);
+      const int a = en / kBand, b = en % kBand;
+      const int lq = (m + 3) / 4, l0 = qt * lq, l1 = min(m, l0 + lq);
+      float g = 0.f;
+      for (int l = l0; l < l1; ++l) g = fmaf(P2[l * kBand + a], P1[l * kVS + b], g);
+      part[qt][en] = g;
+    }
+    __syncthreads();
+    if (tid < kBand * kBand) Gm[tid / kBand][tid % kBand] = part[0][tid] + part[1][tid] + part[2][tid] + part[3][tid];
+    __syncthreads();
+    if (tid < kBand * kBand) {  // (V^T X) T
+      const int a = tid / kBand, j = tid % kBand;
+      float y = 0.f;
+      for (int b = 0; b <= j; ++b) y = fmaf(Gm[a][b], Tm[b][j], y);
+      part[0][tid] = y;
+    }
+    __syncthreads();
+    if (tid < kBand * kBand) {  // S = T^T (V^T X) T
+      const int i = tid / kBand, j = tid % kBand;
+      float y = 0.f;
+      for (int a = 0; a <= i; ++a) y = fmaf(Tm[a][i], part[0][a * kBand + j], y);
+      Sm[i][j] = y;
+    }
+    __syncthreads();
+    float zrow[kBand];  // Z = X T - V S / 2, row tid
+    if (tid < m) {
+      float x[kBand], v[kBand];
+#pragma unroll
+      for (int q = 0; q < kBand; ++q) {
+        x[q] = P1[tid * kVS + q];
+        v[q] = P2[tid * kBand + q];
+      }
+#pragma unroll
+      for (int j = 0; j < kBand; ++j) {
+        float z = 0.f;
+#pragma unroll
+        for (int b = 0; b < kBand; ++b) z = fmaf(x[b], Tm[b][j], z);
+        float vs = 0.f;
+#pragma unroll
+        for (int b = 0; b < kBand; ++b) vs = fmaf(v[b], Sm[b][j], vs);
+        zrow[j] = fmaf(-0.5f, vs, z);
+      }
+    }
+    __syncthreads();  // every row of X read: P1 takes Z with rows of kBand floats
+    if (tid < m)
+#pragma unroll
+      for (int q = 0; q < kBand; ++q) P1[tid * kBand + q] = zrow[q];
+    __syncthreads();
+    // A22 -= V Z^T + Z V^T, thread (r, part) on column r of its rows
+    if (pi < nparts) {
+      const f4* Z4 = reinterpret_cast<const f4*>(P1);
+      float vr[kBand], zr[kBand];
+#pragma unroll
+      for (int q = 0; q < kBand; ++q) {
+        vr[q] = P2[rr * kBand + q];
+        zr[q] = P1[rr * kBand + q];
+      }
+      const int l1 = min(m, (pi + 1) * rl);
+      float* col2 = A + int64_t(r0) * k + r0 + rr;
+      for (int l = pi * rl; l < l1; ++l) {
+        float sum = 0.f;
+#pragma unroll
+        for (int q4 = 0; q4 < kBand / 4; ++q4) {
+          const f4 v = V4[l * (kBand / 4) + q4], z = Z4[l * (kBand / 4) + q4];
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) sum = fmaf(v[e2], zr[4 * q4 + e2], fmaf(z[e2], vr[4 * q4 + e2], sum));
+        }
+        col2[int64_t(l) * k] -= sum;
+      }
+    }
+    __syncthreads();
   }
-  const float vav = block_sum<float, false>(part2, sh.red2);  // v^T A v
-  const float half = 0.5f * tq * tq * vav;
-  for (int r = c0 + tid; r < k; r += kTriThreads) wn[r] = tq * P[r] - half * vn[r];
-  __syncthreads();
 }
 
-template <int KT>
-__device__ void tridiag_body(const AtMat& M, float* __restrict__ A, float* __restrict__ tau, float* __restrict__ d,
-                             float* __restrict__ e, TriShared<KT>& sh) {
-  const int k = M.k;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < k; i += kTriThreads) {
-    sh.V[0][i] = 0.f;
-    sh.Wv[0][i] = 0.f;
+// One chase step (sweep j, step s) by one wave.  Lane = u + 16 g: u indexes the 16 rows
+// (or columns) of the reflector's block, g one of four groups sharing the rest.  `band`
+// holds element (r, c), r >= c, of the lower band at c * 2 kBand + (r - c).  Every load
+// reads an in-range element (indices clamped) and keeps zero where it has no element, so
+// the four independent reductions of each phase run without branches between them.
+__device__ __forceinline__ void chase_step(float* band, float* sv, float* sw, float* __restrict__ R2, int k, int j,
+                                           int s) {
+  const int lane = threadIdx.x & 63, u = lane & 15, g = lane >> 4;
+  const int r0 = j + 1 + s * kBand;
+  const int len = min(kBand, k - r0);
+  const int pc = s == 0 ? j : r0 - kBand;  // the column to clear below row r0
+  auto at = [&](int r, int c) -> float& { return band[c * (2 * kBand) + (r - c)]; };
+  const bool in = u < len;
+  const int uc = in ? u : 0;
+  const float x0 = at(r0 + uc, pc);
+  const float x = in ? x0 : 0.f;
+  const Refl h = make_refl(at(r0, pc), row_sum16(u >= 1 ? x * x : 0.f));
+  const float v = in ? (u == 0 ? 1.f : x * h.scale) : 0.f;
+  float* slot = R2 + (int64_t(j) * chase_steps_max(k) + s) * (kBand + 1);
+  if (g == 0) {
+    slot[u] = v;
+    if (in) at(r0 + u, pc) = u == 0 ? h.beta : 0.f;
+    sv[u] = v;
   }
-  __syncthreads();
-  int cur = 0;
-  // global storage while the trailing block (rows and columns >= q) is too large for LDS
-  const int qlocal = max(0, k - tail_rows<KT>());
-  int q = 0;
-  for (; q + 2 < k && q < qlocal; ++q, cur ^= 1) tri_step<KT, false>(q, k, 0, A, A, tau, d, e, sh, cur);
-  // copy the block from row/column q on into LDS, then continue there
-  const int base = q;
-  for (int r = base + wave; r < k; r += kTriWaves)
-    for (int c = base + lane; c <= r; c += 64) sh.tail[tri_off(r - base) + (c - base)] = A[tri_off(r) + c];
-  __syncthreads();
-  for (; q + 2 < k; ++q, cur ^= 1) tri_step<KT, true>(q, k, base, A, A, tau, d, e, sh, cur);
-  // the last 2 x 2 block (rows and columns k-2, k-1) with the last reflector's update
-  if (tid == 0) {
-    const float* vp = sh.V[cur];
-    const float* wp = sh.Wv[cur];
-    const int i0 = k - 2, i1 = k - 1;
-    auto at = [&](int r, int c) { return sh.tail[tri_off(r - base) + (c - base)]; };
-    d[i0] = at(i0, i0) - 2.f * vp[i0] * wp[i0];
-    e[i0] = at(i1, i0) - vp[i1] * wp[i0] - wp[i1] * vp[i0];
-    d[i1] = at(i1, i1) - 2.f * vp[i1] * wp[i1];
+  if (lane == 0) slot[kBand] = h.tau;
+  if (h.tau == 0.f) return;  // H = I (wave-uniform)
+  const float tau = h.tau;
+  if (s > 0) {  // from the left on the rest of the block the previous step filled
+    float ev[4], y[4];
+#pragma unroll
+    for (int i2 = 0; i2 < 4; ++i2) {
+      const int cc = pc + 1 + g + 4 * i2;
+      const bool ok = in && cc < r0;
+      const float e = at(r0 + uc, ok ? cc : pc + 1);
+      ev[i2] = ok ? e : 0.f;
+    }
+#pragma unroll
+    for (int i2 = 0; i2 < 4; ++i2) y[i2] = row_sum16(v * ev[i2]);
+#pragma unroll
+    for (int i2 = 0; i2 < 4; ++i2) {
+      const int cc = pc + 1 + g + 4 * i2;
+      if (in && cc < r0) at(r0 + u, cc) = ev[i2] - tau * y[i2] * v;
+    }
+  }
+  // both sides of the diagonal block D: p = D v, w = tau p - tau^2 (v^T p) v / 2,
+  // D -= v w^T + w v^T on its lower triangle
+  float pp = 0.f;
+#pragma unroll
+  for (int i2 = 0; i2 < 4; ++i2) {
+    const int u2 = g + 4 * i2;
+    const bool ok = in && u2 < len;
+    const int a2 = ok ? u2 : 0;
+    const float dv = uc >= a2 ? at(r0 + uc, r0 + a2) : at(r0 + a2, r0 + uc);
+    pp = fmaf(ok ? dv : 0.f, sv[u2], pp);
+  }
+  pp += __shfl_xor(pp, 16, 64);
+  pp += __shfl_xor(pp, 32, 64);
+  const float vp = row_sum16(v * pp);
+  const float wv = tau * pp - 0.5f * tau * tau * vp * v;
+  if (g == 0) sw[u] = wv;
+#pragma unroll
+  for (int i2 = 0; i2 < 4; ++i2) {
+    const int u2 = g + 4 * i2;
+    if (in && u2 <= u) at(r0 + u, r0 + u2) -= fmaf(v, sw[u2], wv * sv[u2]);
+  }
+  // from the right on the rows below: the next bulge
+  const int len2 = len == kBand ? min(kBand, k - (r0 + kBand)) : 0;
+  if (len2 > 0) {
+    float ev[4], y[4];
+#pragma unroll
+    for (int i2 = 0; i2 < 4; ++i2) {
+      const int uu = g + 4 * i2;
+      const float e = at(r0 + kBand + (uu < len2 ? uu : 0), r0 + u);
+      ev[i2] = uu < len2 ? e : 0.f;
+    }
+#pragma unroll
+    for (int i2 = 0; i2 < 4; ++i2) y[i2] = row_sum16(ev[i2] * v);
+#pragma unroll
+    for (int i2 = 0; i2 < 4; ++i2) {
+      const int uu = g + 4 * i2;
+      if (uu < len2) at(r0 + kBand + uu, r0 + u) = ev[i2] - tau * y[i2] * v;
+    }
   }
 }
 
-// One launch over every matrix of the plan (`list`), KT set by the widest one (k <= 64 KT):
-// narrower matrices leave slots idle, but every problem runs concurrently and the kernel
-// holds a single register allocation.
-template <int KT>
-__global__ __launch_bounds__(kTriThreads) void at_tridiag(const int32_t* __restrict__ list,
-                                                          const AtMat* __restrict__ mats, float* __restrict__ gram,
-                                                          int64_t gram_ws, float* __restrict__ tau_ws,
+__global__ __launch_bounds__(kChaseThreads) void at_chase(const int32_t* __restrict__ list,
+                                                          const AtMat* __restrict__ mats,
+                                                          const float* __restrict__ gram, int64_t gram_ws,
+                                                          float* __restrict__ refl, int64_t refl_ws,
                                                           float* __restrict__ d_ws, float* __restrict__ e_ws,
                                                           int64_t sv_total) {
-  // grid.x walks the workers, grid.y the matrices in decreasing k: every worker's largest
-  // problems are dispatched first
   const AtMat M = mats[list[blockIdx.y]];
   const int64_t w = blockIdx.x;
-  float* A = gram + w * gram_ws + M.b_off;
-  float* tau = tau_ws + w * sv_total + M.sv_off;
+  const int k = M.k;
+  const float* A = gram + w * gram_ws + M.b_off;
+  float* R2 = refl + w * refl_ws + M.r_off;
   float* d = d_ws + w * sv_total + M.sv_off;
   float* e = e_ws + w * sv_total + M.sv_off;
-  __shared__ TriShared<KT> sh;
-  tridiag_body<KT>(M, A, tau, d, e, sh);
-}
-
-// the width class of a matrix: the smallest of 1, 2, 4, 8, 16 with k <= 64 * class
-inline int tri_class(int k) {
-  const int kt = (k + 63) / 64;
-  return kt > 8 ? 16 : kt > 4 ? 8 : kt > 2 ? 4 : kt > 1 ? 2 : 1;
+  __shared__ float band[kMaxK * 2 * kBand];
+  __shared__ float scratch[kChaseWaves][2][kBand];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  for (int i = tid; i < k * 2 * kBand; i += kChaseThreads) {
+    const int c = i / (2 * kBand), t = i % (2 * kBand);
+    band[i] = (t <= kBand && c + t < k) ? A[int64_t(c + t) * k + c] : 0.f;
+  }
+  __syncthreads();
+  const int rounds = k < 3 ? 0 : kLag * (k - 3) + 1;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform: scalar loop control
+  for (int rho = 0; rho < rounds; ++rho) {
+    // the sweeps of this round: j = jhi, jhi - 1, ... while step rho - 3 j exists
+    const int jhi = min(k - 3, rho / kLag);
+    for (int j = jhi - wv; j >= 0; j -= kChaseWaves) {
+      const int st = rho - kLag * j;
+      if (st >= chase_steps(k, j)) break;  // and every smaller j (wave-uniform)
+      chase_step(band, scratch[wv][0], scratch[wv][1], R2, k, j, st);
+    }
+    lds_barrier();
+  }
+  for (int i = tid; i < k; i += kChaseThreads) {
+    d[i] = band[i * 2 * kBand];
+    if (i + 1 < k) e[i] = band[i * 2 * kBand + 1];
+  }
 }
 
 // ------------------------------------------------------------------ at_eig
@@ -872,100 +1107,263 @@ __global__ __launch_bounds__(kVecThreads) void at_vectors(const AtMat* __restric
   }
 }
 
-// ------------------------------------------------------------------ at_backxform
-// x = H_0 H_1 ... H_{k-3} y for each sent atom (one wave per atom), written as the unit
-// factor of the message: a when k == rows, b when k == cols.  The reflectors are applied
-// from the last to the first; a ring of kBackAhead of them is kept in registers, and the
-// slot a reflector leaves is refilled at once with the one kBackAhead places further on,
-// so each load has kBackAhead - 1 reflector applications to arrive.
-constexpr int kBackAhead = 4;
+// ------------------------------------------------------------------ at_backchase, at_backband
+// x = Q1 Q2 y for each sent atom (one wave per atom, eight atoms per pass), written as the
+// unit factor of the message: a when k == rows, b when k == cols.
+//
+// at_backchase applies Q2 (stage 2), the product of the chase reflectors in the order
+// they were made, to y in place, sweep by sweep from the last, the reflectors of one
+// sweep (disjoint row blocks) together.  Sweep j's block s covers rows j + 1 + s kBand ..
+// + kBand - 1, so the wave keeps y in a window of 64 NS registers whose position p holds
+// row j + 1 + p: block s is then lane group s mod 4 of register s / 4 in every sweep, and
+// moving to sweep j - 1 shifts the window up by one lane (a wave-wide DPP shift, the carry
+// between registers by readlane), row j entering at position 0.  Rows at or above k stay
+// zero.  The reflectors reach the window through LDS, a few sweeps at a time, the next
+// ones loaded into registers by all waves while the current ones are applied.
+//
+// at_backband applies Q1 (stage 1) panel by panel from the last: y[r0:] -= V (T (V^T
+// y[r0:])), with V (unit diagonal, zero above it) and T staged in LDS from where at_band
+// left them, the next panel loaded while the current one is applied, and writes x.
+constexpr int kBackWaves = kBackThreads / 64;
+constexpr int kBackPre = 34;                              // prefetch registers per thread
+constexpr int kBackChunkFl = kBackPre * kBackThreads;     // floats one load brings
+constexpr int kBackVS = kBand + 4;                        // LDS row stride of a staged V
+static_assert(kMaxK * kBand <= kBackChunkFl, "a stage-1 panel (V and T) fits one load");
+static_assert(16 * chase_steps_max(kMaxK) * (kBand + 1) <= kBackChunkFl, "16 sweeps fit one load");
 
-// Every lane loads unconditionally from a clamped column (c <= r reaches back into the
-// previous reflector, or the last element of the packed triangle for r = 0; c >= k reads
-// column k - 1: all inside the problem's k * k floats) and keeps zero where the reflector
-// has no entry, so the loads need no branches.
-template <int KT>
-__device__ __forceinline__ void load_reflector(float (&v)[KT], const float* __restrict__ A, int k, int r, int lane) {
-  const int rr = r < 0 ? 0 : r;
-  const float* row = A + refl_off(k, rr) - (rr + 1);
+// lane L gets lane L - 1 of v; lane 0 gets `in`
+__device__ __forceinline__ float wave_shift_up(float v, float in) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(in), __float_as_int(v), 0x138, 0xf, 0xf, false));  // wave_shr:1
+}
+
+// One sweep of reflectors on the window x (NS registers): block s = 4 i + g, valid below
+// n, its entries at sl[s * (kBand + 1) + u] and tau after them.
+template <int NS>
+__device__ __forceinline__ void back_sweep(float (&x)[NS], const float* sl, int n, int u, int g) {
+  float v[NS], t[NS], d[NS];
 #pragma unroll
-  for (int t = 0; t < KT; ++t) {
-    const int c = lane + 64 * t;
-    const float x = row[c < k ? c : k - 1];
-    v[t] = (r >= 0 && c > r && c < k) ? x : 0.f;
+  for (int i = 0; i < NS; ++i) {
+    const int s = 4 * i + g;
+    const bool ok = s < n;
+    const float vs = sl[(ok ? s : 0) * (kBand + 1) + u];
+    const float ts = sl[(ok ? s : 0) * (kBand + 1) + kBand];
+    v[i] = ok ? vs : 0.f;
+    t[i] = ok ? ts : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < NS; ++i) d[i] = v[i] * x[i];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) d[i] += dpp_mov<0x128, 0xf>(d[i]);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) d[i] += dpp_mov<0x124, 0xf>(d[i]);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) d[i] += dpp_mov<0x122, 0xf>(d[i]);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) d[i] += dpp_mov<0x121, 0xf>(d[i]);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) x[i] = fmaf(-t[i] * d[i], v[i], x[i]);
+}
+
+template <int NS>
+__device__ __forceinline__ void back_shift(float (&x)[NS], float yin) {
+#pragma unroll
+  for (int i = NS - 1; i > 0; --i)
+    x[i] = wave_shift_up(x[i], __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[i - 1]), 63)));
+  x[0] = wave_shift_up(x[0], yin);
+}
+
+// The sweeps jhi down to jl of the chunk staged at `stage` (sweep jl first), on the
+// window of NS = ceil(k / 64) registers, read from and written back to y.
+template <int NS>
+__device__ __forceinline__ void back_chunk_apply(float* y, const float* stage, int k, int jl, int jhi, int slot_fl) {
+  const int lane = threadIdx.x & 63, u = lane & 15, g = lane >> 4;
+  float x[NS];  // the window of sweep jhi starts at row jhi + 1
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int r = jhi + 1 + 64 * i + lane;
+    x[i] = r < k ? y[r] : 0.f;
+  }
+  for (int jj = jhi; jj >= jl; --jj) {
+    back_sweep<NS>(x, stage + (jj - jl) * slot_fl, chase_steps(k, jj), u, g);
+    if (jj > jl) back_shift<NS>(x, y[jj]);
+  }
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int r = jl + 1 + 64 * i + lane;
+    if (r < k) y[r] = x[i];
   }
 }
 
-template <int KT>
-__device__ void backxform_body(const AtMat& M, const float* __restrict__ A, const float* __restrict__ tau,
-                               const float* __restrict__ y_all, int cnt, float* __restrict__ atoms) {
-  const int k = M.k, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int kWaves = kBackThreads / 64;
-  const int64_t stride = int64_t(M.rows) + M.cols;
-  for (int j = wave; j < cnt; j += kWaves) {
-    const float* yin = y_all + int64_t(j) * k;
-    float y[KT];
+__global__ __launch_bounds__(kBackThreads) void at_backchase(const AtMat* __restrict__ mats,
+                                                             const float* __restrict__ refl, float* __restrict__ Y,
+                                                             const int32_t* __restrict__ count, int64_t gram_ws,
+                                                             int64_t refl_ws, int32_t n_mats) {
+  const AtMat M = mats[blockIdx.x];
+  const int64_t w = blockIdx.y;
+  const int cnt = count[w * n_mats + M.mat_index];
+  const int k = M.k;
+  if (cnt == 0 || k < 3) return;
+  const float* R2 = refl + w * refl_ws + M.r_off;
+  float* y_all = Y + w * gram_ws + M.b_off;
+  __shared__ float ys[kBackWaves][kMaxK];
+  __shared__ __align__(16) float stage[kBackChunkFl];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sweeps = k - 2, slot_fl = chase_steps_max(k) * (kBand + 1);
+  const int chunk = kBackChunkFl / slot_fl, ns = (k + 63) / 64;
+  float pre[kBackPre];
+  // the reflectors of sweeps [jlo, jlo + chunk) (a contiguous range of the block); every
+  // load is unconditional, from an index clamped into the range
+  auto load = [&](int jlo) {
+    const float* src = R2 + int64_t(jlo) * slot_fl;
+    const int last = min(chunk, sweeps - jlo) * slot_fl - 1;
 #pragma unroll
-    for (int t = 0; t < KT; ++t) {
-      const int c = lane + 64 * t;
-      y[t] = c < k ? yin[c] : 0.f;
-    }
-    // ring slot d holds reflector r0 - d of the current group (zeros below reflector 0)
-    float ring[kBackAhead][KT], tring[kBackAhead];
+    for (int q = 0; q < kBackPre; ++q) pre[q] = src[min(tid + q * kBackThreads, last)];
+  };
+  for (int j0 = 0; j0 < cnt; j0 += kBackWaves) {
+    const int j = j0 + wave;
+    const bool mine = j < cnt;  // wave-uniform
+    float* y = ys[wave];
+    float* yg = y_all + int64_t(j) * k;
+    if (mine)
+      for (int i = lane; i < k; i += 64) y[i] = yg[i];
+    int jlo = max(0, sweeps - chunk);
+    load(jlo);
+    for (int jhi = sweeps - 1; jhi >= 0;) {
+      __syncthreads();  // the previous chunk is no longer read
 #pragma unroll
-    for (int d = 0; d < kBackAhead; ++d) {
-      load_reflector<KT>(ring[d], A, k, k - 3 - d, lane);
-      tring[d] = k - 3 - d >= 0 ? tau[k - 3 - d] : 0.f;
-    }
-    for (int r0 = k - 3; r0 >= 0; r0 -= kBackAhead) {
-#pragma unroll
-      for (int d = 0; d < kBackAhead; ++d) {
-        const int r = r0 - d;
-        if (r < 0) break;  // wave-uniform
-        float v[KT];
-#pragma unroll
-        for (int t = 0; t < KT; ++t) v[t] = ring[d][t];
-        const float tr = tring[d];
-        load_reflector<KT>(ring[d], A, k, r - kBackAhead, lane);
-        tring[d] = r - kBackAhead >= 0 ? tau[r - kBackAhead] : 0.f;
-        float part = 0.f;
-#pragma unroll
-        for (int t = 0; t < KT; ++t) part = fmaf(v[t], y[t], part);
-        const float f = tr * wave_sum(part);
-#pragma unroll
-        for (int t = 0; t < KT; ++t) y[t] = fmaf(-f, v[t], y[t]);
+      for (int q = 0; q < kBackPre; ++q) stage[tid + q * kBackThreads] = pre[q];
+      __syncthreads();
+      const int jl = jlo;
+      if (jl > 0) load(jlo = max(0, jl - chunk));
+      if (mine) {
+        switch (ns) {
+#define PSGD_BACK_CASE(N) \
+  case N:                 \
+    back_chunk_apply<N>(y, stage, k, jl, jhi, slot_fl); \
+    break;
+          PSGD_BACK_CASE(1) PSGD_BACK_CASE(2) PSGD_BACK_CASE(3) PSGD_BACK_CASE(4)
+          PSGD_BACK_CASE(5) PSGD_BACK_CASE(6) PSGD_BACK_CASE(7) PSGD_BACK_CASE(8)
+          PSGD_BACK_CASE(9) PSGD_BACK_CASE(10) PSGD_BACK_CASE(11) PSGD_BACK_CASE(12)
+          PSGD_BACK_CASE(13) PSGD_BACK_CASE(14) PSGD_BACK_CASE(15) PSGD_BACK_CASE(16)
+#undef PSGD_BACK_CASE
+          default: break;
+        }
       }
+      jhi = jl - 1;
     }
-    float* out = atoms + M.atom_off + int64_t(j) * stride + (M.left ? 0 : M.rows);
-#pragma unroll
-    for (int t = 0; t < KT; ++t) {
-      const int c = lane + 64 * t;
-      if (c < k) out[c] = y[t];
-    }
+    if (mine)
+      for (int i = lane; i < k; i += 64) yg[i] = y[i];
   }
 }
 
-__global__ __launch_bounds__(kBackThreads) void at_backxform(const AtMat* __restrict__ mats,
-                                                             const float* __restrict__ gram,
-                                                             const float* __restrict__ tau_ws,
-                                                             const float* __restrict__ Y,
-                                                             const int32_t* __restrict__ count,
-                                                             float* __restrict__ atoms, int64_t gram_ws,
-                                                             int64_t sv_total, int64_t atom_total, int32_t n_mats) {
+__global__ __launch_bounds__(kBackThreads) void at_backband(const AtMat* __restrict__ mats,
+                                                            const float* __restrict__ gram,
+                                                            const float* __restrict__ Y,
+                                                            const int32_t* __restrict__ count,
+                                                            float* __restrict__ atoms, int64_t gram_ws,
+                                                            int64_t atom_total, int32_t n_mats) {
   const AtMat M = mats[blockIdx.x];
   const int64_t w = blockIdx.y;
   const int cnt = count[w * n_mats + M.mat_index];
   if (cnt == 0) return;
+  const int k = M.k;
   const float* A = gram + w * gram_ws + M.b_off;
-  const float* tau = tau_ws + w * sv_total + M.sv_off;
   const float* y_all = Y + w * gram_ws + M.b_off;
   float* at = atoms + w * atom_total;
-  const int kt = (M.k + 63) / 64;
-  if (kt <= 1) backxform_body<1>(M, A, tau, y_all, cnt, at);
-  else if (kt <= 2) backxform_body<2>(M, A, tau, y_all, cnt, at);
-  else if (kt <= 4) backxform_body<4>(M, A, tau, y_all, cnt, at);
-  else if (kt <= 8) backxform_body<8>(M, A, tau, y_all, cnt, at);
-  else backxform_body<16>(M, A, tau, y_all, cnt, at);
+  __shared__ float ys[kBackWaves][kMaxK];
+  __shared__ __align__(16) float stage[kMaxK * kBackVS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int np = band_panels(k);
+  const int64_t stride = int64_t(M.rows) + M.cols;
+  float pre[kBackPre];
+  // panel p: rows r < m of V, then the kBand rows of T; thread tid always takes column
+  // tid mod 16 (kBackThreads is a multiple of 16), rows tid / 16 + q kBackThreads / 16.
+  // The loads are unconditional, from an index inside the matrix; the masks (V's unit
+  // diagonal and zeros above it, T's upper triangle) are applied when the panel is
+  // stored, so no mask stays live while the loads are in flight.
+  const int ci = tid & 15, rt = tid >> 4;
+  constexpr int kRowStep = kBackThreads / 16;
+  auto load = [&](int p) {
+    const int c = p * kBand, r0 = c + kBand, m = k - r0;
+#pragma unroll
+    for (int q = 0; q < kBackPre; ++q) {
+      const int r = rt + q * kRowStep, a = r - m;
+      const int off = r < m ? (r0 + r) * k + c + ci : (a < kBand ? (c + a) * k + r0 + ci : 0);
+      pre[q] = A[off];
+    }
+  };
+  // V rows at stride kBackVS, T after them
+  auto store = [&](int p) {
+    const int m = k - (p * kBand + kBand), nref = min(kBand, m - 1);
+#pragma unroll
+    for (int q = 0; q < kBackPre; ++q) {
+      const int r = rt + q * kRowStep, a = r - m;
+      const float x = pre[q];
+      const float v = r < m ? (ci < nref && r > ci ? x : (ci < nref && r == ci ? 1.f : 0.f))
+                            : (a <= ci && ci < nref ? x : 0.f);
+      if (a < kBand) stage[r * kBackVS + ci] = v;
+    }
+  };
+  for (int j0 = 0; j0 < cnt; j0 += kBackWaves) {
+    const int j = j0 + wave;
+    const bool mine = j < cnt;  // wave-uniform
+    float* y = ys[wave];
+    if (mine)
+      for (int i = lane; i < k; i += 64) y[i] = y_all[int64_t(j) * k + i];
+    if (np > 0) load(np - 1);
+    for (int p = np - 1; p >= 0; --p) {
+      const int r0 = p * kBand + kBand, m = k - r0;
+      __syncthreads();
+      store(p);
+      __syncthreads();
+      if (p > 0) load(p - 1);
+      if (mine) {
+        const f4* V4 = reinterpret_cast<const f4*>(stage);
+        const f4* T4 = reinterpret_cast<const f4*>(stage + m * kBackVS);
+        float z[kBand];
+#pragma unroll
+        for (int i = 0; i < kBand; ++i) z[i] = 0.f;
+        for (int r = lane; r < m; r += 64) {
+          const float yr = y[r0 + r];
+#pragma unroll
+          for (int q4 = 0; q4 < kBand / 4; ++q4) {
+            const f4 v = V4[r * (kBackVS / 4) + q4];
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) z[4 * q4 + e2] = fmaf(v[e2], yr, z[4 * q4 + e2]);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < kBand; ++i) z[i] = wave_sum(z[i]);
+        float t[kBand];
+#pragma unroll
+        for (int a = 0; a < kBand; ++a) {
+          float acc = 0.f;
+#pragma unroll
+          for (int q4 = a / 4; q4 < kBand / 4; ++q4) {
+            const f4 tv = T4[a * (kBackVS / 4) + q4];
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) acc = fmaf(tv[e2], z[4 * q4 + e2], acc);
+          }
+          t[a] = acc;
+        }
+        for (int r = lane; r < m; r += 64) {
+          float acc = 0.f;
+#pragma unroll
+          for (int q4 = 0; q4 < kBand / 4; ++q4) {
+            const f4 v = V4[r * (kBackVS / 4) + q4];
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) acc = fmaf(v[e2], t[4 * q4 + e2], acc);
+          }
+          y[r0 + r] -= acc;
+        }
+      }
+    }
+    if (mine) {
+      float* out = at + M.atom_off + int64_t(j) * stride + (M.left ? 0 : M.rows);
+      for (int i = lane; i < k; i += 64) out[i] = y[i];
+    }
+  }
 }
 
 // ------------------------------------------------------------------ at_factor
@@ -1208,7 +1606,7 @@ extern "C" psgd_status psgd_atomo_plan_create(const psgd_layer* layers, int32_t 
     plan = new psgd_atomo_plan();
     plan->n_workers = n_workers;
     plan->budget = budget;
-    int64_t off = 0, sv = 0, atom = 0, gram = 0;
+    int64_t off = 0, sv = 0, atom = 0, gram = 0, refl = 0;
     for (int32_t i = 0; i < n_layers; ++i) {
       const int64_t rows = layers[i].rows, cols = layers[i].cols;
       if (rows < 1 || cols < 1 || rows > (int64_t(1) << 31) || cols > (int64_t(1) << 31) ||
@@ -1240,6 +1638,7 @@ extern "C" psgd_status psgd_atomo_plan_create(const psgd_layer* layers, int32_t 
         m.sv_off = sv;
         m.atom_off = atom;
         m.b_off = gram;
+        m.r_off = refl;
         m.rows = int32_t(rows);
         m.cols = int32_t(cols);
         m.k = int32_t(k);
@@ -1249,6 +1648,8 @@ extern "C" psgd_status psgd_atomo_plan_create(const psgd_layer* layers, int32_t 
         sv += k;
         atom += k * (rows + cols);
         gram += (k * k + 63) / 64 * 64;
+        refl += (chase_block(int(k)) + 63) / 64 * 64;
+        plan->max_k = std::max(plan->max_k, int32_t(k));
       }
       plan->info.push_back(li);
       off += (li.numel + 63) / 64 * 64;
@@ -1257,6 +1658,7 @@ extern "C" psgd_status psgd_atomo_plan_create(const psgd_layer* layers, int32_t 
     plan->sv_total = sv;
     plan->atom_total = atom;
     plan->gram_total = gram;
+    plan->refl_total = refl;
     plan->numel = 0;
     const uint64_t W = uint64_t(n_workers);
     uint64_t model = 0;
@@ -1306,10 +1708,7 @@ extern "C" psgd_status psgd_atomo_plan_create(const psgd_layer* layers, int32_t 
       delete plan;
       return fail(PSGD_ERR_UNSUPPORTED, std::string(fn) + ": more than 65535 factor tiles in one plan");
     }
-    for (size_t mi = 0; mi < plan->mats.size(); ++mi) {
-      plan->tri_list.push_back(int32_t(mi));
-      plan->tri_kt = std::max(plan->tri_kt, tri_class(plan->mats[mi].k));
-    }
+    for (size_t mi = 0; mi < plan->mats.size(); ++mi) plan->tri_list.push_back(int32_t(mi));
     std::stable_sort(plan->tri_list.begin(), plan->tri_list.end(),
                      [&](int32_t x, int32_t y) { return plan->mats[size_t(x)].k > plan->mats[size_t(y)].k; });
     for (const auto& li : plan->info)
@@ -1322,8 +1721,8 @@ extern "C" psgd_status psgd_atomo_plan_create(const psgd_layer* layers, int32_t 
     ws = a256(ws + W * uint64_t(gram) * 4);
     plan->ws_y = ws;
     ws = a256(ws + W * uint64_t(gram) * 4);
-    plan->ws_tau = ws;
-    ws = a256(ws + W * uint64_t(sv) * 4);
+    plan->ws_refl = ws;
+    ws = a256(ws + W * uint64_t(refl) * 4);
     plan->ws_d = ws;
     ws = a256(ws + W * uint64_t(sv) * 4);
     plan->ws_e = ws;
@@ -1477,13 +1876,14 @@ extern "C" psgd_status psgd_atomo_step(psgd_atomo_plan* plan, const float* grads
   char* ws = static_cast<char*>(workspace);
   float* gram = reinterpret_cast<float*>(ws + plan->ws_gram);
   float* Y = reinterpret_cast<float*>(ws + plan->ws_y);
-  float* tau = reinterpret_cast<float*>(ws + plan->ws_tau);
+  float* refl = reinterpret_cast<float*>(ws + plan->ws_refl);
   float* dd = reinterpret_cast<float*>(ws + plan->ws_d);
   float* ee = reinterpret_cast<float*>(ws + plan->ws_e);
   float* lam = reinterpret_cast<float*>(ws + plan->ws_lam);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t ld = int64_t(stride);
   const int64_t gws = plan->gram_total;
+  const int64_t rws = plan->refl_total;
   const int64_t svt = plan->sv_total;
   const int64_t att = plan->atom_total;
   const int32_t nmats = int32_t(nm);
@@ -1496,19 +1896,15 @@ extern "C" psgd_status psgd_atomo_step(psgd_atomo_plan* plan, const float* grads
       return s;
     {
       const int32_t* list = dt.tri_list;
-      const dim3 tgrid(mgrid.y, mgrid.x);  // (workers, matrices)
-      switch (plan->tri_kt) {
-        case 16: s = launch(plan, kTridiag, at_tridiag<16>, tgrid, dim3(kTriThreads), st, list, M, gram, gws, tau, dd, ee, svt); break;
-        case 8: s = launch(plan, kTridiag, at_tridiag<8>, tgrid, dim3(kTriThreads), st, list, M, gram, gws, tau, dd, ee, svt); break;
-        case 4: s = launch(plan, kTridiag, at_tridiag<4>, tgrid, dim3(kTriThreads), st, list, M, gram, gws, tau, dd, ee, svt); break;
-        case 2: s = launch(plan, kTridiag, at_tridiag<2>, tgrid, dim3(kTriThreads), st, list, M, gram, gws, tau, dd, ee, svt); break;
-        default: s = launch(plan, kTridiag, at_tridiag<1>, tgrid, dim3(kTriThreads), st, list, M, gram, gws, tau, dd, ee, svt); break;
-      }
-      if (s != PSGD_OK) return s;
+      const dim3 tgrid(mgrid.y, mgrid.x);  // (workers, matrices in decreasing k)
+      if ((s = launch(plan, kBandK, at_band, tgrid, dim3(kBandThreads), st, list, M, gram, gws)) != PSGD_OK) return s;
+      if ((s = launch(plan, kChase, at_chase, tgrid, dim3(kChaseThreads), st, list, M,
+                      static_cast<const float*>(gram), gws, refl, rws, dd, ee, svt)) != PSGD_OK)
+        return s;
     }
     // eigenvalues in slices of kEigSlots per workgroup: a large matrix's bisections
     // spread over several compute units
-    const dim3 egrid(mgrid.x, mgrid.y, unsigned((64 * plan->tri_kt + kEigSlots - 1) / kEigSlots));
+    const dim3 egrid(mgrid.x, mgrid.y, unsigned((plan->max_k + kEigSlots - 1) / kEigSlots));
     if ((s = launch(plan, kEig, at_eig, egrid, dim3(kEigThreads), st, M, static_cast<const float*>(dd),
                     static_cast<const float*>(ee), lam, sigma, svt)) != PSGD_OK)
       return s;
@@ -1520,9 +1916,12 @@ extern "C" psgd_status psgd_atomo_step(psgd_atomo_plan* plan, const float* grads
                     static_cast<const int32_t*>(index), static_cast<const int32_t*>(count), Y, gws, svt, nmats)) !=
         PSGD_OK)
       return s;
-    if ((s = launch(plan, kBack, at_backxform, mgrid, dim3(kBackThreads), st, M, static_cast<const float*>(gram),
-                    static_cast<const float*>(tau), static_cast<const float*>(Y),
-                    static_cast<const int32_t*>(count), atoms, gws, svt, att, nmats)) != PSGD_OK)
+    if ((s = launch(plan, kBackChase, at_backchase, mgrid, dim3(kBackThreads), st, M, static_cast<const float*>(refl),
+                    Y, static_cast<const int32_t*>(count), gws, rws, nmats)) != PSGD_OK)
+      return s;
+    if ((s = launch(plan, kBackBand, at_backband, mgrid, dim3(kBackThreads), st, M, static_cast<const float*>(gram),
+                    static_cast<const float*>(Y), static_cast<const int32_t*>(count), atoms, gws, att, nmats)) !=
+        PSGD_OK)
       return s;
     if ((s = launch(plan, kFactor, at_factor, dim3(unsigned(W), unsigned(plan->ftiles.size())),
                     dim3(kFactorThreads), st, static_cast<const FactorTile*>(dt.ftiles), M, grads, ld,

@@ -121,8 +121,8 @@ psgd_status psgd_atomo_step(psgd_atomo_plan* plan, const float* grads, const flo
                             void* workspace, void* stream);
 
 /* Kernel timing as psgd_plan_set_timing / psgd_plan_kernel_stats.  Kernel names:
- * "at_gram", "at_tridiag", "at_eig", "at_sample", "at_vectors", "at_backxform",
- * "at_factor", "at_update". */
+ * "at_gram", "at_band", "at_chase", "at_eig", "at_sample", "at_vectors", "at_backchase",
+ * "at_backband", "at_factor", "at_update". */
 psgd_status psgd_atomo_plan_set_timing(psgd_atomo_plan* plan, int32_t enable);
 psgd_status psgd_atomo_plan_kernel_stats(psgd_atomo_plan* plan, psgd_kernel_stat* out, int32_t capacity,
                                          int32_t* count, int32_t reset);
