@@ -410,6 +410,16 @@ __device__ __forceinline__ Refl make_refl(float alpha, float sig2) {
   return h;
 }
 
+// LDS index of element (r, c) of an r x kBand matrix stored in rows of kBand floats, its
+// four float4 chunks permuted by row ((c / 4) xor (r / 2) mod 4): lanes that read one
+// chunk of sixteen consecutive rows as float4 then spread over all banks.
+__device__ __forceinline__ int vz(int r, int c) { return r * kBand + ((((c >> 2) ^ (r >> 1)) & 3) << 2) + (c & 3); }
+__device__ __forceinline__ f4 vz4(const float* b, int r, int q4) {
+  return *reinterpret_cast<const f4*>(b + r * kBand + (((q4 ^ (r >> 1)) & 3) << 2));
+}
+
+// KR: registers per lane for a panel column (rows lane + 64 q), so k <= 64 KR.
+template <int KR>
 __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restrict__ list,
                                                         const AtMat* __restrict__ mats, float* __restrict__ gram,
                                                         int64_t gram_ws) {
@@ -419,24 +429,30 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
   const int np = band_panels(k);
   if (np == 0) return;  // already a band
   float* A = gram + int64_t(blockIdx.x) * gram_ws + M.b_off;
-  // P1 rows of kVS = kBand + 1 floats (rows read lane by lane fall in different banks):
-  // the panel, its reflectors, then A22 V (partial sums, then the sums).  P2 rows of kBand
-  // floats, 16-byte aligned for the broadcast reads of the products: V, then (P1) Z.
-  __shared__ __align__(16) float P1[kMaxK * kVS];
-  __shared__ __align__(16) float P2[kMaxK * kBand];
+  // U: the panel in rows of kVS = kBand + 1 floats (rows read lane by lane fall in
+  // different banks) and its clean reflectors, then A22 V, then Z (vz layout).  VB: V in
+  // the vz layout.  Rows from m to the next multiple of 16 hold zeros.
+  __shared__ __align__(16) float U[kMaxK * kVS];
+  __shared__ __align__(16) float VB[kMaxK * kBand];
   __shared__ float Tm[kBand][kBand + 1];
   __shared__ float Gm[kBand][kBand + 1];  // V^T V, then V^T X
   __shared__ float Sm[kBand][kBand + 1];
   __shared__ float part[4][kBand * kBand];
   __shared__ float vbuf[2][kMaxK];  // the current reflector, double-buffered
   __shared__ float hbuf[2][3];      // its tau, scale, beta
+  float* ZB = U;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int kRegs = kMaxK / 64;  // a panel column in registers: row lane + 64 q
+  const int li = lane & 15, lg = lane >> 4;
+  constexpr int kRegs = KR;  // a panel column in registers: row lane + 64 q
+  constexpr int kWaves = kBandThreads / 64;
+  const bool vec = (k & 3) == 0;
   for (int p = 0; p < np; ++p) {
     const int c = p * kBand, r0 = c + kBand, m = k - r0;
     const int nref = min(kBand, m - 1);
+    const int nb = (m + kBand - 1) / kBand;
+    float* A22 = A + int64_t(r0) * k + r0;
     for (int e = tid; e < m * kBand; e += kBandThreads)
-      P1[(e / kBand) * kVS + e % kBand] = A[int64_t(r0 + e / kBand) * k + c + e % kBand];
+      U[(e / kBand) * kVS + e % kBand] = A[int64_t(r0 + e / kBand) * k + c + e % kBand];
     if (tid < kBand * kBand) Tm[tid / kBand][tid % kBand] = 0.f;
     __syncthreads();
     // QR of the panel: wave t holds column t in registers.  Reflector i is formed by wave
@@ -446,7 +462,7 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
 #pragma unroll
     for (int q = 0; q < kRegs; ++q) {
       const int r = lane + 64 * q;
-      col[q] = r < m ? P1[r * kVS + wave] : 0.f;
+      col[q] = r < m ? U[r * kVS + wave] : 0.f;
     }
     // wave w forms reflector w from its column: v (rows > w), beta at row w
     auto form = [&](int i) {
@@ -495,29 +511,32 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
       }
     }
     __syncthreads();
-    // the panel (R on the band, the reflectors below it) back into P1 and the matrix; P1
-    // and P2 become the unit lower trapezoidal matrix V of the reflectors
+    // the panel (R on the band, the reflectors below it) back into U and the matrix; U
+    // and VB become the unit lower trapezoidal matrix V of the reflectors
 #pragma unroll
     for (int q = 0; q < kRegs; ++q) {
       const int r = lane + 64 * q;
-      if (r < m) P1[r * kVS + wave] = col[q];
+      if (r < m) U[r * kVS + wave] = col[q];
     }
     __syncthreads();
-    for (int e = tid; e < m * kBand; e += kBandThreads) {
+    for (int e = tid; e < nb * kBand * kBand; e += kBandThreads) {
       const int i = e / kBand, t = e % kBand;
-      const float x = P1[i * kVS + t];
-      A[int64_t(r0 + i) * k + c + t] = x;
-      const float v = t < nref ? (i > t ? x : (i == t ? 1.f : 0.f)) : 0.f;
-      P1[i * kVS + t] = v;
-      P2[e] = v;
+      float v = 0.f;
+      if (i < m) {
+        const float x = U[i * kVS + t];
+        A[int64_t(r0 + i) * k + c + t] = x;
+        v = t < nref ? (i > t ? x : (i == t ? 1.f : 0.f)) : 0.f;
+        U[i * kVS + t] = v;
+      }
+      VB[vz(i, t)] = v;
     }
     __syncthreads();
     // T: T[i][i] = tau_i, T[0:i, i] = -tau_i T[0:i, 0:i] (V^T v_i)[0:i]
-    for (int pr = wave; pr < kBand * kBand; pr += kBandThreads / 64) {
+    for (int pr = wave; pr < kBand * kBand; pr += kWaves) {
       const int a = pr / kBand, b = pr % kBand;
       if (a < b && b < nref) {
         float g = 0.f;
-        for (int r = b + lane; r < m; r += 64) g = fmaf(P1[r * kVS + a], P1[r * kVS + b], g);
+        for (int r = b + lane; r < m; r += 64) g = fmaf(U[r * kVS + a], U[r * kVS + b], g);
         g = wave_sum(g);
         if (lane == 0) Gm[a][b] = g;
       }
@@ -539,38 +558,94 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
 #pragma unroll
         for (int b = 0; b < kBand; ++b) Tm[lane][b] = tr[b];
     }
-    __syncthreads();
+    __syncthreads();  // U (the panel) is no longer read: it becomes X
     if (tid < nref * nref) A[int64_t(c + tid / nref) * k + r0 + tid % nref] = Tm[tid / nref][tid % nref];
-    // X = A22 V: thread (r, part) sums rows [part * rl, ...) of column r of A22 (its row r
-    // by symmetry), reading along rows; the parts are added in a fixed order
-    const int nparts = max(1, kBandThreads / m);
-    const int rl = (m + nparts - 1) / nparts;
-    const int rr = tid % m, pi = tid / m;
-    const float* A22 = A + int64_t(r0) * k + r0;
-    const f4* V4 = reinterpret_cast<const f4*>(P2);
-    if (pi < nparts) {
-      float x[kBand];
+    // X = A22 V with the matrix instruction D += A B (A 16 x 4, B 4 x 16; lane l gives
+    // A[l mod 16][l / 16] and B[l / 16][l mod 16]; D[i][j] is accumulator i mod 4 of lane
+    // j + 16 (i / 4)).  Wave w takes the row blocks I = w, w + 16, ...: for each column
+    // block J, four instructions with A[i][q] = tile(I, J)[i][4 q + e] and B[q][j] =
+    // V[16 J + 4 q + e][j], e = 0..3.  Only the lower triangle is stored: tile (I, J) is
+    // read from row block I for J < I (along rows), as the transpose of tile (J, I) for
+    // J > I (along columns), and entry by entry from the lower triangle for J = I.  Rows
+    // and columns at or beyond m read as zero (indices clamped into the matrix); the loads
+    // run four tiles ahead of the instructions.
+    for (int I = wave; I < nb; I += kWaves) {
+      const int RI = I * kBand, i = RI + li, ic = min(i, m - 1);
+      const bool iok = i < m;
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+      float bf[4][4];
+      auto mma = [&](const float (&a)[4], int J) {
 #pragma unroll
-      for (int q = 0; q < kBand; ++q) x[q] = 0.f;
-      const int l1 = min(m, (pi + 1) * rl);
-      for (int l = pi * rl; l < l1; ++l) {
-        const float a = A22[int64_t(l) * k + rr];
+        for (int e = 0; e < 4; ++e)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], VB[vz(J * kBand + 4 * lg + e, li)], acc, 0, 0, 0);
+      };
+      {  // J < I: columns below RI < m
+        const float* rowp = A22 + uint32_t(ic * k + 4 * lg);
+        auto ld = [&](int J, float (&a)[4]) {
+          if (vec) {
+            const f4 x = *reinterpret_cast<const f4*>(rowp + J * kBand);
 #pragma unroll
-        for (int q4 = 0; q4 < kBand / 4; ++q4) {
-          const f4 v = V4[l * (kBand / 4) + q4];
+            for (int e = 0; e < 4; ++e) a[e] = iok ? x[e] : 0.f;
+          } else {
 #pragma unroll
-          for (int z = 0; z < 4; ++z) x[4 * q4 + z] = fmaf(a, v[z], x[4 * q4 + z]);
+            for (int e = 0; e < 4; ++e) {
+              const float x = rowp[J * kBand + e];
+              a[e] = iok ? x : 0.f;
+            }
+          }
+        };
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          if (d < I) ld(d, bf[d]);
+        for (int J0 = 0; J0 < I; J0 += 4) {
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const int J = J0 + d;
+            if (J < I) {  // wave-uniform
+              mma(bf[d], J);
+              if (J + 4 < I) ld(J + 4, bf[d]);
+            }
+          }
+        }
+      }
+      {  // J = I
+        float a[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int cix = RI + 4 * lg + e;
+          const bool low = i >= cix;
+          const int rr = min(low ? i : cix, m - 1), cc = min(low ? cix : i, m - 1);
+          const float x = A22[uint32_t(rr * k + cc)];
+          a[e] = (iok && cix < m) ? x : 0.f;
+        }
+        mma(a, I);
+      }
+      {  // J > I: the transposes of stored tiles (J, I), rows 16 J + 4 lg + e
+        const float* colp = A22 + ic;
+        auto ld = [&](int J, float (&a)[4]) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = J * kBand + 4 * lg + e;
+            const float x = colp[uint32_t(min(r, m - 1) * k)];
+            a[e] = (iok && r < m) ? x : 0.f;
+          }
+        };
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          if (I + 1 + d < nb) ld(I + 1 + d, bf[d]);
+        for (int J0 = I + 1; J0 < nb; J0 += 4) {
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const int J = J0 + d;
+            if (J < nb) {  // wave-uniform
+              mma(bf[d], J);
+              if (J + 4 < nb) ld(J + 4, bf[d]);
+            }
+          }
         }
       }
 #pragma unroll
-      for (int q = 0; q < kBand; ++q) P1[(pi * m + rr) * kVS + q] = x[q];
-    }
-    __syncthreads();
-    for (int e = tid; e < m * kBand; e += kBandThreads) {
-      const int r = e / kBand, q = e % kBand;
-      float sum = P1[r * kVS + q];
-      for (int pp = 1; pp < nparts; ++pp) sum += P1[(pp * m + r) * kVS + q];
-      P1[r * kVS + q] = sum;
+      for (int v = 0; v < 4; ++v) ZB[vz(RI + 4 * lg + v, li)] = acc[v];
     }
     __syncthreads();
     {  // V^T X, four row quarters per entry
@@ -578,7 +653,7 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
       const int a = en / kBand, b = en % kBand;
       const int lq = (m + 3) / 4, l0 = qt * lq, l1 = min(m, l0 + lq);
       float g = 0.f;
-      for (int l = l0; l < l1; ++l) g = fmaf(P2[l * kBand + a], P1[l * kVS + b], g);
+      for (int l = l0; l < l1; ++l) g = fmaf(VB[vz(l, a)], ZB[vz(l, b)], g);
       part[qt][en] = g;
     }
     __syncthreads();
@@ -598,13 +673,16 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
       Sm[i][j] = y;
     }
     __syncthreads();
-    float zrow[kBand];  // Z = X T - V S / 2, row tid
-    if (tid < m) {
-      float x[kBand], v[kBand];
+    if (tid < m) {  // Z = X T - V S / 2, row tid, in place of X
+      float x[kBand], v[kBand], zrow[kBand];
 #pragma unroll
-      for (int q = 0; q < kBand; ++q) {
-        x[q] = P1[tid * kVS + q];
-        v[q] = P2[tid * kBand + q];
+      for (int q4 = 0; q4 < kBand / 4; ++q4) {
+        const f4 xv = vz4(ZB, tid, q4), vv = vz4(VB, tid, q4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[4 * q4 + e] = xv[e];
+          v[4 * q4 + e] = vv[e];
+        }
       }
 #pragma unroll
       for (int j = 0; j < kBand; ++j) {
@@ -616,32 +694,41 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
         for (int b = 0; b < kBand; ++b) vs = fmaf(v[b], Sm[b][j], vs);
         zrow[j] = fmaf(-0.5f, vs, z);
       }
+#pragma unroll
+      for (int q4 = 0; q4 < kBand / 4; ++q4)
+        *reinterpret_cast<f4*>(ZB + tid * kBand + (((q4 ^ (tid >> 1)) & 3) << 2)) =
+            f4{zrow[4 * q4], zrow[4 * q4 + 1], zrow[4 * q4 + 2], zrow[4 * q4 + 3]};
     }
-    __syncthreads();  // every row of X read: P1 takes Z with rows of kBand floats
-    if (tid < m)
-#pragma unroll
-      for (int q = 0; q < kBand; ++q) P1[tid * kBand + q] = zrow[q];
     __syncthreads();
-    // A22 -= V Z^T + Z V^T, thread (r, part) on column r of its rows
-    if (pi < nparts) {
-      const f4* Z4 = reinterpret_cast<const f4*>(P1);
-      float vr[kBand], zr[kBand];
+    // A22 -= V Z^T + Z V^T on the stored (lower) tiles, I >= J: the tile is the
+    // accumulator (lane li + 16 lg, register v: row 16 I + 4 lg + v, column 16 J + li),
+    // then eight instructions: A[i][q] = -V[16 I + i][4 q + e], B[q][j] = Z[16 J + j][4 q + e],
+    // and the same with V and Z exchanged.  A diagonal tile keeps its upper triangle.
+    const int nt = nb * (nb + 1) / 2;
+    for (int t = wave; t < nt; t += kWaves) {
+      int I = int((sqrtf(8.f * float(t) + 1.f) - 1.f) * 0.5f);
+      while (I * (I + 1) / 2 > t) --I;
+      while ((I + 1) * (I + 2) / 2 <= t) ++I;
+      const int J = t - I * (I + 1) / 2;
+      const int RI = I * kBand, RJ = J * kBand;
+      const int col = RJ + li, cc = min(col, m - 1);
+      f4 acc;
 #pragma unroll
-      for (int q = 0; q < kBand; ++q) {
-        vr[q] = P2[rr * kBand + q];
-        zr[q] = P1[rr * kBand + q];
+      for (int v = 0; v < 4; ++v) {
+        const int r = RI + 4 * lg + v;
+        const float x = A22[int64_t(min(r, m - 1)) * k + cc];
+        acc[v] = (r < m && col < m) ? x : 0.f;
       }
-      const int l1 = min(m, (pi + 1) * rl);
-      float* col2 = A + int64_t(r0) * k + r0 + rr;
-      for (int l = pi * rl; l < l1; ++l) {
-        float sum = 0.f;
+      const f4 vi = vz4(VB, RI + li, lg), zi = vz4(ZB, RI + li, lg);
+      const f4 vj = vz4(VB, RJ + li, lg), zj = vz4(ZB, RJ + li, lg);
 #pragma unroll
-        for (int q4 = 0; q4 < kBand / 4; ++q4) {
-          const f4 v = V4[l * (kBand / 4) + q4], z = Z4[l * (kBand / 4) + q4];
+      for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(-vi[e], zj[e], acc, 0, 0, 0);
 #pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) sum = fmaf(v[e2], zr[4 * q4 + e2], fmaf(z[e2], vr[4 * q4 + e2], sum));
-        }
-        col2[int64_t(l) * k] -= sum;
+      for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(-zi[e], vj[e], acc, 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = RI + 4 * lg + v;
+        if (r < m && col < m && (I != J || 4 * lg + v >= li)) A22[int64_t(r) * k + col] = acc[v];
       }
     }
     __syncthreads();
@@ -1897,7 +1984,11 @@ extern "C" psgd_status psgd_atomo_step(psgd_atomo_plan* plan, const float* grads
     {
       const int32_t* list = dt.tri_list;
       const dim3 tgrid(mgrid.y, mgrid.x);  // (workers, matrices in decreasing k)
-      if ((s = launch(plan, kBandK, at_band, tgrid, dim3(kBandThreads), st, list, M, gram, gws)) != PSGD_OK) return s;
+      if ((s = plan->max_k <= kMaxK / 2
+                   ? launch(plan, kBandK, at_band<kMaxK / 128>, tgrid, dim3(kBandThreads), st, list, M, gram, gws)
+                   : launch(plan, kBandK, at_band<kMaxK / 64>, tgrid, dim3(kBandThreads), st, list, M, gram, gws)) !=
+          PSGD_OK)
+        return s;
       if ((s = launch(plan, kChase, at_chase, tgrid, dim3(kChaseThreads), st, list, M,
                       static_cast<const float*>(gram), gws, refl, rws, dd, ee, svt)) != PSGD_OK)
         return s;
