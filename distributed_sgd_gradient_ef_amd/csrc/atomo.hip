@@ -137,11 +137,18 @@ __device__ __forceinline__ float dpp_mov(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
 }
 
+// A DPP move that every lane reads from a lane of the wave (row rotates, quad
+// permutes): bound_ctrl set, so a following add folds into one v_add_f32_dpp.
+template <int CTRL>
+__device__ __forceinline__ float dpp_all(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-  v += dpp_mov<0xB1, 0xf>(v);   // quad_perm [1,0,3,2]: pairs
-  v += dpp_mov<0x4E, 0xf>(v);   // quad_perm [2,3,0,1]: quads
-  v += dpp_mov<0x124, 0xf>(v);  // row_ror:4: two quads
-  v += dpp_mov<0x128, 0xf>(v);  // row_ror:8: the 16-lane row
+  v += dpp_all<0xB1>(v);   // quad_perm [1,0,3,2]: pairs
+  v += dpp_all<0x4E>(v);   // quad_perm [2,3,0,1]: quads
+  v += dpp_all<0x124>(v);  // row_ror:4: two quads
+  v += dpp_all<0x128>(v);  // row_ror:8: the 16-lane row
   v += dpp_mov<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3: rows 0+1, 2+3
   v += dpp_mov<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3: lane 63 has all four
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
@@ -384,10 +391,10 @@ __device__ __forceinline__ void lds_barrier() {
 // Sum over each 16-lane row of the wave (every lane of the row gets it): four row rotates.
 // All 64 lanes must be active.
 __device__ __forceinline__ float row_sum16(float v) {
-  v += dpp_mov<0x128, 0xf>(v);  // row_ror:8
-  v += dpp_mov<0x124, 0xf>(v);  // row_ror:4
-  v += dpp_mov<0x122, 0xf>(v);  // row_ror:2
-  v += dpp_mov<0x121, 0xf>(v);  // row_ror:1
+  v += dpp_all<0x128>(v);  // row_ror:8
+  v += dpp_all<0x124>(v);  // row_ror:4
+  v += dpp_all<0x122>(v);  // row_ror:2
+  v += dpp_all<0x121>(v);  // row_ror:1
   return v;
 }
 
@@ -735,88 +742,87 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
   }
 }
 
-// One chase step (sweep j, step s) by one wave.  Lane = u + 16 g: u indexes the 16 rows
-// (or columns) of the reflector's block, g one of four groups sharing the rest.  `band`
-// holds element (r, c), r >= c, of the lower band at c * 2 kBand + (r - c).  Every load
-// reads an in-range element (indices clamped) and keeps zero where it has no element, so
-// the four independent reductions of each phase run without branches between them.
-__device__ __forceinline__ void chase_step(float* band, float* sv, float* sw, float* __restrict__ R2, int k, int j,
-                                           int s) {
-  const int lane = threadIdx.x & 63, u = lane & 15, g = lane >> 4;
+// One chase step (sweep j, step s) by one wave.  Lane = u + 16 g; in every block the lane
+// holds the four entries whose other index is t = 4 g + c, c = 0..3: L(t, u) of the
+// bulge columns left of the block, D(u, t) of the diagonal block, B(u, t) of the rows
+// below it.  A product with the reflector is then four in-register terms and a sum over
+// the four 16-lane rows (two lane swaps).  `band` holds element (r, c), r >= c, of the
+// lower band at c * (2 kBand - 1) + r; with the kChasePad zeros after k (2 kBand) entries
+// every load of a step stays in the array without clamping.  The step's loads are all
+// issued first (the blocks it reads and writes are disjoint, and no other step of the
+// round touches them), and what lies outside the matrix or the block is zeroed by
+// selection.  dk[c] = (2 kBand - 1) min(u, t) + max(u, t) places element (r0 + u, r0 + t)
+// of the diagonal block (lower triangle).
+constexpr int kChaseLd = 2 * kBand - 1;
+constexpr int kChasePad = 2 * kBand * kBand;
+
+// sum of v over the four 16-lane rows (each lane gets the sum for its position in the
+// row): exchange rows 0<->1, 2<->3, then the halves, adding both results of each swap
+__device__ __forceinline__ float rows_sum4(float v) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+__device__ __forceinline__ void chase_step(float* band, float* __restrict__ R2, int k, int j, int s, int u, int g,
+                                           const int (&dk)[4]) {
   const int r0 = j + 1 + s * kBand;
   const int len = min(kBand, k - r0);
+  const int len2 = len == kBand ? min(kBand, k - r0 - kBand) : 0;
   const int pc = s == 0 ? j : r0 - kBand;  // the column to clear below row r0
-  auto at = [&](int r, int c) -> float& { return band[c * (2 * kBand) + (r - c)]; };
+  const int bx = pc * kChaseLd + r0;                         // x(t) = (r0 + t, pc)
+  const int bl = (pc + 1 + u) * kChaseLd + r0 + 4 * g;       // L(4 g + c, u) at + c
+  const int bd = r0 * (kChaseLd + 1);                        // D(u, 4 g + c) at + dk[c]
+  const int bb = (r0 + 4 * g) * kChaseLd + r0 + kBand + u;   // B(u, 4 g + c) at + c kChaseLd
+  const float x0 = band[bx], xu = band[bx + u];
+  float xa[4], L[4], D[4], B[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    xa[c] = band[bx + 4 * g + c];
+    L[c] = band[bl + c];
+    D[c] = band[bd + dk[c]];
+    B[c] = band[bb + c * kChaseLd];
+  }
   const bool in = u < len;
-  const int uc = in ? u : 0;
-  const float x0 = at(r0 + uc, pc);
-  const float x = in ? x0 : 0.f;
-  const Refl h = make_refl(at(r0, pc), row_sum16(u >= 1 ? x * x : 0.f));
-  const float v = in ? (u == 0 ? 1.f : x * h.scale) : 0.f;
+  const float x = in ? xu : 0.f;
+  const Refl h = make_refl(x0, row_sum16(u >= 1 ? x * x : 0.f));
+  const float vu = in ? (u == 0 ? 1.f : x * h.scale) : 0.f;
   float* slot = R2 + (int64_t(j) * chase_steps_max(k) + s) * (kBand + 1);
   if (g == 0) {
-    slot[u] = v;
-    if (in) at(r0 + u, pc) = u == 0 ? h.beta : 0.f;
-    sv[u] = v;
+    slot[u] = vu;
+    if (in) band[bx + u] = u == 0 ? h.beta : 0.f;
   }
-  if (lane == 0) slot[kBand] = h.tau;
+  if (threadIdx.x % 64 == 0) slot[kBand] = h.tau;
   if (h.tau == 0.f) return;  // H = I (wave-uniform)
   const float tau = h.tau;
-  if (s > 0) {  // from the left on the rest of the block the previous step filled
-    float ev[4], y[4];
+  float vv[4], pl = 0.f, pd = 0.f, pb = 0.f;
 #pragma unroll
-    for (int i2 = 0; i2 < 4; ++i2) {
-      const int cc = pc + 1 + g + 4 * i2;
-      const bool ok = in && cc < r0;
-      const float e = at(r0 + uc, ok ? cc : pc + 1);
-      ev[i2] = ok ? e : 0.f;
-    }
-#pragma unroll
-    for (int i2 = 0; i2 < 4; ++i2) y[i2] = row_sum16(v * ev[i2]);
-#pragma unroll
-    for (int i2 = 0; i2 < 4; ++i2) {
-      const int cc = pc + 1 + g + 4 * i2;
-      if (in && cc < r0) at(r0 + u, cc) = ev[i2] - tau * y[i2] * v;
-    }
+  for (int c = 0; c < 4; ++c) {
+    const int t = 4 * g + c;
+    vv[c] = t < len ? (t == 0 ? 1.f : xa[c] * h.scale) : 0.f;
+    L[c] = (s > 0 && u < kBand - 1 && t < len) ? L[c] : 0.f;  // columns pc + 1 + u < r0
+    D[c] = (in && t < len) ? D[c] : 0.f;
+    B[c] = u < len2 ? B[c] : 0.f;
+    pl = fmaf(vv[c], L[c], pl);
+    pd = fmaf(D[c], vv[c], pd);
+    pb = fmaf(B[c], vv[c], pb);
   }
+  const float yl = rows_sum4(pl);  // (v^T L)[u]
+  const float pp = rows_sum4(pd);  // (D v)[u]
+  const float yb = rows_sum4(pb);  // (B v)[u]
   // both sides of the diagonal block D: p = D v, w = tau p - tau^2 (v^T p) v / 2,
-  // D -= v w^T + w v^T on its lower triangle
-  float pp = 0.f;
+  // D -= v w^T + w v^T on its lower triangle; w[4 g + c] comes from lane 20 g + c
+  const float vp = row_sum16(vu * pp);
+  const float c2 = 0.5f * tau * tau * vp;
+  const float w = fmaf(tau, pp, -c2 * vu);
 #pragma unroll
-  for (int i2 = 0; i2 < 4; ++i2) {
-    const int u2 = g + 4 * i2;
-    const bool ok = in && u2 < len;
-    const int a2 = ok ? u2 : 0;
-    const float dv = uc >= a2 ? at(r0 + uc, r0 + a2) : at(r0 + a2, r0 + uc);
-    pp = fmaf(ok ? dv : 0.f, sv[u2], pp);
-  }
-  pp += __shfl_xor(pp, 16, 64);
-  pp += __shfl_xor(pp, 32, 64);
-  const float vp = row_sum16(v * pp);
-  const float wv = tau * pp - 0.5f * tau * tau * vp * v;
-  if (g == 0) sw[u] = wv;
-#pragma unroll
-  for (int i2 = 0; i2 < 4; ++i2) {
-    const int u2 = g + 4 * i2;
-    if (in && u2 <= u) at(r0 + u, r0 + u2) -= fmaf(v, sw[u2], wv * sv[u2]);
-  }
-  // from the right on the rows below: the next bulge
-  const int len2 = len == kBand ? min(kBand, k - (r0 + kBand)) : 0;
-  if (len2 > 0) {
-    float ev[4], y[4];
-#pragma unroll
-    for (int i2 = 0; i2 < 4; ++i2) {
-      const int uu = g + 4 * i2;
-      const float e = at(r0 + kBand + (uu < len2 ? uu : 0), r0 + u);
-      ev[i2] = uu < len2 ? e : 0.f;
-    }
-#pragma unroll
-    for (int i2 = 0; i2 < 4; ++i2) y[i2] = row_sum16(ev[i2] * v);
-#pragma unroll
-    for (int i2 = 0; i2 < 4; ++i2) {
-      const int uu = g + 4 * i2;
-      if (uu < len2) at(r0 + kBand + uu, r0 + u) = ev[i2] - tau * y[i2] * v;
-    }
+  for (int c = 0; c < 4; ++c) {
+    const int t = 4 * g + c;
+    const float wa = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (20 * g + c), __float_as_int(w)));
+    if (s > 0 && u < kBand - 1 && t < len) band[bl + c] = fmaf(-tau * yl, vv[c], L[c]);
+    if (in && t < len && t <= u) band[bd + dk[c]] = D[c] - fmaf(vu, wa, w * vv[c]);
+    if (u < len2) band[bb + c * kChaseLd] = fmaf(-tau * yb, vv[c], B[c]);
   }
 }
 
@@ -833,12 +839,20 @@ __global__ __launch_bounds__(kChaseThreads) void at_chase(const int32_t* __restr
   float* R2 = refl + w * refl_ws + M.r_off;
   float* d = d_ws + w * sv_total + M.sv_off;
   float* e = e_ws + w * sv_total + M.sv_off;
-  __shared__ float band[kMaxK * 2 * kBand];
-  __shared__ float scratch[kChaseWaves][2][kBand];
-  const int tid = threadIdx.x, wave = tid >> 6;
-  for (int i = tid; i < k * 2 * kBand; i += kChaseThreads) {
-    const int c = i / (2 * kBand), t = i % (2 * kBand);
-    band[i] = (t <= kBand && c + t < k) ? A[int64_t(c + t) * k + c] : 0.f;
+  __shared__ float band[kMaxK * (kChaseLd + 1) + kChasePad];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, u = lane & 15, g = lane >> 4;
+  // element (c + t, c) for t <= kBand from the matrix, zero below the band and beyond
+  for (int i = tid; i < k * (kChaseLd + 1) + kChasePad; i += kChaseThreads) band[i] = 0.f;
+  __syncthreads();
+  for (int i = tid; i < k * (kBand + 1); i += kChaseThreads) {
+    const int c = i / (kBand + 1), t = i % (kBand + 1);
+    if (c + t < k) band[c * kChaseLd + c + t] = A[int64_t(c + t) * k + c];
+  }
+  int dk[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int t = 4 * g + c;
+    dk[c] = kChaseLd * min(u, t) + max(u, t);
   }
   __syncthreads();
   const int rounds = k < 3 ? 0 : kLag * (k - 3) + 1;
@@ -849,13 +863,13 @@ __global__ __launch_bounds__(kChaseThreads) void at_chase(const int32_t* __restr
     for (int j = jhi - wv; j >= 0; j -= kChaseWaves) {
       const int st = rho - kLag * j;
       if (st >= chase_steps(k, j)) break;  // and every smaller j (wave-uniform)
-      chase_step(band, scratch[wv][0], scratch[wv][1], R2, k, j, st);
+      chase_step(band, R2, k, j, st, u, g, dk);
     }
     lds_barrier();
   }
   for (int i = tid; i < k; i += kChaseThreads) {
-    d[i] = band[i * 2 * kBand];
-    if (i + 1 < k) e[i] = band[i * 2 * kBand + 1];
+    d[i] = band[i * (kChaseLd + 1)];
+    if (i + 1 < k) e[i] = band[i * (kChaseLd + 1) + 1];
   }
 }
 
@@ -1241,13 +1255,13 @@ __device__ __forceinline__ void back_sweep(float (&x)[NS], const float* sl, int 
 #pragma unroll
   for (int i = 0; i < NS; ++i) d[i] = v[i] * x[i];
 #pragma unroll
-  for (int i = 0; i < NS; ++i) d[i] += dpp_mov<0x128, 0xf>(d[i]);
+  for (int i = 0; i < NS; ++i) d[i] += dpp_all<0x128>(d[i]);
 #pragma unroll
-  for (int i = 0; i < NS; ++i) d[i] += dpp_mov<0x124, 0xf>(d[i]);
+  for (int i = 0; i < NS; ++i) d[i] += dpp_all<0x124>(d[i]);
 #pragma unroll
-  for (int i = 0; i < NS; ++i) d[i] += dpp_mov<0x122, 0xf>(d[i]);
+  for (int i = 0; i < NS; ++i) d[i] += dpp_all<0x122>(d[i]);
 #pragma unroll
-  for (int i = 0; i < NS; ++i) d[i] += dpp_mov<0x121, 0xf>(d[i]);
+  for (int i = 0; i < NS; ++i) d[i] += dpp_all<0x121>(d[i]);
 #pragma unroll
   for (int i = 0; i < NS; ++i) x[i] = fmaf(-t[i] * d[i], v[i], x[i]);
 }
