@@ -442,11 +442,11 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
   __shared__ __align__(16) float U[kMaxK * kVS];
   __shared__ __align__(16) float VB[kMaxK * kBand];
   __shared__ float Tm[kBand][kBand + 1];
-  __shared__ float Gm[kBand][kBand + 1];  // V^T V, then V^T X
-  __shared__ float Sm[kBand][kBand + 1];
-  __shared__ float part[4][kBand * kBand];
-  __shared__ float vbuf[2][kMaxK];  // the current reflector, double-buffered
-  __shared__ float hbuf[2][3];      // its tau, scale, beta
+  __shared__ float Gv[kBand][kBand + 1];  // V^T V
+  __shared__ float Gx[kBand][kBand + 1];  // V^T X
+  __shared__ float Sm[kBand][kBand + 1];  // (V^T X) T, then S
+  __shared__ __align__(16) float vbuf[2][kMaxK];  // the current reflector (double-buffered); Gram partials
+  __shared__ float hbuf[2][3];                    // its tau, scale, beta
   float* ZB = U;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
@@ -458,8 +458,19 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
     const int nref = min(kBand, m - 1);
     const int nb = (m + kBand - 1) / kBand;
     float* A22 = A + int64_t(r0) * k + r0;
-    for (int e = tid; e < m * kBand; e += kBandThreads)
-      U[(e / kBand) * kVS + e % kBand] = A[int64_t(r0 + e / kBand) * k + c + e % kBand];
+    {  // the panel, all of a thread's loads issued together: m * kBand <= kBandThreads * KR
+      float pv[KR];
+#pragma unroll
+      for (int q = 0; q < KR; ++q) {
+        const int e = tid + q * kBandThreads, r = min(e / kBand, m - 1);
+        pv[q] = A[uint32_t((r0 + r) * k + c + e % kBand)];
+      }
+#pragma unroll
+      for (int q = 0; q < KR; ++q) {
+        const int e = tid + q * kBandThreads;
+        if (e < m * kBand) U[(e / kBand) * kVS + e % kBand] = pv[q];
+      }
+    }
     if (tid < kBand * kBand) Tm[tid / kBand][tid % kBand] = 0.f;
     __syncthreads();
     // QR of the panel: wave t holds column t in registers.  Reflector i is formed by wave
@@ -533,40 +544,10 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
         const float x = U[i * kVS + t];
         A[int64_t(r0 + i) * k + c + t] = x;
         v = t < nref ? (i > t ? x : (i == t ? 1.f : 0.f)) : 0.f;
-        U[i * kVS + t] = v;
       }
       VB[vz(i, t)] = v;
     }
-    __syncthreads();
-    // T: T[i][i] = tau_i, T[0:i, i] = -tau_i T[0:i, 0:i] (V^T v_i)[0:i]
-    for (int pr = wave; pr < kBand * kBand; pr += kWaves) {
-      const int a = pr / kBand, b = pr % kBand;
-      if (a < b && b < nref) {
-        float g = 0.f;
-        for (int r = b + lane; r < m; r += 64) g = fmaf(U[r * kVS + a], U[r * kVS + b], g);
-        g = wave_sum(g);
-        if (lane == 0) Gm[a][b] = g;
-      }
-    }
-    __syncthreads();
-    if (wave == 0) {  // lane a holds row a of T; column i needs the finished columns < i
-      float tr[kBand];
-#pragma unroll
-      for (int b = 0; b < kBand; ++b) tr[b] = (lane < kBand && b == lane) ? Tm[lane][lane] : 0.f;
-#pragma unroll
-      for (int i = 1; i < kBand; ++i) {
-        if (i >= nref) break;
-        float g = 0.f;
-#pragma unroll
-        for (int b = 0; b < i; ++b) g = fmaf(tr[b], Gm[b][i], g);
-        tr[i] = lane < i ? -Tm[i][i] * g : tr[i];
-      }
-      if (lane < kBand)
-#pragma unroll
-        for (int b = 0; b < kBand; ++b) Tm[lane][b] = tr[b];
-    }
     __syncthreads();  // U (the panel) is no longer read: it becomes X
-    if (tid < nref * nref) A[int64_t(c + tid / nref) * k + r0 + tid % nref] = Tm[tid / nref][tid % nref];
     // X = A22 V with the matrix instruction D += A B (A 16 x 4, B 4 x 16; lane l gives
     // A[l mod 16][l / 16] and B[l / 16][l mod 16]; D[i][j] is accumulator i mod 4 of lane
     // j + 16 (i / 4)).  Wave w takes the row blocks I = w, w + 16, ...: for each column
@@ -655,56 +636,80 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
       for (int v = 0; v < 4; ++v) ZB[vz(RI + 4 * lg + v, li)] = acc[v];
     }
     __syncthreads();
-    {  // V^T X, four row quarters per entry
-      const int en = tid % (kBand * kBand), qt = tid / (kBand * kBand);
-      const int a = en / kBand, b = en % kBand;
-      const int lq = (m + 3) / 4, l0 = qt * lq, l1 = min(m, l0 + lq);
-      float g = 0.f;
-      for (int l = l0; l < l1; ++l) g = fmaf(VB[vz(l, a)], ZB[vz(l, b)], g);
-      part[qt][en] = g;
+    // V^T V and V^T X: waves 0..3 take the 4-row chunks w, w + 4, ... (A[i][q] = V[4 ch + q][i],
+    // B[q][j] = V or X [4 ch + q][j]), their partial sums go to vbuf and are added in order
+    float* gpart = &vbuf[0][0];  // [4 waves][2][16 x 16]
+    if (wave < 4) {
+      f4 gv = {0.f, 0.f, 0.f, 0.f}, gx = {0.f, 0.f, 0.f, 0.f};
+      for (int ch = wave; ch < nb * 4; ch += 4) {
+        const int r = 4 * ch + lg;
+        const float a = VB[vz(r, li)], x = ZB[vz(r, li)];
+        gv = __builtin_amdgcn_mfma_f32_16x16x4f32(a, a, gv, 0, 0, 0);
+        gx = __builtin_amdgcn_mfma_f32_16x16x4f32(a, x, gx, 0, 0, 0);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        gpart[(wave * 2) * 256 + (4 * lg + v) * kBand + li] = gv[v];
+        gpart[(wave * 2 + 1) * 256 + (4 * lg + v) * kBand + li] = gx[v];
+      }
     }
     __syncthreads();
-    if (tid < kBand * kBand) Gm[tid / kBand][tid % kBand] = part[0][tid] + part[1][tid] + part[2][tid] + part[3][tid];
+    if (tid < kBand * kBand) {
+      float sv = 0.f, sx = 0.f;
+#pragma unroll
+      for (int w4 = 0; w4 < 4; ++w4) {
+        sv += gpart[(w4 * 2) * 256 + tid];
+        sx += gpart[(w4 * 2 + 1) * 256 + tid];
+      }
+      Gv[tid / kBand][tid % kBand] = sv;
+      Gx[tid / kBand][tid % kBand] = sx;
+    }
     __syncthreads();
+    if (wave == 0) {  // T[i][i] = tau_i, T[0:i, i] = -tau_i T[0:i, 0:i] (V^T v_i)[0:i]: lane a holds row a
+      float tr[kBand];
+#pragma unroll
+      for (int b = 0; b < kBand; ++b) tr[b] = (lane < kBand && b == lane) ? Tm[lane][lane] : 0.f;
+#pragma unroll
+      for (int i = 1; i < kBand; ++i) {
+        if (i >= nref) break;
+        float g = 0.f;
+#pragma unroll
+        for (int b = 0; b < i; ++b) g = fmaf(tr[b], Gv[b][i], g);
+        tr[i] = lane < i ? -Tm[i][i] * g : tr[i];
+      }
+      if (lane < kBand)
+#pragma unroll
+        for (int b = 0; b < kBand; ++b) Tm[lane][b] = tr[b];
+    }
+    __syncthreads();
+    if (tid < nref * nref) A[int64_t(c + tid / nref) * k + r0 + tid % nref] = Tm[tid / nref][tid % nref];
     if (tid < kBand * kBand) {  // (V^T X) T
       const int a = tid / kBand, j = tid % kBand;
       float y = 0.f;
-      for (int b = 0; b <= j; ++b) y = fmaf(Gm[a][b], Tm[b][j], y);
-      part[0][tid] = y;
+      for (int b = 0; b <= j; ++b) y = fmaf(Gx[a][b], Tm[b][j], y);
+      Sm[a][j] = y;
     }
     __syncthreads();
+    float sr = 0.f;
     if (tid < kBand * kBand) {  // S = T^T (V^T X) T
       const int i = tid / kBand, j = tid % kBand;
-      float y = 0.f;
-      for (int a = 0; a <= i; ++a) y = fmaf(Tm[a][i], part[0][a * kBand + j], y);
-      Sm[i][j] = y;
+      for (int a = 0; a <= i; ++a) sr = fmaf(Tm[a][i], Sm[a][j], sr);
     }
     __syncthreads();
-    if (tid < m) {  // Z = X T - V S / 2, row tid, in place of X
-      float x[kBand], v[kBand], zrow[kBand];
+    if (tid < kBand * kBand) Sm[tid / kBand][tid % kBand] = -0.5f * sr;
+    __syncthreads();
+    // Z = X T - V S / 2 in place of X, a 16-row block per wave: D = X_blk T + V_blk (-S / 2)
+    for (int I = wave; I < nb; I += kWaves) {
+      const int RI = I * kBand;
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int q4 = 0; q4 < kBand / 4; ++q4) {
-        const f4 xv = vz4(ZB, tid, q4), vv = vz4(VB, tid, q4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[4 * q4 + e] = xv[e];
-          v[4 * q4 + e] = vv[e];
-        }
+      for (int cq = 0; cq < 4; ++cq) {
+        const int q = 4 * cq + lg;
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ZB[vz(RI + li, q)], Tm[q][li], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(VB[vz(RI + li, q)], Sm[q][li], acc, 0, 0, 0);
       }
 #pragma unroll
-      for (int j = 0; j < kBand; ++j) {
-        float z = 0.f;
-#pragma unroll
-        for (int b = 0; b < kBand; ++b) z = fmaf(x[b], Tm[b][j], z);
-        float vs = 0.f;
-#pragma unroll
-        for (int b = 0; b < kBand; ++b) vs = fmaf(v[b], Sm[b][j], vs);
-        zrow[j] = fmaf(-0.5f, vs, z);
-      }
-#pragma unroll
-      for (int q4 = 0; q4 < kBand / 4; ++q4)
-        *reinterpret_cast<f4*>(ZB + tid * kBand + (((q4 ^ (tid >> 1)) & 3) << 2)) =
-            f4{zrow[4 * q4], zrow[4 * q4 + 1], zrow[4 * q4 + 2], zrow[4 * q4 + 3]};
+      for (int v = 0; v < 4; ++v) ZB[vz(RI + 4 * lg + v, li)] = acc[v];
     }
     __syncthreads();
     // A22 -= V Z^T + Z V^T on the stored (lower) tiles, I >= J: the tile is the
