@@ -1051,9 +1051,10 @@ __global__ __launch_bounds__(kSampleThreads) void at_sample(const AtMat* __restr
 // atom's vector -- classical Gram-Schmidt applied twice --; normalise).  Up to kVecSlots
 // atoms are solved side by side, one lane each (the elimination is a sequential
 // recurrence); pivots below 2^-24 ||T|| are raised to that size.
-constexpr int kVecLdsBytes = 2048 * 21;  // slots * k * (5 floats + 1 byte) stays within this
+constexpr int kVecLdsBytes = 2048 * 24;  // slots * k * (5 floats + 1 int) stays within this
 
 __device__ __forceinline__ int vec_slots(int k) { return max(1, min(8, 2048 / k)); }
+constexpr int kVecChunk = 8;  // rows of a recurrence whose loads are issued together
 
 __global__ __launch_bounds__(kVecThreads) void at_vectors(const AtMat* __restrict__ mats,
                                                           const float* __restrict__ d_ws,
@@ -1079,11 +1080,11 @@ __global__ __launch_bounds__(kVecThreads) void at_vectors(const AtMat* __restric
   __shared__ __align__(16) unsigned char pool[kVecLdsBytes];
   const int ns = vec_slots(k);
   float* f0 = reinterpret_cast<float*>(pool);  // 1 / pivot
-  float* f1 = f0 + ns * k;                      // first entry right of the pivot
-  float* f2 = f1 + ns * k;                      // second entry right of the pivot
+  float* f1 = f0 + ns * k;                      // first entry right of the pivot, / pivot
+  float* f2 = f1 + ns * k;                      // second entry right of the pivot, / pivot
   float* fm = f2 + ns * k;                      // multiplier
   float* fy = fm + ns * k;                      // the slot's vector
-  unsigned char* fsw = reinterpret_cast<unsigned char*>(fy + ns * k);  // rows swapped
+  int* fsw = reinterpret_cast<int*>(fy + ns * k);  // rows swapped (0 or 1)
   float tn = 0.f;
   for (int i = tid; i < k; i += kVecThreads) {
     sd[i] = d[i];
@@ -1101,35 +1102,39 @@ __global__ __launch_bounds__(kVecThreads) void at_vectors(const AtMat* __restric
       float* u1 = f1 + s * k;
       float* u2 = f2 + s * k;
       float* ml = fm + s * k;
-      unsigned char* sw = fsw + s * k;
-      float cd = sd[0] - l, c1 = k > 1 ? se[0] : 0.f, c2 = 0.f;
-      for (int t = 0; t + 1 < k; ++t) {
-        const float sub = se[t], nd = sd[t + 1] - l, nsup = t + 2 < k ? se[t + 1] : 0.f;
-        if (fabsf(cd) >= fabsf(sub)) {
-          float piv = cd;
-          if (fabsf(piv) < tiny) piv = piv < 0.f ? -tiny : tiny;
-          const float r = __builtin_amdgcn_rcpf(piv);
-          const float m = sub * r;
-          u0[t] = r;
-          u1[t] = c1;
-          u2[t] = c2;
-          ml[t] = m;
-          sw[t] = 0;
-          cd = nd - m * c1;
-          c1 = nsup - m * c2;
-        } else {
-          const float rs = __builtin_amdgcn_rcpf(sub);
-          const float m = cd * rs;
-          u0[t] = rs;
-          u1[t] = nd;
-          u2[t] = nsup;
-          ml[t] = m;
-          sw[t] = 1;
-          cd = c1 - m * nd;
-          c1 = c2 - m * nsup;
+      int* sw = fsw + s * k;
+      // kVecChunk rows at a time: their loads first, then the recurrence, which carries
+      // only cd and c1 (the second entry right of a pivot is zero unless the rows swapped);
+      // se[k - 1] is zero, so row t's super-diagonal below is se[t + 1] for every t < k - 1
+      float cd = sd[0] - l, c1 = k > 1 ? se[0] : 0.f;
+      auto row = [&](int t, float sub, float dn, float sp) {
+        const bool swap = !(fabsf(cd) >= fabsf(sub));
+        float piv = cd;
+        if (fabsf(piv) < tiny) piv = piv < 0.f ? -tiny : tiny;
+        const float r = __builtin_amdgcn_rcpf(swap ? sub : piv);
+        const float m = (swap ? cd : sub) * r;
+        u0[t] = r;  // the back substitution's row t, scaled by 1 / pivot
+        u1[t] = (swap ? dn : c1) * r;
+        u2[t] = swap ? sp * r : 0.f;
+        ml[t] = m;
+        sw[t] = swap ? 1 : 0;
+        const float ncd = swap ? fmaf(-m, dn, c1) : fmaf(-m, c1, dn);
+        c1 = swap ? -m * sp : sp;
+        cd = ncd;
+      };
+      int t = 0;
+      for (; t + kVecChunk <= k - 1; t += kVecChunk) {
+        float sub[kVecChunk], dn[kVecChunk], sp[kVecChunk];
+#pragma unroll
+        for (int q = 0; q < kVecChunk; ++q) {
+          sub[q] = se[t + q];
+          dn[q] = sd[t + q + 1] - l;
+          sp[q] = se[t + q + 1];
         }
-        c2 = 0.f;
+#pragma unroll
+        for (int q = 0; q < kVecChunk; ++q) row(t + q, sub[q], dn[q], sp[q]);
       }
+      for (; t < k - 1; ++t) row(t, se[t], sd[t + 1] - l, se[t + 1]);
       if (fabsf(cd) < tiny) cd = cd < 0.f ? -tiny : tiny;
       u0[k - 1] = __builtin_amdgcn_rcpf(cd);
       u1[k - 1] = 0.f;
@@ -1149,28 +1154,55 @@ __global__ __launch_bounds__(kVecThreads) void at_vectors(const AtMat* __restric
         const float* u1 = f1 + s * k;
         const float* u2 = f2 + s * k;
         const float* ml = fm + s * k;
-        const unsigned char* sw = fsw + s * k;
+        const int* sw = fsw + s * k;
         float* y = fy + s * k;
+        // forward, kVecChunk rows at a time with their loads first (row t + 1 is read
+        // before it is written, as in the one-row order): (a, b) = (cr, next) or, rows
+        // swapped, (next, cr), and one fma per row
         float cr = y[0];
-        for (int t = 0; t + 1 < k; ++t) {
-          const float nr = y[t + 1];
-          if (sw[t] == 0) {
-            y[t] = cr;
-            cr = nr - ml[t] * cr;
-          } else {
-            y[t] = nr;
-            cr = cr - ml[t] * nr;
+        auto fwd = [&](int t, float nr, float m, int sq) {
+          const float a = sq ? nr : cr, b = sq ? cr : nr;
+          y[t] = a;
+          cr = fmaf(-m, a, b);
+        };
+        int t = 0;
+        for (; t + kVecChunk <= k - 1; t += kVecChunk) {
+          float nr[kVecChunk], mq[kVecChunk];
+          int sq[kVecChunk];
+#pragma unroll
+          for (int q = 0; q < kVecChunk; ++q) {
+            nr[q] = y[t + q + 1];
+            mq[q] = ml[t + q];
+            sq[q] = sw[t + q];
           }
+#pragma unroll
+          for (int q = 0; q < kVecChunk; ++q) fwd(t + q, nr[q], mq[q], sq[q]);
         }
+        for (; t < k - 1; ++t) fwd(t, y[t + 1], ml[t], sw[t]);
         y[k - 1] = cr;
+        // back substitution from the last row: z = y u0 - u1 z1 - u2 z2 (u1, u2 pre-scaled)
         float z1 = 0.f, z2 = 0.f, big = 0.f;
-        for (int t = k - 1; t >= 0; --t) {
-          const float z = (y[t] - u1[t] * z1 - u2[t] * z2) * u0[t];
+        auto bwd = [&](int t, float yv, float a0, float a1, float a2) {
+          const float z = fmaf(-a1, z1, fmaf(-a2, z2, yv * a0));
           y[t] = z;
           z2 = z1;
           z1 = z;
           big = fmaxf(big, fabsf(z));
+        };
+        t = k - 1;
+        for (; t >= kVecChunk - 1; t -= kVecChunk) {
+          float yv[kVecChunk], a0[kVecChunk], a1[kVecChunk], a2[kVecChunk];
+#pragma unroll
+          for (int q = 0; q < kVecChunk; ++q) {
+            yv[q] = y[t - q];
+            a0[q] = u0[t - q];
+            a1[q] = u1[t - q];
+            a2[q] = u2[t - q];
+          }
+#pragma unroll
+          for (int q = 0; q < kVecChunk; ++q) bwd(t - q, yv[q], a0[q], a1[q], a2[q]);
         }
+        for (; t >= 0; --t) bwd(t, y[t], u0[t], u1[t], u2[t]);
         // the scale that keeps the next round from overflowing, applied below by the
         // whole workgroup
         vscale[s] = big > 0.f ? 1.f / big : 0.f;
