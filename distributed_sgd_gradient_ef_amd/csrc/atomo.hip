@@ -366,6 +366,14 @@ __global__ __launch_bounds__(kGramThreads) void at_gram(const GramTile* __restri
 constexpr int kBand = 16;
 constexpr int kVS = kBand + 1;  // LDS row stride of the panel arrays
 constexpr int kBandThreads = 1024;
+#ifndef PSGD_UPD_PRE
+#define PSGD_UPD_PRE 2
+#endif
+#ifndef PSGD_X_PRE
+#define PSGD_X_PRE 2
+#endif
+constexpr int kUpdPre = PSGD_UPD_PRE;  // update tiles in flight per wave
+constexpr int kXPre = PSGD_X_PRE;      // X-pass tiles in flight per wave
 constexpr int kChaseThreads = 1024;
 constexpr int kChaseWaves = kChaseThreads / 64;
 constexpr int kLag = 3;  // rounds between the starts of consecutive sweeps
@@ -385,6 +393,15 @@ __device__ __forceinline__ int band_panels(int k) { return k < kBand + 2 ? 0 : (
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Orders one wave's LDS stores before its later LDS loads, also across lanes (the
+// compiler may otherwise move a lane's load above another lane's store); all lanes of the
+// wave reconverge here.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
@@ -450,6 +467,7 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
   float* ZB = U;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform loop control
   constexpr int kRegs = KR;  // a panel column in registers: row lane + 64 q
   constexpr int kWaves = kBandThreads / 64;
   const bool vec = (k & 3) == 0;
@@ -511,6 +529,8 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
     for (int i = 0; i < nref; ++i) {
       __syncthreads();
       if (wave > i) {
+        // the wave that forms the next reflector is on the critical path: it goes first
+        if (wv == i + 1) __builtin_amdgcn_s_setprio(2);
         const float tau = hbuf[i & 1][0];
         const float* v = vbuf[i & 1];
         float y = 0.f;
@@ -525,7 +545,10 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
           const int r = lane + 64 * q;
           if (r >= i && r < m) col[q] = fmaf(-f, v[r], col[q]);
         }
-        if (wave == i + 1 && i + 1 < nref) form(i + 1);
+        if (wv == i + 1) {
+          if (i + 1 < nref) form(i + 1);
+          __builtin_amdgcn_s_setprio(0);
+        }
       }
     }
     __syncthreads();
@@ -556,12 +579,12 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
     // read from row block I for J < I (along rows), as the transpose of tile (J, I) for
     // J > I (along columns), and entry by entry from the lower triangle for J = I.  Rows
     // and columns at or beyond m read as zero (indices clamped into the matrix); the loads
-    // run four tiles ahead of the instructions.
+    // run kXPre tiles ahead of the instructions.
     for (int I = wave; I < nb; I += kWaves) {
       const int RI = I * kBand, i = RI + li, ic = min(i, m - 1);
       const bool iok = i < m;
       f4 acc = {0.f, 0.f, 0.f, 0.f};
-      float bf[4][4];
+      float bf[kXPre][4];
       auto mma = [&](const float (&a)[4], int J) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -583,15 +606,15 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
           }
         };
 #pragma unroll
-        for (int d = 0; d < 4; ++d)
+        for (int d = 0; d < kXPre; ++d)
           if (d < I) ld(d, bf[d]);
-        for (int J0 = 0; J0 < I; J0 += 4) {
+        for (int J0 = 0; J0 < I; J0 += kXPre) {
 #pragma unroll
-          for (int d = 0; d < 4; ++d) {
+          for (int d = 0; d < kXPre; ++d) {
             const int J = J0 + d;
             if (J < I) {  // wave-uniform
               mma(bf[d], J);
-              if (J + 4 < I) ld(J + 4, bf[d]);
+              if (J + kXPre < I) ld(J + kXPre, bf[d]);
             }
           }
         }
@@ -619,15 +642,15 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
           }
         };
 #pragma unroll
-        for (int d = 0; d < 4; ++d)
+        for (int d = 0; d < kXPre; ++d)
           if (I + 1 + d < nb) ld(I + 1 + d, bf[d]);
-        for (int J0 = I + 1; J0 < nb; J0 += 4) {
+        for (int J0 = I + 1; J0 < nb; J0 += kXPre) {
 #pragma unroll
-          for (int d = 0; d < 4; ++d) {
+          for (int d = 0; d < kXPre; ++d) {
             const int J = J0 + d;
             if (J < nb) {  // wave-uniform
               mma(bf[d], J);
-              if (J + 4 < nb) ld(J + 4, bf[d]);
+              if (J + kXPre < nb) ld(J + kXPre, bf[d]);
             }
           }
         }
@@ -654,49 +677,59 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
       }
     }
     __syncthreads();
-    if (tid < kBand * kBand) {
-      float sv = 0.f, sx = 0.f;
+    // wave 0 alone: the Gram sums, T, P = (V^T X) T and S = T^T P (16 x 16 products on the
+    // matrix instruction), then one barrier for the workgroup
+    if (wv == 0) {
 #pragma unroll
-      for (int w4 = 0; w4 < 4; ++w4) {
-        sv += gpart[(w4 * 2) * 256 + tid];
-        sx += gpart[(w4 * 2 + 1) * 256 + tid];
+      for (int q = 0; q < 4; ++q) {
+        const int e = lane + 64 * q;
+        float sv = 0.f, sx = 0.f;
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) {
+          sv += gpart[(w4 * 2) * 256 + e];
+          sx += gpart[(w4 * 2 + 1) * 256 + e];
+        }
+        Gv[e / kBand][e % kBand] = sv;
+        Gx[e / kBand][e % kBand] = sx;
       }
-      Gv[tid / kBand][tid % kBand] = sv;
-      Gx[tid / kBand][tid % kBand] = sx;
-    }
-    __syncthreads();
-    if (wave == 0) {  // T[i][i] = tau_i, T[0:i, i] = -tau_i T[0:i, 0:i] (V^T v_i)[0:i]: lane a holds row a
-      float tr[kBand];
+      wave_lds_sync();
+      // T[i][i] = tau_i, T[0:i, i] = -tau_i T[0:i, 0:i] (V^T v_i)[0:i]: lane a (mod 16) holds
+      // row a of T and of V^T V; (V^T V)[b][i] is lane i's entry b
+      float gr[kBand], tr[kBand];
+      const int a = lane & 15;
 #pragma unroll
-      for (int b = 0; b < kBand; ++b) tr[b] = (lane < kBand && b == lane) ? Tm[lane][lane] : 0.f;
+      for (int b = 0; b < kBand; ++b) {
+        gr[b] = Gv[a][b];
+        tr[b] = b == a ? Tm[a][a] : 0.f;
+      }
 #pragma unroll
       for (int i = 1; i < kBand; ++i) {
-        if (i >= nref) break;
         float g = 0.f;
 #pragma unroll
-        for (int b = 0; b < i; ++b) g = fmaf(tr[b], Gv[b][i], g);
-        tr[i] = lane < i ? -Tm[i][i] * g : tr[i];
+        for (int b = 0; b < i; ++b)
+          g = fmaf(tr[b], __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gr[b]), i)), g);
+        const float ti = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tr[i]), i));
+        tr[i] = (a < i && i < nref) ? -ti * g : tr[i];
       }
-      if (lane < kBand)
 #pragma unroll
-        for (int b = 0; b < kBand; ++b) Tm[lane][b] = tr[b];
+      for (int b = 0; b < kBand; ++b) Tm[a][b] = tr[b];  // lanes a + 16 g store the same row
+      wave_lds_sync();
+      for (int e = lane; e < nref * nref; e += 64) A[int64_t(c + e / nref) * k + r0 + e % nref] = Tm[e / nref][e % nref];
+      f4 pm = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cq = 0; cq < 4; ++cq)
+        pm = __builtin_amdgcn_mfma_f32_16x16x4f32(Gx[li][4 * cq + lg], Tm[4 * cq + lg][li], pm, 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) Sm[4 * lg + v][li] = pm[v];
+      wave_lds_sync();
+      f4 sm = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cq = 0; cq < 4; ++cq)
+        sm = __builtin_amdgcn_mfma_f32_16x16x4f32(Tm[4 * cq + lg][li], Sm[4 * cq + lg][li], sm, 0, 0, 0);
+      wave_lds_sync();
+#pragma unroll
+      for (int v = 0; v < 4; ++v) Sm[4 * lg + v][li] = -0.5f * sm[v];
     }
-    __syncthreads();
-    if (tid < nref * nref) A[int64_t(c + tid / nref) * k + r0 + tid % nref] = Tm[tid / nref][tid % nref];
-    if (tid < kBand * kBand) {  // (V^T X) T
-      const int a = tid / kBand, j = tid % kBand;
-      float y = 0.f;
-      for (int b = 0; b <= j; ++b) y = fmaf(Gx[a][b], Tm[b][j], y);
-      Sm[a][j] = y;
-    }
-    __syncthreads();
-    float sr = 0.f;
-    if (tid < kBand * kBand) {  // S = T^T (V^T X) T
-      const int i = tid / kBand, j = tid % kBand;
-      for (int a = 0; a <= i; ++a) sr = fmaf(Tm[a][i], Sm[a][j], sr);
-    }
-    __syncthreads();
-    if (tid < kBand * kBand) Sm[tid / kBand][tid % kBand] = -0.5f * sr;
     __syncthreads();
     // Z = X T - V S / 2 in place of X, a 16-row block per wave: D = X_blk T + V_blk (-S / 2)
     for (int I = wave; I < nb; I += kWaves) {
@@ -716,31 +749,58 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
     // accumulator (lane li + 16 lg, register v: row 16 I + 4 lg + v, column 16 J + li),
     // then eight instructions: A[i][q] = -V[16 I + i][4 q + e], B[q][j] = Z[16 J + j][4 q + e],
     // and the same with V and Z exchanged.  A diagonal tile keeps its upper triangle.
+    // Each wave takes the tiles t = w, w + 16, ... (t = I (I + 1) / 2 + J); the tiles' loads
+    // run kUpdPre tiles ahead of the instructions.
     const int nt = nb * (nb + 1) / 2;
-    for (int t = wave; t < nt; t += kWaves) {
-      int I = int((sqrtf(8.f * float(t) + 1.f) - 1.f) * 0.5f);
+    auto tile_of = [&](int t, int& I, int& J) {
+      I = int((sqrtf(8.f * float(t) + 1.f) - 1.f) * 0.5f);
       while (I * (I + 1) / 2 > t) --I;
       while ((I + 1) * (I + 2) / 2 <= t) ++I;
-      const int J = t - I * (I + 1) / 2;
-      const int RI = I * kBand, RJ = J * kBand;
-      const int col = RJ + li, cc = min(col, m - 1);
-      f4 acc;
+      J = t - I * (I + 1) / 2;
+    };
+    auto load_tile = [&](int I, int J, f4& acc) {
+      const int col = J * kBand + li, cc = min(col, m - 1);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int r = RI + 4 * lg + v;
-        const float x = A22[int64_t(min(r, m - 1)) * k + cc];
+        const int r = I * kBand + 4 * lg + v;
+        const float x = A22[uint32_t(min(r, m - 1) * k + cc)];
         acc[v] = (r < m && col < m) ? x : 0.f;
       }
-      const f4 vi = vz4(VB, RI + li, lg), zi = vz4(ZB, RI + li, lg);
-      const f4 vj = vz4(VB, RJ + li, lg), zj = vz4(ZB, RJ + li, lg);
+    };
+    int Iq[kUpdPre], Jq[kUpdPre];
+    f4 cb[kUpdPre];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(-vi[e], zj[e], acc, 0, 0, 0);
+    for (int d = 0; d < kUpdPre; ++d) {
+      const int t = wv + d * kWaves;
+      if (t < nt) {
+        tile_of(t, Iq[d], Jq[d]);
+        load_tile(Iq[d], Jq[d], cb[d]);
+      }
+    }
+    for (int t0 = wv; t0 < nt; t0 += kUpdPre * kWaves) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(-zi[e], vj[e], acc, 0, 0, 0);
+      for (int d = 0; d < kUpdPre; ++d) {
+        const int t = t0 + d * kWaves;
+        if (t < nt) {  // wave-uniform
+          const int I = Iq[d], J = Jq[d], RI = I * kBand, RJ = J * kBand, col = RJ + li;
+          f4 acc = cb[d];
+          const f4 vi = vz4(VB, RI + li, lg), zi = vz4(ZB, RI + li, lg);
+          const f4 vj = vz4(VB, RJ + li, lg), zj = vz4(ZB, RJ + li, lg);
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = RI + 4 * lg + v;
-        if (r < m && col < m && (I != J || 4 * lg + v >= li)) A22[int64_t(r) * k + col] = acc[v];
+          for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(-vi[e], zj[e], acc, 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(-zi[e], vj[e], acc, 0, 0, 0);
+          const int tn = t + kUpdPre * kWaves;
+          if (tn < nt) {
+            tile_of(tn, Iq[d], Jq[d]);
+            load_tile(Iq[d], Jq[d], cb[d]);
+          }
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int r = RI + 4 * lg + v;
+            if (r < m && col < m && (I != J || 4 * lg + v >= li)) A22[uint32_t(r * k + col)] = acc[v];
+          }
+        }
       }
     }
     __syncthreads();
