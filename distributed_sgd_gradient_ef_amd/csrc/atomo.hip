@@ -11,11 +11,12 @@
 // over G.  Launches, each covering every problem of every worker:
 //
 //   at_gram       the Gram matrix, 128 x 128 output tiles of its lower block triangle
-//                 (stored in full, both triangles) with fp32 MFMA, the contraction over
-//                 the long side staged through LDS
+//                 (only the lower triangle is stored) with fp32 MFMA, the contraction
+//                 over the long side staged through LDS
 //   at_band       one workgroup per problem: reduction of the Gram matrix to a band of
 //                 half-bandwidth 16 by panels of 16 columns (Householder QR of the
-//                 panel in LDS, two-sided blocked update of the trailing matrix)
+//                 panel in registers, two-sided blocked update of the trailing matrix's
+//                 lower triangle on fp32 MFMA)
 //   at_chase      one workgroup per problem: the band to tridiagonal form by bulge
 //                 chasing in LDS, the sweeps pipelined three steps apart
 //   at_eig        every eigenvalue of the tridiagonal matrix by bisection on Sturm
@@ -310,10 +311,8 @@ __global__ __launch_bounds__(kGramThreads) void at_gram(const GramTile* __restri
       __syncthreads();
     }
   }
-  // full storage (row-major, leading dimension k): the tile's lower-triangle entries and
-  // their mirror images; a lane's four consecutive accumulators are four consecutive
-  // columns of the mirror row, stored together where rows are 16-byte aligned
-  const bool mvec = (k & 3) == 0;
+  // the tile's lower-triangle entries, row-major with leading dimension k (the upper
+  // triangle is never read: the reduction works on the lower one)
 #pragma unroll
   for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
@@ -324,18 +323,6 @@ __global__ __launch_bounds__(kGramThreads) void at_gram(const GramTile* __restri
         const int a = a0 + wr + 32 * bi + 8 * (v >> 2) + 4 * half + (v & 3);
         if (a < k && b <= a) B[int64_t(a) * k + b] = acc[bi][bj][v];
       }
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int a = a0 + wr + 32 * bi + 8 * g4 + 4 * half;
-        if (mvec && a + 3 < k && b < a) {
-          const f4 m4 = {acc[bi][bj][4 * g4], acc[bi][bj][4 * g4 + 1], acc[bi][bj][4 * g4 + 2], acc[bi][bj][4 * g4 + 3]};
-          *reinterpret_cast<f4*>(B + int64_t(b) * k + a) = m4;
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (a + q < k && b < a + q) B[int64_t(b) * k + a + q] = acc[bi][bj][4 * g4 + q];
-        }
-      }
     }
 }
 
@@ -344,14 +331,13 @@ __global__ __launch_bounds__(kGramThreads) void at_gram(const GramTile* __restri
 //
 // Stage 1 (at_band): to a band of half-bandwidth kBand, by panels of kBand columns.  For
 // the panel of columns [c, c + kBand), the rows below the band (r0 = c + kBand .. k-1)
-// get a Householder QR in LDS (one reflector per column, H_i = I - tau_i v_i v_i^T with
+// get a Householder QR (one reflector per column, H_i = I - tau_i v_i v_i^T with
 // v_i[i] = 1), accumulated as Q = I - V T V^T (T upper triangular); the trailing matrix
 // A22 (rows and columns >= r0) becomes Q^T A22 Q = A22 - V Z^T - Z V^T with
-// W = A22 V T, S = T^T V^T W, Z = W - V S / 2.  The matrix is held in full (both
-// triangles), so the products over A22 read and write it along rows, coalesced.  The
-// panel's R (upper triangle, on the band) and its reflectors (below the band) stay in
-// the matrix, and T goes to the block above the band, the mirror of the panel, which
-// nothing reads afterwards.
+// W = A22 V T, S = T^T V^T W, Z = W - V S / 2.  Only the lower triangle of the matrix is
+// stored and updated: a tile above the diagonal is read as the transpose of its mirror.
+// The panel's R (upper triangle, on the band) and its reflectors (below the band) stay
+// in the matrix, and T goes to the block above the band, which no update touches.
 //
 // Stage 2 (at_chase): band to tridiagonal by bulge chasing in LDS (the lower band, with
 // room for the bulges below it: 2 kBand diagonals).  Sweep j annihilates column j below
