@@ -343,8 +343,8 @@ def test_plan_without_matrices():
 
 
 def test_width_class_129_to_256():
-    """Widest k in 129..256 (the tridiagonalisation's width class that holds the whole
-    matrix in LDS), both orientations and k at the class's upper end, with the separated
+    """Widest k in 129..256 (several band panels, a chase longer than one LDS chunk of the
+    back-transform's smaller cases), both orientations and k = 256, with the separated
     spectra of the parity cases.  The gaps between neighbouring singular values are
     0.15-0.3% of sigma_max here, too close for a vector-by-vector comparison, so sent
     atoms are checked for validity (as in the other wide cases)."""
