@@ -409,15 +409,13 @@ struct Refl {
 };
 // The hardware square root and reciprocal (about 1 ulp each) suffice: the reflector
 // stays orthogonal to rounding, whatever values tau and v take.
+// Branch-free: the sig2 = 0 case is selected, not branched around.
 __device__ __forceinline__ Refl make_refl(float alpha, float sig2) {
-  Refl h{0.f, alpha, 0.f};
-  if (sig2 != 0.f) {
-    const float mu = __builtin_amdgcn_sqrtf(fmaf(alpha, alpha, sig2));
-    h.beta = alpha >= 0.f ? -mu : mu;
-    h.tau = (h.beta - alpha) * __builtin_amdgcn_rcpf(h.beta);
-    h.scale = __builtin_amdgcn_rcpf(alpha - h.beta);
-  }
-  return h;
+  const float mu = __builtin_amdgcn_sqrtf(fmaf(alpha, alpha, sig2));
+  const float beta = alpha >= 0.f ? -mu : mu;
+  const bool nz = sig2 != 0.f;
+  return Refl{nz ? (beta - alpha) * __builtin_amdgcn_rcpf(beta) : 0.f, nz ? beta : alpha,
+              nz ? __builtin_amdgcn_rcpf(alpha - beta) : 0.f};
 }
 
 // LDS index of element (r, c) of an r x kBand matrix stored in rows of kBand floats, its
@@ -797,15 +795,19 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
 // holds the four entries whose other index is t = 4 g + c, c = 0..3: L(t, u) of the
 // bulge columns left of the block, D(u, t) of the diagonal block, B(u, t) of the rows
 // below it.  A product with the reflector is then four in-register terms and a sum over
-// the four 16-lane rows (two lane swaps).  `band` holds element (r, c), r >= c, of the
-// lower band at c * (2 kBand - 1) + r; with the kChasePad zeros after k (2 kBand) entries
-// every load of a step stays in the array without clamping.  The step's loads are all
-// issued first (the blocks it reads and writes are disjoint, and no other step of the
-// round touches them), and what lies outside the matrix or the block is zeroed by
-// selection.  dk[c] = (2 kBand - 1) min(u, t) + max(u, t) places element (r0 + u, r0 + t)
-// of the diagonal block (lower triangle).
-constexpr int kChaseLd = 2 * kBand - 1;
-constexpr int kChasePad = 2 * kBand * kBand;
+// the four 16-lane rows (two lane swaps).  `band` holds element (r, c), c <= r < c + 2 kBand,
+// of the lower band at c kChaseLd + r: column c's 2 kBand diagonals start at
+// c (kChaseLd + 1).  kChaseLd = 2 kBand + 3 leaves four unused words a column; with the
+// 2 kBand - 1 of a packed layout, the lanes of one block access met in the same LDS bank
+// up to four times (the diagonal block) where now at most two do.  With the kChasePad
+// zeros after k columns every load of a step stays in the array without clamping.  The
+// step's loads are all issued first (the blocks it reads and writes are disjoint, and no
+// other step of the round touches them), and what lies outside the matrix or the block
+// is zeroed by selection.  dk[c] = kChaseLd min(u, t) + max(u, t) places element
+// (r0 + u, r0 + t) of the diagonal block (lower triangle).
+constexpr int kChaseLd = 2 * kBand + 3;
+constexpr int kChasePad = kBand * (kChaseLd + 1);
+constexpr int kChaseSink = kMaxK * (kChaseLd + 1) + kChasePad;  // 4 words per lane
 
 // sum of v over the four 16-lane rows (each lane gets the sum for its position in the
 // row): exchange rows 0<->1, 2<->3, then the halves, adding both results of each swap
@@ -816,12 +818,25 @@ __device__ __forceinline__ float rows_sum4(float v) {
   return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
+// a b + c d rounded as two products and a sum, never contracted: the lanes holding (u, t)
+// and (t, u) of a symmetric update then get the same value bit for bit
+__device__ __forceinline__ float sym_dot2(float a, float b, float c, float d) {
+#pragma clang fp contract(off)
+  return a * b + c * d;
+}
+
+// kFull: an interior step (s > 0 and two full blocks of rows from r0 on), where no entry
+// lies outside the matrix and only the lanes of L's column u = kBand - 1 (not part of L)
+// must not store.  Both lanes that hold a pair (u, t), (t, u) of D store the same value
+// (the update is formed symmetrically, without contraction), so D needs no mask either.
+// Stores that a lane must not make go to the lane's own four sink words past the band.
+template <bool kFull>
 __device__ __forceinline__ void chase_step(float* band, float* __restrict__ R2, int k, int j, int s, int u, int g,
-                                           const int (&dk)[4]) {
+                                           const int (&dk)[4], int slot_at, bool tau_lane) {
   const int r0 = j + 1 + s * kBand;
-  const int len = min(kBand, k - r0);
-  const int len2 = len == kBand ? min(kBand, k - r0 - kBand) : 0;
-  const int pc = s == 0 ? j : r0 - kBand;  // the column to clear below row r0
+  const int len = kFull ? kBand : min(kBand, k - r0);
+  const int len2 = kFull ? kBand : len == kBand ? min(kBand, k - r0 - kBand) : 0;
+  const int pc = !kFull && s == 0 ? j : r0 - kBand;  // the column to clear below row r0
   const int bx = pc * kChaseLd + r0;                         // x(t) = (r0 + t, pc)
   const int bl = (pc + 1 + u) * kChaseLd + r0 + 4 * g;       // L(4 g + c, u) at + c
   const int bd = r0 * (kChaseLd + 1);                        // D(u, 4 g + c) at + dk[c]
@@ -835,26 +850,30 @@ __device__ __forceinline__ void chase_step(float* band, float* __restrict__ R2, 
     D[c] = band[bd + dk[c]];
     B[c] = band[bb + c * kChaseLd];
   }
-  const bool in = u < len;
+  __builtin_amdgcn_sched_barrier(0);  // every load goes out before the first wait
+  const bool in = kFull || u < len;
   const float x = in ? xu : 0.f;
   const Refl h = make_refl(x0, row_sum16(u >= 1 ? x * x : 0.f));
   const float vu = in ? (u == 0 ? 1.f : x * h.scale) : 0.f;
-  float* slot = R2 + (int64_t(j) * chase_steps_max(k) + s) * (kBand + 1);
-  if (g == 0) {
-    slot[u] = vu;
-    if (in) band[bx + u] = u == 0 ? h.beta : 0.f;
-  }
-  if (threadIdx.x % 64 == 0) slot[kBand] = h.tau;
-  if (h.tau == 0.f) return;  // H = I (wave-uniform)
+  const int sink = kChaseSink + 4 * (threadIdx.x & 63);
+  // the reflector's slot: v[u] from every lane (the four rows write equal values), tau
+  // from one lane
+  R2[(int64_t(j) * chase_steps_max(k) + s) * (kBand + 1) + slot_at] = tau_lane ? h.tau : vu;
+  band[in ? bx + u : sink] = u == 0 ? h.beta : 0.f;  // the four rows write equal values
+  // tau = 0 (H = I) needs no branch: every update below then leaves its entries as they are
   const float tau = h.tau;
   float vv[4], pl = 0.f, pd = 0.f, pb = 0.f;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int t = 4 * g + c;
-    vv[c] = t < len ? (t == 0 ? 1.f : xa[c] * h.scale) : 0.f;
-    L[c] = (s > 0 && u < kBand - 1 && t < len) ? L[c] : 0.f;  // columns pc + 1 + u < r0
-    D[c] = (in && t < len) ? D[c] : 0.f;
-    B[c] = u < len2 ? B[c] : 0.f;
+    if (kFull) {
+      vv[c] = t == 0 ? 1.f : xa[c] * h.scale;
+    } else {
+      vv[c] = t < len ? (t == 0 ? 1.f : xa[c] * h.scale) : 0.f;
+      L[c] = (s > 0 && u < kBand - 1 && t < len) ? L[c] : 0.f;  // columns pc + 1 + u < r0
+      D[c] = (in && t < len) ? D[c] : 0.f;
+      B[c] = u < len2 ? B[c] : 0.f;
+    }
     pl = fmaf(vv[c], L[c], pl);
     pd = fmaf(D[c], vv[c], pd);
     pb = fmaf(B[c], vv[c], pb);
@@ -867,13 +886,23 @@ __device__ __forceinline__ void chase_step(float* band, float* __restrict__ R2, 
   const float vp = row_sum16(vu * pp);
   const float c2 = 0.5f * tau * tau * vp;
   const float w = fmaf(tau, pp, -c2 * vu);
+  float wa[4];  // the four exchanges go out together, ahead of the stores
+#pragma unroll
+  for (int c = 0; c < 4; ++c) wa[c] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (20 * g + c), __float_as_int(w)));
+  const int bls = (kFull ? u < kBand - 1 : s > 0 && u < kBand - 1) ? bl : sink;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int t = 4 * g + c;
-    const float wa = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (20 * g + c), __float_as_int(w)));
-    if (s > 0 && u < kBand - 1 && t < len) band[bl + c] = fmaf(-tau * yl, vv[c], L[c]);
-    if (in && t < len && t <= u) band[bd + dk[c]] = D[c] - fmaf(vu, wa, w * vv[c]);
-    if (u < len2) band[bb + c * kChaseLd] = fmaf(-tau * yb, vv[c], B[c]);
+    const float dvw = sym_dot2(vu, wa[c], w, vv[c]);
+    if (kFull) {
+      band[bls + c] = fmaf(-tau * yl, vv[c], L[c]);
+      band[bd + dk[c]] = D[c] - dvw;
+      band[bb + c * kChaseLd] = fmaf(-tau * yb, vv[c], B[c]);
+    } else {
+      band[t < len ? bls + c : sink + c] = fmaf(-tau * yl, vv[c], L[c]);
+      band[in && t < len ? bd + dk[c] : sink + c] = D[c] - dvw;
+      band[u < len2 ? bb + c * kChaseLd : sink + c] = fmaf(-tau * yb, vv[c], B[c]);
+    }
   }
 }
 
@@ -890,7 +919,7 @@ __global__ __launch_bounds__(kChaseThreads) void at_chase(const int32_t* __restr
   float* R2 = refl + w * refl_ws + M.r_off;
   float* d = d_ws + w * sv_total + M.sv_off;
   float* e = e_ws + w * sv_total + M.sv_off;
-  __shared__ float band[kMaxK * (kChaseLd + 1) + kChasePad];
+  __shared__ float band[kChaseSink + 4 * 64];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, u = lane & 15, g = lane >> 4;
   // element (c + t, c) for t <= kBand from the matrix, zero below the band and beyond
   for (int i = tid; i < k * (kChaseLd + 1) + kChasePad; i += kChaseThreads) band[i] = 0.f;
@@ -905,6 +934,8 @@ __global__ __launch_bounds__(kChaseThreads) void at_chase(const int32_t* __restr
     const int t = 4 * g + c;
     dk[c] = kChaseLd * min(u, t) + max(u, t);
   }
+  const bool tau_lane = lane == 16;
+  const int slot_at = tau_lane ? kBand : u;
   __syncthreads();
   const int rounds = k < 3 ? 0 : kLag * (k - 3) + 1;
   const int wv = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform: scalar loop control
@@ -914,7 +945,10 @@ __global__ __launch_bounds__(kChaseThreads) void at_chase(const int32_t* __restr
     for (int j = jhi - wv; j >= 0; j -= kChaseWaves) {
       const int st = rho - kLag * j;
       if (st >= chase_steps(k, j)) break;  // and every smaller j (wave-uniform)
-      chase_step(band, R2, k, j, st, u, g, dk);
+      if (st > 0 && k - (j + 1 + st * kBand) >= 2 * kBand)
+        chase_step<true>(band, R2, k, j, st, u, g, dk, slot_at, tau_lane);
+      else
+        chase_step<false>(band, R2, k, j, st, u, g, dk, slot_at, tau_lane);
     }
     lds_barrier();
   }
