@@ -945,10 +945,15 @@ __global__ __launch_bounds__(kChaseThreads) void at_chase(const int32_t* __restr
     for (int j = jhi - wv; j >= 0; j -= kChaseWaves) {
       const int st = rho - kLag * j;
       if (st >= chase_steps(k, j)) break;  // and every smaller j (wave-uniform)
-      if (st > 0 && k - (j + 1 + st * kBand) >= 2 * kBand)
-        chase_step<true>(band, R2, k, j, st, u, g, dk, slot_at, tau_lane);
+      // (j, st) made opaque to the optimiser: otherwise it strength-reduces the step's lane
+      // addresses across rounds into some twenty vector adds and moves per round, which
+      // every wave, also an idle one, then spends on each round
+      int js = j, ss = st;
+      asm volatile("" : "+s"(js), "+s"(ss));
+      if (ss > 0 && k - (js + 1 + ss * kBand) >= 2 * kBand)
+        chase_step<true>(band, R2, k, js, ss, u, g, dk, slot_at, tau_lane);
       else
-        chase_step<false>(band, R2, k, j, st, u, g, dk, slot_at, tau_lane);
+        chase_step<false>(band, R2, k, js, ss, u, g, dk, slot_at, tau_lane);
     }
     lds_barrier();
   }
