@@ -426,6 +426,34 @@ __device__ __forceinline__ f4 vz4(const float* b, int r, int q4) {
   return *reinterpret_cast<const f4*>(b + r * kBand + (((q4 ^ (r >> 1)) & 3) << 2));
 }
 
+// Tile loads that go straight into LDS, holding no registers while in flight: lds_dma4
+// moves 4 bytes per lane to l[lane] (l the same for every lane of the wave).  Written as
+// asm so that the compiler, which cannot tell the slots apart, does not wait for every
+// load in flight before each LDS access; the "memory" clobber keeps it from caching LDS
+// contents across the load, and the explicit waits order the slots' reads.  The update
+// loads kStage tiles of 16 x 16 per wave into LDS slots at a time (the register prefetch
+// holds two at 128 registers); with KR <= 8 (k <= 512) the LDS has the room.
+__device__ __forceinline__ void lds_dma4(const float* g, float* l) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(l)));  // LDS offset
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+}
+constexpr int kStage = 4;
+template <int KR>
+constexpr bool kStaged = KR <= 8;
+// Waits until at most N vector memory operations of the wave are outstanding (loads
+// complete in order; stores issued in between only make the wait longer).
+template <int N>
+__device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+__device__ __forceinline__ void lds_dma_wait(int after) {  // after: tiles loaded since, wave-uniform
+  if (after >= 3) vm_wait<12>();
+  else if (after == 2) vm_wait<8>();
+  else if (after == 1) vm_wait<4>();
+  else vm_wait<0>();
+}
+// Before a slot is loaded again: the reads of what it held have completed.
+__device__ __forceinline__ void lds_slot_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+static_assert(kStage == 4, "lds_dma_wait counts for four slots");
+
 // KR: registers per lane for a panel column (rows lane + 64 q), so k <= 64 KR.
 template <int KR>
 __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restrict__ list,
@@ -440,8 +468,11 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
   // U: the panel in rows of kVS = kBand + 1 floats (rows read lane by lane fall in
   // different banks) and its clean reflectors, then A22 V, then Z (vz layout).  VB: V in
   // the vz layout.  Rows from m to the next multiple of 16 hold zeros.
-  __shared__ __align__(16) float U[kMaxK * kVS];
-  __shared__ __align__(16) float VB[kMaxK * kBand];
+  constexpr int kRows = 64 * KR;  // k <= kRows
+  __shared__ __align__(16) float U[kRows * kVS];
+  __shared__ __align__(16) float VB[kRows * kBand];
+  // the waves' LDS slots for the update's tiles (kStaged only)
+  __shared__ __align__(16) float XS[kStaged<KR> ? kBandThreads / 64 * kStage * 256 : 4];
   __shared__ float Tm[kBand][kBand + 1];
   __shared__ float Gv[kBand][kBand + 1];  // V^T V
   __shared__ float Gx[kBand][kBand + 1];  // V^T X
@@ -751,38 +782,85 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
         acc[v] = (r < m && col < m) ? x : 0.f;
       }
     };
-    int Iq[kUpdPre], Jq[kUpdPre];
-    f4 cb[kUpdPre];
+    if constexpr (kStaged<KR>) {
+      float* stg = XS + wv * (kStage * 256);
+      for (int t0 = wv; t0 < nt; t0 += kStage * kWaves) {
+        lds_slot_fence();
+        int Iq[kStage], Jq[kStage];
+        // slot d: tile t0 + d kWaves; the lane's entry v (row 4 lg + v, column li) at
+        // d 256 + 64 v + lane
 #pragma unroll
-    for (int d = 0; d < kUpdPre; ++d) {
-      const int t = wv + d * kWaves;
-      if (t < nt) {
-        tile_of(t, Iq[d], Jq[d]);
-        load_tile(Iq[d], Jq[d], cb[d]);
-      }
-    }
-    for (int t0 = wv; t0 < nt; t0 += kUpdPre * kWaves) {
+        for (int d = 0; d < kStage; ++d) {
+          const int t = t0 + d * kWaves;
+          if (t < nt) {  // wave-uniform
+            tile_of(t, Iq[d], Jq[d]);
+            const int cc = min(Jq[d] * kBand + li, m - 1);
 #pragma unroll
-      for (int d = 0; d < kUpdPre; ++d) {
-        const int t = t0 + d * kWaves;
-        if (t < nt) {  // wave-uniform
-          const int I = Iq[d], J = Jq[d], RI = I * kBand, RJ = J * kBand, col = RJ + li;
-          f4 acc = cb[d];
-          const f4 vi = vz4(VB, RI + li, lg), zi = vz4(ZB, RI + li, lg);
-          const f4 vj = vz4(VB, RJ + li, lg), zj = vz4(ZB, RJ + li, lg);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(-vi[e], zj[e], acc, 0, 0, 0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(-zi[e], vj[e], acc, 0, 0, 0);
-          const int tn = t + kUpdPre * kWaves;
-          if (tn < nt) {
-            tile_of(tn, Iq[d], Jq[d]);
-            load_tile(Iq[d], Jq[d], cb[d]);
+            for (int v = 0; v < 4; ++v)
+              lds_dma4(A22 + uint32_t(min(Iq[d] * kBand + 4 * lg + v, m - 1) * k + cc), stg + d * 256 + 64 * v);
           }
+        }
+        vm_wait<0>();
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int r = RI + 4 * lg + v;
-            if (r < m && col < m && (I != J || 4 * lg + v >= li)) A22[uint32_t(r * k + col)] = acc[v];
+        for (int d = 0; d < kStage; ++d) {
+          if (t0 + d * kWaves < nt) {  // wave-uniform
+            const int I = Iq[d], J = Jq[d];
+            const float* sl = stg + d * 256;
+            const int RI = I * kBand, RJ = J * kBand, col = RJ + li;
+            f4 acc;
+    #pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const float x = sl[64 * v + lane];
+              acc[v] = (RI + 4 * lg + v < m && col < m) ? x : 0.f;
+            }
+            const f4 vi = vz4(VB, RI + li, lg), zi = vz4(ZB, RI + li, lg);
+            const f4 vj = vz4(VB, RJ + li, lg), zj = vz4(ZB, RJ + li, lg);
+    #pragma unroll
+            for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(-vi[e], zj[e], acc, 0, 0, 0);
+    #pragma unroll
+            for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(-zi[e], vj[e], acc, 0, 0, 0);
+    #pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int r = RI + 4 * lg + v;
+              if (r < m && col < m && (I != J || 4 * lg + v >= li)) A22[uint32_t(r * k + col)] = acc[v];
+            }
+          }
+        }
+      }
+    } else {
+      int Iq[kUpdPre], Jq[kUpdPre];
+      f4 cb[kUpdPre];
+  #pragma unroll
+      for (int d = 0; d < kUpdPre; ++d) {
+        const int t = wv + d * kWaves;
+        if (t < nt) {
+          tile_of(t, Iq[d], Jq[d]);
+          load_tile(Iq[d], Jq[d], cb[d]);
+        }
+      }
+      for (int t0 = wv; t0 < nt; t0 += kUpdPre * kWaves) {
+  #pragma unroll
+        for (int d = 0; d < kUpdPre; ++d) {
+          const int t = t0 + d * kWaves;
+          if (t < nt) {  // wave-uniform
+            const int I = Iq[d], J = Jq[d], RI = I * kBand, RJ = J * kBand, col = RJ + li;
+            f4 acc = cb[d];
+            const f4 vi = vz4(VB, RI + li, lg), zi = vz4(ZB, RI + li, lg);
+            const f4 vj = vz4(VB, RJ + li, lg), zj = vz4(ZB, RJ + li, lg);
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(-vi[e], zj[e], acc, 0, 0, 0);
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(-zi[e], vj[e], acc, 0, 0, 0);
+            const int tn = t + kUpdPre * kWaves;
+            if (tn < nt) {
+              tile_of(tn, Iq[d], Jq[d]);
+              load_tile(Iq[d], Jq[d], cb[d]);
+            }
+  #pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int r = RI + 4 * lg + v;
+              if (r < m && col < m && (I != J || 4 * lg + v >= li)) A22[uint32_t(r * k + col)] = acc[v];
+            }
           }
         }
       }
