@@ -595,15 +595,19 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
     // J > I (along columns), and entry by entry from the lower triangle for J = I.  Rows
     // and columns at or beyond m read as zero (indices clamped into the matrix); the loads
     // run kXPre tiles ahead of the instructions.
-    for (int I = wave; I < nb; I += kWaves) {
+    for (int I = wv; I < nb; I += kWaves) {  // wave-uniform
       const int RI = I * kBand, i = RI + li, ic = min(i, m - 1);
       const bool iok = i < m;
       f4 acc = {0.f, 0.f, 0.f, 0.f};
       float bf[kXPre][4];
+      // entries outside the matrix are zeroed here, where the tile is used, not where it is
+      // loaded: a selection on a loaded value would wait for the load and undo the prefetch
       auto mma = [&](const float (&a)[4], int J) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], VB[vz(J * kBand + 4 * lg + e, li)], acc, 0, 0, 0);
+        for (int e = 0; e < 4; ++e) {
+          const float x = (iok && J * kBand + 4 * lg + e < m) ? a[e] : 0.f;
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x, VB[vz(J * kBand + 4 * lg + e, li)], acc, 0, 0, 0);
+        }
       };
       {  // J < I: columns below RI < m
         const float* rowp = A22 + uint32_t(ic * k + 4 * lg);
@@ -611,13 +615,10 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
           if (vec) {
             const f4 x = *reinterpret_cast<const f4*>(rowp + J * kBand);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) a[e] = iok ? x[e] : 0.f;
+            for (int e = 0; e < 4; ++e) a[e] = x[e];
           } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float x = rowp[J * kBand + e];
-              a[e] = iok ? x : 0.f;
-            }
+            for (int e = 0; e < 4; ++e) a[e] = rowp[J * kBand + e];
           }
         };
 #pragma unroll
@@ -641,8 +642,7 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
           const int cix = RI + 4 * lg + e;
           const bool low = i >= cix;
           const int rr = min(low ? i : cix, m - 1), cc = min(low ? cix : i, m - 1);
-          const float x = A22[uint32_t(rr * k + cc)];
-          a[e] = (iok && cix < m) ? x : 0.f;
+          a[e] = A22[uint32_t(rr * k + cc)];
         }
         mma(a, I);
       }
@@ -650,11 +650,7 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
         const float* colp = A22 + ic;
         auto ld = [&](int J, float (&a)[4]) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = J * kBand + 4 * lg + e;
-            const float x = colp[uint32_t(min(r, m - 1) * k)];
-            a[e] = (iok && r < m) ? x : 0.f;
-          }
+          for (int e = 0; e < 4; ++e) a[e] = colp[uint32_t(min(J * kBand + 4 * lg + e, m - 1) * k)];
         };
 #pragma unroll
         for (int d = 0; d < kXPre; ++d)
