@@ -471,8 +471,12 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
   constexpr int kRows = 64 * KR;  // k <= kRows
   __shared__ __align__(16) float U[kRows * kVS];
   __shared__ __align__(16) float VB[kRows * kBand];
-  // the waves' LDS slots for the update's tiles (kStaged only)
+  // kStaged only: the waves' LDS slots for the update's tiles; before that, in the X
+  // pass, V^T in rows of kVTld floats (a lane's four consecutive entries in one read,
+  // and the rows' starts four banks apart)
   __shared__ __align__(16) float XS[kStaged<KR> ? kBandThreads / 64 * kStage * 256 : 4];
+  constexpr int kVTld = kRows + 4;
+  static_assert(!kStaged<KR> || kBand * kVTld <= kBandThreads / 64 * kStage * 256, "V^T fits the slots");
   __shared__ float Tm[kBand][kBand + 1];
   __shared__ float Gv[kBand][kBand + 1];  // V^T V
   __shared__ float Gx[kBand][kBand + 1];  // V^T X
@@ -584,6 +588,7 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
         v = t < nref ? (i > t ? x : (i == t ? 1.f : 0.f)) : 0.f;
       }
       VB[vz(i, t)] = v;
+      if constexpr (kStaged<KR>) XS[t * kVTld + i] = v;  // V^T for the X pass
     }
     __syncthreads();  // U (the panel) is no longer read: it becomes X
     // X = A22 V with the matrix instruction D += A B (A 16 x 4, B 4 x 16; lane l gives
@@ -603,10 +608,19 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
       // entries outside the matrix are zeroed here, where the tile is used, not where it is
       // loaded: a selection on a loaded value would wait for the load and undo the prefetch
       auto mma = [&](const float (&a)[4], int J) {
+        float b[4];
+        if constexpr (kStaged<KR>) {
+          const f4 x = *reinterpret_cast<const f4*>(XS + li * kVTld + J * kBand + 4 * lg);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) b[e] = x[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) b[e] = VB[vz(J * kBand + 4 * lg + e, li)];
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float x = (iok && J * kBand + 4 * lg + e < m) ? a[e] : 0.f;
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x, VB[vz(J * kBand + 4 * lg + e, li)], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x, b[e], acc, 0, 0, 0);
         }
       };
       {  // J < I: columns below RI < m
