@@ -1110,6 +1110,28 @@ __global__ __launch_bounds__(kEigThreads) void at_eig(const AtMat* __restrict__ 
   const int idx = int(blockIdx.z) * kEigSlots + lane;
   const bool mine = idx < k;
   float a = glo - slack, b = ghi + slack;
+  {
+    // one shared round first: thread t counts the eigenvalues below the probe
+    // a + (t + 1) h0, h0 = (b - a) / (kEigThreads + 1), and every lane takes the probe
+    // interval holding its eigenvalue (the counts do not decrease along the probes; the
+    // first probe with more than idx below it is found by bisection over the probes)
+    __shared__ int cs[kEigThreads];
+    const float h0 = (b - a) * (1.f / float(kEigThreads + 1));
+    cs[tid] = sturm_below(sd, se2, k, a + h0 * float(tid + 1), pivmin);
+    __syncthreads();
+    if (mine) {
+      int lo = 0, hi = kEigThreads;  // the first p with cs[p] > idx lies in [lo, hi]
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (cs[mid] > idx) hi = mid;
+        else lo = mid + 1;
+      }
+      const float na = lo > 0 ? a + h0 * float(lo) : a;
+      const float nb = lo < kEigThreads ? a + h0 * float(lo + 1) : b;
+      a = na;
+      b = nb;
+    }
+  }
   for (int it = 0; it < 96; ++it) {
     const float h = (b - a) * (1.f / float(kEigWaves + 1));
     float xs[kEigWaves];
