@@ -210,18 +210,23 @@ __global__ __launch_bounds__(kGramThreads) void at_gram(const GramTile* __restri
   const int a0 = t.ti * kGramTile, b0 = t.tj * kGramTile;
   __shared__ __align__(16) float sa[kGramKC][kGramTile + 4];
   __shared__ __align__(16) float sb[kGramKC][kGramTile + 4];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wr = (wave >> 1) * 64, wc = (wave & 1) * 64;  // the wave's quadrant
   const int half = lane >> 5, l32 = lane & 31;
   const bool vec = (cols & 3) == 0;  // rows (and the offset, a multiple of 64) 16-byte aligned
+  // in a diagonal tile the quadrant above the diagonal, and in the two on it their upper
+  // right 32 x 32 block, hold no stored entry: their products are skipped (wave-uniform)
+  const bool diag = t.ti == t.tj;
+  const bool live = !diag || wr >= wc, live01 = !diag || wr != wc;
   f16v acc[2][2] = {};
   auto mfma_chunk = [&]() {
+    if (!live) return;
 #pragma unroll
     for (int kk = 0; kk < kGramKC; kk += 2) {
       const float x0 = sa[kk + half][wr + l32], x1 = sa[kk + half][wr + 32 + l32];
       const float y0 = sb[kk + half][wc + l32], y1 = sb[kk + half][wc + 32 + l32];
       acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, y0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, y1, acc[0][1], 0, 0, 0);
+      if (live01) acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, y1, acc[0][1], 0, 0, 0);
       acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, y0, acc[1][0], 0, 0, 0);
       acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, y1, acc[1][1], 0, 0, 0);
     }
