@@ -438,9 +438,16 @@ __device__ __forceinline__ f4 vz4(const float* b, int r, int q4) {
 // contents across the load, and the explicit waits order the slots' reads.  The update
 // loads kStage tiles of 16 x 16 per wave into LDS slots at a time (the register prefetch
 // holds two at 128 registers); with KR <= 8 (k <= 512) the LDS has the room.
+// M0 (the LDS address of the load) is saved and restored inside the asm: the compiler
+// treats M0 as reserved and does not expect an asm statement to change it.
 __device__ __forceinline__ void lds_dma4(const float* g, float* l) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(l)));  // LDS offset
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+  const uint32_t base = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(l)));  // LDS offset
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(base)
+      : "memory");
 }
 constexpr int kStage = 4;
 template <int KR>
