@@ -525,11 +525,16 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
     // QR of the panel: wave t holds column t in registers.  Reflector i is formed by wave
     // i from its column (in the step before, by the wave that updated it last) and put in
     // vbuf; after one barrier the waves t > i apply it, and wave i + 1 forms the next.
+    // Every row of the panel arrays up to kRows is loaded and stored without a branch
+    // (rows at or past m hold zeros): a load under a per-lane condition becomes a branch
+    // that waits for its load before the next one goes out.
     float col[kRegs];
+    {
+      float cu[kRegs];
 #pragma unroll
-    for (int q = 0; q < kRegs; ++q) {
-      const int r = lane + 64 * q;
-      col[q] = r < m ? U[r * kVS + wave] : 0.f;
+      for (int q = 0; q < kRegs; ++q) cu[q] = U[(lane + 64 * q) * kVS + wave];
+#pragma unroll
+      for (int q = 0; q < kRegs; ++q) col[q] = lane + 64 * q < m ? cu[q] : 0.f;
     }
     // wave w forms reflector w from its column: v (rows > w), beta at row w
     auto form = [&](int i) {
@@ -546,8 +551,8 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
 #pragma unroll
       for (int q = 0; q < kRegs; ++q) {
         const int r = lane + 64 * q;
-        const float v = r > i ? col[q] * h.scale : (r == i ? 1.f : 0.f);
-        if (r < m) vbuf[i & 1][r] = v;
+        const float v = r > i ? col[q] * h.scale : (r == i ? 1.f : 0.f);  // 0 at or past m
+        vbuf[i & 1][r] = v;
         if (r > i) col[q] = v;
         if (r == i) col[q] = h.beta;
       }
@@ -559,23 +564,21 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
     if (wave == 0) form(0);
     for (int i = 0; i < nref; ++i) {
       __syncthreads();
-      if (wave > i) {
+      if (wv > i) {  // wave-uniform
         // the wave that forms the next reflector is on the critical path: it goes first
         if (wv == i + 1) __builtin_amdgcn_s_setprio(2);
         const float tau = hbuf[i & 1][0];
         const float* v = vbuf[i & 1];
+        // the whole reflector, all loads at once: it is zero above row i and at or past m
+        float vr[kRegs];
+#pragma unroll
+        for (int q = 0; q < kRegs; ++q) vr[q] = v[lane + 64 * q];
         float y = 0.f;
 #pragma unroll
-        for (int q = 0; q < kRegs; ++q) {
-          const int r = lane + 64 * q;
-          if (r >= i && r < m) y = fmaf(v[r], col[q], y);
-        }
+        for (int q = 0; q < kRegs; ++q) y = fmaf(vr[q], col[q], y);
         const float f = tau * wave_sum(y);
 #pragma unroll
-        for (int q = 0; q < kRegs; ++q) {
-          const int r = lane + 64 * q;
-          if (r >= i && r < m) col[q] = fmaf(-f, v[r], col[q]);
-        }
+        for (int q = 0; q < kRegs; ++q) col[q] = fmaf(-f, vr[q], col[q]);
         if (wv == i + 1) {
           if (i + 1 < nref) form(i + 1);
           __builtin_amdgcn_s_setprio(0);
@@ -586,10 +589,7 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
     // the panel (R on the band, the reflectors below it) back into U and the matrix; U
     // and VB become the unit lower trapezoidal matrix V of the reflectors
 #pragma unroll
-    for (int q = 0; q < kRegs; ++q) {
-      const int r = lane + 64 * q;
-      if (r < m) U[r * kVS + wave] = col[q];
-    }
+    for (int q = 0; q < kRegs; ++q) U[(lane + 64 * q) * kVS + wave] = col[q];
     __syncthreads();
     for (int e = tid; e < nb * kBand * kBand; e += kBandThreads) {
       const int i = e / kBand, t = e % kBand;
