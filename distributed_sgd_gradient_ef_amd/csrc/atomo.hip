@@ -829,19 +829,19 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
             const int I = Iq[d], J = Jq[d];
             const float* sl = stg + d * 256;
             const int RI = I * kBand, RJ = J * kBand, col = RJ + li;
+            // entries at or past m (loaded from clamped, finite addresses) are not zeroed:
+            // an accumulator entry only reaches its own output entry, and those are not
+            // stored (a selection here made the compiler branch around each load)
             f4 acc;
-    #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const float x = sl[64 * v + lane];
-              acc[v] = (RI + 4 * lg + v < m && col < m) ? x : 0.f;
-            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[v] = sl[64 * v + lane];
             const f4 vi = vz4(VB, RI + li, lg), zi = vz4(ZB, RI + li, lg);
             const f4 vj = vz4(VB, RJ + li, lg), zj = vz4(ZB, RJ + li, lg);
-    #pragma unroll
+#pragma unroll
             for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(-vi[e], zj[e], acc, 0, 0, 0);
-    #pragma unroll
+#pragma unroll
             for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(-zi[e], vj[e], acc, 0, 0, 0);
-    #pragma unroll
+#pragma unroll
             for (int v = 0; v < 4; ++v) {
               const int r = RI + 4 * lg + v;
               if (r < m && col < m && (I != J || 4 * lg + v >= li)) A22[uint32_t(r * k + col)] = acc[v];
@@ -852,7 +852,7 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
     } else {
       int Iq[kUpdPre], Jq[kUpdPre];
       f4 cb[kUpdPre];
-  #pragma unroll
+#pragma unroll
       for (int d = 0; d < kUpdPre; ++d) {
         const int t = wv + d * kWaves;
         if (t < nt) {
@@ -861,7 +861,7 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
         }
       }
       for (int t0 = wv; t0 < nt; t0 += kUpdPre * kWaves) {
-  #pragma unroll
+#pragma unroll
         for (int d = 0; d < kUpdPre; ++d) {
           const int t = t0 + d * kWaves;
           if (t < nt) {  // wave-uniform
@@ -869,16 +869,16 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
             f4 acc = cb[d];
             const f4 vi = vz4(VB, RI + li, lg), zi = vz4(ZB, RI + li, lg);
             const f4 vj = vz4(VB, RJ + li, lg), zj = vz4(ZB, RJ + li, lg);
-  #pragma unroll
+#pragma unroll
             for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(-vi[e], zj[e], acc, 0, 0, 0);
-  #pragma unroll
+#pragma unroll
             for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(-zi[e], vj[e], acc, 0, 0, 0);
             const int tn = t + kUpdPre * kWaves;
             if (tn < nt) {
               tile_of(tn, Iq[d], Jq[d]);
               load_tile(Iq[d], Jq[d], cb[d]);
             }
-  #pragma unroll
+#pragma unroll
             for (int v = 0; v < 4; ++v) {
               const int r = RI + 4 * lg + v;
               if (r < m && col < m && (I != J || 4 * lg + v >= li)) A22[uint32_t(r * k + col)] = acc[v];
