@@ -234,63 +234,52 @@ __global__ __launch_bounds__(kGramThreads) void at_gram(const GramTile* __restri
   if (vec) {
     // four consecutive elements along the contiguous direction per thread and step; the
     // next chunk is loaded into registers while the current one is multiplied
+    // With 16-byte aligned rows, L (the row length) and k are multiples of 4 along the
+    // contiguous direction, so a float4 is wholly inside or wholly outside.  The loads go
+    // to clamped addresses without conditions and the entries outside are zeroed when the
+    // chunk is staged, a chunk later: a load under a per-thread condition became a branch
+    // that waited for the previous loads before it went out.
     constexpr int kSteps = kGramTile * kGramKC / 4 / kGramThreads;
     f4 ra[kSteps], rb[kSteps];
     auto fetch = [&](int c0) {
 #pragma unroll
       for (int i = 0; i < kSteps; ++i) {
         const int e = int(threadIdx.x) + i * kGramThreads;
-        f4 va = {0.f, 0.f, 0.f, 0.f}, vb = {0.f, 0.f, 0.f, 0.f};
         if (M.left) {  // G[a][c0 + c .. +3]
-          const int a = e / (kGramKC / 4), c = (e % (kGramKC / 4)) * 4;
-          if (c0 + c + 3 < L) {
-            if (a0 + a < k) va = *reinterpret_cast<const f4*>(g + int64_t(a0 + a) * cols + c0 + c);
-            if (b0 + a < k) vb = *reinterpret_cast<const f4*>(g + int64_t(b0 + a) * cols + c0 + c);
-          } else {
-            for (int q = 0; q < 4; ++q)
-              if (c0 + c + q < L) {
-                if (a0 + a < k) va[q] = g[int64_t(a0 + a) * cols + c0 + c + q];
-                if (b0 + a < k) vb[q] = g[int64_t(b0 + a) * cols + c0 + c + q];
-              }
-          }
+          const int a = e / (kGramKC / 4), c = min(c0 + (e % (kGramKC / 4)) * 4, L - 4);
+          ra[i] = *reinterpret_cast<const f4*>(g + int64_t(min(a0 + a, k - 1)) * cols + c);
+          rb[i] = *reinterpret_cast<const f4*>(g + int64_t(min(b0 + a, k - 1)) * cols + c);
         } else {       // G[c0 + c][a0 + a .. +3]
           const int c = e / (kGramTile / 4), a = (e % (kGramTile / 4)) * 4;
-          if (c0 + c < L) {
-            const float* row = g + int64_t(c0 + c) * cols;
-            if (a0 + a + 3 < k) va = *reinterpret_cast<const f4*>(row + a0 + a);
-            else
-              for (int q = 0; q < 4; ++q)
-                if (a0 + a + q < k) va[q] = row[a0 + a + q];
-            if (b0 + a + 3 < k) vb = *reinterpret_cast<const f4*>(row + b0 + a);
-            else
-              for (int q = 0; q < 4; ++q)
-                if (b0 + a + q < k) vb[q] = row[b0 + a + q];
-          }
+          const float* row = g + int64_t(min(c0 + c, L - 1)) * cols;
+          ra[i] = *reinterpret_cast<const f4*>(row + min(a0 + a, k - 4));
+          rb[i] = *reinterpret_cast<const f4*>(row + min(b0 + a, k - 4));
         }
-        ra[i] = va;
-        rb[i] = vb;
       }
     };
-    auto stage = [&]() {
+    auto stage = [&](int c0) {
 #pragma unroll
       for (int i = 0; i < kSteps; ++i) {
         const int e = int(threadIdx.x) + i * kGramThreads;
         if (M.left) {
           const int a = e / (kGramKC / 4), c = (e % (kGramKC / 4)) * 4;
+          const bool cin = c0 + c < L, ain = cin && a0 + a < k, bin = cin && b0 + a < k;
           for (int q = 0; q < 4; ++q) {
-            sa[c + q][a] = ra[i][q];
-            sb[c + q][a] = rb[i][q];
+            sa[c + q][a] = ain ? ra[i][q] : 0.f;
+            sb[c + q][a] = bin ? rb[i][q] : 0.f;
           }
         } else {
           const int c = e / (kGramTile / 4), a = (e % (kGramTile / 4)) * 4;
-          *reinterpret_cast<f4*>(&sa[c][a]) = ra[i];
-          *reinterpret_cast<f4*>(&sb[c][a]) = rb[i];
+          const bool cin = c0 + c < L;
+          const f4 z = {0.f, 0.f, 0.f, 0.f};
+          *reinterpret_cast<f4*>(&sa[c][a]) = cin && a0 + a < k ? ra[i] : z;
+          *reinterpret_cast<f4*>(&sb[c][a]) = cin && b0 + a < k ? rb[i] : z;
         }
       }
     };
     fetch(0);
     for (int c0 = 0; c0 < L; c0 += kGramKC) {
-      stage();
+      stage(c0);
       __syncthreads();
       if (c0 + kGramKC < L) fetch(c0 + kGramKC);
       mfma_chunk();
