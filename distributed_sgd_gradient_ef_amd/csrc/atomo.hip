@@ -438,22 +438,17 @@ __device__ __forceinline__ void lds_dma4(const float* g, float* l) {
       : "v"(g), "s"(base)
       : "memory");
 }
-constexpr int kStage = 4;
+#ifndef PSGD_BAND_STAGE
+#define PSGD_BAND_STAGE 4
+#endif
+constexpr int kStage = PSGD_BAND_STAGE;
 template <int KR>
 constexpr bool kStaged = KR <= 8;
-// Waits until at most N vector memory operations of the wave are outstanding (loads
-// complete in order; stores issued in between only make the wait longer).
+// Waits until at most N vector memory operations of the wave are outstanding.
 template <int N>
 __device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
-__device__ __forceinline__ void lds_dma_wait(int after) {  // after: tiles loaded since, wave-uniform
-  if (after >= 3) vm_wait<12>();
-  else if (after == 2) vm_wait<8>();
-  else if (after == 1) vm_wait<4>();
-  else vm_wait<0>();
-}
 // Before a slot is loaded again: the reads of what it held have completed.
 __device__ __forceinline__ void lds_slot_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-static_assert(kStage == 4, "lds_dma_wait counts for four slots");
 
 // KR: registers per lane for a panel column (rows lane + 64 q), so k <= 64 KR.
 template <int KR>
