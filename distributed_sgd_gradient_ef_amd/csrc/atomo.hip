@@ -1734,7 +1734,7 @@ __global__ __launch_bounds__(kFactorThreads) void at_factor(const FactorTile* __
       const int c = t.begin + tid;
       if (c < t.end) {
         float acc[kFactorGroup] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
+#pragma unroll 16  // sixteen rows' loads in flight per thread (8: 145 us, 32: 146 us, 16: 131 us)
         for (int r = 0; r < n; ++r) {
           const float gv = g[int64_t(r) * m + c];
 #pragma unroll
