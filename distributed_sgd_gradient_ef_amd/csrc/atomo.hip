@@ -21,7 +21,8 @@
 //                 chasing in LDS, the sweeps pipelined three steps apart
 //   at_eig        every eigenvalue of the tridiagonal matrix by bisection on Sturm
 //                 counts: 64 per workgroup (one per lane; a large matrix spans several
-//                 compute units), four probe points per round (one per wave);
+//                 compute units), a first round of 256 probes shared by the workgroup,
+//                 then four probe points per round (one per wave);
 //                 sigma_i = sqrt(max(eigenvalue, 0))
 //   at_sample     the closed-form probabilities (the largest atoms saturate first),
 //                 the Bernoulli decisions x_i < p_i, and the list of sent atoms
