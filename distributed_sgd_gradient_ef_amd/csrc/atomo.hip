@@ -1238,9 +1238,10 @@ __global__ __launch_bounds__(kSampleThreads) void at_sample(const AtMat* __restr
 
 // ------------------------------------------------------------------ at_vectors
 // Inverse iteration for the eigenvectors of the tridiagonal (d, e) at the sent atoms'
-// eigenvalues: Gaussian elimination with partial pivoting of T - lam I, then three
+// eigenvalues: Gaussian elimination with partial pivoting of T - lam I, then two or three
 // rounds of (solve; orthogonalise each vector, in atom order, against every earlier
-// atom's vector -- classical Gram-Schmidt applied twice --; normalise).  Up to kVecSlots
+// atom's vector -- classical Gram-Schmidt applied twice --; normalise); the third only
+// where the second solve left a residual bound above 2^-20 ||T||.  Up to kVecSlots
 // atoms are solved side by side, one lane each (the elimination is a sequential
 // recurrence); pivots below 2^-24 ||T|| are raised to that size.
 constexpr int kVecLdsBytes = 2048 * 24;  // slots * k * (5 floats + 1 int) stays within this
@@ -1269,6 +1270,7 @@ __global__ __launch_bounds__(kVecThreads) void at_vectors(const AtMat* __restric
   __shared__ float sd[kMaxK], se[kMaxK], dots[kMaxK];
   __shared__ float red[kWaves];
   __shared__ float vscale[8];
+  __shared__ int vconv[8];
   __shared__ __align__(16) unsigned char pool[kVecLdsBytes];
   const int ns = vec_slots(k);
   float* f0 = reinterpret_cast<float*>(pool);  // 1 / pivot
@@ -1396,8 +1398,11 @@ __global__ __launch_bounds__(kVecThreads) void at_vectors(const AtMat* __restric
         }
         for (; t >= 0; --t) bwd(t, y[t], u0[t], u1[t], u2[t]);
         // the scale that keeps the next round from overflowing, applied below by the
-        // whole workgroup
+        // whole workgroup.  From the second round on the solve's input has unit norm, so
+        // its residual is at most 1 / big: at most 16 tiny (about 2^-20 ||T||) counts as
+        // converged
         vscale[s] = big > 0.f ? 1.f / big : 0.f;
+        vconv[s] = it > 0 && big * tiny >= 0x1p-4f;
       }
       __syncthreads();
       for (int e2 = tid; e2 < ng * k; e2 += kVecThreads) fy[e2] *= vscale[e2 / k];
@@ -1433,6 +1438,11 @@ __global__ __launch_bounds__(kVecThreads) void at_vectors(const AtMat* __restric
         }
         __syncthreads();
       }
+      // the third round only where an atom of the group has not converged (the same
+      // decision in every thread)
+      bool done = it == 1;
+      for (int s = 0; s < ng; ++s) done = done && vconv[s];
+      if (done) break;
     }
   }
 }
