@@ -1463,7 +1463,7 @@ __global__ __launch_bounds__(kVecThreads) void at_vectors(const AtMat* __restric
 //
 // at_backband applies Q1 (stage 1) panel by panel from the last: y[r0:] -= V (T (V^T
 // y[r0:])), with V (unit diagonal, zero above it) and T staged in LDS from where at_band
-// left them, the next panel loaded while the current one is applied, and writes x.
+// left them, the next panels loaded while the current one is applied, and writes x.
 constexpr int kBackWaves = kBackThreads / 64;
 constexpr int kBackPre = 34;                              // prefetch registers per thread
 constexpr int kBackChunkFl = kBackPre * kBackThreads;     // floats one load brings
@@ -1616,33 +1616,78 @@ __global__ __launch_bounds__(kBackThreads) void at_backband(const AtMat* __restr
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int np = band_panels(k);
   const int64_t stride = int64_t(M.rows) + M.cols;
-  float pre[kBackPre];
   // panel p: rows r < m of V, then the kBand rows of T; thread tid always takes column
   // tid mod 16 (kBackThreads is a multiple of 16), rows tid / 16 + q kBackThreads / 16.
   // The loads are unconditional, from an index inside the matrix; the masks (V's unit
   // diagonal and zeros above it, T's upper triangle) are applied when the panel is
-  // stored, so no mask stays live while the loads are in flight.
+  // stored, so no mask stays live while the loads are in flight.  With k <= 512 a panel
+  // takes 16 registers per thread and two panels are in flight: the loads of panel p - 2
+  // go out while panel p is applied (a third in flight measured slower).
   const int ci = tid & 15, rt = tid >> 4;
   constexpr int kRowStep = kBackThreads / 16;
-  auto load = [&](int p) {
+  auto load = [&](auto& pre, int p) {
+    constexpr int QN = sizeof(pre) / sizeof(float);
     const int c = p * kBand, r0 = c + kBand, m = k - r0;
 #pragma unroll
-    for (int q = 0; q < kBackPre; ++q) {
+    for (int q = 0; q < QN; ++q) {
       const int r = rt + q * kRowStep, a = r - m;
       const int off = r < m ? (r0 + r) * k + c + ci : (a < kBand ? (c + a) * k + r0 + ci : 0);
       pre[q] = A[off];
     }
   };
   // V rows at stride kBackVS, T after them
-  auto store = [&](int p) {
+  auto store = [&](const auto& pre, int p) {
+    constexpr int QN = sizeof(pre) / sizeof(float);
     const int m = k - (p * kBand + kBand), nref = min(kBand, m - 1);
 #pragma unroll
-    for (int q = 0; q < kBackPre; ++q) {
+    for (int q = 0; q < QN; ++q) {
       const int r = rt + q * kRowStep, a = r - m;
       const float x = pre[q];
       const float v = r < m ? (ci < nref && r > ci ? x : (ci < nref && r == ci ? 1.f : 0.f))
                             : (a <= ci && ci < nref ? x : 0.f);
       if (a < kBand) stage[r * kBackVS + ci] = v;
+    }
+  };
+  // y[r0:] -= V (T (V^T y[r0:])) for the staged panel p
+  auto apply = [&](float* y, int p) {
+    const int r0 = p * kBand + kBand, m = k - r0;
+    const f4* V4 = reinterpret_cast<const f4*>(stage);
+    const f4* T4 = reinterpret_cast<const f4*>(stage + m * kBackVS);
+    float z[kBand];
+#pragma unroll
+    for (int i = 0; i < kBand; ++i) z[i] = 0.f;
+    for (int r = lane; r < m; r += 64) {
+      const float yr = y[r0 + r];
+#pragma unroll
+      for (int q4 = 0; q4 < kBand / 4; ++q4) {
+        const f4 v = V4[r * (kBackVS / 4) + q4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) z[4 * q4 + e2] = fmaf(v[e2], yr, z[4 * q4 + e2]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kBand; ++i) z[i] = wave_sum(z[i]);
+    float t[kBand];
+#pragma unroll
+    for (int a = 0; a < kBand; ++a) {
+      float acc = 0.f;
+#pragma unroll
+      for (int q4 = a / 4; q4 < kBand / 4; ++q4) {
+        const f4 tv = T4[a * (kBackVS / 4) + q4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) acc = fmaf(tv[e2], z[4 * q4 + e2], acc);
+      }
+      t[a] = acc;
+    }
+    for (int r = lane; r < m; r += 64) {
+      float acc = 0.f;
+#pragma unroll
+      for (int q4 = 0; q4 < kBand / 4; ++q4) {
+        const f4 v = V4[r * (kBackVS / 4) + q4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) acc = fmaf(v[e2], t[4 * q4 + e2], acc);
+      }
+      y[r0 + r] -= acc;
     }
   };
   for (int j0 = 0; j0 < cnt; j0 += kBackWaves) {
@@ -1651,52 +1696,34 @@ __global__ __launch_bounds__(kBackThreads) void at_backband(const AtMat* __restr
     float* y = ys[wave];
     if (mine)
       for (int i = lane; i < k; i += 64) y[i] = y_all[int64_t(j) * k + i];
-    if (np > 0) load(np - 1);
-    for (int p = np - 1; p >= 0; --p) {
-      const int r0 = p * kBand + kBand, m = k - r0;
-      __syncthreads();
-      store(p);
-      __syncthreads();
-      if (p > 0) load(p - 1);
-      if (mine) {
-        const f4* V4 = reinterpret_cast<const f4*>(stage);
-        const f4* T4 = reinterpret_cast<const f4*>(stage + m * kBackVS);
-        float z[kBand];
-#pragma unroll
-        for (int i = 0; i < kBand; ++i) z[i] = 0.f;
-        for (int r = lane; r < m; r += 64) {
-          const float yr = y[r0 + r];
-#pragma unroll
-          for (int q4 = 0; q4 < kBand / 4; ++q4) {
-            const f4 v = V4[r * (kBackVS / 4) + q4];
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) z[4 * q4 + e2] = fmaf(v[e2], yr, z[4 * q4 + e2]);
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < kBand; ++i) z[i] = wave_sum(z[i]);
-        float t[kBand];
-#pragma unroll
-        for (int a = 0; a < kBand; ++a) {
-          float acc = 0.f;
-#pragma unroll
-          for (int q4 = a / 4; q4 < kBand / 4; ++q4) {
-            const f4 tv = T4[a * (kBackVS / 4) + q4];
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) acc = fmaf(tv[e2], z[4 * q4 + e2], acc);
-          }
-          t[a] = acc;
-        }
-        for (int r = lane; r < m; r += 64) {
-          float acc = 0.f;
-#pragma unroll
-          for (int q4 = 0; q4 < kBand / 4; ++q4) {
-            const f4 v = V4[r * (kBackVS / 4) + q4];
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) acc = fmaf(v[e2], t[4 * q4 + e2], acc);
-          }
-          y[r0 + r] -= acc;
-        }
+    if (k <= 64 * 8) {  // uniform
+      constexpr int QP = 64 * 8 / kRowStep;  // registers of one k <= 512 panel
+      static_assert(2 * QP <= kBackPre, "two k <= 512 panels fit the prefetch registers");
+      float pa[QP], pb[QP];
+      if (np > 0) load(pa, np - 1);
+      if (np > 1) load(pb, np - 2);
+      for (int p = np - 1; p >= 0; p -= 2) {
+        __syncthreads();
+        store(pa, p);
+        __syncthreads();
+        if (p >= 2) load(pa, p - 2);
+        if (mine) apply(y, p);
+        if (p == 0) break;
+        __syncthreads();
+        store(pb, p - 1);
+        __syncthreads();
+        if (p >= 3) load(pb, p - 3);
+        if (mine) apply(y, p - 1);
+      }
+    } else {
+      float pre[kBackPre];
+      if (np > 0) load(pre, np - 1);
+      for (int p = np - 1; p >= 0; --p) {
+        __syncthreads();
+        store(pre, p);
+        __syncthreads();
+        if (p > 0) load(pre, p - 1);
+        if (mine) apply(y, p);
       }
     }
     if (mine) {
