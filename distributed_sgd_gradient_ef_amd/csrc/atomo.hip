@@ -11,8 +11,9 @@
 // over G.  Launches, each covering every problem of every worker:
 //
 //   at_gram       the Gram matrix, 128 x 128 output tiles of its lower block triangle
-//                 (only the lower triangle is stored) with fp32 MFMA, the contraction
-//                 over the long side staged through LDS
+//                 (only the lower triangle is stored) on bf16 MFMA, each fp32 entry split
+//                 exactly into three bf16 parts, the contraction over the long side
+//                 staged through LDS
 //   at_band       one workgroup per problem: reduction of the Gram matrix to a band of
 //                 half-bandwidth 16 by panels of 16 columns (Householder QR of the
 //                 panel in registers, two-sided blocked update of the trailing matrix's
@@ -189,13 +190,59 @@ __device__ __forceinline__ float block_max(float v, float* red) { return -block_
 
 // ------------------------------------------------------------------ at_gram
 // One 128 x 128 tile of the lower block triangle per workgroup of four waves; each wave
-// computes a 64 x 64 quadrant as 2 x 2 blocks of the fp32 matrix instruction
-// v_mfma_f32_32x32x2_f32 (D += A B with A 32 x 2, B 2 x 32).  Its operands: lane l holds
-// A[l mod 32][l / 32] and B[l / 32][l mod 32]; result D[i][j] is accumulator
-// (i mod 4) + 4 (i / 8) of lane j + 32 ((i / 4) mod 2).  The long side is staged through
-// LDS in chunks of kGramKC, read as float4 where a matrix's rows are 16-byte aligned.
+// computes a 64 x 64 quadrant as 2 x 2 blocks of the bf16 matrix instruction
+// v_mfma_f32_32x32x16_bf16 (D += A B with A 32 x 16, B 16 x 32, fp32 accumulation).
+// Lane l holds row l mod 32 of A and column l mod 32 of B, with eight contraction slots
+// chosen by l / 32; A and B are filled from the same contraction index in each slot, so
+// the sum covers every index once whatever order the instruction gives the slots.  The
+// result D[i][j] is accumulator (i mod 4) + 4 (i / 8) of lane j + 32 ((i / 4) mod 2).
+//
+// fp32 entries on bf16 matrix cores: every entry is split exactly into three bf16 parts,
+// x = h + m + l.  h is x with the low 16 bits of its encoding cleared (sign, exponent
+// and the top 8 significant bits), m the same of x - h, and l = x - h - m, which has at
+// most 8 significant bits left and so is a bf16 too; both subtractions are exact.  With
+// |m| < 2^-7 |x| and |l| < 2^-14 |x|, the six products hh, hm, mh, hl, lh, mm carry x y
+// up to the three left out, ml, lm and ll, together below (2^-20 + 2^-28) |x y| and of
+// either sign: smaller than the fp32 accumulation's own rounding over the long side.
+// (The same splitting of fp32 into bf16 parts is the bf16x6 scheme of Henry, Tang and
+// Heinecke, "Leveraging the bfloat16 artificial intelligence datatype for higher-precision
+// computations", ARITH 2019, there with rounded rather than truncated parts.)  The six
+// products take 6 / 16 of the fp32 instruction's matrix-core time.
+//
+// The long side is staged through LDS in chunks of kGramKC: thread t takes short index
+// a = t mod 128 and eight consecutive long indices, loads them into registers a chunk
+// ahead (to clamped addresses, without conditions), and when staging zeroes the entries
+// outside the matrix, splits them, and writes each part as one 16-byte row piece; a
+// staged row of one part is kGramKC bf16, so a wave's operand read of 64 x 16 bytes is
+// one contiguous kilobyte.
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f16v __attribute__((ext_vector_type(16)));
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+constexpr int kGramRowW = kGramKC / 2;                      // words per staged row of one part
+constexpr int kGramGroups = kGramKC / 8 * kGramTile / kGramThreads;  // 8-index groups per thread
+static_assert(kGramKC % 16 == 0 && kGramGroups >= 1, "whole 16-deep instruction steps per chunk");
+
+// the exact three-part split of eight entries, packed two bf16 a word (even index low)
+__device__ __forceinline__ void gram_split(const float (&x)[8], u4& h, u4& m, u4& l) {
+  uint32_t hb[8], mb[8], lb[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t uh = __float_as_uint(x[e]) & 0xffff0000u;
+    const float r = x[e] - __uint_as_float(uh);
+    const uint32_t um = __float_as_uint(r) & 0xffff0000u;
+    hb[e] = uh;
+    mb[e] = um;
+    lb[e] = __float_as_uint(r - __uint_as_float(um));
+  }
+  // the high halves of two words, the first one low (v_perm_b32 byte select)
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    h[q] = __builtin_amdgcn_perm(hb[2 * q + 1], hb[2 * q], 0x07060302u);
+    m[q] = __builtin_amdgcn_perm(mb[2 * q + 1], mb[2 * q], 0x07060302u);
+    l[q] = __builtin_amdgcn_perm(lb[2 * q + 1], lb[2 * q], 0x07060302u);
+  }
+}
 
 __global__ __launch_bounds__(kGramThreads) void at_gram(const GramTile* __restrict__ tiles,
                                                         const AtMat* __restrict__ mats,
@@ -209,103 +256,154 @@ __global__ __launch_bounds__(kGramThreads) void at_gram(const GramTile* __restri
   const int k = M.k, cols = M.cols;
   const int L = M.left ? M.cols : M.rows;  // contraction length
   const int a0 = t.ti * kGramTile, b0 = t.tj * kGramTile;
-  __shared__ __align__(16) float sa[kGramKC][kGramTile + 4];
-  __shared__ __align__(16) float sb[kGramKC][kGramTile + 4];
+  // [operand][part][short index][words]: operand 0 the tile's rows a0.., 1 its columns b0..
+  // A row's 16-byte pieces are swapped in pairs where bits 2 and 3 of the short index
+  // differ, so that the lanes of one LDS pass (rows r .. r + 7 of 32 banks, or r .. r + 15
+  // of 64, one piece each) meet every bank once; reads and writes of both operands place
+  // the pieces the same way.
+  __shared__ __align__(16) uint32_t sg[2][3][kGramTile][kGramRowW];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wr = (wave >> 1) * 64, wc = (wave & 1) * 64;  // the wave's quadrant
   const int half = lane >> 5, l32 = lane & 31;
-  const bool vec = (cols & 3) == 0;  // rows (and the offset, a multiple of 64) 16-byte aligned
-  // in a diagonal tile the quadrant above the diagonal, and in the two on it their upper
-  // right 32 x 32 block, hold no stored entry: their products are skipped (wave-uniform)
-  const bool diag = t.ti == t.tj;
-  const bool live = !diag || wr >= wc, live01 = !diag || wr != wc;
+  // rows (and the offset, a multiple of 64) 16-byte aligned: L and k are then multiples
+  // of 4 along the contiguous direction, so a float4 is wholly inside or wholly outside
+  const bool vec = M.left && (cols & 3) == 0;
+  // in a diagonal tile the quadrant above the diagonal holds no stored entry: its wave
+  // skips the products (the upper right blocks of the two quadrants on the diagonal are
+  // computed: the wave below them, with four live blocks, sets the pace at each barrier)
+  const bool live = t.ti != t.tj || wr >= wc;
   f16v acc[2][2] = {};
-  auto mfma_chunk = [&]() {
-    if (!live) return;
+  const int rsw = ((lane >> 2) ^ (lane >> 3)) & 1;  // the piece swap of rows wr + 32 bi + l32
+  // in a diagonal tile both operands are the same rows: only operand 0 is loaded and staged
+  auto mfma_chunk = [&](auto diag_c) {
+    constexpr int kOpB = decltype(diag_c)::value ? 0 : 1;
 #pragma unroll
-    for (int kk = 0; kk < kGramKC; kk += 2) {
-      const float x0 = sa[kk + half][wr + l32], x1 = sa[kk + half][wr + 32 + l32];
-      const float y0 = sb[kk + half][wc + l32], y1 = sb[kk + half][wc + 32 + l32];
-      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, y0, acc[0][0], 0, 0, 0);
-      if (live01) acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, y1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, y0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, y1, acc[1][1], 0, 0, 0);
+    for (int ks = 0; ks < kGramKC / 16; ++ks) {
+      bf8 x[2][3], y[2][3];
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi) {
+          x[bi][p] = *reinterpret_cast<const bf8*>(&sg[0][p][wr + 32 * bi + l32][4 * ((2 * ks + half) ^ rsw)]);
+          y[bi][p] = *reinterpret_cast<const bf8*>(&sg[kOpB][p][wc + 32 * bi + l32][4 * ((2 * ks + half) ^ rsw)]);
+        }
+      constexpr int kPa[6] = {2, 0, 1, 1, 0, 0}, kPb[6] = {0, 2, 1, 0, 1, 0};  // smallest first
+#pragma unroll
+      for (int q = 0; q < 6; ++q) {
+        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[0][kPa[q]], y[0][kPb[q]], acc[0][0], 0, 0, 0);
+        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[0][kPa[q]], y[1][kPb[q]], acc[0][1], 0, 0, 0);
+        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[1][kPa[q]], y[0][kPb[q]], acc[1][0], 0, 0, 0);
+        acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[1][kPa[q]], y[1][kPb[q]], acc[1][1], 0, 0, 0);
+      }
     }
   };
-  if (vec) {
-    // four consecutive elements along the contiguous direction per thread and step; the
-    // next chunk is loaded into registers while the current one is multiplied
-    // With 16-byte aligned rows, L (the row length) and k are multiples of 4 along the
-    // contiguous direction, so a float4 is wholly inside or wholly outside.  The loads go
-    // to clamped addresses without conditions and the entries outside are zeroed when the
-    // chunk is staged, a chunk later: a load under a per-thread condition became a branch
-    // that waited for the previous loads before it went out.
-    constexpr int kSteps = kGramTile * kGramKC / 4 / kGramThreads;
-    f4 ra[kSteps], rb[kSteps];
-    auto fetch = [&](int c0) {
+  const int ra = threadIdx.x % kGramTile, rg = threadIdx.x / kGramTile;
+  const int ia = min(a0 + ra, k - 1), ib = min(b0 + ra, k - 1);  // clamped short indices
+  const uint32_t oa = uint32_t(ia) * uint32_t(cols), ob = uint32_t(ib) * uint32_t(cols);  // their rows
+  // path 0: G[a][c] with 16-byte aligned rows, 1: G[a][c] otherwise, 2: G[c][a]
+  auto fetch = [&](auto path, auto diag_c, float (&va)[kGramGroups][8], float (&vb)[kGramGroups][8], int c0) {
+    constexpr int kPath = decltype(path)::value;
+    constexpr bool kB = !decltype(diag_c)::value;  // operand 1 loaded
 #pragma unroll
-      for (int i = 0; i < kSteps; ++i) {
-        const int e = int(threadIdx.x) + i * kGramThreads;
-        if (M.left) {  // G[a][c0 + c .. +3]
-          const int a = e / (kGramKC / 4), c = min(c0 + (e % (kGramKC / 4)) * 4, L - 4);
-          ra[i] = *reinterpret_cast<const f4*>(g + int64_t(min(a0 + a, k - 1)) * cols + c);
-          rb[i] = *reinterpret_cast<const f4*>(g + int64_t(min(b0 + a, k - 1)) * cols + c);
-        } else {       // G[c0 + c][a0 + a .. +3]
-          const int c = e / (kGramTile / 4), a = (e % (kGramTile / 4)) * 4;
-          const float* row = g + int64_t(min(c0 + c, L - 1)) * cols;
-          ra[i] = *reinterpret_cast<const f4*>(row + min(a0 + a, k - 4));
-          rb[i] = *reinterpret_cast<const f4*>(row + min(b0 + a, k - 4));
-        }
-      }
-    };
-    auto stage = [&](int c0) {
+    for (int i = 0; i < kGramGroups; ++i) {
+      const int cg = c0 + 8 * (rg + i * (kGramThreads / kGramTile));  // the group's first long index
+      // offsets within the matrix fit 32 bits: unsigned, they index the uniform base directly
+      if constexpr (kPath == 0) {  // G[a][cg .. cg + 7]
 #pragma unroll
-      for (int i = 0; i < kSteps; ++i) {
-        const int e = int(threadIdx.x) + i * kGramThreads;
-        if (M.left) {
-          const int a = e / (kGramKC / 4), c = (e % (kGramKC / 4)) * 4;
-          const bool cin = c0 + c < L, ain = cin && a0 + a < k, bin = cin && b0 + a < k;
-          for (int q = 0; q < 4; ++q) {
-            sa[c + q][a] = ain ? ra[i][q] : 0.f;
-            sb[c + q][a] = bin ? rb[i][q] : 0.f;
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t c = uint32_t(min(cg + 4 * h, L - 4));
+          const f4 fa = *reinterpret_cast<const f4*>(g + (oa + c));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) va[i][4 * h + e] = fa[e];
+          if constexpr (kB) {
+            const f4 fb = *reinterpret_cast<const f4*>(g + (ob + c));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vb[i][4 * h + e] = fb[e];
           }
-        } else {
-          const int c = e / (kGramTile / 4), a = (e % (kGramTile / 4)) * 4;
-          const bool cin = c0 + c < L;
-          const f4 z = {0.f, 0.f, 0.f, 0.f};
-          *reinterpret_cast<f4*>(&sa[c][a]) = cin && a0 + a < k ? ra[i] : z;
-          *reinterpret_cast<f4*>(&sb[c][a]) = cin && b0 + a < k ? rb[i] : z;
+        }
+      } else if constexpr (kPath == 1) {  // G[a][c], rows not 16-byte aligned
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t c = uint32_t(min(cg + e, L - 1));
+          va[i][e] = g[oa + c];
+          if constexpr (kB) vb[i][e] = g[ob + c];
+        }
+      } else {  // G[c][a]: consecutive threads take consecutive entries of a row
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t row = uint32_t(min(cg + e, L - 1)) * uint32_t(cols);
+          va[i][e] = g[row + uint32_t(ia)];
+          if constexpr (kB) vb[i][e] = g[row + uint32_t(ib)];
         }
       }
-    };
-    fetch(0);
-    for (int c0 = 0; c0 < L; c0 += kGramKC) {
-      stage(c0);
-      __syncthreads();
-      if (c0 + kGramKC < L) fetch(c0 + kGramKC);
-      mfma_chunk();
-      __syncthreads();
     }
-  } else {
-    for (int c0 = 0; c0 < L; c0 += kGramKC) {
-      for (int e = threadIdx.x; e < kGramTile * kGramKC; e += kGramThreads) {
-        if (M.left) {  // element (short index a, long index c) = G[a][c]
-          const int a = e / kGramKC, c = e % kGramKC;
-          const bool cin = c0 + c < L;
-          sa[c][a] = (cin && a0 + a < k) ? g[int64_t(a0 + a) * cols + c0 + c] : 0.f;
-          sb[c][a] = (cin && b0 + a < k) ? g[int64_t(b0 + a) * cols + c0 + c] : 0.f;
-        } else {       // element (short index a, long index c) = G[c][a]
-          const int c = e / kGramTile, a = e % kGramTile;
-          const bool cin = c0 + c < L;
-          sa[c][a] = (cin && a0 + a < k) ? g[int64_t(c0 + c) * cols + a0 + a] : 0.f;
-          sb[c][a] = (cin && b0 + a < k) ? g[int64_t(c0 + c) * cols + b0 + a] : 0.f;
-        }
+  };
+  // Rows past k (loaded from row k - 1) reach only Gram entries that are never stored, so
+  // only the long side is masked, and only in a chunk that runs past L.
+  auto stage_as = [&](auto full_c, auto diag_c, const float (&va)[kGramGroups][8], const float (&vb)[kGramGroups][8],
+                      int c0) {
+    constexpr bool full = decltype(full_c)::value, kB = !decltype(diag_c)::value;
+#pragma unroll
+    for (int i = 0; i < kGramGroups; ++i) {
+      const int gi = rg + i * (kGramThreads / kGramTile), cg = c0 + 8 * gi;
+      float xa[8], xb[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bool cin = full || cg + e < L;
+        xa[e] = cin ? va[i][e] : 0.f;
+        xb[e] = cin && kB ? vb[i][e] : 0.f;
       }
+      const int wo = 4 * (gi ^ (((ra >> 2) ^ (ra >> 3)) & 1));  // the piece's place in the row
+      u4 h, m, l;
+      gram_split(xa, h, m, l);
+      *reinterpret_cast<u4*>(&sg[0][0][ra][wo]) = h;
+      *reinterpret_cast<u4*>(&sg[0][1][ra][wo]) = m;
+      *reinterpret_cast<u4*>(&sg[0][2][ra][wo]) = l;
+      if constexpr (kB) {
+        gram_split(xb, h, m, l);
+        *reinterpret_cast<u4*>(&sg[1][0][ra][wo]) = h;
+        *reinterpret_cast<u4*>(&sg[1][1][ra][wo]) = m;
+        *reinterpret_cast<u4*>(&sg[1][2][ra][wo]) = l;
+      }
+    }
+  };
+  auto stage = [&](auto diag_c, const float (&va)[kGramGroups][8], const float (&vb)[kGramGroups][8], int c0) {
+    if (c0 + kGramKC <= L)  // uniform
+      stage_as(std::true_type{}, diag_c, va, vb, c0);
+    else
+      stage_as(std::false_type{}, diag_c, va, vb, c0);
+  };
+  // the skip is decided once, outside the chunk loop: a branch around the products inside
+  // it made the compiler copy the accumulators between register files every chunk
+  float va[kGramGroups][8], vb[kGramGroups][8];
+  auto run = [&](auto with_products, auto path, auto diag_c) {
+    fetch(path, diag_c, va, vb, 0);
+    for (int c0 = 0; c0 < L; c0 += kGramKC) {
+      stage(diag_c, va, vb, c0);
       __syncthreads();
-      mfma_chunk();
+      if (c0 + kGramKC < L) fetch(path, diag_c, va, vb, c0 + kGramKC);
+      if constexpr (decltype(with_products)::value) mfma_chunk(diag_c);
       __syncthreads();
     }
-  }
+  };
+  auto run_diag = [&](auto with_products, auto path) {
+    if (t.ti == t.tj)
+      run(with_products, path, std::true_type{});
+    else
+      run(with_products, path, std::false_type{});
+  };
+  auto run_path = [&](auto with_products) {
+    if (vec)
+      run_diag(with_products, std::integral_constant<int, 0>{});
+    else if (M.left)
+      run_diag(with_products, std::integral_constant<int, 1>{});
+    else
+      run_diag(with_products, std::integral_constant<int, 2>{});
+  };
+  if (live)
+    run_path(std::true_type{});
+  else
+    run_path(std::false_type{});
   // the tile's lower-triangle entries, row-major with leading dimension k (the upper
   // triangle is never read: the reduction works on the lower one)
 #pragma unroll

@@ -32,8 +32,11 @@
  *     basis of the cluster's singular subspace is as valid as any other;
  *   - arithmetic is float32: the Gram matrix G G^T (or G^T G) of the short side, its
  *     reduction to tridiagonal form, bisection for its eigenvalues (sigma_i^2) and
- *     inverse iteration for the eigenvectors of the sent atoms.  Singular values below
- *     about sqrt(k * 2^-24) * sigma_max carry float32 rounding of that order.
+ *     inverse iteration for the eigenvectors of the sent atoms.  The Gram matrix's
+ *     products run on bf16 matrix cores with every entry split exactly into three bf16
+ *     parts; the six products kept carry each x y to within about 2^-20 |x y|, and the sums
+ *     accumulate in float32.  Singular values below about sqrt(k * 2^-24) * sigma_max
+ *     carry float32 rounding of that order.
  *
  * Memory layout.  The packed layout of psgd.h: every tensor starts at an element offset
  * that is a multiple of 64 (psgd_atomo_plan_layer_info gives it); grads are
