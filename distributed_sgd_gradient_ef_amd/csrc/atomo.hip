@@ -19,7 +19,8 @@
 //                 panel in registers, two-sided blocked update of the trailing matrix's
 //                 lower triangle on fp32 MFMA)
 //   at_chase      one workgroup per problem: the band to tridiagonal form by bulge
-//                 chasing in LDS, the sweeps pipelined three steps apart
+//                 chasing in LDS, the sweeps pipelined three steps apart, each wave
+//                 waiting only on its predecessor sweep's progress
 //   at_eig        every eigenvalue of the tridiagonal matrix by bisection on Sturm
 //                 counts: 64 per workgroup (one per lane; a large matrix spans several
 //                 compute units), a first round of 256 probes shared by the workgroup,
@@ -437,9 +438,11 @@ __global__ __launch_bounds__(kGramThreads) void at_gram(const GramTile* __restri
 // its subdiagonal with a reflector on rows r0 = j + 1 .. j + kBand (step 0); applied from
 // both sides this fills a block below the band, whose first column the next reflector,
 // kBand rows further down, annihilates (step 1), and so on to the end of the matrix.
-// Step s of sweep j runs in round 3 j + s: two sweeps three rounds apart touch disjoint
-// elements, so every wave takes one sweep of a round and the round ends with one
-// barrier.  Every reflector (kBand entries and tau) is kept for the back-transform, where
+// Step s of sweep j (rows r0 = j + 1 + s kBand .. r0 + 2 kBand - 1, columns r0 - kBand ..
+// r0 + kBand - 1) follows step s + 2 of sweep j - 1, which sets the entry (r0 + 31,
+// r0 + 15) that it then updates; steps of two sweeps three or more apart touch disjoint
+// entries.  Each wave runs its own sweeps and waits only for its predecessor sweep's
+// progress, published in LDS (no workgroup barrier between steps).  Every reflector (kBand entries and tau) is kept for the back-transform, where
 // the reflectors of one sweep (disjoint supports) are applied together and the sweeps in
 // reverse order.
 constexpr int kBand = 16;
@@ -455,7 +458,8 @@ constexpr int kUpdPre = PSGD_UPD_PRE;  // update tiles in flight per wave
 constexpr int kXPre = PSGD_X_PRE;      // X-pass tiles in flight per wave
 constexpr int kChaseThreads = 1024;
 constexpr int kChaseWaves = kChaseThreads / 64;
-constexpr int kLag = 3;  // rounds between the starts of consecutive sweeps
+constexpr int kLag = 3;  // steps sweep j - 1 stays ahead of sweep j
+constexpr int kChaseSpin = 1 << 16;  // polls of one wait at most (a step's wait takes tens)
 
 // the most chase steps a sweep of a k x k problem has, and the reflector block's floats
 __host__ __device__ constexpr int chase_steps_max(int k) { return (k + kBand - 1) / kBand; }
@@ -466,14 +470,6 @@ __host__ __device__ constexpr int64_t chase_block(int k) {
 __device__ __forceinline__ int chase_steps(int k, int j) { return j > k - 3 ? 0 : (k - 3 - j) / kBand + 1; }
 // stage-1 panels: columns c = 0, kBand, ... while at least two rows lie below the band
 __device__ __forceinline__ int band_panels(int k) { return k < kBand + 2 ? 0 : (k - kBand - 2) / kBand + 1; }
-
-// A workgroup barrier that orders LDS only: the chase's global stores (the reflectors,
-// read by a later kernel) are not waited for at every round, as __syncthreads() would.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // Orders one wave's LDS stores before its later LDS loads, also across lanes (the
 // compiler may otherwise move a lane's load above another lane's store); all lanes of the
@@ -985,7 +981,7 @@ __global__ __launch_bounds__(kBandThreads) void at_band(const int32_t* __restric
 // up to four times (the diagonal block) where now at most two do.  With the kChasePad
 // zeros after k columns every load of a step stays in the array without clamping.  The
 // step's loads are all issued first (the blocks it reads and writes are disjoint, and no
-// other step of the round touches them), and what lies outside the matrix or the block
+// step running at the same time touches them), and what lies outside the matrix or the block
 // is zeroed by selection.  dk[c] = kChaseLd min(u, t) + max(u, t) places element
 // (r0 + u, r0 + t) of the diagonal block (lower triangle).
 constexpr int kChaseLd = 2 * kBand + 3;
@@ -1119,27 +1115,49 @@ __global__ __launch_bounds__(kChaseThreads) void at_chase(const int32_t* __restr
   }
   const bool tau_lane = lane == 16;
   const int slot_at = tau_lane ? kBand : u;
+  // Wave w runs the sweeps j = w, w + 16, ... in order, each step after the previous
+  // sweep has finished kLag steps more (step s of sweep j once steps 0 .. s + 2 of sweep
+  // j - 1 are done; steps further apart touch disjoint entries).  Progress is published
+  // per wave in LDS as j * 1024 + (steps done) once the step's LDS stores are complete;
+  // sweep j waits only on sweep j - 1, so the waits form a chain that ends at sweep 0.
+  // Each wait is bounded all the same (kChaseSpin polls), and one that runs out stops all
+  // later waits of the workgroup, so that no mistake here could leave a wave spinning.
+  __shared__ int prog[kChaseWaves], bail;
+  if (tid < kChaseWaves) prog[tid] = -1;
+  if (tid == 0) bail = 0;
   __syncthreads();
-  const int rounds = k < 3 ? 0 : kLag * (k - 3) + 1;
   const int wv = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform: scalar loop control
-  for (int rho = 0; rho < rounds; ++rho) {
-    // the sweeps of this round: j = jhi, jhi - 1, ... while step rho - 3 j exists
-    const int jhi = min(k - 3, rho / kLag);
-    for (int j = jhi - wv; j >= 0; j -= kChaseWaves) {
-      const int st = rho - kLag * j;
-      if (st >= chase_steps(k, j)) break;  // and every smaller j (wave-uniform)
-      // (j, st) made opaque to the optimiser: otherwise it strength-reduces the step's lane
-      // addresses across rounds into some twenty vector adds and moves per round, which
-      // every wave, also an idle one, then spends on each round
+  for (int j = wv; j <= k - 3; j += kChaseWaves) {
+    const int ns = chase_steps(k, j), nprev = j > 0 ? chase_steps(k, j - 1) : 0;
+    for (int st = 0; st < ns; ++st) {
+      if (j > 0) {
+        const int need = (j - 1) * 1024 + min(st + kLag, nprev);
+#pragma nounroll
+        for (int it = 0;; ++it) {
+          if (__hip_atomic_load(&prog[(j - 1) % kChaseWaves], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= need ||
+              __hip_atomic_load(&bail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP))
+            break;
+          if (it == kChaseSpin) {
+            if (lane == 0) __hip_atomic_store(&bail, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+      }
+      // (j, st) made opaque to the optimiser: otherwise it strength-reduces the step's
+      // lane addresses across steps into many vector adds and moves
       int js = j, ss = st;
       asm volatile("" : "+s"(js), "+s"(ss));
       if (ss > 0 && k - (js + 1 + ss * kBand) >= 2 * kBand)
         chase_step<true>(band, R2, k, js, ss, u, g, dk, slot_at, tau_lane);
       else
         chase_step<false>(band, R2, k, js, ss, u, g, dk, slot_at, tau_lane);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      if (lane == 0) __hip_atomic_store(&prog[wv], j * 1024 + st + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
-    lds_barrier();
   }
+  __syncthreads();
   for (int i = tid; i < k; i += kChaseThreads) {
     d[i] = band[i * (kChaseLd + 1)];
     if (i + 1 < k) e[i] = band[i * (kChaseLd + 1) + 1];
