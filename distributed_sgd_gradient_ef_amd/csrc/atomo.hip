@@ -61,7 +61,7 @@ constexpr int kMaxK = PSGD_ATOMO_MAX_K;
 constexpr int kGramTile = 128;
 constexpr int kGramKC = 16;
 constexpr int kGramThreads = 256;
-constexpr int kEigSlots = 64;    // eigenvalues per at_eig workgroup, one per lane (grid.z splits a matrix)
+constexpr int kEigSlots = 64;    // eigenvalues per at_eig workgroup, one per lane (a matrix in slices)
 constexpr int kEigWaves = 4;     // probe points per round, one per wave: each round leaves a fifth
 constexpr int kEigThreads = 64 * kEigWaves;
 constexpr int kSampleThreads = 1024;
@@ -115,6 +115,7 @@ struct psgd_atomo_plan {
   std::vector<psgd::atm::FactorTile> ftiles;
   std::vector<psgd::atm::AtUpdTile> utiles;
   std::vector<int32_t> tri_list;  // matrices in decreasing k (the largest start first)
+  std::vector<int32_t> eig_items;  // matrix * 16 + slice of kEigSlots eigenvalues, in decreasing k
   int32_t max_k = 0;
   int64_t worker_stride = 0, numel = 0, sv_total = 0, atom_total = 0, gram_total = 0, refl_total = 0;
   uint64_t ws_gram = 0, ws_y = 0, ws_refl = 0, ws_d = 0, ws_e = 0, ws_lam = 0, workspace_bytes = 0;
@@ -1181,13 +1182,16 @@ __device__ __forceinline__ int sturm_below(const float* sd, const float* se2, in
   return c;
 }
 
-__global__ __launch_bounds__(kEigThreads) void at_eig(const AtMat* __restrict__ mats, const float* __restrict__ d_ws,
-                                                      const float* __restrict__ e_ws, float* __restrict__ lam_ws,
-                                                      float* __restrict__ sigma, int64_t sv_total) {
-  const AtMat M = mats[blockIdx.x];
-  const int64_t w = blockIdx.y;
+// grid (workers, items): item = matrix * 16 + slice, slices of kEigSlots eigenvalues,
+// the items in decreasing k so that the longest workgroups are dispatched first
+__global__ __launch_bounds__(kEigThreads) void at_eig(const int32_t* __restrict__ items, const AtMat* __restrict__ mats,
+                                                      const float* __restrict__ d_ws, const float* __restrict__ e_ws,
+                                                      float* __restrict__ lam_ws, float* __restrict__ sigma,
+                                                      int64_t sv_total) {
+  const int item = items[blockIdx.y], slice = item & 15;
+  const AtMat M = mats[item >> 4];
+  const int64_t w = blockIdx.x;
   const int k = M.k, tid = threadIdx.x;
-  if (int(blockIdx.z) * kEigSlots >= k) return;  // the whole workgroup: no eigenvalue here
   const float* d = d_ws + w * sv_total + M.sv_off;
   const float* e = e_ws + w * sv_total + M.sv_off;
   float* lam = lam_ws + w * sv_total + M.sv_off;
@@ -1220,7 +1224,7 @@ __global__ __launch_bounds__(kEigThreads) void at_eig(const AtMat* __restrict__ 
   // same counts with the same arithmetic, so all waves hold the same interval
   __shared__ int cnt[kEigWaves][64];
   const int lane = tid & 63, wave = tid >> 6;
-  const int idx = int(blockIdx.z) * kEigSlots + lane;
+  const int idx = slice * kEigSlots + lane;
   const bool mine = idx < k;
   float a = glo - slack, b = ghi + slack;
   {
@@ -1365,15 +1369,15 @@ constexpr int kVecLdsBytes = 2048 * 24;  // slots * k * (5 floats + 1 int) stays
 __device__ __forceinline__ int vec_slots(int k) { return max(1, min(8, 2048 / k)); }
 constexpr int kVecChunk = 8;  // rows of a recurrence whose loads are issued together
 
-__global__ __launch_bounds__(kVecThreads) void at_vectors(const AtMat* __restrict__ mats,
+__global__ __launch_bounds__(kVecThreads) void at_vectors(const int32_t* __restrict__ list, const AtMat* __restrict__ mats,
                                                           const float* __restrict__ d_ws,
                                                           const float* __restrict__ e_ws,
                                                           const float* __restrict__ lam_ws,
                                                           const int32_t* __restrict__ index,
                                                           const int32_t* __restrict__ count, float* __restrict__ Y,
                                                           int64_t gram_ws, int64_t sv_total, int32_t n_mats) {
-  const AtMat M = mats[blockIdx.x];
-  const int64_t w = blockIdx.y;
+  const AtMat M = mats[list[blockIdx.y]];  // grid (workers, matrices in decreasing k)
+  const int64_t w = blockIdx.x;
   const int k = M.k, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int kWaves = kVecThreads / 64;
   const int cnt = count[w * n_mats + M.mat_index];
@@ -1651,12 +1655,12 @@ __device__ __forceinline__ void back_chunk_apply(float* y, const float* stage, i
   }
 }
 
-__global__ __launch_bounds__(kBackThreads) void at_backchase(const AtMat* __restrict__ mats,
+__global__ __launch_bounds__(kBackThreads) void at_backchase(const int32_t* __restrict__ list, const AtMat* __restrict__ mats,
                                                              const float* __restrict__ refl, float* __restrict__ Y,
                                                              const int32_t* __restrict__ count, int64_t gram_ws,
                                                              int64_t refl_ws, int32_t n_mats) {
-  const AtMat M = mats[blockIdx.x];
-  const int64_t w = blockIdx.y;
+  const AtMat M = mats[list[blockIdx.y]];  // grid (workers, matrices in decreasing k)
+  const int64_t w = blockIdx.x;
   const int cnt = count[w * n_mats + M.mat_index];
   const int k = M.k;
   if (cnt == 0 || k < 3) return;
@@ -1713,14 +1717,14 @@ __global__ __launch_bounds__(kBackThreads) void at_backchase(const AtMat* __rest
   }
 }
 
-__global__ __launch_bounds__(kBackThreads) void at_backband(const AtMat* __restrict__ mats,
+__global__ __launch_bounds__(kBackThreads) void at_backband(const int32_t* __restrict__ list, const AtMat* __restrict__ mats,
                                                             const float* __restrict__ gram,
                                                             const float* __restrict__ Y,
                                                             const int32_t* __restrict__ count,
                                                             float* __restrict__ atoms, int64_t gram_ws,
                                                             int64_t atom_total, int32_t n_mats) {
-  const AtMat M = mats[blockIdx.x];
-  const int64_t w = blockIdx.y;
+  const AtMat M = mats[list[blockIdx.y]];  // grid (workers, matrices in decreasing k)
+  const int64_t w = blockIdx.x;
   const int cnt = count[w * n_mats + M.mat_index];
   if (cnt == 0) return;
   const int k = M.k;
@@ -1975,6 +1979,7 @@ struct DevTables {
   FactorTile* ftiles;
   AtUpdTile* utiles;
   int32_t* tri_list;
+  int32_t* eig_items;
 };
 
 psgd_status device_tables(psgd_atomo_plan* plan, DevTables* out) {
@@ -1986,10 +1991,11 @@ psgd_status device_tables(psgd_atomo_plan* plan, DevTables* out) {
   const uint64_t bf = a256(plan->ftiles.size() * sizeof(FactorTile) + 1);
   const uint64_t bu = a256(plan->utiles.size() * sizeof(AtUpdTile) + 1);
   const uint64_t bl = a256(plan->tri_list.size() * sizeof(int32_t) + 1);
+  const uint64_t be = a256(plan->eig_items.size() * sizeof(int32_t) + 1);
   auto it = plan->dev.find(dev);
   if (it == plan->dev.end()) {
     void* base = nullptr;
-    e = hipMalloc(&base, bm + bg + bf + bu + bl);
+    e = hipMalloc(&base, bm + bg + bf + bu + bl + be);
     if (e != hipSuccess)
       return fail(PSGD_ERR_NO_MEMORY, std::string("hipMalloc of the plan's device tables: ") + hipGetErrorString(e));
     char* b = static_cast<char*>(base);
@@ -2005,6 +2011,9 @@ psgd_status device_tables(psgd_atomo_plan* plan, DevTables* out) {
     if (e == hipSuccess)
       e = hipMemcpy(b + bm + bg + bf + bu, plan->tri_list.data(), plan->tri_list.size() * sizeof(int32_t),
                     hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+      e = hipMemcpy(b + bm + bg + bf + bu + bl, plan->eig_items.data(), plan->eig_items.size() * sizeof(int32_t),
+                    hipMemcpyHostToDevice);
     if (e != hipSuccess) {
       (void)hipFree(base);
       return hip_fail("hipMemcpy of the plan's device tables", e);
@@ -2017,6 +2026,7 @@ psgd_status device_tables(psgd_atomo_plan* plan, DevTables* out) {
   out->ftiles = reinterpret_cast<FactorTile*>(b + bm + bg);
   out->utiles = reinterpret_cast<AtUpdTile*>(b + bm + bg + bf);
   out->tri_list = reinterpret_cast<int32_t*>(b + bm + bg + bf + bu);
+  out->eig_items = reinterpret_cast<int32_t*>(b + bm + bg + bf + bu + bl);
   return PSGD_OK;
 }
 
@@ -2194,6 +2204,13 @@ extern "C" psgd_status psgd_atomo_plan_create(const psgd_layer* layers, int32_t 
     for (size_t mi = 0; mi < plan->mats.size(); ++mi) plan->tri_list.push_back(int32_t(mi));
     std::stable_sort(plan->tri_list.begin(), plan->tri_list.end(),
                      [&](int32_t x, int32_t y) { return plan->mats[size_t(x)].k > plan->mats[size_t(y)].k; });
+    static_assert(kMaxK / kEigSlots <= 16, "a slice index fits four bits");
+    for (const int32_t mi : plan->tri_list)
+      for (int sl = 0; sl * kEigSlots < plan->mats[size_t(mi)].k; ++sl) plan->eig_items.push_back(mi * 16 + sl);
+    if (plan->eig_items.size() > 65535) {  // the eigenvalue launch's second grid dimension
+      delete plan;
+      return fail(PSGD_ERR_UNSUPPORTED, std::string(fn) + ": more than 65535 eigenvalue slices in one plan");
+    }
     for (const auto& li : plan->info)
       if (!li.compressed)
         for (int64_t b = 0; b < li.numel; b += 4096)
@@ -2391,22 +2408,27 @@ extern "C" psgd_status psgd_atomo_step(psgd_atomo_plan* plan, const float* grads
     }
     // eigenvalues in slices of kEigSlots per workgroup: a large matrix's bisections
     // spread over several compute units
-    const dim3 egrid(mgrid.x, mgrid.y, unsigned((plan->max_k + kEigSlots - 1) / kEigSlots));
-    if ((s = launch(plan, kEig, at_eig, egrid, dim3(kEigThreads), st, M, static_cast<const float*>(dd),
+    const dim3 egrid(unsigned(W), unsigned(plan->eig_items.size()));
+    if ((s = launch(plan, kEig, at_eig, egrid, dim3(kEigThreads), st, static_cast<const int32_t*>(dt.eig_items), M,
+                    static_cast<const float*>(dd),
                     static_cast<const float*>(ee), lam, sigma, svt)) != PSGD_OK)
       return s;
     if ((s = launch(plan, kSample, at_sample, mgrid, dim3(kSampleThreads), st, M, static_cast<const float*>(sigma),
                     uniforms, prob, index, count, svt, nmats, float(plan->budget))) != PSGD_OK)
       return s;
-    if ((s = launch(plan, kVectors, at_vectors, mgrid, dim3(kVecThreads), st, M, static_cast<const float*>(dd),
+    const dim3 lgrid(mgrid.y, mgrid.x);  // (workers, matrices in decreasing k): the largest start first
+    const int32_t* list = dt.tri_list;
+    if ((s = launch(plan, kVectors, at_vectors, lgrid, dim3(kVecThreads), st, list, M, static_cast<const float*>(dd),
                     static_cast<const float*>(ee), static_cast<const float*>(lam),
                     static_cast<const int32_t*>(index), static_cast<const int32_t*>(count), Y, gws, svt, nmats)) !=
         PSGD_OK)
       return s;
-    if ((s = launch(plan, kBackChase, at_backchase, mgrid, dim3(kBackThreads), st, M, static_cast<const float*>(refl),
+    if ((s = launch(plan, kBackChase, at_backchase, lgrid, dim3(kBackThreads), st, list, M,
+                    static_cast<const float*>(refl),
                     Y, static_cast<const int32_t*>(count), gws, rws, nmats)) != PSGD_OK)
       return s;
-    if ((s = launch(plan, kBackBand, at_backband, mgrid, dim3(kBackThreads), st, M, static_cast<const float*>(gram),
+    if ((s = launch(plan, kBackBand, at_backband, lgrid, dim3(kBackThreads), st, list, M,
+                    static_cast<const float*>(gram),
                     static_cast<const float*>(Y), static_cast<const int32_t*>(count), atoms, gws, att, nmats)) !=
         PSGD_OK)
       return s;
