@@ -1364,9 +1364,9 @@ __global__ __launch_bounds__(kSampleThreads) void at_sample(const AtMat* __restr
 // where the second solve left a residual bound above 2^-20 ||T||.  Up to kVecSlots
 // atoms are solved side by side, one lane each (the elimination is a sequential
 // recurrence); pivots below 2^-24 ||T|| are raised to that size.
-constexpr int kVecLdsBytes = 2048 * 24;  // slots * k * (5 floats + 1 int) stays within this
+constexpr int kVecLdsBytes = 4096 * 24;  // slots * k * (5 floats + 1 int) stays within this
 
-__device__ __forceinline__ int vec_slots(int k) { return max(1, min(8, 2048 / k)); }
+__device__ __forceinline__ int vec_slots(int k) { return max(1, min(8, 4096 / k)); }
 constexpr int kVecChunk = 8;  // rows of a recurrence whose loads are issued together
 
 __global__ __launch_bounds__(kVecThreads) void at_vectors(const int32_t* __restrict__ list, const AtMat* __restrict__ mats,
