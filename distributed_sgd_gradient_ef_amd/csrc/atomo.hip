@@ -1361,8 +1361,8 @@ __global__ __launch_bounds__(kSampleThreads) void at_sample(const AtMat* __restr
 // eigenvalues: Gaussian elimination with partial pivoting of T - lam I, then two or three
 // rounds of (solve; orthogonalise each vector, in atom order, against every earlier
 // atom's vector -- classical Gram-Schmidt applied twice --; normalise); the third only
-// where the second solve left a residual bound above 2^-20 ||T||.  Up to kVecSlots
-// atoms are solved side by side, one lane each (the elimination is a sequential
+// where the second solve left a residual bound above 2^-20 ||T||.  Up to vec_slots(k)
+// atoms (eight up to k = 512) are solved side by side, one lane each (the elimination is a sequential
 // recurrence); pivots below 2^-24 ||T|| are raised to that size.
 constexpr int kVecLdsBytes = 4096 * 24;  // slots * k * (5 floats + 1 int) stays within this
 
