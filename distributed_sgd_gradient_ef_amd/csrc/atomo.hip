@@ -1130,6 +1130,12 @@ __global__ __launch_bounds__(kChaseThreads) void at_chase(const int32_t* __restr
   const int wv = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform: scalar loop control
   for (int j = wv; j <= k - 3; j += kChaseWaves) {
     const int ns = chase_steps(k, j), nprev = j > 0 ? chase_steps(k, j - 1) : 0;
+    {  // the reflector slots of the steps this sweep does not have hold zeros: the
+       // back-transform applies them as reflectors that change nothing, without masks
+      const int smax = chase_steps_max(k);
+      float* Rj = R2 + int64_t(j) * smax * (kBand + 1);
+      for (int e = ns * (kBand + 1) + lane; e < smax * (kBand + 1); e += 64) Rj[e] = 0.f;
+    }
     for (int st = 0; st < ns; ++st) {
       if (j > 0) {
         const int need = (j - 1) * 1024 + min(st + kLag, nprev);
@@ -1599,17 +1605,24 @@ __device__ __forceinline__ float wave_shift_up(float v, float in) {
 
 // One sweep of reflectors on the window x (NS registers): block s = 4 i + g, valid below
 // n, its entries at sl[s * (kBand + 1) + u] and tau after them.
-template <int NS>
+// kMask false: every block 4 i + g lies in the sweep's slot (4 NS <= chase_steps_max(k)),
+// and the blocks at or past n hold zeros, so no entry needs a mask.
+template <int NS, bool kMask>
 __device__ __forceinline__ void back_sweep(float (&x)[NS], const float* sl, int n, int u, int g) {
   float v[NS], t[NS], d[NS];
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
     const int s = 4 * i + g;
-    const bool ok = s < n;
-    const float vs = sl[(ok ? s : 0) * (kBand + 1) + u];
-    const float ts = sl[(ok ? s : 0) * (kBand + 1) + kBand];
-    v[i] = ok ? vs : 0.f;
-    t[i] = ok ? ts : 0.f;
+    if constexpr (kMask) {
+      const bool ok = s < n;
+      const float vs = sl[(ok ? s : 0) * (kBand + 1) + u];
+      const float ts = sl[(ok ? s : 0) * (kBand + 1) + kBand];
+      v[i] = ok ? vs : 0.f;
+      t[i] = ok ? ts : 0.f;
+    } else {
+      v[i] = sl[s * (kBand + 1) + u];
+      t[i] = sl[s * (kBand + 1) + kBand];
+    }
   }
 #pragma unroll
   for (int i = 0; i < NS; ++i) d[i] = v[i] * x[i];
@@ -1635,7 +1648,7 @@ __device__ __forceinline__ void back_shift(float (&x)[NS], float yin) {
 
 // The sweeps jhi down to jl of the chunk staged at `stage` (sweep jl first), on the
 // window of NS = ceil(k / 64) registers, read from and written back to y.
-template <int NS>
+template <int NS, bool kMask>
 __device__ __forceinline__ void back_chunk_apply(float* y, const float* stage, int k, int jl, int jhi, int slot_fl) {
   const int lane = threadIdx.x & 63, u = lane & 15, g = lane >> 4;
   float x[NS];  // the window of sweep jhi starts at row jhi + 1
@@ -1645,7 +1658,7 @@ __device__ __forceinline__ void back_chunk_apply(float* y, const float* stage, i
     x[i] = r < k ? y[r] : 0.f;
   }
   for (int jj = jhi; jj >= jl; --jj) {
-    back_sweep<NS>(x, stage + (jj - jl) * slot_fl, chase_steps(k, jj), u, g);
+    back_sweep<NS, kMask>(x, stage + (jj - jl) * slot_fl, chase_steps(k, jj), u, g);
     if (jj > jl) back_shift<NS>(x, y[jj]);
   }
 #pragma unroll
@@ -1698,9 +1711,12 @@ __global__ __launch_bounds__(kBackThreads) void at_backchase(const int32_t* __re
       if (jl > 0) load(jlo = max(0, jl - chunk));
       if (mine) {
         switch (ns) {
-#define PSGD_BACK_CASE(N) \
-  case N:                 \
-    back_chunk_apply<N>(y, stage, k, jl, jhi, slot_fl); \
+#define PSGD_BACK_CASE(N)                                      \
+  case N:                                                      \
+    if (4 * N <= chase_steps_max(k))                           \
+      back_chunk_apply<N, false>(y, stage, k, jl, jhi, slot_fl); \
+    else                                                       \
+      back_chunk_apply<N, true>(y, stage, k, jl, jhi, slot_fl);  \
     break;
           PSGD_BACK_CASE(1) PSGD_BACK_CASE(2) PSGD_BACK_CASE(3) PSGD_BACK_CASE(4)
           PSGD_BACK_CASE(5) PSGD_BACK_CASE(6) PSGD_BACK_CASE(7) PSGD_BACK_CASE(8)
