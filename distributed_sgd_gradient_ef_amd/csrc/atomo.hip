@@ -1766,9 +1766,12 @@ __global__ __launch_bounds__(kBackThreads) void at_backband(const int32_t* __res
     const int c = p * kBand, r0 = c + kBand, m = k - r0;
 #pragma unroll
     for (int q = 0; q < QN; ++q) {
+      // row and column selected first, one product after: with a product in each arm the
+      // selection became a branch around every load
       const int r = rt + q * kRowStep, a = r - m;
-      const int off = r < m ? (r0 + r) * k + c + ci : (a < kBand ? (c + a) * k + r0 + ci : 0);
-      pre[q] = A[off];
+      const bool isv = r < m;
+      const int row = isv ? r0 + r : c + min(a, kBand - 1), col = isv ? c + ci : r0 + ci;
+      pre[q] = A[uint32_t(row * k + col)];
     }
   };
   // V rows at stride kBackVS, T after them
@@ -1781,7 +1784,10 @@ __global__ __launch_bounds__(kBackThreads) void at_backband(const int32_t* __res
       const float x = pre[q];
       const float v = r < m ? (ci < nref && r > ci ? x : (ci < nref && r == ci ? 1.f : 0.f))
                             : (a <= ci && ci < nref ? x : 0.f);
-      if (a < kBand) stage[r * kBackVS + ci] = v;
+      if constexpr (QN * kRowStep <= kMaxK)  // rows past the panel land in unused LDS
+        stage[r * kBackVS + ci] = v;
+      else if (a < kBand)
+        stage[r * kBackVS + ci] = v;
     }
   };
   // y[r0:] -= V (T (V^T y[r0:])) for the staged panel p
