@@ -36,6 +36,7 @@ Prints one JSON line:
 
 from __future__ import annotations
 
+import gc
 import argparse
 import hashlib
 import json
@@ -253,11 +254,19 @@ def timed_steps(torch, step, steps: int, stream):
     """Run `steps` calls of step() with an event recorded on `stream` between calls.
     Returns (mean ms over the whole region, median ms, minimum ms)."""
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    ev[0].record(stream)
-    for i in range(steps):
-        step()
-        ev[i + 1].record(stream)
-    torch.cuda.synchronize()
+    # no garbage-collection pause while the steps are enqueued: a pause of a few ms with
+    # the queue short leaves the GPU idle inside the timed region
+    gc_was_on = gc.isenabled()
+    gc.disable()
+    try:
+        ev[0].record(stream)
+        for i in range(steps):
+            step()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+    finally:
+        if gc_was_on:
+            gc.enable()
     per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     return ev[0].elapsed_time(ev[steps]) / steps, per[len(per) // 2], per[0]
 
