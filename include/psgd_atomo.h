@@ -35,7 +35,9 @@
  *     inverse iteration for the eigenvectors of the sent atoms.  The Gram matrix's
  *     products run on bf16 matrix cores with every entry split exactly into three bf16
  *     parts; the six products kept carry each x y to within about 2^-20 |x y|, and the sums
- *     accumulate in float32.  Singular values below about sqrt(k * 2^-24) * sigma_max
+ *     accumulate in float32 (the five smaller products of a step summed apart from the
+ *     running sum), which keeps the singular values as close to float64 as the float32
+ *     matrix instruction does.  Singular values below about sqrt(k * 2^-24) * sigma_max
  *     carry float32 rounding of that order.
  *
  * Memory layout.  The packed layout of psgd.h: every tensor starts at an element offset
