@@ -16,7 +16,7 @@
 //                 predicted from the previous step, the marking below
 //   rk_select     per segment: the digit-1 bin b1 holding T, and how many of its
 //                 entries belong to the top set; a wrong prediction sends the segment
-//                 to rk_mark (b1 becomes the next step's prediction)
+//                 to rk_mark
 //   rk_mark       (mispredicted segments) re-read M: entries above b1 -> top mask (one
 //                 bit per element); entries in b1 -> the tile's candidate region (key
 //                 bits 19..0 | tile offset), and a histogram of their digit 2; per-tile
@@ -113,7 +113,8 @@ struct RkSeg {
   uint32_t partial;
   uint32_t ntop;   // top-set size found (r)
   uint32_t nkept;  // entries with rank < k
-  uint32_t pad1, pad2, pad3;
+  uint32_t tkey;  // T of the last step whose rule was found (carried from step to step)
+  uint32_t pad2, pad3;
 };
 
 enum KernelId {
@@ -524,8 +525,8 @@ __global__ __launch_bounds__(kSelThreads) void rk_select(const RkLayer* __restri
     st.need1 = r - p.above;
     st.count1 = p.count;
     st.redo = redo ? 1u : 0u;
+    st.tkey = seg[s].tkey;
     seg[s] = st;
-    pred[s] = p.bin;
   }
 }
 
@@ -663,12 +664,30 @@ __global__ __launch_bounds__(kSelThreads) void rk_level3(const RkChunk* __restri
 
 // Per segment, once digit 3 is counted: the rule.  Keys >= sel_lo are in; when the
 // entries equal to T are only partly in, the first need_t of them in index order are.
-__global__ __launch_bounds__(kSelThreads) void rk_rule(const uint32_t* __restrict__ hist3, RkSeg* __restrict__ seg) {
+//
+// The digit-1 bin the next step marks against is predicted here from this step's T and
+// the last one's: T moved on by the same amount again (at most four bins of it, else T
+// as it is).  Under error feedback the top set's threshold drifts steadily from step to
+// step, so T's own bin would miss about every time it crosses a bin edge.  The
+// prediction decides only which kernel marks, never a result.
+__device__ __forceinline__ void predict_next(RkSeg* __restrict__ seg, uint32_t* __restrict__ pred, int64_t s,
+                                             uint32_t t, uint32_t t_last) {
+  const int64_t d = int64_t(t) - int64_t(t_last);
+  const int64_t next = (d >= -(int64_t(4) << 20) && d <= (int64_t(4) << 20)) ? int64_t(t) + d : int64_t(t);
+  seg[s].tkey = t;
+  pred[s] = uint32_t(min(max(next, int64_t(0)), int64_t(0x7fffffff)) >> 20);
+}
+
+__global__ __launch_bounds__(kSelThreads) void rk_rule(const uint32_t* __restrict__ hist3, RkSeg* __restrict__ seg,
+                                                       uint32_t* __restrict__ pred) {
   __shared__ uint32_t lds[16], sh[3];
   const int64_t s = int64_t(blockIdx.y) * gridDim.x + blockIdx.x;
   const RkSeg st = seg[s];
   if (st.settled) {
-    if (threadIdx.x == 0) seg[s].partial = 0u;
+    if (threadIdx.x == 0) {
+      seg[s].partial = 0u;
+      predict_next(seg, pred, s, st.sel_lo, st.tkey);
+    }
     return;
   }
   const Pick p3 = pick_bin<kBins3>(hist3 + s * kBins3, st.need2, lds, sh);
@@ -684,6 +703,7 @@ __global__ __launch_bounds__(kSelThreads) void rk_rule(const uint32_t* __restric
       seg[s].need_t = need3;
       seg[s].partial = 1u;
     }
+    predict_next(seg, pred, s, t, st.tkey);
   }
 }
 
@@ -1305,7 +1325,7 @@ extern "C" psgd_status psgd_rtopk_plan_create(const psgd_layer* layers, int32_t 
     ws = a256(ws + uint64_t(plan->n_seg) * kBins3 * 4);
     plan->ws_seg = ws;
     ws = a256(ws + uint64_t(plan->n_seg) * sizeof(RkSeg));
-    plan->ws_pred = ws;  // digit-1 bin of the previous step per segment (a hint only)
+    plan->ws_pred = ws;  // predicted digit-1 bin per segment (a hint only)
     ws = a256(ws + uint64_t(plan->n_seg) * 4);
     plan->ws_cand = ws;  // same layout as the error buffer, one uint32 per element
     ws = a256(ws + W * uint64_t(plan->worker_stride) * 4);
@@ -1532,8 +1552,8 @@ extern "C" psgd_status psgd_rtopk_step(psgd_rtopk_plan* plan, const void* grads,
                   hist3, static_cast<const uint32_t*>(cand), static_cast<const uint32_t*>(ccnt4), sstride, nl,
                   ntiles)) != PSGD_OK)
     return s;
-  if ((s = launch(plan, kRule, rk_rule, sgrid, dim3(kSelThreads), st, static_cast<const uint32_t*>(hist3), seg)) !=
-      PSGD_OK)
+  if ((s = launch(plan, kRule, rk_rule, sgrid, dim3(kSelThreads), st, static_cast<const uint32_t*>(hist3), seg,
+                  pred)) != PSGD_OK)
     return s;
   if ((s = launch(plan, kFinal, rk_final, cgrid, dim3(kSelThreads), st, C, T, L, static_cast<const RkSeg*>(seg),
                   static_cast<const uint32_t*>(cand), static_cast<const uint32_t*>(ccnt4), mask, tmask, tfin, ttie,
