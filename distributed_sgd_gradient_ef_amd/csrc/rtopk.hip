@@ -746,23 +746,36 @@ __global__ __launch_bounds__(kSelThreads) void rk_final(const RkChunk* __restric
     const uint32_t key = hi | (e >> kLocalBits);
     const uint32_t off = e & uint32_t(kTile - 1);
     const int word = (r >> 2) * kTileWords + int(off >> 5);
-    if (key >= lo) {
+    if (key >= lo)
       atomicOr(&lm[word], 1u << (off & 31));
-      atomicAdd(&c_in[r >> 2], 1u);
-    } else if (partial && key == tie) {
+    else if (partial && key == tie)
       atomicOr(&lt[word], 1u << (off & 31));
-      atomicAdd(&c_tie[r >> 2], 1u);
+  }
+  __syncthreads();
+  // tile begins are multiples of 64 elements, so a tile's mask words are its own.  The
+  // candidates are distinct entries, so a tile's counts are the popcounts of its bitmap
+  // words: summed per wave (a wave's 64 words lie in one tile), one LDS add per wave,
+  // instead of one add per candidate on a counter that the whole wave shares
+  const int nw = (ch.t1 - ch.t0) * kTileWords;
+  for (int i0 = 0; i0 < nw; i0 += kSelThreads) {  // uniform: all lanes reach the sums
+    const int i = i0 + int(threadIdx.x);
+    uint32_t a = 0u, b = 0u;
+    if (i < nw) {
+      a = lm[i];
+      b = lt[i];
+      if ((a | b) != 0u) {
+        const int64_t gw = (cr.tbeg[(i / kTileWords) * 4] >> 5) + (i % kTileWords);
+        if (a) mask[gw] |= a;
+        if (b) tmask[gw] |= b;
+      }
+    }
+    const uint32_t na = wave_sum(uint32_t(__popc(a))), nb = wave_sum(uint32_t(__popc(b)));
+    if ((threadIdx.x & 63) == 0 && i < nw) {
+      if (na) atomicAdd(&c_in[i / kTileWords], na);
+      if (nb) atomicAdd(&c_tie[i / kTileWords], nb);
     }
   }
   __syncthreads();
-  // tile begins are multiples of 64 elements, so a tile's mask words are its own
-  for (int i = threadIdx.x; i < (ch.t1 - ch.t0) * kTileWords; i += kSelThreads) {
-    const uint32_t a = lm[i], b = lt[i];
-    if ((a | b) == 0u) continue;
-    const int64_t gw = (cr.tbeg[(i / kTileWords) * 4] >> 5) + (i % kTileWords);
-    if (a) mask[gw] |= a;
-    if (b) tmask[gw] |= b;
-  }
   if (int(threadIdx.x) < ch.t1 - ch.t0) {
     const int64_t trow = int64_t(w) * ntiles + L.tile_off + ch.t0 + threadIdx.x;
     tfin[trow] = c_in[threadIdx.x];
