@@ -112,7 +112,9 @@ psgd_status psgd_rtopk_plan_destroy(psgd_rtopk_plan* plan);
  *   value     [W][keep_total] float32 out
  *   update    [worker_stride] float32 out, or NULL (then not computed)
  *   workspace workspace_bytes of device memory; contents need not be preserved between
- *             steps, except for deferred-zero plans (see the flag)
+ *             steps, except for deferred-zero plans (see the flag).  Kept from step to
+ *             step, it carries each segment's predicted threshold bin, which spares most
+ *             steps a second read of M; any other contents give the same results
  * Asynchronous on `stream` (a hipStream_t; NULL = default stream). */
 psgd_status psgd_rtopk_step(psgd_rtopk_plan* plan, const void* grads, float* errors, const uint32_t* ranks,
                             int32_t* index, float* value, float* update, void* workspace, void* stream);
