@@ -202,6 +202,34 @@ def test_error_feedback_many_steps(deferred):
 
 
 @pytest.mark.parametrize("deferred", [False, True], ids=["plain", "deferred"])
+def test_threshold_moves_between_steps(deferred):
+    """The digit-1 bin each step marks against first is predicted from the last two
+    thresholds, and a wrong one only costs a second marking pass.  Gradient scales that
+    move the threshold by less than a bin, by one or two bins up and down, and by 4 and
+    6 octaves (past the prediction's four-bin limit) make it hit and miss both ways; every
+    step is compared exactly."""
+    W = 3
+    shapes = [(512, 2304), (64, 576), (10, 512)]
+    tops, keeps = _counts(shapes, 0.01, 2)
+    rng = np.random.default_rng(23)
+    run = RtopkRun(shapes, tops, keeps, W, deferred=deferred)
+    E = [np.zeros((W, r * c), np.float32) for r, c in shapes]
+    scale = 0.05
+    for step, f in enumerate([1.0, 1.05, 1.1, 1.2, 1.2, 0.85, 16.0, 1.0, 1.0 / 64, 1.0, 1.0]):
+        scale *= f
+        print(f"\n[case] threshold moves W={W} deferred={deferred} step {step} scale {scale:.3g}", flush=True)
+        G = [(scale * rng.standard_normal((W, r * c))).astype(np.float32) for r, c in shapes]
+        R = _ranks(rng, W, tops)
+        run.set_grads(G)
+        run.set_ranks(R)
+        run.step()
+        ref = oracle_step(run, G, E, tops, keeps, R, range(len(shapes)))
+        for li, st in ref.items():
+            compare(run, li, st)
+        E = [ref[li].errors for li in range(len(shapes))]
+
+
+@pytest.mark.parametrize("deferred", [False, True], ids=["plain", "deferred"])
 def test_bf16_gradients(deferred):
     print(f"\n[case] bf16 gradients W=4 deferred={deferred}", flush=True)
     W = 4
